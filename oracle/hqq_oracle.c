@@ -1,0 +1,303 @@
+/*
+ * hqq_oracle.c -- plain, slow, fp64 CPU oracle for group-wise HQQ quantization.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The product path (the
+ * HIP library) never calls, links or includes anything from this directory, and
+ * this file includes nothing from the product path.
+ *
+ * Source of the method: the web page "Half-Quadratic Quantization of Large
+ * Machine Learning Models" (Dropbox tech blog, in the csdn translation):
+ *   - section 2: objective argmin_{z,s} phi(W - Q^-1(Q(W))), the affine
+ *     quantizer Q(W) = round(W/s + z) and its inverse Q^-1(W_q) = s(W_q - z),
+ *     the half-quadratic split with s fixed (only z is optimized), and the
+ *     alternating updates sp1 (W_e), sp2 (z), beta <- kappa*beta;
+ *   - section 2.1: generalized lp soft-threshold
+ *       shrink(x, beta) = sign(x) * relu(|x| - |x|^(p-1) / beta);
+ *   - section 2.2: closed-form z update, the mean over the group axis of
+ *       W_q - (W - W_e)/s, implemented with the inverse scale 1/s;
+ *   - section 4.1: p = 0.7, beta = 1, kappa = 1.01, 20 iterations, early
+ *     exit once the error stops improving, group-wise buffers.
+ *
+ * Readings where the page is silent (each listed in the design notes):
+ *   init     min-max: s = (max-min)/qmax, inv_s = qmax/(max-min), z = -min*inv_s
+ *            (real-valued z); a constant group takes s = inv_s = 1.
+ *   round    round half to even (nearbyint under FE_TONEAREST).
+ *   clamp    codes clamped to [0, qmax] after rounding.
+ *   shrink   exactly the section-2.1 operator; 0 at x = 0 (where |x|^(p-1)
+ *            is undefined for p < 1).
+ *   error    e = sum_k |r_k|^err_pow over the group with r = W - Q^-1(Q(W)),
+ *            |0|^anything := 0; err_pow = p is the reading used everywhere
+ *            (phi of the section-2 objective); 1 and 2 exist only as a
+ *            sensitivity switch.
+ *   stop     per group; an evaluation is accepted only if its error is
+ *            strictly below the best so far, otherwise the solver stops and
+ *            keeps the best (last accepted) z.  With T iterations there are at
+ *            most T+1 evaluations and T z-updates.
+ *   storage  codes packed as an LSB-first little-endian bitstream over the
+ *            row-major element order; s and z stored as IEEE binary16 (RNE
+ *            from fp64, no intermediate fp32 rounding).
+ *
+ * Arithmetic: fp64, one thread, scalar loops, sums in index order.  The binary16
+ * conversions are written out from the IEEE 754 definition (no compiler
+ * half-precision type is used).
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "hqq_oracle.h"
+
+/* ------------------------------------------------------------------------- */
+/* IEEE 754 binary16 <-> binary64, by definition.                            */
+/* ------------------------------------------------------------------------- */
+
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+uint16_t oracle_f64_to_f16(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (isnan(v)) return 0x7e00;
+  /* 65520 is the midpoint between 65504 (largest finite, odd significand) and
+   * 2^16; RNE sends it and everything above to infinity. */
+  if (a >= 65520.0) return sign | 0x7c00;
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: quantum 2^-24; n in [0, 1024], n == 1024 encodes the
+     * smallest normal, which the continuous encoding below gives for free. */
+    double n = nearbyint(ldexp(a, 24));
+    return sign | (uint16_t)n;
+  }
+  int E;
+  (void)frexp(a, &E); /* a = f * 2^E, f in [0.5, 1) */
+  int e = E - 1;      /* a in [2^e, 2^(e+1)) */
+  double n = nearbyint(ldexp(a, 10 - e)); /* significand in [1024, 2048] */
+  /* n == 2048 rolls over into the next binade through the encoding itself */
+  uint32_t bits = ((uint32_t)(e + 15) << 10) + (uint32_t)(n - 1024.0);
+  if (bits >= 0x7c00) return sign | 0x7c00;
+  return sign | (uint16_t)bits;
+}
+
+void oracle_f16_to_f64_array(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}
+
+void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out) {
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16(v[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* The steps of the method.                                                  */
+/* ------------------------------------------------------------------------- */
+
+/* Generalized lp soft-threshold of section 2.1, as printed; 0 at x = 0. */
+double oracle_shrink_lp(double x, double beta, double p) {
+  if (x == 0.0) return 0.0;
+  double ax = fabs(x);
+  double v = ax - pow(ax, p - 1.0) / beta;
+  if (v < 0.0) v = 0.0; /* relu */
+  return x > 0.0 ? v : -v;
+}
+
+/* Q_{z,s}(W) of section 2 with the inverse scale: clamp(round(w*inv_s + z)). */
+double oracle_quantize_value(double w, double inv_s, double z, int qmax) {
+  double q = nearbyint(w * inv_s + z);
+  if (q < 0.0) q = 0.0;
+  if (q > (double)qmax) q = (double)qmax;
+  return q;
+}
+
+/* Min-max initialisation (reading: the group min and max map to 0 and qmax). */
+void oracle_minmax_init(const double* w, int g, int qmax, double* s, double* inv_s, double* z) {
+  double mn = w[0], mx = w[0];
+  for (int k = 1; k < g; ++k) {
+    if (w[k] < mn) mn = w[k];
+    if (w[k] > mx) mx = w[k];
+  }
+  if (mx > mn) {
+    *s = (mx - mn) / (double)qmax;
+    *inv_s = (double)qmax / (mx - mn);
+  } else {
+    *s = 1.0;
+    *inv_s = 1.0;
+  }
+  *z = -mn * (*inv_s);
+}
+
+/* sum_k |r_k|^err_pow with |0|^anything := 0 (phi of the section-2 objective). */
+double oracle_group_error(const double* r, int g, double err_pow) {
+  double e = 0.0;
+  for (int k = 0; k < g; ++k) {
+    if (r[k] != 0.0) e += pow(fabs(r[k]), err_pow);
+  }
+  return e;
+}
+
+/* sp2 of section 2.2: z = mean over the group of (W_q - (W - W_e) * inv_s). */
+double oracle_z_update(const double* q, const double* w, const double* we, double inv_s, int g) {
+  double acc = 0.0;
+  for (int k = 0; k < g; ++k) acc += q[k] - (w[k] - we[k]) * inv_s;
+  return acc / (double)g;
+}
+
+/* One group through the whole solver.  `trace` (may be NULL) receives every
+ * evaluated error e_0, e_1, ... in order; *n_trace their count. */
+int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, double kappa,
+                     int iters, int early_stop, double err_pow, uint8_t* codes_out,
+                     oracle_group_result_t* res, double* trace, int* n_trace) {
+  if (g <= 0 || g > ORACLE_MAX_GROUP || nbits < 1 || nbits > 8 || iters < 0) return -1;
+  int qmax = (1 << nbits) - 1;
+  double q[ORACLE_MAX_GROUP], r[ORACLE_MAX_GROUP], we[ORACLE_MAX_GROUP], best_q[ORACLE_MAX_GROUP];
+  double s, inv_s, z;
+  oracle_minmax_init(w, g, qmax, &s, &inv_s, &z);
+
+  double beta = beta0;
+  double best_e = INFINITY, best_z = z, e0 = NAN;
+  int t_star = 0, n_eval = 0;
+  for (int t = 0; t <= iters; ++t) {
+    /* W_q = Q(W) at the current z; residual r = W - Q^-1(W_q). */
+    for (int k = 0; k < g; ++k) q[k] = oracle_quantize_value(w[k], inv_s, z, qmax);
+    for (int k = 0; k < g; ++k) r[k] = w[k] - s * (q[k] - z);
+    double e = oracle_group_error(r, g, err_pow);
+    if (trace) trace[n_eval] = e;
+    ++n_eval;
+    if (t == 0) e0 = e;
+    if (early_stop && !(e < best_e)) break; /* error no longer improves */
+    best_e = e;
+    best_z = z;
+    t_star = t;
+    for (int k = 0; k < g; ++k) best_q[k] = q[k];
+    if (t == iters) break;
+    /* sp1: W_e = shrink(W - Q^-1(Q(W)), beta) */
+    for (int k = 0; k < g; ++k) we[k] = oracle_shrink_lp(r[k], beta, p);
+    /* sp2: closed-form mean */
+    z = oracle_z_update(q, w, we, inv_s, g);
+    beta = kappa * beta;
+  }
+  for (int k = 0; k < g; ++k) codes_out[k] = (uint8_t)best_q[k];
+  res->scale = s;
+  res->inv_scale = inv_s;
+  res->zero = best_z;
+  res->stop_step = t_star;
+  res->err_init = e0;
+  res->err_best = best_e;
+  res->n_eval = n_eval;
+  if (n_trace) *n_trace = n_eval;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Packed storage: LSB-first little-endian bitstream, element n occupies      */
+/* bits [n*nbits, (n+1)*nbits) of the stream, bit i of a byte is 2^i.        */
+/* ------------------------------------------------------------------------- */
+
+int64_t oracle_packed_bytes(int64_t n, int nbits) { return (n * nbits + 7) / 8; }
+
+void oracle_pack_codes(const uint8_t* codes, int64_t n, int nbits, uint8_t* out) {
+  int64_t nbytes = oracle_packed_bytes(n, nbits);
+  memset(out, 0, (size_t)nbytes);
+  for (int64_t i = 0; i < n; ++i) {
+    for (int b = 0; b < nbits; ++b) {
+      if ((codes[i] >> b) & 1) {
+        int64_t bit = i * nbits + b;
+        out[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+      }
+    }
+  }
+}
+
+void oracle_unpack_codes(const uint8_t* packed, int64_t n, int nbits, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) {
+    unsigned c = 0;
+    for (int b = 0; b < nbits; ++b) {
+      int64_t bit = i * nbits + b;
+      c |= (unsigned)((packed[bit >> 3] >> (bit & 7)) & 1) << b;
+    }
+    codes[i] = (uint8_t)c;
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Whole matrix.                                                             */
+/* ------------------------------------------------------------------------- */
+
+int oracle_hqq_quantize(const uint16_t* W_f16, int64_t rows, int64_t cols, int nbits,
+                        int group_size, double p, double beta, double kappa, int iters,
+                        int early_stop, double err_pow, uint8_t* packed, uint16_t* scale_f16,
+                        uint16_t* zero_f16, double* scale_f64, double* zero_f64,
+                        uint8_t* stop_step, double* err_init, double* err_best,
+                        uint8_t* codes_out) {
+  if (rows < 0 || cols < 0 || group_size <= 0 || group_size > ORACLE_MAX_GROUP) return -1;
+  if (cols % group_size != 0) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  int64_t n = rows * cols;
+  int64_t ngroups = n / group_size;
+  double w[ORACLE_MAX_GROUP];
+  uint8_t gc[ORACLE_MAX_GROUP];
+  uint8_t* codes = codes_out;
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    /* groups are contiguous along the row (input dimension); a row holds
+     * cols/group_size of them, so the flat group index is row-major. */
+    const uint16_t* src = W_f16 + gi * group_size;
+    for (int k = 0; k < group_size; ++k) w[k] = oracle_f16_to_f64(src[k]);
+    oracle_group_result_t res;
+    if (oracle_hqq_group(w, group_size, nbits, p, beta, kappa, iters, early_stop, err_pow, gc,
+                         &res, NULL, NULL) != 0)
+      return -1;
+    if (scale_f16) scale_f16[gi] = oracle_f64_to_f16(res.scale);
+    if (zero_f16) zero_f16[gi] = oracle_f64_to_f16(res.zero);
+    if (scale_f64) scale_f64[gi] = res.scale;
+    if (zero_f64) zero_f64[gi] = res.zero;
+    if (stop_step) stop_step[gi] = (uint8_t)res.stop_step;
+    if (err_init) err_init[gi] = res.err_init;
+    if (err_best) err_best[gi] = res.err_best;
+    if (codes) memcpy(codes + gi * group_size, gc, (size_t)group_size);
+    if (packed) {
+      /* group_size * nbits is a multiple of 8 for every group size >= 8, so each
+       * group owns whole bytes of the stream. */
+      if ((group_size * nbits) % 8 == 0) {
+        oracle_pack_codes(gc, group_size, nbits, packed + gi * group_size * nbits / 8);
+      } else {
+        return -1;
+      }
+    }
+  }
+  return 0;
+}
+
+/* Dequantization Q^-1(W_q) = s (W_q - z) from the stored binary16 s and z,
+ * evaluated in fp64 (exact for binary16 operands and codes < 256) and rounded
+ * once to binary16. */
+int oracle_hqq_dequantize(const uint8_t* packed, const uint16_t* scale_f16,
+                          const uint16_t* zero_f16, int64_t rows, int64_t cols, int nbits,
+                          int group_size, uint16_t* W_out_f16) {
+  if (rows < 0 || cols < 0 || group_size <= 0 || cols % group_size != 0) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  int64_t n = rows * cols;
+  for (int64_t i = 0; i < n; ++i) {
+    unsigned c = 0;
+    for (int b = 0; b < nbits; ++b) {
+      int64_t bit = i * nbits + b;
+      c |= (unsigned)((packed[bit >> 3] >> (bit & 7)) & 1) << b;
+    }
+    int64_t gi = i / group_size;
+    double s = oracle_f16_to_f64(scale_f16[gi]);
+    double z = oracle_f16_to_f64(zero_f16[gi]);
+    W_out_f16[i] = oracle_f64_to_f16(s * ((double)c - z));
+  }
+  return 0;
+}

@@ -1,0 +1,62 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a private copy of the oracle's C source
+(a dropped term, a wrong sign or index, a wrong rounding rule, a wrong bit order,
+...), rebuilds that copy with gcc in a temporary directory and runs the pin suite
+against it.  Every mutant must make at least one pin fail.  The real oracle is
+never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "shrink exponent p instead of p-1": ("pow(ax, p - 1.0)", "pow(ax, p)"),
+    "shrink without 1/beta": ("pow(ax, p - 1.0) / beta", "pow(ax, p - 1.0)"),
+    "z update adds W_e": ("(w[k] - we[k]) * inv_s", "(w[k] + we[k]) * inv_s"),
+    "z update drops W_e": ("(w[k] - we[k]) * inv_s", "(w[k]) * inv_s"),
+    "z update divides by g-1": ("return acc / (double)g;", "return acc / (double)(g - 1);"),
+    "residual sign of z": ("r[k] = w[k] - s * (q[k] - z)", "r[k] = w[k] - s * (q[k] + z)"),
+    "init z sign": ("*z = -mn * (*inv_s);", "*z = mn * (*inv_s);"),
+    "min-max skips last element": ("for (int k = 1; k < g; ++k) {\n    if (w[k] < mn)",
+                                   "for (int k = 1; k < g - 1; ++k) {\n    if (w[k] < mn)"),
+    "stop only on strict increase": ("!(e < best_e)", "(e > best_e)"),
+    "return the rejected z": ("if (early_stop && !(e < best_e)) break;",
+                              "if (early_stop && !(e < best_e)) { best_z = z; "
+                              "for (int k = 0; k < g; ++k) best_q[k] = q[k]; break; }"),
+    "stop step off by one": ("t_star = t;", "t_star = t > 0 ? t - 1 : 0;"),
+    "beta never updated": ("beta = kappa * beta;", "beta = beta;"),
+    "round half away from zero": ("nearbyint(w * inv_s + z)", "round(w * inv_s + z)"),
+    "no upper clamp": ("if (q > (double)qmax) q = (double)qmax;", ""),
+    "error of squared residual": ("pow(fabs(r[k]), err_pow)", "pow(r[k] * r[k], err_pow)"),
+    "pack MSB first": ("out[bit >> 3] |= (uint8_t)(1u << (bit & 7));",
+                       "out[bit >> 3] |= (uint8_t)(0x80u >> (bit & 7));"),
+    "binary16 truncates": ("double n = nearbyint(ldexp(a, 10 - e));",
+                           "double n = floor(ldexp(a, 10 - e));"),
+    "groups read column-major": ("const uint16_t* src = W_f16 + gi * group_size;",
+                                 "const uint16_t* src = W_f16 + ((gi % rows) * cols + "
+                                 "(gi / rows) * group_size);"),
+    "dequant adds z": ("s * ((double)c - z)", "s * ((double)c + z)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    before, after = MUTANTS[name]
+    for sub in ("oracle", "workloads", "tests"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    src_path = tmp_path / "oracle" / "hqq_oracle.c"
+    src = src_path.read_text()
+    assert src.count(before) >= 1, f"mutation site for {name!r} not found"
+    src_path.write_text(src.replace(before, after, 1))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
+                       timeout=600, env=env)
+    assert r.returncode != 0, f"mutant {name!r} survived the pins:\n{r.stdout[-2000:]}"
