@@ -1,0 +1,193 @@
+"""MI355X (gfx950) group-wise HQQ weight quantizer: thin Python binding.
+
+Every step of the quantization runs in the HIP kernels of ``libhqq_mi355x.so``
+(built from ``csrc/`` by ``build.py``); this module only marshals arguments
+through ctypes.  PyTorch provides device memory and the current stream.  There
+is no fallback: if the library is missing or no device is usable, calls raise.
+
+Low-level functions carry the names of the C ABI in ``include/hqq.h`` and take
+raw device addresses; :func:`quantize` and :func:`dequantize` wrap them for
+torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhqq_mi355x.so")
+
+HQQ_OK = 0
+HQQ_ERR_INVALID_ARG = 1
+HQQ_ERR_UNSUPPORTED = 2
+HQQ_ERR_ALIGNMENT = 3
+HQQ_ERR_LAUNCH = 4
+
+# Symbols declared in include/hqq.h.
+EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_dequantize", "hqq_packed_bytes",
+                    "hqq_num_groups", "hqq_status_string")
+
+
+class HQQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {hqq_status_string(status)} (status {status})")
+        self.status = status
+
+
+class hqq_options_t(ctypes.Structure):
+    _fields_ = [("early_stop", ctypes.c_int),
+                ("scale_f32", ctypes.c_void_p), ("zero_f32", ctypes.c_void_p),
+                ("stop_step", ctypes.c_void_p), ("err_init", ctypes.c_void_p),
+                ("err_best", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_weight_quantization_amd.build`")
+    lib = ctypes.CDLL(path)
+    I, I64, F, P = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.hqq_quantize.restype = I
+    lib.hqq_quantize.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P, P]
+    lib.hqq_quantize_ex.restype = I
+    lib.hqq_quantize_ex.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
+                                    ctypes.POINTER(hqq_options_t), P]
+    lib.hqq_dequantize.restype = I
+    lib.hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
+    lib.hqq_packed_bytes.restype = I64
+    lib.hqq_packed_bytes.argtypes = [I64, I64, I]
+    lib.hqq_num_groups.restype = I64
+    lib.hqq_num_groups.argtypes = [I64, I64, I]
+    lib.hqq_status_string.restype = ctypes.c_char_p
+    lib.hqq_status_string.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------- C ABI names --
+
+def hqq_status_string(status: int) -> str:
+    return load_library().hqq_status_string(int(status)).decode()
+
+
+def hqq_packed_bytes(rows: int, cols: int, nbits: int) -> int:
+    return load_library().hqq_packed_bytes(rows, cols, nbits)
+
+
+def hqq_num_groups(rows: int, cols: int, group_size: int) -> int:
+    return load_library().hqq_num_groups(rows, cols, group_size)
+
+
+def hqq_quantize(W_f16: int, rows: int, cols: int, nbits: int, group_size: int, p: float,
+                 beta: float, kappa: float, iters: int, packed_codes: int, scale_f16: int,
+                 zero_f16: int, stream: int = 0) -> int:
+    return load_library().hqq_quantize(W_f16, rows, cols, nbits, group_size, p, beta, kappa,
+                                       iters, packed_codes, scale_f16, zero_f16, stream)
+
+
+def hqq_quantize_ex(W_f16: int, rows: int, cols: int, nbits: int, group_size: int, p: float,
+                    beta: float, kappa: float, iters: int, packed_codes: int, scale_f16: int,
+                    zero_f16: int, options: Optional[hqq_options_t], stream: int = 0) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    return load_library().hqq_quantize_ex(W_f16, rows, cols, nbits, group_size, p, beta, kappa,
+                                          iters, packed_codes, scale_f16, zero_f16, opt, stream)
+
+
+def hqq_dequantize(packed_codes: int, scale_f16: int, zero_f16: int, rows: int, cols: int,
+                   nbits: int, group_size: int, W_out_f16: int, stream: int = 0) -> int:
+    return load_library().hqq_dequantize(packed_codes, scale_f16, zero_f16, rows, cols, nbits,
+                                         group_size, W_out_f16, stream)
+
+
+# ----------------------------------------------------------- torch helpers --
+
+@dataclass
+class QuantizedWeight:
+    packed: "torch.Tensor"            # uint8, hqq_packed_bytes(rows, cols, nbits)
+    scale: "torch.Tensor"             # fp16, rows x cols/group_size
+    zero: "torch.Tensor"              # fp16, rows x cols/group_size (code units)
+    rows: int
+    cols: int
+    nbits: int
+    group_size: int
+    scale_f32: Optional["torch.Tensor"] = None
+    zero_f32: Optional["torch.Tensor"] = None
+    stop_step: Optional["torch.Tensor"] = None
+    err_init: Optional["torch.Tensor"] = None
+    err_best: Optional["torch.Tensor"] = None
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _addr(t) -> int:
+    return int(t.data_ptr()) if t is not None else 0
+
+
+def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
+             kappa: float = 1.01, iters: int = 20, early_stop: bool = True, debug: bool = False,
+             out: Optional[QuantizedWeight] = None, stream=None) -> QuantizedWeight:
+    """Quantize a contiguous rows x cols fp16 CUDA tensor on the given (or current) stream.
+
+    ``out`` may supply preallocated output tensors (reused as-is).  With ``debug`` the
+    fp32 s and z, the stop step and the initial/best errors per group are returned too.
+    """
+    import torch
+    if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D float16 CUDA tensor")
+    rows, cols = W.shape
+    ng = hqq_num_groups(rows, cols, group_size)
+    nb = hqq_packed_bytes(rows, cols, nbits)
+    if ng < 0 or nb < 0:
+        raise HQQError(HQQ_ERR_INVALID_ARG if nb >= 0 else HQQ_ERR_UNSUPPORTED, "quantize")
+    dev = W.device
+    if out is None:
+        out = QuantizedWeight(
+            packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
+            scale=torch.empty((rows, cols // group_size), dtype=torch.float16, device=dev),
+            zero=torch.empty((rows, cols // group_size), dtype=torch.float16, device=dev),
+            rows=rows, cols=cols, nbits=nbits, group_size=group_size)
+    if debug and out.stop_step is None:
+        shp = (rows, cols // group_size)
+        out.scale_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
+        out.zero_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
+        out.stop_step = torch.empty(shp, dtype=torch.uint8, device=dev)
+        out.err_init = torch.empty(shp, dtype=torch.float32, device=dev)
+        out.err_best = torch.empty(shp, dtype=torch.float32, device=dev)
+    opts = None
+    if debug or not early_stop:
+        opts = hqq_options_t(int(bool(early_stop)), _addr(out.scale_f32 if debug else None),
+                             _addr(out.zero_f32 if debug else None),
+                             _addr(out.stop_step if debug else None),
+                             _addr(out.err_init if debug else None),
+                             _addr(out.err_best if debug else None))
+    st = hqq_quantize_ex(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
+                         float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
+                         _addr(out.zero), opts, _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_quantize_ex")
+    return out
+
+
+def dequantize(q: QuantizedWeight, out=None, stream=None):
+    """Return s*(W_q - z) as a rows x cols fp16 tensor (single rounding from the exact value)."""
+    import torch
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=torch.float16, device=q.scale.device)
+    st = hqq_dequantize(_addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows, q.cols, q.nbits,
+                        q.group_size, _addr(out), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_dequantize")
+    return out

@@ -1,0 +1,181 @@
+// hqq_api.hip -- extern "C" entry points of the HQQ quantizer (see include/hqq.h):
+// argument validation, grid sizing and the launch on the caller's stream.
+// No allocation, no synchronization, no global mutable state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/hqq.h"
+#include "hqq_internal.h"
+
+namespace {
+
+constexpr int kMaxIters = 255;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool supported_nbits(int nbits) { return nbits == 2 || nbits == 3 || nbits == 4 || nbits == 8; }
+
+bool supported_group(int g) { return g == 16 || g == 32 || g == 64 || g == 128; }
+
+// rows*cols without overflow (both >= 0); -1 on overflow.
+int64_t checked_elems(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  if (rows != 0 && cols > INT64_MAX / 8 / rows) return -1;  // keep *nbits and *2 bytes in range
+  return rows * cols;
+}
+
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+// Wavefronts resident per SIMD that the solver grid aims for, and how many
+// groups one wavefront's queue holds at least (a multiple of its slot count).
+constexpr int kSolveWavesPerSimd = 8;
+constexpr int kSimdsPerCu = 4;
+
+int validate_common(int64_t rows, int64_t cols, int nbits, int group_size) {
+  if (checked_elems(rows, cols) < 0) return HQQ_ERR_INVALID_ARG;
+  if (!supported_nbits(nbits) || !supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
+  if (cols % group_size != 0) return HQQ_ERR_INVALID_ARG;
+  return HQQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hqq_status_string(int status) {
+  switch (status) {
+    case HQQ_OK: return "ok";
+    case HQQ_ERR_INVALID_ARG: return "invalid argument";
+    case HQQ_ERR_UNSUPPORTED: return "unsupported nbits or group_size";
+    case HQQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case HQQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits) {
+  const int64_t n = checked_elems(rows, cols);
+  if (n < 0 || !supported_nbits(nbits)) return -1;
+  return (n * nbits + 7) / 8;
+}
+
+int64_t hqq_num_groups(int64_t rows, int64_t cols, int group_size) {
+  const int64_t n = checked_elems(rows, cols);
+  if (n < 0 || !supported_group(group_size) || cols % group_size != 0) return -1;
+  return n / group_size;
+}
+
+int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                    float p, float beta, float kappa, int iters, void* packed_codes,
+                    void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream) {
+  int st = validate_common(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  if (!(p >= 0.0f && p <= 1.0f)) return HQQ_ERR_INVALID_ARG;
+  if (!(beta > 0.0f) || !isfinite(beta)) return HQQ_ERR_INVALID_ARG;
+  if (!(kappa > 0.0f) || !isfinite(kappa)) return HQQ_ERR_INVALID_ARG;
+  if (iters < 0 || iters > kMaxIters) return HQQ_ERR_INVALID_ARG;
+  const int64_t n = rows * cols;
+  if (n == 0) return HQQ_OK;
+  if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
+      !aligned(zero_f16, 2))
+    return HQQ_ERR_ALIGNMENT;
+  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (opt) {
+    o = *opt;
+    if (o.early_stop != 0 && o.early_stop != 1) return HQQ_ERR_INVALID_ARG;
+    if ((o.scale_f32 && !aligned(o.scale_f32, 4)) || (o.zero_f32 && !aligned(o.zero_f32, 4)) ||
+        (o.err_init && !aligned(o.err_init, 4)) || (o.err_best && !aligned(o.err_best, 4)))
+      return HQQ_ERR_ALIGNMENT;
+  }
+
+  const int64_t ngroups = n / group_size;
+  const int lanes_per_group = group_size / hqq::kLaneElems;
+  const int slots = hqq::kWave / lanes_per_group;  // groups resident in one wavefront
+
+  hqq::SolveParams prm;
+  prm.W = static_cast<const uint4*>(W_f16);
+  prm.packed = static_cast<uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<uint16_t*>(zero_f16);
+  prm.scale32 = o.scale_f32;
+  prm.zero32 = o.zero_f32;
+  prm.stop_step = o.stop_step;
+  prm.err_init = o.err_init;
+  prm.err_best = o.err_best;
+  prm.ngroups = ngroups;
+  prm.qmax = (float)((1 << nbits) - 1);
+  prm.p = p;
+  prm.pm1 = p - 1.0f;
+  prm.pm2 = p - 2.0f;
+  prm.inv_beta0 = (float)(1.0 / (double)beta);
+  prm.inv_kappa = (float)(1.0 / (double)kappa);
+  // The shrink of section 2.1 vanishes for |x|^(2-p) <= 1/beta, i.e. |x| <= beta^(-1/(2-p)).
+  prm.tau0 = (float)pow((double)beta, -1.0 / (2.0 - (double)p));
+  prm.rho = (float)pow((double)kappa, -1.0 / (2.0 - (double)p));
+  prm.iters = iters;
+  prm.early_stop = o.early_stop;
+  prm.nbits = nbits;
+  prm.refill_at = slots / 2 > 0 ? slots / 2 : 1;
+
+  const int power_mode = p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
+
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  const int64_t target_waves = (int64_t)cus * kSimdsPerCu * kSolveWavesPerSimd;
+  int64_t per_wave = (ngroups + target_waves - 1) / target_waves;
+  if (per_wave < slots) per_wave = slots;
+  per_wave = (per_wave + slots - 1) / slots * slots;
+  const int64_t nwaves = (ngroups + per_wave - 1) / per_wave;
+  const int64_t waves_per_block = hqq::kBlock / hqq::kWave;
+  const int64_t blocks = (nwaves + waves_per_block - 1) / waves_per_block;
+  prm.groups_per_wave = per_wave;
+
+  hipError_t err = hqq::launch_solve(prm, group_size, power_mode, (int)blocks,
+                                     static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int hqq_quantize(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size, float p,
+                 float beta, float kappa, int iters, void* packed_codes, void* scale_f16,
+                 void* zero_f16, void* stream) {
+  return hqq_quantize_ex(W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters, packed_codes,
+                         scale_f16, zero_f16, nullptr, stream);
+}
+
+int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* zero_f16,
+                   int64_t rows, int64_t cols, int nbits, int group_size, void* W_out_f16,
+                   void* stream) {
+  int st = validate_common(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  const int64_t n = rows * cols;
+  if (n == 0) return HQQ_OK;
+  if (!packed_codes || !scale_f16 || !zero_f16 || !W_out_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
+      !aligned(W_out_f16, 16))
+    return HQQ_ERR_ALIGNMENT;
+  hqq::DequantParams prm;
+  prm.packed = static_cast<const uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<const uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<const uint16_t*>(zero_f16);
+  prm.out = static_cast<uint4*>(W_out_f16);
+  prm.nchunks = n / hqq::kLaneElems;
+  prm.chunks_per_group = group_size / hqq::kLaneElems;
+  prm.nbits = nbits;
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  int64_t blocks = (prm.nchunks + hqq::kBlock - 1) / hqq::kBlock;
+  const int64_t cap = (int64_t)cus * 16;
+  if (blocks > cap) blocks = cap;
+  hipError_t err = hqq::launch_dequant(prm, (int)blocks, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+}  // extern "C"

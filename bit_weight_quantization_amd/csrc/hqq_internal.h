@@ -1,0 +1,59 @@
+// hqq_internal.h -- launch parameters shared by the host entry points and the
+// gfx950 kernels of the HQQ quantizer.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hqq {
+
+// How the lp power |x|^p is evaluated: general 0 < p < 1 through log2/exp2,
+// or the two exact special cases p = 1 and p = 0.
+enum PowerMode : int { kPowGeneral = 0, kPowOne = 1, kPowZero = 2 };
+
+struct SolveParams {
+  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8
+  uint8_t* packed;         // packed code stream
+  uint16_t* scale16;       // binary16 s per group
+  uint16_t* zero16;        // binary16 z per group
+  float* scale32;          // optional outputs (may be null)
+  float* zero32;
+  uint8_t* stop_step;
+  float* err_init;
+  float* err_best;
+  int64_t ngroups;
+  int64_t groups_per_wave; // contiguous queue length of one wavefront
+  float qmax;
+  float p;                 // lp exponent
+  float pm1;               // p - 1
+  float pm2;               // p - 2
+  float inv_beta0;         // 1 / beta_0
+  float inv_kappa;         // 1 / kappa
+  float tau0;              // beta_0^(-1/(2-p)): the shrink is zero for |r| <= tau
+  float rho;               // kappa^(-1/(2-p)): tau_{t+1} = rho * tau_t
+  int iters;
+  int early_stop;
+  int nbits;
+  int refill_at;           // refill idle group slots once this many are idle
+};
+
+struct DequantParams {
+  const uint8_t* packed;
+  const uint16_t* scale16;
+  const uint16_t* zero16;
+  uint4* out;              // fp16 output as 16-byte chunks of 8
+  int64_t nchunks;         // elements / 8
+  int chunks_per_group;    // group_size / 8
+  int nbits;
+};
+
+// Launchers (return a hipError_t of the launch).
+hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int blocks,
+                        hipStream_t stream);
+hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
+
+// Segment geometry shared with the host grid sizing: each lane holds 8 weights.
+constexpr int kLaneElems = 8;
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+
+}  // namespace hqq

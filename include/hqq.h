@@ -1,0 +1,147 @@
+/*
+ * hqq.h -- C ABI of the MI355X (gfx950) group-wise HQQ weight quantizer.
+ *
+ * The method is the one on the page "Half-Quadratic Quantization of Large
+ * Machine Learning Models" (Dropbox tech blog):
+ *   section 2    affine quantizer Q(W) = round(W/s + z) = W_q and its inverse
+ *                Q^-1(W_q) = s (W_q - z); the error phi(W - Q^-1(Q(W))) with a
+ *                sparsity-promoting lp norm; a half-quadratic split with the
+ *                scale s fixed so that only z is optimized; alternating updates
+ *                sp1 (W_e), sp2 (z) and beta <- kappa * beta;
+ *   section 2.1  sp1 is the generalized soft-threshold
+ *                shrink(x, beta) = sign(x) relu(|x| - |x|^(p-1) / beta);
+ *   section 2.2  sp2 is the mean over the group of W_q - (W - W_e)/s, computed
+ *                with the inverse scale 1/s;
+ *   section 4.1  p = 0.7, beta = 1, kappa = 1.01, 20 iterations, early exit once
+ *                the error stops improving, group-wise quantized buffers.
+ * Readings of points the page leaves open (min-max initialisation, rounding
+ * half to even, clamping to [0, 2^nbits - 1], the per-group lp error
+ * sum |W - Q^-1(Q(W))|^p as the early-stop criterion with strict improvement,
+ * LSB-first bit packing) are stated with each entry point below.
+ *
+ * Conventions for every entry point:
+ *   - Array arguments are DEVICE pointers (HBM of the current HIP device),
+ *     allocated and owned by the caller.  The library never allocates, frees
+ *     or synchronizes.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream).  The status is returned
+ *     synchronously; faults inside a kernel surface at the caller's next
+ *     synchronization, as usual in HIP.
+ *   - All arguments are validated before anything is enqueued: on any error
+ *     nothing is launched and no output byte is written.
+ *   - Inputs are read-only; outputs are fully overwritten.  Inputs and outputs
+ *     must not overlap.  Calls are reentrant: the library holds no mutable
+ *     global state.
+ *   - Matrices are row-major rows x cols.  Groups are group_size consecutive
+ *     elements of a row (the input dimension); cols must be a multiple of
+ *     group_size, so group j of row i has flat index i*(cols/group_size) + j and
+ *     covers elements [j*group_size, (j+1)*group_size) of that row.
+ */
+#ifndef HQQ_MI355X_H
+#define HQQ_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  HQQ_OK = 0,
+  HQQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, parameter out of range,
+                              cols not a multiple of group_size, size overflow */
+  HQQ_ERR_UNSUPPORTED = 2, /* nbits or group_size outside the supported sets */
+  HQQ_ERR_ALIGNMENT = 3,   /* a pointer misses its documented alignment */
+  HQQ_ERR_LAUNCH = 4       /* the HIP runtime refused the launch (e.g. no device) */
+};
+
+/* Optional outputs and switches of hqq_quantize_ex.  Every pointer may be NULL.
+ * Per-group arrays have hqq_num_groups(rows, cols, group_size) elements in the
+ * row-major group order described above. */
+typedef struct {
+  int early_stop;      /* 1: per-group early exit (section 4.1, the default of
+                          hqq_quantize).  0: every iteration is accepted and the
+                          z after `iters` updates is returned. */
+  float* scale_f32;    /* s as computed in fp32, before the binary16 cast */
+  float* zero_f32;     /* returned z in fp32, before the binary16 cast */
+  uint8_t* stop_step;  /* t*: index of the accepted evaluation whose z is
+                          returned (0 = the min-max initialisation) */
+  float* err_init;     /* e_0 = sum |W - Q^-1(Q(W))|^p at the initial z */
+  float* err_best;     /* e_{t*}, the error at the returned z */
+} hqq_options_t;
+
+/*
+ * hqq_quantize -- group-wise asymmetric quantization with the HQQ zero-point
+ * solver (sections 2, 2.1, 2.2 and 4.1 of the page above).
+ *
+ * For every group of group_size weights w_k:
+ *   init  s = (max - min) / qmax, 1/s = qmax / (max - min), z = -min / s
+ *         (qmax = 2^nbits - 1; a constant group takes s = 1);
+ *   for t = 0 .. iters:
+ *         W_q = clamp(round_half_even(w / s + z), 0, qmax)
+ *         r   = w - s (W_q - z)                       residual
+ *         e_t = sum_k |r_k|^p   (|0|^p := 0)          lp error of section 2
+ *         stop unless e_t < best error so far; otherwise accept z;
+ *         if t == iters stop;
+ *         W_e = sign(r) relu(|r| - |r|^(p-1) / beta_t) (0 where r = 0)   sp1
+ *         z   = mean_k (W_q - (w - W_e) / s)                             sp2
+ *         beta_{t+1} = kappa * beta_t
+ *   outputs: the codes W_q at the accepted z, s and z (binary16, RNE).
+ * Arithmetic is fp32 on the device (the page's half-precision pipeline is not
+ * reproduced); the codes are those of the fp32 solver.
+ *
+ * W_f16        rows x cols binary16 weights; 16-byte aligned.
+ * rows, cols   >= 0; rows*cols == 0 is a valid no-op.  cols % group_size == 0.
+ * nbits        2, 3, 4 or 8.
+ * group_size   16, 32, 64 or 128.
+ * p            lp exponent, 0 <= p <= 1 (section 2.1 allows this range).
+ * beta         initial beta > 0, finite.      kappa  > 0, finite.
+ * iters        0 .. 255 (0 gives plain min-max round-to-nearest).
+ * packed_codes hqq_packed_bytes(rows, cols, nbits) bytes: an LSB-first
+ *              little-endian bitstream over the row-major elements (element n
+ *              occupies bits [n*nbits, (n+1)*nbits); bit i of a byte is 2^i).
+ *              nbits = 4: byte k = code[2k] | code[2k+1] << 4.  8-byte aligned.
+ * scale_f16    hqq_num_groups(...) binary16 values of s.  2-byte aligned.
+ * zero_f16     hqq_num_groups(...) binary16 values of z, in code units
+ *              (real-valued, not rounded to an integer).  2-byte aligned.
+ * stream       hipStream_t or NULL.
+ * Returns HQQ_OK or an error code; see the conventions above.
+ */
+int hqq_quantize(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                 float p, float beta, float kappa, int iters, void* packed_codes,
+                 void* scale_f16, void* zero_f16, void* stream);
+
+/* hqq_quantize with the optional outputs and switches of hqq_options_t
+ * (opt == NULL behaves exactly like hqq_quantize).  Optional float outputs
+ * must be 4-byte aligned. */
+int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                    float p, float beta, float kappa, int iters, void* packed_codes,
+                    void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream);
+
+/*
+ * hqq_dequantize -- the inverse quantizer Q^-1(W_q) = s (W_q - z) of section 2,
+ * evaluated from the stored binary16 s and z and rounded once (RNE) to binary16.
+ * The result equals the exact value s*(W_q - z) rounded to binary16.
+ * Layouts and alignment as for hqq_quantize; W_out_f16 (rows x cols) must be
+ * 16-byte aligned.
+ */
+int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* zero_f16,
+                   int64_t rows, int64_t cols, int nbits, int group_size, void* W_out_f16,
+                   void* stream);
+
+/* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
+ * shapes).  Returns -1 for invalid arguments or overflow. */
+int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);
+
+/* Number of groups: rows*cols/group_size.  -1 for invalid arguments. */
+int64_t hqq_num_groups(int64_t rows, int64_t cols, int group_size);
+
+/* Static, never-NULL description of a status code. */
+const char* hqq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQQ_MI355X_H */

@@ -65,6 +65,8 @@ def _load():
     lib.oracle_z_update.argtypes = [P, P, P, D, I]
     lib.oracle_hqq_group.restype = I
     lib.oracle_hqq_group.argtypes = [P, I, I, D, D, D, I, I, D, P, P, P, P]
+    lib.oracle_hqq_group_replay.restype = I
+    lib.oracle_hqq_group_replay.argtypes = [P, I, I, D, D, D, I, I, D, P, P, P, P, P, I, P, P, I, P]
     lib.oracle_packed_bytes.restype = I64
     lib.oracle_packed_bytes.argtypes = [I64, I]
     lib.oracle_pack_codes.argtypes = [P, I64, I, P]
@@ -166,6 +168,34 @@ def hqq_group(w, nbits: int, p: float = 0.7, beta: float = 1.0, kappa: float = 1
         raise ValueError("oracle_hqq_group rejected its arguments")
     return GroupResult(codes, res.scale, res.inv_scale, res.zero, res.stop_step, res.err_init,
                        res.err_best, res.n_eval, trace[: n_trace.value].copy())
+
+
+def hqq_group_replay(w, nbits: int, flips=(), inverts=(), p: float = 0.7, beta: float = 1.0,
+                     kappa: float = 1.01, iters: int = 20, early_stop: bool = True,
+                     err_pow: float | None = None):
+    """hqq_group with the codes of (evaluation, element) pairs in ``flips`` moved to the
+    other rounding neighbour and the stop decision of the evaluations in ``inverts``
+    inverted; also returns the z of every evaluation.  Test infrastructure for showing
+    that a divergent device trajectory left the oracle's at a rounding or error tie."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    g = w.size
+    codes = np.empty(g, np.uint8)
+    trace = np.empty(iters + 1, np.float64)
+    ztr = np.empty(iters + 1, np.float64)
+    n_trace = ctypes.c_int()
+    res = _GroupResult()
+    fe = np.ascontiguousarray([f[0] for f in flips] or [0], dtype=np.int32)
+    fk = np.ascontiguousarray([f[1] for f in flips] or [0], dtype=np.int32)
+    rc = _load().oracle_hqq_group_replay(
+        _ptr(w), g, nbits, float(p), float(beta), float(kappa), int(iters), int(bool(early_stop)),
+        float(p if err_pow is None else err_pow), _ptr(codes), ctypes.byref(res), _ptr(trace),
+        _ptr(ztr), ctypes.byref(n_trace), len(flips), _ptr(fe), _ptr(fk), len(inverts),
+        _ptr(np.ascontiguousarray(list(inverts) or [0], dtype=np.int32)))
+    if rc != 0:
+        raise ValueError("oracle_hqq_group_replay rejected its arguments")
+    n = n_trace.value
+    return GroupResult(codes, res.scale, res.inv_scale, res.zero, res.stop_step, res.err_init,
+                       res.err_best, res.n_eval, trace[:n].copy()), ztr[:n].copy()
 
 
 # ---------------------------------------------------------------- packing ---

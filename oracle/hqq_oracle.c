@@ -22,7 +22,8 @@
  * Readings where the page is silent (each listed in the design notes):
  *   init     min-max: s = (max-min)/qmax, inv_s = qmax/(max-min), z = -min*inv_s
  *            (real-valued z); a constant group takes s = inv_s = 1.
- *   round    round half to even (nearbyint under FE_TONEAREST).
+ *   round    round half to even (nearbyint under FE_TONEAREST), decided on the
+ *            binary32 rounding of the fp64 value w/s + z (the device's precision).
  *   clamp    codes clamped to [0, qmax] after rounding.
  *   shrink   exactly the section-2.1 operator; 0 at x = 0 (where |x|^(p-1)
  *            is undefined for p < 1).
@@ -113,9 +114,16 @@ double oracle_shrink_lp(double x, double beta, double p) {
   return x > 0.0 ? v : -v;
 }
 
-/* Q_{z,s}(W) of section 2 with the inverse scale: clamp(round(w*inv_s + z)). */
+/* Q_{z,s}(W) of section 2 with the inverse scale: clamp(round(w*inv_s + z)).
+ * The pre-round value is formed in fp64 and the integer decision is taken on its
+ * binary32 rounding, the working precision of the device solver, so that both
+ * implementations decide every code in the same precision.  fp64 noise
+ * (~1e-16) is far below a binary32 half-ulp, so an exact mathematical tie such
+ * as the midpoint of min and max is decided half-to-even as in exact
+ * arithmetic. */
 double oracle_quantize_value(double w, double inv_s, double z, int qmax) {
-  double q = nearbyint(w * inv_s + z);
+  double x = (double)(float)(w * inv_s + z);
+  double q = nearbyint(x);
   if (q < 0.0) q = 0.0;
   if (q > (double)qmax) q = (double)qmax;
   return q;
@@ -155,10 +163,21 @@ double oracle_z_update(const double* q, const double* w, const double* we, doubl
 }
 
 /* One group through the whole solver.  `trace` (may be NULL) receives every
- * evaluated error e_0, e_1, ... in order; *n_trace their count. */
-int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, double kappa,
-                     int iters, int early_stop, double err_pow, uint8_t* codes_out,
-                     oracle_group_result_t* res, double* trace, int* n_trace) {
+ * evaluated error e_0, e_1, ... in order and `z_trace` (may be NULL) the z of
+ * each evaluation; *n_trace their count.
+ *
+ * Tie replay (test infrastructure): `n_flip` pairs (flip_eval[i], flip_elem[i])
+ * name evaluations at which one element's code is moved to the other neighbour
+ * of its pre-round value (clamped to [0, qmax]); the `n_invert` evaluations in
+ * invert_eval[] have their stop decision inverted.  With no flips and no
+ * inversions this is the solver as written; the tests use them only to show
+ * that a device result which left the oracle's trajectory did so at a rounding
+ * tie or at a stop test between errors equal to rounding noise. */
+int oracle_hqq_group_replay(const double* w, int g, int nbits, double p, double beta0,
+                            double kappa, int iters, int early_stop, double err_pow,
+                            uint8_t* codes_out, oracle_group_result_t* res, double* trace,
+                            double* z_trace, int* n_trace, int n_flip, const int* flip_eval,
+                            const int* flip_elem, int n_invert, const int* invert_eval) {
   if (g <= 0 || g > ORACLE_MAX_GROUP || nbits < 1 || nbits > 8 || iters < 0) return -1;
   int qmax = (1 << nbits) - 1;
   double q[ORACLE_MAX_GROUP], r[ORACLE_MAX_GROUP], we[ORACLE_MAX_GROUP], best_q[ORACLE_MAX_GROUP];
@@ -171,12 +190,31 @@ int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, 
   for (int t = 0; t <= iters; ++t) {
     /* W_q = Q(W) at the current z; residual r = W - Q^-1(W_q). */
     for (int k = 0; k < g; ++k) q[k] = oracle_quantize_value(w[k], inv_s, z, qmax);
+    for (int f = 0; f < n_flip; ++f) {
+      if (flip_eval[f] != n_eval || flip_elem[f] < 0 || flip_elem[f] >= g) continue;
+      int k = flip_elem[f];
+      double x = (double)(float)(w[k] * inv_s + z);
+      double other = x > q[k] ? q[k] + 1.0 : q[k] - 1.0;
+      if (other >= 0.0 && other <= (double)qmax) q[k] = other;
+    }
     for (int k = 0; k < g; ++k) r[k] = w[k] - s * (q[k] - z);
+    if (err_pow == 0.0) {
+      /* The l0 error counts non-zero residuals: whether a residual is zero is an
+       * integer decision, taken like the code decision on the binary32 pre-round
+       * value (zero when it equals the code).  fp64 would count the rounding
+       * noise of, e.g., the max element, whose residual is exactly 0. */
+      for (int k = 0; k < g; ++k)
+        if ((double)(float)(w[k] * inv_s + z) == q[k]) r[k] = 0.0;
+    }
     double e = oracle_group_error(r, g, err_pow);
     if (trace) trace[n_eval] = e;
+    if (z_trace) z_trace[n_eval] = z;
     ++n_eval;
     if (t == 0) e0 = e;
-    if (early_stop && !(e < best_e)) break; /* error no longer improves */
+    int improves = e < best_e;
+    for (int f = 0; f < n_invert; ++f)
+      if (invert_eval[f] == n_eval - 1 && n_eval > 1) improves = !improves;
+    if (early_stop && !improves) break; /* error no longer improves */
     best_e = e;
     best_z = z;
     t_star = t;
@@ -198,6 +236,13 @@ int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, 
   res->n_eval = n_eval;
   if (n_trace) *n_trace = n_eval;
   return 0;
+}
+
+int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, double kappa,
+                     int iters, int early_stop, double err_pow, uint8_t* codes_out,
+                     oracle_group_result_t* res, double* trace, int* n_trace) {
+  return oracle_hqq_group_replay(w, g, nbits, p, beta0, kappa, iters, early_stop, err_pow,
+                                 codes_out, res, trace, NULL, n_trace, 0, NULL, NULL, 0, NULL);
 }
 
 /* ------------------------------------------------------------------------- */

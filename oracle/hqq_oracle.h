@@ -34,6 +34,12 @@ int oracle_hqq_group(const double* w, int g, int nbits, double p, double beta0, 
                      int iters, int early_stop, double err_pow, uint8_t* codes_out,
                      oracle_group_result_t* res, double* trace, int* n_trace);
 
+int oracle_hqq_group_replay(const double* w, int g, int nbits, double p, double beta0,
+                            double kappa, int iters, int early_stop, double err_pow,
+                            uint8_t* codes_out, oracle_group_result_t* res, double* trace,
+                            double* z_trace, int* n_trace, int n_flip, const int* flip_eval,
+                            const int* flip_elem, int n_invert, const int* invert_eval);
+
 int64_t oracle_packed_bytes(int64_t n, int nbits);
 void oracle_pack_codes(const uint8_t* codes, int64_t n, int nbits, uint8_t* out);
 void oracle_unpack_codes(const uint8_t* packed, int64_t n, int nbits, uint8_t* codes);

@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function that include/hqq.h declares, and
+reject invalid arguments with the documented status before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_weight_quantization_amd as hq
+import bit_weight_quantization_amd.build  # noqa: F401  (hq.build)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hqq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(hqq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hq.LIB_PATH):  # build only when nothing is built
+        hq.build.build()
+    return hq.load_library()
+
+
+def test_header_declares_the_python_symbol_list():
+    assert _declared_functions() == sorted(hq.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", hq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(hqq_\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_size_helpers(lib):
+    assert hq.hqq_packed_bytes(4096, 4096, 4) == 4096 * 4096 // 2
+    assert hq.hqq_packed_bytes(11008, 4096, 3) == 11008 * 4096 * 3 // 8
+    assert hq.hqq_packed_bytes(10, 16, 2) == 40
+    assert hq.hqq_packed_bytes(10, 16, 8) == 160
+    assert hq.hqq_packed_bytes(0, 0, 4) == 0
+    assert hq.hqq_packed_bytes(-1, 16, 4) == -1
+    assert hq.hqq_packed_bytes(4, 16, 5) == -1
+    assert hq.hqq_packed_bytes(1 << 40, 1 << 40, 4) == -1  # overflow
+    assert hq.hqq_num_groups(4096, 4096, 64) == 4096 * 64
+    assert hq.hqq_num_groups(3, 96, 32) == 9
+    assert hq.hqq_num_groups(3, 100, 32) == -1
+    assert hq.hqq_num_groups(3, 96, 48) == -1
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert hq.hqq_status_string(st)
+    assert hq.hqq_status_string(0) == "ok"
+    assert hq.hqq_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20  # a 1 MiB-aligned fake device address: never dereferenced, validation fails first
+
+
+def _q(**kw):
+    a = dict(W_f16=FAKE, rows=16, cols=128, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01,
+             iters=20, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, stream=0)
+    a.update(kw)
+    return hq.hqq_quantize(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nbits=5), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(nbits=1), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(group_size=48), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(group_size=256), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(cols=100), hq.HQQ_ERR_INVALID_ARG),
+    (dict(rows=-1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(p=1.5), hq.HQQ_ERR_INVALID_ARG),
+    (dict(p=-0.1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(p=float("nan")), hq.HQQ_ERR_INVALID_ARG),
+    (dict(beta=0.0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(beta=float("inf")), hq.HQQ_ERR_INVALID_ARG),
+    (dict(kappa=-1.0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(iters=-1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(iters=256), hq.HQQ_ERR_INVALID_ARG),
+    (dict(W_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(packed_codes=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(scale_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(W_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+    (dict(packed_codes=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    (dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+    (dict(zero_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_quantize_rejects_before_launch(lib, kw, status):
+    assert _q(**kw) == status
+
+
+def test_empty_matrix_is_a_no_op(lib):
+    assert _q(rows=0, W_f16=0, packed_codes=0, scale_f16=0, zero_f16=0) == hq.HQQ_OK
+    assert _q(rows=5, cols=0, W_f16=0, packed_codes=0, scale_f16=0, zero_f16=0) == hq.HQQ_OK
+    assert hq.hqq_dequantize(0, 0, 0, 0, 64, 4, 64, 0, 0) == hq.HQQ_OK
+
+
+def test_quantize_ex_option_validation(lib):
+    opt = hq.hqq_options_t(2, 0, 0, 0, 0, 0)
+    assert hq.hqq_quantize_ex(FAKE, 16, 128, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE, opt,
+                              0) == hq.HQQ_ERR_INVALID_ARG
+    opt = hq.hqq_options_t(1, FAKE + 2, 0, 0, 0, 0)
+    assert hq.hqq_quantize_ex(FAKE, 16, 128, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE, opt,
+                              0) == hq.HQQ_ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, FAKE, 16, 128, 6, 64, FAKE), hq.HQQ_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, 16, 100, 4, 64, FAKE), hq.HQQ_ERR_INVALID_ARG),
+    ((0, FAKE, FAKE, 16, 128, 4, 64, FAKE), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, 16, 128, 4, 64, 0), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, 16, 128, 4, 64, FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
+    ((FAKE + 1, FAKE, FAKE, 16, 128, 4, 64, FAKE), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_dequantize_rejects_before_launch(lib, args, status):
+    assert hq.hqq_dequantize(*args, 0) == status
+
+
+def test_library_does_not_link_the_oracle(lib):
+    out = subprocess.run(["nm", "-D", hq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "oracle_" not in out
+    deps = subprocess.run(["ldd", hq.LIB_PATH], capture_output=True, text=True).stdout
+    assert "hqq_oracle" not in deps

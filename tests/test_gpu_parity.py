@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs are seeded synthetic matrices with the shapes and distributions of the
+workload table in ``workloads``; both sides read the same fp16 bits.  Small
+matrices are compared in full; full-size matrices of the 7B/70B stacks are
+quantized whole (the call the benchmark times) and compared on sampled rows,
+which the oracle computes on its own (rows are independent).  Tolerances are in
+``tests/parity.py``.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hq():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    import bit_weight_quantization_amd as m
+    m.load_library()
+    return m
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def _run(hq, W, nbits, g, **kw):
+    q = hq.quantize(W, nbits, g, debug=True, **kw)
+    torch.cuda.synchronize()
+    return q
+
+
+def _check_full(hq, W, nbits, g, p=0.7, beta=1.0, kappa=1.01, iters=20, early_stop=True,
+                **floors):
+    q = _run(hq, W, nbits, g, p=p, beta=beta, kappa=kappa, iters=iters, early_stop=early_stop)
+    dev = parity.from_quantized(q)
+    W16 = W.cpu().numpy().view(np.uint16)
+    rep = parity.compare(W16, dev, nbits, g, p=p, beta=beta, kappa=kappa, iters=iters,
+                         early_stop=early_stop, **floors)
+    _say(f"  {rep}")
+    return q, rep
+
+
+def _sample_rows(rows, seed, n=62):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, rows - 1), size=min(n, rows - 2), replace=False)
+    return np.unique(np.concatenate([[0, rows - 1], mid]))
+
+
+def _check_sampled(hq, W, nbits, g, seed, **kw):
+    """Quantize the whole matrix on the GPU, compare sampled rows against the oracle."""
+    q = _run(hq, W, nbits, g, **kw)
+    rows, cols = W.shape
+    idx = _sample_rows(rows, seed)
+    it = torch.as_tensor(idx, device=W.device)
+    ngr = cols // g
+    bytes_per_row = cols * nbits // 8
+    packed = q.packed.view(rows, bytes_per_row)[it].cpu().numpy().ravel()
+    dev = parity.DeviceResult(
+        packed=packed, scale16=q.scale[it].cpu().numpy().view(np.uint16),
+        zero16=q.zero[it].cpu().numpy().view(np.uint16), scale32=q.scale_f32[it].cpu().numpy(),
+        zero32=q.zero_f32[it].cpu().numpy(), stop=q.stop_step[it].cpu().numpy(),
+        err_init=q.err_init[it].cpu().numpy(), err_best=q.err_best[it].cpu().numpy())
+    assert dev.scale16.shape == (len(idx), ngr)
+    W16 = W[it].cpu().numpy().view(np.uint16)
+    rep = parity.compare(W16, dev, nbits, g, **kw)
+    _say(f"  sampled {len(idx)} rows: {rep}")
+    return rep
+
+
+# ------------------------------------------------------------- workloads --
+
+def test_single_256x512_full(hq):
+    wl = workloads.WORKLOADS["single_256x512"]
+    _say("single_256x512 b4 g64 seed 1")
+    W = workloads.generate_matrix(wl, 0, "cuda")
+    _check_full(hq, W, 4, 64)
+
+
+def test_attn_4096x4096_full(hq):
+    wl = workloads.WORKLOADS["attn_4096x4096"]
+    _say("attn_4096x4096 b4 g64 seed 2")
+    W = workloads.generate_matrix(wl, 0, "cuda")
+    _check_full(hq, W, 4, 64)
+
+
+@pytest.mark.parametrize("nbits,g", [(2, 16), (2, 32)])
+def test_mlp_11008x4096(hq, nbits, g):
+    wl = workloads.WORKLOADS["mlp_11008x4096"]
+    _say(f"mlp 11008x4096 (full) and 4096x11008 (sampled) b{nbits} g{g} seeds 3, 4")
+    W = workloads.generate_matrix(wl, 0, "cuda")
+    _check_full(hq, W, nbits, g)
+    W = workloads.generate_matrix(wl, 1, "cuda")
+    _check_sampled(hq, W, nbits, g, seed=4)
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (3, 64)])
+def test_llama7b_stack_sampled(hq, nbits, g):
+    wl = workloads.WORKLOADS["llama7b_stack"]
+    for m in (0, 4, 6, 7 * 31 + 5):  # 4096x4096, 11008x4096, 4096x11008 (layer 0), 11008x4096 (layer 31)
+        mat = wl.matrices[m]
+        _say(f"llama7b matrix {m} {mat.rows}x{mat.cols} seed {mat.seed} b{nbits} g{g}")
+        W = workloads.generate_matrix(wl, m, "cuda")
+        _check_sampled(hq, W, nbits, g, seed=mat.seed)
+
+
+@pytest.mark.parametrize("nbits,g", [(2, 32), (4, 64)])
+def test_llama70b_stack_sampled(hq, nbits, g):
+    wl = workloads.WORKLOADS["llama70b_stack"]
+    for m in (0, 2, 4, 6, 7 * 79 + 4):  # 8192^2, 1024x8192, 28672x8192, 8192x28672, last layer
+        mat = wl.matrices[m]
+        _say(f"llama70b matrix {m} {mat.rows}x{mat.cols} seed {mat.seed} b{nbits} g{g}")
+        W = workloads.generate_matrix(wl, m, "cuda")
+        _check_sampled(hq, W, nbits, g, seed=mat.seed)
+        del W
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------- branches and extremes --
+
+def _c1(device="cuda"):
+    return workloads.generate_matrix(workloads.WORKLOADS["single_256x512"], 0, device)
+
+
+@pytest.mark.parametrize("nbits,g", [(8, 64), (3, 64), (4, 128), (4, 16), (8, 128), (3, 16)])
+def test_bits_and_group_sizes(hq, nbits, g):
+    _say(f"single_256x512 b{nbits} g{g}")
+    _check_full(hq, _c1(), nbits, g)
+
+
+def test_active_shrink_large_beta(hq):
+    _say("single_256x512 beta=1e4 (shrink active)")
+    _check_full(hq, _c1(), 4, 64, beta=1e4)
+    _check_full(hq, _c1(), 2, 32, beta=3e3, kappa=1.1)
+
+
+def test_scaled_weights(hq):
+    _say("single_256x512 x50 (shrink active near outliers)")
+    W = (_c1().float() * 50).half()
+    _check_full(hq, W, 4, 64)
+    _check_full(hq, W, 2, 16)
+
+
+@pytest.mark.parametrize("p", [1.0, 0.0, 0.5])
+def test_other_p(hq, p):
+    """p = 1 (l1, soft-threshold shrink) and p = 0 (l0) are the ends of the range the page
+    allows.  The l1 error is piecewise linear in z: runs of exactly equal errors make the
+    stop test a coin toss between fp32 and fp64, so p = 1 only needs 75% of the groups on
+    the oracle's exact trajectory, and every other group explained as a tie."""
+    _say(f"single_256x512 p={p}")
+    floors = dict(min_agree=0.75, min_code_agree=0.999) if p == 1.0 else {}
+    _check_full(hq, _c1(), 4, 64, p=p, **floors)
+    _check_full(hq, _c1(), 2, 32, p=p, beta=1e3, **floors)
+
+
+def test_no_early_stop_and_zero_iters(hq):
+    _say("single_256x512 early_stop=0 T=20; T=0; T=255")
+    _check_full(hq, _c1(), 4, 64, early_stop=False)
+    _check_full(hq, _c1(), 4, 64, iters=0)
+    _check_full(hq, _c1(), 3, 32, iters=255)
+
+
+def test_ragged_shapes(hq):
+    """Group counts that fill no whole wavefront or queue; one row; one group."""
+    dist = workloads.WORKLOADS["attn_4096x4096"].dist
+    for rows, cols, nbits, g, seed in [(37, 96, 4, 32, 11), (1, 16, 2, 16, 12), (3, 128, 3, 128, 13),
+                                       (1001, 80, 4, 16, 14), (5, 4224, 8, 64, 15),
+                                       (2049, 64, 2, 64, 16)]:
+        _say(f"ragged {rows}x{cols} b{nbits} g{g} seed {seed}")
+        W = workloads.generate(rows, cols, dist, seed, "cuda")
+        _check_full(hq, W, nbits, g)
+
+
+def test_constant_same_sign_and_grid_groups(hq):
+    _say("constant / same-sign / on-grid groups")
+    rng = np.random.default_rng(0)
+    rows, cols = 64, 256
+    W = np.empty((rows, cols), np.float16)
+    W[:16] = np.repeat(rng.standard_normal((16, 4)) * 0.02, 64, axis=1)            # constant groups
+    W[16:32] = np.abs(rng.standard_normal((16, cols)) * 0.02) + 0.01               # all positive
+    W[32:48] = -np.abs(rng.standard_normal((16, cols)) * 0.02) - 0.01              # all negative
+    k = rng.integers(0, 16, (16, cols)).astype(np.float64)
+    k[:, ::64] = 0
+    k[:, 1::64] = 15
+    W[48:] = (0.5 * (k - 3.0)).astype(np.float16)                                 # on a code grid
+    Wt = torch.from_numpy(W).cuda()
+    q, _ = _check_full(hq, Wt, 4, 64)
+    ref = oracle.hqq_quantize(W, 4, 64)
+    codes = oracle.unpack_codes(q.packed.cpu().numpy(), rows * cols, 4).reshape(rows, cols)
+    assert np.array_equal(codes[:16], ref.codes[:16]) and (codes[:16] == 0).all()
+    assert np.array_equal(codes[48:], ref.codes[48:])
+    assert (q.stop_step[48:].cpu().numpy() == 0).all()
+
+
+def test_exact_ties_round_half_even(hq):
+    """s = 1 and integer z: every w/s + z is exact in fp32 and fp64, ties are real ties."""
+    _say("tie-engineered groups")
+    rng = np.random.default_rng(1)
+    rows, cols = 32, 64
+    v = rng.integers(0, 7, (rows, cols)).astype(np.float64) / 2.0  # multiples of 1/2 in [0, 3]
+    v[:, ::16] = 0.0
+    v[:, 1::16] = 3.0  # min 0, max 3 -> s = 1, z = 0 for 2-bit groups of 16
+    W = torch.from_numpy(v.astype(np.float16)).cuda()
+    q = _run(hq, W, 2, 16, iters=0)
+    ref = oracle.hqq_quantize(v.astype(np.float16), 2, 16, iters=0)
+    codes = oracle.unpack_codes(q.packed.cpu().numpy(), rows * cols, 2).reshape(rows, cols)
+    assert np.array_equal(codes, ref.codes)
+
+
+def test_hand_examples_are_exact_on_gpu(hq):
+    """The worked examples of the oracle pins, duplicated to a group of 16, in dyadic arithmetic."""
+    _say("hand examples")
+    w8 = np.array([0.0] + [0.25] * 6 + [3.0])
+    W = torch.from_numpy(np.tile(w8, 2)[None, :].astype(np.float16)).cuda()
+    q = _run(hq, W, 2, 16, p=0.7)
+    assert q.stop_step.item() == 1 and q.zero_f32.item() == -0.1875
+    q = _run(hq, W, 2, 16, p=1.0, beta=8.0, kappa=2.0, iters=3)
+    assert q.stop_step.item() == 3 and q.zero_f32.item() == -0.140625
+    assert abs(q.err_best.item() - 2 * 0.9375) <= 1e-6
+    codes = oracle.unpack_codes(q.packed.cpu().numpy(), 16, 2)
+    assert codes.tolist() == ([0] * 7 + [3]) * 2
+
+
+# ------------------------------------------------------- dequant and API --
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (3, 64), (2, 16), (2, 32), (8, 128)])
+def test_dequantize_is_single_rounding(hq, nbits, g):
+    _say(f"dequant b{nbits} g{g}")
+    W = workloads.generate(512, 1024, workloads.WORKLOADS["mlp_11008x4096"].dist, 21, "cuda")
+    q = hq.quantize(W, nbits, g)
+    Wd = hq.dequantize(q)
+    torch.cuda.synchronize()
+    ref = oracle.hqq_dequantize(q.packed.cpu().numpy(), q.scale.cpu().numpy(),
+                                q.zero.cpu().numpy(), 512, 1024, nbits, g)
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint16), ref)
+
+
+def test_plain_entry_point_equals_debug_entry_point_and_is_deterministic(hq):
+    _say("hqq_quantize vs hqq_quantize_ex, repeatability, side stream")
+    W = workloads.generate_matrix(workloads.WORKLOADS["attn_4096x4096"], 0, "cuda")
+    a = hq.quantize(W, 4, 64)
+    b = hq.quantize(W, 4, 64, debug=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = hq.quantize(W, 4, 64, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    for x, y in ((a, b), (a, c)):
+        assert torch.equal(x.packed, y.packed)
+        assert torch.equal(x.scale.view(torch.int16), y.scale.view(torch.int16))
+        assert torch.equal(x.zero.view(torch.int16), y.zero.view(torch.int16))
+    # rows are independent: a block of rows gives the bit-identical result
+    top = hq.quantize(W[:100].contiguous(), 4, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(top.packed, a.packed[: 100 * 2048])
+    assert torch.equal(top.zero.view(torch.int16), a.zero[:100].view(torch.int16))
+
+
+def test_empty_input(hq):
+    W = torch.empty((0, 64), dtype=torch.float16, device="cuda")
+    q = hq.quantize(W, 4, 64)
+    assert q.packed.numel() == 0 and q.scale.numel() == 0

@@ -25,13 +25,14 @@ MUTANTS = {
     "init z sign": ("*z = -mn * (*inv_s);", "*z = mn * (*inv_s);"),
     "min-max skips last element": ("for (int k = 1; k < g; ++k) {\n    if (w[k] < mn)",
                                    "for (int k = 1; k < g - 1; ++k) {\n    if (w[k] < mn)"),
-    "stop only on strict increase": ("!(e < best_e)", "(e > best_e)"),
-    "return the rejected z": ("if (early_stop && !(e < best_e)) break;",
-                              "if (early_stop && !(e < best_e)) { best_z = z; "
+    "stop only on strict increase": ("int improves = e < best_e;", "int improves = e <= best_e;"),
+    "return the rejected z": ("if (early_stop && !improves) break;",
+                              "if (early_stop && !improves) { best_z = z; "
                               "for (int k = 0; k < g; ++k) best_q[k] = q[k]; break; }"),
     "stop step off by one": ("t_star = t;", "t_star = t > 0 ? t - 1 : 0;"),
     "beta never updated": ("beta = kappa * beta;", "beta = beta;"),
-    "round half away from zero": ("nearbyint(w * inv_s + z)", "round(w * inv_s + z)"),
+    "round half away from zero": ("double q = nearbyint(x);", "double q = round(x);"),
+    "decision in fp64": ("double x = (double)(float)(w * inv_s + z);", "double x = w * inv_s + z;"),
     "no upper clamp": ("if (q > (double)qmax) q = (double)qmax;", ""),
     "error of squared residual": ("pow(fabs(r[k]), err_pow)", "pow(r[k] * r[k], err_pow)"),
     "pack MSB first": ("out[bit >> 3] |= (uint8_t)(1u << (bit & 7));",
