@@ -1,0 +1,317 @@
+"""Throughput of group-wise HQQ quantization on one MI355X.
+
+One step quantizes every matrix of a synthetic Llama-2-70B-shaped stack (80
+layers x {2x 8192x8192, 2x 1024x8192, 2x 28672x8192, 1x 8192x28672}, 68.45 G
+fp16 weights, Student-t nu=4, std 0.015, resident in HBM) once with 2-bit /
+group 32 and once with 4-bit / group 64 (p = 0.7, beta = 1, kappa = 1.01, 20
+iterations, per-group early stop: the settings of section 4.1 of the HQQ page),
+through the C ABI, on one stream.  Inputs are generated on the device before the
+timed region; outputs are written to HBM.
+
+Prints one JSON line (stdout).  The roofline object describes the solver kernel:
+it is bound by VALU issue, so `achieved` counts the algorithmic VALU lane-ops of
+the groups processed (from the measured stop-step histogram) per second of
+kernel time.  `cpu_baseline` is the fp64 oracle on a bounded row sample, timed
+on one host core.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weights quantized/sec (G/s) + % of binding VALU/HBM roofline, 1 MI355X"
+PROFILE_PMC = os.path.join(ROOT, "profiles", "hqq_solve_llama70b_pmc.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", "hqq_kernels.hip")
+
+# MI355X: 256 CUs x 4 SIMDs x 16 fp32 lanes per clock x 2.4 GHz.  Packed-fp32 issue is
+# not used, so this is the VALU ceiling for the solver; v_log_f32 / v_exp_f32 issue at
+# half rate and are counted as 2 lane-ops each (measured on the device).
+PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+PEAK_HBM = 8.0e12
+
+# Algorithmic VALU lane-ops per weight (general 0 < p < 1):
+#   init   4: fp16->fp32, min, max, w/s + z
+#   eval  10: x = w/s + z, round, clamp, residual, log2 (2), *p, exp2 (2), error sum
+#   update 1: code sum for the z mean (no shrink: every |r| is below its threshold)
+#   final  4: x, round, clamp, pack
+OPS_INIT, OPS_EVAL, OPS_UPDATE, OPS_FINAL = 4, 10, 1, 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(launches_per_step: int):
+    """HBM bytes per solver launch from the committed rocprofv3 PMC summary, or None if
+    absent or taken on a different kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    with open(PROFILE_PMC) as f:
+        prof = json.load(f)
+    if prof.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if prof.get("launches_per_step") != launches_per_step:
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama70b_stack")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="use only the first L layers (for profiling runs); 0 = all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 4 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the quantizer has no multi-GPU path "
+              "(every group is independent; a stack shards by whole matrices).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import bit_weight_quantization_amd as hq
+
+    if not torch.cuda.is_available():
+        log("no ROCm device available")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        n = 4 << 30
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        return
+
+    lib = hq.load_library()
+    wl = workloads.WORKLOADS[args.workload]
+    solver = wl.solver
+    mats = list(wl.matrices)
+    if args.layers:  # the Llama stacks hold 7 matrices per layer
+        mats = mats[: 7 * args.layers]
+    n_weights = sum(m.rows * m.cols for m in mats)
+    settings = list(wl.settings)
+
+    # ---- inputs, resident in HBM -------------------------------------------------
+    t0 = time.time()
+    Ws = []
+    for i, m in enumerate(mats):
+        Ws.append(workloads.generate(m.rows, m.cols, wl.dist, m.seed, dev))
+        if i % 70 == 0:
+            log(f"generated {i + 1}/{len(mats)} matrices ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    log(f"inputs: {len(mats)} matrices, {n_weights / 1e9:.2f} G weights, "
+        f"{2 * n_weights / 1e9:.1f} GB, generated in {time.time() - t0:.1f}s")
+
+    # ---- outputs: one buffer set sized for the largest setting, reused ------------
+    max_packed = max(n_weights * b // 8 for b, g in settings)
+    max_groups = max(n_weights // g for b, g in settings)
+    packed = torch.empty(max_packed, dtype=torch.uint8, device=dev)
+    scale = torch.empty(max_groups, dtype=torch.float16, device=dev)
+    zero = torch.empty(max_groups, dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = int(stream.cuda_stream)
+
+    calls = []  # (setting index, args for hqq_quantize)
+    for si, (nb, g) in enumerate(settings):
+        off_p = off_g = 0
+        for W in Ws:
+            r, c = W.shape
+            calls.append((si, (W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
+                               solver.iters, packed.data_ptr() + off_p,
+                               scale.data_ptr() + 2 * off_g, zero.data_ptr() + 2 * off_g, sh)))
+            off_p += r * c * nb // 8
+            off_g += r * c // g
+    launches_per_step = len(calls)
+
+    def step(events=None):
+        cur = -1
+        for si, a in calls:
+            if events is not None and si != cur:
+                events[si][0].record(stream)
+                if cur >= 0:
+                    events[cur][1].record(stream)
+                cur = si
+            st = lib.hqq_quantize(*a)
+            if st != 0:
+                raise RuntimeError(f"hqq_quantize failed: {hq.hqq_status_string(st)}")
+        if events is not None:
+            events[cur][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region ------------------------------------------------------------
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per_setting_ms = [0.0] * len(settings)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    log(f"timed {args.steps} steps: {total_ms:.1f} ms (events), {wall * 1e3:.1f} ms (wall)")
+
+    # per-setting split (one extra step with events between the settings; not in `value`)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in settings]
+    step(evs)
+    torch.cuda.synchronize()
+    per_setting_ms = [a.elapsed_time(b) for a, b in evs]
+
+    weights_per_step = n_weights * len(settings)
+    value = weights_per_step * args.steps / (total_ms * 1e-3) / 1e9
+
+    # ---- stop-step histogram (separate, untimed pass) --------------------------------
+    hist = []
+    for si, (nb, g) in enumerate(settings):
+        h = torch.zeros(256, dtype=torch.int64, device=dev)
+        stop = torch.empty(max(W.numel() for W in Ws) // g, dtype=torch.uint8, device=dev)
+        opts = hq.hqq_options_t(1, 0, 0, stop.data_ptr(), 0, 0)
+        for W in Ws:
+            r, c = W.shape
+            ngr = r * c // g
+            st = hq.hqq_quantize_ex(W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
+                                    solver.iters, packed.data_ptr(), scale.data_ptr(),
+                                    zero.data_ptr(), opts, sh)
+            assert st == 0
+            h += torch.bincount(stop[:ngr].to(torch.int64), minlength=256)
+        hist.append(h.cpu().numpy())
+    torch.cuda.synchronize()
+
+    def op_count(h, g):
+        t = np.arange(256)
+        n_eval = np.where(t == solver.iters, solver.iters + 1, t + 2)
+        n_upd = n_eval - 1
+        groups = h.sum()
+        ops = g * np.sum(h * (OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval + OPS_UPDATE * n_upd))
+        return float(ops), float(np.sum(h * n_eval) / groups)
+
+    ops_step = 0.0
+    detail = []
+    for si, (nb, g) in enumerate(settings):
+        ops, mean_eval = op_count(hist[si], g)
+        ops_step += ops
+        bytes_alg = n_weights * (2 + nb / 8 + 4 / g)
+        detail.append({
+            "setting": f"b{nb}g{g}", "ms": round(per_setting_ms[si], 3),
+            "G_weights_per_s": round(n_weights / (per_setting_ms[si] * 1e-3) / 1e9, 1),
+            "mean_evals_per_group": round(mean_eval, 4),
+            "stop_step_hist": [int(x) for x in hist[si][: solver.iters + 1]],
+            "valu_TOPs": round(ops / (per_setting_ms[si] * 1e-3) / 1e12, 2),
+            "valu_frac": round(ops / (per_setting_ms[si] * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+            "hbm_GBs_algorithmic": round(bytes_alg / (per_setting_ms[si] * 1e-3) / 1e9, 1),
+        })
+    avg_launch_s = total_ms * 1e-3 / (args.steps * launches_per_step)
+    achieved = ops_step / launches_per_step / avg_launch_s  # lane-ops/s
+    bytes_step = sum(n_weights * (2 + nb / 8 + 4 / g) for nb, g in settings)
+    traffic = traffic_from_profile(launches_per_step)
+
+    # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle._load()
+        done_w = 0
+        t_cpu = 0.0
+        sample = []
+        budget = args.cpu_seconds
+        layer0 = mats[:7] if len(mats) >= 7 else mats
+        rows_each = 16
+        while t_cpu < budget:
+            progressed = False
+            for si, (nb, g) in enumerate(settings):
+                for mi, W in enumerate(Ws[: len(layer0)]):
+                    r0 = (len(sample) * 7919) % (W.shape[0] - rows_each)
+                    host = W[r0: r0 + rows_each].cpu().numpy().view(np.uint16)
+                    t1 = time.process_time()
+                    oracle.hqq_quantize(host, nb, g, p=solver.p, beta=solver.beta,
+                                        kappa=solver.kappa, iters=solver.iters)
+                    t_cpu += time.process_time() - t1
+                    done_w += host.size
+                    sample.append((si, mi, r0))
+                    progressed = True
+                    if t_cpu >= budget:
+                        break
+                if t_cpu >= budget:
+                    break
+            if not progressed:
+                break
+        cpu = {"value": round(done_w / t_cpu / 1e9, 6), "unit": "G weights/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{len(sample)} blocks of {rows_each} consecutive rows from the 7 matrices "
+                         f"of layer 0, both settings alternating, {done_w / 1e6:.1f} M weights, "
+                         f"{t_cpu:.1f} s CPU (process time) on one thread of the host"}
+        log(f"cpu baseline: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "G weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Student-t nu=4, std 0.015, generated on the device)",
+        "config": {
+            "workload": args.workload + (f"[first {args.layers} layers]" if args.layers else ""),
+            "matrices": len(mats), "weights_per_setting": n_weights,
+            "settings": [f"b{nb}g{g}" for nb, g in settings],
+            "p": solver.p, "beta": solver.beta, "kappa": solver.kappa, "iters": solver.iters,
+            "early_stop": "per group", "launches_per_step": launches_per_step,
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved / 1e12, 3),
+            "peak": round(PEAK_VALU_LANE_OPS / 1e12, 3),
+            "unit": "TOP/s",
+            "frac": round(achieved / PEAK_VALU_LANE_OPS, 4),
+            "traffic": traffic,
+            "kernel": "hqq_solve_kernel<32|64, general p>",
+            "ops_per_launch": round(ops_step / launches_per_step),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "hbm_frac_algorithmic": round(bytes_step / (ms_per_step * 1e-3) / PEAK_HBM, 4),
+        },
+        "per_setting": detail,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
