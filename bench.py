@@ -64,9 +64,81 @@ def traffic_from_profile(launches_per_step: int):
         prof = json.load(f)
     if prof.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    if prof.get("launches_per_step") != launches_per_step:
+    if prof.get("workload") != "llama70b_stack":
         return None
-    return prof.get("hbm_bytes_per_launch")
+    # the profiled layers repeat the per-layer shapes of the full stack, so the average
+    # bytes per launch carry over to every launch of a full step
+    return round(prof["hbm_bytes_per_launch"])
+
+
+def _kernel_key(name: str):
+    for g in (16, 32, 64, 128):
+        if f"hqq_solve_kernel<{g}," in name:
+            return f"hqq_solve_kernel<{g}>"
+    if "hqq_dequant_kernel" in name:
+        return "hqq_dequant_kernel"
+    if "rocclr_copyBuffer" in name:  # the runtime's device-to-device copy (tensor.copy_)
+        return "plain_copy"
+    return None
+
+
+def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, layers: int):
+    """Write the committed rocprofv3 summaries: per-kernel trace statistics and HBM traffic
+    per solver launch (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, each scaled by what the
+    same counter reads for a plain device copy of known size)."""
+    import collections
+    import csv
+
+    def counters(path):
+        acc = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            k = _kernel_key(r["Kernel_Name"])
+            if k:
+                acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch = counters(os.path.join(pmc_dir, "fetch", "run_counter_collection.csv"))
+    write = counters(os.path.join(pmc_dir, "write", "run_counter_collection.csv"))
+    cf = counters(os.path.join(pmc_dir, "copy_fetch", "run_counter_collection.csv"))
+    cw = counters(os.path.join(pmc_dir, "copy_write", "run_counter_collection.csv"))
+    copy_bytes = 4 << 30
+    f_fac = copy_bytes / (cf["plain_copy"]["FETCH_SIZE"][0] * 1024)
+    w_fac = copy_bytes / (cw["plain_copy"]["WRITE_SIZE"][0] * 1024)
+    solve = [k for k in fetch if k.startswith("hqq_solve")]
+    n = sum(len(fetch[k]["FETCH_SIZE"]) for k in solve)
+    rd = sum(sum(fetch[k]["FETCH_SIZE"]) for k in solve) * 1024 * f_fac / n
+    wr = sum(sum(write[k]["WRITE_SIZE"]) for k in solve) * 1024 * w_fac / n
+    sq = counters(os.path.join(pmc_dir, "sq", "run_counter_collection.csv"))
+    extra = {}
+    for k in solve:
+        c = {name: sum(v) / len(v) for name, v in sq[k].items()}
+        if c:
+            extra[k] = {
+                "valu_wave_instr_per_launch": c.get("SQ_INSTS_VALU"),
+                "trans_wave_instr_per_launch": c.get("SQ_INSTS_VALU_TRANS_F32"),
+                "active_lane_fraction": c.get("SQ_THREAD_CYCLES_VALU", 0) / max(
+                    64 * c.get("SQ_ACTIVE_INST_VALU", 1), 1),
+                "waves": c.get("SQ_WAVES")}
+    stats = {}
+    kt_csv = os.path.join(kt_dir, "kt_kernel_stats.csv")
+    for r in csv.DictReader(open(kt_csv)):
+        k = _kernel_key(r["Name"])
+        if k:
+            stats[k] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                        "total_ms": float(r["TotalDurationNs"]) / 1e6}
+    summary = {
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "workload": "llama70b_stack", "layers_profiled": layers,
+        "fetch_calibration": f_fac, "write_calibration": w_fac,
+        "solver_launches_profiled": n,
+        "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+        "hbm_bytes_per_launch": rd + wr,
+        "sq": extra, "kernel_stats": stats, "command": command,
+    }
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_solve_llama70b_pmc.json"), "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary, indent=1))
 
 
 def main():
@@ -81,7 +153,17 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="generate, then run warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
+                    help="write profiles/ summaries from rocprofv3 counter and trace output")
+    ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles[0], args.summarize_profiles[1],
+                           os.path.join(ROOT, "profiles"), args.profile_command, args.layers)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the quantizer has no multi-GPU path "
@@ -182,6 +264,12 @@ def main():
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
     log(f"timed {args.steps} steps: {total_ms:.1f} ms (events), {wall * 1e3:.1f} ms (wall)")
+
+    if args.profile_run:
+        log(json.dumps({"value_G_weights_per_s": round(
+            n_weights * len(settings) * args.steps / (total_ms * 1e-3) / 1e9, 3),
+            "launches_per_step": launches_per_step}))
+        return
 
     # per-setting split (one extra step with events between the settings; not in `value`)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -87,10 +87,11 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
       !aligned(zero_f16, 2))
     return HQQ_ERR_ALIGNMENT;
-  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr};
+  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
   if (opt) {
     o = *opt;
     if (o.early_stop != 0 && o.early_stop != 1) return HQQ_ERR_INVALID_ARG;
+    if (o.refill_threshold < 0) return HQQ_ERR_INVALID_ARG;
     if ((o.scale_f32 && !aligned(o.scale_f32, 4)) || (o.zero_f32 && !aligned(o.zero_f32, 4)) ||
         (o.err_init && !aligned(o.err_init, 4)) || (o.err_best && !aligned(o.err_best, 4)))
       return HQQ_ERR_ALIGNMENT;
@@ -112,6 +113,7 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   prm.err_best = o.err_best;
   prm.ngroups = ngroups;
   prm.qmax = (float)((1 << nbits) - 1);
+  prm.inv_qmax = (float)(1.0 / (double)((1 << nbits) - 1));
   prm.p = p;
   prm.pm1 = p - 1.0f;
   prm.pm2 = p - 2.0f;
@@ -123,7 +125,8 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   prm.iters = iters;
   prm.early_stop = o.early_stop;
   prm.nbits = nbits;
-  prm.refill_at = slots / 2 > 0 ? slots / 2 : 1;
+  int refill = o.refill_threshold > 0 ? o.refill_threshold : slots / 2;
+  prm.refill_at = refill < 1 ? 1 : (refill > slots ? slots : refill);
 
   const int power_mode = p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
 

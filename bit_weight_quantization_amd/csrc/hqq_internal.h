@@ -23,6 +23,7 @@ struct SolveParams {
   int64_t ngroups;
   int64_t groups_per_wave; // contiguous queue length of one wavefront
   float qmax;
+  float inv_qmax;          // 1/qmax rounded to fp32
   float p;                 // lp exponent
   float pm1;               // p - 1
   float pm2;               // p - 2

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
 
   // Per-lane copy of the state of the lane's group (identical across the segment).
   float u[kLaneElems];  // w/s + z_0, correctly rounded
-  float s = 1.f, inv_s = 1.f, cs = 1.f;  // cs = s^(p-2)
+  float s = 1.f, inv_s = 1.f;
   float z0 = 0.f, usum = 0.f;            // initial zero point, sum of u over the group
   float delta = 0.f, best_delta = 0.f, best_e = 0.f, e0 = 0.f;
   float inv_beta = 0.f, tau = 0.f;
@@ -203,9 +203,15 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
         const float mn = seg_min<L>(lmn);
         const float mx = seg_max<L>(lmx);
         const float d = mx - mn;
+        // s = d / qmax and 1/s = qmax / d, each correctly rounded: a reciprocal
+        // estimate, then one exact FMA residual step (d, qmax and the residuals
+        // are exact in fp32).
+        const float rcp_d = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
         if (d > 0.f) {
-          s = d / qmax;
-          inv_s = qmax / d;
+          const float s0 = d * P.inv_qmax;
+          s = __builtin_fmaf(__builtin_fmaf(-s0, qmax, d), P.inv_qmax, s0);
+          const float i0 = qmax * rcp_d;
+          inv_s = __builtin_fmaf(__builtin_fmaf(-i0, d, qmax), rcp_d, i0);
         } else {  // constant group: s = 1, every u is 0
           s = 1.f;
           inv_s = 1.f;
@@ -215,7 +221,6 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
         // carried exactly as p + e; r = a*qmax - q0*d is the exact residual of the
         // first quotient q0 = a * (qmax/d), and q0 + r/d is the correctly rounded
         // quotient.  A constant group has a = 0 and rcp_d = 0, hence u = 0.
-        const float rcp_d = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
         float lsum = 0.f;
 #pragma unroll
         for (int k = 0; k < kLaneElems; ++k) {
@@ -236,9 +241,6 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
         t_star = 0;
         inv_beta = P.inv_beta0;
         tau = P.tau0;
-        if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(s));
-        else if constexpr (PM == kPowOne) cs = inv_s;
-        else cs = inv_s * inv_s;
         active = true;
       }
     }
@@ -253,14 +255,15 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
     bool done = false;
     if (active) {
       // ---- evaluation at the current z: codes, residual, lp error --------
-      float e = 0.f, sq = 0.f;
+      float e, sq;
 #pragma unroll
       for (int k = 0; k < kLaneElems; ++k) {
         const float x = u[k] + delta;
         const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
         const float rc = x - q;
-        e += pow_p<PM>(rc, P.p);
-        sq += q;
+        const float a = pow_p<PM>(rc, P.p);
+        e = k == 0 ? a : e + a;
+        sq = k == 0 ? q : sq + q;
       }
       e = seg_sum<L>(e);
       sq = seg_sum<L>(sq);  // exact: a sum of small integers
@@ -279,6 +282,10 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
         const bool need = bound >= tau * inv_s * (1.0f - 1e-4f);
         if (ballot(need) != 0) {
           if (need) {
+            float cs;  // s^(p-2)
+            if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(s));
+            else if constexpr (PM == kPowOne) cs = inv_s;
+            else cs = inv_s * inv_s;
             const float ib = cs * inv_beta;  // s^(p-2) / beta_t
             float acc = 0.f;
 #pragma unroll
