@@ -33,11 +33,6 @@ int compute_units() {
   return cus;
 }
 
-// Wavefronts resident per SIMD that the solver grid aims for, and how many
-// groups one wavefront's queue holds at least (a multiple of its slot count).
-constexpr int kSolveWavesPerSimd = 8;
-constexpr int kSimdsPerCu = 4;
-
 int validate_common(int64_t rows, int64_t cols, int nbits, int group_size) {
   if (checked_elems(rows, cols) < 0) return HQQ_ERR_INVALID_ARG;
   if (!supported_nbits(nbits) || !supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
@@ -118,30 +113,24 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   prm.pm1 = p - 1.0f;
   prm.pm2 = p - 2.0f;
   prm.inv_beta0 = (float)(1.0 / (double)beta);
-  prm.inv_kappa = (float)(1.0 / (double)kappa);
   // The shrink of section 2.1 vanishes for |x|^(2-p) <= 1/beta, i.e. |x| <= beta^(-1/(2-p)).
-  prm.tau0 = (float)pow((double)beta, -1.0 / (2.0 - (double)p));
-  prm.rho = (float)pow((double)kappa, -1.0 / (2.0 - (double)p));
+  const double tau0 = pow((double)beta, -1.0 / (2.0 - (double)p));
+  const double log2_rho = -log2((double)kappa) / (2.0 - (double)p);
+  prm.tau0 = (float)tau0;
+  prm.log2_rho = (float)log2_rho;
+  prm.log2_kappa = (float)log2((double)kappa);
+  prm.tau_min = (float)(log2_rho < 0.0 ? tau0 * exp2(log2_rho * iters) : tau0);
   prm.iters = iters;
   prm.early_stop = o.early_stop;
   prm.nbits = nbits;
-  int refill = o.refill_threshold > 0 ? o.refill_threshold : slots / 2;
+  int refill = o.refill_threshold > 0 ? o.refill_threshold : 1;
   prm.refill_at = refill < 1 ? 1 : (refill > slots ? slots : refill);
 
   const int power_mode = p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
 
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;
-  const int64_t target_waves = (int64_t)cus * kSimdsPerCu * kSolveWavesPerSimd;
-  int64_t per_wave = (ngroups + target_waves - 1) / target_waves;
-  if (per_wave < slots) per_wave = slots;
-  per_wave = (per_wave + slots - 1) / slots * slots;
-  const int64_t nwaves = (ngroups + per_wave - 1) / per_wave;
-  const int64_t waves_per_block = hqq::kBlock / hqq::kWave;
-  const int64_t blocks = (nwaves + waves_per_block - 1) / waves_per_block;
-  prm.groups_per_wave = per_wave;
-
-  hipError_t err = hqq::launch_solve(prm, group_size, power_mode, (int)blocks,
+  hipError_t err = hqq::launch_solve(prm, group_size, power_mode, cus,
                                      static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }

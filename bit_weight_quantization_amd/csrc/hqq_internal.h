@@ -21,20 +21,21 @@ struct SolveParams {
   float* err_init;
   float* err_best;
   int64_t ngroups;
-  int64_t groups_per_wave; // contiguous queue length of one wavefront
+  int64_t groups_per_wave; // contiguous queue length of one wavefront (set by the launcher)
   float qmax;
   float inv_qmax;          // 1/qmax rounded to fp32
   float p;                 // lp exponent
   float pm1;               // p - 1
   float pm2;               // p - 2
   float inv_beta0;         // 1 / beta_0
-  float inv_kappa;         // 1 / kappa
   float tau0;              // beta_0^(-1/(2-p)): the shrink is zero for |r| <= tau
-  float rho;               // kappa^(-1/(2-p)): tau_{t+1} = rho * tau_t
+  float log2_rho;          // log2 kappa^(-1/(2-p)): tau_t = tau0 * 2^(t log2_rho)
+  float log2_kappa;        // 1/beta_t = (1/beta_0) * 2^(-t log2_kappa)
+  float tau_min;           // smallest tau_t over the run
   int iters;
   int early_stop;
   int nbits;
-  int refill_at;           // refill idle group slots once this many are idle
+  int refill_at;           // hand stopped groups over once this many segments are stopped
 };
 
 struct DequantParams {
@@ -48,7 +49,7 @@ struct DequantParams {
 };
 
 // Launchers (return a hipError_t of the launch).
-hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int blocks,
+hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream);
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
 

@@ -34,12 +34,14 @@
 //     and u = qmax), so a per-group bound decides (with a 1e-4 relative margin
 //     that keeps the result bit-identical to evaluating the shrink) whether the
 //     wave evaluates it;
-//   * groups stop at different steps.  A segment whose group has stopped writes
-//     its outputs and becomes idle; once `refill_at` segments of the wave are
-//     idle they take the next groups of the wave's contiguous queue, so a wave
-//     does not wait for its slowest group.  Every group is computed by exactly
-//     the same instruction sequence whatever its slot, so results do not depend
-//     on the schedule.
+//   * groups stop at different steps.  Each wavefront owns an LDS standby pool of
+//     S initialized groups and a done ring of 2S stopped groups.  A segment whose
+//     group stopped copies its u values and header into the done ring and takes a
+//     standby group in the same pass (a few LDS instructions), so lanes stay busy;
+//     standby groups are initialized, and done groups packed and written, in dense
+//     batches of S in which every lane works.  Every group is computed by exactly
+//     the same instruction sequence whatever its slot, so results do not depend on
+//     the schedule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -153,227 +155,414 @@ __device__ __forceinline__ float scalar_pow(float x, float p) {
 
 // ------------------------------------------------------------------ solver --
 
+// Group scalars fixed at load.
+struct GroupInit {
+  float s, inv_s, z0, usum;
+  bool may_shrink;  // the shrink can be non-zero at some step (|r| <= max - min always)
+};
+
+// The lane's 16-byte chunk of group `gi` (zero past the end of the wave's queue).
+template <int L>
+__device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, int64_t gi, int64_t g_end,
+                                             int sl) {
+  return gi < g_end ? P.W[gi * L + sl] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// From the lane's 8 raw binary16 weights, compute its u values and the group scalars.
+// Called by all L lanes of a segment together (segment-wide DPP reductions).
+template <int L>
+__device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint4& raw,
+                                                float (&u)[kLaneElems]) {
+  const float qmax = P.qmax;
+  float w[kLaneElems];
+  load8(raw, w);
+  float lmn = w[0], lmx = w[0];
+#pragma unroll
+  for (int k = 1; k < kLaneElems; ++k) {
+    lmn = __builtin_fminf(lmn, w[k]);
+    lmx = __builtin_fmaxf(lmx, w[k]);
+  }
+  const float mn = seg_min<L>(lmn);
+  const float mx = seg_max<L>(lmx);
+  const float d = mx - mn;
+  GroupInit g;
+  // s = d / qmax and 1/s = qmax / d, each correctly rounded: a reciprocal estimate,
+  // then one exact FMA residual step (d, qmax and the residuals are exact in fp32).
+  const float rcp_d = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
+  if (d > 0.f) {
+    const float s0 = d * P.inv_qmax;
+    g.s = __builtin_fmaf(__builtin_fmaf(-s0, qmax, d), P.inv_qmax, s0);
+    const float i0 = qmax * rcp_d;
+    g.inv_s = __builtin_fmaf(__builtin_fmaf(-i0, d, qmax), rcp_d, i0);
+  } else {  // constant group: s = 1, every u is 0
+    g.s = 1.f;
+    g.inv_s = 1.f;
+  }
+  // u = (w - mn) * qmax / d rounded once: a = w - mn is exact for the binary16
+  // inputs of a group (barring extreme exponent spans); a*qmax is carried exactly
+  // as p + e; r = a*qmax - q0*d is the exact residual of the first quotient
+  // q0 = a * (qmax/d), and q0 + r/d is the correctly rounded quotient.  A constant
+  // group has a = 0 and rcp_d = 0, hence u = 0.
+  float lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    const float a = w[k] - mn;
+    const float q0 = a * g.inv_s;
+    const float p = a * qmax;
+    const float e = __builtin_fmaf(a, qmax, -p);
+    const float r = __builtin_fmaf(-q0, d, p) + e;
+    u[k] = __builtin_fmaf(r, rcp_d, q0);
+    lsum += u[k];
+  }
+  g.usum = seg_sum<L>(lsum);
+  g.z0 = -(mn * g.inv_s);
+  // Without shrink every code lies in [0, qmax], so |z - z0| <= qmax and every
+  // |r| = s|x - W_q| <= s * max(0.5, qmax) = d: the shrink stays zero if d is below
+  // the smallest threshold beta_t^(-1/(2-p)) of the run (1e-4 relative margin).
+  g.may_shrink = d >= P.tau_min * (1.0f - 1e-4f);
+  return g;
+}
+
+// Orders this wave's LDS accesses: lanes hand group state to other lanes of the same
+// wavefront through LDS (the standby pool and the done ring below).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Per-wavefront LDS: slots [0, S) are the standby pool (initialized groups waiting for
+// a free segment), slots [S, 3S) the done ring (stopped groups waiting to be written).
+// A slot holds the G code-unit values u of a group and an 8-word header.
+template <int G>
+struct SolveLds {
+  static constexpr int S = kWave * kLaneElems / G;
+  static constexpr int kSlots = 3 * S;
+  float u[kWavesPerBlock][kSlots][G];
+  uint32_t hdr[kWavesPerBlock][kSlots][8];
+};
+
+// Header words.  Standby: gidx lo/hi, s, 1/s, z0, sum u, may_shrink.  Done: gidx
+// lo/hi, s, z0, best delta, e0, best e, t*.
+
+
+// Values every lane of the wave computes identically, kept in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+template <int G>
+__device__ __forceinline__ void store_u(float* slot_u, int sl, const float (&u)[kLaneElems]) {
+  float4* dst = reinterpret_cast<float4*>(slot_u + sl * kLaneElems);
+  dst[0] = make_float4(u[0], u[1], u[2], u[3]);
+  dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+}
+
+template <int G>
+__device__ __forceinline__ void load_u(const float* slot_u, int sl, float (&u)[kLaneElems]) {
+  const float4* src = reinterpret_cast<const float4*>(slot_u + sl * kLaneElems);
+  const float4 a = src[0], b = src[1];
+  u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
+  u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+}
+
+// One evaluation of the lane's 8 weights at x = u + delta: the segment's lp error
+// (code units) and code sum.  CLAMP = false is the exact shortcut for |delta| < 1/2.
+template <int L, int PM, bool CLAMP>
+__device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float delta, float qmax,
+                                           float p, float& e, float& sq) {
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    const float x = u[k] + delta;
+    float q = __builtin_rintf(x);
+    if constexpr (CLAMP) q = __builtin_amdgcn_fmed3f(q, 0.f, qmax);
+    const float rc = x - q;
+    const float a = pow_p<PM>(rc, p);
+    e = k == 0 ? a : e + a;
+    sq = k == 0 ? q : sq + q;
+  }
+  e = seg_sum<L>(e);
+  sq = seg_sum<L>(sq);  // exact: a sum of small integers
+}
+
 template <int G, int PM>
 __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
-  constexpr int S = kWave / L;       // groups per wavefront
+  constexpr int S = kWave / L;       // group slots (segments) per wavefront
+  constexpr int kDone = 2 * S;       // done-ring capacity
   constexpr float kInvG = 1.0f / (float)G;
+  __shared__ SolveLds<G> lds;
 
+  const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
+  const int seg = lane / L;
   const int sl = lane & (L - 1);
   const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
   const int64_t g_begin = wave * P.groups_per_wave;
   const int64_t g_end = g_begin + P.groups_per_wave < P.ngroups ? g_begin + P.groups_per_wave
                                                                 : P.ngroups;
-  if (g_begin >= g_end) return;  // wave-uniform
+  if (g_begin >= g_end) return;  // wave-uniform; the kernel has no block-wide barrier
 
+  float (*U)[G] = lds.u[wid];
+  uint32_t (*H)[8] = lds.hdr[wid];
   const float qmax = P.qmax;
 
-  // Per-lane copy of the state of the lane's group (identical across the segment).
-  float u[kLaneElems];  // w/s + z_0, correctly rounded
-  float s = 1.f, inv_s = 1.f;
-  float z0 = 0.f, usum = 0.f;            // initial zero point, sum of u over the group
+  // State of the group in this lane's segment (identical across the segment).
+  float u[kLaneElems];
+  float s = 1.f, inv_s = 1.f, z0 = 0.f, usum = 0.f;
   float delta = 0.f, best_delta = 0.f, best_e = 0.f, e0 = 0.f;
-  float inv_beta = 0.f, tau = 0.f;
   int t = 0, t_star = 0;
   int64_t gidx = 0;
-  bool active = false;
+  bool may_shrink = false;
+  bool active = false;   // iterating
+  bool pending = false;  // stopped, state not yet handed to the done ring
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) u[k] = 0.f;
 
-  int64_t next = g_begin;  // wave-uniform: next unassigned group of this wave
+  // Wave-uniform bookkeeping.
+  int64_t next = g_begin;  // next group of the wave's queue
+  int n_standby = 0;       // standby slots [0, n_standby) hold groups
+  int done_head = 0, done_count = 0;
 
-  // Hand the next groups of the queue to the idle segments, in lane order.
-  auto refill = [&]() {
-    const uint64_t idle = ballot(!active);
-    const int rank = lanes_below(idle) / L;  // idle segments below this one
-    const int nidle = __builtin_popcountll(idle) / L;
-    if (!active) {
-      const int64_t gi = next + rank;
-      if (gi < g_end) {
-        gidx = gi;
-        float w[kLaneElems];
-        load8(P.W[gi * L + sl], w);
-        float lmn = w[0], lmx = w[0];
-#pragma unroll
-        for (int k = 1; k < kLaneElems; ++k) {
-          lmn = __builtin_fminf(lmn, w[k]);
-          lmx = __builtin_fmaxf(lmx, w[k]);
-        }
-        const float mn = seg_min<L>(lmn);
-        const float mx = seg_max<L>(lmx);
-        const float d = mx - mn;
-        // s = d / qmax and 1/s = qmax / d, each correctly rounded: a reciprocal
-        // estimate, then one exact FMA residual step (d, qmax and the residuals
-        // are exact in fp32).
-        const float rcp_d = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
-        if (d > 0.f) {
-          const float s0 = d * P.inv_qmax;
-          s = __builtin_fmaf(__builtin_fmaf(-s0, qmax, d), P.inv_qmax, s0);
-          const float i0 = qmax * rcp_d;
-          inv_s = __builtin_fmaf(__builtin_fmaf(-i0, d, qmax), rcp_d, i0);
-        } else {  // constant group: s = 1, every u is 0
-          s = 1.f;
-          inv_s = 1.f;
-        }
-        // u = (w - mn) * qmax / d rounded once: a = w - mn is exact for the
-        // binary16 inputs of a group (barring extreme exponent spans); a*qmax is
-        // carried exactly as p + e; r = a*qmax - q0*d is the exact residual of the
-        // first quotient q0 = a * (qmax/d), and q0 + r/d is the correctly rounded
-        // quotient.  A constant group has a = 0 and rcp_d = 0, hence u = 0.
-        float lsum = 0.f;
-#pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) {
-          const float a = w[k] - mn;
-          const float q0 = a * inv_s;
-          const float p = a * qmax;
-          const float e = __builtin_fmaf(a, qmax, -p);
-          const float r = __builtin_fmaf(-q0, d, p) + e;
-          u[k] = __builtin_fmaf(r, rcp_d, q0);
-          lsum += u[k];
-        }
-        usum = seg_sum<L>(lsum);
-        z0 = -(mn * inv_s);
-        delta = 0.f;
-        best_delta = 0.f;
-        best_e = __builtin_inff();
-        t = 0;
-        t_star = 0;
-        inv_beta = P.inv_beta0;
-        tau = P.tau0;
-        active = true;
-      }
-    }
-    next += nidle;
+  auto begin_iterating = [&](const GroupInit& gq) {
+    s = gq.s;
+    inv_s = gq.inv_s;
+    z0 = gq.z0;
+    usum = gq.usum;
+    delta = 0.f;
+    best_delta = 0.f;
+    may_shrink = gq.may_shrink;
+    best_e = __builtin_inff();
+    t = 0;
+    t_star = 0;
+    active = true;
   };
 
-  refill();
+  // The weights of the next standby batch are fetched one batch ahead, so the
+  // HBM latency overlaps the iterations in between.
+  uint4 prefetch = make_uint4(0u, 0u, 0u, 0u);
 
-  while (true) {
-    const uint64_t act = ballot(active);
-    if (act == 0) break;  // queue drained and every group written
-    bool done = false;
-    if (active) {
-      // ---- evaluation at the current z: codes, residual, lp error --------
-      float e, sq;
+  // Dense batch: segment j initializes group next + j into standby slot j.
+  auto fill_standby = [&]() {
+    const int64_t avail = g_end - next;
+    const int n = avail < S ? (int)avail : S;
+    if (seg < n) {
+      float uu[kLaneElems];
+      const int64_t gi = next + seg;
+      const GroupInit gq = init_group<L>(P, prefetch, uu);
+      store_u<G>(U[seg], sl, uu);
+      if (sl == 0) {
+        uint4* h = reinterpret_cast<uint4*>(H[seg]);
+        h[0] = make_uint4((uint32_t)gi, (uint32_t)(gi >> 32), fbits(gq.s), fbits(gq.inv_s));
+        h[1] = make_uint4(fbits(gq.z0), fbits(gq.usum), gq.may_shrink ? 1u : 0u, 0u);
+      }
+    }
+    n_standby = uniform(n);
+    next = uniform64(next + n);
+    prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
+    wave_lds_sync();
+  };
+
+  // Segments with `want` set take standby groups, highest slot first.
+  auto take_standby = [&](bool want) {
+    const uint64_t m = ballot(want);
+    const int rank = lanes_below(m) / L;
+    const int cnt = __builtin_popcountll(m) / L;
+    if (want && rank < n_standby) {
+      const int slot = n_standby - 1 - rank;
+      load_u<G>(U[slot], sl, u);
+      const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
+      const uint4 h0 = h[0], h1 = h[1];
+      gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
+      GroupInit gq;
+      gq.s = bitsf(h0.z);
+      gq.inv_s = bitsf(h0.w);
+      gq.z0 = bitsf(h1.x);
+      gq.usum = bitsf(h1.y);
+      gq.may_shrink = h1.z != 0u;
+      begin_iterating(gq);
+    }
+    n_standby = uniform(n_standby - (cnt < n_standby ? cnt : n_standby));
+    wave_lds_sync();
+  };
+
+  // Dense batch: segment j writes the codes and meta of done slot head + j.
+  auto finalize = [&](int n) {
+    if (seg < n) {
+      const int slot = S + ((unsigned)(done_head + seg) & (kDone - 1));
+      float uu[kLaneElems];
+      load_u<G>(U[slot], sl, uu);
+      const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
+      const uint4 h0 = h[0], h1 = h[1];
+      const int64_t gi = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
+      const float bd = bitsf(h1.x);
+      uint32_t c[kLaneElems];
 #pragma unroll
       for (int k = 0; k < kLaneElems; ++k) {
-        const float x = u[k] + delta;
-        const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-        const float rc = x - q;
-        const float a = pow_p<PM>(rc, P.p);
-        e = k == 0 ? a : e + a;
-        sq = k == 0 ? q : sq + q;
+        const float x = uu[k] + bd;
+        c[k] = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
       }
-      e = seg_sum<L>(e);
-      sq = seg_sum<L>(sq);  // exact: a sum of small integers
-      if (t == 0) e0 = e;
+      const int64_t chunk = gi * L + sl;  // index of this lane's 8 elements
+      switch (P.nbits) {
+        case 4: {
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (4 * k);
+          reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
+          break;
+        }
+        case 2: {
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (2 * k);
+          reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)v;
+          break;
+        }
+        case 8: {
+          uint2 v;
+          v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+          v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+          reinterpret_cast<uint2*>(P.packed)[chunk] = v;
+          break;
+        }
+        default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
+          uint32_t v = 0;
+#pragma unroll
+          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (3 * k);
+          uint8_t* dst = P.packed + chunk * 3;
+          dst[0] = (uint8_t)v;
+          dst[1] = (uint8_t)(v >> 8);
+          dst[2] = (uint8_t)(v >> 16);
+          break;
+        }
+      }
+      if (sl == 0) {
+        const float gs = bitsf(h0.z);
+        const float best_z = bitsf(h0.w) + bd;
+        P.scale16[gi] = float_to_half_bits(gs);
+        P.zero16[gi] = float_to_half_bits(best_z);
+        if (P.scale32) P.scale32[gi] = gs;
+        if (P.zero32) P.zero32[gi] = best_z;
+        if (P.stop_step) P.stop_step[gi] = (uint8_t)h1.w;
+        if (P.err_init || P.err_best) {
+          const float sp = scalar_pow<PM>(gs, P.p);
+          if (P.err_init) P.err_init[gi] = bitsf(h1.y) * sp;
+          if (P.err_best) P.err_best[gi] = bitsf(h1.z) * sp;
+        }
+      }
+    }
+    done_head = uniform((int)((unsigned)(done_head + n) & (kDone - 1)));
+    done_count = uniform(done_count - n);
+    wave_lds_sync();
+  };
+
+  // First groups go straight to the segments, the next ones to the standby pool.
+  {
+    const int64_t avail = g_end - next;
+    const int n = avail < S ? (int)avail : S;
+    prefetch = fetch_chunk<L>(P, next + S + seg, g_end, sl);
+    if (seg < n) {
+      gidx = next + seg;
+      begin_iterating(init_group<L>(P, fetch_chunk<L>(P, gidx, g_end, sl), u));
+    }
+    next = uniform64(next + n);
+  }
+  if (next < g_end) fill_standby();
+
+  while (true) {
+    if (ballot(active || pending) == 0) break;
+    // Clamping is a no-op while every |delta| < 1/2: u lies in [0, qmax], so
+    // x = u + delta stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
+    const bool clamp = ballot(active && !(__builtin_fabsf(delta) < 0.4999f)) != 0;
+    if (active) {
+      // ---- evaluation at the current z: codes, residual, lp error ----------
+      float e, sq;
+      if (clamp) {
+        eval_group<L, PM, true>(u, delta, qmax, P.p, e, sq);
+      } else {
+        eval_group<L, PM, false>(u, delta, qmax, P.p, e, sq);
+      }
+      if (P.err_init && t == 0) e0 = e;
       const bool accept = !P.early_stop || (e < best_e);
       if (accept) {
         best_e = e;
         best_delta = delta;
         t_star = t;
       }
-      done = !accept || t == P.iters;
-      if (!done) {
+      if (!accept || t == P.iters) {
+        active = false;
+        pending = true;
+      } else {
         // ---- sp1 shrink (only where it can be non-zero) + sp2 mean ---------
         float num = sq - usum;
-        const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(delta)) + 1e-5f * (qmax + 1.f);
-        const bool need = bound >= tau * inv_s * (1.0f - 1e-4f);
-        if (ballot(need) != 0) {
-          if (need) {
-            float cs;  // s^(p-2)
-            if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(s));
-            else if constexpr (PM == kPowOne) cs = inv_s;
-            else cs = inv_s * inv_s;
-            const float ib = cs * inv_beta;  // s^(p-2) / beta_t
-            float acc = 0.f;
+        if (ballot(may_shrink) != 0) {
+          // beta_t^(-1/(2-p)) and 1/beta_t, from t
+          const float tf = (float)t;
+          const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
+          const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(delta)) + 1e-5f * (qmax + 1.f);
+          const bool need = may_shrink && bound >= tau * inv_s * (1.0f - 1e-4f);
+          if (ballot(need) != 0) {
+            if (need) {
+              float cs;  // s^(p-2)
+              if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(s));
+              else if constexpr (PM == kPowOne) cs = inv_s;
+              else cs = inv_s * inv_s;
+              const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
+              const float ib = cs * inv_beta;  // s^(p-2) / beta_t
+              float acc = 0.f;
 #pragma unroll
-            for (int k = 0; k < kLaneElems; ++k) {
-              const float x = u[k] + delta;
-              const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-              const float rc = x - q;
-              const float a = __builtin_fabsf(rc);
-              float m = 0.f;
-              if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
-              acc += __builtin_copysignf(m, rc);  // W_e / s
+              for (int k = 0; k < kLaneElems; ++k) {
+                const float x = u[k] + delta;
+                const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
+                const float rc = x - q;
+                const float a = __builtin_fabsf(rc);
+                float m = 0.f;
+                if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
+                acc += __builtin_copysignf(m, rc);  // W_e / s
+              }
+              num += seg_sum<L>(acc);
             }
-            num += seg_sum<L>(acc);
           }
         }
         delta = num * kInvG;
-        inv_beta *= P.inv_kappa;
-        tau *= P.rho;
         ++t;
       }
     }
 
-    // ---- groups that stopped: final codes, packing, meta ---------------------
-    if (ballot(active && done) != 0) {
-      if (active && done) {
-        uint32_t c[kLaneElems];
-#pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) {
-          const float x = u[k] + best_delta;
-          c[k] = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-        }
-        const int64_t chunk = gidx * L + sl;  // index of this lane's 8 elements
-        switch (P.nbits) {
-          case 4: {
-            uint32_t v = 0;
-#pragma unroll
-            for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (4 * k);
-            reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
-            break;
-          }
-          case 2: {
-            uint32_t v = 0;
-#pragma unroll
-            for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (2 * k);
-            reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)v;
-            break;
-          }
-          case 8: {
-            uint2 v;
-            v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-            v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-            reinterpret_cast<uint2*>(P.packed)[chunk] = v;
-            break;
-          }
-          default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
-            uint32_t v = 0;
-#pragma unroll
-            for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (3 * k);
-            uint8_t* dst = P.packed + chunk * 3;
-            dst[0] = (uint8_t)v;
-            dst[1] = (uint8_t)(v >> 8);
-            dst[2] = (uint8_t)(v >> 16);
-            break;
-          }
-        }
+    // ---- stopped groups: hand them to the done ring, take standby groups -------
+    const uint64_t pm = ballot(pending);
+    const int npend = __builtin_popcountll(pm) / L;
+    if (npend > 0 && (npend >= P.refill_at || ballot(active) == 0)) {
+      const int rank = lanes_below(pm) / L;
+      if (pending) {
+        const int slot = S + ((unsigned)(done_head + done_count + rank) & (kDone - 1));
+        store_u<G>(U[slot], sl, u);
         if (sl == 0) {
-          const float best_z = z0 + best_delta;
-          P.scale16[gidx] = float_to_half_bits(s);
-          P.zero16[gidx] = float_to_half_bits(best_z);
-          if (P.scale32) P.scale32[gidx] = s;
-          if (P.zero32) P.zero32[gidx] = best_z;
-          if (P.stop_step) P.stop_step[gidx] = (uint8_t)t_star;
-          if (P.err_init || P.err_best) {
-            const float sp = scalar_pow<PM>(s, P.p);
-            if (P.err_init) P.err_init[gidx] = e0 * sp;
-            if (P.err_best) P.err_best[gidx] = best_e * sp;
-          }
+          uint4* h = reinterpret_cast<uint4*>(H[slot]);
+          h[0] = make_uint4((uint32_t)gidx, (uint32_t)(gidx >> 32), fbits(s), fbits(z0));
+          h[1] = make_uint4(fbits(best_delta), fbits(e0), fbits(best_e), (uint32_t)t_star);
         }
-        active = false;
       }
+      done_count = uniform(done_count + npend);
+      wave_lds_sync();
+      const bool want = pending;
+      pending = false;
+      take_standby(want);
     }
-
-    // ---- refill idle slots from the wave's queue -----------------------------
-    if (next < g_end) {
-      const int nidle = S - __builtin_popcountll(ballot(active)) / L;
-      if (nidle >= P.refill_at) refill();
+    if (done_count >= S) finalize(S);
+    if (n_standby == 0 && next < g_end) {
+      fill_standby();
+      if (ballot(!active && !pending) != 0) take_standby(!active && !pending);
     }
   }
+  while (done_count > 0) finalize(done_count < S ? done_count : S);
 }
 
 // ---------------------------------------------------------------- dequant --
@@ -448,32 +637,44 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
   }
 }
 
-template <int G>
-hipError_t launch_solve_g(const SolveParams& prm, int power_mode, int blocks, hipStream_t st) {
-  switch (power_mode) {
-    case kPowOne:
-      hipLaunchKernelGGL((hqq_solve_kernel<G, kPowOne>), dim3(blocks), dim3(kBlock), 0, st, prm);
-      break;
-    case kPowZero:
-      hipLaunchKernelGGL((hqq_solve_kernel<G, kPowZero>), dim3(blocks), dim3(kBlock), 0, st, prm);
-      break;
-    default:
-      hipLaunchKernelGGL((hqq_solve_kernel<G, kPowGeneral>), dim3(blocks), dim3(kBlock), 0, st,
-                         prm);
-      break;
-  }
+// Persistent grid: as many blocks as can be resident at once (LDS and VGPRs set the
+// limit), each wavefront owning one contiguous queue of groups.
+template <int G, int PM>
+hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
+  auto kernel = hqq_solve_kernel<G, PM>;
+  int per_cu = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) per_cu = 1;
+  constexpr int S = kWave * kLaneElems / G;
+  const int64_t resident_waves = (int64_t)cus * per_cu * (kBlock / kWave);
+  int64_t per_wave = (prm.ngroups + resident_waves - 1) / resident_waves;
+  if (per_wave < S) per_wave = S;
+  const int64_t nwaves = (prm.ngroups + per_wave - 1) / per_wave;
+  const int64_t blocks = (nwaves + kBlock / kWave - 1) / (kBlock / kWave);
+  prm.groups_per_wave = per_wave;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, prm);
   return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_solve_g(const SolveParams& prm, int power_mode, int cus, hipStream_t st) {
+  switch (power_mode) {
+    case kPowOne: return launch_solve_gp<G, kPowOne>(prm, cus, st);
+    case kPowZero: return launch_solve_gp<G, kPowZero>(prm, cus, st);
+    default: return launch_solve_gp<G, kPowGeneral>(prm, cus, st);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int blocks,
+hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream) {
   switch (group_size) {
-    case 16: return launch_solve_g<16>(prm, power_mode, blocks, stream);
-    case 32: return launch_solve_g<32>(prm, power_mode, blocks, stream);
-    case 64: return launch_solve_g<64>(prm, power_mode, blocks, stream);
-    case 128: return launch_solve_g<128>(prm, power_mode, blocks, stream);
+    case 16: return launch_solve_g<16>(prm, power_mode, cus, stream);
+    case 32: return launch_solve_g<32>(prm, power_mode, cus, stream);
+    case 64: return launch_solve_g<64>(prm, power_mode, cus, stream);
+    case 128: return launch_solve_g<128>(prm, power_mode, cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
