@@ -232,13 +232,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int kWavesPerBlock = kBlock / kWave;
 
+// Groups iterated concurrently by one segment of lanes.
+#ifndef HQQ_SLOTS_PER_SEGMENT
+#define HQQ_SLOTS_PER_SEGMENT 1
+#endif
+constexpr int kSlotsPerSegment = HQQ_SLOTS_PER_SEGMENT;
+
 // Per-wavefront LDS: slots [0, S) are the standby pool (initialized groups waiting for
 // a free segment), slots [S, 3S) the done ring (stopped groups waiting to be written).
 // A slot holds the G code-unit values u of a group and an 8-word header.
 template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
-  static constexpr int kSlots = 3 * S;
+  static constexpr int kSlots = S + S + S / 2;
   float u[kWavesPerBlock][kSlots][G];
   uint32_t hdr[kWavesPerBlock][kSlots][8];
 };
@@ -292,11 +298,25 @@ __device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float d
   sq = seg_sum<L>(sq);  // exact: a sum of small integers
 }
 
-template <int G, int PM>
+// State of one group held by a segment (identical in all L lanes of the segment).
+struct Slot {
+  float u[kLaneElems];  // this lane's code-unit values
+  float s, inv_s, z0, usum;
+  float delta, best_delta, best_e, e0;
+  int t, t_star;
+  int64_t gidx;
+  bool may_shrink;
+  bool active;   // iterating
+  bool pending;  // stopped, not yet handed to the done ring
+};
+
+// Each segment iterates NS independent groups ("slots"), so the per-iteration
+// bookkeeping and the hand-over passes are shared by NS groups.
+template <int G, int PM, int NS>
 __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
-  constexpr int S = kWave / L;       // group slots (segments) per wavefront
-  constexpr int kDone = 2 * S;       // done-ring capacity
+  constexpr int S = kWave / L;       // segments per wavefront
+  constexpr int kDone = S + S / 2;   // done-ring capacity
   constexpr float kInvG = 1.0f / (float)G;
   __shared__ SolveLds<G> lds;
 
@@ -314,35 +334,35 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
   uint32_t (*H)[8] = lds.hdr[wid];
   const float qmax = P.qmax;
 
-  // State of the group in this lane's segment (identical across the segment).
-  float u[kLaneElems];
-  float s = 1.f, inv_s = 1.f, z0 = 0.f, usum = 0.f;
-  float delta = 0.f, best_delta = 0.f, best_e = 0.f, e0 = 0.f;
-  int t = 0, t_star = 0;
-  int64_t gidx = 0;
-  bool may_shrink = false;
-  bool active = false;   // iterating
-  bool pending = false;  // stopped, state not yet handed to the done ring
+  Slot sg[NS];
 #pragma unroll
-  for (int k = 0; k < kLaneElems; ++k) u[k] = 0.f;
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int k = 0; k < kLaneElems; ++k) sg[j].u[k] = 0.f;
+    sg[j].s = sg[j].inv_s = 1.f;
+    sg[j].z0 = sg[j].usum = sg[j].delta = sg[j].best_delta = sg[j].best_e = sg[j].e0 = 0.f;
+    sg[j].t = sg[j].t_star = 0;
+    sg[j].gidx = 0;
+    sg[j].may_shrink = sg[j].active = sg[j].pending = false;
+  }
 
   // Wave-uniform bookkeeping.
   int64_t next = g_begin;  // next group of the wave's queue
   int n_standby = 0;       // standby slots [0, n_standby) hold groups
   int done_head = 0, done_count = 0;
 
-  auto begin_iterating = [&](const GroupInit& gq) {
-    s = gq.s;
-    inv_s = gq.inv_s;
-    z0 = gq.z0;
-    usum = gq.usum;
-    delta = 0.f;
-    best_delta = 0.f;
-    may_shrink = gq.may_shrink;
-    best_e = __builtin_inff();
-    t = 0;
-    t_star = 0;
-    active = true;
+  auto begin_iterating = [&](Slot& q, const GroupInit& gq) {
+    q.s = gq.s;
+    q.inv_s = gq.inv_s;
+    q.z0 = gq.z0;
+    q.usum = gq.usum;
+    q.delta = 0.f;
+    q.best_delta = 0.f;
+    q.may_shrink = gq.may_shrink;
+    q.best_e = __builtin_inff();
+    q.t = 0;
+    q.t_star = 0;
+    q.active = true;
   };
 
   // The weights of the next standby batch are fetched one batch ahead, so the
@@ -370,33 +390,38 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
     wave_lds_sync();
   };
 
-  // Segments with `want` set take standby groups, highest slot first.
-  auto take_standby = [&](bool want) {
-    const uint64_t m = ballot(want);
-    const int rank = lanes_below(m) / L;
-    const int cnt = __builtin_popcountll(m) / L;
-    if (want && rank < n_standby) {
-      const int slot = n_standby - 1 - rank;
-      load_u<G>(U[slot], sl, u);
-      const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
-      const uint4 h0 = h[0], h1 = h[1];
-      gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
-      GroupInit gq;
-      gq.s = bitsf(h0.z);
-      gq.inv_s = bitsf(h0.w);
-      gq.z0 = bitsf(h1.x);
-      gq.usum = bitsf(h1.y);
-      gq.may_shrink = h1.z != 0u;
-      begin_iterating(gq);
+  // Slots with want[j] set take standby groups (slot-major order, highest standby
+  // slot first).
+  auto take_standby = [&](const bool (&want)[NS]) {
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint64_t m = ballot(want[j]);
+      const int rank = base + lanes_below(m) / L;
+      if (want[j] && rank < n_standby) {
+        const int slot = n_standby - 1 - rank;
+        load_u<G>(U[slot], sl, sg[j].u);
+        const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
+        const uint4 h0 = h[0], h1 = h[1];
+        sg[j].gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
+        GroupInit gq;
+        gq.s = bitsf(h0.z);
+        gq.inv_s = bitsf(h0.w);
+        gq.z0 = bitsf(h1.x);
+        gq.usum = bitsf(h1.y);
+        gq.may_shrink = h1.z != 0u;
+        begin_iterating(sg[j], gq);
+      }
+      base += __builtin_popcountll(m) / L;
     }
-    n_standby = uniform(n_standby - (cnt < n_standby ? cnt : n_standby));
+    n_standby = uniform(n_standby - (base < n_standby ? base : n_standby));
     wave_lds_sync();
   };
 
   // Dense batch: segment j writes the codes and meta of done slot head + j.
   auto finalize = [&](int n) {
     if (seg < n) {
-      const int slot = S + ((unsigned)(done_head + seg) & (kDone - 1));
+      const int slot = S + (int)((unsigned)(done_head + seg) % (unsigned)kDone);
       float uu[kLaneElems];
       load_u<G>(U[slot], sl, uu);
       const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
@@ -458,108 +483,148 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
         }
       }
     }
-    done_head = uniform((int)((unsigned)(done_head + n) & (kDone - 1)));
+    done_head = uniform((int)((unsigned)(done_head + n) % (unsigned)kDone));
     done_count = uniform(done_count - n);
     wave_lds_sync();
   };
 
-  // First groups go straight to the segments, the next ones to the standby pool.
-  {
+  // The first NS*S groups go straight to the slots, the next S to the standby pool.
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
     const int64_t avail = g_end - next;
-    const int n = avail < S ? (int)avail : S;
-    prefetch = fetch_chunk<L>(P, next + S + seg, g_end, sl);
+    const int n = avail < S ? (int)(avail > 0 ? avail : 0) : S;
     if (seg < n) {
-      gidx = next + seg;
-      begin_iterating(init_group<L>(P, fetch_chunk<L>(P, gidx, g_end, sl), u));
+      sg[j].gidx = next + seg;
+      begin_iterating(sg[j], init_group<L>(P, fetch_chunk<L>(P, sg[j].gidx, g_end, sl), sg[j].u));
     }
     next = uniform64(next + n);
   }
+  prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
   if (next < g_end) fill_standby();
 
   while (true) {
-    if (ballot(active || pending) == 0) break;
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) any = any || sg[j].active || sg[j].pending;
+    if (ballot(any) == 0) break;
+
     // Clamping is a no-op while every |delta| < 1/2: u lies in [0, qmax], so
     // x = u + delta stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
-    const bool clamp = ballot(active && !(__builtin_fabsf(delta) < 0.4999f)) != 0;
-    if (active) {
-      // ---- evaluation at the current z: codes, residual, lp error ----------
-      float e, sq;
-      if (clamp) {
-        eval_group<L, PM, true>(u, delta, qmax, P.p, e, sq);
-      } else {
-        eval_group<L, PM, false>(u, delta, qmax, P.p, e, sq);
-      }
-      if (P.err_init && t == 0) e0 = e;
-      const bool accept = !P.early_stop || (e < best_e);
-      if (accept) {
-        best_e = e;
-        best_delta = delta;
-        t_star = t;
-      }
-      if (!accept || t == P.iters) {
-        active = false;
-        pending = true;
-      } else {
-        // ---- sp1 shrink (only where it can be non-zero) + sp2 mean ---------
-        float num = sq - usum;
-        if (ballot(may_shrink) != 0) {
-          // beta_t^(-1/(2-p)) and 1/beta_t, from t
-          const float tf = (float)t;
-          const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
-          const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(delta)) + 1e-5f * (qmax + 1.f);
-          const bool need = may_shrink && bound >= tau * inv_s * (1.0f - 1e-4f);
-          if (ballot(need) != 0) {
-            if (need) {
-              float cs;  // s^(p-2)
-              if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(s));
-              else if constexpr (PM == kPowOne) cs = inv_s;
-              else cs = inv_s * inv_s;
-              const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
-              const float ib = cs * inv_beta;  // s^(p-2) / beta_t
-              float acc = 0.f;
+    bool far = false;
 #pragma unroll
-              for (int k = 0; k < kLaneElems; ++k) {
-                const float x = u[k] + delta;
-                const float q = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-                const float rc = x - q;
-                const float a = __builtin_fabsf(rc);
-                float m = 0.f;
-                if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
-                acc += __builtin_copysignf(m, rc);  // W_e / s
+    for (int j = 0; j < NS; ++j) far = far || (sg[j].active && !(__builtin_fabsf(sg[j].delta) < 0.4999f));
+    const bool clamp = ballot(far) != 0;
+
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      Slot& q = sg[j];
+      if (q.active) {
+        // ---- evaluation at the current z: codes, residual, lp error --------
+        float e, sq;
+        if (clamp) {
+          eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
+        } else {
+          eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
+        }
+        if (P.err_init && q.t == 0) q.e0 = e;
+        const bool accept = !P.early_stop || (e < q.best_e);
+        if (accept) {
+          q.best_e = e;
+          q.best_delta = q.delta;
+          q.t_star = q.t;
+        }
+        if (!accept || q.t == P.iters) {
+          q.active = false;
+          q.pending = true;
+        } else {
+          // ---- sp1 shrink (only where it can be non-zero) + sp2 mean -------
+          float num = sq - q.usum;
+          if (ballot(q.may_shrink) != 0) {
+            // beta_t^(-1/(2-p)) and 1/beta_t, from t
+            const float tf = (float)q.t;
+            const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
+            const float bound =
+                __builtin_fmaxf(0.5f, __builtin_fabsf(q.delta)) + 1e-5f * (qmax + 1.f);
+            const bool need = q.may_shrink && bound >= tau * q.inv_s * (1.0f - 1e-4f);
+            if (ballot(need) != 0) {
+              if (need) {
+                float cs;  // s^(p-2)
+                if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
+                else if constexpr (PM == kPowOne) cs = q.inv_s;
+                else cs = q.inv_s * q.inv_s;
+                const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
+                const float ib = cs * inv_beta;  // s^(p-2) / beta_t
+                float acc = 0.f;
+#pragma unroll
+                for (int k = 0; k < kLaneElems; ++k) {
+                  const float x = q.u[k] + q.delta;
+                  const float qc = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
+                  const float rc = x - qc;
+                  const float a = __builtin_fabsf(rc);
+                  float m = 0.f;
+                  if (a > 0.f)
+                    m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
+                  acc += __builtin_copysignf(m, rc);  // W_e / s
+                }
+                num += seg_sum<L>(acc);
               }
-              num += seg_sum<L>(acc);
             }
           }
+          q.delta = num * kInvG;
+          ++q.t;
         }
-        delta = num * kInvG;
-        ++t;
       }
     }
 
     // ---- stopped groups: hand them to the done ring, take standby groups -------
-    const uint64_t pm = ballot(pending);
-    const int npend = __builtin_popcountll(pm) / L;
-    if (npend > 0 && (npend >= P.refill_at || ballot(active) == 0)) {
-      const int rank = lanes_below(pm) / L;
-      if (pending) {
-        const int slot = S + ((unsigned)(done_head + done_count + rank) & (kDone - 1));
-        store_u<G>(U[slot], sl, u);
-        if (sl == 0) {
-          uint4* h = reinterpret_cast<uint4*>(H[slot]);
-          h[0] = make_uint4((uint32_t)gidx, (uint32_t)(gidx >> 32), fbits(s), fbits(z0));
-          h[1] = make_uint4(fbits(best_delta), fbits(e0), fbits(best_e), (uint32_t)t_star);
+    uint64_t pm[NS];
+    int npend = 0;
+    bool any_active = false;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      pm[j] = ballot(sg[j].pending);
+      npend += __builtin_popcountll(pm[j]) / L;
+      any_active = any_active || sg[j].active;
+    }
+    if (npend > 0 && (npend >= P.refill_at || ballot(any_active) == 0)) {
+      if (done_count + npend > kDone) finalize(done_count);  // rare: make room first
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const Slot& q = sg[j];
+        const int rank = base + lanes_below(pm[j]) / L;
+        if (q.pending) {
+          const int slot = S + (int)((unsigned)(done_head + done_count + rank) % (unsigned)kDone);
+          store_u<G>(U[slot], sl, q.u);
+          if (sl == 0) {
+            uint4* h = reinterpret_cast<uint4*>(H[slot]);
+            h[0] = make_uint4((uint32_t)q.gidx, (uint32_t)(q.gidx >> 32), fbits(q.s), fbits(q.z0));
+            h[1] = make_uint4(fbits(q.best_delta), fbits(q.e0), fbits(q.best_e), (uint32_t)q.t_star);
+          }
         }
+        base += __builtin_popcountll(pm[j]) / L;
       }
       done_count = uniform(done_count + npend);
       wave_lds_sync();
-      const bool want = pending;
-      pending = false;
+      bool want[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        want[j] = sg[j].pending;
+        sg[j].pending = false;
+      }
       take_standby(want);
     }
-    if (done_count >= S) finalize(S);
+    while (done_count >= S) finalize(S);
     if (n_standby == 0 && next < g_end) {
       fill_standby();
-      if (ballot(!active && !pending) != 0) take_standby(!active && !pending);
+      bool idle[NS];
+      bool any_idle = false;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        idle[j] = !sg[j].active && !sg[j].pending;
+        any_idle = any_idle || idle[j];
+      }
+      if (ballot(any_idle) != 0) take_standby(idle);
     }
   }
   while (done_count > 0) finalize(done_count < S ? done_count : S);
@@ -641,7 +706,7 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 // limit), each wavefront owning one contiguous queue of groups.
 template <int G, int PM>
 hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
-  auto kernel = hqq_solve_kernel<G, PM>;
+  auto kernel = hqq_solve_kernel<G, PM, kSlotsPerSegment>;
   int per_cu = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
   if (err != hipSuccess) return err;
