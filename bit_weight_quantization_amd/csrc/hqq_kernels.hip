@@ -58,10 +58,16 @@ constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kDppRowHalfMirror = 0x141; // lane i of 8 reads lane 7-i
 constexpr int kDppRowMirror = 0x140;     // lane i of 16 reads lane 15-i
 
+// Every control used here reads a lane of the same row, so no source is out of
+// bounds and bound_ctrl only spares the compiler an initialisation of the old value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
 }
 
 // Butterfly sum over an aligned segment of L lanes; commutativity of IEEE
@@ -72,24 +78,6 @@ __device__ __forceinline__ float seg_sum(float v) {
   if constexpr (L >= 4) v += dpp<kDppQuadSwap2>(v);
   if constexpr (L >= 8) v += dpp<kDppRowHalfMirror>(v);
   if constexpr (L >= 16) v += dpp<kDppRowMirror>(v);
-  return v;
-}
-
-template <int L>
-__device__ __forceinline__ float seg_min(float v) {
-  if constexpr (L >= 2) v = __builtin_fminf(v, dpp<kDppQuadSwap1>(v));
-  if constexpr (L >= 4) v = __builtin_fminf(v, dpp<kDppQuadSwap2>(v));
-  if constexpr (L >= 8) v = __builtin_fminf(v, dpp<kDppRowHalfMirror>(v));
-  if constexpr (L >= 16) v = __builtin_fminf(v, dpp<kDppRowMirror>(v));
-  return v;
-}
-
-template <int L>
-__device__ __forceinline__ float seg_max(float v) {
-  if constexpr (L >= 2) v = __builtin_fmaxf(v, dpp<kDppQuadSwap1>(v));
-  if constexpr (L >= 4) v = __builtin_fmaxf(v, dpp<kDppQuadSwap2>(v));
-  if constexpr (L >= 8) v = __builtin_fmaxf(v, dpp<kDppRowHalfMirror>(v));
-  if constexpr (L >= 16) v = __builtin_fmaxf(v, dpp<kDppRowMirror>(v));
   return v;
 }
 
@@ -104,16 +92,36 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Unpack the 8 fp16 weights of one 16-byte chunk into fp32.
-__device__ __forceinline__ void load8(const uint4& v, float (&w)[kLaneElems]) {
-  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xffffu));
-    _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
-    w[2 * i] = (float)lo;
-    w[2 * i + 1] = (float)hi;
-  }
+// Packed binary16 min/max on two halves at once (v_pk_min_f16 / v_pk_max_f16).
+// Written as instructions because the compiler would otherwise quiet every
+// operand first; inputs are finite weights, so quieting is not needed.
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// Low half: max(-a.lo, -b.lo); high half: max(a.hi, b.hi).
+__device__ __forceinline__ uint32_t pk_max_neglo_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2 neg_lo:[1,1]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// w - m in fp32 for the binary16 in the low (HI = false) or high half of `pair`:
+// one fused operation w*1 + (-m) with a single rounding (v_fma_mix_f32).
+template <bool HI>
+__device__ __forceinline__ float half_minus(uint32_t pair, float m) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(m));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(pair), "v"(m));
+  return r;
 }
 
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
@@ -174,16 +182,19 @@ template <int L>
 __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint4& raw,
                                                 float (&u)[kLaneElems]) {
   const float qmax = P.qmax;
-  float w[kLaneElems];
-  load8(raw, w);
-  float lmn = w[0], lmx = w[0];
-#pragma unroll
-  for (int k = 1; k < kLaneElems; ++k) {
-    lmn = __builtin_fminf(lmn, w[k]);
-    lmx = __builtin_fmaxf(lmx, w[k]);
-  }
-  const float mn = seg_min<L>(lmn);
-  const float mx = seg_max<L>(lmx);
+  // Group min and max on the binary16 values themselves (exact): pairwise packed
+  // min/max over the 4 words, then one word (-min, max) reduced over the segment
+  // with packed max.
+  const uint32_t m = pk_min_f16(pk_min_f16(raw.x, raw.y), pk_min_f16(raw.z, raw.w));
+  const uint32_t M = pk_max_f16(pk_max_f16(raw.x, raw.y), pk_max_f16(raw.z, raw.w));
+  uint32_t v = pk_max_neglo_f16(__builtin_amdgcn_perm(M, m, 0x05040100u),   // (m.lo, M.lo)
+                                __builtin_amdgcn_perm(M, m, 0x07060302u));  // (m.hi, M.hi)
+  if constexpr (L >= 2) v = pk_max_f16(v, dpp_u32<kDppQuadSwap1>(v));
+  if constexpr (L >= 4) v = pk_max_f16(v, dpp_u32<kDppQuadSwap2>(v));
+  if constexpr (L >= 8) v = pk_max_f16(v, dpp_u32<kDppRowHalfMirror>(v));
+  if constexpr (L >= 16) v = pk_max_f16(v, dpp_u32<kDppRowMirror>(v));
+  const float mn = -(float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+  const float mx = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
   const float d = mx - mn;
   GroupInit g;
   // s = d / qmax and 1/s = qmax / d, each correctly rounded: a reciprocal estimate,
@@ -198,21 +209,23 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
     g.s = 1.f;
     g.inv_s = 1.f;
   }
-  // u = (w - mn) * qmax / d rounded once: a = w - mn is exact for the binary16
-  // inputs of a group (barring extreme exponent spans); a*qmax is carried exactly
-  // as p + e; r = a*qmax - q0*d is the exact residual of the first quotient
-  // q0 = a * (qmax/d), and q0 + r/d is the correctly rounded quotient.  A constant
-  // group has a = 0 and rcp_d = 0, hence u = 0.
-  float lsum = 0.f;
+  // u = (w - mn) * qmax / d rounded once.  a = w - mn is exact for the binary16
+  // inputs of a group (barring extreme exponent spans).  qmax/d is carried as the
+  // pair c_hi + c_lo (c_hi = 1/s correctly rounded; c_lo = the exact remainder
+  // qmax - c_hi*d times 1/d), and u = fma(a, c_hi, a*c_lo) adds the small term to
+  // the exact product a*c_hi: before its single rounding the sum is within 2^-46
+  // relative of the exact quotient, so u is exact whenever the quotient is
+  // representable (a rounding tie of the initial quantizer stays a tie) and
+  // correctly rounded otherwise except within 2^-46 of a rounding midpoint.  A
+  // constant group has a = 0, hence u = 0.
+  const float c_lo = __builtin_fmaf(-g.inv_s, d, qmax) * rcp_d;
+  const uint32_t pair[4] = {raw.x, raw.y, raw.z, raw.w};
+  float lsum;
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
-    const float a = w[k] - mn;
-    const float q0 = a * g.inv_s;
-    const float p = a * qmax;
-    const float e = __builtin_fmaf(a, qmax, -p);
-    const float r = __builtin_fmaf(-q0, d, p) + e;
-    u[k] = __builtin_fmaf(r, rcp_d, q0);
-    lsum += u[k];
+    const float a = (k & 1) ? half_minus<true>(pair[k / 2], mn) : half_minus<false>(pair[k / 2], mn);
+    u[k] = __builtin_fmaf(a, g.inv_s, a * c_lo);
+    lsum = k == 0 ? u[0] : lsum + u[k];
   }
   g.usum = seg_sum<L>(lsum);
   g.z0 = -(mn * g.inv_s);
