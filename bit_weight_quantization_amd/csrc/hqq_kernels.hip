@@ -9,15 +9,15 @@
 //
 // Solver kernel layout (one fused pass: load, init, iterate, pack, store):
 //   * every lane holds 8 consecutive fp16 weights (one 16-byte load, fully
-//     coalesced inside a wavefront) converted once to fp32 registers;
+//     coalesced inside a wavefront); group min/max run on the binary16 pairs;
 //   * a group of G weights lives in a segment of L = G/8 adjacent lanes; a
 //     wavefront holds S = 64/L groups; group sums/min/max are DPP butterflies
 //     inside the segment (quad_perm, row_half_mirror, row_mirror), so every
 //     lane of a segment ends with the bit-identical total;
 //   * the iteration runs in "code units".  At load each weight becomes
-//     u = (w - min) * qmax / (max - min) = w/s + z_0, rounded once to fp32 (a
-//     reciprocal product plus an exact FMA residual correction), so an exact tie
-//     of the initial quantizer (e.g. the midpoint of min and max) stays exact.  With
+//     u = (w - min) * qmax / (max - min) = w/s + z_0, rounded once to fp32 (an
+//     FMA of the exact product with a double-float qmax/(max - min)), so an exact
+//     tie of the initial quantizer (e.g. the midpoint of min and max) stays exact.  With
 //     z = z_0 + delta, the pre-round value is x = u + delta and rc = x - W_q;
 //     the residual is r = s*rc, the error sum|r|^p is s^p * sum|rc|^p (the stop
 //     test compares the code-unit sums, which differ by the constant factor s^p),
@@ -34,14 +34,16 @@
 //     and u = qmax), so a per-group bound decides (with a 1e-4 relative margin
 //     that keeps the result bit-identical to evaluating the shrink) whether the
 //     wave evaluates it;
-//   * groups stop at different steps.  Each wavefront owns an LDS standby pool of
-//     S initialized groups and a done ring of 2S stopped groups.  A segment whose
-//     group stopped copies its u values and header into the done ring and takes a
-//     standby group in the same pass (a few LDS instructions), so lanes stay busy;
-//     standby groups are initialized, and done groups packed and written, in dense
-//     batches of S in which every lane works.  Every group is computed by exactly
-//     the same instruction sequence whatever its slot, so results do not depend on
-//     the schedule.
+//   * groups stop at different steps, but every group takes at least two
+//     evaluations (t = 0 is always accepted).  So a wavefront runs init and the
+//     first two solver steps densely for S fresh groups at a time ("prime"
+//     batches) and writes the groups that stopped at once (about 60% of them on
+//     heavy-tailed weights).  The others wait in an LDS standby pool; each segment
+//     of the wave iterates one of them, and a segment whose group stopped copies
+//     its u values and header into an LDS done ring and takes a standby group in
+//     the same pass.  Done groups are packed and written in dense batches of S.
+//     Every group runs exactly the same instruction sequence whatever its batch or
+//     slot, so results do not depend on the schedule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -169,11 +171,13 @@ struct GroupInit {
   bool may_shrink;  // the shrink can be non-zero at some step (|r| <= max - min always)
 };
 
-// The lane's 16-byte chunk of group `gi` (zero past the end of the wave's queue).
+// The lane's 16-byte chunk of group `gi`.  Past the end of the wave's queue the
+// lane reads the queue's last group instead (a valid address; the value is unused),
+// so the load is unconditional and its registers need no other initialisation.
 template <int L>
 __device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, int64_t gi, int64_t g_end,
                                              int sl) {
-  return gi < g_end ? P.W[gi * L + sl] : make_uint4(0u, 0u, 0u, 0u);
+  return P.W[(gi < g_end ? gi : g_end - 1) * L + sl];
 }
 
 // From the lane's 8 raw binary16 weights, compute its u values and the group scalars.
@@ -245,26 +249,23 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// Groups iterated concurrently by one segment of lanes.
-#ifndef HQQ_SLOTS_PER_SEGMENT
-#define HQQ_SLOTS_PER_SEGMENT 1
-#endif
-constexpr int kSlotsPerSegment = HQQ_SLOTS_PER_SEGMENT;
-
-// Per-wavefront LDS: slots [0, S) are the standby pool (initialized groups waiting for
-// a free segment), slots [S, 3S) the done ring (stopped groups waiting to be written).
-// A slot holds the G code-unit values u of a group and an 8-word header.
+// Per-wavefront LDS: u slots [0, kStandby) are the standby pool (groups past their
+// first two evaluations, waiting for a free segment), u slots [kStandby, kStandby + S)
+// the done ring (stopped groups waiting to be written).  A slot holds the G
+// code-unit values u of a group; standby slots have a 12-word header (the full solver
+// state), done slots an 8-word one.
 template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
-  static constexpr int kSlots = S + S + S / 2;
-  float u[kWavesPerBlock][kSlots][G];
-  uint32_t hdr[kWavesPerBlock][kSlots][8];
+  // A prime batch adds up to S groups to the pool, a hand-over up to S to the ring.
+  // The pool holds 1.5 S groups (S for G = 16, to stay within the LDS of six
+  // wavefronts per SIMD), so it is restocked before it runs dry.
+  static constexpr int kStandby = G == 16 ? S : S + S / 2;
+  static constexpr int kDone = S;
+  float u[kWavesPerBlock][kStandby + kDone][G];
+  uint4 standby_hdr[kWavesPerBlock][kStandby][3];
+  uint4 done_hdr[kWavesPerBlock][kDone][2];
 };
-
-// Header words.  Standby: gidx lo/hi, s, 1/s, z0, sum u, may_shrink.  Done: gidx
-// lo/hi, s, z0, best delta, e0, best e, t*.
-
 
 // Values every lane of the wave computes identically, kept in scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -320,17 +321,165 @@ struct Slot {
   int64_t gidx;
   bool may_shrink;
   bool active;   // iterating
-  bool pending;  // stopped, not yet handed to the done ring
+  bool pending;  // stopped, outputs not yet written or handed to the done ring
 };
 
-// Each segment iterates NS independent groups ("slots"), so the per-iteration
-// bookkeeping and the hand-over passes are shared by NS groups.
-template <int G, int PM, int NS>
-__global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) {
+// Clamping is a no-op while |delta| < 1/2: u lies in [0, qmax], so x = u + delta
+// stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
+__device__ __forceinline__ bool far_delta(float delta) { return !(__builtin_fabsf(delta) < 0.4999f); }
+__device__ __forceinline__ bool needs_clamp(const Slot& q) { return q.active && far_delta(q.delta); }
+
+// One step of the solver for an active group: evaluation at the current z (codes,
+// residual, lp error), the early-stop test of section 4.1, and unless the group
+// stops, the sp1 shrink (only where it can be non-zero) and the sp2 mean.
+template <int L, int PM>
+__device__ __forceinline__ void solver_step(const SolveParams& P, Slot& q, bool clamp) {
+  constexpr float kInvG = 1.0f / (float)(L * kLaneElems);
+  const float qmax = P.qmax;
+  float e, sq;
+  if (clamp) {
+    eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
+  } else {
+    eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
+  }
+  if (P.err_init && q.t == 0) q.e0 = e;
+  const bool accept = !P.early_stop || (e < q.best_e);
+  if (accept) {
+    q.best_e = e;
+    q.best_delta = q.delta;
+    q.t_star = q.t;
+  }
+  if (!accept || q.t == P.iters) {
+    q.active = false;
+    q.pending = true;
+    return;
+  }
+  float num = sq - q.usum;
+  if (ballot(q.may_shrink) != 0) {
+    // beta_t^(-1/(2-p)) and 1/beta_t, from t
+    const float tf = (float)q.t;
+    const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
+    const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(q.delta)) + 1e-5f * (qmax + 1.f);
+    const bool need = q.may_shrink && bound >= tau * q.inv_s * (1.0f - 1e-4f);
+    if (ballot(need) != 0) {
+      if (need) {
+        float cs;  // s^(p-2)
+        if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
+        else if constexpr (PM == kPowOne) cs = q.inv_s;
+        else cs = q.inv_s * q.inv_s;
+        const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
+        const float ib = cs * inv_beta;  // s^(p-2) / beta_t
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) {
+          const float x = q.u[k] + q.delta;
+          const float qc = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
+          const float rc = x - qc;
+          const float a = __builtin_fabsf(rc);
+          float m = 0.f;
+          if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
+          acc += __builtin_copysignf(m, rc);  // W_e / s
+        }
+        num += seg_sum<L>(acc);
+      }
+    }
+  }
+  q.delta = num * kInvG;
+  ++q.t;
+}
+
+// Codes at the accepted z, packed into the LSB-first bitstream, and the group's
+// binary16 s and z (plus the optional fp32 and error outputs).  Called by the L lanes
+// of a segment; lane sl writes the codes of its 8 elements.  CLAMP = false is exact
+// when |bd| < 1/2 (the argument of needs_clamp).
+template <int L, int PM, bool CLAMP>
+__device__ __forceinline__ void write_group(const SolveParams& P, int sl,
+                                            const float (&u)[kLaneElems], int64_t gi, float gs,
+                                            float z0, float bd, float e0, float best_e,
+                                            int t_star) {
+  const float qmax = P.qmax;
+  uint32_t c[kLaneElems];
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    const float q = __builtin_rintf(u[k] + bd);
+    c[k] = (uint32_t)(CLAMP ? __builtin_amdgcn_fmed3f(q, 0.f, qmax) : q);
+  }
+  const int64_t chunk = gi * L + sl;  // index of this lane's 8 elements
+  switch (P.nbits) {
+    case 4: {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (4 * k);
+      reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
+      break;
+    }
+    case 2: {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (2 * k);
+      reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)v;
+      break;
+    }
+    case 8: {
+      uint2 v;
+      v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      reinterpret_cast<uint2*>(P.packed)[chunk] = v;
+      break;
+    }
+    default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (3 * k);
+      uint8_t* dst = P.packed + chunk * 3;
+      dst[0] = (uint8_t)v;
+      dst[1] = (uint8_t)(v >> 8);
+      dst[2] = (uint8_t)(v >> 16);
+      break;
+    }
+  }
+  if (sl == 0) {
+    const float best_z = z0 + bd;
+    P.scale16[gi] = float_to_half_bits(gs);
+    P.zero16[gi] = float_to_half_bits(best_z);
+    if (P.scale32) P.scale32[gi] = gs;
+    if (P.zero32) P.zero32[gi] = best_z;
+    if (P.stop_step) P.stop_step[gi] = (uint8_t)t_star;
+    if (P.err_init || P.err_best) {
+      const float sp = scalar_pow<PM>(gs, P.p);
+      if (P.err_init) P.err_init[gi] = e0 * sp;
+      if (P.err_best) P.err_best[gi] = best_e * sp;
+    }
+  }
+}
+
+// write_group with the clamp only where some written group of the wave needs it.
+template <int L, int PM>
+__device__ __forceinline__ void write_group_any(const SolveParams& P, bool write, int sl,
+                                                const float (&u)[kLaneElems], int64_t gi, float gs,
+                                                float z0, float bd, float e0, float best_e,
+                                                int t_star) {
+  if (ballot(write && far_delta(bd)) != 0) {
+    if (write) write_group<L, PM, true>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
+  } else {
+    if (write) write_group<L, PM, false>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
+  }
+}
+
+// Every group takes at least two evaluations (t = 0 is always accepted), so a wave
+// runs them densely for S fresh groups at a time ("prime" batches): init and two
+// solver steps in every segment.  Groups that stopped are written at once; the
+// others wait in the standby pool for a segment of the iterating set.  Iterating
+// segments whose group stops hand it to the done ring and take a standby group in
+// the same pass; done groups are written in dense batches of S.  Every group runs
+// exactly the same instruction sequence whatever its batch or slot, so results do
+// not depend on the schedule.
+template <int G, int PM>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
   constexpr int S = kWave / L;       // segments per wavefront
-  constexpr int kDone = S + S / 2;   // done-ring capacity
-  constexpr float kInvG = 1.0f / (float)G;
+  constexpr int kStandby = SolveLds<G>::kStandby;  // standby-pool capacity
+  constexpr int kDone = SolveLds<G>::kDone;        // done-ring capacity
   __shared__ SolveLds<G> lds;
 
   const int wid = threadIdx.x / kWave;
@@ -344,301 +493,152 @@ __global__ __launch_bounds__(kBlock) void hqq_solve_kernel(const SolveParams P) 
   if (g_begin >= g_end) return;  // wave-uniform; the kernel has no block-wide barrier
 
   float (*U)[G] = lds.u[wid];
-  uint32_t (*H)[8] = lds.hdr[wid];
-  const float qmax = P.qmax;
+  uint4 (*H)[3] = lds.standby_hdr[wid];
+  uint4 (*D)[2] = lds.done_hdr[wid];  // done slot j has u slot kStandby + j
 
-  Slot sg[NS];
+  Slot sg;  // the group this segment iterates
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-#pragma unroll
-    for (int k = 0; k < kLaneElems; ++k) sg[j].u[k] = 0.f;
-    sg[j].s = sg[j].inv_s = 1.f;
-    sg[j].z0 = sg[j].usum = sg[j].delta = sg[j].best_delta = sg[j].best_e = sg[j].e0 = 0.f;
-    sg[j].t = sg[j].t_star = 0;
-    sg[j].gidx = 0;
-    sg[j].may_shrink = sg[j].active = sg[j].pending = false;
-  }
+  for (int k = 0; k < kLaneElems; ++k) sg.u[k] = 0.f;
+  sg.s = sg.inv_s = 1.f;
+  sg.z0 = sg.usum = sg.delta = sg.best_delta = sg.best_e = sg.e0 = 0.f;
+  sg.t = sg.t_star = 0;
+  sg.gidx = 0;
+  sg.may_shrink = sg.active = sg.pending = false;
 
   // Wave-uniform bookkeeping.
   int64_t next = g_begin;  // next group of the wave's queue
   int n_standby = 0;       // standby slots [0, n_standby) hold groups
   int done_head = 0, done_count = 0;
 
-  auto begin_iterating = [&](Slot& q, const GroupInit& gq) {
-    q.s = gq.s;
-    q.inv_s = gq.inv_s;
-    q.z0 = gq.z0;
-    q.usum = gq.usum;
-    q.delta = 0.f;
-    q.best_delta = 0.f;
-    q.may_shrink = gq.may_shrink;
-    q.best_e = __builtin_inff();
-    q.t = 0;
-    q.t_star = 0;
-    q.active = true;
-  };
+  // The weights of the next prime batch are fetched one batch ahead, so the HBM
+  // latency overlaps the work in between.
+  uint4 prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
 
-  // The weights of the next standby batch are fetched one batch ahead, so the
-  // HBM latency overlaps the iterations in between.
-  uint4 prefetch = make_uint4(0u, 0u, 0u, 0u);
-
-  // Dense batch: segment j initializes group next + j into standby slot j.
-  auto fill_standby = [&]() {
+  // Dense batch: segment j initializes group next + j and runs its first two steps.
+  auto prime = [&]() {
     const int64_t avail = g_end - next;
     const int n = avail < S ? (int)avail : S;
+    Slot a;
+    a.active = a.pending = false;
     if (seg < n) {
-      float uu[kLaneElems];
-      const int64_t gi = next + seg;
-      const GroupInit gq = init_group<L>(P, prefetch, uu);
-      store_u<G>(U[seg], sl, uu);
-      if (sl == 0) {
-        uint4* h = reinterpret_cast<uint4*>(H[seg]);
-        h[0] = make_uint4((uint32_t)gi, (uint32_t)(gi >> 32), fbits(gq.s), fbits(gq.inv_s));
-        h[1] = make_uint4(fbits(gq.z0), fbits(gq.usum), gq.may_shrink ? 1u : 0u, 0u);
-      }
+      a.gidx = next + seg;
+      const GroupInit gq = init_group<L>(P, prefetch, a.u);
+      a.s = gq.s;
+      a.inv_s = gq.inv_s;
+      a.z0 = gq.z0;
+      a.usum = gq.usum;
+      a.may_shrink = gq.may_shrink;
+      a.delta = a.best_delta = a.e0 = 0.f;
+      a.best_e = __builtin_inff();
+      a.t = a.t_star = 0;
+      a.active = true;
     }
-    n_standby = uniform(n);
     next = uniform64(next + n);
     prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
+    // t = 0: delta = 0, no clamp needed.
+    if (a.active) solver_step<L, PM>(P, a, false);
+    if (ballot(a.active) != 0) {
+      const bool clamp = ballot(needs_clamp(a)) != 0;
+      if (a.active) solver_step<L, PM>(P, a, clamp);
+    }
+    write_group_any<L, PM>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0, a.best_e,
+                           a.t_star);
+    const uint64_t m = ballot(a.active);
+    if (a.active) {
+      const int slot = n_standby + lanes_below(m) / L;  // n_standby <= kStandby - S
+      store_u<G>(U[slot], sl, a.u);
+      if (sl == 0) {
+        H[slot][0] = make_uint4((uint32_t)a.gidx, (uint32_t)(a.gidx >> 32), fbits(a.s), fbits(a.inv_s));
+        H[slot][1] = make_uint4(fbits(a.z0), fbits(a.usum), fbits(a.delta), fbits(a.best_delta));
+        H[slot][2] = make_uint4(fbits(a.best_e), fbits(a.e0),
+                                (uint32_t)a.t | ((uint32_t)a.t_star << 8) |
+                                    (a.may_shrink ? 0x10000u : 0u),
+                                0u);
+      }
+    }
+    n_standby = uniform(n_standby + __builtin_popcountll(m) / L);
     wave_lds_sync();
   };
 
-  // Slots with want[j] set take standby groups (slot-major order, highest standby
-  // slot first).
-  auto take_standby = [&](const bool (&want)[NS]) {
-    int base = 0;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const uint64_t m = ballot(want[j]);
-      const int rank = base + lanes_below(m) / L;
-      if (want[j] && rank < n_standby) {
-        const int slot = n_standby - 1 - rank;
-        load_u<G>(U[slot], sl, sg[j].u);
-        const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
-        const uint4 h0 = h[0], h1 = h[1];
-        sg[j].gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
-        GroupInit gq;
-        gq.s = bitsf(h0.z);
-        gq.inv_s = bitsf(h0.w);
-        gq.z0 = bitsf(h1.x);
-        gq.usum = bitsf(h1.y);
-        gq.may_shrink = h1.z != 0u;
-        begin_iterating(sg[j], gq);
-      }
-      base += __builtin_popcountll(m) / L;
+  // Segments with `want` set take standby groups (highest standby slot first).
+  auto take_standby = [&](bool want) {
+    const uint64_t m = ballot(want);
+    const int rank = lanes_below(m) / L;
+    if (want && rank < n_standby) {
+      const int slot = n_standby - 1 - rank;
+      load_u<G>(U[slot], sl, sg.u);
+      const uint4 h0 = H[slot][0], h1 = H[slot][1], h2 = H[slot][2];
+      sg.gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
+      sg.s = bitsf(h0.z);
+      sg.inv_s = bitsf(h0.w);
+      sg.z0 = bitsf(h1.x);
+      sg.usum = bitsf(h1.y);
+      sg.delta = bitsf(h1.z);
+      sg.best_delta = bitsf(h1.w);
+      sg.best_e = bitsf(h2.x);
+      sg.e0 = bitsf(h2.y);
+      sg.t = (int)(h2.z & 0xffu);
+      sg.t_star = (int)((h2.z >> 8) & 0xffu);
+      sg.may_shrink = (h2.z & 0x10000u) != 0u;
+      sg.active = true;
     }
-    n_standby = uniform(n_standby - (base < n_standby ? base : n_standby));
+    const int taken = __builtin_popcountll(m) / L;
+    n_standby = uniform(n_standby - (taken < n_standby ? taken : n_standby));
     wave_lds_sync();
   };
 
   // Dense batch: segment j writes the codes and meta of done slot head + j.
   auto finalize = [&](int n) {
-    if (seg < n) {
-      const int slot = S + (int)((unsigned)(done_head + seg) % (unsigned)kDone);
-      float uu[kLaneElems];
-      load_u<G>(U[slot], sl, uu);
-      const uint4* h = reinterpret_cast<const uint4*>(H[slot]);
-      const uint4 h0 = h[0], h1 = h[1];
-      const int64_t gi = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
-      const float bd = bitsf(h1.x);
-      uint32_t c[kLaneElems];
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) {
-        const float x = uu[k] + bd;
-        c[k] = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-      }
-      const int64_t chunk = gi * L + sl;  // index of this lane's 8 elements
-      switch (P.nbits) {
-        case 4: {
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (4 * k);
-          reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
-          break;
-        }
-        case 2: {
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (2 * k);
-          reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)v;
-          break;
-        }
-        case 8: {
-          uint2 v;
-          v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-          v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-          reinterpret_cast<uint2*>(P.packed)[chunk] = v;
-          break;
-        }
-        default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
-          uint32_t v = 0;
-#pragma unroll
-          for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (3 * k);
-          uint8_t* dst = P.packed + chunk * 3;
-          dst[0] = (uint8_t)v;
-          dst[1] = (uint8_t)(v >> 8);
-          dst[2] = (uint8_t)(v >> 16);
-          break;
-        }
-      }
-      if (sl == 0) {
-        const float gs = bitsf(h0.z);
-        const float best_z = bitsf(h0.w) + bd;
-        P.scale16[gi] = float_to_half_bits(gs);
-        P.zero16[gi] = float_to_half_bits(best_z);
-        if (P.scale32) P.scale32[gi] = gs;
-        if (P.zero32) P.zero32[gi] = best_z;
-        if (P.stop_step) P.stop_step[gi] = (uint8_t)h1.w;
-        if (P.err_init || P.err_best) {
-          const float sp = scalar_pow<PM>(gs, P.p);
-          if (P.err_init) P.err_init[gi] = bitsf(h1.y) * sp;
-          if (P.err_best) P.err_best[gi] = bitsf(h1.z) * sp;
-        }
-      }
-    }
+    const bool write = seg < n;
+    const int slot = kStandby + (int)((unsigned)(done_head + (write ? seg : 0)) % (unsigned)kDone);
+    float uu[kLaneElems];
+    load_u<G>(U[slot], sl, uu);
+    const uint4 h0 = D[slot - kStandby][0], h1 = D[slot - kStandby][1];
+    write_group_any<L, PM>(P, write, sl, uu, (int64_t)(((uint64_t)h0.y << 32) | h0.x),
+                           bitsf(h0.z), bitsf(h0.w), bitsf(h1.x), bitsf(h1.y), bitsf(h1.z),
+                           (int)h1.w);
     done_head = uniform((int)((unsigned)(done_head + n) % (unsigned)kDone));
     done_count = uniform(done_count - n);
     wave_lds_sync();
   };
 
-  // The first NS*S groups go straight to the slots, the next S to the standby pool.
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    const int64_t avail = g_end - next;
-    const int n = avail < S ? (int)(avail > 0 ? avail : 0) : S;
-    if (seg < n) {
-      sg[j].gidx = next + seg;
-      begin_iterating(sg[j], init_group<L>(P, fetch_chunk<L>(P, sg[j].gidx, g_end, sl), sg[j].u));
-    }
-    next = uniform64(next + n);
-  }
-  prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
-  if (next < g_end) fill_standby();
-
+  // One pass per solver step of the iterating set.  A pass hands stopped groups to
+  // the done ring, writes full done batches, primes a batch when segments are idle
+  // and the pool is empty, and gives idle segments standby groups.
   while (true) {
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) any = any || sg[j].active || sg[j].pending;
-    if (ballot(any) == 0) break;
-
-    // Clamping is a no-op while every |delta| < 1/2: u lies in [0, qmax], so
-    // x = u + delta stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
-    bool far = false;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) far = far || (sg[j].active && !(__builtin_fabsf(sg[j].delta) < 0.4999f));
-    const bool clamp = ballot(far) != 0;
-
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      Slot& q = sg[j];
-      if (q.active) {
-        // ---- evaluation at the current z: codes, residual, lp error --------
-        float e, sq;
-        if (clamp) {
-          eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
-        } else {
-          eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
-        }
-        if (P.err_init && q.t == 0) q.e0 = e;
-        const bool accept = !P.early_stop || (e < q.best_e);
-        if (accept) {
-          q.best_e = e;
-          q.best_delta = q.delta;
-          q.t_star = q.t;
-        }
-        if (!accept || q.t == P.iters) {
-          q.active = false;
-          q.pending = true;
-        } else {
-          // ---- sp1 shrink (only where it can be non-zero) + sp2 mean -------
-          float num = sq - q.usum;
-          if (ballot(q.may_shrink) != 0) {
-            // beta_t^(-1/(2-p)) and 1/beta_t, from t
-            const float tf = (float)q.t;
-            const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
-            const float bound =
-                __builtin_fmaxf(0.5f, __builtin_fabsf(q.delta)) + 1e-5f * (qmax + 1.f);
-            const bool need = q.may_shrink && bound >= tau * q.inv_s * (1.0f - 1e-4f);
-            if (ballot(need) != 0) {
-              if (need) {
-                float cs;  // s^(p-2)
-                if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
-                else if constexpr (PM == kPowOne) cs = q.inv_s;
-                else cs = q.inv_s * q.inv_s;
-                const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
-                const float ib = cs * inv_beta;  // s^(p-2) / beta_t
-                float acc = 0.f;
-#pragma unroll
-                for (int k = 0; k < kLaneElems; ++k) {
-                  const float x = q.u[k] + q.delta;
-                  const float qc = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-                  const float rc = x - qc;
-                  const float a = __builtin_fabsf(rc);
-                  float m = 0.f;
-                  if (a > 0.f)
-                    m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
-                  acc += __builtin_copysignf(m, rc);  // W_e / s
-                }
-                num += seg_sum<L>(acc);
-              }
-            }
-          }
-          q.delta = num * kInvG;
-          ++q.t;
-        }
-      }
+    const bool any_active = ballot(sg.active) != 0;
+    if (!any_active && n_standby == 0 && next >= g_end) break;
+    if (any_active) {
+      const bool clamp = ballot(needs_clamp(sg)) != 0;
+      if (sg.active) solver_step<L, PM>(P, sg, clamp);
     }
 
-    // ---- stopped groups: hand them to the done ring, take standby groups -------
-    uint64_t pm[NS];
-    int npend = 0;
-    bool any_active = false;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      pm[j] = ballot(sg[j].pending);
-      npend += __builtin_popcountll(pm[j]) / L;
-      any_active = any_active || sg[j].active;
-    }
-    if (npend > 0 && (npend >= P.refill_at || ballot(any_active) == 0)) {
+    // ---- stopped groups: hand them to the done ring ---------------------------
+    const uint64_t pm = ballot(sg.pending);
+    const int npend = __builtin_popcountll(pm) / L;
+    if (npend > 0 && (npend >= P.refill_at || ballot(sg.active) == 0)) {
       if (done_count + npend > kDone) finalize(done_count);  // rare: make room first
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const Slot& q = sg[j];
-        const int rank = base + lanes_below(pm[j]) / L;
-        if (q.pending) {
-          const int slot = S + (int)((unsigned)(done_head + done_count + rank) % (unsigned)kDone);
-          store_u<G>(U[slot], sl, q.u);
-          if (sl == 0) {
-            uint4* h = reinterpret_cast<uint4*>(H[slot]);
-            h[0] = make_uint4((uint32_t)q.gidx, (uint32_t)(q.gidx >> 32), fbits(q.s), fbits(q.z0));
-            h[1] = make_uint4(fbits(q.best_delta), fbits(q.e0), fbits(q.best_e), (uint32_t)q.t_star);
-          }
+      if (sg.pending) {
+        const int rank = lanes_below(pm) / L;
+        const int slot = kStandby + (int)((unsigned)(done_head + done_count + rank) % (unsigned)kDone);
+        store_u<G>(U[slot], sl, sg.u);
+        if (sl == 0) {
+          D[slot - kStandby][0] = make_uint4((uint32_t)sg.gidx, (uint32_t)(sg.gidx >> 32), fbits(sg.s),
+                                      fbits(sg.z0));
+          D[slot - kStandby][1] = make_uint4(fbits(sg.best_delta), fbits(sg.e0), fbits(sg.best_e),
+                                      (uint32_t)sg.t_star);
         }
-        base += __builtin_popcountll(pm[j]) / L;
       }
       done_count = uniform(done_count + npend);
+      sg.pending = false;
       wave_lds_sync();
-      bool want[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        want[j] = sg[j].pending;
-        sg[j].pending = false;
-      }
-      take_standby(want);
+      if (done_count >= S) finalize(S);
     }
-    while (done_count >= S) finalize(S);
-    if (n_standby == 0 && next < g_end) {
-      fill_standby();
-      bool idle[NS];
-      bool any_idle = false;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        idle[j] = !sg[j].active && !sg[j].pending;
-        any_idle = any_idle || idle[j];
-      }
-      if (ballot(any_idle) != 0) take_standby(idle);
-    }
+
+    // ---- keep the pool stocked (a batch adds at most S), feed idle segments ------
+    if (n_standby <= kStandby - S && next < g_end) prime();
+    const bool idle = !sg.active && !sg.pending;
+    if (n_standby > 0 && ballot(idle) != 0) take_standby(idle);
   }
   while (done_count > 0) finalize(done_count < S ? done_count : S);
 }
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 // limit), each wavefront owning one contiguous queue of groups.
 template <int G, int PM>
 hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
-  auto kernel = hqq_solve_kernel<G, PM, kSlotsPerSegment>;
+  auto kernel = hqq_solve_kernel<G, PM>;
   int per_cu = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
   if (err != hipSuccess) return err;
