@@ -26,8 +26,8 @@ HQQ_ERR_ALIGNMENT = 3
 HQQ_ERR_LAUNCH = 4
 
 # Symbols declared in include/hqq.h.
-EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_dequantize", "hqq_packed_bytes",
-                    "hqq_num_groups", "hqq_status_string")
+EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
+                    "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
 
 
 class HQQError(RuntimeError):
@@ -41,6 +41,11 @@ class hqq_options_t(ctypes.Structure):
                 ("scale_f32", ctypes.c_void_p), ("zero_f32", ctypes.c_void_p),
                 ("stop_step", ctypes.c_void_p), ("err_init", ctypes.c_void_p),
                 ("err_best", ctypes.c_void_p), ("refill_threshold", ctypes.c_int)]
+
+
+class hqq_batch_entry_t(ctypes.Structure):
+    _fields_ = [("W_f16", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("first_group", ctypes.c_int64)]
 
 
 _lib = None
@@ -60,6 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_ex.restype = I
     lib.hqq_quantize_ex.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
                                     ctypes.POINTER(hqq_options_t), P]
+    lib.hqq_quantize_batch.restype = I
+    lib.hqq_quantize_batch.argtypes = [ctypes.POINTER(hqq_batch_entry_t), P, I, I, I, F, F, F, I,
+                                       P, P, P, P]
     lib.hqq_dequantize.restype = I
     lib.hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
     lib.hqq_packed_bytes.restype = I64
@@ -99,6 +107,15 @@ def hqq_quantize_ex(W_f16: int, rows: int, cols: int, nbits: int, group_size: in
     opt = ctypes.byref(options) if options is not None else None
     return load_library().hqq_quantize_ex(W_f16, rows, cols, nbits, group_size, p, beta, kappa,
                                           iters, packed_codes, scale_f16, zero_f16, opt, stream)
+
+
+def hqq_quantize_batch(entries, entries_device: int, count: int, nbits: int, group_size: int,
+                       p: float, beta: float, kappa: float, iters: int, packed_codes: int,
+                       scale_f16: int, zero_f16: int, stream: int = 0) -> int:
+    """``entries``: a ctypes array of ``hqq_batch_entry_t`` (host copy)."""
+    return load_library().hqq_quantize_batch(entries, entries_device, count, nbits, group_size, p,
+                                             beta, kappa, iters, packed_codes, scale_f16, zero_f16,
+                                             stream)
 
 
 def hqq_dequantize(packed_codes: int, scale_f16: int, zero_f16: int, rows: int, cols: int,
@@ -179,6 +196,81 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
                          _addr(out.zero), opts, _stream_handle(stream))
     if st != HQQ_OK:
         raise HQQError(st, "hqq_quantize_ex")
+    return out
+
+
+@dataclass
+class QuantizedBatch:
+    """Outputs of :func:`quantize_batch`: one arena for all matrices, in list order."""
+    packed: "torch.Tensor"            # uint8, total_groups * group_size * nbits / 8
+    scale: "torch.Tensor"             # fp16, total_groups
+    zero: "torch.Tensor"              # fp16, total_groups (code units)
+    shapes: list                      # (rows, cols) per matrix
+    first_group: list                 # first group index per matrix
+    nbits: int
+    group_size: int
+    table: "torch.Tensor"             # device copy of the entry table (kept for the launch)
+
+    def matrix(self, i: int) -> QuantizedWeight:
+        """Views of matrix i's outputs (no copy)."""
+        rows, cols = self.shapes[i]
+        g0, ng = self.first_group[i], rows * cols // self.group_size
+        b0 = g0 * self.group_size * self.nbits // 8
+        nb = ng * self.group_size * self.nbits // 8
+        return QuantizedWeight(packed=self.packed[b0:b0 + nb],
+                               scale=self.scale[g0:g0 + ng].view(rows, cols // self.group_size),
+                               zero=self.zero[g0:g0 + ng].view(rows, cols // self.group_size),
+                               rows=rows, cols=cols, nbits=self.nbits, group_size=self.group_size)
+
+
+def batch_table(Ws, group_size: int):
+    """Host entry table (ctypes array) for a list of contiguous 2-D fp16 CUDA tensors."""
+    entries = (hqq_batch_entry_t * max(len(Ws), 1))()
+    total = 0
+    for i, W in enumerate(Ws):
+        rows, cols = W.shape
+        entries[i].W_f16 = _addr(W)
+        entries[i].rows, entries[i].cols, entries[i].first_group = rows, cols, total
+        total += rows * cols // group_size
+    return entries, total
+
+
+def quantize_batch(Ws, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
+                   kappa: float = 1.01, iters: int = 20, out: Optional[QuantizedBatch] = None,
+                   stream=None) -> QuantizedBatch:
+    """Quantize a list of contiguous rows x cols fp16 CUDA tensors in one launch.
+
+    Results equal those of :func:`quantize` on each tensor; the outputs go to one arena
+    (``QuantizedBatch.matrix(i)`` gives the views of tensor i).  ``out`` may supply a
+    previous result for the same shapes, whose buffers and entry table are reused.
+    """
+    import torch
+    for W in Ws:
+        if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
+            raise ValueError("every W must be a contiguous 2-D float16 CUDA tensor")
+    entries, total = batch_table(Ws, group_size)
+    if out is None:
+        dev = Ws[0].device if Ws else torch.device("cuda")
+        nb = total * group_size * nbits // 8
+        starts, g = [], 0
+        for W in Ws:
+            starts.append(g)
+            g += W.numel() // group_size
+        out = QuantizedBatch(
+            packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
+            scale=torch.empty(total, dtype=torch.float16, device=dev),
+            zero=torch.empty(total, dtype=torch.float16, device=dev),
+            shapes=[tuple(W.shape) for W in Ws], first_group=starts, nbits=nbits,
+            group_size=group_size,
+            table=torch.empty(max(len(Ws), 1) * ctypes.sizeof(hqq_batch_entry_t), dtype=torch.uint8,
+                              device=dev))
+    host = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8)
+    out.table.copy_(host[: out.table.numel()], non_blocking=False)
+    st = hqq_quantize_batch(entries, _addr(out.table), len(Ws), nbits, group_size, float(p),
+                            float(beta), float(kappa), int(iters), _addr(out.packed),
+                            _addr(out.scale), _addr(out.zero), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_quantize_batch")
     return out
 
 

@@ -3,6 +3,7 @@
 // No allocation, no synchronization, no global mutable state.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/hqq.h"
@@ -40,6 +41,42 @@ int validate_common(int64_t rows, int64_t cols, int nbits, int group_size) {
   return HQQ_OK;
 }
 
+int validate_solver(float p, float beta, float kappa, int iters) {
+  if (!(p >= 0.0f && p <= 1.0f)) return HQQ_ERR_INVALID_ARG;
+  if (!(beta > 0.0f) || !isfinite(beta)) return HQQ_ERR_INVALID_ARG;
+  if (!(kappa > 0.0f) || !isfinite(kappa)) return HQQ_ERR_INVALID_ARG;
+  if (iters < 0 || iters > kMaxIters) return HQQ_ERR_INVALID_ARG;
+  return HQQ_OK;
+}
+
+// Solver constants shared by the single-matrix and batched entry points.
+void set_solver_params(hqq::SolveParams& prm, int nbits, int group_size, float p, float beta,
+                       float kappa, int iters, int early_stop, int refill_threshold) {
+  const int slots = hqq::kWave * hqq::kLaneElems / group_size;  // groups resident in a wavefront
+  prm.qmax = (float)((1 << nbits) - 1);
+  prm.inv_qmax = (float)(1.0 / (double)((1 << nbits) - 1));
+  prm.p = p;
+  prm.pm1 = p - 1.0f;
+  prm.pm2 = p - 2.0f;
+  prm.inv_beta0 = (float)(1.0 / (double)beta);
+  // The shrink of section 2.1 vanishes for |x|^(2-p) <= 1/beta, i.e. |x| <= beta^(-1/(2-p)).
+  const double tau0 = pow((double)beta, -1.0 / (2.0 - (double)p));
+  const double log2_rho = -log2((double)kappa) / (2.0 - (double)p);
+  prm.tau0 = (float)tau0;
+  prm.log2_rho = (float)log2_rho;
+  prm.log2_kappa = (float)log2((double)kappa);
+  prm.tau_min = (float)(log2_rho < 0.0 ? tau0 * exp2(log2_rho * iters) : tau0);
+  prm.iters = iters;
+  prm.early_stop = early_stop;
+  prm.nbits = nbits;
+  const int refill = refill_threshold > 0 ? refill_threshold : 1;
+  prm.refill_at = refill > slots ? slots : refill;
+}
+
+int power_mode_of(float p) {
+  return p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,10 +109,8 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
                     void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream) {
   int st = validate_common(rows, cols, nbits, group_size);
   if (st != HQQ_OK) return st;
-  if (!(p >= 0.0f && p <= 1.0f)) return HQQ_ERR_INVALID_ARG;
-  if (!(beta > 0.0f) || !isfinite(beta)) return HQQ_ERR_INVALID_ARG;
-  if (!(kappa > 0.0f) || !isfinite(kappa)) return HQQ_ERR_INVALID_ARG;
-  if (iters < 0 || iters > kMaxIters) return HQQ_ERR_INVALID_ARG;
+  st = validate_solver(p, beta, kappa, iters);
+  if (st != HQQ_OK) return st;
   const int64_t n = rows * cols;
   if (n == 0) return HQQ_OK;
   if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
@@ -92,12 +127,10 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
       return HQQ_ERR_ALIGNMENT;
   }
 
-  const int64_t ngroups = n / group_size;
-  const int lanes_per_group = group_size / hqq::kLaneElems;
-  const int slots = hqq::kWave / lanes_per_group;  // groups resident in one wavefront
-
-  hqq::SolveParams prm;
+  hqq::SolveParams prm = {};
   prm.W = static_cast<const uint4*>(W_f16);
+  prm.batch = nullptr;
+  prm.batch_count = 0;
   prm.packed = static_cast<uint8_t*>(packed_codes);
   prm.scale16 = static_cast<uint16_t*>(scale_f16);
   prm.zero16 = static_cast<uint16_t*>(zero_f16);
@@ -106,31 +139,64 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   prm.stop_step = o.stop_step;
   prm.err_init = o.err_init;
   prm.err_best = o.err_best;
-  prm.ngroups = ngroups;
-  prm.qmax = (float)((1 << nbits) - 1);
-  prm.inv_qmax = (float)(1.0 / (double)((1 << nbits) - 1));
-  prm.p = p;
-  prm.pm1 = p - 1.0f;
-  prm.pm2 = p - 2.0f;
-  prm.inv_beta0 = (float)(1.0 / (double)beta);
-  // The shrink of section 2.1 vanishes for |x|^(2-p) <= 1/beta, i.e. |x| <= beta^(-1/(2-p)).
-  const double tau0 = pow((double)beta, -1.0 / (2.0 - (double)p));
-  const double log2_rho = -log2((double)kappa) / (2.0 - (double)p);
-  prm.tau0 = (float)tau0;
-  prm.log2_rho = (float)log2_rho;
-  prm.log2_kappa = (float)log2((double)kappa);
-  prm.tau_min = (float)(log2_rho < 0.0 ? tau0 * exp2(log2_rho * iters) : tau0);
-  prm.iters = iters;
-  prm.early_stop = o.early_stop;
-  prm.nbits = nbits;
-  int refill = o.refill_threshold > 0 ? o.refill_threshold : 1;
-  prm.refill_at = refill < 1 ? 1 : (refill > slots ? slots : refill);
-
-  const int power_mode = p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
+  prm.ngroups = n / group_size;
+  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, o.early_stop,
+                    o.refill_threshold);
+  const int power_mode = power_mode_of(p);
 
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;
   hipError_t err = hqq::launch_solve(prm, group_size, power_mode, cus,
+                                     static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t* entries_device,
+                       int count, int nbits, int group_size, float p, float beta, float kappa,
+                       int iters, void* packed_codes, void* scale_f16, void* zero_f16,
+                       void* stream) {
+  static_assert(sizeof(hqq_batch_entry_t) == sizeof(hqq::BatchEntry), "entry layout");
+  static_assert(offsetof(hqq_batch_entry_t, first_group) == offsetof(hqq::BatchEntry, first_group),
+                "entry layout");
+  if (count < 0) return HQQ_ERR_INVALID_ARG;
+  if (!supported_nbits(nbits) || !supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
+  int st = validate_solver(p, beta, kappa, iters);
+  if (st != HQQ_OK) return st;
+  if (count == 0) return HQQ_OK;
+  if (!entries || !entries_device) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(entries_device, 8)) return HQQ_ERR_ALIGNMENT;
+  int64_t total = 0;  // groups of the entries so far
+  for (int i = 0; i < count; ++i) {
+    const hqq_batch_entry_t& e = entries[i];
+    st = validate_common(e.rows, e.cols, nbits, group_size);
+    if (st != HQQ_OK) return st;
+    if (e.first_group != total) return HQQ_ERR_INVALID_ARG;
+    const int64_t n = e.rows * e.cols;
+    if (n > 0) {
+      if (!e.W_f16) return HQQ_ERR_INVALID_ARG;
+      if (!aligned(e.W_f16, 16)) return HQQ_ERR_ALIGNMENT;
+    }
+    const int64_t groups = n / group_size;
+    if (groups > INT64_MAX / 8 / group_size - total) return HQQ_ERR_INVALID_ARG;  // size overflow
+    total += groups;
+  }
+  if (total == 0) return HQQ_OK;
+  if (!packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2))
+    return HQQ_ERR_ALIGNMENT;
+
+  hqq::SolveParams prm = {};
+  prm.W = nullptr;
+  prm.batch = reinterpret_cast<const hqq::BatchEntry*>(entries_device);
+  prm.batch_count = count;
+  prm.packed = static_cast<uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<uint16_t*>(zero_f16);
+  prm.ngroups = total;
+  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, 1, 0);
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_solve(prm, group_size, power_mode_of(p), cus,
                                      static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }

@@ -10,8 +10,17 @@ namespace hqq {
 // or the two exact special cases p = 1 and p = 0.
 enum PowerMode : int { kPowGeneral = 0, kPowOne = 1, kPowZero = 2 };
 
-struct SolveParams {
+// Device view of one hqq_batch_entry_t (same 32-byte layout).
+struct BatchEntry {
   const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8
+  int64_t rows, cols;
+  int64_t first_group;     // global index of the matrix's first group
+};
+
+struct SolveParams {
+  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8 (single matrix)
+  const BatchEntry* batch; // device entry table (batched launch), else null
+  int batch_count;
   uint8_t* packed;         // packed code stream
   uint16_t* scale16;       // binary16 s per group
   uint16_t* zero16;        // binary16 z per group
@@ -21,7 +30,7 @@ struct SolveParams {
   float* err_init;
   float* err_best;
   int64_t ngroups;
-  int64_t groups_per_wave; // contiguous queue length of one wavefront (set by the launcher)
+  int64_t chunk_groups;    // groups per queue chunk, a multiple of S (set by the launcher)
   float qmax;
   float inv_qmax;          // 1/qmax rounded to fp32
   float p;                 // lp exponent
@@ -50,7 +59,7 @@ struct DequantParams {
 
 // Launchers (return a hipError_t of the launch).
 hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
-                        hipStream_t stream);
+                        hipStream_t stream);  // batched when prm.batch != nullptr
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
 
 // Segment geometry shared with the host grid sizing: each lane holds 8 weights.

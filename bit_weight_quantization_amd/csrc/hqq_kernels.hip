@@ -171,13 +171,64 @@ struct GroupInit {
   bool may_shrink;  // the shrink can be non-zero at some step (|r| <= max - min always)
 };
 
+// The entry of a batched launch that holds the wave's next group: its index, its
+// group range [first, end) and its weights.  Wave-uniform.
+struct BatchCursor {
+  int m;
+  int64_t first, end;
+  const uint4* W;
+};
+
+// The entry holding global group g (binary search for the last entry whose first
+// group is <= g; empty entries share their successor's first group).
+__device__ __forceinline__ BatchCursor batch_cursor(const SolveParams& P, int64_t g) {
+  int lo = 0, hi = P.batch_count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.batch[mid].first_group <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  BatchCursor c;
+  c.m = lo;
+  c.first = P.batch[lo].first_group;
+  c.end = lo + 1 < P.batch_count ? P.batch[lo + 1].first_group : P.ngroups;
+  c.W = P.batch[lo].W;
+  return c;
+}
+
+// Moves the cursor forward to the entry holding group g (g < number of groups).
+__device__ __forceinline__ void batch_advance(const SolveParams& P, BatchCursor& c, int64_t g) {
+  while (g >= c.end) {
+    ++c.m;
+    c.first = c.end;
+    c.W = P.batch[c.m].W;
+    c.end = c.m + 1 < P.batch_count ? P.batch[c.m + 1].first_group : P.ngroups;
+  }
+}
+
 // The lane's 16-byte chunk of group `gi`.  Past the end of the wave's queue the
 // lane reads the queue's last group instead (a valid address; the value is unused),
-// so the load is unconditional and its registers need no other initialisation.
-template <int L>
-__device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, int64_t gi, int64_t g_end,
-                                             int sl) {
-  return P.W[(gi < g_end ? gi : g_end - 1) * L + sl];
+// so the load is unconditional and its registers need no other initialisation.  In a
+// batched launch the chunk comes from the entry holding the group: the cursor's,
+// or for segments past it (only near an entry boundary) a later one.
+template <int L, bool BATCH>
+__device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, const BatchCursor& c,
+                                             int64_t gi, int64_t g_end, int sl) {
+  if constexpr (!BATCH) {
+    return P.W[(gi < g_end ? gi : g_end - 1) * L + sl];
+  } else {
+    // Past the queue the lane reads the cursor's first group (its entry is never empty).
+    const int64_t g = gi < g_end ? gi : c.first;
+    const uint4* W = c.W;
+    int64_t first = c.first;
+    if (g >= c.end) {
+      int m = c.m + 1;
+      while (m + 1 < P.batch_count && g >= P.batch[m + 1].first_group) ++m;
+      W = P.batch[m].W;
+      first = P.batch[m].first_group;
+    }
+    return W[(g - first) * L + sl];
+  }
 }
 
 // From the lane's 8 raw binary16 weights, compute its u values and the group scalars.
@@ -474,7 +525,7 @@ __device__ __forceinline__ void write_group_any(const SolveParams& P, bool write
 // the same pass; done groups are written in dense batches of S.  Every group runs
 // exactly the same instruction sequence whatever its batch or slot, so results do
 // not depend on the schedule.
-template <int G, int PM>
+template <int G, int PM, bool BATCH>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
   constexpr int S = kWave / L;       // segments per wavefront
@@ -486,11 +537,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
   const int lane = threadIdx.x & (kWave - 1);
   const int seg = lane / L;
   const int sl = lane & (L - 1);
-  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
-  const int64_t g_begin = wave * P.groups_per_wave;
-  const int64_t g_end = g_begin + P.groups_per_wave < P.ngroups ? g_begin + P.groups_per_wave
-                                                                : P.ngroups;
-  if (g_begin >= g_end) return;  // wave-uniform; the kernel has no block-wide barrier
+  // The wave's queue: chunks wave, wave + nwaves, wave + 2 nwaves, ... of C groups
+  // (C a multiple of S), so all wavefronts sweep the weights together through a
+  // window of nwaves * C groups (page and TLB locality) and finish within a chunk
+  // of each other.
+  const int64_t wave = uniform64(((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t C = P.chunk_groups;
+  int64_t chunk = wave;
+  if (chunk * C >= P.ngroups) return;  // wave-uniform; the kernel has no block-wide barrier
+  int64_t next = chunk * C;            // next group of the wave's queue
+  int64_t q_end = next + C < P.ngroups ? next + C : P.ngroups;  // end of the current chunk
 
   float (*U)[G] = lds.u[wid];
   uint4 (*H)[3] = lds.standby_hdr[wid];
@@ -505,18 +562,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
   sg.gidx = 0;
   sg.may_shrink = sg.active = sg.pending = false;
 
-  // Wave-uniform bookkeeping.
-  int64_t next = g_begin;  // next group of the wave's queue
+  // Wave-uniform bookkeeping.  The queue is exhausted when next == q_end == ngroups.
   int n_standby = 0;       // standby slots [0, n_standby) hold groups
   int done_head = 0, done_count = 0;
 
   // The weights of the next prime batch are fetched one batch ahead, so the HBM
   // latency overlaps the work in between.
-  uint4 prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
+  BatchCursor cursor = {0, 0, P.ngroups, P.W};
+  if constexpr (BATCH) cursor = batch_cursor(P, next);
+  uint4 prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
 
   // Dense batch: segment j initializes group next + j and runs its first two steps.
   auto prime = [&]() {
-    const int64_t avail = g_end - next;
+    const int64_t avail = q_end - next;
     const int n = avail < S ? (int)avail : S;
     Slot a;
     a.active = a.pending = false;
@@ -534,7 +592,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
       a.active = true;
     }
     next = uniform64(next + n);
-    prefetch = fetch_chunk<L>(P, next + seg, g_end, sl);
+    if (next >= q_end) {  // next chunk of the queue
+      chunk += nwaves;
+      next = chunk * C < P.ngroups ? chunk * C : P.ngroups;
+      q_end = next + C < P.ngroups ? next + C : P.ngroups;
+    }
+    if constexpr (BATCH) {
+      if (next < q_end) batch_advance(P, cursor, next);
+    }
+    prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
     // t = 0: delta = 0, no clamp needed.
     if (a.active) solver_step<L, PM>(P, a, false);
     if (ballot(a.active) != 0) {
@@ -607,7 +673,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
   // and the pool is empty, and gives idle segments standby groups.
   while (true) {
     const bool any_active = ballot(sg.active) != 0;
-    if (!any_active && n_standby == 0 && next >= g_end) break;
+    if (!any_active && n_standby == 0 && next >= q_end) break;
     if (any_active) {
       const bool clamp = ballot(needs_clamp(sg)) != 0;
       if (sg.active) solver_step<L, PM>(P, sg, clamp);
@@ -636,7 +702,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     }
 
     // ---- keep the pool stocked (a batch adds at most S), feed idle segments ------
-    if (n_standby <= kStandby - S && next < g_end) prime();
+    if (n_standby <= kStandby - S && next < q_end) prime();
     const bool idle = !sg.active && !sg.pending;
     if (n_standby > 0 && ballot(idle) != 0) take_standby(idle);
   }
@@ -716,21 +782,21 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 }
 
 // Persistent grid: as many blocks as can be resident at once (LDS and VGPRs set the
-// limit), each wavefront owning one contiguous queue of groups.
+// limit), or fewer for small inputs; the wavefronts deal the chunks round robin.
+constexpr int kChunkBatches = 4;  // chunk = 4 prime batches
 template <int G, int PM>
 hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
-  auto kernel = hqq_solve_kernel<G, PM>;
+  auto kernel = prm.batch ? hqq_solve_kernel<G, PM, true> : hqq_solve_kernel<G, PM, false>;
   int per_cu = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
   constexpr int S = kWave * kLaneElems / G;
   const int64_t resident_waves = (int64_t)cus * per_cu * (kBlock / kWave);
-  int64_t per_wave = (prm.ngroups + resident_waves - 1) / resident_waves;
-  if (per_wave < S) per_wave = S;
-  const int64_t nwaves = (prm.ngroups + per_wave - 1) / per_wave;
+  prm.chunk_groups = kChunkBatches * S;
+  const int64_t nchunks = (prm.ngroups + prm.chunk_groups - 1) / prm.chunk_groups;
+  const int64_t nwaves = nchunks < resident_waves ? nchunks : resident_waves;
   const int64_t blocks = (nwaves + kBlock / kWave - 1) / (kBlock / kWave);
-  prm.groups_per_wave = per_wave;
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, prm);
   return hipGetLastError();
 }

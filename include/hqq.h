@@ -124,6 +124,45 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
                     float p, float beta, float kappa, int iters, void* packed_codes,
                     void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream);
 
+/* One input matrix of hqq_quantize_batch (32 bytes; the same layout is read on
+ * the host and on the device). */
+typedef struct {
+  const void* W_f16;   /* rows x cols binary16 weights, row-major; 16-byte aligned */
+  int64_t rows;        /* >= 0 */
+  int64_t cols;        /* >= 0, a multiple of group_size */
+  int64_t first_group; /* index of the matrix's first group in the output arrays:
+                          the sum of hqq_num_groups(...) over the entries before it */
+} hqq_batch_entry_t;
+
+/*
+ * hqq_quantize_batch -- hqq_quantize (sections 2, 2.1, 2.2 and 4.1 of the page
+ * above, same readings) applied to `count` matrices that share nbits, group_size
+ * and the solver parameters, in one kernel launch.  The inputs are separate
+ * allocations; the outputs of all matrices go to one set of arrays (an arena) in
+ * entry order: the groups of entry i occupy group indices
+ * [first_group_i, first_group_i + hqq_num_groups(rows_i, cols_i, group_size)).
+ * Every output element equals, bit for bit, what hqq_quantize writes for that
+ * matrix alone into arrays that start at its first group.
+ *
+ * entries         host array of `count` entries; read during the call only, for
+ *                 validation.  first_group must be the running sum described above.
+ * entries_device  device copy of the same `count` entries (8-byte aligned), made by
+ *                 the caller; the kernel reads W_f16 and first_group from it, so it
+ *                 must hold exactly what `entries` holds and stay unchanged until the
+ *                 launch has completed.
+ * count           >= 0; 0 (or no group at all) is a valid no-op.
+ * packed_codes    total_groups * group_size * nbits / 8 bytes, 8-byte aligned; the
+ *                 codes of group k start at byte k * group_size * nbits / 8 (the
+ *                 LSB-first bitstream of hqq_quantize, matrix after matrix).
+ * scale_f16, zero_f16  total_groups binary16 values each, 2-byte aligned.
+ * Other arguments, conventions and errors as for hqq_quantize; every entry is
+ * validated before anything is enqueued.
+ */
+int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t* entries_device,
+                       int count, int nbits, int group_size, float p, float beta, float kappa,
+                       int iters, void* packed_codes, void* scale_f16, void* zero_f16,
+                       void* stream);
+
 /*
  * hqq_dequantize -- the inverse quantizer Q^-1(W_q) = s (W_q - z) of section 2,
  * evaluated from the stored binary16 s and z and rounded once (RNE) to binary16.

@@ -130,6 +130,63 @@ def test_dequantize_rejects_before_launch(lib, args, status):
     assert hq.hqq_dequantize(*args, 0) == status
 
 
+def _entries(shapes, g=64, W=FAKE, first=None):
+    arr = (hq.hqq_batch_entry_t * max(len(shapes), 1))()
+    total = 0
+    for i, (r, c) in enumerate(shapes):
+        arr[i].W_f16, arr[i].rows, arr[i].cols = W, r, c
+        arr[i].first_group = total if first is None else first[i]
+        total += r * c // g if c % g == 0 else 0
+    return arr
+
+
+def _qb(entries, count, **kw):
+    a = dict(entries_device=FAKE, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01, iters=20,
+             packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, stream=0)
+    a.update(kw)
+    return hq.hqq_quantize_batch(entries, a.pop("entries_device"), count, **a)
+
+
+@pytest.mark.parametrize("shapes,first,kw,status", [
+    ([(16, 128)], None, dict(nbits=5), hq.HQQ_ERR_UNSUPPORTED),
+    ([(16, 128)], None, dict(group_size=48), hq.HQQ_ERR_UNSUPPORTED),
+    ([(16, 128)], None, dict(p=2.0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(iters=300), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128), (4, 100)], None, {}, hq.HQQ_ERR_INVALID_ARG),           # cols % g
+    ([(16, 128), (-1, 64)], None, {}, hq.HQQ_ERR_INVALID_ARG),           # negative rows
+    ([(16, 128), (4, 64)], [0, 31], {}, hq.HQQ_ERR_INVALID_ARG),         # first_group not the running sum
+    ([(16, 128), (4, 64)], [1, 33], {}, hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(entries_device=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(entries_device=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(packed_codes=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(packed_codes=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_quantize_batch_rejects_before_launch(lib, shapes, first, kw, status):
+    assert _qb(_entries(shapes, first=first), len(shapes), **kw) == status
+
+
+def test_quantize_batch_entry_checks(lib):
+    e = _entries([(16, 128), (8, 64)])
+    e[1].W_f16 = 0
+    assert _qb(e, 2) == hq.HQQ_ERR_INVALID_ARG
+    e[1].W_f16 = FAKE + 8
+    assert _qb(e, 2) == hq.HQQ_ERR_ALIGNMENT
+    assert _qb(e, -1) == hq.HQQ_ERR_INVALID_ARG
+    assert hq.hqq_quantize_batch(None, FAKE, 1, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE,
+                                 0) == hq.HQQ_ERR_INVALID_ARG
+    assert ctypes.sizeof(hq.hqq_batch_entry_t) == 32
+
+
+def test_quantize_batch_empty_is_a_no_op(lib):
+    assert _qb(_entries([]), 0, entries_device=0, packed_codes=0, scale_f16=0,
+               zero_f16=0) == hq.HQQ_OK
+    # entries without a single group: no launch, outputs may be null
+    assert _qb(_entries([(0, 64), (5, 0)], W=0), 2, packed_codes=0, scale_f16=0,
+               zero_f16=0) == hq.HQQ_OK
+
+
 def test_library_does_not_link_the_oracle(lib):
     out = subprocess.run(["nm", "-D", hq.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout

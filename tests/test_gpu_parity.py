@@ -267,3 +267,53 @@ def test_empty_input(hq):
     W = torch.empty((0, 64), dtype=torch.float16, device="cuda")
     q = hq.quantize(W, 4, 64)
     assert q.packed.numel() == 0 and q.scale.numel() == 0
+
+
+# ----------------------------------------------------------- batched launch --
+
+def _assert_same_outputs(x, y):
+    assert torch.equal(x.packed, y.packed)
+    assert torch.equal(x.scale.reshape(-1).view(torch.int16), y.scale.reshape(-1).view(torch.int16))
+    assert torch.equal(x.zero.reshape(-1).view(torch.int16), y.zero.reshape(-1).view(torch.int16))
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32), (2, 16), (3, 128), (8, 64)])
+def test_batch_equals_per_matrix_calls(hq, nbits, g):
+    """One batched launch writes, bit for bit, what one hqq_quantize per matrix writes
+    (the per-matrix path is the one compared with the oracle above): empty entries,
+    entries with fewer groups than a wavefront holds, ragged group counts and entry
+    boundaries inside a wavefront's queue."""
+    shapes = [(37, 5 * g), (0, g), (1, g), (3, g), (1024, 64 * g), (5, 0), (129, 2 * g),
+              (2049, g), (7, 3 * g), (1, g)]
+    _say(f"hqq_quantize_batch vs per-matrix calls, b{nbits} g{g}, {len(shapes)} entries")
+    dist = workloads.WORKLOADS["mlp_11008x4096"].dist
+    Ws = [workloads.generate(r, c, dist, 900 + i, "cuda") if r * c else
+          torch.empty((r, c), dtype=torch.float16, device="cuda") for i, (r, c) in enumerate(shapes)]
+    b = hq.quantize_batch(Ws, nbits, g)
+    torch.cuda.synchronize()
+    assert b.packed.numel() == sum(r * c for r, c in shapes) * nbits // 8
+    for i, W in enumerate(Ws):
+        one = hq.quantize(W, nbits, g)
+        torch.cuda.synchronize()
+        _assert_same_outputs(b.matrix(i), one)
+    # the arena can be reused for the same shapes (same stream)
+    b2 = hq.quantize_batch(Ws, nbits, g, out=b)
+    torch.cuda.synchronize()
+    assert b2 is b
+    _assert_same_outputs(b.matrix(4), hq.quantize(Ws[4], nbits, g))
+
+
+@pytest.mark.parametrize("nbits,g", [(2, 32), (4, 64)])
+def test_batch_llama70b_layer(hq, nbits, g):
+    """The benchmark's call: a 70B-shaped layer (7 matrices) in one launch equals the
+    per-matrix results."""
+    wl = workloads.WORKLOADS["llama70b_stack"]
+    mats = wl.matrices[:7]
+    _say(f"hqq_quantize_batch on 70B layer 0 (7 matrices), b{nbits} g{g}")
+    Ws = [workloads.generate(m.rows, m.cols, wl.dist, m.seed, "cuda") for m in mats]
+    b = hq.quantize_batch(Ws, nbits, g)
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        one = hq.quantize(W, nbits, g)
+        torch.cuda.synchronize()
+        _assert_same_outputs(b.matrix(i), one)
