@@ -5,7 +5,9 @@ layers x {2x 8192x8192, 2x 1024x8192, 2x 28672x8192, 1x 8192x28672}, 68.45 G
 fp16 weights, Student-t nu=4, std 0.015, resident in HBM) once with 2-bit /
 group 32 and once with 4-bit / group 64 (p = 0.7, beta = 1, kappa = 1.01, 20
 iterations, per-group early stop: the settings of section 4.1 of the HQQ page),
-through the C ABI, on one stream.  Inputs are generated on the device before the
+through the C ABI, on one stream: one hqq_quantize_batch launch per setting over
+all 560 matrices (``--per-matrix``: one hqq_quantize launch per matrix instead;
+the outputs are bit-identical).  Inputs are generated on the device before the
 timed region; outputs are written to HBM.
 
 Prints one JSON line (stdout).  The roofline object describes the solver kernel:
@@ -55,9 +57,10 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(launches_per_step: int):
-    """HBM bytes per solver launch from the committed rocprofv3 PMC summary, or None if
-    absent or taken on a different kernel source."""
+def traffic_from_profile(weights_per_launch: float):
+    """HBM bytes per solver launch from the committed rocprofv3 PMC summary (measured
+    bytes per weight, averaged over both settings, times the weights of one launch), or
+    None if absent or taken on a different kernel source."""
     if not os.path.exists(PROFILE_PMC):
         return None
     with open(PROFILE_PMC) as f:
@@ -66,9 +69,8 @@ def traffic_from_profile(launches_per_step: int):
         return None
     if prof.get("workload") != "llama70b_stack":
         return None
-    # the profiled layers repeat the per-layer shapes of the full stack, so the average
-    # bytes per launch carry over to every launch of a full step
-    return round(prof["hbm_bytes_per_launch"])
+    # the profiled layers repeat the per-layer shapes of the full stack
+    return round(prof["hbm_bytes_per_weight"] * weights_per_launch)
 
 
 def _kernel_key(name: str):
@@ -82,7 +84,8 @@ def _kernel_key(name: str):
     return None
 
 
-def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, layers: int):
+def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, layers: int,
+                       weights_per_launch: float):
     """Write the committed rocprofv3 summaries: per-kernel trace statistics and HBM traffic
     per solver launch (FETCH_SIZE, WRITE_SIZE in KiB per dispatch, each scaled by what the
     same counter reads for a plain device copy of known size)."""
@@ -132,12 +135,32 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
         "fetch_calibration": f_fac, "write_calibration": w_fac,
         "solver_launches_profiled": n,
         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
-        "hbm_bytes_per_launch": rd + wr,
+        "hbm_bytes_per_launch": rd + wr, "weights_per_launch": weights_per_launch,
+        "hbm_bytes_per_weight": (rd + wr) / weights_per_launch,
         "sq": extra, "kernel_stats": stats, "command": command,
     }
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, "hqq_solve_llama70b_pmc.json"), "w") as f:
         json.dump(summary, f, indent=1)
+    # the same figures as a short table
+    lines = ["# hqq_solve_kernel on the Llama-2-70B-shaped stack: rocprofv3 summary", "",
+             f"Kernel source sha256[:16] `{summary['kernel_source_sha256_16']}`; counters on the "
+             f"first {layers} layers (one batched launch per setting), kernel trace on the full "
+             "stack.", "", "| kernel | calls | avg duration (ms) |", "|---|---|---|"]
+    for k, v in sorted(stats.items()):
+        lines.append(f"| {k} | {v['calls']} | {v['avg_us'] / 1e3:.3f} |")
+    lines += ["", "| per solver launch (counters) | value |", "|---|---|",
+              f"| HBM read (FETCH_SIZE x {f_fac:.4f}) | {rd / 1e9:.3f} GB |",
+              f"| HBM write (WRITE_SIZE x {w_fac:.4f}) | {wr / 1e9:.3f} GB |",
+              f"| weights per launch | {weights_per_launch / 1e9:.3f} G |",
+              f"| HBM bytes per weight | {(rd + wr) / weights_per_launch:.4f} |"]
+    for k, v in sorted(extra.items()):
+        lines.append(f"| {k}: VALU wave-instr / trans / active lanes | "
+                     f"{v['valu_wave_instr_per_launch']:.4g} / {v['trans_wave_instr_per_launch']:.4g}"
+                     f" / {v['active_lane_fraction']:.3f} |")
+    lines += ["", "Command:", "", "```", command, "```", ""]
+    with open(os.path.join(out_dir, "hqq_solve_llama70b.md"), "w") as f:
+        f.write("\n".join(lines))
     print(json.dumps(summary, indent=1))
 
 
@@ -149,6 +172,9 @@ def main():
     ap.add_argument("--workload", default="llama70b_stack")
     ap.add_argument("--layers", type=int, default=0,
                     help="use only the first L layers (for profiling runs); 0 = all")
+    ap.add_argument("--per-matrix", action="store_true",
+                    help="one hqq_quantize launch per matrix instead of one batched launch "
+                         "per setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -161,8 +187,14 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profiles:
+        import workloads
+        wl = workloads.WORKLOADS[args.workload]
+        mats = list(wl.matrices)[: 7 * args.layers] if args.layers else list(wl.matrices)
+        n_w = sum(m.rows * m.cols for m in mats)
+        per_launch = n_w / (len(mats) if args.per_matrix else 1)
         summarize_profiles(args.summarize_profiles[0], args.summarize_profiles[1],
-                           os.path.join(ROOT, "profiles"), args.profile_command, args.layers)
+                           os.path.join(ROOT, "profiles"), args.profile_command, args.layers,
+                           per_launch)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -219,29 +251,41 @@ def main():
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
 
-    calls = []  # (setting index, args for hqq_quantize)
+    calls = []  # (setting index, entry point, args)
+    tables = []  # host entry tables and their device copies (kept alive)
     for si, (nb, g) in enumerate(settings):
+        if not args.per_matrix:
+            entries, _ = hq.batch_table(Ws, g)
+            dev_table = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8).to(dev)
+            tables.append((entries, dev_table))
+            calls.append((si, lib.hqq_quantize_batch,
+                          (entries, dev_table.data_ptr(), len(Ws), nb, g, solver.p, solver.beta,
+                           solver.kappa, solver.iters, packed.data_ptr(), scale.data_ptr(),
+                           zero.data_ptr(), sh)))
+            continue
         off_p = off_g = 0
         for W in Ws:
             r, c = W.shape
-            calls.append((si, (W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
-                               solver.iters, packed.data_ptr() + off_p,
-                               scale.data_ptr() + 2 * off_g, zero.data_ptr() + 2 * off_g, sh)))
+            calls.append((si, lib.hqq_quantize,
+                          (W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
+                           solver.iters, packed.data_ptr() + off_p,
+                           scale.data_ptr() + 2 * off_g, zero.data_ptr() + 2 * off_g, sh)))
             off_p += r * c * nb // 8
             off_g += r * c // g
+    torch.cuda.synchronize()
     launches_per_step = len(calls)
 
     def step(events=None):
         cur = -1
-        for si, a in calls:
+        for si, fn, a in calls:
             if events is not None and si != cur:
                 events[si][0].record(stream)
                 if cur >= 0:
                     events[cur][1].record(stream)
                 cur = si
-            st = lib.hqq_quantize(*a)
+            st = fn(*a)
             if st != 0:
-                raise RuntimeError(f"hqq_quantize failed: {hq.hqq_status_string(st)}")
+                raise RuntimeError(f"quantize failed: {hq.hqq_status_string(st)}")
         if events is not None:
             events[cur][1].record(stream)
 
@@ -324,7 +368,7 @@ def main():
     avg_launch_s = total_ms * 1e-3 / (args.steps * launches_per_step)
     achieved = ops_step / launches_per_step / avg_launch_s  # lane-ops/s
     bytes_step = sum(n_weights * (2 + nb / 8 + 4 / g) for nb, g in settings)
-    traffic = traffic_from_profile(launches_per_step)
+    traffic = traffic_from_profile(n_weights * len(settings) / launches_per_step)
 
     # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
     cpu = None
@@ -382,6 +426,7 @@ def main():
             "settings": [f"b{nb}g{g}" for nb, g in settings],
             "p": solver.p, "beta": solver.beta, "kappa": solver.kappa, "iters": solver.iters,
             "early_stop": "per group", "launches_per_step": launches_per_step,
+            "entry_point": "hqq_quantize" if args.per_matrix else "hqq_quantize_batch",
         },
         "roofline": {
             "bound": "alu",
