@@ -346,12 +346,12 @@ __device__ __forceinline__ void load_u(const float* slot_u, int sl, float (&u)[k
 
 // One evaluation of the lane's 8 weights at x = u + delta: the segment's lp error
 // (code units) and code sum.  CLAMP = false is the exact shortcut for |delta| < 1/2.
-template <int L, int PM, bool CLAMP>
+template <int L, int PM, bool CLAMP, bool ZERO = false>
 __device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float delta, float qmax,
                                            float p, float& e, float& sq) {
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
-    const float x = u[k] + delta;
+    const float x = ZERO ? u[k] : u[k] + delta;  // ZERO: delta == 0 (x = u + 0 = u exactly)
     float q = __builtin_rintf(x);
     if constexpr (CLAMP) q = __builtin_amdgcn_fmed3f(q, 0.f, qmax);
     const float rc = x - q;
@@ -383,12 +383,15 @@ __device__ __forceinline__ bool needs_clamp(const Slot& q) { return q.active && 
 // One step of the solver for an active group: evaluation at the current z (codes,
 // residual, lp error), the early-stop test of section 4.1, and unless the group
 // stops, the sp1 shrink (only where it can be non-zero) and the sp2 mean.
-template <int L, int PM>
+// FIRST: the step at t = 0 (delta = 0, no clamp needed).
+template <int L, int PM, bool FIRST = false>
 __device__ __forceinline__ void solver_step(const SolveParams& P, Slot& q, bool clamp) {
   constexpr float kInvG = 1.0f / (float)(L * kLaneElems);
   const float qmax = P.qmax;
   float e, sq;
-  if (clamp) {
+  if constexpr (FIRST) {
+    eval_group<L, PM, false, true>(q.u, 0.f, qmax, P.p, e, sq);
+  } else if (clamp) {
     eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
   } else {
     eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
@@ -449,39 +452,43 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
                                             float z0, float bd, float e0, float best_e,
                                             int t_star) {
   const float qmax = P.qmax;
-  uint32_t c[kLaneElems];
+  float q[kLaneElems];  // codes as fp32 integers in [0, qmax]
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
-    const float q = __builtin_rintf(u[k] + bd);
-    c[k] = (uint32_t)(CLAMP ? __builtin_amdgcn_fmed3f(q, 0.f, qmax) : q);
+    q[k] = __builtin_rintf(u[k] + bd);
+    if (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
   }
+  // Packing: sum_k q_k 2^(nbits k) over up to 24 bits is an exact fp32 integer, so the
+  // fields are assembled with FMAs and converted once.
+  auto horner = [&](int k0, int n, float radix) {
+    float acc = q[k0 + n - 1];
+#pragma unroll
+    for (int k = n - 2; k >= 0; --k) acc = __builtin_fmaf(acc, radix, q[k0 + k]);
+    return (uint32_t)acc;
+  };
   const int64_t chunk = gi * L + sl;  // index of this lane's 8 elements
   switch (P.nbits) {
     case 4: {
-      uint32_t v = 0;
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (4 * k);
+      const uint32_t v = horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16);
       reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
       break;
     }
     case 2: {
-      uint32_t v = 0;
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (2 * k);
-      reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)v;
+      reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)horner(0, 8, 4.f);
       break;
     }
     case 8: {
-      uint2 v;
-      v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      uint2 v = make_uint2(0u, 0u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k], (uint32_t)k, v.x);
+        v.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 4], (uint32_t)k, v.y);
+      }
       reinterpret_cast<uint2*>(P.packed)[chunk] = v;
       break;
     }
     default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
-      uint32_t v = 0;
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) v |= c[k] << (3 * k);
+      const uint32_t v = horner(0, 8, 8.f);
       uint8_t* dst = P.packed + chunk * 3;
       dst[0] = (uint8_t)v;
       dst[1] = (uint8_t)(v >> 8);
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     }
     prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
     // t = 0: delta = 0, no clamp needed.
-    if (a.active) solver_step<L, PM>(P, a, false);
+    if (a.active) solver_step<L, PM, true>(P, a, false);
     if (ballot(a.active) != 0) {
       const bool clamp = ballot(needs_clamp(a)) != 0;
       if (a.active) solver_step<L, PM>(P, a, clamp);
