@@ -171,6 +171,14 @@ struct GroupInit {
   bool may_shrink;  // the shrink can be non-zero at some step (|r| <= max - min always)
 };
 
+// Values every lane of the wave computes identically, kept in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // The entry of a batched launch that holds the wave's next group: its index, its
 // group range [first, end) and its weights.  Wave-uniform.
 struct BatchCursor {
@@ -189,45 +197,38 @@ __device__ __forceinline__ BatchCursor batch_cursor(const SolveParams& P, int64_
     else hi = mid - 1;
   }
   BatchCursor c;
-  c.m = lo;
-  c.first = P.batch[lo].first_group;
-  c.end = lo + 1 < P.batch_count ? P.batch[lo + 1].first_group : P.ngroups;
-  c.W = P.batch[lo].W;
+  c.m = uniform(lo);
+  c.first = uniform64(P.batch[c.m].first_group);
+  c.end = uniform64(c.m + 1 < P.batch_count ? P.batch[c.m + 1].first_group : P.ngroups);
+  c.W = reinterpret_cast<const uint4*>(uniform64(reinterpret_cast<int64_t>(P.batch[c.m].W)));
   return c;
 }
 
 // Moves the cursor forward to the entry holding group g (g < number of groups).
 __device__ __forceinline__ void batch_advance(const SolveParams& P, BatchCursor& c, int64_t g) {
   while (g >= c.end) {
-    ++c.m;
+    c.m = uniform(c.m + 1);
     c.first = c.end;
-    c.W = P.batch[c.m].W;
-    c.end = c.m + 1 < P.batch_count ? P.batch[c.m + 1].first_group : P.ngroups;
+    c.W = reinterpret_cast<const uint4*>(uniform64(reinterpret_cast<int64_t>(P.batch[c.m].W)));
+    c.end = uniform64(c.m + 1 < P.batch_count ? P.batch[c.m + 1].first_group : P.ngroups);
   }
 }
 
 // The lane's 16-byte chunk of group `gi`.  Past the end of the wave's queue the
 // lane reads the queue's last group instead (a valid address; the value is unused),
 // so the load is unconditional and its registers need no other initialisation.  In a
-// batched launch the chunk comes from the entry holding the group: the cursor's,
-// or for segments past it (only near an entry boundary) a later one.
+// batched launch a prime batch never extends past the cursor's entry, so the chunk
+// comes from that entry (past its end or the queue's, the lane reads the entry's
+// first group, a valid address whose value is unused).
 template <int L, bool BATCH>
 __device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, const BatchCursor& c,
                                              int64_t gi, int64_t g_end, int sl) {
   if constexpr (!BATCH) {
     return P.W[(gi < g_end ? gi : g_end - 1) * L + sl];
   } else {
-    // Past the queue the lane reads the cursor's first group (its entry is never empty).
-    const int64_t g = gi < g_end ? gi : c.first;
-    const uint4* W = c.W;
-    int64_t first = c.first;
-    if (g >= c.end) {
-      int m = c.m + 1;
-      while (m + 1 < P.batch_count && g >= P.batch[m + 1].first_group) ++m;
-      W = P.batch[m].W;
-      first = P.batch[m].first_group;
-    }
-    return W[(g - first) * L + sl];
+    const int64_t limit = g_end < c.end ? g_end : c.end;
+    const int64_t g = gi < limit ? gi : c.first;
+    return c.W[(g - c.first) * L + sl];
   }
 }
 
@@ -308,23 +309,18 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
+  // Wavefronts per SIMD the kernel is compiled for (VGPR budget): seven at G = 32,
+  // where the extra wavefront outweighs the smaller pool, six otherwise (measured).
+  static constexpr int kWavesPerSimd = G == 32 ? 7 : 6;
   // A prime batch adds up to S groups to the pool, a hand-over up to S to the ring.
-  // The pool holds 1.5 S groups (S for G = 16, to stay within the LDS of six
-  // wavefronts per SIMD), so it is restocked before it runs dry.
-  static constexpr int kStandby = G == 16 ? S : S + S / 2;
+  // The pool holds 1.5 S groups, so it is restocked before it runs dry, where the LDS
+  // of kWavesPerSimd wavefronts allows (G = 64, 128); S otherwise.
+  static constexpr int kStandby = (G == 16 || G == 32) ? S : S + S / 2;
   static constexpr int kDone = S;
   float u[kWavesPerBlock][kStandby + kDone][G];
   uint4 standby_hdr[kWavesPerBlock][kStandby][3];
   uint4 done_hdr[kWavesPerBlock][kDone][2];
 };
-
-// Values every lane of the wave computes identically, kept in scalar registers.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -445,8 +441,8 @@ __device__ __forceinline__ void solver_step(const SolveParams& P, Slot& q, bool 
 // Codes at the accepted z, packed into the LSB-first bitstream, and the group's
 // binary16 s and z (plus the optional fp32 and error outputs).  Called by the L lanes
 // of a segment; lane sl writes the codes of its 8 elements.  CLAMP = false is exact
-// when |bd| < 1/2 (the argument of needs_clamp).
-template <int L, int PM, bool CLAMP>
+// when |bd| < 1/2 (the argument of needs_clamp); ZERO: bd == 0 (codes rint(u)).
+template <int L, int PM, bool CLAMP, bool ZERO = false>
 __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
                                             const float (&u)[kLaneElems], int64_t gi, float gs,
                                             float z0, float bd, float e0, float best_e,
@@ -455,7 +451,7 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
   float q[kLaneElems];  // codes as fp32 integers in [0, qmax]
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
-    q[k] = __builtin_rintf(u[k] + bd);
+    q[k] = __builtin_rintf(ZERO ? u[k] : u[k] + bd);
     if (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
   }
   // Packing: sum_k q_k 2^(nbits k) over up to 24 bits is an exact fp32 integer, so the
@@ -511,13 +507,16 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
   }
 }
 
-// write_group with the clamp only where some written group of the wave needs it.
-template <int L, int PM>
+// write_group with the clamp only where some written group of the wave needs it;
+// TRY_ZERO adds the shortcut for bd == 0 in every written group.
+template <int L, int PM, bool TRY_ZERO = false>
 __device__ __forceinline__ void write_group_any(const SolveParams& P, bool write, int sl,
                                                 const float (&u)[kLaneElems], int64_t gi, float gs,
                                                 float z0, float bd, float e0, float best_e,
                                                 int t_star) {
-  if (ballot(write && far_delta(bd)) != 0) {
+  if (TRY_ZERO && ballot(write && bd != 0.f) == 0) {
+    if (write) write_group<L, PM, false, true>(P, sl, u, gi, gs, z0, 0.f, e0, best_e, t_star);
+  } else if (ballot(write && far_delta(bd)) != 0) {
     if (write) write_group<L, PM, true>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
   } else {
     if (write) write_group<L, PM, false>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
@@ -533,7 +532,7 @@ __device__ __forceinline__ void write_group_any(const SolveParams& P, bool write
 // exactly the same instruction sequence whatever its batch or slot, so results do
 // not depend on the schedule.
 template <int G, int PM, bool BATCH>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void hqq_solve_kernel(const SolveParams P) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds<G>::kWavesPerSimd))) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
   constexpr int S = kWave / L;       // segments per wavefront
   constexpr int kStandby = SolveLds<G>::kStandby;  // standby-pool capacity
@@ -581,7 +580,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
 
   // Dense batch: segment j initializes group next + j and runs its first two steps.
   auto prime = [&]() {
-    const int64_t avail = q_end - next;
+    // In a batched launch the batch stops at the end of the cursor's entry.
+    const int64_t avail = (BATCH && cursor.end < q_end ? cursor.end : q_end) - next;
     const int n = avail < S ? (int)avail : S;
     Slot a;
     a.active = a.pending = false;
@@ -614,8 +614,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
       const bool clamp = ballot(needs_clamp(a)) != 0;
       if (a.active) solver_step<L, PM>(P, a, clamp);
     }
-    write_group_any<L, PM>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0, a.best_e,
-                           a.t_star);
+    // Groups stopping here have t* = 0 (they stopped at t = 1) unless iters == 1.
+    write_group_any<L, PM, true>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0,
+                                 a.best_e, a.t_star);
     const uint64_t m = ballot(a.active);
     if (a.active) {
       const int slot = n_standby + lanes_below(m) / L;  // n_standby <= kStandby - S
