@@ -75,6 +75,10 @@ def _load():
     lib.oracle_hqq_quantize.argtypes = [P, I64, I64, I, I, D, D, D, I, I, D] + [P] * 9
     lib.oracle_hqq_dequantize.restype = I
     lib.oracle_hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P]
+    lib.oracle_meta_quantize.restype = I64
+    lib.oracle_meta_quantize.argtypes = [P, I64, I64, P, P, P]
+    lib.oracle_meta_dequantize.restype = I
+    lib.oracle_meta_dequantize.argtypes = [P, P, P, I64, I64, P]
     _lib = lib
     return lib
 
@@ -274,4 +278,40 @@ def hqq_dequantize(packed: np.ndarray, scale_f16: np.ndarray, zero_f16: np.ndarr
                                        nbits, group_size, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_hqq_dequantize rejected its arguments")
+    return out
+
+
+def meta_groups(n: int, group: int) -> int:
+    """Number of meta groups: 1 for group = 0 (one group of all n values), else ceil(n/group)."""
+    if n == 0:
+        return 0
+    return 1 if group == 0 else -(-n // group)
+
+
+def meta_quantize(values_f16: np.ndarray, group: int):
+    """8-bit min-max meta quantization (hqq_oracle.c, oracle_meta_quantize) of binary16 bit
+    patterns in groups of `group` (0 = one group).  Returns (codes u8, scale16, offset16)."""
+    v = np.ascontiguousarray(values_f16).view(np.uint16).ravel()
+    n = v.size
+    ng = meta_groups(n, group)
+    codes = np.empty(n, np.uint8)
+    sc = np.empty(max(ng, 1), np.uint16)
+    off = np.empty(max(ng, 1), np.uint16)
+    rc = _load().oracle_meta_quantize(_ptr(v), n, group, _ptr(codes), _ptr(sc), _ptr(off))
+    if rc != ng:
+        raise ValueError("oracle_meta_quantize rejected its arguments")
+    return codes, sc[:ng], off[:ng]
+
+
+def meta_dequantize(codes: np.ndarray, scale16: np.ndarray, offset16: np.ndarray,
+                    group: int) -> np.ndarray:
+    """binary16 bit patterns of offset + scale * code, rounded once from fp64."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).ravel()
+    sc = np.ascontiguousarray(scale16).view(np.uint16).ravel()
+    off = np.ascontiguousarray(offset16).view(np.uint16).ravel()
+    out = np.empty(codes.size, np.uint16)
+    rc = _load().oracle_meta_dequantize(_ptr(codes), _ptr(sc), _ptr(off), codes.size, group,
+                                        _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_meta_dequantize rejected its arguments")
     return out

@@ -38,6 +38,15 @@
  *   storage  codes packed as an LSB-first little-endian bitstream over the
  *            row-major element order; s and z stored as IEEE binary16 (RNE
  *            from fp64, no intermediate fp32 rounding).
+ *   meta     section 4.1 quantizes the zero-points to 8 bits without grouping
+ *            or optimization, and its table note the scales to 8 bits in groups
+ *            of 128: affine min-max round-to-nearest (no solver) over the stored
+ *            binary16 values, one group per array for the zero-points, runs of
+ *            128 consecutive values (row-major group order, shorter last run) for
+ *            the scales; the group min and max map to codes 0 and 255, the code
+ *            is decided on the binary32 rounding of the fp64 quotient (as for the
+ *            weight codes); a constant group takes scale 1, codes 0; the meta
+ *            scale and offset are stored as binary16.
  *
  * Arithmetic: fp64, one thread, scalar loops, sums in index order.  The binary16
  * conversions are written out from the IEEE 754 definition (no compiler
@@ -343,6 +352,65 @@ int oracle_hqq_dequantize(const uint8_t* packed, const uint16_t* scale_f16,
     double s = oracle_f16_to_f64(scale_f16[gi]);
     double z = oracle_f16_to_f64(zero_f16[gi]);
     W_out_f16[i] = oracle_f64_to_f16(s * ((double)c - z));
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Meta quantization of the per-group s or z (section 4.1 and its table note): */
+/* 8-bit affine min-max round-to-nearest, no solver.                          */
+/* ------------------------------------------------------------------------- */
+
+/* Groups of `group` consecutive values (group = 0: one group of all n; the last
+ * group may be shorter).  Per group: mn, mx over the binary16 values; d = mx - mn;
+ * if d > 0 the code of v is clamp(nearbyint(binary32(((v - mn) * 255) / d)), 0, 255)
+ * (v - mn and the product are exact in fp64, the quotient is rounded once) and the
+ * meta scale is d / 255; a constant group has codes 0 and meta scale 1.  The meta
+ * scale is stored as binary16 (RNE from fp64), the offset mn exactly.  Returns the
+ * number of groups, or -1 for invalid arguments. */
+int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, uint8_t* codes,
+                             uint16_t* scale16, uint16_t* offset16) {
+  if (n < 0 || group < 0) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  const int64_t gs = group == 0 ? n : group;
+  int64_t ng = 0;
+  for (int64_t g0 = 0; g0 < n; g0 += gs, ++ng) {
+    const int64_t g1 = g0 + gs < n ? g0 + gs : n;
+    double mn = oracle_f16_to_f64(values[g0]), mx = mn;
+    for (int64_t i = g0 + 1; i < g1; ++i) {
+      const double v = oracle_f16_to_f64(values[i]);
+      if (v < mn) mn = v;
+      if (v > mx) mx = v;
+    }
+    const double d = mx - mn;
+    for (int64_t i = g0; i < g1; ++i) {
+      double c = 0.0;
+      if (d > 0.0) {
+        const double u = ((oracle_f16_to_f64(values[i]) - mn) * 255.0) / d;
+        c = nearbyint((double)(float)u);
+        if (c < 0.0) c = 0.0;
+        if (c > 255.0) c = 255.0;
+      }
+      codes[i] = (uint8_t)c;
+    }
+    scale16[ng] = oracle_f64_to_f16(d > 0.0 ? d / 255.0 : 1.0);
+    offset16[ng] = oracle_f64_to_f16(mn);
+  }
+  return ng;
+}
+
+/* value = offset + scale * code from the stored binary16 meta scale and offset,
+ * exact in fp64 (an 11-bit significand times an 8-bit integer, plus a binary16),
+ * rounded once to binary16. */
+int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,
+                           const uint16_t* offset16, int64_t n, int64_t group, uint16_t* out16) {
+  if (n < 0 || group < 0) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  const int64_t gs = group == 0 ? (n > 0 ? n : 1) : group;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t gi = i / gs;
+    out16[i] = oracle_f64_to_f16(oracle_f16_to_f64(offset16[gi]) +
+                                 oracle_f16_to_f64(scale16[gi]) * (double)codes[i]);
   }
   return 0;
 }

@@ -54,4 +54,9 @@ int oracle_hqq_quantize(const uint16_t* W_f16, int64_t rows, int64_t cols, int n
 int oracle_hqq_dequantize(const uint8_t* packed, const uint16_t* scale_f16,
                           const uint16_t* zero_f16, int64_t rows, int64_t cols, int nbits,
                           int group_size, uint16_t* W_out_f16);
+
+int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, uint8_t* codes,
+                             uint16_t* scale16, uint16_t* offset16);
+int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,
+                           const uint16_t* offset16, int64_t n, int64_t group, uint16_t* out16);
 #endif

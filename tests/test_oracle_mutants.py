@@ -43,6 +43,20 @@ MUTANTS = {
                                  "const uint16_t* src = W_f16 + ((gi % rows) * cols + "
                                  "(gi / rows) * group_size);"),
     "dequant adds z": ("s * ((double)c - z)", "s * ((double)c + z)"),
+    "meta 256 levels": ("* 255.0) / d;", "* 256.0) / d;"),
+    "meta round half away from zero": ("c = nearbyint((double)(float)u);",
+                                       "c = round((double)(float)u);"),
+    "meta decision in fp64": ("c = nearbyint((double)(float)u);", "c = nearbyint(u);"),
+    "meta offset is the max": ("offset16[ng] = oracle_f64_to_f16(mn);",
+                               "offset16[ng] = oracle_f64_to_f16(mx);"),
+    "meta scale over 256": ("d > 0.0 ? d / 255.0 : 1.0", "d > 0.0 ? d / 256.0 : 1.0"),
+    "meta constant group scale 0": ("d > 0.0 ? d / 255.0 : 1.0", "d / 255.0"),
+    "meta min-max skips last element": ("for (int64_t i = g0 + 1; i < g1; ++i) {",
+                                        "for (int64_t i = g0 + 1; i < g1 - 1; ++i) {"),
+    "meta dequant subtracts": ("oracle_f16_to_f64(offset16[gi]) +",
+                               "oracle_f16_to_f64(offset16[gi]) -"),
+    "meta dequant group off by one": ("const int64_t gi = i / gs;",
+                                      "const int64_t gi = (i + 1) / gs;"),
 }
 
 
@@ -58,6 +72,6 @@ def test_pins_catch_mutant(name, tmp_path):
     src_path.write_text(src.replace(before, after, 1))
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
-                       timeout=600, env=env)
+                        "tests/test_oracle_pins.py", "tests/test_oracle_meta_pins.py"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode != 0, f"mutant {name!r} survived the pins:\n{r.stdout[-2000:]}"
