@@ -46,7 +46,7 @@
  *            the scales; the group min and max map to codes 0 and 255, the code
  *            is decided on the binary32 rounding of the fp64 quotient (as for the
  *            weight codes); a constant group takes scale 1, codes 0; the meta
- *            scale and offset are stored as binary16.
+ *            scale and offset are stored as binary16, a zero offset as +0.
  *
  * Arithmetic: fp64, one thread, scalar loops, sums in index order.  The binary16
  * conversions are written out from the IEEE 754 definition (no compiler
@@ -382,6 +382,7 @@ int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, u
       if (v < mn) mn = v;
       if (v > mx) mx = v;
     }
+    if (mn == 0.0) mn = 0.0;  /* a zero minimum is stored as +0 (the order of +-0 is not a min) */
     const double d = mx - mn;
     for (int64_t i = g0; i < g1; ++i) {
       double c = 0.0;

@@ -159,3 +159,11 @@ def test_code_decided_in_binary32():
     v = f16([-1.3779296875, 286.25, 214.625, -1.009765625, 170.625, 166.25])
     codes, _, _ = oracle.meta_quantize(v.view(np.uint16), 3)
     assert codes.tolist() == [0, 255, 192, 0, 255, 248]
+
+
+def test_zero_minimum_is_stored_as_plus_zero():
+    # zero-point arrays hold both -0 (z = -(0 * 1/s)) and +0; min(+0, -0) has no order, so
+    # the offset of a group whose minimum is zero is +0 whichever comes first
+    for vals in ([-0.0, 0.0, 1.0], [0.0, -0.0, 1.0], [-0.0, 2.0, -0.0]):
+        _, _, off = oracle.meta_quantize(f16(vals).view(np.uint16), 0)
+        assert off[0] == 0
