@@ -27,6 +27,7 @@ HQQ_ERR_LAUNCH = 4
 
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
+                    "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
 
 
@@ -68,6 +69,12 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_batch.restype = I
     lib.hqq_quantize_batch.argtypes = [ctypes.POINTER(hqq_batch_entry_t), P, I, I, I, F, F, F, I,
                                        P, P, P, P]
+    lib.hqq_meta_quantize.restype = I
+    lib.hqq_meta_quantize.argtypes = [P, I64, I64, P, P, P, P, P]
+    lib.hqq_meta_dequantize.restype = I
+    lib.hqq_meta_dequantize.argtypes = [P, P, P, I64, I64, P, P]
+    lib.hqq_meta_groups.restype = I64
+    lib.hqq_meta_groups.argtypes = [I64, I64]
     lib.hqq_dequantize.restype = I
     lib.hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
     lib.hqq_packed_bytes.restype = I64
@@ -116,6 +123,22 @@ def hqq_quantize_batch(entries, entries_device: int, count: int, nbits: int, gro
     return load_library().hqq_quantize_batch(entries, entries_device, count, nbits, group_size, p,
                                              beta, kappa, iters, packed_codes, scale_f16, zero_f16,
                                              stream)
+
+
+def hqq_meta_groups(n: int, meta_group: int) -> int:
+    return load_library().hqq_meta_groups(n, meta_group)
+
+
+def hqq_meta_quantize(values_f16: int, n: int, meta_group: int, codes_u8: int, mscale_f16: int,
+                      moffset_f16: int, workspace: int = 0, stream: int = 0) -> int:
+    return load_library().hqq_meta_quantize(values_f16, n, meta_group, codes_u8, mscale_f16,
+                                            moffset_f16, workspace, stream)
+
+
+def hqq_meta_dequantize(codes_u8: int, mscale_f16: int, moffset_f16: int, n: int,
+                        meta_group: int, values_f16: int, stream: int = 0) -> int:
+    return load_library().hqq_meta_dequantize(codes_u8, mscale_f16, moffset_f16, n, meta_group,
+                                              values_f16, stream)
 
 
 def hqq_dequantize(packed_codes: int, scale_f16: int, zero_f16: int, rows: int, cols: int,
@@ -271,6 +294,54 @@ def quantize_batch(Ws, nbits: int, group_size: int, p: float = 0.7, beta: float 
                             _addr(out.scale), _addr(out.zero), _stream_handle(stream))
     if st != HQQ_OK:
         raise HQQError(st, "hqq_quantize_batch")
+    return out
+
+
+@dataclass
+class MetaQuantized:
+    """8-bit meta quantization of a per-group array (codes, binary16 meta scale and offset)."""
+    codes: "torch.Tensor"             # uint8, n
+    scale: "torch.Tensor"             # fp16, hqq_meta_groups(n, meta_group)
+    offset: "torch.Tensor"            # fp16, hqq_meta_groups(n, meta_group)
+    n: int
+    meta_group: int
+    workspace: Optional["torch.Tensor"] = None  # kept alive until the launch has completed
+
+
+def meta_quantize(values, meta_group: int, workspace=None, stream=None) -> MetaQuantized:
+    """8-bit meta quantization of a contiguous fp16 CUDA tensor (e.g. ``QuantizedWeight.zero``
+    with meta_group 0, ``QuantizedWeight.scale`` with meta_group 128)."""
+    import torch
+    if values.dtype != torch.float16 or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous float16 CUDA tensor")
+    n = values.numel()
+    ng = hqq_meta_groups(n, meta_group)
+    if ng < 0:
+        raise HQQError(HQQ_ERR_INVALID_ARG, "meta_quantize")
+    dev = values.device
+    out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
+                        scale=torch.empty(ng, dtype=torch.float16, device=dev),
+                        offset=torch.empty(ng, dtype=torch.float16, device=dev),
+                        n=n, meta_group=meta_group)
+    if meta_group == 0 and workspace is None:
+        workspace = torch.empty(2, dtype=torch.int32, device=dev)
+    out.workspace = workspace
+    st = hqq_meta_quantize(_addr(values), n, meta_group, _addr(out.codes), _addr(out.scale),
+                           _addr(out.offset), _addr(workspace), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_meta_quantize")
+    return out
+
+
+def meta_dequantize(m: MetaQuantized, out=None, stream=None):
+    """offset + scale * code as a flat fp16 tensor of n values (single rounding)."""
+    import torch
+    if out is None:
+        out = torch.empty(m.n, dtype=torch.float16, device=m.codes.device)
+    st = hqq_meta_dequantize(_addr(m.codes), _addr(m.scale), _addr(m.offset), m.n, m.meta_group,
+                             _addr(out), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_meta_dequantize")
     return out
 
 

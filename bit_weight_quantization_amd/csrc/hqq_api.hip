@@ -12,6 +12,7 @@
 namespace {
 
 constexpr int kMaxIters = 255;
+constexpr int64_t kMaxMetaGroup = 1 << 20;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -233,6 +234,49 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
   const int64_t cap = (int64_t)cus * 16;
   if (blocks > cap) blocks = cap;
   hipError_t err = hqq::launch_dequant(prm, (int)blocks, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int64_t hqq_meta_groups(int64_t n, int64_t meta_group) {
+  if (n < 0 || meta_group < 0 || meta_group > kMaxMetaGroup) return -1;
+  if (n == 0) return 0;
+  return meta_group == 0 ? 1 : (n + meta_group - 1) / meta_group;
+}
+
+int hqq_meta_quantize(const void* values_f16, int64_t n, int64_t meta_group, void* codes_u8,
+                      void* mscale_f16, void* moffset_f16, void* workspace, void* stream) {
+  const int64_t ng = hqq_meta_groups(n, meta_group);
+  if (ng < 0) return HQQ_ERR_INVALID_ARG;
+  if (ng > (int64_t)INT32_MAX) return HQQ_ERR_INVALID_ARG;  // grid size
+  if (n == 0) return HQQ_OK;
+  if (!values_f16 || !codes_u8 || !mscale_f16 || !moffset_f16) return HQQ_ERR_INVALID_ARG;
+  if (meta_group == 0 && !workspace) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(values_f16, 2) || !aligned(mscale_f16, 2) || !aligned(moffset_f16, 2))
+    return HQQ_ERR_ALIGNMENT;
+  if (meta_group == 0 && !aligned(workspace, 4)) return HQQ_ERR_ALIGNMENT;
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_meta_quantize(
+      static_cast<const uint16_t*>(values_f16), n, meta_group, static_cast<uint8_t*>(codes_u8),
+      static_cast<uint16_t*>(mscale_f16), static_cast<uint16_t*>(moffset_f16),
+      static_cast<uint32_t*>(workspace), cus, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int hqq_meta_dequantize(const void* codes_u8, const void* mscale_f16, const void* moffset_f16,
+                        int64_t n, int64_t meta_group, void* values_f16, void* stream) {
+  const int64_t ng = hqq_meta_groups(n, meta_group);
+  if (ng < 0) return HQQ_ERR_INVALID_ARG;
+  if (n == 0) return HQQ_OK;
+  if (!codes_u8 || !mscale_f16 || !moffset_f16 || !values_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(values_f16, 2) || !aligned(mscale_f16, 2) || !aligned(moffset_f16, 2))
+    return HQQ_ERR_ALIGNMENT;
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_meta_dequantize(
+      static_cast<const uint8_t*>(codes_u8), static_cast<const uint16_t*>(mscale_f16),
+      static_cast<const uint16_t*>(moffset_f16), n, meta_group, static_cast<uint16_t*>(values_f16),
+      cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 

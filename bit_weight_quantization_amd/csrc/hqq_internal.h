@@ -61,6 +61,13 @@ struct DequantParams {
 hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream);  // batched when prm.batch != nullptr
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
+// Meta quantization (M = 0: one group of all n values; workspace: 2 words, used then).
+hipError_t launch_meta_quantize(const uint16_t* values, int64_t n, int64_t M, uint8_t* codes,
+                                uint16_t* mscale, uint16_t* moffset, uint32_t* workspace,
+                                int cus, hipStream_t stream);
+hipError_t launch_meta_dequantize(const uint8_t* codes, const uint16_t* mscale,
+                                  const uint16_t* moffset, int64_t n, int64_t M, uint16_t* out,
+                                  int cus, hipStream_t stream);
 
 // Segment geometry shared with the host grid sizing: each lane holds 8 weights.
 constexpr int kLaneElems = 8;

@@ -174,6 +174,48 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
                    int64_t rows, int64_t cols, int nbits, int group_size, void* W_out_f16,
                    void* stream);
 
+/*
+ * hqq_meta_quantize -- 8-bit quantization of a per-group meta array: section 4.1
+ * of the page stores the zero-points in 8 bits without grouping or optimization,
+ * and the note under its Llama-2 table quantizes the scales to 8 bits in groups of
+ * 128.  Reading: affine min-max round-to-nearest (no solver) over the binary16
+ * values, in groups of meta_group consecutive values; per group, with mn and mx its
+ * minimum and maximum and d = mx - mn:
+ *   code  = clamp(round_half_even(binary32(((v - mn) * 255) / d)), 0, 255)
+ *           (the fp64 quotient rounded once to binary32, as for the weight codes),
+ *   scale = binary16(d / 255) (nearest even), offset = mn (+0 for a zero minimum);
+ * a constant group has codes 0 and scale 1.  The value is recovered as
+ * offset + scale * code (hqq_meta_dequantize).
+ *
+ * values_f16   n binary16 values, e.g. the zero_f16 (meta_group 0) or scale_f16
+ *              (meta_group 128) output of hqq_quantize; 2-byte aligned.
+ * n            >= 0; 0 is a valid no-op.
+ * meta_group   0: one group of all n values; otherwise 1 .. 2^20 consecutive values
+ *              per group (the last group may be shorter).
+ * codes_u8     n bytes.
+ * mscale_f16, moffset_f16  hqq_meta_groups(n, meta_group) binary16 values each,
+ *              2-byte aligned.
+ * workspace    meta_group 0 only (ignored otherwise, may be NULL): 8 bytes of device
+ *              memory, 4-byte aligned, owned by the caller, that the call uses for
+ *              the array's minimum and maximum; the library initializes it on
+ *              `stream` (no allocation, no memset); it must not be shared by calls
+ *              that may run at the same time.
+ * Conventions and errors as for hqq_quantize.
+ */
+int hqq_meta_quantize(const void* values_f16, int64_t n, int64_t meta_group, void* codes_u8,
+                      void* mscale_f16, void* moffset_f16, void* workspace, void* stream);
+
+/* hqq_meta_dequantize -- offset + scale * code of hqq_meta_quantize's output,
+ * rounded once to binary16 (the exact value is representable in fp64 and the
+ * result equals its nearest-even binary16).  values_f16: n binary16 outputs,
+ * 2-byte aligned; other arguments as above. */
+int hqq_meta_dequantize(const void* codes_u8, const void* mscale_f16, const void* moffset_f16,
+                        int64_t n, int64_t meta_group, void* values_f16, void* stream);
+
+/* Number of meta groups: 0 for n == 0, 1 for meta_group == 0, else
+ * ceil(n / meta_group).  -1 for invalid arguments. */
+int64_t hqq_meta_groups(int64_t n, int64_t meta_group);
+
 /* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
  * shapes).  Returns -1 for invalid arguments or overflow. */
 int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);

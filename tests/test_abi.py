@@ -187,6 +187,43 @@ def test_quantize_batch_empty_is_a_no_op(lib):
                zero_f16=0) == hq.HQQ_OK
 
 
+def test_meta_groups(lib):
+    assert hq.hqq_meta_groups(0, 0) == 0
+    assert hq.hqq_meta_groups(5, 0) == 1
+    assert hq.hqq_meta_groups(300, 128) == 3
+    assert hq.hqq_meta_groups(256, 128) == 2
+    assert hq.hqq_meta_groups(7, 1) == 7
+    assert hq.hqq_meta_groups(-1, 0) == -1
+    assert hq.hqq_meta_groups(5, -1) == -1
+    assert hq.hqq_meta_groups(5, (1 << 20) + 1) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, -1, 128, FAKE, FAKE, FAKE, FAKE), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, -2, FAKE, FAKE, FAKE, FAKE), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, (1 << 20) + 1, FAKE, FAKE, FAKE, FAKE), hq.HQQ_ERR_INVALID_ARG),
+    ((0, 100, 128, FAKE, FAKE, FAKE, 0), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, 128, 0, FAKE, FAKE, 0), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, 128, FAKE, 0, FAKE, 0), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, 128, FAKE, FAKE, 0, 0), hq.HQQ_ERR_INVALID_ARG),
+    ((FAKE, 100, 0, FAKE, FAKE, FAKE, 0), hq.HQQ_ERR_INVALID_ARG),   # whole array needs a workspace
+    ((FAKE + 1, 100, 128, FAKE, FAKE, FAKE, 0), hq.HQQ_ERR_ALIGNMENT),
+    ((FAKE, 100, 128, FAKE, FAKE + 1, FAKE, 0), hq.HQQ_ERR_ALIGNMENT),
+    ((FAKE, 100, 128, FAKE, FAKE, FAKE + 1, 0), hq.HQQ_ERR_ALIGNMENT),
+    ((FAKE, 100, 0, FAKE, FAKE, FAKE, FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_meta_quantize_rejects_before_launch(lib, args, status):
+    assert hq.hqq_meta_quantize(*args, 0) == status
+
+
+def test_meta_empty_is_a_no_op_and_dequant_validation(lib):
+    assert hq.hqq_meta_quantize(0, 0, 0, 0, 0, 0, 0, 0) == hq.HQQ_OK
+    assert hq.hqq_meta_dequantize(0, 0, 0, 0, 128, 0, 0) == hq.HQQ_OK
+    assert hq.hqq_meta_dequantize(FAKE, FAKE, FAKE, 10, -1, FAKE, 0) == hq.HQQ_ERR_INVALID_ARG
+    assert hq.hqq_meta_dequantize(0, FAKE, FAKE, 10, 4, FAKE, 0) == hq.HQQ_ERR_INVALID_ARG
+    assert hq.hqq_meta_dequantize(FAKE, FAKE, FAKE, 10, 4, FAKE + 1, 0) == hq.HQQ_ERR_ALIGNMENT
+
+
 def test_library_does_not_link_the_oracle(lib):
     out = subprocess.run(["nm", "-D", hq.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
