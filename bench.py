@@ -164,6 +164,75 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
     print(json.dumps(summary, indent=1))
 
 
+def measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero, stream, sh, dev):
+    """Time the 8-bit meta quantization (section 4.1 of the HQQ page) of every matrix's z
+    (one group per matrix) and s (groups of 128) after the solver has written them: one
+    hqq_meta_quantize call per array, per-matrix launches as a caller would issue them,
+    HIP events on the launch stream.  Algorithmic HBM bytes: 2 read + 1 written per value
+    (the whole-array mode reads its values twice, min/max then codes).  The largest matrix
+    is also timed alone (kernel-dominated, few launches)."""
+    max_groups = max(sum(W.numel() // g for W in Ws) for _, g in settings)
+    zc = torch.empty(max_groups, dtype=torch.uint8, device=dev)
+    sc_codes = torch.empty(max_groups, dtype=torch.uint8, device=dev)
+    zm = torch.empty((len(Ws), 2), dtype=torch.float16, device=dev)
+    sm_scale = torch.empty(max_groups // 128 + len(Ws), dtype=torch.float16, device=dev)
+    sm_offset = torch.empty_like(sm_scale)
+    ws = torch.empty(hq.hqq_meta_workspace_bytes(), dtype=torch.uint8, device=dev)
+    out = {"entry_point": "hqq_meta_quantize", "zero_points": "8-bit, one group per matrix",
+           "scales": "8-bit, groups of 128", "per_setting": []}
+    for si, (nb, g) in enumerate(settings):
+        for sj, fn, a in calls:  # this setting's outputs into the arena (untimed)
+            if sj == si:
+                assert fn(*a) == 0
+        segs, g0 = [], 0
+        for W in Ws:
+            ng = W.numel() // g
+            segs.append((g0, ng))
+            g0 += ng
+        total = g0
+
+        def run(sel):
+            mo = 0
+            for k in sel:
+                o, ng = segs[k]
+                assert lib.hqq_meta_quantize(zero.data_ptr() + 2 * o, ng, 0, zc.data_ptr() + o,
+                                             zm[k].data_ptr(), zm[k].data_ptr() + 2,
+                                             ws.data_ptr(), sh) == 0
+                assert lib.hqq_meta_quantize(scale.data_ptr() + 2 * o, ng, 128,
+                                             sc_codes.data_ptr() + o,
+                                             sm_scale.data_ptr() + 2 * mo,
+                                             sm_offset.data_ptr() + 2 * mo, 0, sh) == 0
+                mo += -(-ng // 128)
+
+        def timed(sel, reps):
+            run(sel)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                run(sel)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        all_ms = timed(range(len(Ws)), 3)
+        big = max(range(len(Ws)), key=lambda k: segs[k][1])
+        big_ms = timed([big], 20)
+        vals_all = 2 * total
+        vals_big = 2 * segs[big][1]
+        out["per_setting"].append({
+            "setting": f"b{nb}g{g}", "values": vals_all, "launches": 3 * len(Ws),
+            "ms": round(all_ms, 3),
+            "G_values_per_s": round(vals_all / (all_ms * 1e-3) / 1e9, 2),
+            "hbm_GBs_algorithmic": round(3 * vals_all / (all_ms * 1e-3) / 1e9, 1),
+            "largest_matrix": {"values": vals_big, "ms": round(big_ms, 4),
+                               "hbm_GBs_algorithmic": round(3 * vals_big / (big_ms * 1e-3) / 1e9, 1),
+                               "frac_of_hbm_peak": round(3 * vals_big / (big_ms * 1e-3) / PEAK_HBM, 4)},
+        })
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +245,8 @@ def main():
                     help="one hqq_quantize launch per matrix instead of one batched launch "
                          "per setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-meta", action="store_true",
+                    help="skip the 8-bit meta-quantization measurement (next_rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
@@ -370,6 +441,13 @@ def main():
     bytes_step = sum(n_weights * (2 + nb / 8 + 4 / g) for nb, g in settings)
     traffic = traffic_from_profile(n_weights * len(settings) / launches_per_step)
 
+    # ---- next row: 8-bit meta quantization of the solver's s and z (untimed above) -------
+    meta = None
+    if not args.no_meta:
+        meta = measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero, stream, sh,
+                            dev)
+        log(f"meta quantization: {meta}")
+
     # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -442,6 +520,7 @@ def main():
         },
         "per_setting": detail,
         "cpu_baseline": cpu,
+        "next_rows": {"meta_quantization": meta},
     }
     print(json.dumps(out), flush=True)
 

@@ -28,6 +28,7 @@ HQQ_ERR_LAUNCH = 4
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
+                    "hqq_meta_workspace_bytes",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
 
 
@@ -75,6 +76,8 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_meta_dequantize.argtypes = [P, P, P, I64, I64, P, P]
     lib.hqq_meta_groups.restype = I64
     lib.hqq_meta_groups.argtypes = [I64, I64]
+    lib.hqq_meta_workspace_bytes.restype = I64
+    lib.hqq_meta_workspace_bytes.argtypes = []
     lib.hqq_dequantize.restype = I
     lib.hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P, P]
     lib.hqq_packed_bytes.restype = I64
@@ -127,6 +130,10 @@ def hqq_quantize_batch(entries, entries_device: int, count: int, nbits: int, gro
 
 def hqq_meta_groups(n: int, meta_group: int) -> int:
     return load_library().hqq_meta_groups(n, meta_group)
+
+
+def hqq_meta_workspace_bytes() -> int:
+    return load_library().hqq_meta_workspace_bytes()
 
 
 def hqq_meta_quantize(values_f16: int, n: int, meta_group: int, codes_u8: int, mscale_f16: int,
@@ -324,7 +331,7 @@ def meta_quantize(values, meta_group: int, workspace=None, stream=None) -> MetaQ
                         offset=torch.empty(ng, dtype=torch.float16, device=dev),
                         n=n, meta_group=meta_group)
     if meta_group == 0 and workspace is None:
-        workspace = torch.empty(2, dtype=torch.int32, device=dev)
+        workspace = torch.empty(hqq_meta_workspace_bytes(), dtype=torch.uint8, device=dev)
     out.workspace = workspace
     st = hqq_meta_quantize(_addr(values), n, meta_group, _addr(out.codes), _addr(out.scale),
                            _addr(out.offset), _addr(workspace), _stream_handle(stream))

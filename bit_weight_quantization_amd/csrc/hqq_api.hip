@@ -243,6 +243,8 @@ int64_t hqq_meta_groups(int64_t n, int64_t meta_group) {
   return meta_group == 0 ? 1 : (n + meta_group - 1) / meta_group;
 }
 
+int64_t hqq_meta_workspace_bytes(void) { return 2 * hqq::kMetaPartials * (int64_t)sizeof(uint32_t); }
+
 int hqq_meta_quantize(const void* values_f16, int64_t n, int64_t meta_group, void* codes_u8,
                       void* mscale_f16, void* moffset_f16, void* workspace, void* stream) {
   const int64_t ng = hqq_meta_groups(n, meta_group);

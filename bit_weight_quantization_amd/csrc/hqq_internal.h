@@ -61,7 +61,9 @@ struct DequantParams {
 hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream);  // batched when prm.batch != nullptr
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
-// Meta quantization (M = 0: one group of all n values; workspace: 2 words, used then).
+// Meta quantization (M = 0: one group of all n values, using the workspace of
+// 2 * kMetaPartials words for per-block partial minima and maxima).
+constexpr int kMetaPartials = 1024;
 hipError_t launch_meta_quantize(const uint16_t* values, int64_t n, int64_t M, uint8_t* codes,
                                 uint16_t* mscale, uint16_t* moffset, uint32_t* workspace,
                                 int cus, hipStream_t stream);

@@ -120,11 +120,22 @@ __global__ __launch_bounds__(kMetaBlock) void meta_grouped_kernel(const uint16_t
   }
 }
 
-// Whole array: the workspace holds the min and max keys.
-__global__ void meta_init_kernel(uint32_t* ws) {
-  if (threadIdx.x == 0) {
-    ws[0] = 0xffffffffu;
-    ws[1] = 0u;
+// Whole array, two passes without atomics: each reduce block writes the min and max
+// keys of its grid-stride share to workspace[2b], workspace[2b + 1]; every quantize
+// block reduces those partials itself (at most kMetaPartials of them, L2-resident).
+__device__ __forceinline__ void block_minmax(uint32_t& kmin, uint32_t& kmax) {
+  __shared__ uint32_t smin[kMetaBlock / 64], smax[kMetaBlock / 64];
+  wave_minmax(kmin, kmax);
+  const int w = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) {
+    smin[w] = kmin;
+    smax[w] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMetaBlock / 64; ++i) {
+    kmin = smin[i] < kmin ? smin[i] : kmin;
+    kmax = smax[i] > kmax ? smax[i] : kmax;
   }
 }
 
@@ -137,22 +148,141 @@ __global__ __launch_bounds__(kMetaBlock) void meta_reduce_kernel(const uint16_t*
     kmin = k < kmin ? k : kmin;
     kmax = k > kmax ? k : kmax;
   }
-  wave_minmax(kmin, kmax);
-  if ((threadIdx.x & 63) == 0) {
-    atomicMin(&ws[0], kmin);
-    atomicMax(&ws[1], kmax);
+  block_minmax(kmin, kmax);
+  if (threadIdx.x == 0) {
+    ws[2 * blockIdx.x] = kmin;
+    ws[2 * blockIdx.x + 1] = kmax;
   }
 }
 
 __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_kernel(
-    const uint16_t* __restrict__ v, int64_t n, const uint32_t* ws, uint8_t* __restrict__ codes,
-    uint16_t* __restrict__ mscale, uint16_t* __restrict__ moffset) {
+    const uint16_t* __restrict__ v, int64_t n, const uint32_t* __restrict__ ws, int partials,
+    uint8_t* __restrict__ codes, uint16_t* __restrict__ mscale, uint16_t* __restrict__ moffset) {
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int p = threadIdx.x; p < partials; p += kMetaBlock) {
+    const uint32_t a = ws[2 * p], b = ws[2 * p + 1];
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  block_minmax(kmin, kmax);
   double mn, d;
   uint16_t s16, o16;
-  meta_params(ws[0], ws[1], mn, d, s16, o16);
+  meta_params(kmin, kmax, mn, d, s16, o16);
   const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
   for (int64_t i = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; i < n; i += stride)
     codes[i] = meta_code(v[i], mn, d);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    mscale[0] = s16;
+    moffset[0] = o16;
+  }
+}
+
+// ---- vectorized forms: 8 values per lane (one 16-byte load, one 8-byte store) ------
+// Used when values are 16-byte aligned, codes 8-byte aligned and n % 8 == 0.
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_key(uint32_t v) {
+  // quad_perm / row_half_mirror / row_mirror read lanes of the same row: never out of
+  // bounds, so bound_ctrl only spares the compiler an initialisation.
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+
+// Min and max over an aligned segment of L lanes (L <= 16: DPP inside a row).
+template <int L>
+__device__ __forceinline__ void seg_minmax(uint32_t& kmin, uint32_t& kmax) {
+  auto step = [&](uint32_t a, uint32_t b) {
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  };
+  if constexpr (L >= 2) step(dpp_key<0xB1>(kmin), dpp_key<0xB1>(kmax));    // lane ^ 1
+  if constexpr (L >= 4) step(dpp_key<0x4E>(kmin), dpp_key<0x4E>(kmax));    // lane ^ 2
+  if constexpr (L >= 8) step(dpp_key<0x141>(kmin), dpp_key<0x141>(kmax));  // mirror in 8
+  if constexpr (L >= 16) step(dpp_key<0x140>(kmin), dpp_key<0x140>(kmax)); // mirror in 16
+}
+
+__device__ __forceinline__ void chunk_keys(const uint4& raw, uint32_t& kmin, uint32_t& kmax) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t a = key_of((uint16_t)(w[j] & 0xffffu)), b = key_of((uint16_t)(w[j] >> 16));
+    kmin = a < kmin ? a : kmin;
+    kmin = b < kmin ? b : kmin;
+    kmax = a > kmax ? a : kmax;
+    kmax = b > kmax ? b : kmax;
+  }
+}
+
+__device__ __forceinline__ uint2 chunk_codes(const uint4& raw, double mn, double d) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[2 * j] = meta_code((uint16_t)(w[j] & 0xffffu), mn, d);
+    c[2 * j + 1] = meta_code((uint16_t)(w[j] >> 16), mn, d);
+  }
+  return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                    c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+}
+
+// Groups of M = 8 L values: a segment of L lanes per group, grid-stride over waves of
+// 64 chunks (512 values; M divides 512, so segments never straddle a wave).
+template <int L>
+__global__ __launch_bounds__(kMetaBlock) void meta_grouped_vec_kernel(
+    const uint4* __restrict__ v, int64_t nchunks, uint2* __restrict__ codes,
+    uint16_t* __restrict__ mscale, uint16_t* __restrict__ moffset) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * (kMetaBlock / 64);
+  for (int64_t w = uniform64m(((int64_t)blockIdx.x * kMetaBlock + threadIdx.x) / 64);
+       w * 64 < nchunks; w += nwaves) {
+    const int64_t c = w * 64 + lane;
+    const bool in = c < nchunks;
+    const uint4 raw = in ? v[c] : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    if (in) chunk_keys(raw, kmin, kmax);
+    seg_minmax<L>(kmin, kmax);  // lanes past the end contribute neutral keys
+    double mn, d;
+    uint16_t s16, o16;
+    meta_params(kmin, kmax, mn, d, s16, o16);
+    if (in) {
+      codes[c] = chunk_codes(raw, mn, d);
+      if ((lane & (L - 1)) == 0) {
+        mscale[c / L] = s16;
+        moffset[c / L] = o16;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kMetaBlock) void meta_reduce_vec_kernel(const uint4* __restrict__ v,
+                                                                     int64_t nchunks,
+                                                                     uint32_t* ws) {
+  const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int64_t c = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; c < nchunks; c += stride)
+    chunk_keys(v[c], kmin, kmax);
+  block_minmax(kmin, kmax);
+  if (threadIdx.x == 0) {
+    ws[2 * blockIdx.x] = kmin;
+    ws[2 * blockIdx.x + 1] = kmax;
+  }
+}
+
+__global__ __launch_bounds__(kMetaBlock) void meta_quant_all_vec_kernel(
+    const uint4* __restrict__ v, int64_t nchunks, const uint32_t* __restrict__ ws, int partials,
+    uint2* __restrict__ codes, uint16_t* __restrict__ mscale, uint16_t* __restrict__ moffset) {
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int p = threadIdx.x; p < partials; p += kMetaBlock) {
+    const uint32_t a = ws[2 * p], b = ws[2 * p + 1];
+    kmin = a < kmin ? a : kmin;
+    kmax = b > kmax ? b : kmax;
+  }
+  block_minmax(kmin, kmax);
+  double mn, d;
+  uint16_t s16, o16;
+  meta_params(kmin, kmax, mn, d, s16, o16);
+  const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
+  for (int64_t c = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; c < nchunks; c += stride)
+    codes[c] = chunk_codes(v[c], mn, d);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mscale[0] = s16;
     moffset[0] = o16;
@@ -198,13 +328,44 @@ int64_t grid_for(int64_t n, int cus) {
 hipError_t launch_meta_quantize(const uint16_t* values, int64_t n, int64_t M, uint8_t* codes,
                                 uint16_t* mscale, uint16_t* moffset, uint32_t* workspace,
                                 int cus, hipStream_t st) {
+  const bool vec = n % 8 == 0 && (reinterpret_cast<uintptr_t>(values) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(codes) & 7) == 0;
+  const int64_t nchunks = n / 8;
+  if (vec && M == 0) {
+    int64_t partials = (nchunks + kMetaBlock * 4 - 1) / (kMetaBlock * 4);
+    if (partials > kMetaPartials) partials = kMetaPartials;
+    hipLaunchKernelGGL(meta_reduce_vec_kernel, dim3((unsigned)partials), dim3(kMetaBlock), 0, st,
+                       reinterpret_cast<const uint4*>(values), nchunks, workspace);
+    const int64_t blocks = grid_for(nchunks, cus);
+    hipLaunchKernelGGL(meta_quant_all_vec_kernel, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st,
+                       reinterpret_cast<const uint4*>(values), nchunks, workspace, (int)partials,
+                       reinterpret_cast<uint2*>(codes), mscale, moffset);
+    return hipGetLastError();
+  }
+  if (vec && (M == 16 || M == 32 || M == 64 || M == 128)) {
+    const int64_t waves = (nchunks + 63) / 64;
+    int64_t blocks = (waves + kMetaBlock / 64 - 1) / (kMetaBlock / 64);
+    const int64_t cap = (int64_t)cus * 16;
+    if (blocks > cap) blocks = cap;
+    const uint4* vv = reinterpret_cast<const uint4*>(values);
+    uint2* cc = reinterpret_cast<uint2*>(codes);
+    switch (M) {
+      case 16: hipLaunchKernelGGL(meta_grouped_vec_kernel<2>, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, vv, nchunks, cc, mscale, moffset); break;
+      case 32: hipLaunchKernelGGL(meta_grouped_vec_kernel<4>, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, vv, nchunks, cc, mscale, moffset); break;
+      case 64: hipLaunchKernelGGL(meta_grouped_vec_kernel<8>, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, vv, nchunks, cc, mscale, moffset); break;
+      default: hipLaunchKernelGGL(meta_grouped_vec_kernel<16>, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, vv, nchunks, cc, mscale, moffset); break;
+    }
+    return hipGetLastError();
+  }
   if (M == 0) {
+    // reduce: at most kMetaPartials blocks of >= 16 values per thread
+    int64_t partials = (n + kMetaBlock * 16 - 1) / (kMetaBlock * 16);
+    if (partials > kMetaPartials) partials = kMetaPartials;
+    hipLaunchKernelGGL(meta_reduce_kernel, dim3((unsigned)partials), dim3(kMetaBlock), 0, st,
+                       values, n, workspace);
     const int64_t blocks = grid_for(n, cus);
-    hipLaunchKernelGGL(meta_init_kernel, dim3(1), dim3(64), 0, st, workspace);
-    hipLaunchKernelGGL(meta_reduce_kernel, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, values,
-                       n, workspace);
     hipLaunchKernelGGL(meta_quant_all_kernel, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st,
-                       values, n, workspace, codes, mscale, moffset);
+                       values, n, workspace, (int)partials, codes, mscale, moffset);
     return hipGetLastError();
   }
   const int64_t ngroups = (n + M - 1) / M;

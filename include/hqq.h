@@ -195,11 +195,11 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
  * codes_u8     n bytes.
  * mscale_f16, moffset_f16  hqq_meta_groups(n, meta_group) binary16 values each,
  *              2-byte aligned.
- * workspace    meta_group 0 only (ignored otherwise, may be NULL): 8 bytes of device
- *              memory, 4-byte aligned, owned by the caller, that the call uses for
- *              the array's minimum and maximum; the library initializes it on
- *              `stream` (no allocation, no memset); it must not be shared by calls
- *              that may run at the same time.
+ * workspace    meta_group 0 only (ignored otherwise, may be NULL):
+ *              hqq_meta_workspace_bytes() bytes of device memory, 4-byte aligned,
+ *              owned by the caller; the call writes partial minima and maxima there
+ *              and reads them back on `stream` (no allocation, no memset); it must
+ *              not be shared by calls that may run at the same time.
  * Conventions and errors as for hqq_quantize.
  */
 int hqq_meta_quantize(const void* values_f16, int64_t n, int64_t meta_group, void* codes_u8,
@@ -215,6 +215,9 @@ int hqq_meta_dequantize(const void* codes_u8, const void* mscale_f16, const void
 /* Number of meta groups: 0 for n == 0, 1 for meta_group == 0, else
  * ceil(n / meta_group).  -1 for invalid arguments. */
 int64_t hqq_meta_groups(int64_t n, int64_t meta_group);
+
+/* Bytes of the workspace hqq_meta_quantize needs with meta_group 0 (8192). */
+int64_t hqq_meta_workspace_bytes(void);
 
 /* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
  * shapes).  Returns -1 for invalid arguments or overflow. */

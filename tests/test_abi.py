@@ -188,6 +188,7 @@ def test_quantize_batch_empty_is_a_no_op(lib):
 
 
 def test_meta_groups(lib):
+    assert hq.hqq_meta_workspace_bytes() == 8192
     assert hq.hqq_meta_groups(0, 0) == 0
     assert hq.hqq_meta_groups(5, 0) == 1
     assert hq.hqq_meta_groups(300, 128) == 3

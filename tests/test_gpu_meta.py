@@ -92,8 +92,11 @@ def test_meta_ragged_and_small_groups(hq):
     _check(hq, q.scale.cpu().numpy().view(np.uint16).ravel(), 128)
     _check(hq, q.zero.cpu().numpy().view(np.uint16).ravel(), 0)
     v = np.asarray(rng.standard_normal(5003) * 4, np.float16).view(np.uint16)
-    for group in (1, 3, 5, 64, 65, 1000, 4096):
+    for group in (1, 3, 5, 64, 65, 1000, 4096):  # n % 8 != 0: the per-value kernels
         _check(hq, v, group)
+    v8 = np.asarray(rng.standard_normal(5008) * 4, np.float16).view(np.uint16)
+    for group in (0, 16, 32, 64, 128):  # the 8-values-per-lane kernels, ragged last group
+        _check(hq, v8, group)
 
 
 def test_meta_edge_cases(hq):
