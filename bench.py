@@ -165,72 +165,103 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
 
 
 def measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero, stream, sh, dev):
-    """Time the 8-bit meta quantization (section 4.1 of the HQQ page) of every matrix's z
-    (one group per matrix) and s (groups of 128) after the solver has written them: one
-    hqq_meta_quantize call per array, per-matrix launches as a caller would issue them,
-    HIP events on the launch stream.  Algorithmic HBM bytes: 2 read + 1 written per value
-    (the whole-array mode reads its values twice, min/max then codes).  The largest matrix
-    is also timed alone (kernel-dominated, few launches)."""
+    """Time the 8-bit meta quantization (section 4.1 of the HQQ page) of the solver's z (one
+    group per matrix) and s (groups of 128) over the whole stack after the solver has written
+    them: one hqq_meta_quantize_batch call per array (the arena form: 3 launches for z, 1 for
+    s), HIP events on the launch stream.  Algorithmic HBM bytes: 2 read + 1 written per
+    value (z reads its values twice by design, min/max then codes).  The largest matrix is
+    also timed alone with hqq_meta_quantize."""
     max_groups = max(sum(W.numel() // g for W in Ws) for _, g in settings)
     zc = torch.empty(max_groups, dtype=torch.uint8, device=dev)
     sc_codes = torch.empty(max_groups, dtype=torch.uint8, device=dev)
-    zm = torch.empty((len(Ws), 2), dtype=torch.float16, device=dev)
-    sm_scale = torch.empty(max_groups // 128 + len(Ws), dtype=torch.float16, device=dev)
+    zm_scale = torch.empty(len(Ws), dtype=torch.float16, device=dev)
+    zm_offset = torch.empty_like(zm_scale)
+    sm_scale = torch.empty(max_groups // 128 + 1, dtype=torch.float16, device=dev)
     sm_offset = torch.empty_like(sm_scale)
-    ws = torch.empty(hq.hqq_meta_workspace_bytes(), dtype=torch.uint8, device=dev)
-    out = {"entry_point": "hqq_meta_quantize", "zero_points": "8-bit, one group per matrix",
+    ws = torch.empty(max(8 * len(Ws), hq.hqq_meta_workspace_bytes()), dtype=torch.uint8,
+                     device=dev)
+    out = {"entry_point": "hqq_meta_quantize_batch", "zero_points": "8-bit, one group per matrix",
            "scales": "8-bit, groups of 128", "per_setting": []}
     for si, (nb, g) in enumerate(settings):
         for sj, fn, a in calls:  # this setting's outputs into the arena (untimed)
             if sj == si:
                 assert fn(*a) == 0
-        segs, g0 = [], 0
-        for W in Ws:
-            ng = W.numel() // g
-            segs.append((g0, ng))
-            g0 += ng
-        total = g0
+        entries, total = hq.batch_table(Ws, g)
+        table = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8).to(dev)
+        torch.cuda.synchronize()
 
-        def run(sel):
-            mo = 0
-            for k in sel:
-                o, ng = segs[k]
-                assert lib.hqq_meta_quantize(zero.data_ptr() + 2 * o, ng, 0, zc.data_ptr() + o,
-                                             zm[k].data_ptr(), zm[k].data_ptr() + 2,
-                                             ws.data_ptr(), sh) == 0
-                assert lib.hqq_meta_quantize(scale.data_ptr() + 2 * o, ng, 128,
-                                             sc_codes.data_ptr() + o,
-                                             sm_scale.data_ptr() + 2 * mo,
-                                             sm_offset.data_ptr() + 2 * mo, 0, sh) == 0
-                mo += -(-ng // 128)
+        def run_stack():
+            assert lib.hqq_meta_quantize_batch(entries, table.data_ptr(), len(Ws), g,
+                                               zero.data_ptr(), 0, zc.data_ptr(),
+                                               zm_scale.data_ptr(), zm_offset.data_ptr(),
+                                               ws.data_ptr(), sh) == 0
+            assert lib.hqq_meta_quantize_batch(entries, table.data_ptr(), len(Ws), g,
+                                               scale.data_ptr(), 128, sc_codes.data_ptr(),
+                                               sm_scale.data_ptr(), sm_offset.data_ptr(), 0,
+                                               sh) == 0
 
-        def timed(sel, reps):
-            run(sel)
+        big = max(range(len(Ws)), key=lambda k: Ws[k].numel())
+        b0 = sum(Ws[k].numel() // g for k in range(big))
+        nbig = Ws[big].numel() // g
+
+        def run_big():
+            assert lib.hqq_meta_quantize(zero.data_ptr() + 2 * b0, nbig, 0, zc.data_ptr(),
+                                         zm_scale.data_ptr(), zm_offset.data_ptr(),
+                                         ws.data_ptr(), sh) == 0
+            assert lib.hqq_meta_quantize(scale.data_ptr() + 2 * b0, nbig, 128,
+                                         sc_codes.data_ptr(), sm_scale.data_ptr(),
+                                         sm_offset.data_ptr(), 0, sh) == 0
+
+        def timed(fn, reps):
+            fn()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(reps):
-                run(sel)
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
-        all_ms = timed(range(len(Ws)), 3)
-        big = max(range(len(Ws)), key=lambda k: segs[k][1])
-        big_ms = timed([big], 20)
-        vals_all = 2 * total
-        vals_big = 2 * segs[big][1]
+        all_ms = timed(run_stack, 5)
+        big_ms = timed(run_big, 20)
+        vals_all, vals_big = 2 * total, 2 * nbig
         out["per_setting"].append({
-            "setting": f"b{nb}g{g}", "values": vals_all, "launches": 3 * len(Ws),
-            "ms": round(all_ms, 3),
+            "setting": f"b{nb}g{g}", "values": vals_all, "launches": 4, "ms": round(all_ms, 3),
             "G_values_per_s": round(vals_all / (all_ms * 1e-3) / 1e9, 2),
             "hbm_GBs_algorithmic": round(3 * vals_all / (all_ms * 1e-3) / 1e9, 1),
-            "largest_matrix": {"values": vals_big, "ms": round(big_ms, 4),
-                               "hbm_GBs_algorithmic": round(3 * vals_big / (big_ms * 1e-3) / 1e9, 1),
-                               "frac_of_hbm_peak": round(3 * vals_big / (big_ms * 1e-3) / PEAK_HBM, 4)},
+            "frac_of_hbm_peak": round(3 * vals_all / (all_ms * 1e-3) / PEAK_HBM, 4),
+            "largest_matrix_alone": {"values": vals_big, "ms": round(big_ms, 4),
+                                     "hbm_GBs_algorithmic": round(
+                                         3 * vals_big / (big_ms * 1e-3) / 1e9, 1)},
         })
     return out
+
+
+def summarize_meta(kt_dir: str, out_dir: str, command: str):
+    """Kernel-trace statistics of the meta-quantization kernels (profiles/)."""
+    import csv
+    rows = []
+    for r in csv.DictReader(open(os.path.join(kt_dir, "kt_kernel_stats.csv"))):
+        if "meta_" in r["Name"]:
+            name = r["Name"].replace("void ", "").replace("hqq::(anonymous namespace)::", "")
+            name = name.split("(")[0]
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6))
+    lines = ["# Meta-quantization kernels on the Llama-2-70B-shaped stack: rocprofv3 summary", "",
+             "The z (one group per matrix: init, reduce, quantize) and s (groups of 128) arenas "
+             "of the whole stack after the solver, hqq_meta_quantize_batch, both settings, 1 "
+             "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the largest "
+             "matrix alone (bench.py measure_meta).", "",
+             "| kernel | calls | avg duration (us) | total (ms) |", "|---|---|---|---|"]
+    for name, calls, avg, tot in sorted(rows):
+        lines.append(f"| {name} | {calls} | {avg:.2f} | {tot:.3f} |")
+    lines += ["", "Command:", "", "```", command, "```", ""]
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_meta_llama70b.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def main():
@@ -252,10 +283,19 @@ def main():
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
     ap.add_argument("--profile-run", action="store_true",
                     help="generate, then run warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--profile-meta", action="store_true",
+                    help="generate, run the solver once per setting, then only the meta "
+                         "quantization measurement (for rocprofv3 runs)")
+    ap.add_argument("--summarize-meta", metavar="KT_DIR",
+                    help="write profiles/ summary of the meta kernels from a kernel trace")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write profiles/ summaries from rocprofv3 counter and trace output")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_meta:
+        summarize_meta(args.summarize_meta, os.path.join(ROOT, "profiles"), args.profile_command)
+        return
 
     if args.summarize_profiles:
         import workloads
@@ -359,6 +399,11 @@ def main():
                 raise RuntimeError(f"quantize failed: {hq.hqq_status_string(st)}")
         if events is not None:
             events[cur][1].record(stream)
+
+    if args.profile_meta:
+        log(json.dumps(measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero,
+                                    stream, sh, dev)))
+        return
 
     for _ in range(args.warmup):
         step()

@@ -28,7 +28,7 @@ HQQ_ERR_LAUNCH = 4
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
-                    "hqq_meta_workspace_bytes",
+                    "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
 
 
@@ -76,6 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_meta_dequantize.argtypes = [P, P, P, I64, I64, P, P]
     lib.hqq_meta_groups.restype = I64
     lib.hqq_meta_groups.argtypes = [I64, I64]
+    lib.hqq_meta_quantize_batch.restype = I
+    lib.hqq_meta_quantize_batch.argtypes = [ctypes.POINTER(hqq_batch_entry_t), P, I, I, P, I64, P,
+                                            P, P, P, P]
     lib.hqq_meta_workspace_bytes.restype = I64
     lib.hqq_meta_workspace_bytes.argtypes = []
     lib.hqq_dequantize.restype = I
@@ -140,6 +143,14 @@ def hqq_meta_quantize(values_f16: int, n: int, meta_group: int, codes_u8: int, m
                       moffset_f16: int, workspace: int = 0, stream: int = 0) -> int:
     return load_library().hqq_meta_quantize(values_f16, n, meta_group, codes_u8, mscale_f16,
                                             moffset_f16, workspace, stream)
+
+
+def hqq_meta_quantize_batch(entries, entries_device: int, count: int, group_size: int,
+                            values_f16: int, meta_group: int, codes_u8: int, mscale_f16: int,
+                            moffset_f16: int, workspace: int = 0, stream: int = 0) -> int:
+    return load_library().hqq_meta_quantize_batch(entries, entries_device, count, group_size,
+                                                  values_f16, meta_group, codes_u8, mscale_f16,
+                                                  moffset_f16, workspace, stream)
 
 
 def hqq_meta_dequantize(codes_u8: int, mscale_f16: int, moffset_f16: int, n: int,
@@ -337,6 +348,36 @@ def meta_quantize(values, meta_group: int, workspace=None, stream=None) -> MetaQ
                            _addr(out.offset), _addr(workspace), _stream_handle(stream))
     if st != HQQ_OK:
         raise HQQError(st, "hqq_meta_quantize")
+    return out
+
+
+def meta_quantize_batch(b: "QuantizedBatch", which: str, meta_group: int, stream=None,
+                        entries=None) -> MetaQuantized:
+    """Meta-quantize the zero (``which="zero"``, meta_group 0: one group per matrix) or scale
+    (meta_group dividing every matrix's group count) arena of a :func:`quantize_batch` result
+    in one launch sequence."""
+    import torch
+    values = b.zero if which == "zero" else b.scale
+    n = values.numel()
+    count = len(b.shapes)
+    if entries is None:
+        entries = (hqq_batch_entry_t * max(count, 1))()
+        for i, ((rows, cols), g0) in enumerate(zip(b.shapes, b.first_group)):
+            entries[i].W_f16, entries[i].rows, entries[i].cols, entries[i].first_group = \
+                0, rows, cols, g0
+    ng = count if meta_group == 0 else (n // meta_group if meta_group else 0)
+    dev = values.device
+    out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
+                        scale=torch.empty(ng, dtype=torch.float16, device=dev),
+                        offset=torch.empty(ng, dtype=torch.float16, device=dev),
+                        n=n, meta_group=meta_group)
+    if meta_group == 0:
+        out.workspace = torch.empty(max(8 * count, 4), dtype=torch.uint8, device=dev)
+    st = hqq_meta_quantize_batch(entries, _addr(b.table), count, b.group_size, _addr(values),
+                                 meta_group, _addr(out.codes), _addr(out.scale), _addr(out.offset),
+                                 _addr(out.workspace), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_meta_quantize_batch")
     return out
 
 

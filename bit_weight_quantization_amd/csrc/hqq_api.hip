@@ -265,6 +265,44 @@ int hqq_meta_quantize(const void* values_f16, int64_t n, int64_t meta_group, voi
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 
+int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
+                            const hqq_batch_entry_t* entries_device, int count, int group_size,
+                            const void* values_f16, int64_t meta_group, void* codes_u8,
+                            void* mscale_f16, void* moffset_f16, void* workspace, void* stream) {
+  if (count < 0 || meta_group < 0 || meta_group > kMaxMetaGroup) return HQQ_ERR_INVALID_ARG;
+  if (!supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
+  if (count == 0) return HQQ_OK;
+  if (!entries) return HQQ_ERR_INVALID_ARG;
+  int64_t total = 0;
+  bool starts_mod8 = true;  // every entry starts at a multiple of 8 values
+  for (int i = 0; i < count; ++i) {
+    const hqq_batch_entry_t& e = entries[i];
+    if (checked_elems(e.rows, e.cols) < 0 || e.cols % group_size != 0) return HQQ_ERR_INVALID_ARG;
+    if (e.first_group != total) return HQQ_ERR_INVALID_ARG;
+    const int64_t groups = e.rows * e.cols / group_size;
+    if (meta_group > 0 && groups % meta_group != 0) return HQQ_ERR_INVALID_ARG;
+    if (groups % 8 != 0) starts_mod8 = false;
+    total += groups;
+  }
+  if (total == 0) return HQQ_OK;
+  if (meta_group > 0)  // entry-local groups coincide with groups of the whole arena
+    return hqq_meta_quantize(values_f16, total, meta_group, codes_u8, mscale_f16, moffset_f16,
+                             nullptr, stream);
+  if (!entries_device || !values_f16 || !codes_u8 || !mscale_f16 || !moffset_f16 || !workspace)
+    return HQQ_ERR_INVALID_ARG;
+  if (!aligned(entries_device, 8) || !aligned(values_f16, 2) || !aligned(mscale_f16, 2) ||
+      !aligned(moffset_f16, 2) || !aligned(workspace, 4))
+    return HQQ_ERR_ALIGNMENT;
+  if ((total + (1 << 16) - 1) >> 16 > (int64_t)INT32_MAX) return HQQ_ERR_INVALID_ARG;
+  hipError_t err = hqq::launch_meta_quantize_segments(
+      static_cast<const uint16_t*>(values_f16), total,
+      reinterpret_cast<const hqq::BatchEntry*>(entries_device), count, starts_mod8,
+      static_cast<uint8_t*>(codes_u8), static_cast<uint16_t*>(mscale_f16),
+      static_cast<uint16_t*>(moffset_f16), static_cast<uint32_t*>(workspace),
+      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
 int hqq_meta_dequantize(const void* codes_u8, const void* mscale_f16, const void* moffset_f16,
                         int64_t n, int64_t meta_group, void* values_f16, void* stream) {
   const int64_t ng = hqq_meta_groups(n, meta_group);

@@ -67,6 +67,11 @@ constexpr int kMetaPartials = 1024;
 hipError_t launch_meta_quantize(const uint16_t* values, int64_t n, int64_t M, uint8_t* codes,
                                 uint16_t* mscale, uint16_t* moffset, uint32_t* workspace,
                                 int cus, hipStream_t stream);
+// One group per entry of a batched arena (n values, entry e starting at first_group).
+hipError_t launch_meta_quantize_segments(const uint16_t* values, int64_t n,
+                                         const BatchEntry* entries, int count, bool starts_mod8,
+                                         uint8_t* codes, uint16_t* mscale, uint16_t* moffset,
+                                         uint32_t* workspace, hipStream_t stream);
 hipError_t launch_meta_dequantize(const uint8_t* codes, const uint16_t* mscale,
                                   const uint16_t* moffset, int64_t n, int64_t M, uint16_t* out,
                                   int cus, hipStream_t stream);

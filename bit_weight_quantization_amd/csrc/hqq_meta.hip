@@ -289,6 +289,85 @@ __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_vec_kernel(
   }
 }
 
+// ---- one group per entry of a batched arena (hqq_meta_quantize_batch, meta_group 0) ---
+// Block b covers values [b V, (b + 1) V) of the arena; it walks the entries that
+// overlap its range (first group of entry e = firsts[e], the last entry ends at n),
+// and per entry reduces its share and merges it into workspace[2e], [2e + 1] with one
+// atomic min and max per block (a few dozen contenders per address at most).
+constexpr int64_t kSegValues = 65536;
+
+__device__ __forceinline__ int seg_entry_of(const BatchEntry* E, int count, int64_t g) {
+  int lo = 0, hi = count - 1;  // last entry whose first group is <= g
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (E[mid].first_group <= g) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void meta_seg_init_kernel(uint32_t* ws, int count) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < count; e += gridDim.x * blockDim.x) {
+    ws[2 * e] = 0xffffffffu;
+    ws[2 * e + 1] = 0u;
+  }
+}
+
+// VEC: every entry starts at a multiple of 8 values and the arrays are aligned, so the
+// sub-ranges are walked in 8-value chunks (16-byte loads, 8-byte code stores).
+template <bool QUANT, bool VEC>
+__global__ __launch_bounds__(kMetaBlock) void meta_seg_kernel(
+    const uint16_t* __restrict__ v, int64_t n, const BatchEntry* __restrict__ E, int count,
+    uint32_t* ws, uint8_t* __restrict__ codes, uint16_t* __restrict__ mscale,
+    uint16_t* __restrict__ moffset) {
+  const int64_t b0 = (int64_t)blockIdx.x * kSegValues;
+  const int64_t b1 = b0 + kSegValues < n ? b0 + kSegValues : n;
+  int e = (int)uniform32((uint32_t)seg_entry_of(E, count, b0));
+  for (int64_t lo = b0; lo < b1; ++e) {
+    const int64_t e_end = uniform64m(e + 1 < count ? E[e + 1].first_group : n);
+    if (e_end <= lo) continue;  // an empty entry
+    const int64_t hi = e_end < b1 ? e_end : b1;
+    if constexpr (!QUANT) {
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+      if constexpr (VEC) {
+        const uint4* vv = reinterpret_cast<const uint4*>(v);
+        for (int64_t c = lo / 8 + threadIdx.x; c < hi / 8; c += kMetaBlock)
+          chunk_keys(vv[c], kmin, kmax);
+      } else {
+        for (int64_t i = lo + threadIdx.x; i < hi; i += kMetaBlock) {
+          const uint32_t k = key_of(v[i]);
+          kmin = k < kmin ? k : kmin;
+          kmax = k > kmax ? k : kmax;
+        }
+      }
+      block_minmax(kmin, kmax);
+      if (threadIdx.x == 0) {
+        atomicMin(&ws[2 * e], kmin);
+        atomicMax(&ws[2 * e + 1], kmax);
+      }
+      __syncthreads();  // block_minmax's LDS is reused for the next entry
+    } else {
+      double mn, d;
+      uint16_t s16, o16;
+      meta_params(ws[2 * e], ws[2 * e + 1], mn, d, s16, o16);
+      if constexpr (VEC) {
+        const uint4* vv = reinterpret_cast<const uint4*>(v);
+        uint2* cc = reinterpret_cast<uint2*>(codes);
+        for (int64_t c = lo / 8 + threadIdx.x; c < hi / 8; c += kMetaBlock)
+          cc[c] = chunk_codes(vv[c], mn, d);
+      } else {
+        for (int64_t i = lo + threadIdx.x; i < hi; i += kMetaBlock)
+          codes[i] = meta_code(v[i], mn, d);
+      }
+      if (threadIdx.x == 0 && lo == E[e].first_group) {  // the block holding the entry's start
+        mscale[e] = s16;
+        moffset[e] = o16;
+      }
+    }
+    lo = hi;
+  }
+}
+
 // offset + scale * code rounded once to binary16: s * c is exact in fp32 (11 x 8 bits);
 // TwoSum gives the exact sum as hi + lo; round-to-odd on hi makes the final
 // fp32 -> fp16 conversion a single rounding of the exact value.
@@ -372,6 +451,30 @@ hipError_t launch_meta_quantize(const uint16_t* values, int64_t n, int64_t M, ui
   const int64_t blocks = (ngroups + kMetaBlock / 64 - 1) / (kMetaBlock / 64);
   hipLaunchKernelGGL(meta_grouped_kernel, dim3((unsigned)blocks), dim3(kMetaBlock), 0, st, values,
                      n, M, ngroups, codes, mscale, moffset);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_quantize_segments(const uint16_t* values, int64_t n,
+                                         const BatchEntry* entries, int count, bool starts_mod8,
+                                         uint8_t* codes, uint16_t* mscale, uint16_t* moffset,
+                                         uint32_t* workspace, hipStream_t st) {
+  const int64_t blocks = (n + kSegValues - 1) / kSegValues;
+  int init_blocks = (count + kMetaBlock - 1) / kMetaBlock;
+  const bool vec = starts_mod8 && n % 8 == 0 && (reinterpret_cast<uintptr_t>(values) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(codes) & 7) == 0;
+  hipLaunchKernelGGL(meta_seg_init_kernel, dim3((unsigned)init_blocks), dim3(kMetaBlock), 0, st,
+                     workspace, count);
+  if (vec) {
+    hipLaunchKernelGGL((meta_seg_kernel<false, true>), dim3((unsigned)blocks), dim3(kMetaBlock), 0,
+                       st, values, n, entries, count, workspace, codes, mscale, moffset);
+    hipLaunchKernelGGL((meta_seg_kernel<true, true>), dim3((unsigned)blocks), dim3(kMetaBlock), 0,
+                       st, values, n, entries, count, workspace, codes, mscale, moffset);
+  } else {
+    hipLaunchKernelGGL((meta_seg_kernel<false, false>), dim3((unsigned)blocks), dim3(kMetaBlock), 0,
+                       st, values, n, entries, count, workspace, codes, mscale, moffset);
+    hipLaunchKernelGGL((meta_seg_kernel<true, false>), dim3((unsigned)blocks), dim3(kMetaBlock), 0,
+                       st, values, n, entries, count, workspace, codes, mscale, moffset);
+  }
   return hipGetLastError();
 }
 

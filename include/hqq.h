@@ -219,6 +219,26 @@ int64_t hqq_meta_groups(int64_t n, int64_t meta_group);
 /* Bytes of the workspace hqq_meta_quantize needs with meta_group 0 (8192). */
 int64_t hqq_meta_workspace_bytes(void);
 
+/*
+ * hqq_meta_quantize_batch -- hqq_meta_quantize applied to every entry of a
+ * hqq_quantize_batch output arena in one launch sequence: `values_f16` is the
+ * arena's zero_f16 or scale_f16 array (total groups of the entries, in entry
+ * order); groups never span two entries.
+ *   meta_group 0: one group per entry (the zero-points); mscale_f16 and moffset_f16
+ *     hold `count` values (entry order; empty entries get none written and keep
+ *     their slot); workspace: 8 * count bytes of device memory, 4-byte aligned,
+ *     used for per-entry minima and maxima (initialized on `stream`).
+ *   meta_group M > 0: groups of M inside each entry; every entry's group count must
+ *     be a multiple of M, so this equals hqq_meta_quantize over the whole arena
+ *     (total / M meta groups); entries_device and workspace are not used.
+ * entries / entries_device: as for hqq_quantize_batch (W_f16 is not read).
+ * codes_u8: total bytes.  Results equal hqq_meta_quantize on each entry's slice.
+ */
+int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
+                            const hqq_batch_entry_t* entries_device, int count, int group_size,
+                            const void* values_f16, int64_t meta_group, void* codes_u8,
+                            void* mscale_f16, void* moffset_f16, void* workspace, void* stream);
+
 /* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
  * shapes).  Returns -1 for invalid arguments or overflow. */
 int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);

@@ -225,6 +225,41 @@ def test_meta_empty_is_a_no_op_and_dequant_validation(lib):
     assert hq.hqq_meta_dequantize(FAKE, FAKE, FAKE, 10, 4, FAKE + 1, 0) == hq.HQQ_ERR_ALIGNMENT
 
 
+def _mqb(entries, count, **kw):
+    a = dict(entries_device=FAKE, group_size=64, values=FAKE, meta_group=0, codes=FAKE,
+             mscale=FAKE, moffset=FAKE, workspace=FAKE, stream=0)
+    a.update(kw)
+    return hq.hqq_meta_quantize_batch(entries, a["entries_device"], count, a["group_size"],
+                                      a["values"], a["meta_group"], a["codes"], a["mscale"],
+                                      a["moffset"], a["workspace"], a["stream"])
+
+
+@pytest.mark.parametrize("shapes,first,kw,status", [
+    ([(16, 128)], None, dict(group_size=48), hq.HQQ_ERR_UNSUPPORTED),
+    ([(16, 128)], None, dict(meta_group=-1), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128), (4, 100)], None, {}, hq.HQQ_ERR_INVALID_ARG),              # cols % g
+    ([(16, 128), (4, 64)], [0, 31], {}, hq.HQQ_ERR_INVALID_ARG),            # running sum
+    ([(16, 128), (3, 64)], None, dict(meta_group=2), hq.HQQ_ERR_INVALID_ARG),  # 3 % 2 != 0
+    ([(16, 128)], None, dict(workspace=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(entries_device=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(codes=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(workspace=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(values=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(entries_device=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(meta_group=32, values=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_meta_quantize_batch_rejects_before_launch(lib, shapes, first, kw, status):
+    assert _mqb(_entries(shapes, first=first), len(shapes), **kw) == status
+
+
+def test_meta_quantize_batch_empty_is_a_no_op(lib):
+    assert _mqb(_entries([]), 0, entries_device=0, values=0, codes=0, mscale=0, moffset=0,
+                workspace=0) == hq.HQQ_OK
+    assert _mqb(_entries([(0, 64), (5, 0)], W=0), 2, entries_device=0, values=0, codes=0,
+                mscale=0, moffset=0, workspace=0) == hq.HQQ_OK
+    assert _mqb(_entries([(16, 128)]), -1) == hq.HQQ_ERR_INVALID_ARG
+
+
 def test_library_does_not_link_the_oracle(lib):
     out = subprocess.run(["nm", "-D", hq.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout

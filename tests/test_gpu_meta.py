@@ -116,3 +116,44 @@ def test_meta_empty(hq):
     v = torch.empty(0, dtype=torch.float16, device="cuda")
     m = hq.meta_quantize(v, 0)
     assert m.codes.numel() == 0 and m.scale.numel() == 0
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32)])
+def test_meta_batch_equals_per_matrix(hq, nbits, g):
+    """hqq_meta_quantize_batch over a quantize_batch arena equals hqq_meta_quantize on each
+    matrix's slice (z: one group per matrix, with empty and tiny entries and blocks that
+    span several entries; s: groups of 128 where every group count is a multiple of 128)."""
+    _say(f"hqq_meta_quantize_batch vs per-matrix hqq_meta_quantize, b{nbits} g{g}")
+    dist = workloads.WORKLOADS["attn_4096x4096"].dist
+    shapes = [(37, 5 * g), (0, g), (1, g), (1024, 64 * g), (3, g), (2049, g), (4096, 4096)]
+    Ws = [workloads.generate(r, c, dist, 500 + i, "cuda") if r * c else
+          torch.empty((r, c), dtype=torch.float16, device="cuda") for i, (r, c) in enumerate(shapes)]
+    b = hq.quantize_batch(Ws, nbits, g)
+    mz = hq.meta_quantize_batch(b, "zero", 0)
+    torch.cuda.synchronize()
+    for i, (r, c) in enumerate(shapes):
+        g0, ng = b.first_group[i], r * c // g
+        if ng == 0:
+            continue
+        one = hq.meta_quantize(b.zero[g0:g0 + ng].contiguous(), 0)
+        torch.cuda.synchronize()
+        assert torch.equal(mz.codes[g0:g0 + ng], one.codes)
+        assert torch.equal(mz.scale[i:i + 1].view(torch.int16), one.scale.view(torch.int16))
+        assert torch.equal(mz.offset[i:i + 1].view(torch.int16), one.offset.view(torch.int16))
+    # scales: a 70B layer, every matrix's group count a multiple of 128
+    wl = workloads.WORKLOADS["llama70b_stack"]
+    Ws = [workloads.generate(m.rows, m.cols, wl.dist, m.seed, "cuda") for m in wl.matrices[:7]]
+    b = hq.quantize_batch(Ws, nbits, g)
+    ms = hq.meta_quantize_batch(b, "scale", 128)
+    mz = hq.meta_quantize_batch(b, "zero", 0)
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        g0, ng = b.first_group[i], W.numel() // g
+        one_s = hq.meta_quantize(b.scale[g0:g0 + ng].contiguous(), 128)
+        one_z = hq.meta_quantize(b.zero[g0:g0 + ng].contiguous(), 0)
+        torch.cuda.synchronize()
+        assert torch.equal(ms.codes[g0:g0 + ng], one_s.codes)
+        assert torch.equal(ms.scale[g0 // 128:(g0 + ng) // 128].view(torch.int16),
+                           one_s.scale.view(torch.int16))
+        assert torch.equal(mz.codes[g0:g0 + ng], one_z.codes)
+        assert torch.equal(mz.offset[i:i + 1].view(torch.int16), one_z.offset.view(torch.int16))
