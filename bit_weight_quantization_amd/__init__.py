@@ -42,7 +42,8 @@ class hqq_options_t(ctypes.Structure):
     _fields_ = [("early_stop", ctypes.c_int),
                 ("scale_f32", ctypes.c_void_p), ("zero_f32", ctypes.c_void_p),
                 ("stop_step", ctypes.c_void_p), ("err_init", ctypes.c_void_p),
-                ("err_best", ctypes.c_void_p), ("refill_threshold", ctypes.c_int)]
+                ("err_best", ctypes.c_void_p), ("refill_threshold", ctypes.c_int),
+                ("err_metric", ctypes.c_int)]
 
 
 class hqq_batch_entry_t(ctypes.Structure):
@@ -197,7 +198,7 @@ def _addr(t) -> int:
 def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
              kappa: float = 1.01, iters: int = 20, early_stop: bool = True, debug: bool = False,
              out: Optional[QuantizedWeight] = None, stream=None,
-             refill_threshold: int = 0) -> QuantizedWeight:
+             refill_threshold: int = 0, err_metric: int = 0) -> QuantizedWeight:
     """Quantize a contiguous rows x cols fp16 CUDA tensor on the given (or current) stream.
 
     ``out`` may supply preallocated output tensors (reused as-is).  With ``debug`` the
@@ -226,12 +227,13 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
         out.err_init = torch.empty(shp, dtype=torch.float32, device=dev)
         out.err_best = torch.empty(shp, dtype=torch.float32, device=dev)
     opts = None
-    if debug or not early_stop or refill_threshold:
+    if debug or not early_stop or refill_threshold or err_metric:
         opts = hqq_options_t(int(bool(early_stop)), _addr(out.scale_f32 if debug else None),
                              _addr(out.zero_f32 if debug else None),
                              _addr(out.stop_step if debug else None),
                              _addr(out.err_init if debug else None),
-                             _addr(out.err_best if debug else None), int(refill_threshold))
+                             _addr(out.err_best if debug else None), int(refill_threshold),
+                             int(err_metric))
     st = hqq_quantize_ex(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
                          float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
                          _addr(out.zero), opts, _stream_handle(stream))

@@ -52,7 +52,8 @@ int validate_solver(float p, float beta, float kappa, int iters) {
 
 // Solver constants shared by the single-matrix and batched entry points.
 void set_solver_params(hqq::SolveParams& prm, int nbits, int group_size, float p, float beta,
-                       float kappa, int iters, int early_stop, int refill_threshold) {
+                       float kappa, int iters, int early_stop, int refill_threshold,
+                       int err_metric) {
   const int slots = hqq::kWave * hqq::kLaneElems / group_size;  // groups resident in a wavefront
   prm.qmax = (float)((1 << nbits) - 1);
   prm.inv_qmax = (float)(1.0 / (double)((1 << nbits) - 1));
@@ -72,6 +73,7 @@ void set_solver_params(hqq::SolveParams& prm, int nbits, int group_size, float p
   prm.nbits = nbits;
   const int refill = refill_threshold > 0 ? refill_threshold : 1;
   prm.refill_at = refill > slots ? slots : refill;
+  prm.err_metric = err_metric;
 }
 
 int power_mode_of(float p) {
@@ -118,11 +120,12 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
       !aligned(zero_f16, 2))
     return HQQ_ERR_ALIGNMENT;
-  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr, 0};
+  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
   if (opt) {
     o = *opt;
     if (o.early_stop != 0 && o.early_stop != 1) return HQQ_ERR_INVALID_ARG;
     if (o.refill_threshold < 0) return HQQ_ERR_INVALID_ARG;
+    if (o.err_metric < 0 || o.err_metric > 2) return HQQ_ERR_INVALID_ARG;
     if ((o.scale_f32 && !aligned(o.scale_f32, 4)) || (o.zero_f32 && !aligned(o.zero_f32, 4)) ||
         (o.err_init && !aligned(o.err_init, 4)) || (o.err_best && !aligned(o.err_best, 4)))
       return HQQ_ERR_ALIGNMENT;
@@ -142,7 +145,7 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   prm.err_best = o.err_best;
   prm.ngroups = n / group_size;
   set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, o.early_stop,
-                    o.refill_threshold);
+                    o.refill_threshold, o.err_metric);
   const int power_mode = power_mode_of(p);
 
   int cus = compute_units();
@@ -194,7 +197,7 @@ int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t
   prm.scale16 = static_cast<uint16_t*>(scale_f16);
   prm.zero16 = static_cast<uint16_t*>(zero_f16);
   prm.ngroups = total;
-  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, 1, 0);
+  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, 1, 0, hqq::kErrP);
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;
   hipError_t err = hqq::launch_solve(prm, group_size, power_mode_of(p), cus,

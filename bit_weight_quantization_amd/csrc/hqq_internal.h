@@ -9,6 +9,8 @@ namespace hqq {
 // How the lp power |x|^p is evaluated: general 0 < p < 1 through log2/exp2,
 // or the two exact special cases p = 1 and p = 0.
 enum PowerMode : int { kPowGeneral = 0, kPowOne = 1, kPowZero = 2 };
+// Error metric of the early stop: the lp error with the solver's p, l1 or l2.
+enum ErrMetric : int { kErrP = 0, kErrL1 = 1, kErrL2 = 2 };
 
 // Device view of one hqq_batch_entry_t (same 32-byte layout).
 struct BatchEntry {
@@ -45,6 +47,7 @@ struct SolveParams {
   int early_stop;
   int nbits;
   int refill_at;           // hand stopped groups over once this many segments are stopped
+  int err_metric;          // ErrMetric of the early stop
 };
 
 struct DequantParams {

@@ -130,12 +130,21 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, round to nearest even
 }
 
-// |rc|^p for the error sum (|0|^p := 0).
+// The solver mode PM packs the power mode of the shrink (bits 0-1: kPowGeneral,
+// kPowOne, kPowZero) and the early-stop error metric (bits 2-3: kErrP = the lp error
+// with the solver's p, kErrL1, kErrL2).
+constexpr int shrink_mode(int pm) { return pm & 3; }
+constexpr int err_mode(int pm) { return pm >> 2; }
+
+// Error term of one residual in code units for the stop test (|0|^p := 0).
 template <int PM>
 __device__ __forceinline__ float pow_p(float rc, float p) {
-  if constexpr (PM == kPowOne) {
+  constexpr int SM = shrink_mode(PM), EM = err_mode(PM);
+  if constexpr (EM == kErrL1 || (EM == kErrP && SM == kPowOne)) {
     return __builtin_fabsf(rc);
-  } else if constexpr (PM == kPowZero) {
+  } else if constexpr (EM == kErrL2) {
+    return rc * rc;
+  } else if constexpr (SM == kPowZero) {
     return rc != 0.0f ? 1.0f : 0.0f;
   } else {
     // log2(0) = -inf, p*(-inf) = -inf, exp2(-inf) = 0 for 0 < p < 1.
@@ -146,20 +155,22 @@ __device__ __forceinline__ float pow_p(float rc, float p) {
 // |rc|^(p-1), used by the shrink only (+inf at rc = 0 for p < 1).
 template <int PM>
 __device__ __forceinline__ float pow_pm1(float a, float pm1) {
-  if constexpr (PM == kPowOne) {
+  if constexpr (shrink_mode(PM) == kPowOne) {
     return 1.0f;
-  } else if constexpr (PM == kPowZero) {
+  } else if constexpr (shrink_mode(PM) == kPowZero) {
     return __builtin_amdgcn_rcpf(a);
   } else {
     return exp2_hw(pm1 * log2_hw(a));
   }
 }
 
-// x^p for a positive per-group scalar (error reporting and shrink scaling).
+// s^q for the error reported in weight units (q: the error metric's exponent).
 template <int PM>
 __device__ __forceinline__ float scalar_pow(float x, float p) {
-  if constexpr (PM == kPowOne) return x;
-  else if constexpr (PM == kPowZero) return 1.0f;
+  constexpr int SM = shrink_mode(PM), EM = err_mode(PM);
+  if constexpr (EM == kErrL1 || (EM == kErrP && SM == kPowOne)) return x;
+  else if constexpr (EM == kErrL2) return x * x;
+  else if constexpr (SM == kPowZero) return 1.0f;
   else return exp2_hw(p * log2_hw(x));
 }
 
@@ -414,8 +425,8 @@ __device__ __forceinline__ void solver_step(const SolveParams& P, Slot& q, bool 
     if (ballot(need) != 0) {
       if (need) {
         float cs;  // s^(p-2)
-        if constexpr (PM == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
-        else if constexpr (PM == kPowOne) cs = q.inv_s;
+        if constexpr (shrink_mode(PM) == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
+        else if constexpr (shrink_mode(PM) == kPowOne) cs = q.inv_s;
         else cs = q.inv_s * q.inv_s;
         const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
         const float ib = cs * inv_beta;  // s^(p-2) / beta_t
@@ -794,7 +805,10 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 constexpr int kChunkBatches = 4;  // chunk = 4 prime batches
 template <int G, int PM>
 hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
-  auto kernel = prm.batch ? hqq_solve_kernel<G, PM, true> : hqq_solve_kernel<G, PM, false>;
+  auto kernel = hqq_solve_kernel<G, PM, false>;
+  if constexpr (err_mode(PM) == kErrP) {
+    if (prm.batch) kernel = hqq_solve_kernel<G, PM, true>;
+  }
   int per_cu = 0;
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0);
   if (err != hipSuccess) return err;
@@ -809,12 +823,21 @@ hipError_t launch_solve_gp(SolveParams prm, int cus, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int G, int EM>
+hipError_t launch_solve_ge(const SolveParams& prm, int power_mode, int cus, hipStream_t st) {
+  switch (power_mode) {
+    case kPowOne: return launch_solve_gp<G, kPowOne | (EM << 2)>(prm, cus, st);
+    case kPowZero: return launch_solve_gp<G, kPowZero | (EM << 2)>(prm, cus, st);
+    default: return launch_solve_gp<G, kPowGeneral | (EM << 2)>(prm, cus, st);
+  }
+}
+
 template <int G>
 hipError_t launch_solve_g(const SolveParams& prm, int power_mode, int cus, hipStream_t st) {
-  switch (power_mode) {
-    case kPowOne: return launch_solve_gp<G, kPowOne>(prm, cus, st);
-    case kPowZero: return launch_solve_gp<G, kPowZero>(prm, cus, st);
-    default: return launch_solve_gp<G, kPowGeneral>(prm, cus, st);
+  switch (prm.err_metric) {  // batched launches always use the lp error
+    case kErrL1: return launch_solve_ge<G, kErrL1>(prm, power_mode, cus, st);
+    case kErrL2: return launch_solve_ge<G, kErrL2>(prm, power_mode, cus, st);
+    default: return launch_solve_ge<G, kErrP>(prm, power_mode, cus, st);
   }
 }
 

@@ -74,6 +74,10 @@ typedef struct {
                            groups over (replacing them from its standby pool) once this
                            many have stopped.  0 = default (1); values above the slot
                            count are clamped; < 0 invalid. */
+  int err_metric;      /* the error of the early-stop test (and of err_init/err_best):
+                          0 = sum |r|^p with the solver's p (the default reading of
+                          section 4.1's "error"); 1 = sum |r| (l1); 2 = sum r^2 (l2).
+                          The shrink and z update are unchanged.  Other values invalid. */
 } hqq_options_t;
 
 /*

@@ -75,14 +75,14 @@ def _near_f16_midpoint(v: np.ndarray, rel: float) -> np.ndarray:
 
 def compare(W16: np.ndarray, dev: DeviceResult, nbits: int, group_size: int, p=0.7, beta=1.0,
             kappa=1.01, iters=20, early_stop=True, ref=None, strict_ties_only=True,
-            min_agree=STOP_AGREE, min_code_agree=CODE_AGREE) -> dict:
+            min_agree=STOP_AGREE, min_code_agree=CODE_AGREE, err_pow=None) -> dict:
     """Assert the tolerances above for rows x cols binary16 input bits W16."""
     W16 = np.ascontiguousarray(W16).view(np.uint16)
     rows, cols = W16.shape
     qmax = (1 << nbits) - 1
     if ref is None:
         ref = oracle.hqq_quantize(W16, nbits, group_size, p=p, beta=beta, kappa=kappa, iters=iters,
-                                  early_stop=early_stop)
+                                  early_stop=early_stop, err_pow=err_pow)
     rep = {"groups": ref.scale.size, "weights": W16.size}
 
     # ---- s
@@ -139,7 +139,7 @@ def compare(W16: np.ndarray, dev: DeviceResult, nbits: int, group_size: int, p=0
 
     # ---- groups that left the oracle's trajectory: each must be explained
     kinds = {"error_tie": 0, "rounding_tie": 0}
-    params = dict(p=p, beta=beta, kappa=kappa, iters=iters, early_stop=early_stop)
+    params = dict(p=p, beta=beta, kappa=kappa, iters=iters, early_stop=early_stop, err_pow=err_pow)
     for (i, j) in np.argwhere(~agree):
         assert dev.zero32 is not None and dev.stop is not None, "divergent group without debug outputs"
         kind = explain_divergence(Wd[i, j], nbits, int(dev.stop[i, j]), float(dev.zero32[i, j]),

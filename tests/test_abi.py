@@ -109,6 +109,13 @@ def test_empty_matrix_is_a_no_op(lib):
     assert hq.hqq_dequantize(0, 0, 0, 0, 64, 4, 64, 0, 0) == hq.HQQ_OK
 
 
+def test_quantize_ex_err_metric_validation(lib):
+    for bad in (-1, 3):
+        opt = hq.hqq_options_t(1, 0, 0, 0, 0, 0, 0, bad)
+        assert hq.hqq_quantize_ex(FAKE, 16, 128, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE, opt,
+                                  0) == hq.HQQ_ERR_INVALID_ARG
+
+
 def test_quantize_ex_option_validation(lib):
     opt = hq.hqq_options_t(2, 0, 0, 0, 0, 0)
     assert hq.hqq_quantize_ex(FAKE, 16, 128, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE, opt,

@@ -160,6 +160,23 @@ def test_other_p(hq, p):
     _check_full(hq, _c1(), 2, 32, p=p, beta=1e3, **floors)
 
 
+@pytest.mark.parametrize("err_metric,err_pow,floors", [(1, 1.0, dict(min_agree=0.95)),
+                                                      (2, 2.0, dict(min_agree=0.99))])
+def test_error_metric_variants(hq, err_metric, err_pow, floors):
+    """The l1 and l2 early-stop errors (hqq_options_t.err_metric) against the oracle's
+    err_pow switch; the shrink keeps p = 0.7.  With codes fixed, the z update is the exact
+    l2 minimizer, so consecutive l2 errors sit on a flat quadratic minimum and differ by
+    amounts at fp32 noise level: the stop floor is lower (as for p = 1), and every
+    divergent group must still be explained as an error or rounding tie."""
+    for name in ("single_256x512", "attn_4096x4096"):
+        _say(f"{name} b4 g64, early-stop error l{err_metric}")
+        W = workloads.generate_matrix(workloads.WORKLOADS[name], 0, "cuda")
+        q = _run(hq, W, 4, 64, err_metric=err_metric)
+        rep = parity.compare(W.cpu().numpy().view(np.uint16), parity.from_quantized(q), 4, 64,
+                             err_pow=err_pow, **floors)
+        _say(f"  {rep}")
+
+
 def test_no_early_stop_and_zero_iters(hq):
     _say("single_256x512 early_stop=0 T=20; T=0; T=255")
     _check_full(hq, _c1(), 4, 64, early_stop=False)
