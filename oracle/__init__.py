@@ -75,6 +75,8 @@ def _load():
     lib.oracle_hqq_quantize.argtypes = [P, I64, I64, I, I, D, D, D, I, I, D] + [P] * 9
     lib.oracle_hqq_dequantize.restype = I
     lib.oracle_hqq_dequantize.argtypes = [P, P, P, I64, I64, I, I, P]
+    lib.oracle_hqq_quantize_tensor_stop.restype = I
+    lib.oracle_hqq_quantize_tensor_stop.argtypes = [P, I64, I64, I, I, D, D, D, I, D] + [P] * 10
     lib.oracle_meta_quantize.restype = I64
     lib.oracle_meta_quantize.argtypes = [P, I64, I64, P, P, P]
     lib.oracle_meta_dequantize.restype = I
@@ -265,6 +267,34 @@ def hqq_quantize(W_f16_bits: np.ndarray, nbits: int, group_size: int, p: float =
     if rc != 0:
         raise ValueError("oracle_hqq_quantize rejected its arguments")
     return out
+
+
+def hqq_quantize_tensor_stop(W_f16_bits: np.ndarray, nbits: int, group_size: int,
+                             p: float = 0.7, beta: float = 1.0, kappa: float = 1.01,
+                             iters: int = 20, err_pow: float | None = None):
+    """Whole-tensor early stop (hqq_oracle.c, oracle_hqq_quantize_tensor_stop).
+    Returns (QuantResult, t_star, E) with E the total error of every step 0..iters."""
+    W = np.ascontiguousarray(W_f16_bits)
+    if W.dtype == np.float16:
+        W = W.view(np.uint16)
+    assert W.dtype == np.uint16 and W.ndim == 2
+    rows, cols = W.shape
+    mshape = (rows, cols // group_size)
+    out = QuantResult(
+        packed=np.empty(packed_bytes(rows * cols, nbits), np.uint8),
+        scale_f16=np.empty(mshape, np.uint16), zero_f16=np.empty(mshape, np.uint16),
+        scale=np.empty(mshape, np.float64), zero=np.empty(mshape, np.float64),
+        stop_step=np.empty(mshape, np.uint8), err_init=np.empty(mshape, np.float64),
+        err_best=np.empty(mshape, np.float64), codes=np.empty((rows, cols), np.uint8))
+    E = np.empty(iters + 1, np.float64)
+    t_star = _load().oracle_hqq_quantize_tensor_stop(
+        _ptr(W), rows, cols, nbits, group_size, float(p), float(beta), float(kappa), int(iters),
+        float(p if err_pow is None else err_pow), _ptr(E), _ptr(out.packed), _ptr(out.scale_f16),
+        _ptr(out.zero_f16), _ptr(out.scale), _ptr(out.zero), _ptr(out.stop_step),
+        _ptr(out.err_init), _ptr(out.err_best), _ptr(out.codes))
+    if t_star < 0:
+        raise ValueError("oracle_hqq_quantize_tensor_stop rejected its arguments")
+    return out, t_star, E
 
 
 def hqq_dequantize(packed: np.ndarray, scale_f16: np.ndarray, zero_f16: np.ndarray, rows: int,

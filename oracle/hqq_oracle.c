@@ -415,3 +415,57 @@ int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Whole-tensor early stop: the reading alternative to the per-group stop of   */
+/* section 4.1 (the page says only that the solver exits once "the error" no   */
+/* longer improves).                                                           */
+/* ------------------------------------------------------------------------- */
+
+/* All groups of the matrix step together.  E_t = sum over the groups (index
+ * order) of e_{g,t}, the group's lp error (err_pow) at step t; the tensor continues
+ * while E_t is strictly below the best total so far, and every group returns its z
+ * of the last accepted step t*.  A stop decision never changes an update, so each
+ * group's trajectory is that of the solver without early stop and the outputs are
+ * those of oracle_hqq_quantize with early_stop = 0 and iters = t*.  E (may be NULL)
+ * receives E_0 .. E_iters.  Returns t*, or -1 for invalid arguments. */
+int oracle_hqq_quantize_tensor_stop(const uint16_t* W_f16, int64_t rows, int64_t cols, int nbits,
+                                    int group_size, double p, double beta, double kappa,
+                                    int iters, double err_pow, double* E, uint8_t* packed,
+                                    uint16_t* scale_f16, uint16_t* zero_f16, double* scale_f64,
+                                    double* zero_f64, uint8_t* stop_step, double* err_init,
+                                    double* err_best, uint8_t* codes_out) {
+  if (rows < 0 || cols < 0 || group_size <= 0 || group_size > ORACLE_MAX_GROUP) return -1;
+  if (cols % group_size != 0 || iters < 0 || iters > 255) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  const int64_t ngroups = rows * cols / group_size;
+  double total[256];
+  for (int t = 0; t <= iters; ++t) total[t] = 0.0;
+  double w[ORACLE_MAX_GROUP];
+  uint8_t gc[ORACLE_MAX_GROUP];
+  double trace[256];
+  for (int64_t gi = 0; gi < ngroups; ++gi) {
+    const uint16_t* src = W_f16 + gi * group_size;
+    for (int k = 0; k < group_size; ++k) w[k] = oracle_f16_to_f64(src[k]);
+    oracle_group_result_t res;
+    int n_trace = 0;
+    if (oracle_hqq_group(w, group_size, nbits, p, beta, kappa, iters, 0, err_pow, gc, &res,
+                         trace, &n_trace) != 0 || n_trace != iters + 1)
+      return -1;
+    for (int t = 0; t <= iters; ++t) total[t] += trace[t];
+  }
+  int t_star = 0;
+  double best = total[0];
+  for (int t = 1; t <= iters; ++t) {
+    if (!(total[t] < best)) break;
+    best = total[t];
+    t_star = t;
+  }
+  if (E)
+    for (int t = 0; t <= iters; ++t) E[t] = total[t];
+  if (oracle_hqq_quantize(W_f16, rows, cols, nbits, group_size, p, beta, kappa, t_star, 0, err_pow,
+                          packed, scale_f16, zero_f16, scale_f64, zero_f64, stop_step, err_init,
+                          err_best, codes_out) != 0)
+    return -1;
+  return t_star;
+}

@@ -55,6 +55,13 @@ int oracle_hqq_dequantize(const uint8_t* packed, const uint16_t* scale_f16,
                           const uint16_t* zero_f16, int64_t rows, int64_t cols, int nbits,
                           int group_size, uint16_t* W_out_f16);
 
+int oracle_hqq_quantize_tensor_stop(const uint16_t* W_f16, int64_t rows, int64_t cols, int nbits,
+                                    int group_size, double p, double beta, double kappa,
+                                    int iters, double err_pow, double* E, uint8_t* packed,
+                                    uint16_t* scale_f16, uint16_t* zero_f16, double* scale_f64,
+                                    double* zero_f64, uint8_t* stop_step, double* err_init,
+                                    double* err_best, uint8_t* codes_out);
+
 int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, uint8_t* codes,
                              uint16_t* scale16, uint16_t* offset16);
 int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,

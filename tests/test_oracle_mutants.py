@@ -43,6 +43,14 @@ MUTANTS = {
                                  "const uint16_t* src = W_f16 + ((gi % rows) * cols + "
                                  "(gi / rows) * group_size);"),
     "dequant adds z": ("s * ((double)c - z)", "s * ((double)c + z)"),
+    "tensor stop on non-increase": ("if (!(total[t] < best)) break;",
+                                    "if (!(total[t] <= best)) break;"),
+    "tensor stop keeps the global best": ("if (!(total[t] < best)) break;",
+                                          "if (!(total[t] < best)) continue;"),
+    "tensor stop one step late": ("    t_star = t;\n  }\n  if (E)", "    t_star = t + (t < iters);\n  }\n  if (E)"),
+    "tensor total skips the last group": ("for (int t = 0; t <= iters; ++t) total[t] += trace[t];",
+                                          "if (gi + 1 < ngroups) for (int t = 0; t <= iters; ++t) "
+                                          "total[t] += trace[t];"),
     "meta 256 levels": ("* 255.0) / d;", "* 256.0) / d;"),
     "meta round half away from zero": ("c = nearbyint((double)(float)u);",
                                        "c = round((double)(float)u);"),

@@ -441,3 +441,53 @@ def test_replay_hook_without_events_is_the_solver_and_flips_move_one_code():
     # inverting the first stop decision (e1 >= e0) accepts z1 = 1.125
     r2, _ = oracle.hqq_group_replay(w, 2, inverts=(1,), iters=1)
     assert r2.stop_step == 1 and r2.zero == 1.125
+
+
+# ---------------------------------------------------------------- whole-tensor stop --
+
+def test_tensor_stop_of_one_group_is_the_group_stop():
+    # a single group: the total error is the group's error, so the tensor stop is the
+    # per-group early stop (pinned above by the hand examples)
+    rng = np.random.default_rng(11)
+    cases = [np.asarray([-1, 0, 0.5, 2], np.float16)]
+    cases += [np.asarray(rng.standard_t(4, 64) * 0.02, np.float16) for _ in range(20)]
+    for w in cases:
+        g = w.size
+        W = w.reshape(1, g).view(np.uint16)
+        r_t, t_star, E = oracle.hqq_quantize_tensor_stop(W, 4 if g > 4 else 2, g)
+        r_g = oracle.hqq_quantize(W, 4 if g > 4 else 2, g)
+        assert t_star == int(r_g.stop_step[0, 0])
+        assert r_t.zero[0, 0] == r_g.zero[0, 0]
+        assert np.array_equal(r_t.codes, r_g.codes)
+
+
+def test_tensor_stop_of_replicated_groups():
+    # k copies of one group: E_t = k e_t, so t* is the single group's stop step
+    rng = np.random.default_rng(12)
+    for _ in range(5):
+        w = np.asarray(rng.standard_t(3, 32) * 0.02, np.float16)
+        W = np.tile(w, (7, 1)).view(np.uint16)
+        _, t_star, E = oracle.hqq_quantize_tensor_stop(W, 2, 32)
+        r_g = oracle.hqq_quantize(w.reshape(1, 32).view(np.uint16), 2, 32)
+        assert t_star == int(r_g.stop_step[0, 0])
+
+
+def test_tensor_stop_invariants_and_totals():
+    W = workloads.generate_matrix(workloads.WORKLOADS["single_256x512"], 0).numpy().view(np.uint16)
+    iters = 20
+    r, t_star, E = oracle.hqq_quantize_tensor_stop(W, 4, 64, iters=iters)
+    assert np.all(np.diff(E[: t_star + 1]) < 0)                  # strictly improving to t*
+    assert t_star == iters or E[t_star + 1] >= E[t_star]          # stops at the first non-improvement
+    assert np.all(r.stop_step == t_star)
+    # E_0 is the sum of the min-max init errors, computed here from the quantizer alone
+    Wd = oracle.f16_to_f64(W).reshape(-1, 64)
+    e0 = 0.0
+    for w in Wd:
+        s, inv_s, z = oracle.minmax_init(w, 4)
+        q = np.array([oracle.quantize_value(x, inv_s, z, 15) for x in w])
+        e0 += oracle.group_error(w - s * (q - z), 0.7)
+    assert abs(E[0] - e0) <= 1e-9 * e0
+    # E_{t*} is the sum of the returned groups' errors
+    assert abs(E[t_star] - r.err_best.sum()) <= 1e-9 * E[t_star]
+    # the whole-tensor reading iterates longer than most groups would alone
+    assert t_star > np.median(oracle.hqq_quantize(W, 4, 64).stop_step)
