@@ -27,6 +27,7 @@ HQQ_ERR_LAUNCH = 4
 
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
+                    "hqq_quantize_tensor_stop", "hqq_tensor_stop_workspace_bytes",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
@@ -68,6 +69,11 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_ex.restype = I
     lib.hqq_quantize_ex.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
                                     ctypes.POINTER(hqq_options_t), P]
+    lib.hqq_quantize_tensor_stop.restype = I
+    lib.hqq_quantize_tensor_stop.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
+                                             ctypes.POINTER(hqq_options_t), P, P, P, P]
+    lib.hqq_tensor_stop_workspace_bytes.restype = I64
+    lib.hqq_tensor_stop_workspace_bytes.argtypes = [I]
     lib.hqq_quantize_batch.restype = I
     lib.hqq_quantize_batch.argtypes = [ctypes.POINTER(hqq_batch_entry_t), P, I, I, I, F, F, F, I,
                                        P, P, P, P]
@@ -121,6 +127,21 @@ def hqq_quantize_ex(W_f16: int, rows: int, cols: int, nbits: int, group_size: in
     opt = ctypes.byref(options) if options is not None else None
     return load_library().hqq_quantize_ex(W_f16, rows, cols, nbits, group_size, p, beta, kappa,
                                           iters, packed_codes, scale_f16, zero_f16, opt, stream)
+
+
+def hqq_quantize_tensor_stop(W_f16: int, rows: int, cols: int, nbits: int, group_size: int,
+                             p: float, beta: float, kappa: float, iters: int, packed_codes: int,
+                             scale_f16: int, zero_f16: int, options: Optional[hqq_options_t],
+                             totals_f64: int, t_star_i32: int, workspace: int,
+                             stream: int = 0) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    return load_library().hqq_quantize_tensor_stop(W_f16, rows, cols, nbits, group_size, p, beta,
+                                                   kappa, iters, packed_codes, scale_f16, zero_f16,
+                                                   opt, totals_f64, t_star_i32, workspace, stream)
+
+
+def hqq_tensor_stop_workspace_bytes(iters: int) -> int:
+    return load_library().hqq_tensor_stop_workspace_bytes(iters)
 
 
 def hqq_quantize_batch(entries, entries_device: int, count: int, nbits: int, group_size: int,
@@ -204,6 +225,57 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
     ``out`` may supply preallocated output tensors (reused as-is).  With ``debug`` the
     fp32 s and z, the stop step and the initial/best errors per group are returned too.
     """
+    out = _outputs(W, nbits, group_size, debug, out, "quantize")
+    rows, cols = W.shape
+    opts = None
+    if debug or not early_stop or refill_threshold or err_metric:
+        opts = _options(out, debug, early_stop, refill_threshold, err_metric)
+    st = hqq_quantize_ex(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
+                         float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
+                         _addr(out.zero), opts, _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_quantize_ex")
+    return out
+
+
+def quantize_tensor_stop(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
+                         kappa: float = 1.01, iters: int = 20, debug: bool = False,
+                         err_metric: int = 0, out: Optional[QuantizedWeight] = None,
+                         workspace=None, stream=None):
+    """Quantize with the early stop taken over the whole matrix (hqq_quantize_tensor_stop).
+
+    Returns ``(QuantizedWeight, totals, t_star)`` where ``totals`` is a float64 CUDA tensor
+    of the iters + 1 total errors E_t and ``t_star`` a one-element int32 CUDA tensor (both
+    filled on the stream; read them after synchronizing).  ``workspace`` may supply a uint8
+    CUDA tensor of at least hqq_tensor_stop_workspace_bytes(iters) bytes.
+    """
+    import torch
+    out = _outputs(W, nbits, group_size, debug, out, "quantize_tensor_stop")
+    rows, cols = W.shape
+    wb = hqq_tensor_stop_workspace_bytes(int(iters))
+    if wb < 0:
+        raise HQQError(HQQ_ERR_INVALID_ARG, "quantize_tensor_stop")
+    if workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+        if stream is not None:  # freed on return: keep it until the stream's work is done
+            workspace.record_stream(stream)
+    elif workspace.numel() < wb or not workspace.is_cuda:
+        raise ValueError(f"workspace needs {wb} bytes of device memory")
+    totals = torch.empty(int(iters) + 1, dtype=torch.float64, device=W.device)
+    t_star = torch.empty(1, dtype=torch.int32, device=W.device)
+    opts = _options(out, debug, True, 0, err_metric)
+    st = hqq_quantize_tensor_stop(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
+                                  float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
+                                  _addr(out.zero), opts, _addr(totals), _addr(t_star),
+                                  _addr(workspace), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_quantize_tensor_stop")
+    return out, totals, t_star
+
+
+def _outputs(W, nbits: int, group_size: int, debug: bool, out: Optional[QuantizedWeight],
+             where: str) -> QuantizedWeight:
+    """Checks W and allocates the output tensors that ``out`` does not supply."""
     import torch
     if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
         raise ValueError("W must be a contiguous 2-D float16 CUDA tensor")
@@ -211,7 +283,7 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
     ng = hqq_num_groups(rows, cols, group_size)
     nb = hqq_packed_bytes(rows, cols, nbits)
     if ng < 0 or nb < 0:
-        raise HQQError(HQQ_ERR_INVALID_ARG if nb >= 0 else HQQ_ERR_UNSUPPORTED, "quantize")
+        raise HQQError(HQQ_ERR_INVALID_ARG if nb >= 0 else HQQ_ERR_UNSUPPORTED, where)
     dev = W.device
     if out is None:
         out = QuantizedWeight(
@@ -226,20 +298,17 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
         out.stop_step = torch.empty(shp, dtype=torch.uint8, device=dev)
         out.err_init = torch.empty(shp, dtype=torch.float32, device=dev)
         out.err_best = torch.empty(shp, dtype=torch.float32, device=dev)
-    opts = None
-    if debug or not early_stop or refill_threshold or err_metric:
-        opts = hqq_options_t(int(bool(early_stop)), _addr(out.scale_f32 if debug else None),
-                             _addr(out.zero_f32 if debug else None),
-                             _addr(out.stop_step if debug else None),
-                             _addr(out.err_init if debug else None),
-                             _addr(out.err_best if debug else None), int(refill_threshold),
-                             int(err_metric))
-    st = hqq_quantize_ex(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
-                         float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
-                         _addr(out.zero), opts, _stream_handle(stream))
-    if st != HQQ_OK:
-        raise HQQError(st, "hqq_quantize_ex")
     return out
+
+
+def _options(out: QuantizedWeight, debug: bool, early_stop: bool, refill_threshold: int,
+             err_metric: int) -> hqq_options_t:
+    return hqq_options_t(int(bool(early_stop)), _addr(out.scale_f32 if debug else None),
+                         _addr(out.zero_f32 if debug else None),
+                         _addr(out.stop_step if debug else None),
+                         _addr(out.err_init if debug else None),
+                         _addr(out.err_best if debug else None), int(refill_threshold),
+                         int(err_metric))
 
 
 @dataclass

@@ -80,6 +80,60 @@ int power_mode_of(float p) {
   return p == 1.0f ? hqq::kPowOne : (p == 0.0f ? hqq::kPowZero : hqq::kPowGeneral);
 }
 
+// hqq_options_t with its defaults filled in (opt may be NULL), validated.
+int read_options(const hqq_options_t* opt, hqq_options_t& o) {
+  o = {1, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+  if (!opt) return HQQ_OK;
+  o = *opt;
+  if (o.early_stop != 0 && o.early_stop != 1) return HQQ_ERR_INVALID_ARG;
+  if (o.refill_threshold < 0) return HQQ_ERR_INVALID_ARG;
+  if (o.err_metric < 0 || o.err_metric > 2) return HQQ_ERR_INVALID_ARG;
+  if ((o.scale_f32 && !aligned(o.scale_f32, 4)) || (o.zero_f32 && !aligned(o.zero_f32, 4)) ||
+      (o.err_init && !aligned(o.err_init, 4)) || (o.err_best && !aligned(o.err_best, 4)))
+    return HQQ_ERR_ALIGNMENT;
+  return HQQ_OK;
+}
+
+// Launch parameters of one matrix with the outputs of `o`.
+hqq::SolveParams single_matrix_params(const void* W_f16, int64_t n, int nbits, int group_size,
+                                      float p, float beta, float kappa, int iters,
+                                      void* packed_codes, void* scale_f16, void* zero_f16,
+                                      const hqq_options_t& o) {
+  hqq::SolveParams prm = {};
+  prm.W = static_cast<const uint4*>(W_f16);
+  prm.batch = nullptr;
+  prm.batch_count = 0;
+  prm.packed = static_cast<uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<uint16_t*>(zero_f16);
+  prm.scale32 = o.scale_f32;
+  prm.zero32 = o.zero_f32;
+  prm.stop_step = o.stop_step;
+  prm.err_init = o.err_init;
+  prm.err_best = o.err_best;
+  prm.ngroups = n / group_size;
+  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, o.early_stop,
+                    o.refill_threshold, o.err_metric);
+  return prm;
+}
+
+// Checks shared by the single-matrix solver entry points; `n` receives rows * cols.
+int validate_single(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                    float p, float beta, float kappa, int iters, const void* packed_codes,
+                    const void* scale_f16, const void* zero_f16, int64_t& n) {
+  int st = validate_common(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  st = validate_solver(p, beta, kappa, iters);
+  if (st != HQQ_OK) return st;
+  n = rows * cols;
+  if (n == 0) return HQQ_OK;
+  if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
+      !aligned(zero_f16, 2))
+    return HQQ_ERR_ALIGNMENT;
+  return HQQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,48 +164,56 @@ int64_t hqq_num_groups(int64_t rows, int64_t cols, int group_size) {
 int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, int group_size,
                     float p, float beta, float kappa, int iters, void* packed_codes,
                     void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream) {
-  int st = validate_common(rows, cols, nbits, group_size);
+  int64_t n = 0;
+  int st = validate_single(W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters,
+                           packed_codes, scale_f16, zero_f16, n);
+  if (st != HQQ_OK || n == 0) return st;
+  hqq_options_t o;
+  st = read_options(opt, o);
   if (st != HQQ_OK) return st;
-  st = validate_solver(p, beta, kappa, iters);
-  if (st != HQQ_OK) return st;
-  const int64_t n = rows * cols;
-  if (n == 0) return HQQ_OK;
-  if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
-  if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
-      !aligned(zero_f16, 2))
-    return HQQ_ERR_ALIGNMENT;
-  hqq_options_t o = {1, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
-  if (opt) {
-    o = *opt;
-    if (o.early_stop != 0 && o.early_stop != 1) return HQQ_ERR_INVALID_ARG;
-    if (o.refill_threshold < 0) return HQQ_ERR_INVALID_ARG;
-    if (o.err_metric < 0 || o.err_metric > 2) return HQQ_ERR_INVALID_ARG;
-    if ((o.scale_f32 && !aligned(o.scale_f32, 4)) || (o.zero_f32 && !aligned(o.zero_f32, 4)) ||
-        (o.err_init && !aligned(o.err_init, 4)) || (o.err_best && !aligned(o.err_best, 4)))
-      return HQQ_ERR_ALIGNMENT;
-  }
-
-  hqq::SolveParams prm = {};
-  prm.W = static_cast<const uint4*>(W_f16);
-  prm.batch = nullptr;
-  prm.batch_count = 0;
-  prm.packed = static_cast<uint8_t*>(packed_codes);
-  prm.scale16 = static_cast<uint16_t*>(scale_f16);
-  prm.zero16 = static_cast<uint16_t*>(zero_f16);
-  prm.scale32 = o.scale_f32;
-  prm.zero32 = o.zero_f32;
-  prm.stop_step = o.stop_step;
-  prm.err_init = o.err_init;
-  prm.err_best = o.err_best;
-  prm.ngroups = n / group_size;
-  set_solver_params(prm, nbits, group_size, p, beta, kappa, iters, o.early_stop,
-                    o.refill_threshold, o.err_metric);
-  const int power_mode = power_mode_of(p);
-
+  const hqq::SolveParams prm = single_matrix_params(W_f16, n, nbits, group_size, p, beta, kappa,
+                                                    iters, packed_codes, scale_f16, zero_f16, o);
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;
-  hipError_t err = hqq::launch_solve(prm, group_size, power_mode, cus,
+  hipError_t err = hqq::launch_solve(prm, group_size, power_mode_of(p), cus,
                                      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int64_t hqq_tensor_stop_workspace_bytes(int iters) {
+  if (iters < 0 || iters > kMaxIters) return -1;
+  return hqq::tensor_stop_workspace_bytes(iters);
+}
+
+int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int nbits,
+                             int group_size, float p, float beta, float kappa, int iters,
+                             void* packed_codes, void* scale_f16, void* zero_f16,
+                             const hqq_options_t* opt, void* totals_f64, void* t_star_i32,
+                             void* workspace, void* stream) {
+  int64_t n = 0;
+  int st = validate_single(W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters,
+                           packed_codes, scale_f16, zero_f16, n);
+  if (st != HQQ_OK || n == 0) return st;
+  hqq_options_t o;
+  st = read_options(opt, o);
+  if (st != HQQ_OK) return st;
+  if (!workspace) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(workspace, 8) || (totals_f64 && !aligned(totals_f64, 8)) ||
+      (t_star_i32 && !aligned(t_star_i32, 4)))
+    return HQQ_ERR_ALIGNMENT;
+  o.early_stop = 0;  // pass 2 runs the t* updates without a stop
+  o.refill_threshold = 0;
+  const hqq::SolveParams prm = single_matrix_params(W_f16, n, nbits, group_size, p, beta, kappa,
+                                                    iters, packed_codes, scale_f16, zero_f16, o);
+  hqq::TensorStopParams X = {};
+  X.t_star = static_cast<int*>(workspace);
+  X.partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + hqq::kTensorStopHeader);
+  X.totals = static_cast<double*>(totals_f64);
+  X.t_star_out = static_cast<int*>(t_star_i32);
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_tensor_stop(prm, X, group_size, power_mode_of(p), cus,
+                                           static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 

@@ -128,6 +128,43 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
                     float p, float beta, float kappa, int iters, void* packed_codes,
                     void* scale_f16, void* zero_f16, const hqq_options_t* opt, void* stream);
 
+/*
+ * hqq_quantize_tensor_stop -- hqq_quantize_ex with the early exit of section 4.1
+ * taken at the scope of the whole matrix instead of each group (the page does not
+ * say over what the error is measured; this is the reading where it is the error of
+ * the whole tensor):
+ *   E_t  = sum over all groups of e_t, the group error of hqq_quantize in weight
+ *          units (with opt->err_metric), for t = 0 .. iters, every group iterating
+ *          without a stop;
+ *   t*   = the end of the strictly decreasing run E_0 > E_1 > ... > E_t*;
+ *   outputs: exactly those of hqq_quantize_ex with early_stop = 0 and iters = t*
+ *          (every group returns the z after t* updates; stop_step = t* everywhere).
+ * E_t is accumulated in fp64 from the fp32 group errors in an order fixed for a
+ * given device, so repeated calls give the same E_t and t*.
+ *
+ * opt          NULL or the optional outputs and err_metric of hqq_quantize_ex;
+ *              early_stop and refill_threshold are not used.
+ * totals_f64   NULL or iters + 1 doubles (device, 8-byte aligned): E_0 .. E_iters.
+ * t_star_i32   NULL or one int32 (device, 4-byte aligned): t*.
+ * workspace    hqq_tensor_stop_workspace_bytes(iters) bytes of device memory,
+ *              8-byte aligned, owned by the caller: per-wavefront partial totals and
+ *              t*, written and read on `stream` (no allocation, no memset); it must
+ *              not be shared by calls that may run at the same time.
+ * Three kernels run in stream order: every group through steps 0 .. iters
+ * (accumulating the totals), a one-block decision, and every group through t*
+ * updates writing the outputs.  rows*cols == 0 is a no-op (nothing is written).
+ * Other arguments, conventions and errors as for hqq_quantize_ex.
+ */
+int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int nbits,
+                             int group_size, float p, float beta, float kappa, int iters,
+                             void* packed_codes, void* scale_f16, void* zero_f16,
+                             const hqq_options_t* opt, void* totals_f64, void* t_star_i32,
+                             void* workspace, void* stream);
+
+/* Bytes of the workspace of hqq_quantize_tensor_stop for `iters` (256 + 131072 *
+ * (iters + 1)); -1 for iters outside 0 .. 255. */
+int64_t hqq_tensor_stop_workspace_bytes(int iters);
+
 /* One input matrix of hqq_quantize_batch (32 bytes; the same layout is read on
  * the host and on the device). */
 typedef struct {

@@ -125,6 +125,50 @@ def test_quantize_ex_option_validation(lib):
                               0) == hq.HQQ_ERR_ALIGNMENT
 
 
+def _ts(opt=None, **kw):
+    a = dict(W_f16=FAKE, rows=16, cols=128, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01,
+             iters=20, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, options=opt,
+             totals_f64=FAKE, t_star_i32=FAKE, workspace=FAKE, stream=0)
+    a.update(kw)
+    return hq.hqq_quantize_tensor_stop(**a)
+
+
+def test_tensor_stop_workspace_bytes(lib):
+    assert hq.hqq_tensor_stop_workspace_bytes(0) == 256 + 131072
+    assert hq.hqq_tensor_stop_workspace_bytes(20) == 256 + 21 * 131072
+    assert hq.hqq_tensor_stop_workspace_bytes(255) == 256 + 256 * 131072
+    assert hq.hqq_tensor_stop_workspace_bytes(-1) == -1
+    assert hq.hqq_tensor_stop_workspace_bytes(256) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nbits=5), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(group_size=48), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(cols=100), hq.HQQ_ERR_INVALID_ARG),
+    (dict(p=1.5), hq.HQQ_ERR_INVALID_ARG),
+    (dict(iters=256), hq.HQQ_ERR_INVALID_ARG),
+    (dict(W_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(workspace=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(workspace=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    (dict(totals_f64=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    (dict(t_star_i32=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
+    (dict(W_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_tensor_stop_rejects_before_launch(lib, kw, status):
+    assert _ts(**kw) == status
+
+
+def test_tensor_stop_options_and_empty(lib):
+    for bad in (-1, 3):
+        assert _ts(hq.hqq_options_t(1, 0, 0, 0, 0, 0, 0, bad)) == hq.HQQ_ERR_INVALID_ARG
+    assert _ts(hq.hqq_options_t(1, FAKE + 2, 0, 0, 0, 0, 0, 0)) == hq.HQQ_ERR_ALIGNMENT
+    assert _ts(hq.hqq_options_t(1, 0, 0, 0, 0, 0, -1, 0)) == hq.HQQ_ERR_INVALID_ARG
+    # no group: a no-op that needs no buffer at all
+    assert _ts(rows=0, W_f16=0, packed_codes=0, scale_f16=0, zero_f16=0, totals_f64=0,
+               t_star_i32=0, workspace=0) == hq.HQQ_OK
+
+
 @pytest.mark.parametrize("args,status", [
     ((FAKE, FAKE, FAKE, 16, 128, 6, 64, FAKE), hq.HQQ_ERR_UNSUPPORTED),
     ((FAKE, FAKE, FAKE, 16, 100, 4, 64, FAKE), hq.HQQ_ERR_INVALID_ARG),
