@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weights quantized/sec (G/s) + % of binding VALU/HBM roofline, 1 MI355X"
 PROFILE_PMC = os.path.join(ROOT, "profiles", "hqq_solve_llama70b_pmc.json")
-KERNEL_SRC = os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", "hqq_kernels.hip")
+# Sources of the solver kernel (the profile's counters are void once they change).
+KERNEL_SRC = [os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", f)
+              for f in ("hqq_solver.h", "hqq_kernels.hip", "hqq_internal.h")]
 
 # MI355X: 256 CUs x 4 SIMDs x 16 fp32 lanes per clock x 2.4 GHz.  Packed-fp32 issue is
 # not used, so this is the VALU ceiling for the solver; v_log_f32 / v_exp_f32 issue at
@@ -53,8 +55,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(weights_per_launch: float):
@@ -239,6 +244,123 @@ def measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero, strea
     return out
 
 
+def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps=3):
+    """Solver variants on the given matrices (one call per matrix, HIP events on the launch
+    stream, `reps` passes): per-group early stop on the lp (default), l1 and l2 error, no
+    early stop (all iterations), the whole-tensor early stop (hqq_quantize_tensor_stop) and
+    plain min-max round-to-nearest (iters = 0).  For each, an untimed pass measures the
+    reconstruction of W from the stored binary16 s and z (hqq_dequantize): relative
+    Frobenius error, mean |W - W'| relative to mean |W|, and the lp error sum |W - W'|^p per
+    weight; the default variant is also measured with 8-bit meta-quantized s (groups of
+    128) and z (one group per matrix).  VALU lane-ops use the same per-weight counts as the
+    roofline (the tensor stop runs iters + 1 evaluations, then t* + 1 more)."""
+    n_w = sum(W.numel() for W in Ws)
+    iters = solver.iters
+    variants = [("per_group_lp", dict(early_stop=1, err_metric=0, iters=iters)),
+                ("per_group_l1", dict(early_stop=1, err_metric=1, iters=iters)),
+                ("per_group_l2", dict(early_stop=1, err_metric=2, iters=iters)),
+                ("no_stop", dict(early_stop=0, err_metric=0, iters=iters)),
+                ("tensor_stop", dict(tensor=True, err_metric=0, iters=iters)),
+                ("rtn", dict(early_stop=0, err_metric=0, iters=0))]
+    wsb = hq.hqq_tensor_stop_workspace_bytes(iters)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    totals = torch.empty(iters + 1, dtype=torch.float64, device=dev)
+    tstar = torch.empty(len(Ws), dtype=torch.int32, device=dev)
+    out = {"matrices": [list(W.shape) for W in Ws], "weights": n_w, "reps": reps,
+           "per_setting": []}
+
+    def quality(qs, meta=False):
+        fro2 = w2 = l1 = w1 = lp = 0.0
+        for W, q in zip(Ws, qs):
+            if meta:
+                mz = hq.meta_quantize(q.zero.reshape(-1), 0)
+                ms = hq.meta_quantize(q.scale.reshape(-1), 128)
+                q = hq.QuantizedWeight(packed=q.packed, rows=q.rows, cols=q.cols, nbits=q.nbits,
+                                       group_size=q.group_size,
+                                       zero=hq.meta_dequantize(mz).view(q.zero.shape),
+                                       scale=hq.meta_dequantize(ms).view(q.scale.shape))
+            Wd = hq.dequantize(q)
+            w = W.double()
+            d = w - Wd.double()
+            fro2 += float(d.square().sum())
+            w2 += float(w.square().sum())
+            a = d.abs()
+            l1 += float(a.sum())
+            w1 += float(w.abs().sum())
+            lp += float(a.pow(solver.p).sum())
+            del w, d, a, Wd
+        return {"rel_fro": round((fro2 / w2) ** 0.5, 6), "rel_l1": round(l1 / w1, 6),
+                "lp_per_weight": float(f"{lp / n_w:.6g}")}
+
+    for nb, g in settings:
+        outs = [hq.quantize(W, nb, g, iters=0) for W in Ws]  # output buffers, reused
+        stops = [torch.empty(W.numel() // g, dtype=torch.uint8, device=dev) for W in Ws]
+        rows = []
+        for name, v in variants:
+            calls = []
+            for k, (W, q) in enumerate(zip(Ws, outs)):
+                r, c = W.shape
+                if v.get("tensor"):
+                    opts = hq.hqq_options_t(1, 0, 0, stops[k].data_ptr(), 0, 0, 0, v["err_metric"])
+                    calls.append((lib.hqq_quantize_tensor_stop,
+                                  (W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
+                                   v["iters"], q.packed.data_ptr(), q.scale.data_ptr(),
+                                   q.zero.data_ptr(), opts, totals.data_ptr(),
+                                   tstar.data_ptr() + 4 * k, ws.data_ptr(), sh)))
+                else:
+                    opts = hq.hqq_options_t(v["early_stop"], 0, 0, stops[k].data_ptr(), 0, 0, 0,
+                                            v["err_metric"])
+                    calls.append((lib.hqq_quantize_ex,
+                                  (W.data_ptr(), r, c, nb, g, solver.p, solver.beta, solver.kappa,
+                                   v["iters"], q.packed.data_ptr(), q.scale.data_ptr(),
+                                   q.zero.data_ptr(), opts, sh)))
+
+            def run():
+                for fn, a in calls:
+                    assert fn(*a) == 0
+
+            run()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            # VALU lane-ops from the stop steps of the last pass
+            t = torch.cat([x.to(torch.int64) for x in stops]).cpu().numpy()
+            g_per = np.array([W.numel() // g for W in Ws])
+            if v.get("tensor"):
+                ts = tstar.cpu().numpy().astype(np.int64)
+                n_eval = (v["iters"] + 1) + (ts + 1)
+                n_upd = v["iters"] + ts
+                ops = float(np.sum(g_per * g * (2 * OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval +
+                                                OPS_UPDATE * n_upd)))
+                extra = {"t_star_per_matrix": [int(x) for x in ts]}
+            else:
+                it = v["iters"]
+                if v["early_stop"]:
+                    n_eval = np.where(t == it, it + 1, t + 2)
+                else:
+                    n_eval = np.full(t.shape, it + 1)
+                ops = float(g * np.sum(OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval +
+                                       OPS_UPDATE * (n_eval - 1)))
+                extra = {"mean_stop_step": round(float(t.mean()), 4)}
+            row = {"variant": name, "ms": round(ms, 3),
+                   "G_weights_per_s": round(n_w / (ms * 1e-3) / 1e9, 1),
+                   "valu_frac": round(ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                   **extra, "quality": quality(outs)}
+            if name == "per_group_lp":
+                row["quality_meta8"] = quality(outs, meta=True)
+            log(f"variant b{nb}g{g} {row}")
+            rows.append(row)
+        out["per_setting"].append({"setting": f"b{nb}g{g}", "variants": rows})
+        del outs, stops
+    return out
+
+
 def summarize_meta(kt_dir: str, out_dir: str, command: str):
     """Kernel-trace statistics of the meta-quantization kernels (profiles/)."""
     import csv
@@ -276,6 +398,10 @@ def main():
                     help="one hqq_quantize launch per matrix instead of one batched launch "
                          "per setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the solver-variant measurement on the first layer")
+    ap.add_argument("--variants-only", action="store_true",
+                    help="only measure the solver variants (JSON on stderr)")
     ap.add_argument("--no-meta", action="store_true",
                     help="skip the 8-bit meta-quantization measurement (next_rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -400,6 +526,11 @@ def main():
         if events is not None:
             events[cur][1].record(stream)
 
+    if args.variants_only:
+        log(json.dumps(measure_variants(hq, lib, torch, Ws[:7], settings, solver, stream, sh,
+                                        dev)))
+        return
+
     if args.profile_meta:
         log(json.dumps(measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero,
                                     stream, sh, dev)))
@@ -493,6 +624,11 @@ def main():
                             dev)
         log(f"meta quantization: {meta}")
 
+    # ---- next row: solver variants on the first layer (untimed above) ------------------
+    variants = None
+    if not args.no_variants:
+        variants = measure_variants(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
+
     # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -565,7 +701,7 @@ def main():
         },
         "per_setting": detail,
         "cpu_baseline": cpu,
-        "next_rows": {"meta_quantization": meta},
+        "next_rows": {"meta_quantization": meta, "solver_variants": variants},
     }
     print(json.dumps(out), flush=True)
 
