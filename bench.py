@@ -253,7 +253,9 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
     Frobenius error, mean |W - W'| relative to mean |W|, and the lp error sum |W - W'|^p per
     weight; the default variant is also measured with 8-bit meta-quantized s (groups of
     128) and z (one group per matrix).  VALU lane-ops use the same per-weight counts as the
-    roofline (the tensor stop runs iters + 1 evaluations, then t* + 1 more)."""
+    roofline.  For the tensor stop, `nominal_valu_frac` counts the iters + 1 evaluations of
+    pass 1 and the t* + 1 of pass 2 that the definition asks for; its kernels skip the steps
+    of wavefronts whose groups all sit at a fixed point, so it can exceed 1."""
     n_w = sum(W.numel() for W in Ws)
     iters = solver.iters
     variants = [("per_group_lp", dict(early_stop=1, err_metric=0, iters=iters)),
@@ -348,9 +350,10 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
                 ops = float(g * np.sum(OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval +
                                        OPS_UPDATE * (n_eval - 1)))
                 extra = {"mean_stop_step": round(float(t.mean()), 4)}
+            frac_key = "nominal_valu_frac" if v.get("tensor") else "valu_frac"
             row = {"variant": name, "ms": round(ms, 3),
                    "G_weights_per_s": round(n_w / (ms * 1e-3) / 1e9, 1),
-                   "valu_frac": round(ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                   frac_key: round(ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
                    **extra, "quality": quality(outs)}
             if name == "per_group_lp":
                 row["quality_meta8"] = quality(outs, meta=True)
@@ -361,27 +364,43 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
     return out
 
 
-def summarize_meta(kt_dir: str, out_dir: str, command: str):
-    """Kernel-trace statistics of the meta-quantization kernels (profiles/)."""
-    import csv
-    rows = []
-    for r in csv.DictReader(open(os.path.join(kt_dir, "kt_kernel_stats.csv"))):
-        if "meta_" in r["Name"]:
-            name = r["Name"].replace("void ", "").replace("hqq::(anonymous namespace)::", "")
-            name = name.split("(")[0]
-            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
-                         float(r["TotalDurationNs"]) / 1e6))
-    lines = ["# Meta-quantization kernels on the Llama-2-70B-shaped stack: rocprofv3 summary", "",
+KERNEL_SUMMARIES = {
+    # name: (kernel-name filter, file, title, description)
+    "meta": ("meta_", "hqq_meta_llama70b.md",
+             "Meta-quantization kernels on the Llama-2-70B-shaped stack",
              "The z (one group per matrix: init, reduce, quantize) and s (groups of 128) arenas "
              "of the whole stack after the solver, hqq_meta_quantize_batch, both settings, 1 "
-             "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the largest "
-             "matrix alone (bench.py measure_meta).", "",
+             "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the "
+             "largest matrix alone (bench.py measure_meta)."),
+    "variants": ("hqq", "hqq_solver_variants_llama70b_layer0.md",
+                 "Solver variants on the 7 matrices of Llama-2-70B layer 0",
+                 "One call per matrix and variant (per-group stop on the lp / l1 / l2 error: "
+                 "hqq_solve_kernel<G, PM> with PM = shrink mode | metric << 2, no stop, "
+                 "whole-tensor stop: hqq_lockstep_kernel<G, PM, pass 1 | pass 2> and "
+                 "hqq_tensor_total_kernel, RTN), b2 g32 and b4 g64, 1 warm-up + 3 timed passes "
+                 "each, plus the untimed dequantization of the quality report "
+                 "(bench.py measure_variants)."),
+}
+
+
+def summarize_kernels(which: str, kt_dir: str, out_dir: str, command: str):
+    """Kernel-trace statistics of one family of this library's kernels (profiles/)."""
+    import csv
+    filt, fname, title, desc = KERNEL_SUMMARIES[which]
+    rows = []
+    for r in csv.DictReader(open(os.path.join(kt_dir, "kt_kernel_stats.csv"))):
+        if filt in r["Name"] and "hqq" in r["Name"]:
+            name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "")
+            name = name.replace("hqq::", "").split("(")[0]
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6))
+    lines = [f"# {title}: rocprofv3 summary", "", desc, "",
              "| kernel | calls | avg duration (us) | total (ms) |", "|---|---|---|---|"]
     for name, calls, avg, tot in sorted(rows):
         lines.append(f"| {name} | {calls} | {avg:.2f} | {tot:.3f} |")
     lines += ["", "Command:", "", "```", command, "```", ""]
     os.makedirs(out_dir, exist_ok=True)
-    with open(os.path.join(out_dir, "hqq_meta_llama70b.md"), "w") as f:
+    with open(os.path.join(out_dir, fname), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -412,15 +431,17 @@ def main():
     ap.add_argument("--profile-meta", action="store_true",
                     help="generate, run the solver once per setting, then only the meta "
                          "quantization measurement (for rocprofv3 runs)")
-    ap.add_argument("--summarize-meta", metavar="KT_DIR",
-                    help="write profiles/ summary of the meta kernels from a kernel trace")
+    ap.add_argument("--summarize-kernels", nargs=2, metavar=("WHICH", "KT_DIR"),
+                    help="write the profiles/ summary of one kernel family (meta, variants) "
+                         "from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write profiles/ summaries from rocprofv3 counter and trace output")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
 
-    if args.summarize_meta:
-        summarize_meta(args.summarize_meta, os.path.join(ROOT, "profiles"), args.profile_command)
+    if args.summarize_kernels:
+        summarize_kernels(args.summarize_kernels[0], args.summarize_kernels[1],
+                          os.path.join(ROOT, "profiles"), args.profile_command)
         return
 
     if args.summarize_profiles:

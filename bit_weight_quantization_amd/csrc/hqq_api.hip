@@ -8,6 +8,7 @@
 
 #include "../../include/hqq.h"
 #include "hqq_internal.h"
+#include "hqq_tensor_stop.h"
 
 namespace {
 
@@ -206,7 +207,7 @@ int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int 
   const hqq::SolveParams prm = single_matrix_params(W_f16, n, nbits, group_size, p, beta, kappa,
                                                     iters, packed_codes, scale_f16, zero_f16, o);
   hqq::TensorStopParams X = {};
-  X.t_star = static_cast<int*>(workspace);
+  X.totals_ws = static_cast<double*>(workspace);
   X.partials = reinterpret_cast<double*>(static_cast<char*>(workspace) + hqq::kTensorStopHeader);
   X.totals = static_cast<double*>(totals_f64);
   X.t_star_out = static_cast<int*>(t_star_i32);

@@ -50,17 +50,6 @@ struct SolveParams {
   int err_metric;          // ErrMetric of the early stop
 };
 
-// Buffers of the whole-tensor stop.  The caller's workspace holds t* in its first
-// kTensorStopHeader bytes and the per-wavefront partial step totals after it.
-struct TensorStopParams {
-  double* partials;        // [iters + 1][2 * nwaves] fp64 partial totals (pass 1)
-  int64_t nwaves;          // wavefronts of pass 1 (set by the launcher)
-  int* t_star;             // t* in the workspace: written by the decision, read by pass 2
-  double* totals;          // optional E_0 .. E_iters
-  int* t_star_out;         // optional copy of t*
-};
-constexpr int64_t kTensorStopHeader = 256;
-
 struct DequantParams {
   const uint8_t* packed;
   const uint16_t* scale16;
@@ -75,10 +64,6 @@ struct DequantParams {
 hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream);  // batched when prm.batch != nullptr
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream);
-// Whole-tensor stop: pass 1, the decision and pass 2 on `stream` (X.nwaves is set here).
-hipError_t launch_tensor_stop(const SolveParams& prm, const TensorStopParams& X, int group_size,
-                              int power_mode, int cus, hipStream_t stream);
-int64_t tensor_stop_workspace_bytes(int iters);
 // Meta quantization (M = 0: one group of all n values, using the workspace of
 // 2 * kMetaPartials words for per-block partial minima and maxima).
 constexpr int kMetaPartials = 1024;

@@ -73,9 +73,6 @@ struct SolveLds {
   uint4 done_hdr[kWavesPerBlock][kDone][2];
 };
 
-__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
-__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
-
 template <int G>
 __device__ __forceinline__ void store_u(float* slot_u, int sl, const float (&u)[kLaneElems]) {
   float4* dst = reinterpret_cast<float4*>(slot_u + sl * kLaneElems);
@@ -363,7 +360,7 @@ constexpr int kChunkBatches = 4;  // chunk = 4 prime batches
 
 template <int G, int PM>
 struct SolveLaunch {
-  static hipError_t run(SolveParams prm, const TensorStopParams&, int cus, hipStream_t st) {
+  static hipError_t run(SolveParams prm, const int&, int cus, hipStream_t st) {
     auto kernel = hqq_solve_kernel<G, PM, false>;
     if constexpr (err_mode(PM) == kErrP) {  // batched launches always use the lp error
       if (prm.batch) kernel = hqq_solve_kernel<G, PM, true>;
@@ -384,7 +381,7 @@ struct SolveLaunch {
 
 hipError_t launch_solve(const SolveParams& prm, int group_size, int power_mode, int cus,
                         hipStream_t stream) {
-  return dispatch_group<SolveLaunch>(prm, TensorStopParams{}, group_size, power_mode, cus, stream);
+  return dispatch_group<SolveLaunch>(prm, 0, group_size, power_mode, cus, stream);
 }
 
 hipError_t launch_dequant(const DequantParams& prm, int blocks, hipStream_t stream) {

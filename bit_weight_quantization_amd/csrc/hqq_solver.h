@@ -265,6 +265,9 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
   return g;
 }
 
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
 // Orders this wave's LDS accesses: lanes hand group state to other lanes of the same
 // wavefront through LDS (the standby pool and the done ring below).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -470,9 +473,10 @@ hipError_t resident_waves(K kernel, int cus, int64_t& waves) {
   return hipSuccess;
 }
 
-// Dispatch on the group size, the early-stop metric and the shrink's power mode.
-template <template <int, int> class Launch, int G, int EM>
-hipError_t dispatch_power(const SolveParams& prm, const TensorStopParams& X, int power_mode,
+// Dispatch on the group size, the early-stop metric and the shrink's power mode;
+// `X` is passed through to Launch<G, PM>::run (launch-specific buffers).
+template <template <int, int> class Launch, int G, int EM, class Extra>
+hipError_t dispatch_power(const SolveParams& prm, const Extra& X, int power_mode,
                           int cus, hipStream_t st) {
   switch (power_mode) {
     case kPowOne: return Launch<G, kPowOne | (EM << 2)>::run(prm, X, cus, st);
@@ -481,24 +485,24 @@ hipError_t dispatch_power(const SolveParams& prm, const TensorStopParams& X, int
   }
 }
 
-template <template <int, int> class Launch, int G>
-hipError_t dispatch_metric(const SolveParams& prm, const TensorStopParams& X, int power_mode,
+template <template <int, int> class Launch, int G, class Extra>
+hipError_t dispatch_metric(const SolveParams& prm, const Extra& X, int power_mode,
                            int cus, hipStream_t st) {
   switch (prm.err_metric) {
-    case kErrL1: return dispatch_power<Launch, G, kErrL1>(prm, X, power_mode, cus, st);
-    case kErrL2: return dispatch_power<Launch, G, kErrL2>(prm, X, power_mode, cus, st);
-    default: return dispatch_power<Launch, G, kErrP>(prm, X, power_mode, cus, st);
+    case kErrL1: return dispatch_power<Launch, G, kErrL1, Extra>(prm, X, power_mode, cus, st);
+    case kErrL2: return dispatch_power<Launch, G, kErrL2, Extra>(prm, X, power_mode, cus, st);
+    default: return dispatch_power<Launch, G, kErrP, Extra>(prm, X, power_mode, cus, st);
   }
 }
 
-template <template <int, int> class Launch>
-hipError_t dispatch_group(const SolveParams& prm, const TensorStopParams& X, int group_size,
+template <template <int, int> class Launch, class Extra>
+hipError_t dispatch_group(const SolveParams& prm, const Extra& X, int group_size,
                           int power_mode, int cus, hipStream_t st) {
   switch (group_size) {
-    case 16: return dispatch_metric<Launch, 16>(prm, X, power_mode, cus, st);
-    case 32: return dispatch_metric<Launch, 32>(prm, X, power_mode, cus, st);
-    case 64: return dispatch_metric<Launch, 64>(prm, X, power_mode, cus, st);
-    case 128: return dispatch_metric<Launch, 128>(prm, X, power_mode, cus, st);
+    case 16: return dispatch_metric<Launch, 16, Extra>(prm, X, power_mode, cus, st);
+    case 32: return dispatch_metric<Launch, 32, Extra>(prm, X, power_mode, cus, st);
+    case 64: return dispatch_metric<Launch, 64, Extra>(prm, X, power_mode, cus, st);
+    case 128: return dispatch_metric<Launch, 128, Extra>(prm, X, power_mode, cus, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -147,12 +147,13 @@ int hqq_quantize_ex(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
  * totals_f64   NULL or iters + 1 doubles (device, 8-byte aligned): E_0 .. E_iters.
  * t_star_i32   NULL or one int32 (device, 4-byte aligned): t*.
  * workspace    hqq_tensor_stop_workspace_bytes(iters) bytes of device memory,
- *              8-byte aligned, owned by the caller: per-wavefront partial totals and
- *              t*, written and read on `stream` (no allocation, no memset); it must
- *              not be shared by calls that may run at the same time.
+ *              8-byte aligned, owned by the caller: per-block partial totals and the
+ *              totals, written and read on `stream` (no allocation, no memset); it
+ *              must not be shared by calls that may run at the same time.
  * Three kernels run in stream order: every group through steps 0 .. iters
- * (accumulating the totals), a one-block decision, and every group through t*
- * updates writing the outputs.  rows*cols == 0 is a no-op (nothing is written).
+ * (accumulating the totals), one block per step adding them up, and every group
+ * through t* updates writing the outputs (t* found on the device: no host
+ * synchronization).  rows*cols == 0 is a no-op (nothing is written).
  * Other arguments, conventions and errors as for hqq_quantize_ex.
  */
 int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int nbits,
@@ -161,7 +162,7 @@ int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int 
                              const hqq_options_t* opt, void* totals_f64, void* t_star_i32,
                              void* workspace, void* stream);
 
-/* Bytes of the workspace of hqq_quantize_tensor_stop for `iters` (256 + 131072 *
+/* Bytes of the workspace of hqq_quantize_tensor_stop for `iters` (2048 + 16384 *
  * (iters + 1)); -1 for iters outside 0 .. 255. */
 int64_t hqq_tensor_stop_workspace_bytes(int iters);
 

@@ -134,9 +134,9 @@ def _ts(opt=None, **kw):
 
 
 def test_tensor_stop_workspace_bytes(lib):
-    assert hq.hqq_tensor_stop_workspace_bytes(0) == 256 + 131072
-    assert hq.hqq_tensor_stop_workspace_bytes(20) == 256 + 21 * 131072
-    assert hq.hqq_tensor_stop_workspace_bytes(255) == 256 + 256 * 131072
+    assert hq.hqq_tensor_stop_workspace_bytes(0) == 2048 + 16384
+    assert hq.hqq_tensor_stop_workspace_bytes(20) == 2048 + 21 * 16384
+    assert hq.hqq_tensor_stop_workspace_bytes(255) == 2048 + 256 * 16384
     assert hq.hqq_tensor_stop_workspace_bytes(-1) == -1
     assert hq.hqq_tensor_stop_workspace_bytes(256) == -1
 
