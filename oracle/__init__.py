@@ -81,6 +81,8 @@ def _load():
     lib.oracle_meta_quantize.argtypes = [P, I64, I64, P, P, P]
     lib.oracle_meta_dequantize.restype = I
     lib.oracle_meta_dequantize.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_hqq_matmul.restype = I
+    lib.oracle_hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P]
     _lib = lib
     return lib
 
@@ -345,3 +347,25 @@ def meta_dequantize(codes: np.ndarray, scale16: np.ndarray, offset16: np.ndarray
     if rc != 0:
         raise ValueError("oracle_meta_dequantize rejected its arguments")
     return out
+
+
+def hqq_matmul(X_f16: np.ndarray, packed: np.ndarray, scale_f16: np.ndarray,
+               zero_f16: np.ndarray, N: int, nbits: int, group_size: int) -> np.ndarray:
+    """Y = X Q^-1(W_q)^T in fp64 (hqq_oracle.c, oracle_hqq_matmul): X is M x K binary16
+    (bit patterns or float16), the weight N x K as hqq_quantize stores it."""
+    X = np.ascontiguousarray(X_f16)
+    if X.dtype == np.float16:
+        X = X.view(np.uint16)
+    assert X.dtype == np.uint16 and X.ndim == 2
+    M, K = X.shape
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    sc = np.ascontiguousarray(scale_f16).view(np.uint16).ravel()
+    zr = np.ascontiguousarray(zero_f16).view(np.uint16).ravel()
+    assert sc.size == N * (K // group_size) and zr.size == sc.size
+    assert packed.size >= (N * K * nbits + 7) // 8
+    Y = np.empty((M, N), np.float64)
+    rc = _load().oracle_hqq_matmul(_ptr(X), M, K, _ptr(packed), _ptr(sc), _ptr(zr), N, nbits,
+                                   group_size, _ptr(Y))
+    if rc != 0:
+        raise ValueError("oracle_hqq_matmul rejected its arguments")
+    return Y

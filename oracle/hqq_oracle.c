@@ -469,3 +469,45 @@ int oracle_hqq_quantize_tensor_stop(const uint16_t* W_f16, int64_t rows, int64_t
     return -1;
   return t_star;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Product with the quantized weight, the consumer of the stored format:       */
+/* y = x Q^-1(W_q)^T with the inverse quantizer Q^-1(W_q) = s (W_q - z) of     */
+/* section 2, applied to the stored codes and binary16 s and z.               */
+/* ------------------------------------------------------------------------- */
+
+/* X: M x K binary16 activations, row-major.  The weight is N x K (row n holds the
+ * weights of output n, grouped along K) as oracle_hqq_quantize stores it: packed
+ * codes, binary16 s and z per group.  Y (M x N, fp64):
+ *   Y[m][n] = sum over k of x[m][k] * s[n][k/g] * (q[n][k] - z[n][k/g]),
+ * each term computed as (x*s) * (q - z) (x*s and q - z are exact in fp64, the
+ * product is rounded once) and summed in index order.  Returns 0, or -1 for
+ * invalid arguments. */
+int oracle_hqq_matmul(const uint16_t* X_f16, int64_t M, int64_t K, const uint8_t* packed,
+                      const uint16_t* scale_f16, const uint16_t* zero_f16, int64_t N, int nbits,
+                      int group_size, double* Y) {
+  if (M < 0 || K < 0 || N < 0 || group_size <= 0 || K % group_size != 0) return -1;
+  if (nbits < 1 || nbits > 8) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  const int64_t gpr = K / group_size; /* groups per weight row */
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t elem = n * K + k; /* row-major element index of the weight */
+        unsigned c = 0;
+        for (int b = 0; b < nbits; ++b) {
+          const int64_t bit = elem * nbits + b;
+          c |= (unsigned)((packed[bit >> 3] >> (bit & 7)) & 1) << b;
+        }
+        const int64_t gi = n * gpr + k / group_size;
+        const double x = oracle_f16_to_f64(X_f16[m * K + k]);
+        const double s = oracle_f16_to_f64(scale_f16[gi]);
+        const double z = oracle_f16_to_f64(zero_f16[gi]);
+        acc += (x * s) * ((double)c - z);
+      }
+      Y[m * N + n] = acc;
+    }
+  }
+  return 0;
+}

@@ -66,4 +66,7 @@ int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, u
                              uint16_t* scale16, uint16_t* offset16);
 int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,
                            const uint16_t* offset16, int64_t n, int64_t group, uint16_t* out16);
+int oracle_hqq_matmul(const uint16_t* X_f16, int64_t M, int64_t K, const uint8_t* packed,
+                      const uint16_t* scale_f16, const uint16_t* zero_f16, int64_t N, int nbits,
+                      int group_size, double* Y);
 #endif

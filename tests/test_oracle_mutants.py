@@ -65,6 +65,18 @@ MUTANTS = {
                                "oracle_f16_to_f64(offset16[gi]) -"),
     "meta dequant group off by one": ("const int64_t gi = i / gs;",
                                       "const int64_t gi = (i + 1) / gs;"),
+    "matmul drops the zero-point": ("acc += (x * s) * ((double)c - z);",
+                                    "acc += (x * s) * ((double)c);"),
+    "matmul adds the zero-point": ("acc += (x * s) * ((double)c - z);",
+                                   "acc += (x * s) * ((double)c + z);"),
+    "matmul reads the weight transposed": ("const int64_t elem = n * K + k;",
+                                           "const int64_t elem = k * N + n;"),
+    "matmul group along the wrong axis": ("const int64_t gi = n * gpr + k / group_size;",
+                                          "const int64_t gi = (k / group_size) * N + n % gpr;"),
+    "matmul code bits reversed": ("const int64_t bit = elem * nbits + b;",
+                                  "const int64_t bit = elem * nbits + (nbits - 1 - b);"),
+    "matmul skips the last k": ("for (int64_t k = 0; k < K; ++k) {\n        const int64_t elem",
+                                "for (int64_t k = 0; k < K - 1; ++k) {\n        const int64_t elem"),
 }
 
 
@@ -80,6 +92,7 @@ def test_pins_catch_mutant(name, tmp_path):
     src_path.write_text(src.replace(before, after, 1))
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_meta_pins.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_meta_pins.py",
+                        "tests/test_oracle_matmul_pins.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode != 0, f"mutant {name!r} survived the pins:\n{r.stdout[-2000:]}"
