@@ -27,7 +27,7 @@ HQQ_ERR_LAUNCH = 4
 
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
-                    "hqq_quantize_tensor_stop", "hqq_tensor_stop_workspace_bytes",
+                    "hqq_quantize_tensor_stop", "hqq_tensor_stop_workspace_bytes", "hqq_matmul",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_tensor_stop.restype = I
     lib.hqq_quantize_tensor_stop.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
                                              ctypes.POINTER(hqq_options_t), P, P, P, P]
+    lib.hqq_matmul.restype = I
+    lib.hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P, I, P]
     lib.hqq_tensor_stop_workspace_bytes.restype = I64
     lib.hqq_tensor_stop_workspace_bytes.argtypes = [I]
     lib.hqq_quantize_batch.restype = I
@@ -138,6 +140,12 @@ def hqq_quantize_tensor_stop(W_f16: int, rows: int, cols: int, nbits: int, group
     return load_library().hqq_quantize_tensor_stop(W_f16, rows, cols, nbits, group_size, p, beta,
                                                    kappa, iters, packed_codes, scale_f16, zero_f16,
                                                    opt, totals_f64, t_star_i32, workspace, stream)
+
+
+def hqq_matmul(X_f16: int, M: int, K: int, packed_codes: int, scale_f16: int, zero_f16: int,
+               N: int, nbits: int, group_size: int, Y: int, out_f32: int, stream: int = 0) -> int:
+    return load_library().hqq_matmul(X_f16, M, K, packed_codes, scale_f16, zero_f16, N, nbits,
+                                     group_size, Y, out_f32, stream)
 
 
 def hqq_tensor_stop_workspace_bytes(iters: int) -> int:
@@ -309,6 +317,28 @@ def _options(out: QuantizedWeight, debug: bool, early_stop: bool, refill_thresho
                          _addr(out.err_init if debug else None),
                          _addr(out.err_best if debug else None), int(refill_threshold),
                          int(err_metric))
+
+
+def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, stream=None):
+    """Y = X Q^-1(W_q)^T (hqq_matmul) for a contiguous M x K float16 CUDA tensor X and a
+    weight quantized as q (rows = N outputs, cols = K inputs).  Returns an M x N float16
+    (or float32) tensor, or fills ``out``."""
+    import torch
+    if X.dtype != torch.float16 or X.dim() != 2 or not X.is_cuda or not X.is_contiguous():
+        raise ValueError("X must be a contiguous 2-D float16 CUDA tensor")
+    M, K = X.shape
+    if K != q.cols:
+        raise ValueError(f"X has {K} columns, the weight {q.cols}")
+    dt = torch.float32 if out_f32 else torch.float16
+    if out is None:
+        out = torch.empty((M, q.rows), dtype=dt, device=X.device)
+    elif out.dtype != dt or tuple(out.shape) != (M, q.rows) or not out.is_contiguous():
+        raise ValueError("out has the wrong dtype or shape")
+    st = hqq_matmul(_addr(X), M, K, _addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows,
+                    q.nbits, q.group_size, _addr(out), int(bool(out_f32)), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_matmul")
+    return out
 
 
 @dataclass

@@ -8,6 +8,7 @@
 
 #include "../../include/hqq.h"
 #include "hqq_internal.h"
+#include "hqq_matmul.h"
 #include "hqq_tensor_stop.h"
 
 namespace {
@@ -300,6 +301,41 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
   const int64_t cap = (int64_t)cus * 16;
   if (blocks > cap) blocks = cap;
   hipError_t err = hqq::launch_dequant(prm, (int)blocks, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes,
+               const void* scale_f16, const void* zero_f16, int64_t N, int nbits,
+               int group_size, void* Y, int out_f32, void* stream) {
+  if (checked_elems(M, K) < 0 || checked_elems(N, K) < 0 || checked_elems(M, N) < 0)
+    return HQQ_ERR_INVALID_ARG;
+  if (!supported_nbits(nbits) || !supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
+  if (K % group_size != 0) return HQQ_ERR_INVALID_ARG;
+  if (K % 32 != 0) return HQQ_ERR_UNSUPPORTED;
+  if (out_f32 != 0 && out_f32 != 1) return HQQ_ERR_INVALID_ARG;
+  if (M > (int64_t)65535 * 128) return HQQ_ERR_INVALID_ARG;  // grid size
+  if (M == 0 || N == 0) return HQQ_OK;
+  if (!Y) return HQQ_ERR_INVALID_ARG;
+  if (K > 0 && (!X_f16 || !packed_codes || !scale_f16 || !zero_f16)) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(Y, out_f32 ? 4 : 2)) return HQQ_ERR_ALIGNMENT;
+  if (K > 0 && (!aligned(X_f16, 16) || !aligned(packed_codes, 16) || !aligned(scale_f16, 2) ||
+                !aligned(zero_f16, 2)))
+    return HQQ_ERR_ALIGNMENT;
+  hqq::MatmulParams prm;
+  prm.X = static_cast<const uint16_t*>(X_f16);
+  prm.packed = static_cast<const uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<const uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<const uint16_t*>(zero_f16);
+  prm.Y = Y;
+  prm.M = M;
+  prm.N = N;
+  prm.K = K;
+  prm.nbits = nbits;
+  prm.group_size = group_size;
+  prm.out_f32 = out_f32;
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_matmul(prm, cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 

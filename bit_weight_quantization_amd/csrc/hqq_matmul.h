@@ -1,0 +1,25 @@
+// hqq_matmul.h -- launch interface of the product with a quantized weight
+// (hqq_matmul.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hqq {
+
+struct MatmulParams {
+  const uint16_t* X;        // M x K binary16 activations, row-major
+  const uint8_t* packed;    // N x K codes, LSB-first bitstream over row-major elements
+  const uint16_t* scale16;  // N x K/g binary16 s
+  const uint16_t* zero16;   // N x K/g binary16 z
+  void* Y;                  // M x N, binary16 or fp32
+  int64_t M, N, K;
+  int nbits, group_size;
+  int out_f32;
+};
+
+// Rows of X up to which the wavefront-per-row kernel is used (above: the MFMA kernel).
+constexpr int kGemvMaxRows = 8;
+
+hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream);
+
+}  // namespace hqq

@@ -1,0 +1,279 @@
+// hqq_matmul.hip -- gfx950 kernels of the product with a quantized weight,
+// Y = X Q^-1(W_q)^T, where Q^-1(W_q) = s (W_q - z) is the inverse quantizer of section 2
+// of "Half-Quadratic Quantization of Large Machine Learning Models" (Dropbox tech blog)
+// applied to the codes and binary16 s and z that hqq_quantize stores.  The weight is
+// N x K (row n holds output n, grouped along the input dimension K); X is M x K
+// binary16; accumulation is fp32.
+//
+// Two kernels:
+//   * few rows of X (decode, M <= 8): one wavefront per weight row; each lane takes
+//     32-code chunks of the row and, per 16 codes (always inside one group), adds
+//     s (sum x q - z sum x): the group's scale and zero are applied once per 16 codes,
+//     the codes enter as exact small integers.  Bound by HBM reads of the codes.
+//   * more rows (prefill): 128 x 128 output tiles per block of four wavefronts (64 x 64
+//     each, 2 x 2 tiles of v_mfma_f32_32x32x16_f16); per 32-wide step of K the block
+//     stages the X tile in LDS and dequantizes the weight tile once into LDS as binary16
+//     (fp32 s*q - s*z, one rounding, then to binary16), then every wavefront runs its
+//     MFMAs from LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hqq_internal.h"
+#include "hqq_matmul.h"
+
+namespace hqq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float h2f(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Code j (0-based, compile-time after unrolling) of an LSB-first string held in words w.
+template <int NB, int NW>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int j) {
+  const int bit = NB * j;
+  const int wi = bit >> 5, sh = bit & 31;
+  constexpr uint32_t mask = (1u << NB) - 1u;
+  if (sh + NB <= 32) return (w[wi] >> sh) & mask;
+  return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+}
+
+// The 32 codes (32*NB bits, NB words) starting at p (4*NB-byte aligned).
+template <int NB>
+__device__ __forceinline__ void load_codes32(const uint8_t* p, uint32_t (&w)[NB]) {
+  if constexpr (NB == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (NB == 3) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    w[0] = q[0]; w[1] = q[1]; w[2] = q[2];
+  } else if constexpr (NB == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+}
+
+// Words holding 16 codes, and their load from p (2*NB-byte aligned).
+template <int NB>
+struct Codes16 {
+  static constexpr int kWords = (16 * NB + 31) / 32;
+  uint32_t w[kWords];
+  __device__ __forceinline__ void load(const uint8_t* p) {
+    if constexpr (NB == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (NB == 3) {  // 6 bytes, 2-byte aligned
+      const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+      w[0] = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+      w[1] = q[2];
+    } else if constexpr (NB == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+  }
+};
+
+// ------------------------------------------------------------------- GEMV --
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// One wavefront per weight row n (grid-stride over the rows); lane l takes the 32-code
+// chunks l, l + 64, ... of the row.  MB >= M rows of X are handled together.
+template <int NB, int MB>
+__global__ __launch_bounds__(kBlock) void hqq_gemv_kernel(const MatmulParams P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlock / kWave);
+  const int64_t chunks = P.K >> 5;
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K / P.group_size;
+  const int M = (int)P.M;
+  for (int64_t n = wave; n < P.N; n += nwaves) {
+    float acc[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = 0.f;
+    const uint8_t* row = P.packed + n * row_bytes;
+    for (int64_t c = lane; c < chunks; c += kWave) {
+      uint32_t w[NB];
+      load_codes32<NB>(row + c * (4 * NB), w);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // 16 codes lie inside one group (g >= 16)
+        const int64_t k0 = c * 32 + 16 * h;
+        const int64_t gi = n * gpr + k0 / P.group_size;
+        const float s = h2f(P.scale16[gi]);
+        const float z = h2f(P.zero16[gi]);
+        float q[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) q[j] = (float)code_at<NB>(w, 16 * h + j);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          if (m < M) {
+            const uint4* xp = reinterpret_cast<const uint4*>(P.X + m * P.K + k0);
+            const uint4 a = xp[0], b = xp[1];
+            const uint32_t xw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float p = 0.f, sx = 0.f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float x = h2f((j & 1) ? (xw[j >> 1] >> 16) : (xw[j >> 1] & 0xffffu));
+              p = __builtin_fmaf(x, q[j], p);
+              sx += x;
+            }
+            acc[m] = __builtin_fmaf(s, __builtin_fmaf(-z, sx, p), acc[m]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = wave_sum(acc[m]);
+    if (lane == 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m < M) {
+          if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = acc[m];
+          else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)acc[m];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------- GEMM --
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kLdsRow = kBK + 8;  // binary16 per LDS row (16-byte pad)
+
+template <int NB>
+__global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) {
+  __shared__ __align__(16) _Float16 As[kBM][kLdsRow];
+  __shared__ __align__(16) _Float16 Bs[kBN][kLdsRow];
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
+  const int wm = wid >> 1, wn = wid & 1;  // the wavefront's 64 x 64 quarter of the tile
+  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K / P.group_size;
+  // loaders: thread t stages row t / 2 of both tiles, elements 16 (t % 2) .. + 16 of the step
+  const int lr = tid >> 1, lh = tid & 1;
+  const int64_t am = m0 + lr, bn = n0 + lr;
+  float16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  for (int64_t k0 = 0; k0 < P.K; k0 += kBK) {
+    const int64_t e0 = k0 + 16 * lh;
+    uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0, b0 = a0, b1 = a0;
+    if (am < P.M) {
+      const uint4* xp = reinterpret_cast<const uint4*>(P.X + am * P.K + e0);
+      a0 = xp[0];
+      a1 = xp[1];
+    }
+    if (bn < P.N) {
+      Codes16<NB> cw;
+      cw.load(P.packed + bn * row_bytes + (e0 >> 3) * NB);
+      const int64_t gi = bn * gpr + e0 / P.group_size;
+      const float s = h2f(P.scale16[gi]);
+      const float sz = s * h2f(P.zero16[gi]);  // exact: two 11-bit significands
+      uint32_t hw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w0 = __builtin_fmaf(s, (float)code_at<NB>(cw.w, 2 * j), -sz);
+        const float w1 = __builtin_fmaf(s, (float)code_at<NB>(cw.w, 2 * j + 1), -sz);
+        hw[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w1) << 16);
+      }
+      b0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      b1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    }
+    uint4* ad = reinterpret_cast<uint4*>(&As[lr][16 * lh]);
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[lr][16 * lh]);
+    ad[0] = a0;
+    ad[1] = a1;
+    bd[0] = b0;
+    bd[1] = b1;
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      half8_t af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 64 + i * 32 + (lane & 31)][kk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // C tile (i, j): lane l, element v holds row 8 (v / 4) + 4 (l / 32) + v % 4, col l % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m < P.M && n < P.N) {
+          if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = acc[i][j][v];
+          else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
+template <int NB>
+hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
+  if (P.M <= kGemvMaxRows) {
+    int64_t blocks = (P.N + kBlock / kWave - 1) / (kBlock / kWave);  // a wavefront per row
+    const int64_t cap = (int64_t)cus * 32;
+    if (blocks > cap) blocks = cap;
+    const dim3 grid((unsigned)blocks), block(kBlock);
+    if (P.M <= 1) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 1>), grid, block, 0, st, P);
+    else if (P.M <= 2) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 2>), grid, block, 0, st, P);
+    else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 4>), grid, block, 0, st, P);
+    else hipLaunchKernelGGL((hqq_gemv_kernel<NB, 8>), grid, block, 0, st, P);
+  } else {
+    const dim3 grid((unsigned)((P.N + kBN - 1) / kBN), (unsigned)((P.M + kBM - 1) / kBM));
+    hipLaunchKernelGGL(hqq_gemm_kernel<NB>, grid, dim3(kBlock), 0, st, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream) {
+  switch (prm.nbits) {
+    case 2: return launch_nb<2>(prm, cus, stream);
+    case 3: return launch_nb<3>(prm, cus, stream);
+    case 4: return launch_nb<4>(prm, cus, stream);
+    case 8: return launch_nb<8>(prm, cus, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace hqq

@@ -281,6 +281,34 @@ int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
                             const void* values_f16, int64_t meta_group, void* codes_u8,
                             void* mscale_f16, void* moffset_f16, void* workspace, void* stream);
 
+/*
+ * hqq_matmul -- Y = X Q^-1(W_q)^T: the product of activations X with a weight stored
+ * by hqq_quantize, through the inverse quantizer Q^-1(W_q) = s (W_q - z) of section 2
+ * of the page above (the consumer of the stored format; the page reports the runtime
+ * memory of models stored this way, section 4.1).  The weight is N x K: row n holds
+ * the K inputs of output n, grouped along K, exactly as hqq_quantize(rows = N,
+ * cols = K) writes packed_codes, scale_f16 and zero_f16.
+ *   Y[m][n] = sum over k of X[m][k] * s[n][k/g] * (q[n][k] - z[n][k/g])
+ * with the stored binary16 s and z.  Arithmetic: fp32 accumulation in an order that
+ * depends on the path (not bit-reproducible against another order).  M <= 8: per
+ * 16 codes, s * (sum x q - z sum x) in fp32 (the codes enter exactly).  M > 8: the
+ * weight is dequantized to binary16 (s*q - s*z in fp32, one rounding, then to
+ * binary16) and multiplied on the matrix cores with fp32 accumulation.
+ *
+ * X_f16        M x K binary16, row-major, 16-byte aligned.
+ * M, N, K      >= 0; K a multiple of group_size and of 32 (else HQQ_ERR_UNSUPPORTED);
+ *              M <= 8388480.  M == 0 or N == 0 is a no-op; K == 0 writes zeros.
+ * packed_codes, scale_f16, zero_f16  the N x K weight as hqq_quantize stores it;
+ *              packed_codes 16-byte aligned.
+ * nbits, group_size  as quantized (2, 3, 4, 8 and 16, 32, 64, 128).
+ * Y            M x N row-major: binary16 (out_f32 = 0, RNE of the fp32 sum; 2-byte
+ *              aligned) or fp32 (out_f32 = 1; 4-byte aligned).
+ * Conventions and errors as for hqq_quantize.
+ */
+int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes,
+               const void* scale_f16, const void* zero_f16, int64_t N, int nbits,
+               int group_size, void* Y, int out_f32, void* stream);
+
 /* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
  * shapes).  Returns -1 for invalid arguments or overflow. */
 int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);

@@ -125,6 +125,40 @@ def test_quantize_ex_option_validation(lib):
                               0) == hq.HQQ_ERR_ALIGNMENT
 
 
+def _mm(**kw):
+    a = dict(X_f16=FAKE, M=4, K=256, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, N=16,
+             nbits=4, group_size=64, Y=FAKE, out_f32=0, stream=0)
+    a.update(kw)
+    return hq.hqq_matmul(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nbits=5), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(group_size=48), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(K=240), hq.HQQ_ERR_INVALID_ARG),          # not a multiple of the group size
+    (dict(K=48, group_size=16), hq.HQQ_ERR_UNSUPPORTED),  # not a multiple of 32
+    (dict(M=-1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(N=-1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(out_f32=2), hq.HQQ_ERR_INVALID_ARG),
+    (dict(M=65535 * 128 + 1), hq.HQQ_ERR_INVALID_ARG),
+    (dict(Y=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(X_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(packed_codes=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(X_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+    (dict(packed_codes=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+    (dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+    (dict(Y=FAKE + 2, out_f32=1), hq.HQQ_ERR_ALIGNMENT),
+    (dict(Y=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_matmul_rejects_before_launch(lib, kw, status):
+    assert _mm(**kw) == status
+
+
+def test_matmul_empty_is_a_no_op(lib):
+    assert _mm(M=0, X_f16=0, packed_codes=0, scale_f16=0, zero_f16=0, Y=0) == hq.HQQ_OK
+    assert _mm(N=0, X_f16=0, packed_codes=0, scale_f16=0, zero_f16=0, Y=0) == hq.HQQ_OK
+
+
 def _ts(opt=None, **kw):
     a = dict(W_f16=FAKE, rows=16, cols=128, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01,
              iters=20, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, options=opt,

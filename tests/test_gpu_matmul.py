@@ -1,0 +1,182 @@
+"""GPU parity of hqq_matmul (Y = X Q^-1(W_q)^T, through the C ABI) against the oracle.
+
+Weights are stored-format inputs built on the host (random codes packed by the
+oracle's packer, binary16 s and z), so nothing on the oracle side comes from the
+device.  Two kinds of checks:
+  * exact cases: s a power of two, z an integer, X small integers: every product and
+    partial sum is exact in fp32 whatever the order, so fp32 outputs equal the oracle
+    bit for bit and binary16 outputs equal the oracle's value rounded once.  This pins
+    the indexing of both kernels (rows of X up to 8: the per-row kernel; above: the
+    matrix-core kernel) over ragged tiles, all bit widths and group sizes;
+  * general inputs: |y_dev - y_oracle| within a bound derived from the arithmetic of the
+    path (``_bound``), on full small products and on sampled outputs of the Llama-2-70B
+    layer shapes at full size.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+U32 = 2.0 ** -24
+U16 = 2.0 ** -11
+
+
+@pytest.fixture(scope="module")
+def hq():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    import bit_weight_quantization_amd as m
+    m.load_library()
+    return m
+
+
+def _say(msg):
+    print(f"[gpu-matmul] {msg}", flush=True)
+
+
+def _weight(N, K, nbits, g, seed, exact=False):
+    rng = np.random.default_rng(seed)
+    qmax = (1 << nbits) - 1
+    codes = rng.integers(0, qmax + 1, (N, K), dtype=np.uint8)
+    G = K // g
+    if exact:
+        s = (2.0 ** -rng.integers(3, 7, (N, G))).astype(np.float16)
+        z = rng.integers(0, qmax + 1, (N, G)).astype(np.float16)
+    else:
+        s = np.asarray(rng.uniform(2e-4, 4e-3, (N, G)), np.float16)
+        z = np.asarray(rng.uniform(-0.5, qmax + 0.5, (N, G)), np.float16)
+    packed = oracle.pack_codes(codes.ravel(), nbits)
+    return codes, packed, s, z
+
+
+def _run(hq, X, packed, s, z, N, nbits, g, out_f32):
+    M, K = X.shape
+    Xd = torch.from_numpy(X.view(np.int16).copy()).view(torch.float16).cuda()
+    pd = torch.from_numpy(packed.copy()).cuda()
+    sd = torch.from_numpy(s.view(np.int16).copy()).cuda()
+    zd = torch.from_numpy(z.view(np.int16).copy()).cuda()
+    Y = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
+    st = hq.hqq_matmul(Xd.data_ptr(), M, K, pd.data_ptr(), sd.data_ptr(), zd.data_ptr(), N, nbits,
+                       g, Y.data_ptr(), int(out_f32), 0)
+    assert st == hq.HQQ_OK, hq.hqq_status_string(st)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy().astype(np.float64)
+
+
+def _bound(X, codes, s, z, g, gemv, out_f32, y):
+    """Worst-case |y_dev - y_exact| of the device path, elementwise (M x N).
+    per-row path: per 16 codes fp32 sums of x q and x, then s (p - z sx) accumulated over
+      K/16 blocks and a 64-lane tree: <= (K/16 + 30) u32 sum_k |x| |s| (|q| + |z|);
+    matrix-core path: the weight rounded to fp32 then binary16 (<= (u16 + 2 u32) |w| +
+      2^-25 absolute, binary16 subnormals), exact products, fp32 sums over K:
+      <= sum_k |x| ((u16 + 2 u32) |w| + 2^-25) + (K + 8) u32 sum_k |x| |w| (1 + 2 u16);
+    plus u16 |y| for a binary16 output."""
+    K = X.shape[1]
+    x = np.abs(X.astype(np.float64))
+    sk = np.repeat(s.astype(np.float64), g, axis=1)
+    zk = np.repeat(z.astype(np.float64), g, axis=1)
+    w = sk * (codes.astype(np.float64) - zk)
+    if gemv:
+        b = (K / 16 + 30) * U32 * (x @ (np.abs(sk) * (codes + np.abs(zk))).T)
+    else:
+        aw = np.abs(w)
+        b = x @ ((U16 + 2 * U32) * aw + 2.0 ** -25).T + (K + 8) * U32 * (1 + 2 * U16) * (x @ aw.T)
+    if not out_f32:
+        b = b + U16 * np.abs(y) + 2.0 ** -25
+    return b
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32), (2, 16), (3, 32), (8, 128), (4, 16)])
+def test_exact_products_all_paths(hq, nbits, g):
+    rng = np.random.default_rng(nbits * 100 + g)
+    shapes = [(1, 7, 128), (2, 3, 256), (3, 128, 64 if g <= 64 else 128), (5, 300, 256),
+              (8, 129, 384), (9, 128, 128), (16, 257, 256), (130, 300, 512), (257, 64, 1024)]
+    for M, N, K in shapes:
+        if K % g:
+            continue
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=M * 7 + N, exact=True)
+        X = rng.integers(-2, 3, (M, K)).astype(np.float16)
+        ref = oracle.hqq_matmul(X, packed, s, z, N, nbits, g)
+        for out_f32 in (1, 0):
+            Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32)
+            want = ref if out_f32 else oracle.f16_to_f64(oracle.f64_to_f16(ref))
+            bad = np.argwhere(Y != want)
+            assert bad.size == 0, (M, N, K, out_f32, bad[:5], Y[tuple(bad[0])], want[tuple(bad[0])])
+    _say(f"b{nbits} g{g}: exact on {len(shapes)} shapes, fp32 and binary16 outputs")
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32), (3, 64), (8, 32)])
+def test_general_inputs_within_the_bound(hq, nbits, g):
+    rng = np.random.default_rng(nbits + 7 * g)
+    for M in (1, 4, 8, 24, 200):
+        N, K = 160, 1024
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=M + 1000)
+        X = np.asarray(rng.standard_normal((M, K)), np.float16)
+        ref = oracle.hqq_matmul(X, packed, s, z, N, nbits, g)
+        for out_f32 in (1, 0):
+            Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32)
+            b = _bound(X, codes, s, z, g, M <= 8, out_f32, ref)
+            err = np.abs(Y - ref)
+            assert np.all(err <= b), (M, out_f32, float((err / b).max()))
+            _say(f"b{nbits} g{g} M={M} out_f32={out_f32}: max err/bound {float((err / b).max()):.3g}, "
+                 f"max rel err {float((err / np.maximum(np.abs(ref), 1e-6)).max()):.3g}")
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32)])
+def test_llama70b_layer_shapes_sampled(hq, nbits, g):
+    """The 7 weight shapes of a Llama-2-70B layer at full size (N x K = 8192 x 8192,
+    1024 x 8192, 28672 x 8192, 8192 x 28672), decode (M = 1) and prefill (M = 512)
+    activations; outputs checked on sampled weight rows and activation rows."""
+    rng = np.random.default_rng(70 + nbits)
+    for N, K in [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)]:
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=N + K + nbits)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 46, replace=False)]))
+        bpr = K * nbits // 8
+        sub_packed = packed.reshape(N, bpr)[rows].ravel()
+        for M in (1, 512):
+            X = np.asarray(rng.standard_normal((M, K)) * 0.5, np.float16)
+            Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
+            ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 6), replace=False)]))
+            ref = oracle.hqq_matmul(X[ms], sub_packed, s[rows], z[rows], len(rows), nbits, g)
+            b = _bound(X[ms], codes[rows], s[rows], z[rows], g, M <= 8, 1, ref)
+            err = np.abs(Y[np.ix_(ms, rows)] - ref)
+            assert np.all(err <= b)
+            _say(f"{N}x{K} b{nbits} g{g} M={M}: max err/bound {float((err / b).max()):.3g}")
+
+
+def test_quantize_then_matmul_matches_dequantize(hq):
+    """The device quantizer's output fed to the product equals (within the bound of the
+    matrix-core path) the product with the device's binary16 dequantization."""
+    import workloads
+    W = workloads.generate_matrix(workloads.WORKLOADS["attn_4096x4096"], 0, "cuda")
+    q = hq.quantize(W, 4, 64)
+    Wd = hq.dequantize(q).float()
+    X = torch.randn((64, 4096), device="cuda").half()
+    Y = hq.matmul(X, q, out_f32=True)
+    ref = X.float() @ Wd.T
+    torch.cuda.synchronize()
+    err = (Y - ref).abs()
+    scale = X.float().abs() @ Wd.abs().T
+    assert float((err / (scale * 2.0 ** -9 + 1e-6)).max()) <= 1.0
+    Y1 = hq.matmul(X[:1].contiguous(), q, out_f32=True)
+    torch.cuda.synchronize()
+    assert float(((Y1 - Y[:1]).abs() / (scale[:1] * 2.0 ** -9 + 1e-6)).max()) <= 1.0
+
+
+def test_empty_and_zero_k(hq):
+    X = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    assert hq.hqq_matmul(X.data_ptr(), 0, 64, 0, 0, 0, 5, 4, 64, 0, 0, 0) == hq.HQQ_OK
+    Y = torch.full((3, 5), 7.0, dtype=torch.float32, device="cuda")
+    dummy = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    st = hq.hqq_matmul(dummy.data_ptr(), 3, 0, dummy.data_ptr(), dummy.data_ptr(),
+                       dummy.data_ptr(), 5, 4, 64, Y.data_ptr(), 1, 0)
+    torch.cuda.synchronize()
+    assert st == hq.HQQ_OK and torch.equal(Y, torch.zeros_like(Y))
+    Y2 = torch.full((12, 5), 7.0, dtype=torch.float32, device="cuda")  # matrix-core path
+    st = hq.hqq_matmul(dummy.data_ptr(), 12, 0, dummy.data_ptr(), dummy.data_ptr(),
+                       dummy.data_ptr(), 5, 4, 64, Y2.data_ptr(), 1, 0)
+    torch.cuda.synchronize()
+    assert st == hq.HQQ_OK and torch.equal(Y2, torch.zeros_like(Y2))
