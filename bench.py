@@ -364,6 +364,75 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
     return out
 
 
+PEAK_MFMA_F16 = 2.5e15  # dense fp16 matrix-core peak of the MI355X
+
+
+def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
+                   rows=(1, 4, 16, 512, 4096)):
+    """The product with the quantized weight (hqq_matmul) over the given matrices, each
+    quantized with every setting: Y = X Q^-1(W_q)^T with random binary16 X of M rows and
+    binary16 Y, one call per matrix, HIP events on the launch stream.  Algorithmic HBM
+    bytes per call: codes N K b/8 + s and z 4 N K/g + X 2 M K + Y 2 M N; algorithmic
+    flops 2 M N K.  Decode rows (M <= 8) are reported against the HBM peak, the others
+    against the dense fp16 matrix-core peak (and their HBM rate).  The 7 launches of a
+    pass are captured in a HIP graph and replayed between the events (no host launch
+    gaps; the graph holds no memset node)."""
+    out = {"entry_point": "hqq_matmul", "matrices": [list(W.shape) for W in Ws],
+           "per_setting": []}
+    for nb, g in settings:
+        qs = [hq.quantize(W, nb, g, p=solver.p, beta=solver.beta, kappa=solver.kappa,
+                          iters=solver.iters) for W in Ws]
+        torch.cuda.synchronize()
+        rows_out = []
+        for M in rows:
+            Xs = [(torch.randn((M, W.shape[1]), device=dev) * 0.5).half() for W in Ws]
+            Ys = [torch.empty((M, W.shape[0]), dtype=torch.float16, device=dev) for W in Ws]
+            calls = [(X.data_ptr(), M, W.shape[1], q.packed.data_ptr(), q.scale.data_ptr(),
+                      q.zero.data_ptr(), W.shape[0], nb, g, Y.data_ptr(), 0, sh)
+                     for W, q, X, Y in zip(Ws, qs, Xs, Ys)]
+
+            def run(handle):
+                for a in calls:
+                    assert lib.hqq_matmul(*a[:-1], handle) == 0
+
+            run(sh)
+            torch.cuda.synchronize()
+            # the 7 launches captured once as a graph and replayed: the timing sees the
+            # kernels (and the gaps between graph nodes), not the host's launch calls
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    run(int(cap.cuda_stream))
+            torch.cuda.synchronize()
+            reps = 50 if M <= 16 else (5 if M <= 512 else 2)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            del graph
+            nbytes = sum(W.numel() * nb / 8 + W.numel() // g * 4 + 2 * M * W.shape[1] +
+                         2 * M * W.shape[0] for W in Ws)
+            flops = sum(2.0 * M * W.numel() for W in Ws)
+            row = {"M": M, "path": "gemv" if M <= 8 else "mfma", "ms": round(ms, 4),
+                   "hbm_GBs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                   "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4),
+                   "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                   "mfma_frac": round(flops / (ms * 1e-3) / PEAK_MFMA_F16, 4)}
+            log(f"matmul b{nb}g{g} {row}")
+            rows_out.append(row)
+            del Xs, Ys
+        out["per_setting"].append({"setting": f"b{nb}g{g}", "rows": rows_out})
+        del qs
+    return out
+
+
 KERNEL_SUMMARIES = {
     # name: (kernel-name filter, file, title, description)
     "meta": ("meta_", "hqq_meta_llama70b.md",
@@ -372,6 +441,12 @@ KERNEL_SUMMARIES = {
              "of the whole stack after the solver, hqq_meta_quantize_batch, both settings, 1 "
              "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the "
              "largest matrix alone (bench.py measure_meta)."),
+    "matmul": ("_gem", "hqq_matmul_llama70b_layer0.md",
+               "Product with the quantized weight on the 7 matrices of Llama-2-70B layer 0",
+               "hqq_matmul, one call per matrix, M = 1, 4, 16, 512, 4096 rows of X, b2 g32 and "
+               "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
+               "(bench.py measure_matmul); hqq_gemv_kernel<b, M rows> for M <= 8, "
+               "hqq_gemm_kernel<b> above."),
     "variants": ("hqq", "hqq_solver_variants_llama70b_layer0.md",
                  "Solver variants on the 7 matrices of Llama-2-70B layer 0",
                  "One call per matrix and variant (per-group stop on the lp / l1 / l2 error: "
@@ -417,6 +492,10 @@ def main():
                     help="one hqq_quantize launch per matrix instead of one batched launch "
                          "per setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-matmul", action="store_true",
+                    help="skip the quantized-weight product measurement on the first layer")
+    ap.add_argument("--matmul-only", action="store_true",
+                    help="only measure the quantized-weight product (JSON on stderr)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the solver-variant measurement on the first layer")
     ap.add_argument("--variants-only", action="store_true",
@@ -547,6 +626,11 @@ def main():
         if events is not None:
             events[cur][1].record(stream)
 
+    if args.matmul_only:
+        log(json.dumps(measure_matmul(hq, lib, torch, Ws[:7], settings, solver, stream, sh,
+                                      dev)))
+        return
+
     if args.variants_only:
         log(json.dumps(measure_variants(hq, lib, torch, Ws[:7], settings, solver, stream, sh,
                                         dev)))
@@ -650,6 +734,11 @@ def main():
     if not args.no_variants:
         variants = measure_variants(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
 
+    # ---- next row: the product with the quantized weight, first layer ----------------
+    matmul = None
+    if not args.no_matmul:
+        matmul = measure_matmul(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
+
     # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -722,7 +811,8 @@ def main():
         },
         "per_setting": detail,
         "cpu_baseline": cpu,
-        "next_rows": {"meta_quantization": meta, "solver_variants": variants},
+        "next_rows": {"meta_quantization": meta, "solver_variants": variants,
+                      "quantized_matmul": matmul},
     }
     print(json.dumps(out), flush=True)
 

@@ -332,6 +332,7 @@ int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes
   prm.K = K;
   prm.nbits = nbits;
   prm.group_size = group_size;
+  prm.group_shift = group_size == 16 ? 4 : group_size == 32 ? 5 : group_size == 64 ? 6 : 7;
   prm.out_f32 = out_f32;
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;

@@ -14,6 +14,7 @@ struct MatmulParams {
   void* Y;                  // M x N, binary16 or fp32
   int64_t M, N, K;
   int nbits, group_size;
+  int group_shift;          // log2(group_size)
   int out_f32;
 };
 

@@ -5,11 +5,13 @@
 // N x K (row n holds output n, grouped along the input dimension K); X is M x K
 // binary16; accumulation is fp32.
 //
-// Two kernels:
-//   * few rows of X (decode, M <= 8): one wavefront per weight row; each lane takes
-//     32-code chunks of the row and, per 16 codes (always inside one group), adds
-//     s (sum x q - z sum x): the group's scale and zero are applied once per 16 codes,
-//     the codes enter as exact small integers.  Bound by HBM reads of the codes.
+// Two kinds of kernel:
+//   * few rows of X (decode, M <= 8): per 16 codes (always inside one group) a lane adds
+//     s (sum x q - z sum x): the group's scale and zero are applied once per 16 codes and
+//     the codes enter as exact small integers.  For 2-, 4- and 8-bit codes the sum x q is
+//     taken on packed binary16 pairs with v_dot2_f32_f16 (one to four weight rows per
+//     wavefront); 3-bit codes (which straddle bytes) use a wavefront per row and fp32
+//     arithmetic.  Bound by HBM reads of the codes.
 //   * more rows (prefill): 128 x 128 output tiles per block of four wavefronts (64 x 64
 //     each, 2 x 2 tiles of v_mfma_f32_32x32x16_f16); per 32-wide step of K the block
 //     stages the X tile in LDS and dequantizes the weight tile once into LDS as binary16
@@ -151,6 +153,215 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_kernel(const MatmulParams P) 
   }
 }
 
+// Packed-binary16 form of the codes for the dot products: every 32-bit word is a
+// pair of consecutive codes as exact binary16 integers.  A byte of codes is placed
+// beside the binary16 exponent byte 0x64 (1024 + mantissa) with one byte permute, the
+// other code fields of the byte are masked off, and one packed FMA scales and shifts
+// each half to the code itself (1024 + 16 c -> c: exact in binary16).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+template <int NB>
+struct CodePairs {  // the 16 codes of one 16-code block as 8 pairs
+  static constexpr int kWords = 16 * NB / 32;
+  half2_t q[8];
+  __device__ __forceinline__ void from(const uint32_t (&w)[kWords]) {
+    constexpr uint32_t kMagic = 0x64646464u;
+    if constexpr (NB == 8) {  // one code per byte: bytes 2i, 2i+1
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = 0x04000400u | (uint32_t)((2 * i) & 3) | ((uint32_t)((2 * i + 1) & 3) << 16);
+        const uint32_t t = __builtin_amdgcn_perm(kMagic, w[i / 2], sel);
+        q[i] = as_h2(t) - (half2_t){(_Float16)1024.f, (_Float16)1024.f};
+      }
+    } else if constexpr (NB == 4) {  // two codes per byte
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = (uint32_t)(i & 3);
+        const uint32_t t = __builtin_amdgcn_perm(kMagic, w[i / 4], 0x04000400u | b | (b << 16)) &
+                           0xFFF0FF0Fu;
+        q[i] = __builtin_elementwise_fma(as_h2(t), (half2_t){(_Float16)1.f, (_Float16)0.0625f},
+                                         (half2_t){(_Float16)-1024.f, (_Float16)-64.f});
+      }
+    } else {  // NB == 2: four codes per byte
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t b = (uint32_t)i;
+        const uint32_t t = __builtin_amdgcn_perm(kMagic, w[0], 0x04000400u | b | (b << 16));
+        q[2 * i] = __builtin_elementwise_fma(as_h2(t & 0xFF0CFF03u),
+                                             (half2_t){(_Float16)1.f, (_Float16)0.25f},
+                                             (half2_t){(_Float16)-1024.f, (_Float16)-256.f});
+        q[2 * i + 1] = __builtin_elementwise_fma(as_h2(t & 0xFFC0FF30u),
+                                                 (half2_t){(_Float16)0.0625f, (_Float16)0.015625f},
+                                                 (half2_t){(_Float16)-64.f, (_Float16)-16.f});
+      }
+    }
+  }
+};
+
+// One wavefront per group of R weight rows.  Lane l takes the 32-code chunks l, l + 64,
+// ... of the rows: per chunk it reads 4 NB bytes of codes in each of the R rows and the
+// chunk of X once for all R rows; the next chunk's codes are loaded before the current
+// one is computed, so two chunks' loads are in flight per lane.  Per 16 codes (one
+// group): p = sum of x*q (packed dot products, exact products, fp32 sums) and
+// s (p - z sum x).  The lanes' partial sums are added by a butterfly in fixed order.
+template <int NB>
+__device__ __forceinline__ void load_chunk_codes(const uint8_t* cp, uint32_t (&w)[NB]) {
+  if constexpr (NB == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(cp);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (NB == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(cp);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else {
+    const uint4 v0 = reinterpret_cast<const uint4*>(cp)[0];
+    const uint4 v1 = reinterpret_cast<const uint4*>(cp)[1];
+    w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+    w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+  }
+}
+
+// Everything one chunk step of the GEMV reads: the codes of the chunk in each of the R
+// rows, the chunk of each row of X, and the binary16 s and z of the chunk's two halves.
+template <int NB, int MB, int R>
+struct GemvStage {
+  uint32_t w[R][NB];
+  uint4 x[MB][4];
+  uint32_t s[R][2], z[R][2];
+};
+
+template <int NB, int MB, int R>
+__global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulParams P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  const int64_t n0 = wave * R;
+  if (n0 >= P.N) return;  // wave-uniform; the kernel has no block-wide barrier
+  const int64_t nchunk = P.K >> 5;  // 32-code chunks per row
+  if (nchunk == 0) {
+    // K = 0: the product is zero
+    if (lane == 0) {
+      const int nr0 = P.N - n0 < R ? (int)(P.N - n0) : R;
+      for (int r = 0; r < nr0; ++r)
+        for (int m = 0; m < (int)P.M; ++m) {
+          if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n0 + r] = 0.f;
+          else static_cast<_Float16*>(P.Y)[m * P.N + n0 + r] = (_Float16)0.f;
+        }
+    }
+    return;
+  }
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K >> P.group_shift;
+  const int g2 = P.group_size == 16 ? 1 : 0;  // second half of a chunk: next group at g = 16
+  const int M = (int)P.M;
+  const int nr = P.N - n0 < R ? (int)(P.N - n0) : R;
+  const half2_t kOnes = {(_Float16)1.f, (_Float16)1.f};
+  // rows past the end of the weight (or of X) re-read the last valid one; results unused
+  const uint8_t* rowp[R];
+  const uint16_t* sp[R];
+  const uint16_t* zp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t n = n0 + (r < nr ? r : nr - 1);
+    rowp[r] = P.packed + n * row_bytes;
+    sp[r] = P.scale16 + n * gpr;
+    zp[r] = P.zero16 + n * gpr;
+  }
+  const uint16_t* xrow[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) xrow[m] = P.X + (int64_t)(m < M ? m : M - 1) * P.K;
+
+  // chunk c's loads (c < nchunk)
+  auto load = [&](GemvStage<NB, MB, R>& st, int64_t c) {
+    const int64_t k0 = c << 5;
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_chunk_codes<NB>(rowp[r] + c * (4 * NB), st.w[r]);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xrow[m] + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.x[m][i] = xp[i];
+    }
+    const int64_t g0 = k0 >> P.group_shift;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      st.s[r][0] = sp[r][g0];
+      st.z[r][0] = zp[r][g0];
+      st.s[r][1] = sp[r][g0 + g2];
+      st.z[r][1] = zp[r][g0 + g2];
+    }
+  };
+
+  float acc[R][MB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[r][m] = 0.f;
+
+  // per step, every load of the chunk is issued before any arithmetic (the scheduling
+  // barrier keeps the compiler from sinking loads next to their first use), so a step
+  // costs one memory round trip, hidden by the other wavefronts of the SIMD
+  for (int64_t c = lane; c < nchunk; c += kWave) {
+    GemvStage<NB, MB, R> cur;
+    load(cur, c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // 16-code halves
+      uint32_t xw[MB][8];
+      float sx[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const uint4 a = cur.x[m][2 * h], b = cur.x[m][2 * h + 1];
+        xw[m][0] = a.x; xw[m][1] = a.y; xw[m][2] = a.z; xw[m][3] = a.w;
+        xw[m][4] = b.x; xw[m][5] = b.y; xw[m][6] = b.z; xw[m][7] = b.w;
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t = __builtin_amdgcn_fdot2(as_h2(xw[m][j]), kOnes, t, false);
+        sx[m] = t;
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t hw[CodePairs<NB>::kWords];
+#pragma unroll
+        for (int i = 0; i < CodePairs<NB>::kWords; ++i) hw[i] = cur.w[r][h * CodePairs<NB>::kWords + i];
+        CodePairs<NB> cq;
+        cq.from(hw);
+        const float sv = h2f(cur.s[r][h]);
+        const float zv = h2f(cur.z[r][h]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          float p = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p = __builtin_amdgcn_fdot2(as_h2(xw[m][j]), cq.q[j], p, false);
+          acc[r][m] = __builtin_fmaf(sv, __builtin_fmaf(-zv, sx[m], p), acc[r][m]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const float v = wave_sum(acc[r][m]);
+      if (lane == 0 && r < nr && m < M) {
+        const int64_t n = n0 + r;
+        if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = v;
+        else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)v;
+      }
+    }
+  }
+}
+
+template <int NB, int R>
+hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
+  constexpr int kRowsPerBlock = R * (kBlock / kWave);
+  const dim3 grid((unsigned)((P.N + kRowsPerBlock - 1) / kRowsPerBlock)), block(kBlock);
+  if (P.M <= 1) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 1, R>), grid, block, 0, st, P);
+  else if (P.M <= 2) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 2, R>), grid, block, 0, st, P);
+  else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 4, R>), grid, block, 0, st, P);
+  else hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 8, R>), grid, block, 0, st, P);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------- GEMM --
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
@@ -248,6 +459,15 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 
 template <int NB>
 hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
+  if constexpr (NB != 3) {  // packed binary16 codes (3-bit codes straddle bytes)
+    if (P.M <= kGemvMaxRows) {
+      // rows per wavefront: enough wavefronts to fill the chip (>= 2048) with as many
+      // rows sharing each chunk of X as that allows
+      if (P.N >= 8192) return launch_gemv_packed<NB, 4>(P, st);
+      if (P.N >= 4096) return launch_gemv_packed<NB, 2>(P, st);
+      return launch_gemv_packed<NB, 1>(P, st);
+    }
+  }
   if (P.M <= kGemvMaxRows) {
     int64_t blocks = (P.N + kBlock / kWave - 1) / (kBlock / kWave);  // a wavefront per row
     const int64_t cap = (int64_t)cus * 32;
