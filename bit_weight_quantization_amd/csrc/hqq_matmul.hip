@@ -13,10 +13,10 @@
 //     wavefront); 3-bit codes (which straddle bytes) use a wavefront per row and fp32
 //     arithmetic.  Bound by HBM reads of the codes.
 //   * more rows (prefill): 128 x 128 output tiles per block of four wavefronts (64 x 64
-//     each, 2 x 2 tiles of v_mfma_f32_32x32x16_f16); per 32-wide step of K the block
+//     each, 2 x 2 tiles of v_mfma_f32_32x32x16_f16); per 64-wide step of K the block
 //     stages the X tile in LDS and dequantizes the weight tile once into LDS as binary16
-//     (fp32 s*q - s*z, one rounding, then to binary16), then every wavefront runs its
-//     MFMAs from LDS.
+//     (fp32 s*q - s*z, one rounding, then to binary16), double-buffered, then every
+//     wavefront runs its MFMAs from LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,28 +62,6 @@ __device__ __forceinline__ void load_codes32(const uint8_t* p, uint32_t (&w)[NB]
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
   }
 }
-
-// Words holding 16 codes, and their load from p (2*NB-byte aligned).
-template <int NB>
-struct Codes16 {
-  static constexpr int kWords = (16 * NB + 31) / 32;
-  uint32_t w[kWords];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    if constexpr (NB == 2) {
-      w[0] = *reinterpret_cast<const uint32_t*>(p);
-    } else if constexpr (NB == 3) {  // 6 bytes, 2-byte aligned
-      const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
-      w[0] = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
-      w[1] = q[2];
-    } else if constexpr (NB == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p);
-      w[0] = v.x; w[1] = v.y;
-    } else {
-      const uint4 v = *reinterpret_cast<const uint4*>(p);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    }
-  }
-};
 
 // ------------------------------------------------------------------- GEMV --
 
@@ -207,6 +185,7 @@ struct CodePairs {  // the 16 codes of one 16-code block as 8 pairs
 // s (p - z sum x).  The lanes' partial sums are added by a butterfly in fixed order.
 template <int NB>
 __device__ __forceinline__ void load_chunk_codes(const uint8_t* cp, uint32_t (&w)[NB]) {
+  static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned codes only");
   if constexpr (NB == 2) {
     const uint2 v = *reinterpret_cast<const uint2*>(cp);
     w[0] = v.x; w[1] = v.y;
@@ -364,22 +343,95 @@ hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
 
 // ------------------------------------------------------------------- GEMM --
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLdsRow = kBK + 8;  // binary16 per LDS row (16-byte pad)
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsRow = kBK + 8;  // binary16 per LDS row: 144 bytes (16-byte aligned, rows 4 banks apart)
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Dequantize 32 codes of one weight row to binary16: w = s*q - s*z in fp32 (s*z exact,
+// one rounding) rounded to binary16 (v_cvt_pk_f16_f32, nearest even).  s0, sz0 for
+// codes 0..15 and s1, sz1 for 16..31 (different groups only when g = 16).
+template <int NB>
+__device__ __forceinline__ void dequant32(const uint32_t (&w)[NB], float s0, float sz0, float s1,
+                                          float sz1, uint4 (&out)[4]) {
+  uint32_t h[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float s = j < 8 ? s0 : s1;
+    const float sz = j < 8 ? sz0 : sz1;
+    const float w0 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j), -sz);
+    const float w1 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j + 1), -sz);
+    h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+}
+
+// 128 x 128 output tile per block of four wavefronts (64 x 64 each: 2 x 2 tiles of
+// v_mfma_f32_32x32x16_f16).  K advances in steps of 64: thread t stages row t / 2 of both
+// tiles, elements 32 (t % 2) .. + 32 of the step (the X values as they are, the weight
+// dequantized to binary16).  LDS is double-buffered: the next step's global loads are
+// issued before this step's MFMAs and written to the other buffer after them, with one
+// barrier per step.
 template <int NB>
 __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) {
-  __shared__ __align__(16) _Float16 As[kBM][kLdsRow];
-  __shared__ __align__(16) _Float16 Bs[kBN][kLdsRow];
+  __shared__ __align__(16) _Float16 As[2][kBM][kLdsRow];
+  __shared__ __align__(16) _Float16 Bs[2][kBN][kLdsRow];
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
   const int wm = wid >> 1, wn = wid & 1;  // the wavefront's 64 x 64 quarter of the tile
   const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
   const int64_t row_bytes = (P.K >> 3) * NB;
-  const int64_t gpr = P.K / P.group_size;
-  // loaders: thread t stages row t / 2 of both tiles, elements 16 (t % 2) .. + 16 of the step
+  const int64_t gpr = P.K >> P.group_shift;
+  const int g2 = P.group_size == 16 ? 1 : 0;
   const int lr = tid >> 1, lh = tid & 1;
   const int64_t am = m0 + lr, bn = n0 + lr;
+  const bool a_ok = am < P.M, b_ok = bn < P.N;
+  const uint16_t* xrow = P.X + (a_ok ? am : 0) * P.K;
+  const uint8_t* crow = P.packed + (b_ok ? bn : 0) * row_bytes;
+  const uint16_t* srow = P.scale16 + (b_ok ? bn : 0) * gpr;
+  const uint16_t* zrow = P.zero16 + (b_ok ? bn : 0) * gpr;
+
+  // the loader's registers for one step
+  uint4 ar[4];
+  uint32_t cw[NB];
+  uint32_t s16[2], z16[2];
+  auto load_global = [&](int64_t k0) {
+    const int64_t e0 = k0 + 32 * lh;
+    const bool in = e0 < P.K;  // K % 64 == 32: the last step's upper half is past the end
+    if (a_ok && in) {
+      const uint4* xp = reinterpret_cast<const uint4*>(xrow + e0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = xp[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int64_t ec = in ? e0 : 0;  // a valid address; the values are not used
+    load_codes32<NB>(crow + (ec >> 5) * (4 * NB), cw);
+    const int64_t g0 = ec >> P.group_shift;
+    s16[0] = srow[g0];
+    z16[0] = zrow[g0];
+    s16[1] = srow[g0 + g2];
+    z16[1] = zrow[g0 + g2];
+  };
+  auto store_lds = [&](int buf, int64_t k0) {
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr][32 * lh]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ad[i] = ar[i];
+    uint4 bv[4];
+    if (b_ok && k0 + 32 * lh < P.K) {
+      const float s0 = h2f(s16[0]), s1 = h2f(s16[1]);
+      dequant32<NB>(cw, s0, s0 * h2f(z16[0]), s1, s1 * h2f(z16[1]), bv);  // s*z exact
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr][32 * lh]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bd[i] = bv[i];
+  };
+
   float16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -388,54 +440,32 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  if (P.K > 0) {
+    load_global(0);
+    store_lds(0, 0);
+  }
+  __syncthreads();
   for (int64_t k0 = 0; k0 < P.K; k0 += kBK) {
-    const int64_t e0 = k0 + 16 * lh;
-    uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0, b0 = a0, b1 = a0;
-    if (am < P.M) {
-      const uint4* xp = reinterpret_cast<const uint4*>(P.X + am * P.K + e0);
-      a0 = xp[0];
-      a1 = xp[1];
-    }
-    if (bn < P.N) {
-      Codes16<NB> cw;
-      cw.load(P.packed + bn * row_bytes + (e0 >> 3) * NB);
-      const int64_t gi = bn * gpr + e0 / P.group_size;
-      const float s = h2f(P.scale16[gi]);
-      const float sz = s * h2f(P.zero16[gi]);  // exact: two 11-bit significands
-      uint32_t hw[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float w0 = __builtin_fmaf(s, (float)code_at<NB>(cw.w, 2 * j), -sz);
-        const float w1 = __builtin_fmaf(s, (float)code_at<NB>(cw.w, 2 * j + 1), -sz);
-        hw[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w0) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)w1) << 16);
-      }
-      b0 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      b1 = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-    }
-    uint4* ad = reinterpret_cast<uint4*>(&As[lr][16 * lh]);
-    uint4* bd = reinterpret_cast<uint4*>(&Bs[lr][16 * lh]);
-    ad[0] = a0;
-    ad[1] = a1;
-    bd[0] = b0;
-    bd[1] = b1;
-    __syncthreads();
+    const int buf = (int)((k0 / kBK) & 1);
+    const bool more = k0 + kBK < P.K;
+    if (more) load_global(k0 + kBK);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
       half8_t af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&As[wm * 64 + i * 32 + (lane & 31)][kk]);
+        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * 64 + i * 32 + (lane & 31)][kk]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[wn * 64 + j * 32 + (lane & 31)][kk]);
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][wn * 64 + j * 32 + (lane & 31)][kk]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+    if (more) store_lds(buf ^ 1, k0 + kBK);  // last read in the previous step, before its barrier
     __syncthreads();
   }
 
