@@ -81,6 +81,8 @@ def _load():
     lib.oracle_meta_quantize.argtypes = [P, I64, I64, P, P, P]
     lib.oracle_meta_dequantize.restype = I
     lib.oracle_meta_dequantize.argtypes = [P, P, P, I64, I64, P]
+    lib.oracle_hqq_residual.restype = I
+    lib.oracle_hqq_residual.argtypes = [P, P, P, P, I64, I64, I, I, P]
     lib.oracle_hqq_matmul.restype = I
     lib.oracle_hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P]
     _lib = lib
@@ -369,3 +371,42 @@ def hqq_matmul(X_f16: np.ndarray, packed: np.ndarray, scale_f16: np.ndarray,
     if rc != 0:
         raise ValueError("oracle_hqq_matmul rejected its arguments")
     return Y
+
+
+def hqq_residual(W_f16: np.ndarray, packed: np.ndarray, scale_f16: np.ndarray,
+                 zero_f16: np.ndarray, nbits: int, group_size: int) -> np.ndarray:
+    """Delta W = W - s (W_q - z) in fp64 (hqq_oracle.c, oracle_hqq_residual)."""
+    W = np.ascontiguousarray(W_f16)
+    if W.dtype == np.float16:
+        W = W.view(np.uint16)
+    assert W.dtype == np.uint16 and W.ndim == 2
+    rows, cols = W.shape
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    sc = np.ascontiguousarray(scale_f16).view(np.uint16).ravel()
+    zr = np.ascontiguousarray(zero_f16).view(np.uint16).ravel()
+    assert sc.size == rows * (cols // group_size) and zr.size == sc.size
+    out = np.empty((rows, cols), np.float64)
+    rc = _load().oracle_hqq_residual(_ptr(W), _ptr(packed), _ptr(sc), _ptr(zr), rows, cols, nbits,
+                                     group_size, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_hqq_residual rejected its arguments")
+    return out
+
+
+def lowrank_svd(dW: np.ndarray, rank: int):
+    """The LoRA factors of the plain SVD compensation (EoRA page, section 1): with
+    Delta W = U Sigma V^T (singular values in decreasing order), B = U_r Sigma_r (rows x r)
+    and A = V_r^T (r x cols), so that B A is the best rank-r approximation of Delta W in
+    the Frobenius norm.  fp64, LAPACK's SVD as the library step.  Returns (B, A, sigma)
+    with sigma all min(rows, cols) singular values.  Each pair of singular vectors is
+    signed so that the largest-magnitude entry of the column of A^T is positive (the
+    SVD fixes the pair only up to a common sign)."""
+    dW = np.asarray(dW, np.float64)
+    U, sig, Vt = np.linalg.svd(dW, full_matrices=False)
+    r = min(rank, sig.size)
+    U, S, Vt = U[:, :r], sig[:r], Vt[:r]
+    flip = np.sign(Vt[np.arange(r), np.argmax(np.abs(Vt), axis=1)])
+    flip[flip == 0] = 1.0
+    B = U * (S * flip)
+    A = Vt * flip[:, None]
+    return B, A, sig

@@ -511,3 +511,33 @@ int oracle_hqq_matmul(const uint16_t* X_f16, int64_t M, int64_t K, const uint8_t
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* The quantization error Delta W = W - Q^-1(W_q) that a low-rank correction   */
+/* compensates (the plain SVD compensation on the EoRA page, section 1: the    */
+/* LoRA factors B = U Sigma, A = V^T of the truncated SVD of Delta W).          */
+/* ------------------------------------------------------------------------- */
+
+/* dW[i] = w[i] - s (q[i] - z) in fp64 for the rows x cols binary16 weight W and its
+ * stored codes and binary16 s, z (s (q - z) is exact in fp64, the difference is rounded
+ * once).  Returns 0, or -1 for invalid arguments. */
+int oracle_hqq_residual(const uint16_t* W_f16, const uint8_t* packed, const uint16_t* scale_f16,
+                        const uint16_t* zero_f16, int64_t rows, int64_t cols, int nbits,
+                        int group_size, double* dW) {
+  if (rows < 0 || cols < 0 || group_size <= 0 || cols % group_size != 0) return -1;
+  if (nbits < 1 || nbits > 8) return -1;
+  if (fegetround() != FE_TONEAREST) fesetround(FE_TONEAREST);
+  const int64_t n = rows * cols;
+  for (int64_t i = 0; i < n; ++i) {
+    unsigned c = 0;
+    for (int b = 0; b < nbits; ++b) {
+      const int64_t bit = i * nbits + b;
+      c |= (unsigned)((packed[bit >> 3] >> (bit & 7)) & 1) << b;
+    }
+    const int64_t gi = i / group_size;
+    const double s = oracle_f16_to_f64(scale_f16[gi]);
+    const double z = oracle_f16_to_f64(zero_f16[gi]);
+    dW[i] = oracle_f16_to_f64(W_f16[i]) - s * ((double)c - z);
+  }
+  return 0;
+}

@@ -69,4 +69,7 @@ int oracle_meta_dequantize(const uint8_t* codes, const uint16_t* scale16,
 int oracle_hqq_matmul(const uint16_t* X_f16, int64_t M, int64_t K, const uint8_t* packed,
                       const uint16_t* scale_f16, const uint16_t* zero_f16, int64_t N, int nbits,
                       int group_size, double* Y);
+int oracle_hqq_residual(const uint16_t* W_f16, const uint8_t* packed, const uint16_t* scale_f16,
+                        const uint16_t* zero_f16, int64_t rows, int64_t cols, int nbits,
+                        int group_size, double* dW);
 #endif

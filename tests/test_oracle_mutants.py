@@ -1,6 +1,7 @@
 """Mutation check of the oracle's pins (CPU only).
 
-Each case plants one plausible mistake in a private copy of the oracle's C source
+Each case plants one plausible mistake in a private copy of the oracle's C source (or,
+marked "py", of its Python module)
 (a dropped term, a wrong sign or index, a wrong rounding rule, a wrong bit order,
 ...), rebuilds that copy with gcc in a temporary directory and runs the pin suite
 against it.  Every mutant must make at least one pin fail.  The real oracle is
@@ -75,6 +76,14 @@ MUTANTS = {
                                           "const int64_t gi = (k / group_size) * N + n % gpr;"),
     "matmul code bits reversed": ("const int64_t bit = elem * nbits + b;",
                                   "const int64_t bit = elem * nbits + (nbits - 1 - b);"),
+    "residual adds the zero-point": ("dW[i] = oracle_f16_to_f64(W_f16[i]) - s * ((double)c - z);",
+                                     "dW[i] = oracle_f16_to_f64(W_f16[i]) - s * ((double)c + z);"),
+    "residual group off by one": ("    const int64_t gi = i / group_size;\n    const double s = oracle_f16_to_f64(scale_f16[gi]);\n    const double z = oracle_f16_to_f64(zero_f16[gi]);\n    dW[i]",
+                                  "    const int64_t gi = (i + 1) / group_size % (n / group_size);\n    const double s = oracle_f16_to_f64(scale_f16[gi]);\n    const double z = oracle_f16_to_f64(zero_f16[gi]);\n    dW[i]"),
+    "py: lowrank B without Sigma": ("B = U * (S * flip)", "B = U * flip", "py"),
+    "py: lowrank keeps the smallest": ("U, S, Vt = U[:, :r], sig[:r], Vt[:r]",
+                                       "U, S, Vt = U[:, -r:], sig[-r:], Vt[-r:]", "py"),
+    "py: lowrank A is V": ("A = Vt * flip[:, None]", "A = (Vt.T * flip).T[::-1]", "py"),
     "matmul skips the last k": ("for (int64_t k = 0; k < K; ++k) {\n        const int64_t elem",
                                 "for (int64_t k = 0; k < K - 1; ++k) {\n        const int64_t elem"),
 }
@@ -82,17 +91,18 @@ MUTANTS = {
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name, tmp_path):
-    before, after = MUTANTS[name]
+    before, after = MUTANTS[name][:2]
+    target = "__init__.py" if MUTANTS[name][2:] == ("py",) else "hqq_oracle.c"
     for sub in ("oracle", "workloads", "tests"):
         shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
                         ignore=shutil.ignore_patterns("*.so", "__pycache__"))
-    src_path = tmp_path / "oracle" / "hqq_oracle.c"
+    src_path = tmp_path / "oracle" / target
     src = src_path.read_text()
     assert src.count(before) >= 1, f"mutation site for {name!r} not found"
     src_path.write_text(src.replace(before, after, 1))
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py", "tests/test_oracle_meta_pins.py",
-                        "tests/test_oracle_matmul_pins.py"],
+                        "tests/test_oracle_matmul_pins.py", "tests/test_oracle_lowrank_pins.py"],
                        cwd=tmp_path, capture_output=True, text=True, timeout=600, env=env)
     assert r.returncode != 0, f"mutant {name!r} survived the pins:\n{r.stdout[-2000:]}"
