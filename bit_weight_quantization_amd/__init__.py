@@ -28,6 +28,7 @@ HQQ_ERR_LAUNCH = 4
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
                     "hqq_quantize_tensor_stop", "hqq_tensor_stop_workspace_bytes", "hqq_matmul",
+                    "hqq_residual", "hqq_lowrank", "hqq_lowrank_workspace_bytes",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
                     "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
@@ -72,6 +73,12 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_tensor_stop.restype = I
     lib.hqq_quantize_tensor_stop.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
                                              ctypes.POINTER(hqq_options_t), P, P, P, P]
+    lib.hqq_residual.restype = I
+    lib.hqq_residual.argtypes = [P, P, P, P, I64, I64, I, I, P, P, P]
+    lib.hqq_lowrank.restype = I
+    lib.hqq_lowrank.argtypes = [P, P, P, P, I64, I64, I, I, I, I, I, P, P, P, P, P, P]
+    lib.hqq_lowrank_workspace_bytes.restype = I64
+    lib.hqq_lowrank_workspace_bytes.argtypes = [I64, I64, I, I]
     lib.hqq_matmul.restype = I
     lib.hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P, I, P]
     lib.hqq_tensor_stop_workspace_bytes.restype = I64
@@ -146,6 +153,26 @@ def hqq_matmul(X_f16: int, M: int, K: int, packed_codes: int, scale_f16: int, ze
                N: int, nbits: int, group_size: int, Y: int, out_f32: int, stream: int = 0) -> int:
     return load_library().hqq_matmul(X_f16, M, K, packed_codes, scale_f16, zero_f16, N, nbits,
                                      group_size, Y, out_f32, stream)
+
+
+def hqq_residual(W_f16: int, packed_codes: int, scale_f16: int, zero_f16: int, rows: int,
+                 cols: int, nbits: int, group_size: int, dW_f16: int, dWT_f16: int,
+                 stream: int = 0) -> int:
+    return load_library().hqq_residual(W_f16, packed_codes, scale_f16, zero_f16, rows, cols, nbits,
+                                       group_size, dW_f16, dWT_f16, stream)
+
+
+def hqq_lowrank(W_f16: int, packed_codes: int, scale_f16: int, zero_f16: int, rows: int,
+                cols: int, nbits: int, group_size: int, rank: int, oversample: int,
+                power_iters: int, omega_f16: int, B_f32: int, A_f32: int, sigma_f32: int,
+                workspace: int, stream: int = 0) -> int:
+    return load_library().hqq_lowrank(W_f16, packed_codes, scale_f16, zero_f16, rows, cols, nbits,
+                                      group_size, rank, oversample, power_iters, omega_f16, B_f32,
+                                      A_f32, sigma_f32, workspace, stream)
+
+
+def hqq_lowrank_workspace_bytes(rows: int, cols: int, rank: int, oversample: int) -> int:
+    return load_library().hqq_lowrank_workspace_bytes(rows, cols, rank, oversample)
 
 
 def hqq_tensor_stop_workspace_bytes(iters: int) -> int:
@@ -339,6 +366,49 @@ def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, stream=None
     if st != HQQ_OK:
         raise HQQError(st, "hqq_matmul")
     return out
+
+
+def residual(W, q: "QuantizedWeight", transposed: bool = False, stream=None):
+    """Delta W = W - Q^-1(W_q) as float16 (hqq_residual); with ``transposed`` also its
+    transpose.  Returns dW or (dW, dWT)."""
+    import torch
+    dW = torch.empty_like(W)
+    dWT = torch.empty((W.shape[1], W.shape[0]), dtype=W.dtype, device=W.device) if transposed else None
+    st = hqq_residual(_addr(W), _addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows, q.cols,
+                      q.nbits, q.group_size, _addr(dW), _addr(dWT), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_residual")
+    return (dW, dWT) if transposed else dW
+
+
+def lowrank(W, q: "QuantizedWeight", rank: int, oversample: int = 32, power_iters: int = 4,
+            omega=None, seed: int = 0, workspace=None, stream=None):
+    """LoRA factors (B: rows x rank, A: rank x cols, sigma) of the quantization error of W
+    under q (hqq_lowrank).  ``omega`` may supply the (rank + oversample) x cols float16 test
+    matrix; otherwise it is drawn from a standard normal with ``seed`` on W's device."""
+    import torch
+    rows, cols = W.shape
+    width = rank + oversample
+    if omega is None:
+        gen = torch.Generator(device=W.device)
+        gen.manual_seed(int(seed))
+        omega = torch.randn((width, cols), generator=gen, device=W.device).half()
+    wb = hqq_lowrank_workspace_bytes(rows, cols, rank, oversample)
+    if wb < 0:
+        raise HQQError(HQQ_ERR_INVALID_ARG, "lowrank")
+    if workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+        if stream is not None:
+            workspace.record_stream(stream)
+    B = torch.empty((rows, rank), dtype=torch.float32, device=W.device)
+    A = torch.empty((rank, cols), dtype=torch.float32, device=W.device)
+    sigma = torch.empty(rank, dtype=torch.float32, device=W.device)
+    st = hqq_lowrank(_addr(W), _addr(q.packed), _addr(q.scale), _addr(q.zero), rows, cols, q.nbits,
+                     q.group_size, rank, oversample, power_iters, _addr(omega), _addr(B), _addr(A),
+                     _addr(sigma), _addr(workspace), _stream_handle(stream))
+    if st != HQQ_OK:
+        raise HQQError(st, "hqq_lowrank")
+    return B, A, sigma
 
 
 @dataclass

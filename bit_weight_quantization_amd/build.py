@@ -13,10 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libhqq_mi355x.so")
 SOURCES = [os.path.join(CSRC, "hqq_kernels.hip"), os.path.join(CSRC, "hqq_tensor_stop.hip"),
-           os.path.join(CSRC, "hqq_matmul.hip"),
+           os.path.join(CSRC, "hqq_matmul.hip"), os.path.join(CSRC, "hqq_lowrank.hip"),
            os.path.join(CSRC, "hqq_meta.hip"), os.path.join(CSRC, "hqq_api.hip")]
 HEADERS = [os.path.join(CSRC, "hqq_internal.h"), os.path.join(CSRC, "hqq_solver.h"),
            os.path.join(CSRC, "hqq_tensor_stop.h"), os.path.join(CSRC, "hqq_matmul.h"),
+           os.path.join(CSRC, "hqq_lowrank.h"),
            os.path.join(ROOT, "include", "hqq.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -8,6 +8,7 @@
 
 #include "../../include/hqq.h"
 #include "hqq_internal.h"
+#include "hqq_lowrank.h"
 #include "hqq_matmul.h"
 #include "hqq_tensor_stop.h"
 
@@ -337,6 +338,82 @@ int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;
   hipError_t err = hqq::launch_matmul(prm, cus, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+// Shapes of the residual and low-rank entry points: rows and cols multiples of 64,
+// cols a multiple of the group size.
+int validate_lowrank_shape(int64_t rows, int64_t cols, int nbits, int group_size) {
+  int st = validate_common(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  if (rows % 64 != 0 || cols % 64 != 0) return HQQ_ERR_UNSUPPORTED;
+  return HQQ_OK;
+}
+
+int hqq_residual(const void* W_f16, const void* packed_codes, const void* scale_f16,
+                 const void* zero_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                 void* dW_f16, void* dWT_f16, void* stream) {
+  int st = validate_lowrank_shape(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  if (rows * cols == 0) return HQQ_OK;
+  if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16 || !dW_f16) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(W_f16, 16) || !aligned(packed_codes, 16) || !aligned(scale_f16, 2) ||
+      !aligned(zero_f16, 2) || !aligned(dW_f16, 16) || (dWT_f16 && !aligned(dWT_f16, 16)))
+    return HQQ_ERR_ALIGNMENT;
+  hipError_t err = hqq::launch_residual(
+      static_cast<const uint16_t*>(W_f16), static_cast<const uint8_t*>(packed_codes),
+      static_cast<const uint16_t*>(scale_f16), static_cast<const uint16_t*>(zero_f16), rows, cols,
+      nbits, group_size, static_cast<uint16_t*>(dW_f16), static_cast<uint16_t*>(dWT_f16),
+      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+int64_t hqq_lowrank_workspace_bytes(int64_t rows, int64_t cols, int rank, int oversample) {
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 64 != 0) return -1;
+  if (checked_elems(rows, cols) < 0) return -1;
+  if (rank < 1 || oversample < 0) return -1;
+  const int64_t width = (int64_t)rank + oversample;
+  if (width % 32 != 0 || width > 512 || width > rows || width > cols) return -1;
+  return hqq::lowrank_workspace_bytes(rows, cols, (int)width);
+}
+
+int hqq_lowrank(const void* W_f16, const void* packed_codes, const void* scale_f16,
+                const void* zero_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                int rank, int oversample, int power_iters, const void* omega_f16, void* B_f32,
+                void* A_f32, void* sigma_f32, void* workspace, void* stream) {
+  int st = validate_lowrank_shape(rows, cols, nbits, group_size);
+  if (st != HQQ_OK) return st;
+  if (rows == 0 || cols == 0) return HQQ_ERR_INVALID_ARG;
+  if (hqq_lowrank_workspace_bytes(rows, cols, rank, oversample) < 0) return HQQ_ERR_INVALID_ARG;
+  if (power_iters < 0 || power_iters > 16) return HQQ_ERR_INVALID_ARG;
+  if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16 || !omega_f16 || !B_f32 || !A_f32 ||
+      !sigma_f32 || !workspace)
+    return HQQ_ERR_INVALID_ARG;
+  if (!aligned(W_f16, 16) || !aligned(packed_codes, 16) || !aligned(scale_f16, 2) ||
+      !aligned(zero_f16, 2) || !aligned(omega_f16, 16) || !aligned(B_f32, 4) ||
+      !aligned(A_f32, 4) || !aligned(sigma_f32, 4) || !aligned(workspace, 256))
+    return HQQ_ERR_ALIGNMENT;
+  hqq::LowrankParams prm;
+  prm.W = static_cast<const uint16_t*>(W_f16);
+  prm.packed = static_cast<const uint8_t*>(packed_codes);
+  prm.scale16 = static_cast<const uint16_t*>(scale_f16);
+  prm.zero16 = static_cast<const uint16_t*>(zero_f16);
+  prm.m = rows;
+  prm.n = cols;
+  prm.nbits = nbits;
+  prm.group_size = group_size;
+  prm.group_shift = group_size == 16 ? 4 : group_size == 32 ? 5 : group_size == 64 ? 6 : 7;
+  prm.rank = rank;
+  prm.width = rank + oversample;
+  prm.power_iters = power_iters;
+  prm.omega = static_cast<const uint16_t*>(omega_f16);
+  prm.B = static_cast<float*>(B_f32);
+  prm.A = static_cast<float*>(A_f32);
+  prm.sigma = static_cast<float*>(sigma_f32);
+  prm.workspace = workspace;
+  int cus = compute_units();
+  if (cus <= 0) return HQQ_ERR_LAUNCH;
+  hipError_t err = hqq::launch_lowrank(prm, cus, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 

@@ -1,0 +1,573 @@
+// hqq_lowrank.hip -- gfx950 kernels of the data-free low-rank compensation of the
+// quantization error: the plain SVD compensation described on the EoRA page (section 1):
+// Delta W = W - W_hat = U Sigma V^T, LoRA factors B = U_r Sigma_r, A = V_r^T, with W_hat
+// = s (W_q - z) the inverse quantizer of section 2 of "Half-Quadratic Quantization of
+// Large Machine Learning Models" applied to the stored codes.
+//
+// The truncated SVD is computed by randomized subspace iteration: Y = Delta W Omega for
+// a caller-supplied Gaussian test matrix Omega (n x l, l = r + oversampling), q power
+// steps Y <- Delta W orth(Delta W^T orth(Y)), Q = orth(Y), then the SVD of the small
+// B_m = Q^T Delta W through the eigendecomposition of B_m B_m^T.  The heavy work is the
+// products with Delta W, which is materialized once as binary16 in both layouts so every
+// product is a plain matrix-core GEMM with fp32 accumulation; orthonormalization is by
+// the eigendecomposition of the l x l Gram matrix (Q = Y V Lambda^-1/2), computed by
+// cyclic Jacobi in fp64 in one block.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hqq_internal.h"
+#include "hqq_lowrank.h"
+
+namespace hqq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float h2f(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---------------------------------------------------------------- residual --
+
+constexpr int kTile = 64;
+
+// One 64 x 64 tile of Delta W per block: thread t computes row t / 4, 16 consecutive
+// columns (inside one group), w - (s q - s z) in fp32 (s z exact, two roundings), stores
+// binary16 to Delta W and, through LDS, to its transpose.
+template <int NB>
+__global__ __launch_bounds__(kBlock) void residual_kernel(const uint16_t* __restrict__ W,
+                                                          const uint8_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ s16,
+                                                          const uint16_t* __restrict__ z16,
+                                                          int64_t m, int64_t n, int gshift,
+                                                          uint16_t* __restrict__ dW,
+                                                          uint16_t* __restrict__ dWT) {
+  __shared__ uint16_t tile[kTile][kTile + 2];
+  const int t = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.y * kTile, k0 = (int64_t)blockIdx.x * kTile;
+  const int ri = t >> 2, ck = (t & 3) * 16;
+  const int64_t e = (i0 + ri) * n + k0 + ck;  // flat element index of the 16 weights
+  const uint4* wp = reinterpret_cast<const uint4*>(W + e);
+  const uint4 wa = wp[0], wb = wp[1];
+  const uint32_t ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+  uint32_t cw[2] = {0u, 0u};  // the 16 codes: 2 NB bytes at byte e NB / 8
+  const uint8_t* cp = packed + (e >> 3) * NB;
+  if constexpr (NB == 2) {
+    cw[0] = *reinterpret_cast<const uint32_t*>(cp);
+  } else if constexpr (NB == 3) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(cp);
+    cw[0] = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+    cw[1] = q[2];
+  } else if constexpr (NB == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(cp);
+    cw[0] = v.x; cw[1] = v.y;
+  }
+  uint32_t cw8[4] = {0u, 0u, 0u, 0u};
+  if constexpr (NB == 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(cp);
+    cw8[0] = v.x; cw8[1] = v.y; cw8[2] = v.z; cw8[3] = v.w;
+  }
+  const int64_t gi = e >> gshift;
+  const float s = h2f(s16[gi]);
+  const float sz = s * h2f(z16[gi]);
+  uint32_t out[8];
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    uint32_t q0, q1;
+    if constexpr (NB == 8) {
+      q0 = (cw8[j >> 2] >> (8 * (j & 3))) & 255u;
+      q1 = (cw8[(j + 1) >> 2] >> (8 * ((j + 1) & 3))) & 255u;
+    } else {
+      const int b0 = NB * j, b1 = NB * (j + 1);
+      constexpr uint32_t mask = (1u << NB) - 1u;
+      q0 = (b0 >> 5) == ((b0 + NB - 1) >> 5)
+               ? (cw[b0 >> 5] >> (b0 & 31)) & mask
+               : __builtin_amdgcn_alignbit(cw[1], cw[0], b0 & 31) & mask;
+      q1 = (b1 >> 5) == ((b1 + NB - 1) >> 5)
+               ? (cw[b1 >> 5] >> (b1 & 31)) & mask
+               : __builtin_amdgcn_alignbit(cw[1], cw[0], b1 & 31) & mask;
+    }
+    const float r0 = h2f(ww[j >> 1] & 0xffffu) - __builtin_fmaf(s, (float)q0, -sz);
+    const float r1 = h2f(ww[j >> 1] >> 16) - __builtin_fmaf(s, (float)q1, -sz);
+    out[j >> 1] = f2h(r0) | (f2h(r1) << 16);
+  }
+  uint4* dp = reinterpret_cast<uint4*>(dW + e);
+  dp[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dp[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  if (!dWT) return;  // block-uniform: no transposed copy wanted
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tile[ri][ck + 2 * j] = (uint16_t)(out[j] & 0xffffu);
+    tile[ri][ck + 2 * j + 1] = (uint16_t)(out[j] >> 16);
+  }
+  __syncthreads();
+  const int rk = t >> 2, ci = (t & 3) * 16;  // transposed: row k0 + rk, columns i0 + ci ..
+  uint32_t tw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    tw[j] = (uint32_t)tile[ci + 2 * j][rk] | ((uint32_t)tile[ci + 2 * j + 1][rk] << 16);
+  uint4* tp = reinterpret_cast<uint4*>(dWT + (k0 + rk) * m + i0 + ci);
+  tp[0] = make_uint4(tw[0], tw[1], tw[2], tw[3]);
+  tp[1] = make_uint4(tw[4], tw[5], tw[6], tw[7]);
+}
+
+// -------------------------------------------------------------- fp16 GEMM --
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsRow = kBK + 8;
+
+// P[z][i][j] = sum over k in split z's slice of A[i][k] * B[j][k]: A is M x K and B is
+// L x K binary16 (K contiguous), P fp32 (M x L per split).  128 x 128 tiles of four
+// wavefronts (2 x 2 v_mfma_f32_32x32x16_f16 each), 64-wide K steps through double-buffered
+// LDS.  M and K are multiples of 64; rows of B past L are zero.
+__global__ __launch_bounds__(kBlock) void gemm16_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B,
+                                                        int64_t M, int64_t K, int L,
+                                                        int64_t kslice, float* __restrict__ P) {
+  __shared__ __align__(16) _Float16 As[2][kBM][kLdsRow];
+  __shared__ __align__(16) _Float16 Bs[2][kBN][kLdsRow];
+  const int tid = threadIdx.x;
+  const int wid = tid / kWave, lane = tid & (kWave - 1);
+  const int wm = wid >> 1, wn = wid & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * kBM;
+  const int n0 = blockIdx.y * kBN;
+  const int64_t kb = (int64_t)blockIdx.z * kslice;
+  const int64_t ke = kb + kslice < K ? kb + kslice : K;
+  const int lr = tid >> 1, lh = tid & 1;
+  const bool a_ok = m0 + lr < M, b_ok = n0 + lr < L;
+  const uint16_t* arow = A + (a_ok ? m0 + lr : 0) * K;
+  const uint16_t* brow = B + (int64_t)(b_ok ? n0 + lr : 0) * K;
+  uint4 ar[4], br[4];
+  auto load_global = [&](int64_t k0) {
+    const uint4* ap = reinterpret_cast<const uint4*>(arow + k0 + 32 * lh);
+    const uint4* bp = reinterpret_cast<const uint4*>(brow + k0 + 32 * lh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ar[i] = a_ok ? ap[i] : make_uint4(0u, 0u, 0u, 0u);
+      br[i] = b_ok ? bp[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_lds = [&](int buf) {
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr][32 * lh]);
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr][32 * lh]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ad[i] = ar[i];
+      bd[i] = br[i];
+    }
+  };
+  float16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (kb < ke) {
+    load_global(kb);
+    store_lds(0);
+  }
+  __syncthreads();
+  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    const int buf = (int)(((k0 - kb) / kBK) & 1);
+    const bool more = k0 + kBK < ke;
+    if (more) load_global(k0 + kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      half8_t af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * 64 + i * 32 + (lane & 31)][kk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][wn * 64 + j * 32 + (lane & 31)][kk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store_lds(buf ^ 1);
+    __syncthreads();
+  }
+  float* out = P + (int64_t)blockIdx.z * M * L;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t mm = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (mm < M && n < L) out[mm * L + n] = acc[i][j][v];
+      }
+    }
+  }
+}
+
+// out[e] = sum over splits s (in order) of P[s][e], e < count.
+__global__ __launch_bounds__(kBlock) void split_sum_kernel(const float* __restrict__ P, int splits,
+                                                           int64_t count, float* __restrict__ out) {
+  for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * kBlock) {
+    float v = P[e];
+    for (int s = 1; s < splits; ++s) v += P[(int64_t)s * count + e];
+    out[e] = v;
+  }
+}
+
+// ------------------------------------------------------------------- Gram --
+
+// G[a][b] = sum over rows i of X[i][a] X[i][b] for X (M x L fp32): block (a0, b0) of
+// 32 x 32 entries; 64-row chunks of the two column slabs through LDS, fp32 sums per chunk
+// added in fp64.  Thread t: entry a0 + t % 32, b0 + 4 (t / 32) .. + 4.
+__global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ X, int64_t M, int L,
+                                                      double* __restrict__ G) {
+  __shared__ float xa[64][33], xb[64][33];
+  const int t = threadIdx.x;
+  const int a0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
+  const int ta = t & 31, tb = (t >> 5) * 4;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t i0 = 0; i0 < M; i0 += 64) {
+    // 64 rows x 32 columns of each slab: 2048 values each, 8 per thread
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = t + u * kBlock;
+      const int r = idx >> 5, c = idx & 31;
+      const int64_t i = i0 + r;
+      xa[r][c] = i < M ? X[i * L + a0 + c] : 0.f;
+      xb[r][c] = i < M ? X[i * L + b0 + c] : 0.f;
+    }
+    __syncthreads();
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int r = 0; r < 64; ++r) {
+      const float va = xa[r][ta];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[j] = __builtin_fmaf(va, xb[r][tb + j], part[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += (double)part[j];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) G[(int64_t)(a0 + ta) * L + b0 + tb + j] = acc[j];
+}
+
+// ------------------------------------------------------- symmetric eigen --
+
+constexpr int kEigThreads = 1024;
+constexpr int kMaxWidth = 512;
+
+// Cyclic Jacobi on the symmetric L x L matrix S (fp64, overwritten; L even): round-robin
+// ordering, L / 2 disjoint rotations per round (all computed first, then applied to the
+// rows, then to the columns and to V), rounds of L - 1 per sweep until the off-diagonal
+// norm is below 1e-15 of the diagonal's (at most 30 sweeps).  On exit: V (L x L) holds
+// the eigenvectors in its columns, evals the eigenvalues, order their indices by
+// decreasing eigenvalue.  One block.
+__global__ __launch_bounds__(kEigThreads) void jacobi_kernel(double* __restrict__ S, int L,
+                                                             double* __restrict__ V,
+                                                             double* __restrict__ evals,
+                                                             int* __restrict__ order) {
+  __shared__ int pp[kMaxWidth / 2], qq[kMaxWidth / 2];
+  __shared__ double cc[kMaxWidth / 2], ss[kMaxWidth / 2];
+  __shared__ double red[kEigThreads / kWave][2];
+  __shared__ int done;
+  const int t = threadIdx.x;
+  const int half = L / 2;
+  for (int64_t e = t; e < (int64_t)L * L; e += kEigThreads)
+    V[e] = (e / L == e % L) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    // convergence test: off-diagonal vs diagonal squared norms
+    double off = 0.0, dia = 0.0;
+    for (int64_t e = t; e < (int64_t)L * L; e += kEigThreads) {
+      const double v = S[e];
+      if (e / L == e % L) dia += v * v;
+      else off += v * v;
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o, kWave);
+      dia += __shfl_xor(dia, o, kWave);
+    }
+    if ((t & (kWave - 1)) == 0) {
+      red[t / kWave][0] = off;
+      red[t / kWave][1] = dia;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double o2 = 0.0, d2 = 0.0;
+      for (int w = 0; w < kEigThreads / kWave; ++w) {
+        o2 += red[w][0];
+        d2 += red[w][1];
+      }
+      done = (o2 <= 1e-30 * d2) ? 1 : 0;
+    }
+    __syncthreads();
+    if (done) break;
+    for (int round = 0; round < L - 1; ++round) {
+      if (t < half) {
+        // pair t: positions t and L - 1 - t; position 0 holds index 0, the others rotate
+        const int pa = t, pb = L - 1 - t;
+        const int ia = pa == 0 ? 0 : 1 + (pa - 1 + round) % (L - 1);
+        const int ib = 1 + (pb - 1 + round) % (L - 1);
+        const int p = ia < ib ? ia : ib, q = ia < ib ? ib : ia;
+        const double apq = S[(int64_t)p * L + q];
+        const double app = S[(int64_t)p * L + p], aqq = S[(int64_t)q * L + q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0 && __builtin_fabs(apq) > 1e-300) {
+          const double tau = (aqq - app) / (2.0 * apq);
+          const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (__builtin_fabs(tau) + __builtin_sqrt(1.0 + tau * tau));
+          c = 1.0 / __builtin_sqrt(1.0 + tt * tt);
+          s = tt * c;
+        }
+        pp[t] = p;
+        qq[t] = q;
+        cc[t] = c;
+        ss[t] = s;
+      }
+      __syncthreads();
+      // rows p, q of S: S <- J^T S
+      for (int64_t w = t; w < (int64_t)half * L; w += kEigThreads) {
+        const int j = (int)(w / L), col = (int)(w % L);
+        const int p = pp[j], q = qq[j];
+        const double c = cc[j], s = ss[j];
+        const double a = S[(int64_t)p * L + col], b = S[(int64_t)q * L + col];
+        S[(int64_t)p * L + col] = c * a - s * b;
+        S[(int64_t)q * L + col] = s * a + c * b;
+      }
+      __syncthreads();
+      // columns p, q of S and of V: S <- S J, V <- V J
+      for (int64_t w = t; w < (int64_t)half * L; w += kEigThreads) {
+        const int j = (int)(w / L), row = (int)(w % L);
+        const int p = pp[j], q = qq[j];
+        const double c = cc[j], s = ss[j];
+        const double a = S[(int64_t)row * L + p], b = S[(int64_t)row * L + q];
+        S[(int64_t)row * L + p] = c * a - s * b;
+        S[(int64_t)row * L + q] = s * a + c * b;
+        const double va = V[(int64_t)row * L + p], vb = V[(int64_t)row * L + q];
+        V[(int64_t)row * L + p] = c * va - s * vb;
+        V[(int64_t)row * L + q] = s * va + c * vb;
+      }
+      __syncthreads();
+    }
+  }
+  // eigenvalues and their order (rank by decreasing value, ties by index)
+  for (int i = t; i < L; i += kEigThreads) evals[i] = S[(int64_t)i * L + i];
+  __syncthreads();
+  for (int i = t; i < L; i += kEigThreads) {
+    const double v = evals[i];
+    int rank = 0;
+    for (int j = 0; j < L; ++j) {
+      const double u = evals[j];
+      rank += (u > v || (u == v && j < i)) ? 1 : 0;
+    }
+    order[rank] = i;
+  }
+}
+
+// T[b][c] = V[b][order[c]] * f(order[c]) for c < C (L x C fp32), where f is
+// mode 0: 1/sqrt(lambda) (0 for lambda <= 1e-12 lambda_max: orthonormalization);
+// mode 1: sqrt(lambda) (sigma); mode 2: 1/sqrt(lambda) as mode 0.  sigma (may be null):
+// sqrt(lambda) of the first C eigenvalues in decreasing order.
+__global__ __launch_bounds__(kBlock) void transform_kernel(const double* __restrict__ V,
+                                                           const double* __restrict__ evals,
+                                                           const int* __restrict__ order, int L,
+                                                           int C, int mode, float* __restrict__ T,
+                                                           float* __restrict__ sigma) {
+  const double lmax = evals[order[0]];
+  for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < (int64_t)L * C;
+       e += (int64_t)gridDim.x * kBlock) {
+    const int b = (int)(e / C), c = (int)(e % C);
+    const int k = order[c];
+    const double lam = evals[k];
+    double f;
+    if (mode == 1) f = lam > 0.0 ? __builtin_sqrt(lam) : 0.0;
+    else f = (lam > 1e-12 * lmax && lam > 0.0) ? 1.0 / __builtin_sqrt(lam) : 0.0;
+    T[e] = (float)(V[(int64_t)b * L + k] * f);
+    if (sigma && b == 0) sigma[c] = (float)(lam > 0.0 ? __builtin_sqrt(lam) : 0.0);
+  }
+}
+
+// Out = X T for X (M x L fp32, row-major) and T (L x C fp32): block of 64 rows x 32
+// columns, T's 32 columns staged in LDS; thread t: column c0 + t % 32, rows 8 (t / 32) ..
+// + 8.  Outputs (each may be null): row-major fp32 (M x C), transposed fp32 (C x M),
+// transposed binary16 (C x M, row stride ldt).
+__global__ __launch_bounds__(kBlock) void apply_kernel(const float* __restrict__ X, int64_t M, int L,
+                                                       const float* __restrict__ T, int C,
+                                                       float* __restrict__ out_rm,
+                                                       float* __restrict__ out_t32,
+                                                       uint16_t* __restrict__ out_t16) {
+  __shared__ float ts[kMaxWidth][33];
+  const int t = threadIdx.x;
+  const int c0 = blockIdx.y * 32;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  for (int e = t; e < L * 32; e += kBlock) {
+    const int b = e >> 5, c = e & 31;
+    ts[b][c] = c0 + c < C ? T[(int64_t)b * C + c0 + c] : 0.f;
+  }
+  __syncthreads();
+  const int c = t & 31, rb = (t >> 5) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < L; ++b) {
+    const float tv = ts[b][c];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t i = i0 + rb + r;
+      const float xv = i < M ? X[i * L + b] : 0.f;
+      acc[r] = __builtin_fmaf(xv, tv, acc[r]);
+    }
+  }
+  if (c0 + c < C) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t i = i0 + rb + r;
+      if (i < M) {
+        if (out_rm) out_rm[i * C + c0 + c] = acc[r];
+        if (out_t32) out_t32[(int64_t)(c0 + c) * M + i] = acc[r];
+        if (out_t16) out_t16[(int64_t)(c0 + c) * M + i] = (uint16_t)f2h(acc[r]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ driver --
+
+struct Carve {
+  char* p;
+  template <typename T>
+  T* take(int64_t count) {
+    T* r = reinterpret_cast<T*>(p);
+    p += (count * (int64_t)sizeof(T) + 255) & ~(int64_t)255;
+    return r;
+  }
+};
+
+constexpr int64_t kPartialBudget = 64ll << 20;  // bytes of split-K partials at most
+
+int gemm_splits(int64_t M, int64_t K, int L) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((L + kBN - 1) / kBN);
+  int64_t s = (512 + tiles - 1) / tiles;
+  if (s > 8) s = 8;
+  if (s > K / kBK) s = K / kBK;
+  const int64_t cap = kPartialBudget / (M * L * 4);
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : (int)s;
+}
+
+}  // namespace
+
+int64_t lowrank_workspace_bytes(int64_t m, int64_t n, int width) {
+  const int64_t L = width, mx = m > n ? m : n;
+  auto al = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
+  const int64_t sm = gemm_splits(m, n, width), sn = gemm_splits(n, m, width);
+  const int64_t part = (sm * m > sn * n ? sm * m : sn * n) * L * 4;
+  return al(m * n * 2) * 2 + al(mx * L * 4) + al(part) + al(L * mx * 2) + al(m * L * 4) +
+         al(L * L * 8) * 2 + al(L * 8) + al(L * 4) + al(L * L * 4);
+}
+
+hipError_t launch_residual(const uint16_t* W, const uint8_t* packed, const uint16_t* scale16,
+                           const uint16_t* zero16, int64_t m, int64_t n, int nbits, int group_size,
+                           uint16_t* dW, uint16_t* dWT, hipStream_t st) {
+  const int gshift = group_size == 16 ? 4 : group_size == 32 ? 5 : group_size == 64 ? 6 : 7;
+  const dim3 grid((unsigned)(n / kTile), (unsigned)(m / kTile));
+  switch (nbits) {
+    case 2: hipLaunchKernelGGL(residual_kernel<2>, grid, dim3(kBlock), 0, st, W, packed, scale16, zero16, m, n, gshift, dW, dWT); break;
+    case 3: hipLaunchKernelGGL(residual_kernel<3>, grid, dim3(kBlock), 0, st, W, packed, scale16, zero16, m, n, gshift, dW, dWT); break;
+    case 4: hipLaunchKernelGGL(residual_kernel<4>, grid, dim3(kBlock), 0, st, W, packed, scale16, zero16, m, n, gshift, dW, dWT); break;
+    case 8: hipLaunchKernelGGL(residual_kernel<8>, grid, dim3(kBlock), 0, st, W, packed, scale16, zero16, m, n, gshift, dW, dWT); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
+  const int L = P.width;
+  const int64_t m = P.m, n = P.n, mx = m > n ? m : n;
+  Carve cv{static_cast<char*>(P.workspace)};
+  uint16_t* dW = cv.take<uint16_t>(m * n);
+  uint16_t* dWT = cv.take<uint16_t>(m * n);
+  float* Y = cv.take<float>(mx * L);
+  const int64_t sm = gemm_splits(m, n, L), sn = gemm_splits(n, m, L);
+  float* part = cv.take<float>((sm * m > sn * n ? sm * m : sn * n) * L);
+  uint16_t* Q16 = cv.take<uint16_t>((int64_t)L * mx);
+  float* Q32 = cv.take<float>(m * L);
+  double* G = cv.take<double>((int64_t)L * L);
+  double* V = cv.take<double>((int64_t)L * L);
+  double* ev = cv.take<double>(L);
+  int* ord = cv.take<int>(L);
+  float* T = cv.take<float>((int64_t)L * L);
+  hipError_t err;
+  const int64_t grid_cap = (int64_t)cus * 8;
+
+  // Y (M x L) = A (M x K) B^T for B (L x K)
+  auto gemm = [&](const uint16_t* A, int64_t M, int64_t K, const uint16_t* B) -> hipError_t {
+    const int s = gemm_splits(M, K, L);
+    const int64_t steps = K / kBK;
+    const int64_t kslice = ((steps + s - 1) / s) * kBK;
+    const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((L + kBN - 1) / kBN), (unsigned)s);
+    hipLaunchKernelGGL(gemm16_kernel, grid, dim3(kBlock), 0, st, A, B, M, K, L, kslice, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t count = M * L;
+    int64_t blocks = (count + kBlock - 1) / kBlock;
+    if (blocks > grid_cap) blocks = grid_cap;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, part, s, count, Y);
+    return hipGetLastError();
+  };
+  // eigendecomposition of the Gram matrix of Y (M x L)
+  auto eig_of_gram = [&](int64_t M) -> hipError_t {
+    hipLaunchKernelGGL(gram_kernel, dim3(L / 32, L / 32), dim3(kBlock), 0, st, Y, M, L, G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+    return hipGetLastError();
+  };
+  // Q^T (L x M, binary16) = (Y V Lambda^-1/2)^T, and Q (M x L fp32) if q32
+  auto orth = [&](int64_t M, float* q32) -> hipError_t {
+    hipError_t e = eig_of_gram(M);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * L + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       st, V, ev, ord, L, L, 0, T, (float*)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock), 0,
+                       st, Y, M, L, T, L, q32, (float*)nullptr, Q16);
+    return hipGetLastError();
+  };
+
+  if ((err = launch_residual(P.W, P.packed, P.scale16, P.zero16, m, n, P.nbits, P.group_size, dW,
+                             dWT, st)) != hipSuccess)
+    return err;
+  if ((err = gemm(dW, m, n, P.omega)) != hipSuccess) return err;  // Y = dW Omega
+  for (int it = 0; it < P.power_iters; ++it) {
+    if ((err = orth(m, nullptr)) != hipSuccess) return err;       // Q16 = orth(Y)^T
+    if ((err = gemm(dWT, n, m, Q16)) != hipSuccess) return err;   // Y = dW^T Q   (n x L)
+    if ((err = orth(n, nullptr)) != hipSuccess) return err;       // Q16 = orth(Y)^T
+    if ((err = gemm(dW, m, n, Q16)) != hipSuccess) return err;    // Y = dW Q     (m x L)
+  }
+  if ((err = orth(m, Q32)) != hipSuccess) return err;             // Q (m x L)
+  if ((err = gemm(dWT, n, m, Q16)) != hipSuccess) return err;     // Y = dW^T Q = B_m^T (n x L)
+  if ((err = eig_of_gram(n)) != hipSuccess) return err;           // B_m B_m^T = U~ Lambda U~^T
+  const int r = P.rank;
+  // B = Q U~_r Sigma_r (m x r);  A = Sigma_r^-1 U~_r^T B_m = (B_m^T U~_r Sigma_r^-1)^T (r x n)
+  hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                     V, ev, ord, L, r, 1, T, P.sigma);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((m + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
+                     st, Q32, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                     V, ev, ord, L, r, 2, T, (float*)nullptr);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
+                     st, Y, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace hqq

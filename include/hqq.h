@@ -309,6 +309,60 @@ int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes
                const void* scale_f16, const void* zero_f16, int64_t N, int nbits,
                int group_size, void* Y, int out_f32, void* stream);
 
+/*
+ * hqq_residual -- the quantization error Delta W = W - Q^-1(W_q) of a weight quantized
+ * by hqq_quantize (Q^-1(W_q) = s (W_q - z), section 2 of the page above), as binary16:
+ * w - (s q - s z) in fp32 (s z exact) rounded to binary16.
+ * W_f16, packed_codes, scale_f16, zero_f16  the rows x cols weight and its stored
+ *              quantization (W 16-byte, packed_codes 16-byte, s and z 2-byte aligned).
+ * rows, cols   multiples of 64 (else HQQ_ERR_UNSUPPORTED); cols % group_size == 0.
+ * dW_f16       rows x cols binary16, row-major, 16-byte aligned.
+ * dWT_f16      NULL, or its transpose (cols x rows, row-major), 16-byte aligned.
+ * Conventions and errors as for hqq_quantize.
+ */
+int hqq_residual(const void* W_f16, const void* packed_codes, const void* scale_f16,
+                 const void* zero_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                 void* dW_f16, void* dWT_f16, void* stream);
+
+/*
+ * hqq_lowrank -- data-free low-rank compensation of the quantization error: the plain
+ * SVD compensation described on the page "Boost 2-bit LLM accuracy with EoRA" (section
+ * on finding adapters in the eigenspace): with Delta W = W - Q^-1(W_q) = U Sigma V^T, the
+ * LoRA factors B = U_r Sigma_r and A = V_r^T, so W_hat + B A corrects the quantized
+ * weight.  Reading: the truncated SVD is computed by randomized subspace iteration with
+ * a caller-supplied Gaussian test matrix Omega (width l = rank + oversample columns):
+ * Y = Delta W Omega; power_iters times Y <- Delta W orth(Delta W^T orth(Y)); Q = orth(Y);
+ * the SVD of Q^T Delta W gives U = Q U~, Sigma, V.  The accuracy against the exact SVD is
+ * set by oversample and power_iters (the quantization error has a flat spectrum, so the
+ * exact rank-r subspace is itself nearly degenerate).  Delta W is used in binary16 (as
+ * hqq_residual computes it), products accumulate in fp32 on the matrix cores, the small
+ * l x l eigenproblems are solved in fp64.
+ *
+ * W_f16, packed_codes, scale_f16, zero_f16, rows, cols, nbits, group_size  as for
+ *              hqq_residual; rows, cols > 0.
+ * rank         r >= 1; rank + oversample (>= 0) a multiple of 32, at most 512 and at most
+ *              min(rows, cols).
+ * power_iters  0 .. 16.
+ * omega_f16    (rank + oversample) x cols binary16 test matrix (row-major, 16-byte aligned),
+ *              e.g. standard normal samples; the caller's random numbers.
+ * B_f32        rows x rank fp32 (row-major): U_r Sigma_r.
+ * A_f32        rank x cols fp32 (row-major): V_r^T (orthonormal rows).
+ * sigma_f32    rank fp32: the singular values, in decreasing order.  Each singular pair is
+ *              determined up to a common sign of its column of B and row of A.
+ * workspace    hqq_lowrank_workspace_bytes(rows, cols, rank, oversample) bytes of device
+ *              memory, 256-byte aligned, owned by the caller, not shared by calls that may
+ *              run at the same time (it holds Delta W in both layouts and the iterates).
+ * All outputs are alignment 4.  Work is enqueued on `stream` (no allocation, no
+ * synchronization); conventions and errors as for hqq_quantize.
+ */
+int hqq_lowrank(const void* W_f16, const void* packed_codes, const void* scale_f16,
+                const void* zero_f16, int64_t rows, int64_t cols, int nbits, int group_size,
+                int rank, int oversample, int power_iters, const void* omega_f16, void* B_f32,
+                void* A_f32, void* sigma_f32, void* workspace, void* stream);
+
+/* Bytes of the workspace of hqq_lowrank; -1 for invalid shapes or widths. */
+int64_t hqq_lowrank_workspace_bytes(int64_t rows, int64_t cols, int rank, int oversample);
+
 /* Bytes of the packed code stream: rows*cols*nbits/8 (exact for supported
  * shapes).  Returns -1 for invalid arguments or overflow. */
 int64_t hqq_packed_bytes(int64_t rows, int64_t cols, int nbits);

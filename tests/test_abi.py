@@ -159,6 +159,56 @@ def test_matmul_empty_is_a_no_op(lib):
     assert _mm(N=0, X_f16=0, packed_codes=0, scale_f16=0, zero_f16=0, Y=0) == hq.HQQ_OK
 
 
+def _lr(**kw):
+    a = dict(W_f16=FAKE, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, rows=128, cols=256,
+             nbits=4, group_size=64, rank=32, oversample=32, power_iters=2, omega_f16=FAKE,
+             B_f32=FAKE, A_f32=FAKE, sigma_f32=FAKE, workspace=FAKE, stream=0)
+    a.update(kw)
+    return hq.hqq_lowrank(**a)
+
+
+def test_lowrank_workspace_bytes(lib):
+    assert hq.hqq_lowrank_workspace_bytes(128, 256, 32, 32) > 2 * 128 * 256 * 2
+    assert hq.hqq_lowrank_workspace_bytes(100, 256, 32, 32) == -1   # rows not a multiple of 64
+    assert hq.hqq_lowrank_workspace_bytes(128, 256, 32, 16) == -1   # width not a multiple of 32
+    assert hq.hqq_lowrank_workspace_bytes(128, 256, 200, 0) == -1   # width > rows
+    assert hq.hqq_lowrank_workspace_bytes(1024, 1024, 512, 32) == -1  # width > 512
+    assert hq.hqq_lowrank_workspace_bytes(1024, 1024, 500, 12) > 0    # width 512
+    assert hq.hqq_lowrank_workspace_bytes(128, 256, 0, 32) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=100), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(cols=96, group_size=32), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(nbits=5), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(rank=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(oversample=16), hq.HQQ_ERR_INVALID_ARG),
+    (dict(power_iters=17), hq.HQQ_ERR_INVALID_ARG),
+    (dict(rows=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(omega_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(workspace=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(workspace=FAKE + 128), hq.HQQ_ERR_ALIGNMENT),
+    (dict(omega_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+    (dict(B_f32=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_lowrank_rejects_before_launch(lib, kw, status):
+    assert _lr(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=100), hq.HQQ_ERR_UNSUPPORTED),
+    (dict(dW_f16=0), hq.HQQ_ERR_INVALID_ARG),
+    (dict(dW_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+    (dict(dWT_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
+])
+def test_residual_rejects_before_launch(lib, kw, status):
+    a = dict(W_f16=FAKE, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, rows=128, cols=256,
+             nbits=4, group_size=64, dW_f16=FAKE, dWT_f16=0, stream=0)
+    a.update(kw)
+    assert hq.hqq_residual(**a) == status
+    assert hq.hqq_residual(0, 0, 0, 0, 0, 128, 4, 64, 0, 0, 0) == hq.HQQ_OK  # no rows: no-op
+
+
 def _ts(opt=None, **kw):
     a = dict(W_f16=FAKE, rows=16, cols=128, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01,
              iters=20, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, options=opt,
