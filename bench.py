@@ -433,6 +433,69 @@ def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
     return out
 
 
+def measure_lowrank(hq, lib, torch, Ws, settings, solver, stream, sh, dev, rank=64,
+                    oversample=32, power_iters=4):
+    """Low-rank compensation of the quantization error (hqq_lowrank: residual, randomized
+    truncated SVD) on the given matrices, each quantized with every setting; one call per
+    matrix between HIP events (milliseconds each, so launch gaps do not matter).
+    Algorithmic HBM bytes per call: the residual (read W, codes, s, z; write Delta W in two
+    layouts: 2 + b/8 + 4/g + 4 bytes per weight) and 2 q + 2 passes of the matrix-core
+    products over the binary16 Delta W (2 bytes per weight each).  Quality: the relative
+    Frobenius error of W_hat and of W_hat + B A against W."""
+    out = {"entry_point": "hqq_lowrank", "rank": rank, "oversample": oversample,
+           "power_iters": power_iters, "matrices": [list(W.shape) for W in Ws], "per_setting": []}
+    wmax = max(hq.hqq_lowrank_workspace_bytes(W.shape[0], W.shape[1], rank, oversample)
+               for W in Ws)
+    ws = torch.empty(wmax, dtype=torch.uint8, device=dev)
+    for nb, g in settings:
+        rows = []
+        tot_ms = tot_bytes = 0.0
+        err0 = err1 = wn = 0.0
+        for W in Ws:
+            q = hq.quantize(W, nb, g, p=solver.p, beta=solver.beta, kappa=solver.kappa,
+                            iters=solver.iters)
+            m, n = W.shape
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(1)
+            omega = torch.randn((rank + oversample, n), generator=gen, device=dev).half()
+            B = torch.empty((m, rank), dtype=torch.float32, device=dev)
+            A = torch.empty((rank, n), dtype=torch.float32, device=dev)
+            S = torch.empty(rank, dtype=torch.float32, device=dev)
+            args = (W.data_ptr(), q.packed.data_ptr(), q.scale.data_ptr(), q.zero.data_ptr(), m, n,
+                    nb, g, rank, oversample, power_iters, omega.data_ptr(), B.data_ptr(),
+                    A.data_ptr(), S.data_ptr(), ws.data_ptr(), sh)
+            assert lib.hqq_lowrank(*args) == 0
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(2):
+                assert lib.hqq_lowrank(*args) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 2
+            nbytes = W.numel() * (2 + nb / 8 + 4 / g + 4) + (2 * power_iters + 2) * 2 * W.numel()
+            tot_ms += ms
+            tot_bytes += nbytes
+            dW = hq.residual(W, q).float()
+            Wf = W.float()
+            wn += float((Wf.double() ** 2).sum())
+            err0 += float((dW.double() ** 2).sum())
+            err1 += float(((dW - B @ A).double() ** 2).sum())
+            rows.append({"shape": [m, n], "ms": round(ms, 3),
+                         "hbm_GBs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+            del dW, Wf, q
+        rec = {"setting": f"b{nb}g{g}", "matrices": rows, "total_ms": round(tot_ms, 3),
+               "hbm_GBs_algorithmic": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(tot_bytes / (tot_ms * 1e-3) / PEAK_HBM, 4),
+               "rel_fro_quantized": round((err0 / wn) ** 0.5, 6),
+               "rel_fro_with_lowrank": round((err1 / wn) ** 0.5, 6),
+               "captured_fraction_of_error": round(1 - err1 / err0, 5)}
+        log(f"lowrank b{nb}g{g} {rec}")
+        out["per_setting"].append(rec)
+    return out
+
+
 KERNEL_SUMMARIES = {
     # name: (kernel-name filter, file, title, description)
     "meta": ("meta_", "hqq_meta_llama70b.md",
@@ -447,6 +510,15 @@ KERNEL_SUMMARIES = {
                "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
                "(bench.py measure_matmul); hqq_gemv_kernel<b, M rows> for M <= 8, "
                "hqq_gemm_kernel<b> above."),
+    "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
+                "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
+                "hqq_lowrank (residual_kernel, gemm16_kernel split-K products over the binary16 "
+                "Delta W, split_sum_kernel, gram_kernel + gram_sum_kernel, chol_inverse_kernel "
+                "in the power steps, jacobi_kernel for the final orthonormalization and SVD, "
+                "transform/apply kernels), "
+                "oversample 32, 4 power steps, b2 g32 and b4 g64 weights from hqq_quantize, "
+                "1 warm-up + 2 timed calls per matrix, plus the quantization and the quality "
+                "check (bench.py measure_lowrank)."),
     "variants": ("hqq", "hqq_solver_variants_llama70b_layer0.md",
                  "Solver variants on the 7 matrices of Llama-2-70B layer 0",
                  "One call per matrix and variant (per-group stop on the lp / l1 / l2 error: "
@@ -492,6 +564,10 @@ def main():
                     help="one hqq_quantize launch per matrix instead of one batched launch "
                          "per setting")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lowrank", action="store_true",
+                    help="skip the low-rank compensation measurement on the first layer")
+    ap.add_argument("--lowrank-only", action="store_true",
+                    help="only measure the low-rank compensation (JSON on stderr)")
     ap.add_argument("--no-matmul", action="store_true",
                     help="skip the quantized-weight product measurement on the first layer")
     ap.add_argument("--matmul-only", action="store_true",
@@ -626,6 +702,11 @@ def main():
         if events is not None:
             events[cur][1].record(stream)
 
+    if args.lowrank_only:
+        log(json.dumps(measure_lowrank(hq, lib, torch, Ws[:7], settings, solver, stream, sh,
+                                       dev)))
+        return
+
     if args.matmul_only:
         log(json.dumps(measure_matmul(hq, lib, torch, Ws[:7], settings, solver, stream, sh,
                                       dev)))
@@ -739,6 +820,11 @@ def main():
     if not args.no_matmul:
         matmul = measure_matmul(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
 
+    # ---- next row: low-rank compensation of the quantization error, first layer --------
+    lowrank = None
+    if not args.no_lowrank:
+        lowrank = measure_lowrank(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
+
     # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -812,7 +898,7 @@ def main():
         "per_setting": detail,
         "cpu_baseline": cpu,
         "next_rows": {"meta_quantization": meta, "solver_variants": variants,
-                      "quantized_matmul": matmul},
+                      "quantized_matmul": matmul, "lowrank_compensation": lowrank},
     }
     print(json.dumps(out), flush=True)
 

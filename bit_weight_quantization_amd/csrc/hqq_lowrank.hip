@@ -6,12 +6,14 @@
 //
 // The truncated SVD is computed by randomized subspace iteration: Y = Delta W Omega for
 // a caller-supplied Gaussian test matrix Omega (n x l, l = r + oversampling), q power
-// steps Y <- Delta W orth(Delta W^T orth(Y)), Q = orth(Y), then the SVD of the small
+// steps Y <- Delta W basis(Delta W^T basis(Y)), Q = orth(Y), then the SVD of the small
 // B_m = Q^T Delta W through the eigendecomposition of B_m B_m^T.  The heavy work is the
 // products with Delta W, which is materialized once as binary16 in both layouts so every
-// product is a plain matrix-core GEMM with fp32 accumulation; orthonormalization is by
-// the eigendecomposition of the l x l Gram matrix (Q = Y V Lambda^-1/2), computed by
-// cyclic Jacobi in fp64 in one block.
+// product is a plain matrix-core GEMM with fp32 accumulation.  Bases come from Cholesky
+// QR of the l x l Gram matrix in fp64 (Q = Y R^-1, with nearly dependent columns
+// dropped): one pass inside the power steps, where only the spanned subspace matters,
+// two for the final orthonormal Q.  The SVD of B_m comes from the eigendecomposition of
+// B_m B_m^T by cyclic Jacobi in fp64 in one block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -223,25 +225,27 @@ __global__ __launch_bounds__(kBlock) void split_sum_kernel(const float* __restri
 
 // ------------------------------------------------------------------- Gram --
 
-// G[a][b] = sum over rows i of X[i][a] X[i][b] for X (M x L fp32): block (a0, b0) of
-// 32 x 32 entries; 64-row chunks of the two column slabs through LDS, fp32 sums per chunk
-// added in fp64.  Thread t: entry a0 + t % 32, b0 + 4 (t / 32) .. + 4.
+// Partial Gram matrices: Gp[z][a][b] = sum over the rows i of split z (rows z * rs ..
+// + rs) of X[i][a] X[i][b] for X (M x L fp32): block (a0, b0, z) of 32 x 32 entries;
+// 64-row chunks of the two column slabs through LDS, fp32 sums per chunk added in fp64.
+// Thread t: entry a0 + t % 32, b0 + 4 (t / 32) .. + 4.
 __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ X, int64_t M, int L,
-                                                      double* __restrict__ G) {
+                                                      int64_t rs, double* __restrict__ Gp) {
   __shared__ float xa[64][33], xb[64][33];
   const int t = threadIdx.x;
   const int a0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
+  const int64_t r0 = (int64_t)blockIdx.z * rs;
+  const int64_t r1 = r0 + rs < M ? r0 + rs : M;
   const int ta = t & 31, tb = (t >> 5) * 4;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int64_t i0 = 0; i0 < M; i0 += 64) {
-    // 64 rows x 32 columns of each slab: 2048 values each, 8 per thread
+  for (int64_t i0 = r0; i0 < r1; i0 += 64) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 8; ++u) {  // 64 rows x 32 columns of each slab, 8 values per thread
       const int idx = t + u * kBlock;
       const int r = idx >> 5, c = idx & 31;
       const int64_t i = i0 + r;
-      xa[r][c] = i < M ? X[i * L + a0 + c] : 0.f;
-      xb[r][c] = i < M ? X[i * L + b0 + c] : 0.f;
+      xa[r][c] = i < r1 ? X[i * L + a0 + c] : 0.f;
+      xb[r][c] = i < r1 ? X[i * L + b0 + c] : 0.f;
     }
     __syncthreads();
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -255,113 +259,217 @@ __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ 
     for (int j = 0; j < 4; ++j) acc[j] += (double)part[j];
     __syncthreads();
   }
+  double* G = Gp + (int64_t)blockIdx.z * L * L;
 #pragma unroll
   for (int j = 0; j < 4; ++j) G[(int64_t)(a0 + ta) * L + b0 + tb + j] = acc[j];
+}
+
+// G[e] = sum over splits z (in order) of Gp[z][e].
+__global__ __launch_bounds__(kBlock) void gram_sum_kernel(const double* __restrict__ Gp, int splits,
+                                                          int64_t count, double* __restrict__ G) {
+  for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * kBlock) {
+    double v = Gp[e];
+    for (int z = 1; z < splits; ++z) v += Gp[(int64_t)z * count + e];
+    G[e] = v;
+  }
 }
 
 // ------------------------------------------------------- symmetric eigen --
 
 constexpr int kEigThreads = 1024;
+constexpr int kEigWaves = kEigThreads / kWave;
 constexpr int kMaxWidth = 512;
+constexpr int kLdsWidth = 96;  // widths up to this keep their two fp64 matrices in LDS
 
-// Cyclic Jacobi on the symmetric L x L matrix S (fp64, overwritten; L even): round-robin
-// ordering, L / 2 disjoint rotations per round (all computed first, then applied to the
-// rows, then to the columns and to V), rounds of L - 1 per sweep until the off-diagonal
-// norm is below 1e-15 of the diagonal's (at most 30 sweeps).  On exit: V (L x L) holds
-// the eigenvectors in its columns, evals the eigenvalues, order their indices by
-// decreasing eigenvalue.  One block.
-__global__ __launch_bounds__(kEigThreads) void jacobi_kernel(double* __restrict__ S, int L,
-                                                             double* __restrict__ V,
+// Pair j of round `round` of the round-robin ordering of L indices: positions j and
+// L - 1 - j, position 0 holding index 0 and the others rotating; p < q.
+__device__ __forceinline__ void rr_pair(int j, int round, int L, int& p, int& q) {
+  const int ia = j == 0 ? 0 : 1 + (j - 1 + round) % (L - 1);
+  const int ib = 1 + (L - 2 - j + round) % (L - 1);
+  p = ia < ib ? ia : ib;
+  q = ia < ib ? ib : ia;
+}
+
+// Cyclic Jacobi on the symmetric L x L matrix S (fp64; L even): round-robin ordering,
+// L / 2 disjoint rotations per round, rounds of L - 1 per sweep, until the off-diagonal
+// squared norm is below 1e-28 of the diagonal's or a sweep applied no rotation (at most
+// 30 sweeps); a rotation is skipped when |s_pq| <= 1e-17 sqrt(|s_pp s_qq|).  Wave w owns
+// the pairs j = w, w + 16, ...: lane l computes the rotation of its l-th pair, the wave
+// applies it to rows p and q of S (which only this wave writes in the round, so the
+// rotation's inputs are read before any change), then, after a barrier, to columns p and
+// q of S and of V; lanes run along the rows or columns.  LOCAL: S and V are copied to LDS
+// with row stride L + 1 (L <= kLdsWidth; the odd stride keeps the column accesses of a
+// wave on distinct banks), else they are worked on in place in global memory.  On exit:
+// V (L x L) holds the eigenvectors in its columns, evals the eigenvalues, order their
+// indices by decreasing eigenvalue.  One block.
+template <bool LOCAL>
+__global__ __launch_bounds__(kEigThreads) void jacobi_kernel(double* __restrict__ Sg, int L,
+                                                             double* __restrict__ Vg,
                                                              double* __restrict__ evals,
                                                              int* __restrict__ order) {
-  __shared__ int pp[kMaxWidth / 2], qq[kMaxWidth / 2];
-  __shared__ double cc[kMaxWidth / 2], ss[kMaxWidth / 2];
-  __shared__ double red[kEigThreads / kWave][2];
+  __shared__ double red[kEigWaves][2];
   __shared__ int done;
-  const int t = threadIdx.x;
+  __shared__ double Sl[LOCAL ? kLdsWidth * (kLdsWidth + 1) : 1],
+      Vl[LOCAL ? kLdsWidth * (kLdsWidth + 1) : 1];
+  double* S = LOCAL ? Sl : Sg;
+  double* V = LOCAL ? Vl : Vg;
+  const int ld = LOCAL ? L + 1 : L;
+  // a batch: PB pairs x NC chunks of 64 lanes along the rows or columns
+  constexpr int NC = LOCAL ? (kLdsWidth + kWave - 1) / kWave : 2;
+  constexpr int PB = LOCAL ? 2 : 1;
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   const int half = L / 2;
-  for (int64_t e = t; e < (int64_t)L * L; e += kEigThreads)
-    V[e] = (e / L == e % L) ? 1.0 : 0.0;
-  __syncthreads();
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    // convergence test: off-diagonal vs diagonal squared norms
-    double off = 0.0, dia = 0.0;
-    for (int64_t e = t; e < (int64_t)L * L; e += kEigThreads) {
-      const double v = S[e];
-      if (e / L == e % L) dia += v * v;
-      else off += v * v;
+  for (int i = wv; i < L; i += kEigWaves)
+    for (int j = lane; j < L; j += kWave) {
+      if (LOCAL) S[i * ld + j] = Sg[i * L + j];
+      V[i * ld + j] = i == j ? 1.0 : 0.0;
     }
+  __syncthreads();
+  int rotated = 1;  // lane's rotations of the last sweep: some was applied
+  for (int sweep = 0; sweep < 30; ++sweep) {
+    if (!__syncthreads_or(rotated)) break;  // a sweep without rotations changes nothing
+    rotated = 0;
+    double off = 0.0, dia = 0.0;
+    for (int i = wv; i < L; i += kEigWaves)
+      for (int j = lane; j < L; j += kWave) {
+        const double v = S[i * ld + j];
+        if (i == j) dia += v * v;
+        else off += v * v;
+      }
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) {
       off += __shfl_xor(off, o, kWave);
       dia += __shfl_xor(dia, o, kWave);
     }
-    if ((t & (kWave - 1)) == 0) {
-      red[t / kWave][0] = off;
-      red[t / kWave][1] = dia;
+    if (lane == 0) {
+      red[wv][0] = off;
+      red[wv][1] = dia;
     }
     __syncthreads();
     if (t == 0) {
       double o2 = 0.0, d2 = 0.0;
-      for (int w = 0; w < kEigThreads / kWave; ++w) {
+      for (int w = 0; w < kEigWaves; ++w) {
         o2 += red[w][0];
         d2 += red[w][1];
       }
-      done = (o2 <= 1e-30 * d2) ? 1 : 0;
+      done = (o2 <= 1e-28 * d2) ? 1 : 0;
     }
     __syncthreads();
     if (done) break;
     for (int round = 0; round < L - 1; ++round) {
-      if (t < half) {
-        // pair t: positions t and L - 1 - t; position 0 holds index 0, the others rotate
-        const int pa = t, pb = L - 1 - t;
-        const int ia = pa == 0 ? 0 : 1 + (pa - 1 + round) % (L - 1);
-        const int ib = 1 + (pb - 1 + round) % (L - 1);
-        const int p = ia < ib ? ia : ib, q = ia < ib ? ib : ia;
-        const double apq = S[(int64_t)p * L + q];
-        const double app = S[(int64_t)p * L + p], aqq = S[(int64_t)q * L + q];
-        double c = 1.0, s = 0.0;
-        if (apq != 0.0 && __builtin_fabs(apq) > 1e-300) {
-          const double tau = (aqq - app) / (2.0 * apq);
-          const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (__builtin_fabs(tau) + __builtin_sqrt(1.0 + tau * tau));
-          c = 1.0 / __builtin_sqrt(1.0 + tt * tt);
-          s = tt * c;
+      // lane l: rotation of pair wv + 16 l
+      double cl = 1.0, sl = 0.0;
+      {
+        const int j = wv + kEigWaves * lane;
+        if (j < half) {
+          int p, q;
+          rr_pair(j, round, L, p, q);
+          const double apq = S[p * ld + q], app = S[p * ld + p], aqq = S[q * ld + q];
+          if (__builtin_fabs(apq) > 1e-17 * __builtin_sqrt(__builtin_fabs(app * aqq)) &&
+              __builtin_fabs(apq) > 1e-300) {
+            const double tau = (aqq - app) / (2.0 * apq);
+            const double tt = (tau >= 0.0 ? 1.0 : -1.0) /
+                              (__builtin_fabs(tau) + __builtin_sqrt(1.0 + tau * tau));
+            cl = 1.0 / __builtin_sqrt(1.0 + tt * tt);
+            sl = tt * cl;
+            rotated = 1;
+          }
         }
-        pp[t] = p;
-        qq[t] = q;
-        cc[t] = c;
-        ss[t] = s;
+      }
+      // rows: S <- J^T S, then columns: S J and V J; the wave's pairs in batches of PB,
+      // all loads of a batch issued before its stores
+      for (int j0 = 0; wv + kEigWaves * j0 < half; j0 += PB) {
+        int pp[PB], qq[PB];
+        double cc[PB], ss[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int j = wv + kEigWaves * (j0 + u);
+          ss[u] = __shfl(sl, (j0 + u) & (kWave - 1), kWave);
+          cc[u] = __shfl(cl, (j0 + u) & (kWave - 1), kWave);
+          if (j < half) rr_pair(j, round, L, pp[u], qq[u]);
+          else {
+            pp[u] = qq[u] = 0;
+            ss[u] = 0.0;
+          }
+        }
+        for (int c0 = 0; c0 < L; c0 += NC * kWave) {
+          double ra[PB][NC], rb[PB][NC];
+#pragma unroll
+          for (int u = 0; u < PB; ++u)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int col = c0 + lane + kWave * c;
+              if (ss[u] != 0.0 && col < L) {
+                ra[u][c] = S[pp[u] * ld + col];
+                rb[u][c] = S[qq[u] * ld + col];
+              }
+            }
+#pragma unroll
+          for (int u = 0; u < PB; ++u)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int col = c0 + lane + kWave * c;
+              if (ss[u] != 0.0 && col < L) {
+                S[pp[u] * ld + col] = cc[u] * ra[u][c] - ss[u] * rb[u][c];
+                S[qq[u] * ld + col] = ss[u] * ra[u][c] + cc[u] * rb[u][c];
+              }
+            }
+        }
       }
       __syncthreads();
-      // rows p, q of S: S <- J^T S
-      for (int64_t w = t; w < (int64_t)half * L; w += kEigThreads) {
-        const int j = (int)(w / L), col = (int)(w % L);
-        const int p = pp[j], q = qq[j];
-        const double c = cc[j], s = ss[j];
-        const double a = S[(int64_t)p * L + col], b = S[(int64_t)q * L + col];
-        S[(int64_t)p * L + col] = c * a - s * b;
-        S[(int64_t)q * L + col] = s * a + c * b;
-      }
-      __syncthreads();
-      // columns p, q of S and of V: S <- S J, V <- V J
-      for (int64_t w = t; w < (int64_t)half * L; w += kEigThreads) {
-        const int j = (int)(w / L), row = (int)(w % L);
-        const int p = pp[j], q = qq[j];
-        const double c = cc[j], s = ss[j];
-        const double a = S[(int64_t)row * L + p], b = S[(int64_t)row * L + q];
-        S[(int64_t)row * L + p] = c * a - s * b;
-        S[(int64_t)row * L + q] = s * a + c * b;
-        const double va = V[(int64_t)row * L + p], vb = V[(int64_t)row * L + q];
-        V[(int64_t)row * L + p] = c * va - s * vb;
-        V[(int64_t)row * L + q] = s * va + c * vb;
+      for (int j0 = 0; wv + kEigWaves * j0 < half; j0 += PB) {
+        int pp[PB], qq[PB];
+        double cc[PB], ss[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int j = wv + kEigWaves * (j0 + u);
+          ss[u] = __shfl(sl, (j0 + u) & (kWave - 1), kWave);
+          cc[u] = __shfl(cl, (j0 + u) & (kWave - 1), kWave);
+          if (j < half) rr_pair(j, round, L, pp[u], qq[u]);
+          else {
+            pp[u] = qq[u] = 0;
+            ss[u] = 0.0;
+          }
+        }
+        for (int c0 = 0; c0 < L; c0 += NC * kWave) {
+          double sa[PB][NC], sb[PB][NC], va[PB][NC], vb[PB][NC];
+#pragma unroll
+          for (int u = 0; u < PB; ++u)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int row = c0 + lane + kWave * c;
+              if (ss[u] != 0.0 && row < L) {
+                sa[u][c] = S[row * ld + pp[u]];
+                sb[u][c] = S[row * ld + qq[u]];
+                va[u][c] = V[row * ld + pp[u]];
+                vb[u][c] = V[row * ld + qq[u]];
+              }
+            }
+#pragma unroll
+          for (int u = 0; u < PB; ++u)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int row = c0 + lane + kWave * c;
+              if (ss[u] != 0.0 && row < L) {
+                S[row * ld + pp[u]] = cc[u] * sa[u][c] - ss[u] * sb[u][c];
+                S[row * ld + qq[u]] = ss[u] * sa[u][c] + cc[u] * sb[u][c];
+                V[row * ld + pp[u]] = cc[u] * va[u][c] - ss[u] * vb[u][c];
+                V[row * ld + qq[u]] = ss[u] * va[u][c] + cc[u] * vb[u][c];
+              }
+            }
+        }
       }
       __syncthreads();
     }
   }
-  // eigenvalues and their order (rank by decreasing value, ties by index)
-  for (int i = t; i < L; i += kEigThreads) evals[i] = S[(int64_t)i * L + i];
+  for (int i = t; i < L; i += kEigThreads) evals[i] = S[i * ld + i];
+  if (LOCAL) {
+    for (int i = wv; i < L; i += kEigWaves)
+      for (int j = lane; j < L; j += kWave) Vg[i * L + j] = V[i * ld + j];
+  }
   __syncthreads();
-  for (int i = t; i < L; i += kEigThreads) {
+  for (int i = t; i < L; i += kEigThreads) {  // rank by decreasing value, ties by index
     const double v = evals[i];
     int rank = 0;
     for (int j = 0; j < L; ++j) {
@@ -372,10 +480,123 @@ __global__ __launch_bounds__(kEigThreads) void jacobi_kernel(double* __restrict_
   }
 }
 
+constexpr int kCholThreads = 1024;
+constexpr int kCholWaves = kCholThreads / kWave;
+
+// Cholesky QR with dropped pivots: G = U^T D U (U unit upper triangular, D diagonal) by
+// right-looking elimination in the upper triangle, a pivot d_k <= 2^-16 g_kk (the column's
+// squared distance from the span of the earlier ones below 2^-16 of its squared norm, or
+// no larger than the error of the Gram matrix's fp32 sums, whose entries are within
+// 2^-18 sqrt(g_aa g_bb)) drops column k; T = U^-1 D^-1/2 (L x L fp32, upper triangular)
+// with zero row and column for dropped indices, so that the columns of Y T are the
+// Gram-Schmidt vectors of Y's columns: orthonormal up to the Gram matrix's error relative
+// to the pivots, zero where dropped.  Applied twice (the second time to Y T), the basis
+// is orthonormal to about 2^-18.  Waves run over rows, lanes along them, the fixed row
+// of a step in registers and the loads of PB rows issued before their stores; one
+// barrier per step.  LOCAL: the factor and the inverse live in LDS (L <= kLdsWidth), else in place in
+// the global buffers Ag (the Gram matrix, overwritten) and Xg (scratch, L x L).  One block.
+template <bool LOCAL>
+__global__ __launch_bounds__(kCholThreads) void chol_inverse_kernel(double* __restrict__ Ag,
+                                                                    double* __restrict__ Xg, int L,
+                                                                    float* __restrict__ T) {
+  __shared__ double Al[LOCAL ? kLdsWidth * kLdsWidth : 1], Xl[LOCAL ? kLdsWidth * kLdsWidth : 1];
+  __shared__ double piv[kMaxWidth];  // 1 / d_k, 0 for a dropped column
+  double* A = LOCAL ? Al : Ag;
+  double* X = LOCAL ? Xl : Xg;
+  constexpr int NC = ((LOCAL ? kLdsWidth : kMaxWidth) + kWave - 1) / kWave;  // 64-lane chunks
+  constexpr int PB = LOCAL ? 4 : 2;  // rows whose LDS accesses are batched
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  for (int k = t; k < L; k += kCholThreads) piv[k] = Ag[k * L + k];  // g_kk, kept until step k
+  for (int i = wv; i < L; i += kCholWaves)
+    for (int j = lane; j < L; j += kWave) {
+      if (LOCAL) A[i * L + j] = Ag[i * L + j];
+      X[i * L + j] = i == j ? 1.0 : 0.0;
+    }
+  __syncthreads();
+  // step k: a_ij -= a_ki a_kj / d_k for k < i, k < j (a_k. is row k of D U, unscaled; the
+  // entries below the diagonal are updated too and never read)
+  for (int k = 0; k < L - 1; ++k) {
+    const double d = A[k * L + k];
+    const double inv = d > 0x1p-16 * piv[k] ? 1.0 / d : 0.0;
+    if (inv != 0.0) {
+      double rk[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int j = lane + kWave * c;
+        rk[c] = (j > k && j < L) ? A[k * L + j] * inv : 0.0;
+      }
+      for (int i0 = k + 1 + wv; i0 < L; i0 += PB * kCholWaves) {
+        double f[PB], a[PB][NC];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int i = i0 + u * kCholWaves;
+          f[u] = i < L ? A[k * L + i] : 0.0;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int j = lane + kWave * c;
+            if (i < L && j > k && j < L) a[u][c] = A[i * L + j];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+          const int i = i0 + u * kCholWaves;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int j = lane + kWave * c;
+            if (i < L && j > k && j < L) A[i * L + j] = a[u][c] - f[u] * rk[c];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int k = t; k < L; k += kCholThreads) {
+    const double d = A[k * L + k];
+    piv[k] = d > 0x1p-16 * piv[k] ? 1.0 / d : 0.0;
+  }
+  __syncthreads();
+  // X = U^-1 by back substitution on U X = I (u_ik = a_ik / d_i), one row finished per step
+  for (int k = L - 1; k > 0; --k) {
+    double xk[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int j = lane + kWave * c;
+      xk[c] = (j >= k && j < L) ? X[k * L + j] : 0.0;
+    }
+    for (int i0 = wv; i0 < k; i0 += PB * kCholWaves) {  // columns k .. L - 1 of rows < k
+      double uu[PB], x[PB][NC];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int i = i0 + u * kCholWaves;
+        uu[u] = i < k ? A[i * L + k] * piv[i] : 0.0;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j = lane + kWave * c;
+          if (i < k && j >= k && j < L) x[u][c] = X[i * L + j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int i = i0 + u * kCholWaves;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j = lane + kWave * c;
+          if (i < k && j >= k && j < L) X[i * L + j] = x[u][c] - uu[u] * xk[c];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // T = X D^-1/2, column j scaled by 1 / sqrt(d_j), zero for dropped rows and columns
+  for (int i = wv; i < L; i += kCholWaves)
+    for (int j = lane; j < L; j += kWave)
+      T[i * L + j] = (piv[i] != 0.0 && piv[j] != 0.0) ? (float)(X[i * L + j] * __builtin_sqrt(piv[j]))
+                                                      : 0.f;
+}
+
 // T[b][c] = V[b][order[c]] * f(order[c]) for c < C (L x C fp32), where f is
-// mode 0: 1/sqrt(lambda) (0 for lambda <= 1e-12 lambda_max: orthonormalization);
-// mode 1: sqrt(lambda) (sigma); mode 2: 1/sqrt(lambda) as mode 0.  sigma (may be null):
-// sqrt(lambda) of the first C eigenvalues in decreasing order.
+// mode 1: sqrt(lambda) (sigma); mode 2: 1/sqrt(lambda), 0 for lambda <= 1e-12 lambda_max.
+// sigma (may be null): sqrt(lambda) of the first C eigenvalues in decreasing order.
 __global__ __launch_bounds__(kBlock) void transform_kernel(const double* __restrict__ V,
                                                            const double* __restrict__ evals,
                                                            const int* __restrict__ order, int L,
@@ -450,6 +671,17 @@ struct Carve {
 };
 
 constexpr int64_t kPartialBudget = 64ll << 20;  // bytes of split-K partials at most
+constexpr int64_t kGramBudget = 16ll << 20;     // bytes of partial Gram matrices at most
+
+// Row splits of a Gram computation over M rows: enough blocks to fill the chip.
+int gram_splits(int64_t M, int L) {
+  const int64_t tiles = (int64_t)(L / 32) * (L / 32);
+  int64_t s = (256 + tiles - 1) / tiles;
+  if (s > (M + 63) / 64) s = (M + 63) / 64;
+  const int64_t cap = kGramBudget / ((int64_t)L * L * 8);
+  if (s > cap) s = cap;
+  return s < 1 ? 1 : (int)s;
+}
 
 int gemm_splits(int64_t M, int64_t K, int L) {
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((L + kBN - 1) / kBN);
@@ -468,8 +700,9 @@ int64_t lowrank_workspace_bytes(int64_t m, int64_t n, int width) {
   auto al = [](int64_t b) { return (b + 255) & ~(int64_t)255; };
   const int64_t sm = gemm_splits(m, n, width), sn = gemm_splits(n, m, width);
   const int64_t part = (sm * m > sn * n ? sm * m : sn * n) * L * 4;
-  return al(m * n * 2) * 2 + al(mx * L * 4) + al(part) + al(L * mx * 2) + al(m * L * 4) +
-         al(L * L * 8) * 2 + al(L * 8) + al(L * 4) + al(L * L * 4);
+  return al(m * n * 2) * 2 + al(mx * L * 4) + al(part) + al(L * mx * 2) + al(mx * L * 4) +
+         al(L * L * 8) * 2 + al(L * 8) + al(L * 4) + al(L * L * 4) +
+         al((int64_t)gram_splits(mx, width) * L * L * 8);  // gram_splits grows with M
 }
 
 hipError_t launch_residual(const uint16_t* W, const uint8_t* packed, const uint16_t* scale16,
@@ -497,17 +730,18 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   const int64_t sm = gemm_splits(m, n, L), sn = gemm_splits(n, m, L);
   float* part = cv.take<float>((sm * m > sn * n ? sm * m : sn * n) * L);
   uint16_t* Q16 = cv.take<uint16_t>((int64_t)L * mx);
-  float* Q32 = cv.take<float>(m * L);
+  float* Q32 = cv.take<float>(mx * L);
   double* G = cv.take<double>((int64_t)L * L);
   double* V = cv.take<double>((int64_t)L * L);
   double* ev = cv.take<double>(L);
   int* ord = cv.take<int>(L);
   float* T = cv.take<float>((int64_t)L * L);
+  double* Gp = cv.take<double>((int64_t)gram_splits(mx, L) * L * L);
   hipError_t err;
   const int64_t grid_cap = (int64_t)cus * 8;
 
-  // Y (M x L) = A (M x K) B^T for B (L x K)
-  auto gemm = [&](const uint16_t* A, int64_t M, int64_t K, const uint16_t* B) -> hipError_t {
+  // Out (M x L fp32) = A (M x K) B^T for B (L x K)
+  auto gemm = [&](const uint16_t* A, int64_t M, int64_t K, const uint16_t* B, float* out) -> hipError_t {
     const int s = gemm_splits(M, K, L);
     const int64_t steps = K / kBK;
     const int64_t kslice = ((steps + s - 1) / s) * kBK;
@@ -518,55 +752,69 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
     const int64_t count = M * L;
     int64_t blocks = (count + kBlock - 1) / kBlock;
     if (blocks > grid_cap) blocks = grid_cap;
-    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, part, s, count, Y);
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, part, s, count, out);
     return hipGetLastError();
   };
-  // eigendecomposition of the Gram matrix of Y (M x L)
-  auto eig_of_gram = [&](int64_t M) -> hipError_t {
-    hipLaunchKernelGGL(gram_kernel, dim3(L / 32, L / 32), dim3(kBlock), 0, st, Y, M, L, G);
+  // G (L x L fp64) = X^T X for X (M x L fp32)
+  auto gram = [&](const float* X, int64_t M) -> hipError_t {
+    const int gs = gram_splits(M, L);
+    const int64_t rs = (((M + gs - 1) / gs + 63) / 64) * 64;
+    hipLaunchKernelGGL(gram_kernel, dim3(L / 32, L / 32, gs), dim3(kBlock), 0, st, X, M, L, rs, Gp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+    const int64_t count = (int64_t)L * L;
+    hipLaunchKernelGGL(gram_sum_kernel, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, st, Gp, gs, count, G);
     return hipGetLastError();
   };
-  // Q^T (L x M, binary16) = (Y V Lambda^-1/2)^T, and Q (M x L fp32) if q32
-  auto orth = [&](int64_t M, float* q32) -> hipError_t {
-    hipError_t e = eig_of_gram(M);
+  // out32 (M x L fp32, may be null) and out16 (L x M binary16, transposed, may be null) =
+  // X T with T from the Cholesky QR of X (M x L fp32): the Gram-Schmidt basis of X
+  auto cholqr = [&](const float* X, int64_t M, float* out32, uint16_t* out16) -> hipError_t {
+    hipError_t e = gram(X, M);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * L + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       st, V, ev, ord, L, L, 0, T, (float*)nullptr);
+    if (L <= kLdsWidth)
+      hipLaunchKernelGGL(chol_inverse_kernel<true>, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
+    else
+      hipLaunchKernelGGL(chol_inverse_kernel<false>, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock), 0,
-                       st, Y, M, L, T, L, q32, (float*)nullptr, Q16);
+                       st, X, M, L, T, L, out32, (float*)nullptr, out16);
     return hipGetLastError();
   };
 
   if ((err = launch_residual(P.W, P.packed, P.scale16, P.zero16, m, n, P.nbits, P.group_size, dW,
                              dWT, st)) != hipSuccess)
     return err;
-  if ((err = gemm(dW, m, n, P.omega)) != hipSuccess) return err;  // Y = dW Omega
+  if ((err = gemm(dW, m, n, P.omega, Y)) != hipSuccess) return err;  // Y = dW Omega
   for (int it = 0; it < P.power_iters; ++it) {
-    if ((err = orth(m, nullptr)) != hipSuccess) return err;       // Q16 = orth(Y)^T
-    if ((err = gemm(dWT, n, m, Q16)) != hipSuccess) return err;   // Y = dW^T Q   (n x L)
-    if ((err = orth(n, nullptr)) != hipSuccess) return err;       // Q16 = orth(Y)^T
-    if ((err = gemm(dW, m, n, Q16)) != hipSuccess) return err;    // Y = dW Q     (m x L)
+    if ((err = cholqr(Y, m, nullptr, Q16)) != hipSuccess) return err;  // Q16 = basis(Y)^T
+    if ((err = gemm(dWT, n, m, Q16, Y)) != hipSuccess) return err;     // Y = dW^T Q  (n x L)
+    if ((err = cholqr(Y, n, nullptr, Q16)) != hipSuccess) return err;  // Q16 = basis(Y)^T
+    if ((err = gemm(dW, m, n, Q16, Y)) != hipSuccess) return err;      // Y = dW Q    (m x L)
   }
-  if ((err = orth(m, Q32)) != hipSuccess) return err;             // Q (m x L)
-  if ((err = gemm(dWT, n, m, Q16)) != hipSuccess) return err;     // Y = dW^T Q = B_m^T (n x L)
-  if ((err = eig_of_gram(n)) != hipSuccess) return err;           // B_m B_m^T = U~ Lambda U~^T
+  // Q = orth(Y) by two passes of Cholesky QR: Q1 -> Q32, Q -> Y (fp32) and Q16
+  if ((err = cholqr(Y, m, Q32, nullptr)) != hipSuccess) return err;
+  if ((err = cholqr(Q32, m, Y, Q16)) != hipSuccess) return err;
+  if ((err = gemm(dWT, n, m, Q16, Q32)) != hipSuccess) return err;     // Z = dW^T Q = B_m^T (n x L)
+  if ((err = gram(Q32, n)) != hipSuccess) return err;                  // B_m B_m^T = U~ Lambda U~^T
+  if (L <= kLdsWidth)
+    hipLaunchKernelGGL(jacobi_kernel<true>, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+  else
+    hipLaunchKernelGGL(jacobi_kernel<false>, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int r = P.rank;
-  // B = Q U~_r Sigma_r (m x r);  A = Sigma_r^-1 U~_r^T B_m = (B_m^T U~_r Sigma_r^-1)^T (r x n)
+  // B = Q U~_r Sigma_r (m x r);  A = Sigma_r^-1 U~_r^T B_m = (Z U~_r Sigma_r^-1)^T (r x n)
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 1, T, P.sigma);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((m + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
-                     st, Q32, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
+                     st, Y, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 2, T, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
-                     st, Y, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
+                     st, Q32, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
   return hipGetLastError();
 }
 

@@ -331,12 +331,14 @@ int hqq_residual(const void* W_f16, const void* packed_codes, const void* scale_
  * LoRA factors B = U_r Sigma_r and A = V_r^T, so W_hat + B A corrects the quantized
  * weight.  Reading: the truncated SVD is computed by randomized subspace iteration with
  * a caller-supplied Gaussian test matrix Omega (width l = rank + oversample columns):
- * Y = Delta W Omega; power_iters times Y <- Delta W orth(Delta W^T orth(Y)); Q = orth(Y);
- * the SVD of Q^T Delta W gives U = Q U~, Sigma, V.  The accuracy against the exact SVD is
- * set by oversample and power_iters (the quantization error has a flat spectrum, so the
- * exact rank-r subspace is itself nearly degenerate).  Delta W is used in binary16 (as
- * hqq_residual computes it), products accumulate in fp32 on the matrix cores, the small
- * l x l eigenproblems are solved in fp64.
+ * Y = Delta W Omega; power_iters times Y <- Delta W basis(Delta W^T basis(Y)), where
+ * basis() is a well-conditioned basis of the column space (shifted Cholesky QR); then
+ * Q = orth(Y) with orthonormal columns, and the SVD of Q^T Delta W gives U = Q U~, Sigma,
+ * V.  The accuracy against the exact SVD is set by oversample and power_iters (the
+ * quantization error has a flat spectrum, so the exact rank-r subspace is itself nearly
+ * degenerate).  Delta W is used in binary16 (as hqq_residual computes it), products
+ * accumulate in fp32 on the matrix cores, the small l x l eigenproblems and Cholesky
+ * factorizations are solved in fp64.
  *
  * W_f16, packed_codes, scale_f16, zero_f16, rows, cols, nbits, group_size  as for
  *              hqq_residual; rows, cols > 0.

@@ -96,14 +96,18 @@ def _zero_quantization(rows, cols, nbits, g):
     return packed, s16, z16
 
 
-@pytest.mark.parametrize("rows,cols,rank,over", [(256, 512, 32, 32), (512, 256, 64, 32),
-                                                 (128, 1024, 16, 16)])
-def test_planted_spectrum_matches_the_exact_truncation(hq, rows, cols, rank, over):
+# widths rank + over: 64, 96 (factorizations in LDS), 32, 128 and 512 (in global memory)
+@pytest.mark.parametrize("rows,cols,rank,over,decay", [(256, 512, 32, 32, 0.9),
+                                                       (512, 256, 64, 32, 0.9),
+                                                       (128, 1024, 16, 16, 0.9),
+                                                       (256, 512, 96, 32, 0.99),
+                                                       (640, 768, 448, 64, 0.995)])
+def test_planted_spectrum_matches_the_exact_truncation(hq, rows, cols, rank, over, decay):
     rng = np.random.default_rng(rows * 3 + rank)
     k = rank + 24
     U, _ = np.linalg.qr(rng.standard_normal((rows, k)))
     V, _ = np.linalg.qr(rng.standard_normal((cols, k)))
-    sig = 0.9 ** np.arange(k)
+    sig = decay ** np.arange(k)
     sig[rank:] *= 0.2  # a clear gap after the rank-r part
     W = np.asarray((U * sig) @ V.T + rng.standard_normal((rows, cols)) * 1e-4, np.float16)
     packed, s16, z16 = _zero_quantization(rows, cols, 4, 64)
