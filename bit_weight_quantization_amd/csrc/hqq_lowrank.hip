@@ -277,206 +277,498 @@ __global__ __launch_bounds__(kBlock) void gram_sum_kernel(const double* __restri
 
 // ------------------------------------------------------- symmetric eigen --
 
-constexpr int kEigThreads = 1024;
-constexpr int kEigWaves = kEigThreads / kWave;
 constexpr int kMaxWidth = 512;
 constexpr int kLdsWidth = 96;  // widths up to this keep their two fp64 matrices in LDS
+constexpr int kGrid = 32;                    // 32 x 32 threads own a small matrix
+constexpr int kSmallBlocks = kLdsWidth / kGrid;  // entries per thread and side, at most
+constexpr int kSyevThreads = kGrid * kGrid;
+constexpr int kSyevWaves = kSyevThreads / kWave;
 
-// Pair j of round `round` of the round-robin ordering of L indices: positions j and
-// L - 1 - j, position 0 holding index 0 and the others rotating; p < q.
-__device__ __forceinline__ void rr_pair(int j, int round, int L, int& p, int& q) {
-  const int ia = j == 0 ? 0 : 1 + (j - 1 + round) % (L - 1);
-  const int ib = 1 + (L - 2 - j + round) % (L - 1);
-  p = ia < ib ? ia : ib;
-  q = ia < ib ? ib : ia;
+// Lane permutations of fp64 values by DPP (two 32-bit moves): quad_perm [1,0,3,2] and
+// [2,3,0,1], row_half_mirror, row_mirror.
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Sums over the 16 lanes of each DPP row, the 32 lanes of each half-wave and the 64
+// lanes of the wave (every lane gets the sum, bit-identical): pairs combined by DPP
+// within rows of 16, then across rows.
+__device__ __forceinline__ double sum16_f64(double v) {
+  v += dpp64<0xB1>(v);
+  v += dpp64<0x4E>(v);
+  v += dpp64<0x141>(v);
+  return v + dpp64<0x140>(v);
+}
+__device__ __forceinline__ double sum32_f64(double v) {
+  v = sum16_f64(v);
+  return v + __shfl_xor(v, 16, kWave);
+}
+// Sum over the kGrid lanes sharing a row of the thread grid.
+__device__ __forceinline__ double sumrow_f64(double v) {
+  if constexpr (kGrid == 16) return sum16_f64(v);
+  else return sum32_f64(v);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = sum32_f64(v);
+  return v + __shfl_xor(v, 32, kWave);
+}
+// 1 / q from the hardware estimate and one Newton step.
+__device__ __forceinline__ double recip(double q) {
+  const double r = __builtin_amdgcn_rcp(q);
+  return __builtin_fma(__builtin_fma(-q, r, 1.0), r, r);
 }
 
-// Cyclic Jacobi on the symmetric L x L matrix S (fp64; L even): round-robin ordering,
-// L / 2 disjoint rotations per round, rounds of L - 1 per sweep, until the off-diagonal
-// squared norm is below 1e-28 of the diagonal's or a sweep applied no rotation (at most
-// 30 sweeps); a rotation is skipped when |s_pq| <= 1e-17 sqrt(|s_pp s_qq|).  Wave w owns
-// the pairs j = w, w + 16, ...: lane l computes the rotation of its l-th pair, the wave
-// applies it to rows p and q of S (which only this wave writes in the round, so the
-// rotation's inputs are read before any change), then, after a barrier, to columns p and
-// q of S and of V; lanes run along the rows or columns.  LOCAL: S and V are copied to LDS
-// with row stride L + 1 (L <= kLdsWidth; the odd stride keeps the column accesses of a
-// wave on distinct banks), else they are worked on in place in global memory.  On exit:
-// V (L x L) holds the eigenvectors in its columns, evals the eigenvalues, order their
-// indices by decreasing eigenvalue.  One block.
+// Eigendecomposition of the symmetric L x L matrix S (fp64), one block, in four phases:
+//  1. Householder reduction to tridiagonal form T = H^T S H (H = H_0 ... H_{L-3}): step k
+//     reflects row k right of the diagonal, x, onto alpha e_1 with v = x - alpha e_1,
+//     alpha = -sign(x_0) |x|, tau = 2 / v^T v, and updates the trailing block by
+//     S <- S - v w^T - w v^T, p = tau S v, w = p - (tau / 2)(p^T v) v (Golub and Van Loan,
+//     Matrix Computations, section 8.3.1); row k keeps v (its first entry apart).
+//  2. The nev largest eigenvalues of T by bisection on Sturm counts (the number of
+//     negative pivots of T - x I, each pivot's reciprocal from the hardware estimate and
+//     one Newton step), G-way multisection per eigenvalue by G lanes, to 2^-32 |T|.
+//  3. Their eigenvectors by inverse iteration (three solves with the LU factors of
+//     T - lambda I, pivots below eps |T| raised to eps |T|), one lane per eigenvalue;
+//     eigenvalues closer than 1e-7 |T| to their predecessor form clusters whose members
+//     are computed one level at a time and orthogonalized against the earlier ones.
+//     Each eigenvalue is then the Rayleigh quotient of its unit eigenvector.
+//  4. Back-transformation of the eigenvectors by the reflectors, last to first.
+// On exit columns L - nev .. L - 1 of V (L x L) hold the eigenvectors (the other columns
+// zero), evals the eigenvalues in increasing order (zero below L - nev), order the
+// indices by decreasing eigenvalue.  LOCAL (L <= kLdsWidth):
+// in phase 1 the 32 x 32 threads hold rows ti + 32 a and columns tj + 32 b of S in
+// registers, step k publishing row k (which then keeps v) and its norm in LDS, then
+// exchanging p and the row groups' parts of v^T S v through LDS, row sums being lane
+// sums (DPP within 16 lanes, one shuffle across); in phase 4 they hold rows tj + 32 b and
+// columns ti + 32 a of the eigenvectors, so the column sums v^T X are lane sums and a
+// step needs no barrier.  Otherwise S
+// and the eigenvectors live in the global buffers Sg and Vg, waves running over rows and
+// lanes along them.  ug: L x L fp64 scratch (the LU pivots of each lane's solves).
 template <bool LOCAL>
-__global__ __launch_bounds__(kEigThreads) void jacobi_kernel(double* __restrict__ Sg, int L,
-                                                             double* __restrict__ Vg,
-                                                             double* __restrict__ evals,
-                                                             int* __restrict__ order) {
-  __shared__ double red[kEigWaves][2];
-  __shared__ int done;
-  __shared__ double Sl[LOCAL ? kLdsWidth * (kLdsWidth + 1) : 1],
-      Vl[LOCAL ? kLdsWidth * (kLdsWidth + 1) : 1];
-  double* S = LOCAL ? Sl : Sg;
-  double* V = LOCAL ? Vl : Vg;
-  const int ld = LOCAL ? L + 1 : L;
-  // a batch: PB pairs x NC chunks of 64 lanes along the rows or columns
-  constexpr int NC = LOCAL ? (kLdsWidth + kWave - 1) / kWave : 2;
-  constexpr int PB = LOCAL ? 2 : 1;
+__global__ __launch_bounds__(kSyevThreads) void syev_kernel(double* __restrict__ Sg, int L, int nev,
+                                                            double* __restrict__ Vg,
+                                                            double* __restrict__ ug,
+                                                            double* __restrict__ evals,
+                                                            int* __restrict__ order) {
+  constexpr int W = LOCAL ? kLdsWidth : kMaxWidth;
+  constexpr int NC = (W + kWave - 1) / kWave;  // 64-lane chunks of a row
+  __shared__ double Al[LOCAL ? kLdsWidth * kLdsWidth : 1], Xl[LOCAL ? kLdsWidth * kLdsWidth : 1];
+  __shared__ double dd[W], ee[W], tau[W], vz[W], lam[W];
+  __shared__ double part[LOCAL ? 1 : kSyevWaves][W];  // partial sums (LOCAL: p)
+  __shared__ int pos[W];
+  __shared__ double sh_lo, sh_hi, sh_tn, sh_pivmin, s2buf[2], kpart[kGrid];
+  __shared__ int sh_maxpos;
+  double* A = LOCAL ? Al : Sg;
+  double* X = LOCAL ? Xl : Vg;
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
-  const int half = L / 2;
-  for (int i = wv; i < L; i += kEigWaves)
-    for (int j = lane; j < L; j += kWave) {
-      if (LOCAL) S[i * ld + j] = Sg[i * L + j];
-      V[i * ld + j] = i == j ? 1.0 : 0.0;
-    }
-  __syncthreads();
-  int rotated = 1;  // lane's rotations of the last sweep: some was applied
-  for (int sweep = 0; sweep < 30; ++sweep) {
-    if (!__syncthreads_or(rotated)) break;  // a sweep without rotations changes nothing
-    rotated = 0;
-    double off = 0.0, dia = 0.0;
-    for (int i = wv; i < L; i += kEigWaves)
-      for (int j = lane; j < L; j += kWave) {
-        const double v = S[i * ld + j];
-        if (i == j) dia += v * v;
-        else off += v * v;
-      }
+  const int ti = t / kGrid, tj = t % kGrid, nb = L / kGrid;
+
+  // ---- 1. tridiagonalization
+  if constexpr (LOCAL) {
+    double a[kSmallBlocks][kSmallBlocks];
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-      off += __shfl_xor(off, o, kWave);
-      dia += __shfl_xor(dia, o, kWave);
+    for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q)
+        a[p][q] = (p < nb && q < nb) ? Sg[(ti + kGrid * p) * L + tj + kGrid * q] : 0.0;
+    // row k of the registers into LDS row k, and the squared norm of its entries past
+    // column k + 1 into s2buf[k & 1]
+    auto publish = [&](int k) {
+      if (ti == k % kGrid) {
+        double s2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < kSmallBlocks; ++q) {
+          double v = a[0][q];
+#pragma unroll
+          for (int p = 1; p < kSmallBlocks; ++p)
+            if (p == k / kGrid) v = a[p][q];
+          const int j = tj + kGrid * q;
+          if (q < nb) A[k * L + j] = v;
+          if (q < nb && j > k + 1) s2 += v * v;
+        }
+        s2 = sumrow_f64(s2);
+        if (tj == 0) s2buf[k & 1] = s2;
+      }
+    };
+    for (int k = 0; k < L - 2; ++k) {
+      const int b = k + 1;
+      publish(k);
+      __syncthreads();
+      const double s2 = s2buf[k & 1];
+      const double x0 = A[k * L + b];
+      double tk = 0.0, v0 = x0, al = x0;
+      if (s2 > 0.0) {
+        const double mu = __builtin_sqrt(x0 * x0 + s2);
+        al = x0 > 0.0 ? -mu : mu;
+        v0 = x0 - al;
+        tk = 2.0 / (v0 * v0 + s2);
+      }
+      if (t == 0) {
+        dd[k] = A[k * L + k];
+        ee[k] = al;
+        tau[k] = tk;
+        vz[k] = v0;
+      }
+      if (tk != 0.0) {  // uniform
+        double vi[kSmallBlocks], vj[kSmallBlocks], ps[kSmallBlocks];
+#pragma unroll
+        for (int p = 0; p < kSmallBlocks; ++p) {
+          const int i = ti + kGrid * p, j = tj + kGrid * p;
+          vi[p] = (p < nb && i >= b) ? (i == b ? v0 : A[k * L + i]) : 0.0;
+          vj[p] = (p < nb && j >= b) ? (j == b ? v0 : A[k * L + j]) : 0.0;
+        }
+#pragma unroll
+        for (int p = 0; p < kSmallBlocks; ++p) {
+          double acc = 0.0;
+#pragma unroll
+          for (int q = 0; q < kSmallBlocks; ++q) acc += a[p][q] * vj[q];
+          ps[p] = sumrow_f64(acc);
+        }
+        if (tj == 0) {  // p_i for the row group's rows, and its part of v^T S' v
+          double vsv = 0.0;
+#pragma unroll
+          for (int p = 0; p < kSmallBlocks; ++p) {
+            if (p < nb) part[0][ti + kGrid * p] = tk * ps[p];
+            vsv += ps[p] * vi[p];
+          }
+          kpart[ti] = vsv;
+        }
+        __syncthreads();
+        // K = (tau / 2) p^T v = (tau^2 / 2) v^T S' v
+        const double K = 0.5 * tk * tk * sumrow_f64(kpart[tj]);
+        double wi[kSmallBlocks], wj[kSmallBlocks];
+#pragma unroll
+        for (int p = 0; p < kSmallBlocks; ++p) {
+          wi[p] = p < nb ? part[0][ti + kGrid * p] - K * vi[p] : 0.0;
+          wj[p] = p < nb ? part[0][tj + kGrid * p] - K * vj[p] : 0.0;
+        }
+#pragma unroll
+        for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+          for (int q = 0; q < kSmallBlocks; ++q)
+            if (ti + kGrid * p >= b && tj + kGrid * q >= b) a[p][q] -= vi[p] * wj[q] + wi[p] * vj[q];
+      }
     }
-    if (lane == 0) {
-      red[wv][0] = off;
-      red[wv][1] = dia;
-    }
+    publish(L - 2);
+    publish(L - 1);
     __syncthreads();
+  } else {
+  for (int k = 0; k < L - 2; ++k) {
+    const int b = k + 1, n1 = L - b;
+    double vv[NC];  // v_i for i = lane + 64 c (0 past the end)
+    double s2 = 0.0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int i = lane + kWave * c;
+      vv[c] = i < n1 ? A[k * L + b + i] : 0.0;
+      if (i >= 1) s2 += vv[c] * vv[c];
+    }
+    s2 = wave_sum_f64(s2);  // the same in every wave
+    const double x0 = A[k * L + b];
+    double tk = 0.0, v0 = x0, al = x0;
+    if (s2 > 0.0) {
+      const double mu = __builtin_sqrt(x0 * x0 + s2);
+      al = x0 > 0.0 ? -mu : mu;
+      v0 = x0 - al;
+      tk = 2.0 / (v0 * v0 + s2);
+    }
+    if (lane == 0) vv[0] = v0;
     if (t == 0) {
-      double o2 = 0.0, d2 = 0.0;
-      for (int w = 0; w < kEigWaves; ++w) {
-        o2 += red[w][0];
-        d2 += red[w][1];
+      dd[k] = A[k * L + k];
+      ee[k] = al;
+      tau[k] = tk;
+      vz[k] = v0;
+    }
+    if (tk != 0.0) {  // uniform
+      // part[w][i] = sum over the rows j of wave w's slice of S'[j][i] v_j
+      const int j0 = (wv * n1) / kSyevWaves, j1 = ((wv + 1) * n1) / kSyevWaves;
+      double acc[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = 0.0;
+      for (int j = j0; j < j1; ++j) {
+        const double vj = j == 0 ? v0 : A[k * L + b + j];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int i = lane + kWave * c;
+          if (i < n1) acc[c] += A[(b + j) * L + b + i] * vj;
+        }
       }
-      done = (o2 <= 1e-28 * d2) ? 1 : 0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int i = lane + kWave * c;
+        if (i < n1) part[wv][i] = acc[c];
+      }
+      __syncthreads();
+      double ww[NC], kd = 0.0;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int i = lane + kWave * c;
+        double p = 0.0;
+        if (i < n1) {
+          for (int w = 0; w < kSyevWaves; ++w) p += part[w][i];
+          p *= tk;
+        }
+        ww[c] = p;
+        kd += p * vv[c];
+      }
+      const double K = 0.5 * tk * wave_sum_f64(kd);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) ww[c] -= K * vv[c];
+      for (int i = wv; i < n1; i += kSyevWaves) {  // S' -= v w^T + w v^T, row i
+        double vsel = vv[0], wsel = ww[0];
+#pragma unroll
+        for (int c = 1; c < NC; ++c)
+          if ((i >> 6) == c) {
+            vsel = vv[c];
+            wsel = ww[c];
+          }
+        const double vi = __shfl(vsel, i & (kWave - 1), kWave);
+        const double wi = __shfl(wsel, i & (kWave - 1), kWave);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int j = lane + kWave * c;
+          if (j < n1) A[(b + i) * L + b + j] -= vi * ww[c] + wi * vv[c];
+        }
+      }
     }
     __syncthreads();
-    if (done) break;
-    for (int round = 0; round < L - 1; ++round) {
-      // lane l: rotation of pair wv + 16 l
-      double cl = 1.0, sl = 0.0;
-      {
-        const int j = wv + kEigWaves * lane;
-        if (j < half) {
-          int p, q;
-          rr_pair(j, round, L, p, q);
-          const double apq = S[p * ld + q], app = S[p * ld + p], aqq = S[q * ld + q];
-          if (__builtin_fabs(apq) > 1e-17 * __builtin_sqrt(__builtin_fabs(app * aqq)) &&
-              __builtin_fabs(apq) > 1e-300) {
-            const double tau = (aqq - app) / (2.0 * apq);
-            const double tt = (tau >= 0.0 ? 1.0 : -1.0) /
-                              (__builtin_fabs(tau) + __builtin_sqrt(1.0 + tau * tau));
-            cl = 1.0 / __builtin_sqrt(1.0 + tt * tt);
-            sl = tt * cl;
-            rotated = 1;
-          }
-        }
-      }
-      // rows: S <- J^T S, then columns: S J and V J; the wave's pairs in batches of PB,
-      // all loads of a batch issued before its stores
-      for (int j0 = 0; wv + kEigWaves * j0 < half; j0 += PB) {
-        int pp[PB], qq[PB];
-        double cc[PB], ss[PB];
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          const int j = wv + kEigWaves * (j0 + u);
-          ss[u] = __shfl(sl, (j0 + u) & (kWave - 1), kWave);
-          cc[u] = __shfl(cl, (j0 + u) & (kWave - 1), kWave);
-          if (j < half) rr_pair(j, round, L, pp[u], qq[u]);
-          else {
-            pp[u] = qq[u] = 0;
-            ss[u] = 0.0;
-          }
-        }
-        for (int c0 = 0; c0 < L; c0 += NC * kWave) {
-          double ra[PB][NC], rb[PB][NC];
-#pragma unroll
-          for (int u = 0; u < PB; ++u)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const int col = c0 + lane + kWave * c;
-              if (ss[u] != 0.0 && col < L) {
-                ra[u][c] = S[pp[u] * ld + col];
-                rb[u][c] = S[qq[u] * ld + col];
-              }
-            }
-#pragma unroll
-          for (int u = 0; u < PB; ++u)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const int col = c0 + lane + kWave * c;
-              if (ss[u] != 0.0 && col < L) {
-                S[pp[u] * ld + col] = cc[u] * ra[u][c] - ss[u] * rb[u][c];
-                S[qq[u] * ld + col] = ss[u] * ra[u][c] + cc[u] * rb[u][c];
-              }
-            }
-        }
-      }
-      __syncthreads();
-      for (int j0 = 0; wv + kEigWaves * j0 < half; j0 += PB) {
-        int pp[PB], qq[PB];
-        double cc[PB], ss[PB];
-#pragma unroll
-        for (int u = 0; u < PB; ++u) {
-          const int j = wv + kEigWaves * (j0 + u);
-          ss[u] = __shfl(sl, (j0 + u) & (kWave - 1), kWave);
-          cc[u] = __shfl(cl, (j0 + u) & (kWave - 1), kWave);
-          if (j < half) rr_pair(j, round, L, pp[u], qq[u]);
-          else {
-            pp[u] = qq[u] = 0;
-            ss[u] = 0.0;
-          }
-        }
-        for (int c0 = 0; c0 < L; c0 += NC * kWave) {
-          double sa[PB][NC], sb[PB][NC], va[PB][NC], vb[PB][NC];
-#pragma unroll
-          for (int u = 0; u < PB; ++u)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const int row = c0 + lane + kWave * c;
-              if (ss[u] != 0.0 && row < L) {
-                sa[u][c] = S[row * ld + pp[u]];
-                sb[u][c] = S[row * ld + qq[u]];
-                va[u][c] = V[row * ld + pp[u]];
-                vb[u][c] = V[row * ld + qq[u]];
-              }
-            }
-#pragma unroll
-          for (int u = 0; u < PB; ++u)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-              const int row = c0 + lane + kWave * c;
-              if (ss[u] != 0.0 && row < L) {
-                S[row * ld + pp[u]] = cc[u] * sa[u][c] - ss[u] * sb[u][c];
-                S[row * ld + qq[u]] = ss[u] * sa[u][c] + cc[u] * sb[u][c];
-                V[row * ld + pp[u]] = cc[u] * va[u][c] - ss[u] * vb[u][c];
-                V[row * ld + qq[u]] = ss[u] * va[u][c] + cc[u] * vb[u][c];
-              }
-            }
-        }
-      }
-      __syncthreads();
-    }
   }
-  for (int i = t; i < L; i += kEigThreads) evals[i] = S[i * ld + i];
-  if (LOCAL) {
-    for (int i = wv; i < L; i += kEigWaves)
-      for (int j = lane; j < L; j += kWave) Vg[i * L + j] = V[i * ld + j];
+  }
+  if (t == 0) {
+    dd[L - 2] = A[(L - 2) * L + L - 2];
+    dd[L - 1] = A[(L - 1) * L + L - 1];
+    ee[L - 2] = A[(L - 2) * L + L - 1];
+    ee[L - 1] = 0.0;
+    tau[L - 2] = tau[L - 1] = 0.0;
+    double lo = 0.0, hi = 0.0, e2max = 0.0;  // Gershgorin interval of T
+    for (int i = 0; i < L; ++i) {
+      const double r = (i > 0 ? __builtin_fabs(ee[i - 1]) : 0.0) + __builtin_fabs(ee[i]);
+      const double l = dd[i] - r, h = dd[i] + r;
+      lo = i == 0 || l < lo ? l : lo;
+      hi = i == 0 || h > hi ? h : hi;
+      e2max = ee[i] * ee[i] > e2max ? ee[i] * ee[i] : e2max;
+    }
+    const double tn = __builtin_fmax(__builtin_fabs(lo), __builtin_fabs(hi));
+    const double pivmin = __DBL_MIN__ * (e2max > 1.0 ? e2max : 1.0);
+    sh_lo = lo - (2.0 * __DBL_EPSILON__ * tn + pivmin);
+    sh_hi = hi + (2.0 * __DBL_EPSILON__ * tn + pivmin);
+    sh_tn = tn;
+    sh_pivmin = pivmin;
   }
   __syncthreads();
-  for (int i = t; i < L; i += kEigThreads) {  // rank by decreasing value, ties by index
-    const double v = evals[i];
-    int rank = 0;
-    for (int j = 0; j < L; ++j) {
-      const double u = evals[j];
-      rank += (u > v || (u == v && j < i)) ? 1 : 0;
+
+  // ---- 2. eigenvalues L - nev .. L - 1 (ascending): lanes g G .. g G + G - 1 bracket the
+  // (L - nev + g)-th smallest to 2^-32 |T|
+  const double tn = sh_tn, pivmin = sh_pivmin;
+  const int first = L - nev;
+  {
+    int G = 1;
+    while (G < 8 && 2 * G * nev <= kSyevThreads) G *= 2;
+    const int m = t % G, gbase = lane & ~(G - 1);
+    const double tol = 0x1p-32 * tn + pivmin;
+    for (int g = t / G; g < nev; g += kSyevThreads / G) {
+      const int gi = first + g;
+      double lo = sh_lo, hi = sh_hi;
+      for (int it = 0; it < 200; ++it) {
+        const double wdt = hi - lo;
+        if (!(wdt > tol)) break;
+        const double x = lo + (double)(m + 1) * wdt / (double)(G + 1);
+        double q = dd[0] - x;
+        if (__builtin_fabs(q) < pivmin) q = -pivmin;
+        int cnt = q < 0.0 ? 1 : 0;
+        for (int i = 1; i < L; ++i) {
+          const double e = ee[i - 1];
+          q = __builtin_fma(-(e * e), recip(q), dd[i] - x);
+          if (__builtin_fabs(q) < pivmin) q = -pivmin;
+          cnt += q < 0.0 ? 1 : 0;
+        }
+        double nlo = lo, nhi = hi;
+        for (int mm = 0; mm < G; ++mm) {  // largest point with count <= gi, smallest with > gi
+          const int cm = __shfl(cnt, gbase + mm, kWave);
+          const double xm = lo + (double)(mm + 1) * wdt / (double)(G + 1);
+          if (cm <= gi) nlo = xm;
+        }
+        for (int mm = G - 1; mm >= 0; --mm) {
+          const int cm = __shfl(cnt, gbase + mm, kWave);
+          const double xm = lo + (double)(mm + 1) * wdt / (double)(G + 1);
+          if (cm > gi) nhi = xm;
+        }
+        lo = nlo;
+        hi = nhi;
+      }
+      if (m == 0) lam[gi] = 0.5 * (lo + hi);
     }
-    order[rank] = i;
+  }
+  for (int e = t; e < L * first; e += kSyevThreads) X[(e / first) * L + e % first] = 0.0;
+  __syncthreads();
+
+  // ---- 3. eigenvectors of T, cluster level by cluster level; each eigenvalue is then
+  // refined to the Rayleigh quotient x^T T x of its unit eigenvector
+  const double tnz = tn > 0.0 ? tn : 1.0;
+  if (t == 0) {
+    int mp = 0;
+    pos[first] = 0;
+    for (int i = first + 1; i < L; ++i) {
+      pos[i] = lam[i] - lam[i - 1] <= 1e-7 * tnz ? pos[i - 1] + 1 : 0;
+      mp = pos[i] > mp ? pos[i] : mp;
+    }
+    sh_maxpos = mp;
+  }
+  __syncthreads();
+  {
+    const double tiny = __DBL_EPSILON__ * tnz;
+    const int maxpos = sh_maxpos;
+    for (int lev = 0; lev <= maxpos; ++lev) {
+      for (int i = first + t; i < L; i += kSyevThreads) {
+        if (pos[i] != lev) continue;
+        const double li = lam[i];
+        for (int r = 0; r < L; ++r) X[r * L + i] = 1.0 + (double)((r * 40503 + i * 34283) & 1023) / 4096.0;
+        for (int it = 0; it < 3; ++it) {
+          // T - li I = L U: forward elimination fused with L y = x (y over x); ug keeps
+          // the pivots' reciprocals
+          double up = dd[0] - li;
+          if (__builtin_fabs(up) < tiny) up = tiny;
+          double rup = recip(up);
+          ug[i] = rup;
+          double y = X[i];
+          for (int j = 1; j < L; ++j) {
+            const double mlt = ee[j - 1] * rup;
+            up = dd[j] - li - mlt * ee[j - 1];
+            if (__builtin_fabs(up) < tiny) up = tiny;
+            rup = recip(up);
+            ug[j * L + i] = rup;
+            y = X[j * L + i] - mlt * y;
+            X[j * L + i] = y;
+          }
+          // U x = y
+          double xn = y * rup, nrm = xn * xn;
+          X[(L - 1) * L + i] = xn;
+          for (int j0 = L - 2; j0 >= 0; j0 -= 8) {  // pivots of 8 rows loaded ahead
+            double uu[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) uu[q] = j0 - q >= 0 ? ug[(j0 - q) * L + i] : 1.0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int j = j0 - q;
+              if (j >= 0) {
+                xn = (X[j * L + i] - ee[j] * xn) * uu[q];
+                X[j * L + i] = xn;
+                nrm += xn * xn;
+              }
+            }
+          }
+          if (!(nrm > 0.0 && nrm < __DBL_MAX__)) {  // no usable solve: start from e_i
+            for (int r = 0; r < L; ++r) X[r * L + i] = r == i ? 1.0 : 0.0;
+            nrm = 1.0;
+          }
+          double sc = 1.0 / __builtin_sqrt(nrm);
+          for (int r = 0; r < L; ++r) X[r * L + i] *= sc;
+          if (lev > 0) {  // orthogonalize against the cluster's earlier members
+            for (int jj = i - lev; jj < i; ++jj) {
+              double dot = 0.0;
+              for (int r = 0; r < L; ++r) dot += X[r * L + jj] * X[r * L + i];
+              for (int r = 0; r < L; ++r) X[r * L + i] -= dot * X[r * L + jj];
+            }
+            nrm = 0.0;
+            for (int r = 0; r < L; ++r) nrm += X[r * L + i] * X[r * L + i];
+            sc = nrm > 0.0 ? 1.0 / __builtin_sqrt(nrm) : 0.0;
+            for (int r = 0; r < L; ++r) X[r * L + i] *= sc;
+          }
+        }
+        double rq = 0.0, xp = X[i];
+        for (int r = 0; r < L; ++r) {
+          const double xr = xp;
+          xp = r + 1 < L ? X[(r + 1) * L + i] : 0.0;
+          rq += xr * (dd[r] * xr + 2.0 * ee[r] * xp);
+        }
+        lam[i] = rq;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 4. back-transformation X <- H_k X, k = L - 3 .. 0
+  if constexpr (LOCAL) {
+    double x[kSmallBlocks][kSmallBlocks];  // x[q][p] = X[tj + 32 q][ti + 32 p]
+#pragma unroll
+    for (int q = 0; q < kSmallBlocks; ++q)
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p)
+        x[q][p] = (p < nb && q < nb) ? X[(tj + kGrid * q) * L + ti + kGrid * p] : 0.0;
+    for (int k = L - 3; k >= 0; --k) {
+      const double tk = tau[k];
+      if (tk == 0.0) continue;
+      const int b = k + 1;
+      double vr[kSmallBlocks];
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q) {
+        const int r = tj + kGrid * q;
+        vr[q] = (q < nb && r >= b) ? (r == b ? vz[k] : A[k * L + r]) : 0.0;
+      }
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p) {
+        double y = 0.0;
+#pragma unroll
+        for (int q = 0; q < kSmallBlocks; ++q) y += vr[q] * x[q][p];
+        y = tk * sumrow_f64(y);
+#pragma unroll
+        for (int q = 0; q < kSmallBlocks; ++q) x[q][p] -= vr[q] * y;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kSmallBlocks; ++q)
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p)
+        if (p < nb && q < nb) Vg[(tj + kGrid * q) * L + ti + kGrid * p] = x[q][p];
+  } else {
+  for (int k = L - 3; k >= 0; --k) {
+    const double tk = tau[k];
+    if (tk == 0.0) continue;  // uniform
+    const int b = k + 1, n1 = L - b;
+    const int i0 = (wv * n1) / kSyevWaves, i1 = ((wv + 1) * n1) / kSyevWaves;
+    double acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.0;
+    for (int i = i0; i < i1; ++i) {
+      const double vi = i == 0 ? vz[k] : A[k * L + b + i];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int col = lane + kWave * c;
+        if (col < L) acc[c] += vi * X[(b + i) * L + col];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = lane + kWave * c;
+      if (col < L) part[wv][col] = acc[c];
+    }
+    __syncthreads();
+    double yc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int col = lane + kWave * c;
+      double y = 0.0;
+      if (col < L)
+        for (int w = 0; w < kSyevWaves; ++w) y += part[w][col];
+      yc[c] = tk * y;
+    }
+    for (int i = wv; i < n1; i += kSyevWaves) {
+      const double vi = i == 0 ? vz[k] : A[k * L + b + i];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int col = lane + kWave * c;
+        if (col < L) X[(b + i) * L + col] -= vi * yc[c];
+      }
+    }
+    __syncthreads();
+  }
+  }
+  for (int i = t; i < L; i += kSyevThreads) {
+    evals[i] = i >= first ? lam[i] : 0.0;
+    order[i] = L - 1 - i;
   }
 }
 
@@ -491,27 +783,119 @@ constexpr int kCholWaves = kCholThreads / kWave;
 // with zero row and column for dropped indices, so that the columns of Y T are the
 // Gram-Schmidt vectors of Y's columns: orthonormal up to the Gram matrix's error relative
 // to the pivots, zero where dropped.  Applied twice (the second time to Y T), the basis
-// is orthonormal to about 2^-18.  Waves run over rows, lanes along them, the fixed row
-// of a step in registers and the loads of PB rows issued before their stores; one
-// barrier per step.  LOCAL: the factor and the inverse live in LDS (L <= kLdsWidth), else in place in
-// the global buffers Ag (the Gram matrix, overwritten) and Xg (scratch, L x L).  One block.
-template <bool LOCAL>
-__global__ __launch_bounds__(kCholThreads) void chol_inverse_kernel(double* __restrict__ Ag,
-                                                                    double* __restrict__ Xg, int L,
-                                                                    float* __restrict__ T) {
-  __shared__ double Al[LOCAL ? kLdsWidth * kLdsWidth : 1], Xl[LOCAL ? kLdsWidth * kLdsWidth : 1];
-  __shared__ double piv[kMaxWidth];  // 1 / d_k, 0 for a dropped column
-  double* A = LOCAL ? Al : Ag;
-  double* X = LOCAL ? Xl : Xg;
-  constexpr int NC = ((LOCAL ? kLdsWidth : kMaxWidth) + kWave - 1) / kWave;  // 64-lane chunks
-  constexpr int PB = LOCAL ? 4 : 2;  // rows whose LDS accesses are batched
-  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
-  for (int k = t; k < L; k += kCholThreads) piv[k] = Ag[k * L + k];  // g_kk, kept until step k
-  for (int i = wv; i < L; i += kCholWaves)
-    for (int j = lane; j < L; j += kWave) {
-      if (LOCAL) A[i * L + j] = Ag[i * L + j];
-      X[i * L + j] = i == j ? 1.0 : 0.0;
+// is orthonormal to about 2^-18.
+//
+// Widths up to kLdsWidth (chol_inverse_small_kernel): the matrix lives in registers, the
+// 32 x 32 threads owning rows ti + 32 a and columns tj + 32 b (a, b < L / 32); step k
+// broadcasts row k through LDS (one barrier) and every thread updates its entries.  The
+// rows of D U stay in LDS for the back substitution, whose step k broadcasts row k of
+// U^-1 through a double-buffered LDS row.  Wider (chol_inverse_kernel): the matrices
+// live in global memory (Ag, the Gram matrix, overwritten, and Xg, scratch), waves run
+// over rows and lanes along them.  One block.
+__global__ __launch_bounds__(kGrid * kGrid) void chol_inverse_small_kernel(const double* __restrict__ Ag,
+                                                                          int L,
+                                                                          float* __restrict__ T) {
+  __shared__ double R[kLdsWidth * kLdsWidth];  // row k: row k of D U once step k starts
+  __shared__ double xrow[2][kLdsWidth];
+  __shared__ double diag[kLdsWidth], piv[kLdsWidth];
+  const int t = threadIdx.x, ti = t / kGrid, tj = t % kGrid;
+  const int nb = L / kGrid;  // entries per thread along rows and columns
+  double a[kSmallBlocks][kSmallBlocks];
+#pragma unroll
+  for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+    for (int q = 0; q < kSmallBlocks; ++q)
+      a[p][q] = (p < nb && q < nb) ? Ag[(ti + kGrid * p) * L + tj + kGrid * q] : 0.0;
+  for (int i = t; i < L; i += kGrid * kGrid) diag[i] = Ag[i * L + i];
+  // step k: a_ij -= a_ki a_kj / d_k for k < i, k < j (entries below the diagonal too)
+  for (int k = 0; k < L; ++k) {
+    if (ti == k % kGrid) {  // owners of row k publish it
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q)
+        if (q < nb) {
+          double v = a[0][q];
+#pragma unroll
+          for (int p = 1; p < kSmallBlocks; ++p)
+            if (p == k / kGrid) v = a[p][q];
+          R[k * L + tj + kGrid * q] = v;
+        }
     }
+    __syncthreads();
+    const double d = R[k * L + k];
+    const double inv = d > 0x1p-16 * diag[k] ? 1.0 / d : 0.0;
+    if (inv != 0.0) {
+      double fi[kSmallBlocks], rj[kSmallBlocks];
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p) {
+        fi[p] = p < nb ? R[k * L + ti + kGrid * p] * inv : 0.0;
+        rj[p] = p < nb ? R[k * L + tj + kGrid * p] : 0.0;
+      }
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+        for (int q = 0; q < kSmallBlocks; ++q)
+          if (ti + kGrid * p > k && tj + kGrid * q > k) a[p][q] -= fi[p] * rj[q];
+    }
+  }
+  for (int i = t; i < L; i += kGrid * kGrid) {
+    const double d = R[i * L + i];
+    piv[i] = d > 0x1p-16 * diag[i] ? 1.0 / d : 0.0;
+  }
+  // X = U^-1 by back substitution on U X = I (u_ik = r_ik / d_i): step k publishes row k
+  // of X (final) and rows i < k lose u_ik times it
+#pragma unroll
+  for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+    for (int q = 0; q < kSmallBlocks; ++q) a[p][q] = (ti + kGrid * p == tj + kGrid * q) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int k = L - 1; k > 0; --k) {
+    double* xr = xrow[k & 1];
+    if (ti == k % kGrid) {
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q)
+        if (q < nb) {
+          double v = a[0][q];
+#pragma unroll
+          for (int p = 1; p < kSmallBlocks; ++p)
+            if (p == k / kGrid) v = a[p][q];
+          xr[tj + kGrid * q] = v;
+        }
+    }
+    __syncthreads();
+    double ui[kSmallBlocks], xj[kSmallBlocks];
+#pragma unroll
+    for (int p = 0; p < kSmallBlocks; ++p) {
+      const int i = ti + kGrid * p;
+      ui[p] = (p < nb && i < k) ? R[i * L + k] * piv[i] : 0.0;
+      xj[p] = p < nb ? xr[tj + kGrid * p] : 0.0;
+    }
+#pragma unroll
+    for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q)
+        if (tj + kGrid * q >= k) a[p][q] -= ui[p] * xj[q];
+  }
+  // T = X D^-1/2, column j scaled by 1 / sqrt(d_j), zero for dropped rows and columns
+#pragma unroll
+  for (int p = 0; p < kSmallBlocks; ++p)
+#pragma unroll
+    for (int q = 0; q < kSmallBlocks; ++q) {
+      const int i = ti + kGrid * p, j = tj + kGrid * q;
+      if (p < nb && q < nb)
+        T[i * L + j] = (piv[i] != 0.0 && piv[j] != 0.0) ? (float)(a[p][q] * __builtin_sqrt(piv[j])) : 0.f;
+    }
+}
+
+__global__ __launch_bounds__(kCholThreads) void chol_inverse_kernel(double* __restrict__ A,
+                                                                   double* __restrict__ X, int L,
+                                                                   float* __restrict__ T) {
+  __shared__ double piv[kMaxWidth];  // 1 / d_k, 0 for a dropped column
+  constexpr int NC = kMaxWidth / kWave;  // 64-lane chunks of a row
+  constexpr int PB = 2;                  // rows whose accesses are batched
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  for (int k = t; k < L; k += kCholThreads) piv[k] = A[k * L + k];  // g_kk, kept until step k
+  for (int i = wv; i < L; i += kCholWaves)
+    for (int j = lane; j < L; j += kWave) X[i * L + j] = i == j ? 1.0 : 0.0;
   __syncthreads();
   // step k: a_ij -= a_ki a_kj / d_k for k < i, k < j (a_k. is row k of D U, unscaled; the
   // entries below the diagonal are updated too and never read)
@@ -773,9 +1157,9 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
     hipError_t e = gram(X, M);
     if (e != hipSuccess) return e;
     if (L <= kLdsWidth)
-      hipLaunchKernelGGL(chol_inverse_kernel<true>, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
+      hipLaunchKernelGGL(chol_inverse_small_kernel, dim3(1), dim3(kGrid * kGrid), 0, st, G, L, T);
     else
-      hipLaunchKernelGGL(chol_inverse_kernel<false>, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
+      hipLaunchKernelGGL(chol_inverse_kernel, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock), 0,
                        st, X, M, L, T, L, out32, (float*)nullptr, out16);
@@ -798,9 +1182,9 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   if ((err = gemm(dWT, n, m, Q16, Q32)) != hipSuccess) return err;     // Z = dW^T Q = B_m^T (n x L)
   if ((err = gram(Q32, n)) != hipSuccess) return err;                  // B_m B_m^T = U~ Lambda U~^T
   if (L <= kLdsWidth)
-    hipLaunchKernelGGL(jacobi_kernel<true>, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+    hipLaunchKernelGGL(syev_kernel<true>, dim3(1), dim3(kSyevThreads), 0, st, G, L, P.rank, V, Gp, ev, ord);
   else
-    hipLaunchKernelGGL(jacobi_kernel<false>, dim3(1), dim3(kEigThreads), 0, st, G, L, V, ev, ord);
+    hipLaunchKernelGGL(syev_kernel<false>, dim3(1), dim3(kSyevThreads), 0, st, G, L, P.rank, V, Gp, ev, ord);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int r = P.rank;
   // B = Q U~_r Sigma_r (m x r);  A = Sigma_r^-1 U~_r^T B_m = (Z U~_r Sigma_r^-1)^T (r x n)
