@@ -226,23 +226,30 @@ __global__ __launch_bounds__(kBlock) void split_sum_kernel(const float* __restri
 // ------------------------------------------------------------------- Gram --
 
 // Partial Gram matrices: Gp[z][a][b] = sum over the rows i of split z (rows z * rs ..
-// + rs) of X[i][a] X[i][b] for X (M x L fp32): block (a0, b0, z) of 32 x 32 entries;
-// 64-row chunks of the two column slabs through LDS, fp32 sums per chunk added in fp64.
+// + rs) of X[i][a] X[i][b] for X (M x L fp32), for the 32 x 32 tiles on and above the
+// diagonal only (block x: tile (A, B), A <= B, in row order; block y: split z); 64-row
+// chunks of the two column slabs through LDS, fp32 sums per chunk added in fp64.
 // Thread t: entry a0 + t % 32, b0 + 4 (t / 32) .. + 4.
 __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ X, int64_t M, int L,
                                                       int64_t rs, double* __restrict__ Gp) {
   __shared__ float xa[64][33], xb[64][33];
   const int t = threadIdx.x;
-  const int a0 = blockIdx.x * 32, b0 = blockIdx.y * 32;
-  const int64_t r0 = (int64_t)blockIdx.z * rs;
+  const int nt = L / 32;
+  int A = 0, idx = blockIdx.x;
+  while (idx >= nt - A) {
+    idx -= nt - A;
+    ++A;
+  }
+  const int a0 = A * 32, b0 = (A + idx) * 32;
+  const int64_t r0 = (int64_t)blockIdx.y * rs;
   const int64_t r1 = r0 + rs < M ? r0 + rs : M;
   const int ta = t & 31, tb = (t >> 5) * 4;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   for (int64_t i0 = r0; i0 < r1; i0 += 64) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {  // 64 rows x 32 columns of each slab, 8 values per thread
-      const int idx = t + u * kBlock;
-      const int r = idx >> 5, c = idx & 31;
+      const int e = t + u * kBlock;
+      const int r = e >> 5, c = e & 31;
       const int64_t i = i0 + r;
       xa[r][c] = i < r1 ? X[i * L + a0 + c] : 0.f;
       xb[r][c] = i < r1 ? X[i * L + b0 + c] : 0.f;
@@ -259,19 +266,41 @@ __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ 
     for (int j = 0; j < 4; ++j) acc[j] += (double)part[j];
     __syncthreads();
   }
-  double* G = Gp + (int64_t)blockIdx.z * L * L;
+  double* G = Gp + (int64_t)blockIdx.y * L * L;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) G[(int64_t)(a0 + ta) * L + b0 + tb + j] = acc[j];
+  for (int j = 0; j < 4; ++j) G[(a0 + ta) * L + b0 + tb + j] = acc[j];
 }
 
-// G[e] = sum over splits z (in order) of Gp[z][e].
+// G[a][b] = sum over the splits of Gp[z][a][b], read from the tile on or above the
+// diagonal (so G is exactly symmetric).  Block: 64 entries x 4 groups of splits; group g
+// sums splits g, g + 4, ... in order, then the four group sums are added in order.
+constexpr int kGramSumGroups = kBlock / 64;
 __global__ __launch_bounds__(kBlock) void gram_sum_kernel(const double* __restrict__ Gp, int splits,
-                                                          int64_t count, double* __restrict__ G) {
-  for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < count;
-       e += (int64_t)gridDim.x * kBlock) {
-    double v = Gp[e];
-    for (int z = 1; z < splits; ++z) v += Gp[(int64_t)z * count + e];
-    G[e] = v;
+                                                          int L, double* __restrict__ G) {
+  __shared__ double red[kGramSumGroups][64];
+  const int t = threadIdx.x, eo = t & 63, g = t >> 6;
+  const int64_t count = (int64_t)L * L;
+  const int64_t e = (int64_t)blockIdx.x * 64 + eo;
+  double v = 0.0;
+  int64_t src = 0;
+  if (e < count) {
+    const int a = (int)(e / L), b = (int)(e % L);
+    src = (a >> 5) <= (b >> 5) ? e : (int64_t)b * L + a;
+    double s0 = 0.0, s1 = 0.0;  // two chains over alternate splits of the group
+    int z = g;
+    for (; z + kGramSumGroups < splits; z += 2 * kGramSumGroups) {
+      s0 += Gp[(int64_t)z * count + src];
+      s1 += Gp[(int64_t)(z + kGramSumGroups) * count + src];
+    }
+    if (z < splits) s0 += Gp[(int64_t)z * count + src];
+    v = s0 + s1;
+  }
+  red[g][eo] = v;
+  __syncthreads();
+  if (g == 0 && e < count) {
+    double s = red[0][eo];
+    for (int k = 1; k < kGramSumGroups; ++k) s += red[k][eo];
+    G[e] = s;
   }
 }
 
@@ -1000,45 +1029,69 @@ __global__ __launch_bounds__(kBlock) void transform_kernel(const double* __restr
   }
 }
 
-// Out = X T for X (M x L fp32, row-major) and T (L x C fp32): block of 64 rows x 32
-// columns, T's 32 columns staged in LDS; thread t: column c0 + t % 32, rows 8 (t / 32) ..
-// + 8.  Outputs (each may be null): row-major fp32 (M x C), transposed fp32 (C x M),
-// transposed binary16 (C x M, row stride ldt).
+// Out = X T for X (M x L fp32, row-major, M a multiple of 8) and T (L x C fp32): block of
+// 64 rows x 32 columns; T's 32 columns and 64 x 32 tiles of X (coalesced row segments)
+// staged in LDS; thread t: column c0 + t % 32, rows 8 (t / 32) .. + 8.  Outputs (each
+// may be null): row-major fp32 (M x C), transposed fp32 (C x M) and transposed binary16
+// (C x M, 16-byte aligned), the transposed ones stored 8 rows at a time as vectors (the
+// fp32 one when its buffer is 16-byte aligned).
 __global__ __launch_bounds__(kBlock) void apply_kernel(const float* __restrict__ X, int64_t M, int L,
                                                        const float* __restrict__ T, int C,
                                                        float* __restrict__ out_rm,
                                                        float* __restrict__ out_t32,
                                                        uint16_t* __restrict__ out_t16) {
-  __shared__ float ts[kMaxWidth][33];
+  extern __shared__ float ts[];  // L x 33: T's 32 columns (dynamic, L * 33 floats)
+  __shared__ float xs[64][33];
   const int t = threadIdx.x;
   const int c0 = blockIdx.y * 32;
   const int64_t i0 = (int64_t)blockIdx.x * 64;
   for (int e = t; e < L * 32; e += kBlock) {
     const int b = e >> 5, c = e & 31;
-    ts[b][c] = c0 + c < C ? T[(int64_t)b * C + c0 + c] : 0.f;
+    ts[b * 33 + c] = c0 + c < C ? T[(int64_t)b * C + c0 + c] : 0.f;
   }
-  __syncthreads();
   const int c = t & 31, rb = (t >> 5) * 8;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < L; ++b) {
-    const float tv = ts[b][c];
+  for (int b0 = 0; b0 < L; b0 += 32) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t i = i0 + rb + r;
-      const float xv = i < M ? X[i * L + b] : 0.f;
-      acc[r] = __builtin_fmaf(xv, tv, acc[r]);
+    for (int u = 0; u < 8; ++u) {  // rows i0 .. + 64, columns b0 .. + 32 of X
+      const int e = t + u * kBlock;
+      const int r = e >> 5, col = e & 31;
+      const int64_t i = i0 + r;
+      xs[r][col] = i < M ? X[i * L + b0 + col] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int b = 0; b < 32; ++b) {
+      const float tv = ts[(b0 + b) * 33 + c];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) acc[r] = __builtin_fmaf(xs[rb + r][b], tv, acc[r]);
+    }
+    __syncthreads();
+  }
+  if (c0 + c >= C) return;
+  const int64_t ib = i0 + rb;  // a multiple of 8; all 8 rows valid when ib < M
+  if (ib >= M) return;
+  if (out_rm) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) out_rm[(ib + r) * C + c0 + c] = acc[r];
+  }
+  if (out_t32) {
+    float* o = out_t32 + (int64_t)(c0 + c) * M + ib;
+    if ((reinterpret_cast<uintptr_t>(out_t32) & 15) == 0) {  // the caller's buffer may be 4-aligned
+      reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) o[r] = acc[r];
     }
   }
-  if (c0 + c < C) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int64_t i = i0 + rb + r;
-      if (i < M) {
-        if (out_rm) out_rm[i * C + c0 + c] = acc[r];
-        if (out_t32) out_t32[(int64_t)(c0 + c) * M + i] = acc[r];
-        if (out_t16) out_t16[(int64_t)(c0 + c) * M + i] = (uint16_t)f2h(acc[r]);
-      }
-    }
+  if (out_t16) {
+    uint4 h;
+    h.x = f2h(acc[0]) | (f2h(acc[1]) << 16);
+    h.y = f2h(acc[2]) | (f2h(acc[3]) << 16);
+    h.z = f2h(acc[4]) | (f2h(acc[5]) << 16);
+    h.w = f2h(acc[6]) | (f2h(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out_t16 + (int64_t)(c0 + c) * M + ib) = h;
   }
 }
 
@@ -1059,8 +1112,8 @@ constexpr int64_t kGramBudget = 16ll << 20;     // bytes of partial Gram matrice
 
 // Row splits of a Gram computation over M rows: enough blocks to fill the chip.
 int gram_splits(int64_t M, int L) {
-  const int64_t tiles = (int64_t)(L / 32) * (L / 32);
-  int64_t s = (256 + tiles - 1) / tiles;
+  const int64_t nt = L / 32, tiles = nt * (nt + 1) / 2;  // tiles on and above the diagonal
+  int64_t s = (768 + tiles - 1) / tiles;
   if (s > (M + 63) / 64) s = (M + 63) / 64;
   const int64_t cap = kGramBudget / ((int64_t)L * L * 8);
   if (s > cap) s = cap;
@@ -1123,6 +1176,7 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   double* Gp = cv.take<double>((int64_t)gram_splits(mx, L) * L * L);
   hipError_t err;
   const int64_t grid_cap = (int64_t)cus * 8;
+  const size_t apply_lds = (size_t)L * 33 * sizeof(float);  // apply_kernel's T slab
 
   // Out (M x L fp32) = A (M x K) B^T for B (L x K)
   auto gemm = [&](const uint16_t* A, int64_t M, int64_t K, const uint16_t* B, float* out) -> hipError_t {
@@ -1143,12 +1197,13 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   auto gram = [&](const float* X, int64_t M) -> hipError_t {
     const int gs = gram_splits(M, L);
     const int64_t rs = (((M + gs - 1) / gs + 63) / 64) * 64;
-    hipLaunchKernelGGL(gram_kernel, dim3(L / 32, L / 32, gs), dim3(kBlock), 0, st, X, M, L, rs, Gp);
+    const int nt = L / 32;
+    hipLaunchKernelGGL(gram_kernel, dim3(nt * (nt + 1) / 2, gs), dim3(kBlock), 0, st, X, M, L, rs, Gp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t count = (int64_t)L * L;
-    hipLaunchKernelGGL(gram_sum_kernel, dim3((unsigned)((count + kBlock - 1) / kBlock)), dim3(kBlock),
-                       0, st, Gp, gs, count, G);
+    hipLaunchKernelGGL(gram_sum_kernel, dim3((unsigned)((count + 63) / 64)), dim3(kBlock), 0, st, Gp, gs,
+                       L, G);
     return hipGetLastError();
   };
   // out32 (M x L fp32, may be null) and out16 (L x M binary16, transposed, may be null) =
@@ -1161,8 +1216,8 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
     else
       hipLaunchKernelGGL(chol_inverse_kernel, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock), 0,
-                       st, X, M, L, T, L, out32, (float*)nullptr, out16);
+    hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock),
+                       apply_lds, st, X, M, L, T, L, out32, (float*)nullptr, out16);
     return hipGetLastError();
   };
 
@@ -1191,14 +1246,14 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 1, T, P.sigma);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((m + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
-                     st, Y, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
+  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((m + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock),
+                     apply_lds, st, Y, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 2, T, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock), 0,
-                     st, Q32, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
+  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock),
+                     apply_lds, st, Q32, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
