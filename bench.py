@@ -508,14 +508,15 @@ KERNEL_SUMMARIES = {
                "Product with the quantized weight on the 7 matrices of Llama-2-70B layer 0",
                "hqq_matmul, one call per matrix, M = 1, 4, 16, 512, 4096 rows of X, b2 g32 and "
                "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
-               "(bench.py measure_matmul); hqq_gemv_kernel<b, M rows> for M <= 8, "
-               "hqq_gemm_kernel<b> above."),
+               "(bench.py measure_matmul); hqq_gemv_packed_kernel<b, M rows, weight rows per "
+               "wave> for M <= 8, hqq_gemm_kernel<b> above."),
     "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
                 "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
-                "hqq_lowrank (residual_kernel, gemm16_kernel split-K products over the binary16 "
-                "Delta W, split_sum_kernel, gram_kernel + gram_sum_kernel, chol_inverse_kernel "
-                "in the power steps, jacobi_kernel for the final orthonormalization and SVD, "
-                "transform/apply kernels), "
+                "hqq_lowrank (residual_kernel; gemm16_kernel split-K products over the binary16 "
+                "Delta W and split_sum_kernel; gram_kernel + gram_sum_kernel; "
+                "chol_inverse_small_kernel, the Cholesky QR of the power steps and of the two "
+                "final orthonormalization passes; syev_kernel, the tridiagonal eigensolver of "
+                "B_m B_m^T; transform/apply kernels), "
                 "oversample 32, 4 power steps, b2 g32 and b4 g64 weights from hqq_quantize, "
                 "1 warm-up + 2 timed calls per matrix, plus the quantization and the quality "
                 "check (bench.py measure_lowrank)."),
