@@ -332,7 +332,8 @@ int hqq_residual(const void* W_f16, const void* packed_codes, const void* scale_
  * weight.  Reading: the truncated SVD is computed by randomized subspace iteration with
  * a caller-supplied Gaussian test matrix Omega (width l = rank + oversample columns):
  * Y = Delta W Omega; power_iters times Y <- Delta W basis(Delta W^T basis(Y)), where
- * basis() is a well-conditioned basis of the column space (shifted Cholesky QR); then
+ * basis() is the Gram-Schmidt basis of the column space (Cholesky QR of the Gram matrix,
+ * nearly dependent columns dropped); then
  * Q = orth(Y) with orthonormal columns, and the SVD of Q^T Delta W gives U = Q U~, Sigma,
  * V.  The accuracy against the exact SVD is set by oversample and power_iters (the
  * quantization error has a flat spectrum, so the exact rank-r subspace is itself nearly
