@@ -368,13 +368,13 @@ PEAK_MFMA_F16 = 2.5e15  # dense fp16 matrix-core peak of the MI355X
 
 
 def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
-                   rows=(1, 4, 16, 512, 4096)):
+                   rows=(1, 4, 16, 64, 512, 4096)):
     """The product with the quantized weight (hqq_matmul) over the given matrices, each
     quantized with every setting: Y = X Q^-1(W_q)^T with random binary16 X of M rows and
     binary16 Y, one call per matrix, HIP events on the launch stream.  Algorithmic HBM
     bytes per call: codes N K b/8 + s and z 4 N K/g + X 2 M K + Y 2 M N; algorithmic
-    flops 2 M N K.  Decode rows (M <= 8) are reported against the HBM peak, the others
-    against the dense fp16 matrix-core peak (and their HBM rate).  The 7 launches of a
+    flops 2 M N K.  Both rates are reported for every M: the per-row (M <= 8) and skinny
+    (M <= 64) paths are bound by HBM, the tiled one by the dense fp16 matrix-core peak.  The 7 launches of a
     pass are captured in a HIP graph and replayed between the events (no host launch
     gaps; the graph holds no memset node)."""
     out = {"entry_point": "hqq_matmul", "matrices": [list(W.shape) for W in Ws],
@@ -420,7 +420,8 @@ def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
             nbytes = sum(W.numel() * nb / 8 + W.numel() // g * 4 + 2 * M * W.shape[1] +
                          2 * M * W.shape[0] for W in Ws)
             flops = sum(2.0 * M * W.numel() for W in Ws)
-            row = {"M": M, "path": "gemv" if M <= 8 else "mfma", "ms": round(ms, 4),
+            path = "gemv" if M <= 8 else ("mfma_skinny" if M <= 64 else "mfma")
+            row = {"M": M, "path": path, "ms": round(ms, 4),
                    "hbm_GBs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
                    "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4),
                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -506,10 +507,11 @@ KERNEL_SUMMARIES = {
              "largest matrix alone (bench.py measure_meta)."),
     "matmul": ("_gem", "hqq_matmul_llama70b_layer0.md",
                "Product with the quantized weight on the 7 matrices of Llama-2-70B layer 0",
-               "hqq_matmul, one call per matrix, M = 1, 4, 16, 512, 4096 rows of X, b2 g32 and "
+               "hqq_matmul, one call per matrix, M = 1, 4, 16, 64, 512, 4096 rows of X, b2 g32 and "
                "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
                "(bench.py measure_matmul); hqq_gemv_packed_kernel<b, M rows, weight rows per "
-               "wave> for M <= 8, hqq_gemm_kernel<b> above."),
+               "wave> for M <= 8, hqq_skinny_kernel<b, 16-row blocks of X> for M <= 64, "
+               "hqq_gemm_kernel<b> above."),
     "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
                 "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
                 "hqq_lowrank (residual_kernel; gemm16_kernel split-K products over the binary16 "

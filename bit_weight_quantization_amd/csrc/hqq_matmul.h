@@ -18,8 +18,10 @@ struct MatmulParams {
   int out_f32;
 };
 
-// Rows of X up to which the wavefront-per-row kernel is used (above: the MFMA kernel).
+// Rows of X up to which the wavefront-per-row kernel is used, and up to which the
+// skinny matrix-core kernel is used above that (then the tiled matrix-core kernel).
 constexpr int kGemvMaxRows = 8;
+constexpr int kSkinnyMaxRows = 64;
 
 hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream);
 

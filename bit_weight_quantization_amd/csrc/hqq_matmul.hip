@@ -12,6 +12,9 @@
 //     taken on packed binary16 pairs with v_dot2_f32_f16 (one to four weight rows per
 //     wavefront); 3-bit codes (which straddle bytes) use a wavefront per row and fp32
 //     arithmetic.  Bound by HBM reads of the codes.
+//   * 9 to 64 rows: a block of eight wavefronts per 16 or 32 weight rows splits K;
+//     each lane decodes its codes straight into the B operand of v_mfma_f32_16x16x32_f16
+//     (no LDS staging), so every weight is read and dequantized once per call.
 //   * more rows (prefill): 128 x 128 output tiles per block of four wavefronts (64 x 64
 //     each, 2 x 2 tiles of v_mfma_f32_32x32x16_f16); per 64-wide step of K the block
 //     stages the X tile in LDS and dequantizes the weight tile once into LDS as binary16
@@ -487,6 +490,169 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
   }
 }
 
+// ----------------------------------------------------------- skinny GEMM --
+
+typedef float float4_t __attribute__((ext_vector_type(4)));
+constexpr int kSkinnyWaves = 8;  // wavefronts per block, splitting K
+
+// Few rows of X (8 < M <= 16 MT): a block of kSkinnyWaves wavefronts over 16 NW weight
+// rows; the wavefronts take consecutive shares of the 256-wide blocks of K and their
+// partial tiles are added in LDS in a fixed order.  Lane l = j + 16 kq (j < 16, kq < 4)
+// holds, per block at k0, the 64 codes k0 + 64 kq .. + 64 of weight rows n0 + 16 w + j
+// (the four lanes of a row read one contiguous 128-byte line at 4 bits) and the same 64
+// elements of X rows 16 t + j; the next block's codes, s and z are loaded before this
+// block's arithmetic.  MFMA step (h, s) (v_mfma_f32_16x16x32_f16) takes elements
+// 32 h + 8 s .. + 8 of every lane's slice: the instruction's k index 8 kq + e stands for
+// the real k0 + 64 kq + 32 h + 8 s + e on both operands, so the product is the same sum
+// in another order.  The weight enters as binary16 exactly as in the large-M kernel
+// (s*q - s*z in fp32, one rounding, then to binary16).  C: lane j + 16 (i / 4), element
+// i % 4 holds row i (of the 16 X rows), column j.
+template <int NB, int MT, int NW>
+__global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const MatmulParams P) {
+  __shared__ float red[kSkinnyWaves][MT][NW][4][kWave];
+  const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int j = lane & 15, kq = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NW;
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K >> P.group_shift;
+  const int g2 = P.group_size == 16 ? 1 : 0;
+  const int64_t nblk = (P.K + 255) >> 8;
+  const int64_t c0 = wid * nblk / kSkinnyWaves, c1 = (wid + 1) * nblk / kSkinnyWaves;
+  float4_t acc[MT][NW];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc[t][w] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  // the weight side of block c: per 32-code half h of the lane's slice, the codes and
+  // the raw binary16 s, z of both 16-code halves (s = 0 where nothing is loaded)
+  struct Wt {
+    uint32_t cw[2][NW][NB];
+    uint16_t s16[2][NW][2], z16[2][NW][2];
+  };
+  auto load_weights = [&](int64_t c, Wt& o) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t kl = (c << 8) + 64 * kq + 32 * h;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int64_t n = n0 + 16 * w + j;
+        const bool ok = kl < P.K && n < P.N;
+        const int64_t nn = ok ? n : 0, kk = ok ? kl : 0;  // a valid address when unused
+        load_codes32<NB>(P.packed + nn * row_bytes + (kk >> 5) * (4 * NB), o.cw[h][w]);
+        const int64_t gi = nn * gpr + (kk >> P.group_shift);
+        o.s16[h][w][0] = ok ? P.scale16[gi] : (uint16_t)0;
+        o.z16[h][w][0] = P.zero16[gi];
+        o.s16[h][w][1] = ok ? P.scale16[gi + g2] : (uint16_t)0;
+        o.z16[h][w][1] = P.zero16[gi + g2];
+      }
+    }
+  };
+  Wt cur, nxt;
+  if (c0 < c1) load_weights(c0, nxt);
+  for (int64_t c = c0; c < c1; ++c) {
+    cur = nxt;
+    if (c + 1 < c1) load_weights(c + 1, nxt);  // in flight during this block's arithmetic
+    // X rows 16 t + j at the lane's 64 elements (both halves loaded together up to 32
+    // rows; 64 rows load each half before its use, registers allowing)
+    constexpr int XH = MT <= 2 ? 2 : 1;
+    uint4 xa[XH][MT][4];
+    auto load_x = [&](int h, uint4 (&xr)[MT][4]) {
+      const int64_t kl = (c << 8) + 64 * kq + 32 * h;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int64_t m = 16 * t + j;
+        if (kl < P.K && m < P.M) {
+          const uint4* xp = reinterpret_cast<const uint4*>(P.X + m * P.K + kl);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[t][i] = xp[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[t][i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    };
+    if constexpr (XH == 2) {
+      load_x(0, xa[0]);
+      load_x(1, xa[XH - 1]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float sc[NW][2], sz[NW][2];
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const float sv = h2f(cur.s16[h][w][q]);
+          sc[w][q] = sv;
+          sz[w][q] = sv * h2f(cur.z16[h][w][q]);  // exact
+        }
+      if constexpr (XH == 1) load_x(h, xa[0]);
+      const uint4 (&xr)[MT][4] = xa[XH == 2 ? h : 0];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        half8_t bf[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int q = st >> 1;  // codes 16 .. 31 of the half: second group when g = 16
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float w0 = __builtin_fmaf(sc[w][q], (float)code_at<NB>(cur.cw[h][w], 8 * st + e), -sz[w][q]);
+            const float w1 =
+                __builtin_fmaf(sc[w][q], (float)code_at<NB>(cur.cw[h][w], 8 * st + e + 1), -sz[w][q]);
+            const half2_t hv = __builtin_convertvector((float2_t){w0, w1}, half2_t);
+            bf[w][e] = hv[0];
+            bf[w][e + 1] = hv[1];
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const half8_t af = __builtin_bit_cast(half8_t, xr[t][st]);
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            acc[t][w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[w], acc[t][w], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wid][t][w][v][lane] = acc[t][w][v];
+  __syncthreads();
+  // wavefront wid writes the tiles (t, w) with (t NW + w) % kSkinnyWaves == wid, adding
+  // the wavefronts' parts in order
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if ((t * NW + w) % kSkinnyWaves != wid) continue;
+      const int64_t n = n0 + 16 * w + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = red[0][t][w][v][lane];
+#pragma unroll
+        for (int u = 1; u < kSkinnyWaves; ++u) y += red[u][t][w][v][lane];
+        const int64_t m = 16 * t + 4 * kq + v;
+        if (m < P.M && n < P.N) {
+          if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = y;
+          else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)y;
+        }
+      }
+    }
+}
+
+template <int NB, int MT>
+void launch_skinny(const MatmulParams& P, hipStream_t st) {
+  const dim3 block(kSkinnyWaves * kWave);
+  if (P.N >= 4096)  // 32 weight rows per block where there are enough rows
+    hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, 2>), dim3((unsigned)((P.N + 31) / 32)), block, 0, st, P);
+  else
+    hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, 1>), dim3((unsigned)((P.N + 15) / 16)), block, 0, st, P);
+}
+
 template <int NB>
 hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
   if constexpr (NB != 3) {  // packed binary16 codes (3-bit codes straddle bytes)
@@ -497,6 +663,12 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
       if (P.N >= 4096) return launch_gemv_packed<NB, 2>(P, st);
       return launch_gemv_packed<NB, 1>(P, st);
     }
+  }
+  if (P.M > kGemvMaxRows && P.M <= kSkinnyMaxRows) {
+    if (P.M <= 16) launch_skinny<NB, 1>(P, st);
+    else if (P.M <= 32) launch_skinny<NB, 2>(P, st);
+    else launch_skinny<NB, 4>(P, st);
+    return hipGetLastError();
   }
   if (P.M <= kGemvMaxRows) {
     int64_t blocks = (P.N + kBlock / kWave - 1) / (kBlock / kWave);  // a wavefront per row

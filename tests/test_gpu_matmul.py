@@ -93,7 +93,8 @@ def _bound(X, codes, s, z, g, gemv, out_f32, y):
 def test_exact_products_all_paths(hq, nbits, g):
     rng = np.random.default_rng(nbits * 100 + g)
     shapes = [(1, 7, 128), (2, 3, 256), (3, 128, 64 if g <= 64 else 128), (5, 300, 256),
-              (8, 129, 384), (9, 128, 128), (16, 257, 256), (130, 300, 512), (257, 64, 1024)]
+              (8, 129, 384), (9, 128, 128), (16, 257, 256), (20, 33, 160 if g <= 32 else 256),
+              (33, 70, 256), (64, 129, 384), (130, 300, 512), (257, 64, 1024)]
     for M, N, K in shapes:
         if K % g:
             continue
@@ -111,7 +112,7 @@ def test_exact_products_all_paths(hq, nbits, g):
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32), (3, 64), (8, 32)])
 def test_general_inputs_within_the_bound(hq, nbits, g):
     rng = np.random.default_rng(nbits + 7 * g)
-    for M in (1, 4, 8, 24, 200):
+    for M in (1, 4, 8, 24, 40, 64, 200):
         N, K = 160, 1024
         codes, packed, s, z = _weight(N, K, nbits, g, seed=M + 1000)
         X = np.asarray(rng.standard_normal((M, K)), np.float16)
@@ -128,15 +129,16 @@ def test_general_inputs_within_the_bound(hq, nbits, g):
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32)])
 def test_llama70b_layer_shapes_sampled(hq, nbits, g):
     """The 7 weight shapes of a Llama-2-70B layer at full size (N x K = 8192 x 8192,
-    1024 x 8192, 28672 x 8192, 8192 x 28672), decode (M = 1) and prefill (M = 512)
-    activations; outputs checked on sampled weight rows and activation rows."""
+    1024 x 8192, 28672 x 8192, 8192 x 28672), decode (M = 1), small-batch (M = 16, 64) and
+    prefill (M = 512) activations; outputs checked on sampled weight rows and activation
+    rows."""
     rng = np.random.default_rng(70 + nbits)
     for N, K in [(8192, 8192), (1024, 8192), (28672, 8192), (8192, 28672)]:
         codes, packed, s, z = _weight(N, K, nbits, g, seed=N + K + nbits)
         rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 46, replace=False)]))
         bpr = K * nbits // 8
         sub_packed = packed.reshape(N, bpr)[rows].ravel()
-        for M in (1, 512):
+        for M in (1, 16, 64, 512):
             X = np.asarray(rng.standard_normal((M, K)) * 0.5, np.float16)
             Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
             ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 6), replace=False)]))
