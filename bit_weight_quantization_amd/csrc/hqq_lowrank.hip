@@ -817,26 +817,32 @@ constexpr int kCholWaves = kCholThreads / kWave;
 // Widths up to kLdsWidth (chol_inverse_small_kernel): the matrix lives in registers, the
 // 32 x 32 threads owning rows ti + 32 a and columns tj + 32 b (a, b < L / 32); step k
 // broadcasts row k through LDS (one barrier) and every thread updates its entries.  The
-// rows of D U stay in LDS for the back substitution, whose step k broadcasts row k of
-// U^-1 through a double-buffered LDS row.  Wider (chol_inverse_kernel): the matrices
-// live in global memory (Ag, the Gram matrix, overwritten, and Xg, scratch), waves run
-// over rows and lanes along them.  One block.
+// same eliminations applied to the identity, kept below the diagonal, leave L^-1 there
+// (G = L D L^T, U = L^T), so no back substitution is needed.  Wider
+// (chol_inverse_kernel): the matrices live in global memory (Ag, the Gram matrix,
+// overwritten, and Xg, scratch), waves run over rows and lanes along them.  One block.
 __global__ __launch_bounds__(kGrid * kGrid) void chol_inverse_small_kernel(const double* __restrict__ Ag,
                                                                           int L,
                                                                           float* __restrict__ T) {
-  __shared__ double R[kLdsWidth * kLdsWidth];  // row k: row k of D U once step k starts
-  __shared__ double xrow[2][kLdsWidth];
+  __shared__ double R[kLdsWidth * kLdsWidth];  // row k: the matrix's row k when step k starts
   __shared__ double diag[kLdsWidth], piv[kLdsWidth];
   const int t = threadIdx.x, ti = t / kGrid, tj = t % kGrid;
   const int nb = L / kGrid;  // entries per thread along rows and columns
+  // m[i][j]: on and above the diagonal the matrix being eliminated (rows of D U once
+  // final); below it the eliminations applied to the identity, i.e. L^-1 (unit diagonal
+  // implied) for G = L D L^T
   double a[kSmallBlocks][kSmallBlocks];
 #pragma unroll
   for (int p = 0; p < kSmallBlocks; ++p)
 #pragma unroll
-    for (int q = 0; q < kSmallBlocks; ++q)
-      a[p][q] = (p < nb && q < nb) ? Ag[(ti + kGrid * p) * L + tj + kGrid * q] : 0.0;
+    for (int q = 0; q < kSmallBlocks; ++q) {
+      const int i = ti + kGrid * p, j = tj + kGrid * q;
+      a[p][q] = (p < nb && q < nb && j >= i) ? Ag[i * L + j] : 0.0;
+    }
   for (int i = t; i < L; i += kGrid * kGrid) diag[i] = Ag[i * L + i];
-  // step k: a_ij -= a_ki a_kj / d_k for k < i, k < j (entries below the diagonal too)
+  // step k: rows i > k lose l_ik times row k, l_ik = m_ki / d_k: in the upper part
+  // (j >= i) the elimination, in the lower part (j < k) and at j = k (the identity's 1)
+  // the same operation on the identity
   for (int k = 0; k < L; ++k) {
     if (ti == k % kGrid) {  // owners of row k publish it
 #pragma unroll
@@ -862,56 +868,30 @@ __global__ __launch_bounds__(kGrid * kGrid) void chol_inverse_small_kernel(const
 #pragma unroll
       for (int p = 0; p < kSmallBlocks; ++p)
 #pragma unroll
-        for (int q = 0; q < kSmallBlocks; ++q)
-          if (ti + kGrid * p > k && tj + kGrid * q > k) a[p][q] -= fi[p] * rj[q];
+        for (int q = 0; q < kSmallBlocks; ++q) {
+          const int i = ti + kGrid * p, j = tj + kGrid * q;
+          const double r = j == k ? 1.0 : ((j >= i || j < k) ? rj[q] : 0.0);
+          if (i > k) a[p][q] -= fi[p] * r;
+        }
     }
   }
   for (int i = t; i < L; i += kGrid * kGrid) {
     const double d = R[i * L + i];
     piv[i] = d > 0x1p-16 * diag[i] ? 1.0 / d : 0.0;
   }
-  // X = U^-1 by back substitution on U X = I (u_ik = r_ik / d_i): step k publishes row k
-  // of X (final) and rows i < k lose u_ik times it
-#pragma unroll
-  for (int p = 0; p < kSmallBlocks; ++p)
-#pragma unroll
-    for (int q = 0; q < kSmallBlocks; ++q) a[p][q] = (ti + kGrid * p == tj + kGrid * q) ? 1.0 : 0.0;
   __syncthreads();
-  for (int k = L - 1; k > 0; --k) {
-    double* xr = xrow[k & 1];
-    if (ti == k % kGrid) {
-#pragma unroll
-      for (int q = 0; q < kSmallBlocks; ++q)
-        if (q < nb) {
-          double v = a[0][q];
-#pragma unroll
-          for (int p = 1; p < kSmallBlocks; ++p)
-            if (p == k / kGrid) v = a[p][q];
-          xr[tj + kGrid * q] = v;
-        }
-    }
-    __syncthreads();
-    double ui[kSmallBlocks], xj[kSmallBlocks];
-#pragma unroll
-    for (int p = 0; p < kSmallBlocks; ++p) {
-      const int i = ti + kGrid * p;
-      ui[p] = (p < nb && i < k) ? R[i * L + k] * piv[i] : 0.0;
-      xj[p] = p < nb ? xr[tj + kGrid * p] : 0.0;
-    }
-#pragma unroll
-    for (int p = 0; p < kSmallBlocks; ++p)
-#pragma unroll
-      for (int q = 0; q < kSmallBlocks; ++q)
-        if (tj + kGrid * q >= k) a[p][q] -= ui[p] * xj[q];
-  }
-  // T = X D^-1/2, column j scaled by 1 / sqrt(d_j), zero for dropped rows and columns
+  // T = U^-1 D^-1/2 = (L^-1)^T D^-1/2: T[c][r] = m[r][c] / sqrt(d_r) for c < r, 1 / sqrt(d_r)
+  // at c = r, zero for dropped rows and columns (the thread owning m[r][c] writes it)
 #pragma unroll
   for (int p = 0; p < kSmallBlocks; ++p)
 #pragma unroll
     for (int q = 0; q < kSmallBlocks; ++q) {
-      const int i = ti + kGrid * p, j = tj + kGrid * q;
-      if (p < nb && q < nb)
-        T[i * L + j] = (piv[i] != 0.0 && piv[j] != 0.0) ? (float)(a[p][q] * __builtin_sqrt(piv[j])) : 0.f;
+      const int r = ti + kGrid * p, c = tj + kGrid * q;
+      if (p < nb && q < nb) {
+        const bool keep = piv[r] != 0.0 && piv[c] != 0.0 && c <= r;
+        const double x = c == r ? 1.0 : a[p][q];
+        T[c * L + r] = keep ? (float)(x * __builtin_sqrt(piv[r])) : 0.f;
+      }
     }
 }
 
