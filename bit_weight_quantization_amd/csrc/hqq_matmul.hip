@@ -358,13 +358,34 @@ template <int NB>
 __device__ __forceinline__ void dequant32(const uint32_t (&w)[NB], float s0, float sz0, float s1,
                                           float sz1, uint4 (&out)[4]) {
   uint32_t h[16];
+  if constexpr (NB == 3) {
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const float s = j < 8 ? s0 : s1;
-    const float sz = j < 8 ? sz0 : sz1;
-    const float w0 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j), -sz);
-    const float w1 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j + 1), -sz);
-    h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+    for (int j = 0; j < 16; ++j) {
+      const float s = j < 8 ? s0 : s1;
+      const float sz = j < 8 ? sz0 : sz1;
+      const float w0 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j), -sz);
+      const float w1 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j + 1), -sz);
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+    }
+  } else {  // the codes as exact binary16 pairs, converted inside the fp32 FMA (v_fma_mix_f32)
+    constexpr int HW = NB / 2;  // words per 16 codes
+    CodePairs<NB> cp[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t ws[HW];
+#pragma unroll
+      for (int i = 0; i < HW; ++i) ws[i] = w[hh * HW + i];
+      cp[hh].from(ws);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float s = j < 8 ? s0 : s1;
+      const float sz = j < 8 ? sz0 : sz1;
+      const half2_t qq = cp[j >> 3].q[j & 7];
+      const float w0 = __builtin_fmaf(s, (float)qq[0], -sz);
+      const float w1 = __builtin_fmaf(s, (float)qq[1], -sz);
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+    }
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
@@ -589,6 +610,21 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
         }
       if constexpr (XH == 1) load_x(h, xa[0]);
       const uint4 (&xr)[MT][4] = xa[XH == 2 ? h : 0];
+      // the 32 codes of each row as exact binary16 pairs (byte-aligned widths); 3-bit
+      // codes are extracted one by one
+      constexpr int HW = NB == 3 ? 1 : NB / 2;  // words per 16 codes
+      CodePairs<NB == 3 ? 2 : NB> cpa[NW][2];
+      if constexpr (NB != 3) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            uint32_t ws[HW];
+#pragma unroll
+            for (int i = 0; i < HW; ++i) ws[i] = cur.cw[h][w][hh * HW + i];
+            cpa[w][hh].from(ws);
+          }
+      }
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         half8_t bf[NW];
@@ -597,9 +633,17 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
           const int q = st >> 1;  // codes 16 .. 31 of the half: second group when g = 16
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const float w0 = __builtin_fmaf(sc[w][q], (float)code_at<NB>(cur.cw[h][w], 8 * st + e), -sz[w][q]);
-            const float w1 =
-                __builtin_fmaf(sc[w][q], (float)code_at<NB>(cur.cw[h][w], 8 * st + e + 1), -sz[w][q]);
+            float c0, c1;
+            if constexpr (NB == 3) {
+              c0 = (float)code_at<NB>(cur.cw[h][w], 8 * st + e);
+              c1 = (float)code_at<NB>(cur.cw[h][w], 8 * st + e + 1);
+            } else {
+              const half2_t qq = cpa[w][q].q[((8 * st + e) & 15) >> 1];
+              c0 = (float)qq[0];
+              c1 = (float)qq[1];
+            }
+            const float w0 = __builtin_fmaf(sc[w][q], c0, -sz[w][q]);
+            const float w1 = __builtin_fmaf(sc[w][q], c1, -sz[w][q]);
             const half2_t hv = __builtin_convertvector((float2_t){w0, w1}, half2_t);
             bf[w][e] = hv[0];
             bf[w][e + 1] = hv[1];
