@@ -13,7 +13,8 @@
 // QR of the l x l Gram matrix in fp64 (Q = Y R^-1, with nearly dependent columns
 // dropped): one pass inside the power steps, where only the spanned subspace matters,
 // two for the final orthonormal Q.  The SVD of B_m comes from the eigendecomposition of
-// B_m B_m^T by cyclic Jacobi in fp64 in one block.
+// B_m B_m^T (Householder tridiagonalization, bisection, inverse iteration) in fp64 in one
+// block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
