@@ -346,7 +346,7 @@ hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
 
 // ------------------------------------------------------------------- GEMM --
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kLdsRow = kBK + 8;  // binary16 per LDS row: 144 bytes (16-byte aligned, rows 4 banks apart)
 
 typedef float float2_t __attribute__((ext_vector_type(2)));
@@ -391,76 +391,87 @@ __device__ __forceinline__ void dequant32(const uint32_t (&w)[NB], float s0, flo
   for (int i = 0; i < 4; ++i) out[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
 }
 
-// 128 x 128 output tile per block of four wavefronts (64 x 64 each: 2 x 2 tiles of
-// v_mfma_f32_32x32x16_f16).  K advances in steps of 64: thread t stages row t / 2 of both
-// tiles, elements 32 (t % 2) .. + 32 of the step (the X values as they are, the weight
-// dequantized to binary16).  LDS is double-buffered: the next step's global loads are
-// issued before this step's MFMAs and written to the other buffer after them, with one
-// barrier per step.
-template <int NB>
+// (64 TI) x (64 TJ) output tile per block of four wavefronts (2 x 2 of them, each
+// (32 TI) x (32 TJ): TI x TJ tiles of v_mfma_f32_32x32x16_f16).  K advances in steps of
+// 64: thread t stages rows t / 2 + 128 r of both tiles, elements 32 (t % 2) .. + 32 of the
+// step (the X values as they are, the weight dequantized to binary16).  LDS is
+// double-buffered: the next step's global loads are issued before this step's MFMAs and
+// written to the other buffer after them, with one barrier per step.  Larger TI, TJ read
+// fewer LDS operands per MFMA.
+template <int NB, int TI, int TJ>
 __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) {
-  __shared__ __align__(16) _Float16 As[2][kBM][kLdsRow];
-  __shared__ __align__(16) _Float16 Bs[2][kBN][kLdsRow];
+  constexpr int BM = 64 * TI, BN = 64 * TJ, RA = BM / 128, RB = BN / 128;
+  __shared__ __align__(16) _Float16 As[2][BM][kLdsRow];
+  __shared__ __align__(16) _Float16 Bs[2][BN][kLdsRow];
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
-  const int wm = wid >> 1, wn = wid & 1;  // the wavefront's 64 x 64 quarter of the tile
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int wm = wid >> 1, wn = wid & 1;  // the wavefront's quarter of the tile
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int64_t row_bytes = (P.K >> 3) * NB;
   const int64_t gpr = P.K >> P.group_shift;
   const int g2 = P.group_size == 16 ? 1 : 0;
   const int lr = tid >> 1, lh = tid & 1;
-  const int64_t am = m0 + lr, bn = n0 + lr;
-  const bool a_ok = am < P.M, b_ok = bn < P.N;
-  const uint16_t* xrow = P.X + (a_ok ? am : 0) * P.K;
-  const uint8_t* crow = P.packed + (b_ok ? bn : 0) * row_bytes;
-  const uint16_t* srow = P.scale16 + (b_ok ? bn : 0) * gpr;
-  const uint16_t* zrow = P.zero16 + (b_ok ? bn : 0) * gpr;
 
   // the loader's registers for one step
-  uint4 ar[4];
-  uint32_t cw[NB];
-  uint32_t s16[2], z16[2];
+  uint4 ar[RA][4];
+  uint32_t cw[RB][NB];
+  uint32_t s16[RB][2], z16[RB][2];
   auto load_global = [&](int64_t k0) {
     const int64_t e0 = k0 + 32 * lh;
     const bool in = e0 < P.K;  // K % 64 == 32: the last step's upper half is past the end
-    if (a_ok && in) {
-      const uint4* xp = reinterpret_cast<const uint4*>(xrow + e0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = xp[i];
-    } else {
+    for (int r = 0; r < RA; ++r) {
+      const int64_t am = m0 + lr + 128 * r;
+      if (am < P.M && in) {
+        const uint4* xp = reinterpret_cast<const uint4*>(P.X + am * P.K + e0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < 4; ++i) ar[r][i] = xp[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[r][i] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
     const int64_t ec = in ? e0 : 0;  // a valid address; the values are not used
-    load_codes32<NB>(crow + (ec >> 5) * (4 * NB), cw);
-    const int64_t g0 = ec >> P.group_shift;
-    s16[0] = srow[g0];
-    z16[0] = zrow[g0];
-    s16[1] = srow[g0 + g2];
-    z16[1] = zrow[g0 + g2];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int64_t bn = n0 + lr + 128 * r;
+      const int64_t nn = bn < P.N ? bn : 0;
+      load_codes32<NB>(P.packed + nn * row_bytes + (ec >> 5) * (4 * NB), cw[r]);
+      const int64_t g0 = nn * gpr + (ec >> P.group_shift);
+      s16[r][0] = P.scale16[g0];
+      z16[r][0] = P.zero16[g0];
+      s16[r][1] = P.scale16[g0 + g2];
+      z16[r][1] = P.zero16[g0 + g2];
+    }
   };
   auto store_lds = [&](int buf, int64_t k0) {
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr][32 * lh]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ad[i] = ar[i];
-    uint4 bv[4];
-    if (b_ok && k0 + 32 * lh < P.K) {
-      const float s0 = h2f(s16[0]), s1 = h2f(s16[1]);
-      dequant32<NB>(cw, s0, s0 * h2f(z16[0]), s1, s1 * h2f(z16[1]), bv);  // s*z exact
-    } else {
+    for (int r = 0; r < RA; ++r) {
+      uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr + 128 * r][32 * lh]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bv[i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 4; ++i) ad[i] = ar[r][i];
     }
-    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr][32 * lh]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bd[i] = bv[i];
+    for (int r = 0; r < RB; ++r) {
+      uint4 bv[4];
+      if (n0 + lr + 128 * r < P.N && k0 + 32 * lh < P.K) {
+        const float s0 = h2f(s16[r][0]), s1 = h2f(s16[r][1]);
+        dequant32<NB>(cw[r], s0, s0 * h2f(z16[r][0]), s1, s1 * h2f(z16[r][1]), bv);  // s*z exact
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr + 128 * r][32 * lh]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bd[i] = bv[i];
+    }
   };
 
-  float16_t acc[2][2];
+  float16_t acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -476,17 +487,17 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
-      half8_t af[2], bf[2];
+      half8_t af[TI], bf[TJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * 64 + i * 32 + (lane & 31)][kk]);
+      for (int i = 0; i < TI; ++i)
+        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * (BM / 2) + i * 32 + (lane & 31)][kk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][wn * 64 + j * 32 + (lane & 31)][kk]);
+      for (int j = 0; j < TJ; ++j)
+        bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][wn * (BN / 2) + j * 32 + (lane & 31)][kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if (more) store_lds(buf ^ 1, k0 + kBK);  // last read in the previous step, before its barrier
@@ -495,13 +506,13 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 
   // C tile (i, j): lane l, element v holds row 8 (v / 4) + 4 (l / 32) + v % 4, col l % 32
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < TI; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t m = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < P.M && n < P.N) {
           if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = acc[i][j][v];
           else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)acc[i][j][v];
@@ -724,8 +735,10 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
     else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 4>), grid, block, 0, st, P);
     else hipLaunchKernelGGL((hqq_gemv_kernel<NB, 8>), grid, block, 0, st, P);
   } else {
-    const dim3 grid((unsigned)((P.N + kBN - 1) / kBN), (unsigned)((P.M + kBM - 1) / kBM));
-    hipLaunchKernelGGL(hqq_gemm_kernel<NB>, grid, dim3(kBlock), 0, st, P);
+    // 128 x 128 tiles: two blocks per CU (a 256 x 128 tile fits one, and one wavefront
+    // per SIMD leaves the global loads' latency exposed)
+    const dim3 grid((unsigned)((P.N + 127) / 128), (unsigned)((P.M + 127) / 128));
+    hipLaunchKernelGGL((hqq_gemm_kernel<NB, 2, 2>), grid, dim3(kBlock), 0, st, P);
   }
   return hipGetLastError();
 }

@@ -109,6 +109,25 @@ def test_exact_products_all_paths(hq, nbits, g):
     _say(f"b{nbits} g{g}: exact on {len(shapes)} shapes, fp32 and binary16 outputs")
 
 
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 32), (8, 128)])
+def test_exact_products_large_tiles(hq, nbits, g):
+    """A large ragged product on the matrix-core kernel (M = 1040 and N = 16500, 645+
+    tiles, ragged against 128 and 256): bit-exact on exact inputs, checked on sampled
+    weight rows (every activation row)."""
+    rng = np.random.default_rng(nbits * 7 + g)
+    M, N, K = 1040, 16500, 256
+    codes, packed, s, z = _weight(N, K, nbits, g, seed=N + nbits, exact=True)
+    X = rng.integers(-2, 3, (M, K)).astype(np.float16)
+    rows = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.choice(N, 36, replace=False)]))
+    bpr = K * nbits // 8
+    sub_packed = packed.reshape(N, bpr)[rows].ravel()
+    ref = oracle.hqq_matmul(X, sub_packed, s[rows], z[rows], len(rows), nbits, g)
+    Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
+    bad = np.argwhere(Y[:, rows] != ref)
+    assert bad.size == 0, (bad[:5],)
+    _say(f"b{nbits} g{g}: {M}x{N}x{K} exact on {len(rows)} sampled weight rows")
+
+
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 32), (3, 64), (8, 32)])
 def test_general_inputs_within_the_bound(hq, nbits, g):
     rng = np.random.default_rng(nbits + 7 * g)
