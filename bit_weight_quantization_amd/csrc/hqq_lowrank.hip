@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "hqq_internal.h"
 #include "hqq_lowrank.h"
 
@@ -825,62 +827,83 @@ constexpr int kCholWaves = kCholThreads / kWave;
 __global__ __launch_bounds__(kGrid * kGrid) void chol_inverse_small_kernel(const double* __restrict__ Ag,
                                                                           int L,
                                                                           float* __restrict__ T) {
-  __shared__ double R[kLdsWidth * kLdsWidth];  // row k: the matrix's row k when step k starts
-  __shared__ double diag[kLdsWidth], piv[kLdsWidth];
+  // R row k: the matrix's row k when step k starts, with 1 (the identity's entry) in
+  // place of the pivot d_k; rinv[k] = 1 / d_k, 0 for a dropped column
+  __shared__ double R[kLdsWidth * kLdsWidth];
+  __shared__ double rinv[kLdsWidth];
   const int t = threadIdx.x, ti = t / kGrid, tj = t % kGrid;
   const int nb = L / kGrid;  // entries per thread along rows and columns
   // m[i][j]: on and above the diagonal the matrix being eliminated (rows of D U once
   // final); below it the eliminations applied to the identity, i.e. L^-1 (unit diagonal
   // implied) for G = L D L^T
   double a[kSmallBlocks][kSmallBlocks];
+  double thr[kSmallBlocks];  // threads with ti = tj: 2^-16 g_ii of their diagonal entries
 #pragma unroll
-  for (int p = 0; p < kSmallBlocks; ++p)
+  for (int p = 0; p < kSmallBlocks; ++p) {
 #pragma unroll
     for (int q = 0; q < kSmallBlocks; ++q) {
       const int i = ti + kGrid * p, j = tj + kGrid * q;
       a[p][q] = (p < nb && q < nb && j >= i) ? Ag[i * L + j] : 0.0;
     }
-  for (int i = t; i < L; i += kGrid * kGrid) diag[i] = Ag[i * L + i];
-  // step k: rows i > k lose l_ik times row k, l_ik = m_ki / d_k: in the upper part
-  // (j >= i) the elimination, in the lower part (j < k) and at j = k (the identity's 1)
-  // the same operation on the identity
-  for (int k = 0; k < L; ++k) {
-    if (ti == k % kGrid) {  // owners of row k publish it
+    thr[p] = 0x1p-16 * a[p][p];
+  }
+  // step k: rows i > k lose l_ik times row k, l_ik = m_ki / d_k, in the upper part (j >= i)
+  // the elimination, in the lower part (j < k) and at j = k (the identity's 1) the same
+  // operation on the identity.  Entry (i, k) is assigned -l_ik rather than updated, and
+  // lower entries k < j < i take meaningless updates until step j assigns them: row k of
+  // the identity's image is zero there, so nothing read later depends on them.  Finished
+  // entries (rows <= k) are never read again, so blocks of rows all <= k skip the step and
+  // rows <= k inside a live block take l = 0.
+  // The step body is instantiated per block KB = k / 32 so that the selects for row and
+  // column k (i > k, j = k) appear only in the block row and column that hold them.
+  int k = 0;
+  auto step = [&](auto kb_const) {
+    constexpr int KB = decltype(kb_const)::value;
+    const int kr = k - KB * kGrid;
+    if (ti == kr) {  // owners of row k publish it
 #pragma unroll
       for (int q = 0; q < kSmallBlocks; ++q)
         if (q < nb) {
-          double v = a[0][q];
-#pragma unroll
-          for (int p = 1; p < kSmallBlocks; ++p)
-            if (p == k / kGrid) v = a[p][q];
+          double v = a[KB][q];
+          if (q == KB && tj == kr) {  // the pivot (ti = tj here)
+            rinv[k] = v > thr[KB] ? recip(v) : 0.0;
+            v = 1.0;
+          }
           R[k * L + tj + kGrid * q] = v;
         }
     }
     __syncthreads();
-    const double d = R[k * L + k];
-    const double inv = d > 0x1p-16 * diag[k] ? 1.0 / d : 0.0;
-    if (inv != 0.0) {
-      double fi[kSmallBlocks], rj[kSmallBlocks];
+    // every read of the step at once (k L + 95 stays inside R for L <= kLdsWidth)
+    const double inv = rinv[k];
+    double rj[kSmallBlocks], rk[kSmallBlocks];
 #pragma unroll
-      for (int p = 0; p < kSmallBlocks; ++p) {
-        fi[p] = p < nb ? R[k * L + ti + kGrid * p] * inv : 0.0;
-        rj[p] = p < nb ? R[k * L + tj + kGrid * p] : 0.0;
-      }
-#pragma unroll
-      for (int p = 0; p < kSmallBlocks; ++p)
-#pragma unroll
-        for (int q = 0; q < kSmallBlocks; ++q) {
-          const int i = ti + kGrid * p, j = tj + kGrid * q;
-          const double r = j == k ? 1.0 : ((j >= i || j < k) ? rj[q] : 0.0);
-          if (i > k) a[p][q] -= fi[p] * r;
-        }
+    for (int q = 0; q < kSmallBlocks; ++q) {
+      rj[q] = R[k * L + tj + kGrid * q];
+      rk[q] = R[k * L + ti + kGrid * q];
     }
+#pragma unroll
+    for (int p = KB; p < kSmallBlocks; ++p) {  // blocks p < KB hold rows <= k only
+      if (p >= nb) continue;
+      double f = rk[p] * inv;
+      if (p == KB) f = ti > kr ? f : 0.0;
+#pragma unroll
+      for (int q = 0; q < kSmallBlocks; ++q) {
+        if (q >= nb) continue;
+        double base = a[p][q];
+        if (q == KB) base = tj == kr ? 0.0 : base;
+        a[p][q] = __builtin_fma(-f, rj[q], base);
+      }
+    }
+  };
+  static_assert(kSmallBlocks == 3, "one instantiation per block of rows");
+  for (; k < L; ++k) {
+    if (k < kGrid)
+      step(std::integral_constant<int, 0>{});
+    else if (k < 2 * kGrid)
+      step(std::integral_constant<int, 1>{});
+    else
+      step(std::integral_constant<int, 2>{});
   }
-  for (int i = t; i < L; i += kGrid * kGrid) {
-    const double d = R[i * L + i];
-    piv[i] = d > 0x1p-16 * diag[i] ? 1.0 / d : 0.0;
-  }
-  __syncthreads();
   // T = U^-1 D^-1/2 = (L^-1)^T D^-1/2: T[c][r] = m[r][c] / sqrt(d_r) for c < r, 1 / sqrt(d_r)
   // at c = r, zero for dropped rows and columns (the thread owning m[r][c] writes it)
 #pragma unroll
@@ -889,9 +912,9 @@ __global__ __launch_bounds__(kGrid * kGrid) void chol_inverse_small_kernel(const
     for (int q = 0; q < kSmallBlocks; ++q) {
       const int r = ti + kGrid * p, c = tj + kGrid * q;
       if (p < nb && q < nb) {
-        const bool keep = piv[r] != 0.0 && piv[c] != 0.0 && c <= r;
+        const bool keep = rinv[r] != 0.0 && rinv[c] != 0.0 && c <= r;
         const double x = c == r ? 1.0 : a[p][q];
-        T[c * L + r] = keep ? (float)(x * __builtin_sqrt(piv[r])) : 0.f;
+        T[c * L + r] = keep ? (float)(x * __builtin_sqrt(rinv[r])) : 0.f;
       }
     }
 }
