@@ -4,9 +4,11 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,24 +24,40 @@ HEADERS = [os.path.join(CSRC, "hqq_internal.h"), os.path.join(CSRC, "hqq_solver.
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     # packed fp32 VALU forms stay off: every fp32 op is a plain single-lane op
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# hipcc's host pass warns that it does not know the packed-fp32 feature; that is harmless.
+_NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd: list[str]) -> list[str]:
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if _NOISE not in ln and ln.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    return msgs
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature; that is harmless.
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    """Compile the library (always recompiles) and return its path.  The sources are
+    compiled to objects in parallel, then linked into the shared library."""
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)))
+    with tempfile.TemporaryDirectory(prefix="hqq_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.splitext(os.path.basename(s))[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", s, "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=max(jobs, 1)) as ex:
+            msgs = [m for ms in ex.map(_run, cmds) for m in ms]
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+        if verbose:
+            print(" ".join(link), flush=True)
+        msgs += _run(link)
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(LIB + ".tmp", LIB)

@@ -182,10 +182,12 @@ struct CodePairs {  // the 16 codes of one 16-code block as 8 pairs
 
 // One wavefront per group of R weight rows.  Lane l takes the 32-code chunks l, l + 64,
 // ... of the rows: per chunk it reads 4 NB bytes of codes in each of the R rows and the
-// chunk of X once for all R rows; the next chunk's codes are loaded before the current
-// one is computed, so two chunks' loads are in flight per lane.  Per 16 codes (one
-// group): p = sum of x*q (packed dot products, exact products, fp32 sums) and
-// s (p - z sum x).  The lanes' partial sums are added by a butterfly in fixed order.
+// chunk of X once for all R rows; a step covers U chunks per lane (2 for M <= 2, 1 for
+// more activation rows, whose X chunks fill the registers), all loaded before any is
+// computed.
+// Per 16 codes (one group when g = 16, half of one otherwise): p = sum of x*q (packed
+// dot products, exact products, fp32 sums) and s (p - z sum x).  The lanes' partial sums
+// are added by a butterfly in fixed order.
 template <int NB>
 __device__ __forceinline__ void load_chunk_codes(const uint8_t* cp, uint32_t (&w)[NB]) {
   static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned codes only");
@@ -204,15 +206,17 @@ __device__ __forceinline__ void load_chunk_codes(const uint8_t* cp, uint32_t (&w
 }
 
 // Everything one chunk step of the GEMV reads: the codes of the chunk in each of the R
-// rows, the chunk of each row of X, and the binary16 s and z of the chunk's two halves.
-template <int NB, int MB, int R>
+// rows, the chunk of each row of X, and the binary16 s and z of the chunk's groups (two
+// when g = 16, G16; one otherwise).
+template <int NB, int MB, int R, bool G16>
 struct GemvStage {
+  static constexpr int kGroups = G16 ? 2 : 1;
   uint32_t w[R][NB];
   uint4 x[MB][4];
-  uint32_t s[R][2], z[R][2];
+  uint32_t s[R][kGroups], z[R][kGroups];
 };
 
-template <int NB, int MB, int R>
+template <int NB, int MB, int R, bool G16>
 __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulParams P) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
@@ -233,7 +237,6 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
   }
   const int64_t row_bytes = (P.K >> 3) * NB;
   const int64_t gpr = P.K >> P.group_shift;
-  const int g2 = P.group_size == 16 ? 1 : 0;  // second half of a chunk: next group at g = 16
   const int M = (int)P.M;
   const int nr = P.N - n0 < R ? (int)(P.N - n0) : R;
   const half2_t kOnes = {(_Float16)1.f, (_Float16)1.f};
@@ -253,7 +256,8 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
   for (int m = 0; m < MB; ++m) xrow[m] = P.X + (int64_t)(m < M ? m : M - 1) * P.K;
 
   // chunk c's loads (c < nchunk)
-  auto load = [&](GemvStage<NB, MB, R>& st, int64_t c) {
+  using Stage = GemvStage<NB, MB, R, G16>;
+  auto load = [&](Stage& st, int64_t c) {
     const int64_t k0 = c << 5;
 #pragma unroll
     for (int r = 0; r < R; ++r) load_chunk_codes<NB>(rowp[r] + c * (4 * NB), st.w[r]);
@@ -266,10 +270,11 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
     const int64_t g0 = k0 >> P.group_shift;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      st.s[r][0] = sp[r][g0];
-      st.z[r][0] = zp[r][g0];
-      st.s[r][1] = sp[r][g0 + g2];
-      st.z[r][1] = zp[r][g0 + g2];
+#pragma unroll
+      for (int g = 0; g < Stage::kGroups; ++g) {
+        st.s[r][g] = sp[r][g0 + g];
+        st.z[r][g] = zp[r][g0 + g];
+      }
     }
   };
 
@@ -279,13 +284,7 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[r][m] = 0.f;
 
-  // per step, every load of the chunk is issued before any arithmetic (the scheduling
-  // barrier keeps the compiler from sinking loads next to their first use), so a step
-  // costs one memory round trip, hidden by the other wavefronts of the SIMD
-  for (int64_t c = lane; c < nchunk; c += kWave) {
-    GemvStage<NB, MB, R> cur;
-    load(cur, c);
-    __builtin_amdgcn_sched_barrier(0);
+  auto compute = [&](const Stage& cur, bool valid) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 16-code halves
       uint32_t xw[MB][8];
@@ -307,17 +306,39 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
         for (int i = 0; i < CodePairs<NB>::kWords; ++i) hw[i] = cur.w[r][h * CodePairs<NB>::kWords + i];
         CodePairs<NB> cq;
         cq.from(hw);
-        const float sv = h2f(cur.s[r][h]);
-        const float zv = h2f(cur.z[r][h]);
+        const int g = G16 ? h : 0;
+        const float sv = h2f(cur.s[r][g]);
+        const float zv = h2f(cur.z[r][g]);
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           float p = 0.f;
 #pragma unroll
           for (int j = 0; j < 8; ++j) p = __builtin_amdgcn_fdot2(as_h2(xw[m][j]), cq.q[j], p, false);
-          acc[r][m] = __builtin_fmaf(sv, __builtin_fmaf(-zv, sx[m], p), acc[r][m]);
+          const float v = __builtin_fmaf(sv, __builtin_fmaf(-zv, sx[m], p), acc[r][m]);
+          acc[r][m] = valid ? v : acc[r][m];
         }
       }
     }
+  };
+
+  // Wave-uniform steps of U x 64 chunks: every load of a step (all its chunks) is issued
+  // before any of its arithmetic, behind a scheduling barrier, so a step costs one memory
+  // round trip for U chunks per lane.  Loads and arithmetic are
+  // unconditional (no divergent branch, so the compiler's waits stay per load): a lane
+  // whose chunk is past the end reads the last chunk (all such lanes the same address)
+  // and keeps its sums.
+  constexpr int U = MB <= 2 ? 2 : 1;
+  const int64_t last = nchunk - 1;
+  for (int64_t c0 = 0; c0 < nchunk; c0 += U * kWave) {
+    Stage st[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave + lane;
+      load(st[u], c < last ? c : last);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) compute(st[u], c0 + u * kWave + lane < nchunk);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -333,14 +354,20 @@ __global__ __launch_bounds__(kBlock) void hqq_gemv_packed_kernel(const MatmulPar
   }
 }
 
-template <int NB, int R>
-hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
+template <int NB, int R, bool G16>
+void launch_gemv_packed_g(const MatmulParams& P, hipStream_t st) {
   constexpr int kRowsPerBlock = R * (kBlock / kWave);
   const dim3 grid((unsigned)((P.N + kRowsPerBlock - 1) / kRowsPerBlock)), block(kBlock);
-  if (P.M <= 1) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 1, R>), grid, block, 0, st, P);
-  else if (P.M <= 2) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 2, R>), grid, block, 0, st, P);
-  else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 4, R>), grid, block, 0, st, P);
-  else hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 8, R>), grid, block, 0, st, P);
+  if (P.M <= 1) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 1, R, G16>), grid, block, 0, st, P);
+  else if (P.M <= 2) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 2, R, G16>), grid, block, 0, st, P);
+  else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 4, R, G16>), grid, block, 0, st, P);
+  else hipLaunchKernelGGL((hqq_gemv_packed_kernel<NB, 8, R, G16>), grid, block, 0, st, P);
+}
+
+template <int NB, int R>
+hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
+  if (P.group_size == 16) launch_gemv_packed_g<NB, R, true>(P, st);
+  else launch_gemv_packed_g<NB, R, false>(P, st);
   return hipGetLastError();
 }
 
@@ -527,7 +554,9 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int kSkinnyWaves = 8;  // wavefronts per block, splitting K
 
-// Few rows of X (8 < M <= 16 MT): a block of kSkinnyWaves wavefronts over 16 NW weight
+// Few rows of X (8 < M <= 16 MT), any K (a multiple of 32), any width and group size
+// (hqq_skinny_kernel below covers the common aligned cases with fewer memory accesses):
+// a block of kSkinnyWaves wavefronts over 16 NW weight
 // rows; the wavefronts take consecutive shares of the 256-wide blocks of K and their
 // partial tiles are added in LDS in a fixed order.  Lane l = j + 16 kq (j < 16, kq < 4)
 // holds, per block at k0, the 64 codes k0 + 64 kq .. + 64 of weight rows n0 + 16 w + j
@@ -540,7 +569,7 @@ constexpr int kSkinnyWaves = 8;  // wavefronts per block, splitting K
 // (s*q - s*z in fp32, one rounding, then to binary16).  C: lane j + 16 (i / 4), element
 // i % 4 holds row i (of the 16 X rows), column j.
 template <int NB, int MT, int NW>
-__global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const MatmulParams P) {
+__global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_general_kernel(const MatmulParams P) {
   __shared__ float red[kSkinnyWaves][MT][NW][4][kWave];
   const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15, kq = lane >> 4;
@@ -699,13 +728,245 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
     }
 }
 
+// Few rows of X (8 < M <= 16 MT) for 2-, 4- and 8-bit codes, groups of GS = 5, 6, 7
+// (32, 64, 128 weights), K a multiple of 256 and 16-byte aligned s and z: a block of
+// kSkinnyWaves wavefronts over 16 NW weight rows; the wavefronts take consecutive shares of
+// the 256-wide blocks of K and their partial tiles are added in LDS in a fixed order.
+// Per block of K (k0) the MFMA steps i = 0..7 (v_mfma_f32_16x16x32_f16) take k0 + 32 i +
+// 8 kq .. + 8 in lane j + 16 kq on both operands, the instruction's own k order, so that
+// each X load of a step covers 64 contiguous bytes of 16 rows.  The codes of a step are
+// NB bytes per lane at a stride of 4 NB; a lane instead loads 8 NB contiguous bytes of its
+// row (the codes of steps 2 kq and 2 kq + 1 of all four lanes) and the wavefront
+// transposes them through its own LDS buffer (8-bit pieces are loaded in place).  s and
+// z of the block's groups come in one load per row.  The next block's codes, s and z are
+// loaded before this block's arithmetic; the weight enters the MFMA as in the other
+// kernels (s*q - s*z in fp32, one rounding, binary16).  C: lane j + 16 kq, element v
+// holds X row 16 t + 4 kq + v, weight row n0 + 16 w + j.
+template <int NB, int MT, int NW, int GS>
+__global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const MatmulParams P) {
+  static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
+  static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
+  constexpr bool kStage = NB != 8;        // pieces of NB bytes transposed through LDS
+  constexpr int kRowBytes = 32 * NB + 16;  // a row's 4 x 8 pieces, 16 bytes of padding
+  constexpr int kStageBytes = kStage ? kSkinnyWaves * NW * 16 * kRowBytes : 0;
+  constexpr int kRedBytes = kSkinnyWaves * MT * NW * 4 * kWave * 4;
+  constexpr int kLdsBytes = kStageBytes > kRedBytes ? kStageBytes : kRedBytes;
+  constexpr int kSW = 256 >> GS < 2 ? 1 : (256 >> GS) / 2;  // 32-bit words of s (and z) per block
+  constexpr int XD = 4;                                      // steps of X held at once
+  __shared__ __align__(16) unsigned char lds[kLdsBytes];
+  const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int j = lane & 15, kq = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NW;
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K >> GS;
+  const int64_t nblk = P.K >> 8;
+  const int64_t c0 = wid * nblk / kSkinnyWaves, c1 = (wid + 1) * nblk / kSkinnyWaves;
+  // rows past N (or past M for X) read the last valid one; their results are not stored
+  int64_t wrow[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int64_t n = n0 + 16 * w + j;
+    wrow[w] = n < P.N ? n : P.N - 1;
+  }
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int64_t m = 16 * t + j;
+    xrow[t] = P.X + (m < P.M ? m : P.M - 1) * P.K + 8 * kq;
+  }
+  float4_t acc[MT][NW];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc[t][w] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  struct Wt {
+    uint32_t cw[NW][2 * NB];       // staged: 8 NB bytes of the row from 8 NB kq; else piece i at 2i
+    uint32_t sw[NW][kSW], zw[NW][kSW];  // binary16 s, z of the block's groups
+  };
+  auto load_wt = [&](int64_t c, Wt& o) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint8_t* cp = P.packed + wrow[w] * row_bytes + c * (32 * NB);
+      if constexpr (kStage) {
+        const uint4* p4 = reinterpret_cast<const uint4*>(cp + 8 * NB * kq);
+#pragma unroll
+        for (int h = 0; h < NB / 2; ++h) {
+          const uint4 v = p4[h];
+          o.cw[w][4 * h] = v.x; o.cw[w][4 * h + 1] = v.y; o.cw[w][4 * h + 2] = v.z; o.cw[w][4 * h + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint2 v = *reinterpret_cast<const uint2*>(cp + 32 * i + 8 * kq);
+          o.cw[w][2 * i] = v.x; o.cw[w][2 * i + 1] = v.y;
+        }
+      }
+      const int64_t g0 = wrow[w] * gpr + ((c << 8) >> GS);
+      const uint16_t* sp = P.scale16 + g0;
+      const uint16_t* zp = P.zero16 + g0;
+      if constexpr (kSW == 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(sp), b = *reinterpret_cast<const uint4*>(zp);
+        o.sw[w][0] = a.x; o.sw[w][1] = a.y; o.sw[w][2] = a.z; o.sw[w][3] = a.w;
+        o.zw[w][0] = b.x; o.zw[w][1] = b.y; o.zw[w][2] = b.z; o.zw[w][3] = b.w;
+      } else if constexpr (kSW == 2) {
+        const uint2 a = *reinterpret_cast<const uint2*>(sp), b = *reinterpret_cast<const uint2*>(zp);
+        o.sw[w][0] = a.x; o.sw[w][1] = a.y;
+        o.zw[w][0] = b.x; o.zw[w][1] = b.y;
+      } else {
+        o.sw[w][0] = *reinterpret_cast<const uint32_t*>(sp);
+        o.zw[w][0] = *reinterpret_cast<const uint32_t*>(zp);
+      }
+    }
+  };
+  // the wavefront's LDS rows: [w][row j][kq][step] pieces of NB bytes
+  unsigned char* stage = lds + wid * (NW * 16 * kRowBytes);
+
+  Wt cur, nxt;
+  if (c0 < c1) load_wt(c0, nxt);
+  for (int64_t c = c0; c < c1; ++c) {
+    cur = nxt;
+    const int64_t k0 = c << 8;
+    uint4 xa[XD][MT];
+    auto load_x = [&](int i) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) xa[i % XD][t] = *reinterpret_cast<const uint4*>(xrow[t] + k0 + 32 * i);
+    };
+#pragma unroll
+    for (int i = 0; i < XD - 1; ++i) load_x(i);
+    // the next block's weights (the last block re-reads itself: no branch, so the waits
+    // for this block's loads count exactly)
+    load_wt(c + 1 < c1 ? c + 1 : c, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t cr[NW][2 * NB];  // piece i of the lane's codes: bytes NB i .. of its 8 NB
+    if constexpr (kStage) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        unsigned char* rowp = stage + (w * 16 + j) * kRowBytes;
+        // loaded piece (b, q) = bytes (4 b + q) NB of the lane's 8 NB: step 2 kq + b of lane q
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            unsigned char* dst = rowp + q * (8 * NB) + (2 * kq + b) * NB;
+            const int e = (4 * b + q) * NB;  // byte offset in cur.cw[w]
+            if constexpr (NB == 2)
+              *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(cur.cw[w][e >> 2] >> (8 * (e & 3)));
+            else
+              *reinterpret_cast<uint32_t*>(dst) = cur.cw[w][e >> 2];
+          }
+      }
+      __builtin_amdgcn_wave_barrier();  // LDS accesses of a wavefront execute in order
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint4* src = reinterpret_cast<const uint4*>(stage + (w * 16 + j) * kRowBytes + kq * (8 * NB));
+#pragma unroll
+        for (int h = 0; h < NB / 2; ++h) {
+          const uint4 v = src[h];
+          cr[w][4 * h] = v.x; cr[w][4 * h + 1] = v.y; cr[w][4 * h + 2] = v.z; cr[w][4 * h + 3] = v.w;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int i = 0; i < 2 * NB; ++i) cr[w][i] = cur.cw[w][i];
+    }
+#pragma unroll
+    for (int ip = 0; ip < 4; ++ip) {  // steps 2 ip, 2 ip + 1: 16 codes per row
+      half8_t bf[2][NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        CodePairs<NB> cp;
+        uint32_t ws[CodePairs<NB>::kWords];
+#pragma unroll
+        for (int u = 0; u < CodePairs<NB>::kWords; ++u) ws[u] = cr[w][ip * CodePairs<NB>::kWords + u];
+        cp.from(ws);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int i = 2 * ip + b;
+          const int g = (32 * i) >> GS;  // the step's group within the block
+          const float sv = h2f((cur.sw[w][g >> 1] >> (16 * (g & 1))) & 0xffffu);
+          const float sz = sv * h2f((cur.zw[w][g >> 1] >> (16 * (g & 1))) & 0xffffu);  // exact
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const half2_t qq = cp.q[4 * b + e];
+            const float w0 = __builtin_fmaf(sv, (float)qq[0], -sz);
+            const float w1 = __builtin_fmaf(sv, (float)qq[1], -sz);
+            const half2_t hv = __builtin_convertvector((float2_t){w0, w1}, half2_t);
+            bf[b][w][2 * e] = hv[0];
+            bf[b][w][2 * e + 1] = hv[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int i = 2 * ip + b;
+        if (i + XD - 1 < 8) load_x(i + XD - 1);  // XD - 1 steps ahead
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const half8_t af = __builtin_bit_cast(half8_t, xa[i % XD][t]);
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            acc[t][w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b][w], acc[t][w], 0, 0, 0);
+        }
+      }
+    }
+  }
+  __syncthreads();  // the staging buffers become the reduction buffer
+  float* red = reinterpret_cast<float*>(lds);  // [wave][t][w][v][lane]
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(((wid * MT + t) * NW + w) * 4 + v) * kWave + lane] = acc[t][w][v];
+  __syncthreads();
+  // wavefront wid writes the tiles (t, w) with (t NW + w) % kSkinnyWaves == wid, adding
+  // the wavefronts' parts in order
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if ((t * NW + w) % kSkinnyWaves != wid) continue;
+      const int64_t n = n0 + 16 * w + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float y = red[((t * NW + w) * 4 + v) * kWave + lane];
+#pragma unroll
+        for (int u = 1; u < kSkinnyWaves; ++u) y += red[(((u * MT + t) * NW + w) * 4 + v) * kWave + lane];
+        const int64_t m = 16 * t + 4 * kq + v;
+        if (m < P.M && n < P.N) {
+          if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = y;
+          else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)y;
+        }
+      }
+    }
+}
+
+template <int NB, int MT, int NW>
+void launch_skinny_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
+  const dim3 block(kSkinnyWaves * kWave);
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(P.scale16) | reinterpret_cast<uintptr_t>(P.zero16)) & 15) == 0;
+  if constexpr (NB != 3) {
+    if (P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7) {
+      switch (P.group_shift) {
+        case 5: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 5>), grid, block, 0, st, P); return;
+        case 6: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 6>), grid, block, 0, st, P); return;
+        default: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 7>), grid, block, 0, st, P); return;
+      }
+    }
+  }
+  hipLaunchKernelGGL((hqq_skinny_general_kernel<NB, MT, NW>), grid, block, 0, st, P);
+}
+
 template <int NB, int MT>
 void launch_skinny(const MatmulParams& P, hipStream_t st) {
-  const dim3 block(kSkinnyWaves * kWave);
   if (P.N >= 4096)  // 32 weight rows per block where there are enough rows
-    hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, 2>), dim3((unsigned)((P.N + 31) / 32)), block, 0, st, P);
+    launch_skinny_nw<NB, MT, 2>(P, dim3((unsigned)((P.N + 31) / 32)), st);
   else
-    hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, 1>), dim3((unsigned)((P.N + 15) / 16)), block, 0, st, P);
+    launch_skinny_nw<NB, MT, 1>(P, dim3((unsigned)((P.N + 15) / 16)), st);
 }
 
 template <int NB>

@@ -52,15 +52,18 @@ def _weight(N, K, nbits, g, seed, exact=False):
     return codes, packed, s, z
 
 
-def _run(hq, X, packed, s, z, N, nbits, g, out_f32):
+def _run(hq, X, packed, s, z, N, nbits, g, out_f32, sz_offset=0):
+    """sz_offset binary16 elements of padding in front of s and z (their device pointers
+    then lose 16-byte alignment when it is odd)."""
     M, K = X.shape
     Xd = torch.from_numpy(X.view(np.int16).copy()).view(torch.float16).cuda()
     pd = torch.from_numpy(packed.copy()).cuda()
-    sd = torch.from_numpy(s.view(np.int16).copy()).cuda()
-    zd = torch.from_numpy(z.view(np.int16).copy()).cuda()
+    pad = np.zeros(sz_offset, np.int16)
+    sd = torch.from_numpy(np.concatenate([pad, s.view(np.int16).ravel()])).cuda()
+    zd = torch.from_numpy(np.concatenate([pad, z.view(np.int16).ravel()])).cuda()
     Y = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
-    st = hq.hqq_matmul(Xd.data_ptr(), M, K, pd.data_ptr(), sd.data_ptr(), zd.data_ptr(), N, nbits,
-                       g, Y.data_ptr(), int(out_f32), 0)
+    st = hq.hqq_matmul(Xd.data_ptr(), M, K, pd.data_ptr(), sd.data_ptr() + 2 * sz_offset,
+                       zd.data_ptr() + 2 * sz_offset, N, nbits, g, Y.data_ptr(), int(out_f32), 0)
     assert st == hq.HQQ_OK, hq.hqq_status_string(st)
     torch.cuda.synchronize()
     return Y.cpu().numpy().astype(np.float64)
@@ -107,6 +110,29 @@ def test_exact_products_all_paths(hq, nbits, g):
             bad = np.argwhere(Y != want)
             assert bad.size == 0, (M, N, K, out_f32, bad[:5], Y[tuple(bad[0])], want[tuple(bad[0])])
     _say(f"b{nbits} g{g}: exact on {len(shapes)} shapes, fp32 and binary16 outputs")
+
+
+@pytest.mark.parametrize("nbits", [2, 4, 8])
+def test_exact_products_skinny_paths(hq, nbits):
+    """Small batches (8 < M <= 64) on the matrix-core skinny kernels: K a multiple of 256
+    with 1, 9 (split unevenly over the 8 wavefronts of a block) and 16 blocks of 256, one
+    and two 16-row weight groups per block (N below and above 4096, ragged), every
+    16-row tile count of X (M = 9 .. 64), groups of 32, 64 and 128, and s, z off 16-byte
+    alignment (the general kernel): bit-exact on exact inputs."""
+    rng = np.random.default_rng(400 + nbits)
+    cases = [(9, 100, 256, 32, 0), (16, 300, 2304, 64, 0), (17, 129, 4096, 128, 0),
+             (32, 4100, 2304, 32, 0), (33, 70, 2304, 64, 0), (64, 4097, 512, 128, 0),
+             (40, 200, 4096, 32, 0), (24, 130, 2304, 64, 1), (48, 4100, 768, 32, 3)]
+    for M, N, K, g, off in cases:
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=M + N + K, exact=True)
+        X = rng.integers(-2, 3, (M, K)).astype(np.float16)
+        ref = oracle.hqq_matmul(X, packed, s, z, N, nbits, g)
+        for out_f32 in (1, 0):
+            Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32, sz_offset=off)
+            want = ref if out_f32 else oracle.f16_to_f64(oracle.f64_to_f16(ref))
+            bad = np.argwhere(Y != want)
+            assert bad.size == 0, (M, N, K, g, off, out_f32, bad[:5], Y[tuple(bad[0])], want[tuple(bad[0])])
+        _say(f"b{nbits} M={M} N={N} K={K} g{g} s/z offset {off}: exact")
 
 
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 32), (8, 128)])
