@@ -505,13 +505,14 @@ KERNEL_SUMMARIES = {
              "of the whole stack after the solver, hqq_meta_quantize_batch, both settings, 1 "
              "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the "
              "largest matrix alone (bench.py measure_meta)."),
-    "matmul": ("_gem", "hqq_matmul_llama70b_layer0.md",
+    "matmul": (("_gem", "_skinny"), "hqq_matmul_llama70b_layer0.md",
                "Product with the quantized weight on the 7 matrices of Llama-2-70B layer 0",
                "hqq_matmul, one call per matrix, M = 1, 4, 16, 64, 512, 4096 rows of X, b2 g32 and "
                "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
                "(bench.py measure_matmul); hqq_gemv_packed_kernel<b, M rows, weight rows per "
-               "wave> for M <= 8, hqq_skinny_kernel<b, 16-row blocks of X> for M <= 64, "
-               "hqq_gemm_kernel<b> above."),
+               "wave, g = 16> for M <= 8, hqq_skinny_kernel<b, 16-row blocks of X, 16-row "
+               "weight groups per wavefront, log2 g> for M <= 64, hqq_gemm_kernel<b, 2, 2> "
+               "(128 x 128 tiles) above."),
     "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
                 "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
                 "hqq_lowrank (residual_kernel; gemm16_kernel split-K products over the binary16 "
@@ -539,7 +540,8 @@ def summarize_kernels(which: str, kt_dir: str, out_dir: str, command: str):
     filt, fname, title, desc = KERNEL_SUMMARIES[which]
     rows = []
     for r in csv.DictReader(open(os.path.join(kt_dir, "kt_kernel_stats.csv"))):
-        if filt in r["Name"] and "hqq" in r["Name"]:
+        filts = filt if isinstance(filt, tuple) else (filt,)
+        if any(f in r["Name"] for f in filts) and "hqq" in r["Name"]:
             name = r["Name"].replace("void ", "").replace("(anonymous namespace)::", "")
             name = name.replace("hqq::", "").split("(")[0]
             rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
@@ -551,6 +553,41 @@ def summarize_kernels(which: str, kt_dir: str, out_dir: str, command: str):
     lines += ["", "Command:", "", "```", command, "```", ""]
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, fname), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_counters(dirs: list, out_dir: str, command: str):
+    """Per-kernel averages of rocprofv3 --pmc passes over bench.py --profile-matmul
+    (profiles/hqq_matmul_counters_28672x8192.md)."""
+    import csv
+    import glob
+    import re
+    tab = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            acc = {}
+            for r in csv.DictReader(open(f)):
+                m = re.search(r"(hqq_\w+_kernel<[^>]*>)", r["Kernel_Name"])
+                if not m or "solve" in m.group(1):
+                    continue
+                acc.setdefault(m.group(1), {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+            for k, c in acc.items():
+                for n, v in c.items():
+                    tab.setdefault(k, {})[n] = sum(v) / len(v)
+    names = sorted({n for c in tab.values() for n in c})
+    kernels = sorted(tab)
+    lines = ["# Counters of the product kernels on one 28672 x 8192 b2 g32 weight", "",
+             "hqq_matmul at M = 1, 4 (hqq_gemv_packed_kernel) and M = 16, 64 (hqq_skinny_kernel), "
+             "5 calls each (bench.py --profile-matmul); values per dispatch, averaged. "
+             "GRBM_GUI_ACTIVE counts on every XCD (8 per device).", "",
+             "| counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
+    for n in names:
+        lines.append(f"| {n} | " + " | ".join(f"{tab[k].get(n, float('nan')):.4g}" for k in kernels) + " |")
+    lines += ["", "Command:", "", "```", command, "```", ""]
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_matmul_counters_28672x8192.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
 
@@ -589,17 +626,28 @@ def main():
     ap.add_argument("--profile-meta", action="store_true",
                     help="generate, run the solver once per setting, then only the meta "
                          "quantization measurement (for rocprofv3 runs)")
+    ap.add_argument("--profile-matmul", action="store_true",
+                    help="only the products with one 28672 x 8192 b2 g32 weight at M = 16, 1, "
+                         "4, 64 (5 calls each; for rocprofv3 counter runs)")
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("WHICH", "KT_DIR"),
                     help="write the profiles/ summary of one kernel family (meta, variants) "
                          "from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write profiles/ summaries from rocprofv3 counter and trace output")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write the profiles/ summary of rocprofv3 --pmc passes over "
+                         "--profile-matmul")
     ap.add_argument("--profile-command", default="", help="command recorded in the summary")
     args = ap.parse_args()
 
     if args.summarize_kernels:
         summarize_kernels(args.summarize_kernels[0], args.summarize_kernels[1],
                           os.path.join(ROOT, "profiles"), args.profile_command)
+        return
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, os.path.join(ROOT, "profiles"),
+                           args.profile_command)
         return
 
     if args.summarize_profiles:
@@ -640,6 +688,17 @@ def main():
 
     lib = hq.load_library()
     wl = workloads.WORKLOADS[args.workload]
+    if args.profile_matmul:
+        W = workloads.generate(28672, 8192, wl.dist, 3, dev)
+        q = hq.quantize(W, 2, 32)
+        del W
+        for M in (16, 1, 4, 64):
+            X = torch.randn((M, 8192), device=dev).half()
+            log(f"profile-matmul: 28672 x 8192 b2 g32, M = {M}, 5 calls")
+            for _ in range(5):
+                hq.matmul(X, q, out_f32=True)
+            torch.cuda.synchronize()
+        return
     solver = wl.solver
     mats = list(wl.matrices)
     if args.layers:  # the Llama stacks hold 7 matrices per layer

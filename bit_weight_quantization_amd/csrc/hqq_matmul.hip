@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_general_kerne
 
 // Few rows of X (8 < M <= 16 MT) for 2-, 4- and 8-bit codes, groups of GS = 5, 6, 7
 // (32, 64, 128 weights), K a multiple of 256 and 16-byte aligned s and z: a block of
-// kSkinnyWaves wavefronts over 16 NW weight rows; the wavefronts take consecutive shares of
+// kSkinnyWaves2 wavefronts over 16 NW weight rows; the wavefronts take consecutive shares of
 // the 256-wide blocks of K and their partial tiles are added in LDS in a fixed order.
 // Per block of K (k0) the MFMA steps i = 0..7 (v_mfma_f32_16x16x32_f16) take k0 + 32 i +
 // 8 kq .. + 8 in lane j + 16 kq on both operands, the instruction's own k order, so that
@@ -742,25 +742,42 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_general_kerne
 // loaded before this block's arithmetic; the weight enters the MFMA as in the other
 // kernels (s*q - s*z in fp32, one rounding, binary16).  C: lane j + 16 kq, element v
 // holds X row 16 t + 4 kq + v, weight row n0 + 16 w + j.
+// LDS staging types of the skinny kernel: its buffers are written and read with
+// different widths, so every access goes through may_alias types (no type-based alias
+// assumption can reorder a read of a staged value before its write)
+typedef uint16_t __attribute__((may_alias)) lds_u16;
+typedef uint32_t __attribute__((may_alias)) lds_u32;
+typedef unsigned int lds_u32x4 __attribute__((ext_vector_type(4), may_alias));
+
+constexpr int kSkinnyWaves2 = 4;  // wavefronts per block of hqq_skinny_kernel, splitting K
+
 template <int NB, int MT, int NW, int GS>
-__global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const MatmulParams P) {
+__global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const MatmulParams P) {
   static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
   static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
   constexpr bool kStage = NB != 8;        // pieces of NB bytes transposed through LDS
   constexpr int kRowBytes = 32 * NB + 16;  // a row's 4 x 8 pieces, 16 bytes of padding
-  constexpr int kStageBytes = kStage ? kSkinnyWaves * NW * 16 * kRowBytes : 0;
-  constexpr int kRedBytes = kSkinnyWaves * MT * NW * 4 * kWave * 4;
-  constexpr int kLdsBytes = kStageBytes > kRedBytes ? kStageBytes : kRedBytes;
+  constexpr int kStageBytes = kStage ? kSkinnyWaves2 * NW * 16 * kRowBytes : 0;
+  // X through LDS (up to 32 rows): per wavefront one block of X, MT tiles of two halves
+  // (steps 0-3, 4-7) of 4 slabs, a slab 4 rows x 256 bytes (+16 bytes of padding)
+  constexpr bool XS = MT <= 2;
+  constexpr int kSlab = 4 * 256 + 16;
+  constexpr int kXBytes = XS ? kSkinnyWaves2 * 2 * MT * 4 * kSlab : 0;
+  constexpr int kRedBytes = kSkinnyWaves2 * MT * NW * 4 * kWave * 4;
+  // the code staging and the X buffers; the reduction at the end reuses the second
+  constexpr int kLds1 = kStageBytes > 16 ? kStageBytes : 16;
+  constexpr int kLds2 = kXBytes > kRedBytes ? kXBytes : kRedBytes;
   constexpr int kSW = 256 >> GS < 2 ? 1 : (256 >> GS) / 2;  // 32-bit words of s (and z) per block
-  constexpr int XD = 4;                                      // steps of X held at once
-  __shared__ __align__(16) unsigned char lds[kLdsBytes];
-  const int wid = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  constexpr int XD = 4;                                      // steps of X held at once (not XS)
+  __shared__ __align__(16) unsigned char lds[kLds1];
+  __shared__ __align__(16) unsigned char lds2[kLds2];
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
   const int j = lane & 15, kq = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NW;
   const int64_t row_bytes = (P.K >> 3) * NB;
   const int64_t gpr = P.K >> GS;
   const int64_t nblk = P.K >> 8;
-  const int64_t c0 = wid * nblk / kSkinnyWaves, c1 = (wid + 1) * nblk / kSkinnyWaves;
+  const int64_t c0 = wid * nblk / kSkinnyWaves2, c1 = (wid + 1) * nblk / kSkinnyWaves2;
   // rows past N (or past M for X) read the last valid one; their results are not stored
   int64_t wrow[NW];
 #pragma unroll
@@ -821,22 +838,61 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
   };
   // the wavefront's LDS rows: [w][row j][kq][step] pieces of NB bytes
   unsigned char* stage = lds + wid * (NW * 16 * kRowBytes);
+  // XS: the wavefront's X buffer [half][t][slab]; a slab is 4 rows of X (16 t + 4 n ..)
+  // x 256 contiguous bytes (16 granules of 16 bytes) of one half-block, loaded by one
+  // instruction: lane 16 r + q takes row r, granule (q + 4 r) % 16, so the 16 lanes of a
+  // row read two whole 128-byte lines, and writes it to LDS at 16 (16 r + q); the step
+  // reads below (row j, granule 4 s + kq) then fall on 16 different 4-bank groups
+  unsigned char* xbuf = lds2 + wid * (2 * MT * 4 * kSlab);
+  const int xr = lane >> 4, xg = ((lane & 15) + 4 * xr) & 15;
+  lds_u32x4 xs[XS ? MT : 1][8];  // [t][4 half + slab]
+  auto load_xs = [&](int64_t c) {
+#pragma unroll
+    for (int t = 0; t < (XS ? MT : 0); ++t)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int64_t m = 16 * t + 4 * n + xr;
+        const uint16_t* g = P.X + (m < P.M ? m : P.M - 1) * P.K + (c << 8) + 8 * xg;
+        xs[t][n] = *reinterpret_cast<const lds_u32x4*>(g);
+        xs[t][4 + n] = *reinterpret_cast<const lds_u32x4*>(g + 128);
+      }
+  };
+  auto write_xs = [&]() {
+#pragma unroll
+    for (int t = 0; t < (XS ? MT : 0); ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+          *reinterpret_cast<lds_u32x4*>(xbuf + ((h * MT + t) * 4 + n) * kSlab + 16 * lane) = xs[t][4 * h + n];
+  };
+  auto read_x = [&](int i, int t) -> half8_t {
+    const int h = i >> 2, st = i & 3, r = j & 3;
+    const int off = ((h * MT + t) * 4 + (j >> 2)) * kSlab + 256 * r + 16 * ((4 * st + kq - 4 * r) & 15);
+    return __builtin_bit_cast(half8_t, *reinterpret_cast<const lds_u32x4*>(xbuf + off));
+  };
 
-  Wt cur, nxt;
-  if (c0 < c1) load_wt(c0, nxt);
-  for (int64_t c = c0; c < c1; ++c) {
-    cur = nxt;
+  // one block of K: cur holds its weights, nxt receives the next block's (with X through
+  // LDS two Wt sets alternate, so no prefetched register is copied: a copy would wait for
+  // the prefetch)
+  auto block = [&](int64_t c, const Wt& cur, Wt& nxt) {
     const int64_t k0 = c << 8;
+    const int64_t cn = c + 1 < c1 ? c + 1 : c;  // the next block (the last re-reads itself)
     uint4 xa[XD][MT];
     auto load_x = [&](int i) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) xa[i % XD][t] = *reinterpret_cast<const uint4*>(xrow[t] + k0 + 32 * i);
     };
+    if constexpr (!XS) {
 #pragma unroll
-    for (int i = 0; i < XD - 1; ++i) load_x(i);
-    // the next block's weights (the last block re-reads itself: no branch, so the waits
-    // for this block's loads count exactly)
-    load_wt(c + 1 < c1 ? c + 1 : c, nxt);
+      for (int i = 0; i < XD - 1; ++i) load_x(i);
+    } else {
+      load_xs(cn);  // the next block's X, before its weights: written after this block
+      __builtin_amdgcn_sched_barrier(0);  // (the write then waits for these loads only)
+    }
+    // the next block's weights (unconditional: no branch, so the waits for this block's
+    // loads count exactly)
+    load_wt(cn, nxt);
     __builtin_amdgcn_sched_barrier(0);
     uint32_t cr[NW][2 * NB];  // piece i of the lane's codes: bytes NB i .. of its 8 NB
     if constexpr (kStage) {
@@ -851,18 +907,18 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
             unsigned char* dst = rowp + q * (8 * NB) + (2 * kq + b) * NB;
             const int e = (4 * b + q) * NB;  // byte offset in cur.cw[w]
             if constexpr (NB == 2)
-              *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(cur.cw[w][e >> 2] >> (8 * (e & 3)));
+              *reinterpret_cast<lds_u16*>(dst) = (uint16_t)(cur.cw[w][e >> 2] >> (8 * (e & 3)));
             else
-              *reinterpret_cast<uint32_t*>(dst) = cur.cw[w][e >> 2];
+              *reinterpret_cast<lds_u32*>(dst) = cur.cw[w][e >> 2];
           }
       }
       __builtin_amdgcn_wave_barrier();  // LDS accesses of a wavefront execute in order
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const uint4* src = reinterpret_cast<const uint4*>(stage + (w * 16 + j) * kRowBytes + kq * (8 * NB));
+        const lds_u32x4* src = reinterpret_cast<const lds_u32x4*>(stage + (w * 16 + j) * kRowBytes + kq * (8 * NB));
 #pragma unroll
         for (int h = 0; h < NB / 2; ++h) {
-          const uint4 v = src[h];
+          const lds_u32x4 v = src[h];
           cr[w][4 * h] = v.x; cr[w][4 * h + 1] = v.y; cr[w][4 * h + 2] = v.z; cr[w][4 * h + 3] = v.w;
         }
       }
@@ -903,19 +959,44 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int i = 2 * ip + b;
-        if (i + XD - 1 < 8) load_x(i + XD - 1);  // XD - 1 steps ahead
+        if constexpr (!XS) {
+          if (i + XD - 1 < 8) load_x(i + XD - 1);  // XD - 1 steps ahead
+        }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const half8_t af = __builtin_bit_cast(half8_t, xa[i % XD][t]);
+          half8_t af;
+          if constexpr (XS) af = read_x(i, t);
+          else af = __builtin_bit_cast(half8_t, xa[i % XD][t]);
 #pragma unroll
           for (int w = 0; w < NW; ++w)
             acc[t][w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b][w], acc[t][w], 0, 0, 0);
         }
       }
     }
+    if constexpr (XS) write_xs();  // this block's reads are done (LDS accesses run in order)
+  };
+  if constexpr (XS) {
+    Wt wa, wb;
+    if (c0 < c1) {
+      load_xs(c0);
+      load_wt(c0, wa);
+      write_xs();
+    }
+    for (int64_t c = c0; c < c1; c += 2) {
+      block(c, wa, wb);
+      if (c + 1 >= c1) break;
+      block(c + 1, wb, wa);
+    }
+  } else {  // 64 rows: the registers allow one copy of the block body only
+    Wt cur, nxt;
+    if (c0 < c1) load_wt(c0, nxt);
+    for (int64_t c = c0; c < c1; ++c) {
+      cur = nxt;
+      block(c, cur, nxt);
+    }
   }
-  __syncthreads();  // the staging buffers become the reduction buffer
-  float* red = reinterpret_cast<float*>(lds);  // [wave][t][w][v][lane]
+  __syncthreads();  // the X buffers become the reduction buffer
+  float* red = reinterpret_cast<float*>(lds2);  // [wave][t][w][v][lane]
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -923,19 +1004,19 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[(((wid * MT + t) * NW + w) * 4 + v) * kWave + lane] = acc[t][w][v];
   __syncthreads();
-  // wavefront wid writes the tiles (t, w) with (t NW + w) % kSkinnyWaves == wid, adding
+  // wavefront wid writes the tiles (t, w) with (t NW + w) % kSkinnyWaves2 == wid, adding
   // the wavefronts' parts in order
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      if ((t * NW + w) % kSkinnyWaves != wid) continue;
+      if ((t * NW + w) % kSkinnyWaves2 != wid) continue;
       const int64_t n = n0 + 16 * w + j;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         float y = red[((t * NW + w) * 4 + v) * kWave + lane];
 #pragma unroll
-        for (int u = 1; u < kSkinnyWaves; ++u) y += red[(((u * MT + t) * NW + w) * 4 + v) * kWave + lane];
+        for (int u = 1; u < kSkinnyWaves2; ++u) y += red[(((u * MT + t) * NW + w) * 4 + v) * kWave + lane];
         const int64_t m = 16 * t + 4 * kq + v;
         if (m < P.M && n < P.N) {
           if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = y;
@@ -947,14 +1028,14 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void hqq_skinny_kernel(const 
 
 template <int NB, int MT, int NW>
 void launch_skinny_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
-  const dim3 block(kSkinnyWaves * kWave);
+  const dim3 block(kSkinnyWaves * kWave), block2(kSkinnyWaves2 * kWave);
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(P.scale16) | reinterpret_cast<uintptr_t>(P.zero16)) & 15) == 0;
   if constexpr (NB != 3) {
     if (P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7) {
       switch (P.group_shift) {
-        case 5: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 5>), grid, block, 0, st, P); return;
-        case 6: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 6>), grid, block, 0, st, P); return;
-        default: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 7>), grid, block, 0, st, P); return;
+        case 5: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 5>), grid, block2, 0, st, P); return;
+        case 6: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 6>), grid, block2, 0, st, P); return;
+        default: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 7>), grid, block2, 0, st, P); return;
       }
     }
   }
