@@ -420,7 +420,7 @@ def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
             nbytes = sum(W.numel() * nb / 8 + W.numel() // g * 4 + 2 * M * W.shape[1] +
                          2 * M * W.shape[0] for W in Ws)
             flops = sum(2.0 * M * W.numel() for W in Ws)
-            path = "gemv" if M <= 8 else ("mfma_skinny" if M <= 64 else "mfma")
+            path = "gemv" if M <= 2 else ("mfma_skinny" if M <= 64 else "mfma")
             row = {"M": M, "path": path, "ms": round(ms, 4),
                    "hbm_GBs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
                    "hbm_frac": round(nbytes / (ms * 1e-3) / PEAK_HBM, 4),
@@ -579,7 +579,7 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     names = sorted({n for c in tab.values() for n in c})
     kernels = sorted(tab)
     lines = ["# Counters of the product kernels on one 28672 x 8192 b2 g32 weight", "",
-             "hqq_matmul at M = 1, 4 (hqq_gemv_packed_kernel) and M = 16, 64 (hqq_skinny_kernel), "
+             "hqq_matmul at M = 1 (hqq_gemv_packed_kernel) and M = 4, 16, 64 (hqq_skinny_kernel), "
              "5 calls each (bench.py --profile-matmul); values per dispatch, averaged. "
              "GRBM_GUI_ACTIVE counts on every XCD (8 per device).", "",
              "| counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]

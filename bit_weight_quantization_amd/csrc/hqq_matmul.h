@@ -18,9 +18,12 @@ struct MatmulParams {
   int out_f32;
 };
 
-// Rows of X up to which the wavefront-per-row kernel is used, and up to which the
-// skinny matrix-core kernel is used above that (then the tiled matrix-core kernel).
+// Rows of X up to which the wavefront-per-row kernel is used (kGemvAlignedMaxRows where
+// the aligned skinny kernel applies: 2-, 4-, 8-bit codes, groups of 32-128, K a multiple
+// of 256, 16-byte aligned s and z), and up to which a skinny matrix-core kernel is used
+// above that (then the tiled matrix-core kernel).
 constexpr int kGemvMaxRows = 8;
+constexpr int kGemvAlignedMaxRows = 2;
 constexpr int kSkinnyMaxRows = 64;
 
 hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream);

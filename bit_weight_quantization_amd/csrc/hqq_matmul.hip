@@ -1026,12 +1026,18 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
     }
 }
 
+// The aligned skinny kernel applies: byte-aligned codes, groups of 32-128, K a multiple
+// of 256, 16-byte aligned s and z.
+bool skinny_aligned(const MatmulParams& P) {
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(P.scale16) | reinterpret_cast<uintptr_t>(P.zero16)) & 15) == 0;
+  return P.nbits != 3 && P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7;
+}
+
 template <int NB, int MT, int NW>
 void launch_skinny_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
   const dim3 block(kSkinnyWaves * kWave), block2(kSkinnyWaves2 * kWave);
-  const bool aligned16 = ((reinterpret_cast<uintptr_t>(P.scale16) | reinterpret_cast<uintptr_t>(P.zero16)) & 15) == 0;
   if constexpr (NB != 3) {
-    if (P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7) {
+    if (skinny_aligned(P)) {
       switch (P.group_shift) {
         case 5: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 5>), grid, block2, 0, st, P); return;
         case 6: hipLaunchKernelGGL((hqq_skinny_kernel<NB, MT, NW, 6>), grid, block2, 0, st, P); return;
@@ -1052,8 +1058,10 @@ void launch_skinny(const MatmulParams& P, hipStream_t st) {
 
 template <int NB>
 hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
+  // the aligned skinny kernel costs about the same for 3-16 rows as the per-row one for 3
+  const int64_t gemv_max = skinny_aligned(P) ? kGemvAlignedMaxRows : kGemvMaxRows;
   if constexpr (NB != 3) {  // packed binary16 codes (3-bit codes straddle bytes)
-    if (P.M <= kGemvMaxRows) {
+    if (P.M <= gemv_max) {
       // rows per wavefront: enough wavefronts to fill the chip (>= 2048) with as many
       // rows sharing each chunk of X as that allows
       if (P.N >= 8192) return launch_gemv_packed<NB, 4>(P, st);
@@ -1061,7 +1069,7 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
       return launch_gemv_packed<NB, 1>(P, st);
     }
   }
-  if (P.M > kGemvMaxRows && P.M <= kSkinnyMaxRows) {
+  if (P.M > gemv_max && P.M <= kSkinnyMaxRows) {
     if (P.M <= 16) launch_skinny<NB, 1>(P, st);
     else if (P.M <= 32) launch_skinny<NB, 2>(P, st);
     else launch_skinny<NB, 4>(P, st);

@@ -290,9 +290,10 @@ int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
  * cols = K) writes packed_codes, scale_f16 and zero_f16.
  *   Y[m][n] = sum over k of X[m][k] * s[n][k/g] * (q[n][k] - z[n][k/g])
  * with the stored binary16 s and z.  Arithmetic: fp32 accumulation in an order that
- * depends on the path (not bit-reproducible against another order).  M <= 8: per
- * 16 codes, s * (sum x q - z sum x) in fp32 (the codes enter exactly).  M > 8: the
- * weight is dequantized to binary16 (s*q - s*z in fp32, one rounding, then to
+ * depends on the path (not bit-reproducible against another order).  M <= 2 (M <= 8
+ * for 3-bit codes, groups of 16, K not a multiple of 256 or s, z not 16-byte aligned):
+ * per 16 codes, s * (sum x q - z sum x) in fp32 (the codes enter exactly).  More rows:
+ * the weight is dequantized to binary16 (s*q - s*z in fp32, one rounding, then to
  * binary16) and multiplied on the matrix cores with fp32 accumulation.
  *
  * X_f16        M x K binary16, row-major, 16-byte aligned.

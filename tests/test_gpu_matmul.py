@@ -6,8 +6,9 @@ device.  Two kinds of checks:
   * exact cases: s a power of two, z an integer, X small integers: every product and
     partial sum is exact in fp32 whatever the order, so fp32 outputs equal the oracle
     bit for bit and binary16 outputs equal the oracle's value rounded once.  This pins
-    the indexing of both kernels (rows of X up to 8: the per-row kernel; above: the
-    matrix-core kernel) over ragged tiles, all bit widths and group sizes;
+    the indexing of every kernel (few rows of X: the per-row kernel; up to 64: the
+    skinny matrix-core kernels; above: the tiled one) over ragged tiles, all bit widths
+    and group sizes;
   * general inputs: |y_dev - y_oracle| within a bound derived from the arithmetic of the
     path (``_bound``), on full small products and on sampled outputs of the Llama-2-70B
     layer shapes at full size.
@@ -69,6 +70,14 @@ def _run(hq, X, packed, s, z, N, nbits, g, out_f32, sz_offset=0):
     return Y.cpu().numpy().astype(np.float64)
 
 
+def _per_row_path(M, K, nbits, g):
+    """hqq_matmul's per-row path (exact codes): M <= 2 where the aligned small-batch
+    kernel applies (2, 4, 8 bits, g >= 32, K % 256 == 0; these tests' s and z are
+    16-byte aligned), else M <= 8."""
+    aligned = nbits != 3 and g >= 32 and K % 256 == 0
+    return M <= (2 if aligned else 8)
+
+
 def _bound(X, codes, s, z, g, gemv, out_f32, y):
     """Worst-case |y_dev - y_exact| of the device path, elementwise (M x N).
     per-row path: per 16 codes fp32 sums of x q and x, then s (p - z sx) accumulated over
@@ -114,13 +123,14 @@ def test_exact_products_all_paths(hq, nbits, g):
 
 @pytest.mark.parametrize("nbits", [2, 4, 8])
 def test_exact_products_skinny_paths(hq, nbits):
-    """Small batches (8 < M <= 64) on the matrix-core skinny kernels: K a multiple of 256
+    """Small batches (2 < M <= 64) on the matrix-core skinny kernels: K a multiple of 256
     with 1, 9 (split unevenly over the 8 wavefronts of a block) and 16 blocks of 256, one
     and two 16-row weight groups per block (N below and above 4096, ragged), every
     16-row tile count of X (M = 9 .. 64), groups of 32, 64 and 128, and s, z off 16-byte
     alignment (the general kernel): bit-exact on exact inputs."""
     rng = np.random.default_rng(400 + nbits)
-    cases = [(9, 100, 256, 32, 0), (16, 300, 2304, 64, 0), (17, 129, 4096, 128, 0),
+    cases = [(3, 100, 512, 32, 0), (4, 130, 2304, 128, 0), (8, 4100, 256, 64, 0),
+             (9, 100, 256, 32, 0), (16, 300, 2304, 64, 0), (17, 129, 4096, 128, 0),
              (32, 4100, 2304, 32, 0), (33, 70, 2304, 64, 0), (64, 4097, 512, 128, 0),
              (40, 200, 4096, 32, 0), (24, 130, 2304, 64, 1), (48, 4100, 768, 32, 3)]
     for M, N, K, g, off in cases:
@@ -164,7 +174,7 @@ def test_general_inputs_within_the_bound(hq, nbits, g):
         ref = oracle.hqq_matmul(X, packed, s, z, N, nbits, g)
         for out_f32 in (1, 0):
             Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32)
-            b = _bound(X, codes, s, z, g, M <= 8, out_f32, ref)
+            b = _bound(X, codes, s, z, g, _per_row_path(M, K, nbits, g), out_f32, ref)
             err = np.abs(Y - ref)
             assert np.all(err <= b), (M, out_f32, float((err / b).max()))
             _say(f"b{nbits} g{g} M={M} out_f32={out_f32}: max err/bound {float((err / b).max()):.3g}, "
@@ -188,7 +198,7 @@ def test_llama70b_layer_shapes_sampled(hq, nbits, g):
             Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
             ms = np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(M, 6), replace=False)]))
             ref = oracle.hqq_matmul(X[ms], sub_packed, s[rows], z[rows], len(rows), nbits, g)
-            b = _bound(X[ms], codes[rows], s[rows], z[rows], g, M <= 8, 1, ref)
+            b = _bound(X[ms], codes[rows], s[rows], z[rows], g, _per_row_path(M, K, nbits, g), 1, ref)
             err = np.abs(Y[np.ix_(ms, rows)] - ref)
             assert np.all(err <= b)
             _say(f"{N}x{K} b{nbits} g{g} M={M}: max err/bound {float((err / b).max()):.3g}")
