@@ -579,7 +579,8 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     names = sorted({n for c in tab.values() for n in c})
     kernels = sorted(tab)
     lines = ["# Counters of the product kernels on one 28672 x 8192 b2 g32 weight", "",
-             "hqq_matmul at M = 1 (hqq_gemv_packed_kernel) and M = 4, 16, 64 (hqq_skinny_kernel), "
+             "hqq_matmul at M = 1 (hqq_gemv_packed_kernel), M = 4, 16, 64 (hqq_skinny_kernel) "
+             "and M = 512, 4096 (hqq_gemm_kernel), "
              "5 calls each (bench.py --profile-matmul); values per dispatch, averaged. "
              "GRBM_GUI_ACTIVE counts on every XCD (8 per device).", "",
              "| counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
@@ -628,7 +629,7 @@ def main():
                          "quantization measurement (for rocprofv3 runs)")
     ap.add_argument("--profile-matmul", action="store_true",
                     help="only the products with one 28672 x 8192 b2 g32 weight at M = 16, 1, "
-                         "4, 64 (5 calls each; for rocprofv3 counter runs)")
+                         "4, 64, 512, 4096 (5 calls each; for rocprofv3 counter runs)")
     ap.add_argument("--summarize-kernels", nargs=2, metavar=("WHICH", "KT_DIR"),
                     help="write the profiles/ summary of one kernel family (meta, variants) "
                          "from a rocprofv3 kernel trace")
@@ -692,7 +693,7 @@ def main():
         W = workloads.generate(28672, 8192, wl.dist, 3, dev)
         q = hq.quantize(W, 2, 32)
         del W
-        for M in (16, 1, 4, 64):
+        for M in (16, 1, 4, 64, 512, 4096):
             X = torch.randn((M, 8192), device=dev).half()
             log(f"profile-matmul: 28672 x 8192 b2 g32, M = {M}, 5 calls")
             for _ in range(5):

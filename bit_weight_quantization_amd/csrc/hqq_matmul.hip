@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "hqq_internal.h"
 #include "hqq_matmul.h"
 
@@ -418,80 +420,140 @@ __device__ __forceinline__ void dequant32(const uint32_t (&w)[NB], float s0, flo
   for (int i = 0; i < 4; ++i) out[i] = make_uint4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
 }
 
-// (64 TI) x (64 TJ) output tile per block of four wavefronts (2 x 2 of them, each
-// (32 TI) x (32 TJ): TI x TJ tiles of v_mfma_f32_32x32x16_f16).  K advances in steps of
-// 64: thread t stages rows t / 2 + 128 r of both tiles, elements 32 (t % 2) .. + 32 of the
-// step (the X values as they are, the weight dequantized to binary16).  LDS is
-// double-buffered: the next step's global loads are issued before this step's MFMAs and
-// written to the other buffer after them, with one barrier per step.  Larger TI, TJ read
-// fewer LDS operands per MFMA.
-template <int NB, int TI, int TJ>
-__global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) {
-  constexpr int BM = 64 * TI, BN = 64 * TJ, RA = BM / 128, RB = BN / 128;
+// The 16 codes (16*NB bits) starting at p (2*NB-byte aligned), LSB first in words.
+template <int NB>
+struct Codes16 {
+  static constexpr int kWords = (16 * NB + 31) / 32;
+};
+template <int NB>
+__device__ __forceinline__ void load_codes16(const uint8_t* p, uint32_t (&w)[Codes16<NB>::kWords]) {
+  if constexpr (NB == 2) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (NB == 3) {  // 6 bytes, 2-byte aligned
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    w[0] = (uint32_t)q[0] | ((uint32_t)q[1] << 16);
+    w[1] = q[2];
+  } else if constexpr (NB == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+}
+
+// Dequantize 16 codes of one group to binary16, as dequant32 (w = s*q - s*z in fp32, one
+// rounding, then binary16).
+template <int NB>
+__device__ __forceinline__ void dequant16(const uint32_t (&w)[Codes16<NB>::kWords], float s, float sz,
+                                          uint4 (&out)[2]) {
+  uint32_t h[8];
+  if constexpr (NB == 3) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w0 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j), -sz);
+      const float w1 = __builtin_fmaf(s, (float)code_at<NB>(w, 2 * j + 1), -sz);
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+    }
+  } else {
+    CodePairs<NB> cp;
+    cp.from(w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w0 = __builtin_fmaf(s, (float)cp.q[j][0], -sz);
+      const float w1 = __builtin_fmaf(s, (float)cp.q[j][1], -sz);
+      h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){w0, w1}, half2_t));
+    }
+  }
+  out[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  out[1] = make_uint4(h[4], h[5], h[6], h[7]);
+}
+
+// (32 TI WM) x (64 TJ) output tile per block of WM x 2 wavefronts, each (32 TI) x (32 TJ):
+// TI x TJ tiles of v_mfma_f32_32x32x16_f16.  K advances in steps of 64: thread t stages
+// rows (t + T r) / 2 of both tiles, elements 32 (t % 2) .. + 32 of the step (the X values
+// as they are, the weight dequantized to binary16).  LDS is double-buffered: the next
+// step's global loads are issued before this step's MFMAs and written to the other buffer
+// after them, with one barrier per step.  Larger TI, TJ read fewer LDS operands per MFMA;
+// a larger WM dequantizes each weight tile for more rows of X.
+template <int NB, int WM, int TI, int TJ>
+__global__ __launch_bounds__(2 * WM * kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void hqq_gemm_kernel(const MatmulParams P) {
+  constexpr int T = 2 * WM * kWave;                 // threads: WM x 2 wavefronts
+  constexpr int BM = 32 * TI * WM, BN = 64 * TJ;    // the block's tile
+  static_assert(2 * BM == T, "one 32-value item of X per thread and step");
+  constexpr int CB = 64 * BN / T;                   // codes per thread and step
+  static_assert(CB == 16 || CB == 32, "16 or 32 codes of the weight per thread and step");
+  constexpr int BP = 64 / CB;                       // threads per weight row
+  constexpr int CW = CB == 32 ? NB : Codes16<NB>::kWords;
   __shared__ __align__(16) _Float16 As[2][BM][kLdsRow];
   __shared__ __align__(16) _Float16 Bs[2][BN][kLdsRow];
   const int tid = threadIdx.x;
   const int wid = tid / kWave, lane = tid & (kWave - 1);
-  const int wm = wid >> 1, wn = wid & 1;  // the wavefront's quarter of the tile
+  const int wm = wid >> 1, wn = wid & 1;  // the wavefront's part of the tile
   const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int64_t row_bytes = (P.K >> 3) * NB;
   const int64_t gpr = P.K >> P.group_shift;
   const int g2 = P.group_size == 16 ? 1 : 0;
-  const int lr = tid >> 1, lh = tid & 1;
+  // this thread's items of a step: X row tid / 2, values 32 (tid % 2) ..; weight row
+  // tid / BP, codes CB (tid % BP) .. (rows past M or N read the last valid row; values
+  // outside the matrices become zeros in LDS)
+  const int xr = tid >> 1, xh = tid & 1;
+  const int br = tid / BP, bp = tid % BP;
+  const uint16_t* xrow = P.X + (m0 + xr < P.M ? m0 + xr : P.M - 1) * P.K;
+  const int64_t wrow_n = n0 + br < P.N ? n0 + br : P.N - 1;
+  const uint8_t* wrow = P.packed + wrow_n * row_bytes;
+  const uint16_t* srow = P.scale16 + wrow_n * gpr;
+  const uint16_t* zrow = P.zero16 + wrow_n * gpr;
 
-  // the loader's registers for one step
-  uint4 ar[RA][4];
-  uint32_t cw[RB][NB];
-  uint32_t s16[RB][2], z16[RB][2];
-  auto load_global = [&](int64_t k0) {
-    const int64_t e0 = k0 + 32 * lh;
-    const bool in = e0 < P.K;  // K % 64 == 32: the last step's upper half is past the end
+  // the loader's registers, two steps deep: stage S holds the loads of steps S, S + 2, ..
+  uint4 ar[2][4];
+  uint32_t cw[2][CW];
+  uint32_t s16[2][2], z16[2][2];
+  auto load_global = [&](auto st_const, int64_t k0) {
+    constexpr int S = decltype(st_const)::value;
+    const int64_t ea = k0 + 32 * xh;
+    const uint4* xp = reinterpret_cast<const uint4*>(xrow + (ea < P.K ? ea : 0));
 #pragma unroll
-    for (int r = 0; r < RA; ++r) {
-      const int64_t am = m0 + lr + 128 * r;
-      if (am < P.M && in) {
-        const uint4* xp = reinterpret_cast<const uint4*>(P.X + am * P.K + e0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ar[r][i] = xp[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ar[r][i] = make_uint4(0u, 0u, 0u, 0u);
-      }
+    for (int i = 0; i < 4; ++i) ar[S][i] = xp[i];
+    const int64_t eb0 = k0 + CB * bp;
+    const int64_t eb = eb0 < P.K ? eb0 : 0;  // K % 64 == 32: the last step's upper half
+    if constexpr (CB == 32) {
+      load_codes32<NB>(wrow + (eb >> 5) * (4 * NB), cw[S]);
+    } else {
+      load_codes16<NB>(wrow + (eb >> 4) * (2 * NB), cw[S]);
     }
-    const int64_t ec = in ? e0 : 0;  // a valid address; the values are not used
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int64_t bn = n0 + lr + 128 * r;
-      const int64_t nn = bn < P.N ? bn : 0;
-      load_codes32<NB>(P.packed + nn * row_bytes + (ec >> 5) * (4 * NB), cw[r]);
-      const int64_t g0 = nn * gpr + (ec >> P.group_shift);
-      s16[r][0] = P.scale16[g0];
-      z16[r][0] = P.zero16[g0];
-      s16[r][1] = P.scale16[g0 + g2];
-      z16[r][1] = P.zero16[g0 + g2];
+    const int64_t g0 = eb >> P.group_shift;
+    s16[S][0] = srow[g0];
+    z16[S][0] = zrow[g0];
+    if constexpr (CB == 32) {
+      s16[S][1] = srow[g0 + g2];
+      z16[S][1] = zrow[g0 + g2];
     }
   };
-  auto store_lds = [&](int buf, int64_t k0) {
-#pragma unroll
-    for (int r = 0; r < RA; ++r) {
-      uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr + 128 * r][32 * lh]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ad[i] = ar[r][i];
+  // the weight of step k0 (stage S) as binary16, zeros outside the matrix (s = 0)
+  auto dequant_b = [&](auto st_const, int64_t k0, uint4 (&bv)[CB / 8]) {
+    constexpr int S = decltype(st_const)::value;
+    const bool ok = n0 + br < P.N && k0 + CB * bp < P.K;
+    const float s0 = ok ? h2f(s16[S][0]) : 0.f;
+    const float sz0 = ok ? s0 * h2f(z16[S][0]) : 0.f;  // s*z exact
+    if constexpr (CB == 32) {
+      const float s1 = ok ? h2f(s16[S][1]) : 0.f;
+      const float sz1 = ok ? s1 * h2f(z16[S][1]) : 0.f;
+      dequant32<NB>(cw[S], s0, sz0, s1, sz1, bv);
+    } else {
+      dequant16<NB>(cw[S], s0, sz0, bv);
     }
+  };
+  auto write_lds = [&](auto st_const, int buf, int64_t k0, const uint4 (&bv)[CB / 8]) {
+    constexpr int S = decltype(st_const)::value;
+    const bool ok = k0 + 32 * xh < P.K && m0 + xr < P.M;
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][xr][32 * xh]);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      uint4 bv[4];
-      if (n0 + lr + 128 * r < P.N && k0 + 32 * lh < P.K) {
-        const float s0 = h2f(s16[r][0]), s1 = h2f(s16[r][1]);
-        dequant32<NB>(cw[r], s0, s0 * h2f(z16[r][0]), s1, s1 * h2f(z16[r][1]), bv);  // s*z exact
-      } else {
+    for (int i = 0; i < 4; ++i) ad[i] = ok ? ar[S][i] : make_uint4(0u, 0u, 0u, 0u);
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][br][CB * bp]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr + 128 * r][32 * lh]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bd[i] = bv[i];
-    }
+    for (int i = 0; i < CB / 8; ++i) bd[i] = bv[i];
   };
 
   float16_t acc[TI][TJ];
@@ -502,22 +564,14 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (P.K > 0) {
-    load_global(0);
-    store_lds(0, 0);
-  }
-  __syncthreads();
-  for (int64_t k0 = 0; k0 < P.K; k0 += kBK) {
-    const int buf = (int)((k0 / kBK) & 1);
-    const bool more = k0 + kBK < P.K;
-    if (more) load_global(k0 + kBK);
+  auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
       half8_t af[TI], bf[TJ];
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * (BM / 2) + i * 32 + (lane & 31)][kk]);
+        af[i] = *reinterpret_cast<const half8_t*>(&As[buf][wm * (32 * TI) + i * 32 + (lane & 31)][kk]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
         bf[j] = *reinterpret_cast<const half8_t*>(&Bs[buf][wn * (BN / 2) + j * 32 + (lane & 31)][kk]);
@@ -527,8 +581,36 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store_lds(buf ^ 1, k0 + kBK);  // last read in the previous step, before its barrier
-    __syncthreads();
+  };
+  // step k0 (LDS buffer S, stage S): prefetch step k0 + 128 into stage S (its step k0 went
+  // to LDS one step ago; past the end it re-reads step 0, unused), dequantize step k0 + 64
+  // from stage S ^ 1 (loaded one step ago) in the same basic block as this step's MFMAs,
+  // so the compiler can interleave them, write it to buffer S ^ 1, barrier
+  auto step = [&](auto st_const, int64_t k0) {
+    constexpr int S = decltype(st_const)::value;
+    constexpr std::integral_constant<int, S ^ 1> other{};
+    load_global(st_const, k0 + 2 * kBK < P.K ? k0 + 2 * kBK : 0);
+    uint4 bv[CB / 8];
+    dequant_b(other, k0 + kBK, bv);
+    mfma_step(S);
+    write_lds(other, S ^ 1, k0 + kBK, bv);  // (after the last step: unused; unconditional, so
+    __syncthreads();                         // the dequantization is not sunk past the MFMAs)
+  };
+
+  if (P.K > 0) {
+    constexpr std::integral_constant<int, 0> s0{};
+    constexpr std::integral_constant<int, 1> s1{};
+    load_global(s0, 0);
+    load_global(s1, kBK < P.K ? kBK : 0);
+    uint4 bv[CB / 8];
+    dequant_b(s0, 0, bv);
+    write_lds(s0, 0, 0, bv);
+  }
+  __syncthreads();
+  for (int64_t k0 = 0; k0 < P.K; k0 += 2 * kBK) {
+    step(std::integral_constant<int, 0>{}, k0);
+    if (k0 + kBK >= P.K) break;
+    step(std::integral_constant<int, 1>{}, k0 + kBK);
   }
 
   // C tile (i, j): lane l, element v holds row 8 (v / 4) + 4 (l / 32) + v % 4, col l % 32
@@ -539,7 +621,7 @@ __global__ __launch_bounds__(kBlock) void hqq_gemm_kernel(const MatmulParams P) 
       const int64_t n = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t m = m0 + wm * (32 * TI) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < P.M && n < P.N) {
           if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = acc[i][j][v];
           else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)acc[i][j][v];
@@ -1085,10 +1167,17 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
     else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 4>), grid, block, 0, st, P);
     else hipLaunchKernelGGL((hqq_gemv_kernel<NB, 8>), grid, block, 0, st, P);
   } else {
-    // 128 x 128 tiles: two blocks per CU (a 256 x 128 tile fits one, and one wavefront
-    // per SIMD leaves the global loads' latency exposed)
-    const dim3 grid((unsigned)((P.N + 127) / 128), (unsigned)((P.M + 127) / 128));
-    hipLaunchKernelGGL((hqq_gemm_kernel<NB, 2, 2>), grid, dim3(kBlock), 0, st, P);
+    // 256 x 128 tiles of 8 wavefronts for many rows (each weight tile is dequantized once
+    // per 256 rows of X: half the decode per MFMA of 128 x 128 tiles), else 128 x 128 (4
+    // wavefronts: twice the blocks, a shorter tail at a few hundred rows); both 64 x 64
+    // per wavefront, 2 wavefronts per SIMD
+    if (P.M >= 1024) {
+      const dim3 grid((unsigned)((P.N + 127) / 128), (unsigned)((P.M + 255) / 256));
+      hipLaunchKernelGGL((hqq_gemm_kernel<NB, 4, 2, 2>), grid, dim3(8 * kWave), 0, st, P);
+    } else {
+      const dim3 grid((unsigned)((P.N + 127) / 128), (unsigned)((P.M + 127) / 128));
+      hipLaunchKernelGGL((hqq_gemm_kernel<NB, 2, 2, 2>), grid, dim3(4 * kWave), 0, st, P);
+    }
   }
   return hipGetLastError();
 }
