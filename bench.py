@@ -510,9 +510,9 @@ KERNEL_SUMMARIES = {
                "hqq_matmul, one call per matrix, M = 1, 4, 16, 64, 512, 4096 rows of X, b2 g32 and "
                "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
                "(bench.py measure_matmul); hqq_gemv_packed_kernel<b, M rows, weight rows per "
-               "wave, g = 16> for M <= 8, hqq_skinny_kernel<b, 16-row blocks of X, 16-row "
-               "weight groups per wavefront, log2 g> for M <= 64, hqq_gemm_kernel<b, 2, 2> "
-               "(128 x 128 tiles) above."),
+               "wave, g = 16> for M <= 2, hqq_skinny_kernel<b, 16-row blocks of X, 16-row "
+               "weight groups per wavefront, log2 g> for M <= 64, hqq_gemm_kernel<b, "
+               "wavefront rows WM, 2, 2> ((64 WM) x 128 tiles) above."),
     "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
                 "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
                 "hqq_lowrank (residual_kernel; gemm16_kernel split-K products over the binary16 "
