@@ -1167,11 +1167,11 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
     else if (P.M <= 4) hipLaunchKernelGGL((hqq_gemv_kernel<NB, 4>), grid, block, 0, st, P);
     else hipLaunchKernelGGL((hqq_gemv_kernel<NB, 8>), grid, block, 0, st, P);
   } else {
-    // 256 x 128 tiles of 8 wavefronts for many rows (each weight tile is dequantized once
+    // 256 x 128 tiles of 8 wavefronts from 512 rows (each weight tile is dequantized once
     // per 256 rows of X: half the decode per MFMA of 128 x 128 tiles), else 128 x 128 (4
-    // wavefronts: twice the blocks, a shorter tail at a few hundred rows); both 64 x 64
-    // per wavefront, 2 wavefronts per SIMD
-    if (P.M >= 1024) {
+    // wavefronts: twice the blocks for a few hundred rows); both 64 x 64 per wavefront, 2
+    // wavefronts per SIMD
+    if (P.M >= 512) {
       const dim3 grid((unsigned)((P.N + 127) / 128), (unsigned)((P.M + 255) / 256));
       hipLaunchKernelGGL((hqq_gemm_kernel<NB, 4, 2, 2>), grid, dim3(8 * kWave), 0, st, P);
     } else {
