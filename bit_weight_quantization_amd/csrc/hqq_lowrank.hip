@@ -425,64 +425,110 @@ __global__ __launch_bounds__(kSyevThreads) void syev_kernel(double* __restrict__
         if (tj == 0) s2buf[k & 1] = s2;
       }
     };
-    for (int k = 0; k < L - 2; ++k) {
-      const int b = k + 1;
-      publish(k);
-      __syncthreads();
-      const double s2 = s2buf[k & 1];
-      const double x0 = A[k * L + b];
-      double tk = 0.0, v0 = x0, al = x0;
-      if (s2 > 0.0) {
-        const double mu = __builtin_sqrt(x0 * x0 + s2);
-        al = x0 > 0.0 ? -mu : mu;
-        v0 = x0 - al;
-        tk = 2.0 / (v0 * v0 + s2);
-      }
-      if (t == 0) {
-        dd[k] = A[k * L + k];
-        ee[k] = al;
-        tau[k] = tk;
-        vz[k] = v0;
-      }
-      if (tk != 0.0) {  // uniform
-        double vi[kSmallBlocks], vj[kSmallBlocks], ps[kSmallBlocks];
+    // step k, instantiated per block KP = k / 32 of row k and block KB = (k + 1) / 32 where
+    // the reflector starts, so that the tests i, j >= k + 1 are compile-time outside the
+    // block that straddles k + 1.  The owners of row k publish it; the one holding entry
+    // k + 1 computes the reflector (alpha, v0, tau) once and stores v0 in its place.
+    auto hstep = [&](auto kp_const, auto kb_const, int k) {
+      constexpr int KP = decltype(kp_const)::value, KB = decltype(kb_const)::value;
+      const int b = k + 1, kr = k - KP * kGrid, br = b - KB * kGrid;
+      if (ti == kr) {
+        double s2 = 0.0;
 #pragma unroll
-        for (int p = 0; p < kSmallBlocks; ++p) {
-          const int i = ti + kGrid * p, j = tj + kGrid * p;
-          vi[p] = (p < nb && i >= b) ? (i == b ? v0 : A[k * L + i]) : 0.0;
-          vj[p] = (p < nb && j >= b) ? (j == b ? v0 : A[k * L + j]) : 0.0;
+        for (int q = 0; q < kSmallBlocks; ++q) {
+          if (q >= nb) continue;
+          const double v = a[KP][q];
+          const int j = tj + kGrid * q;
+          A[k * L + j] = v;
+          if (j > b) s2 += v * v;
         }
-#pragma unroll
-        for (int p = 0; p < kSmallBlocks; ++p) {
-          double acc = 0.0;
-#pragma unroll
-          for (int q = 0; q < kSmallBlocks; ++q) acc += a[p][q] * vj[q];
-          ps[p] = sumrow_f64(acc);
-        }
-        if (tj == 0) {  // p_i for the row group's rows, and its part of v^T S' v
-          double vsv = 0.0;
-#pragma unroll
-          for (int p = 0; p < kSmallBlocks; ++p) {
-            if (p < nb) part[0][ti + kGrid * p] = tk * ps[p];
-            vsv += ps[p] * vi[p];
+        s2 = sumrow_f64(s2);
+        if (tj == kr) dd[k] = a[KP][KP];
+        if (tj == br) {  // entry b = tj + 32 KB
+          const double x0 = a[KP][KB];
+          double tk = 0.0, v0 = x0, al = x0;
+          if (s2 > 0.0) {
+            const double mu = __builtin_sqrt(x0 * x0 + s2);
+            al = x0 > 0.0 ? -mu : mu;
+            v0 = x0 - al;
+            tk = 2.0 / (v0 * v0 + s2);
           }
-          kpart[ti] = vsv;
+          A[k * L + b] = v0;
+          ee[k] = al;
+          tau[k] = tk;
+          vz[k] = v0;
         }
-        __syncthreads();
-        // K = (tau / 2) p^T v = (tau^2 / 2) v^T S' v
-        const double K = 0.5 * tk * tk * sumrow_f64(kpart[tj]);
-        double wi[kSmallBlocks], wj[kSmallBlocks];
-#pragma unroll
-        for (int p = 0; p < kSmallBlocks; ++p) {
-          wi[p] = p < nb ? part[0][ti + kGrid * p] - K * vi[p] : 0.0;
-          wj[p] = p < nb ? part[0][tj + kGrid * p] - K * vj[p] : 0.0;
-        }
-#pragma unroll
-        for (int p = 0; p < kSmallBlocks; ++p)
-#pragma unroll
-          for (int q = 0; q < kSmallBlocks; ++q)
-            if (ti + kGrid * p >= b && tj + kGrid * q >= b) a[p][q] -= vi[p] * wj[q] + wi[p] * vj[q];
       }
+      __syncthreads();
+      const double tk = tau[k];
+      if (tk == 0.0) return;  // uniform
+      const double* R = A + k * L;  // v: R[i] for i >= b, 0 before
+      double vi[kSmallBlocks], vj[kSmallBlocks], ps[kSmallBlocks];
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p) {
+        vi[p] = vj[p] = 0.0;
+        if (p < KB || p >= nb) continue;
+        const double ri = R[ti + kGrid * p], rj = R[tj + kGrid * p];
+        vi[p] = (p > KB || ti >= br) ? ri : 0.0;
+        vj[p] = (p > KB || tj >= br) ? rj : 0.0;
+      }
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p) {
+        ps[p] = 0.0;
+        if (p < KB || p >= nb) continue;
+        double acc = 0.0;
+#pragma unroll
+        for (int q = KB; q < kSmallBlocks; ++q)
+          if (q < nb) acc += a[p][q] * vj[q];
+        ps[p] = sumrow_f64(acc);
+      }
+      if (tj == 0) {  // p_i for the row group's rows, and its part of v^T S' v
+        double vsv = 0.0;
+#pragma unroll
+        for (int p = KB; p < kSmallBlocks; ++p) {
+          if (p >= nb) continue;
+          part[0][ti + kGrid * p] = tk * ps[p];
+          vsv += ps[p] * vi[p];
+        }
+        kpart[ti] = vsv;
+      }
+      __syncthreads();
+      // K = (tau / 2) p^T v = (tau^2 / 2) v^T S' v
+      const double K = 0.5 * tk * tk * sumrow_f64(kpart[tj]);
+      double wi[kSmallBlocks], wj[kSmallBlocks];
+#pragma unroll
+      for (int p = 0; p < kSmallBlocks; ++p) {
+        wi[p] = wj[p] = 0.0;
+        if (p < KB || p >= nb) continue;
+        wi[p] = part[0][ti + kGrid * p] - K * vi[p];
+        wj[p] = part[0][tj + kGrid * p] - K * vj[p];
+      }
+#pragma unroll
+      for (int p = KB; p < kSmallBlocks; ++p) {
+        if (p >= nb) continue;
+#pragma unroll
+        for (int q = KB; q < kSmallBlocks; ++q) {
+          if (q >= nb) continue;
+          const double d = vi[p] * wj[q] + wi[p] * vj[q];
+          if (p == KB || q == KB) {  // the straddling block: only entries i, j >= b
+            const bool in = (p > KB || ti >= br) && (q > KB || tj >= br);
+            a[p][q] = in ? a[p][q] - d : a[p][q];
+          } else {
+            a[p][q] -= d;
+          }
+        }
+      }
+    };
+    static_assert(kSmallBlocks == 3, "one instantiation per pair of blocks");
+    for (int k = 0; k < L - 2; ++k) {
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      if (k < kGrid - 1) hstep(I0{}, I0{}, k);
+      else if (k == kGrid - 1) hstep(I0{}, I1{}, k);
+      else if (k < 2 * kGrid - 1) hstep(I1{}, I1{}, k);
+      else if (k == 2 * kGrid - 1) hstep(I1{}, I2{}, k);
+      else hstep(I2{}, I2{}, k);
     }
     publish(L - 2);
     publish(L - 1);
