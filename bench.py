@@ -519,7 +519,7 @@ KERNEL_SUMMARIES = {
                 "Delta W and split_sum_kernel; gram_kernel + gram_sum_kernel; "
                 "chol_inverse_small_kernel, the Cholesky QR of the power steps and of the two "
                 "final orthonormalization passes; syev_kernel, the tridiagonal eigensolver of "
-                "B_m B_m^T; transform/apply kernels), "
+                "B_m B_m^T; transform_kernel, apply_small_kernel), "
                 "oversample 32, 4 power steps, b2 g32 and b4 g64 weights from hqq_quantize, "
                 "1 warm-up + 2 timed calls per matrix, plus the quantization and the quality "
                 "check (bench.py measure_lowrank)."),

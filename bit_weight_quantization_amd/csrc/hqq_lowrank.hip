@@ -1145,6 +1145,82 @@ __global__ __launch_bounds__(kBlock) void apply_kernel(const float* __restrict__
   }
 }
 
+// apply_kernel for L = 32 LB <= 96: the block's 64 rows of X (all L columns) and T's 32
+// columns come in with one round of 16-byte loads, all issued before any is stored to
+// LDS (one global latency per block instead of one per 32 columns).  Same outputs.
+template <int LB>
+__global__ __launch_bounds__(kBlock) void apply_small_kernel(const float* __restrict__ X, int64_t M,
+                                                             const float* __restrict__ T, int C,
+                                                             float* __restrict__ out_rm,
+                                                             float* __restrict__ out_t32,
+                                                             uint16_t* __restrict__ out_t16) {
+  constexpr int L = 32 * LB, XR = L + 1;  // X rows in LDS: odd stride
+  constexpr int NX = 64 * L / 4 / kBlock, NT = L * 32 / 4 / kBlock;  // 16-byte loads per thread
+  __shared__ float xs[64 * XR], ts[L * 33];
+  const int t = threadIdx.x;
+  const int c0 = blockIdx.y * 32;
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  float4 xv[NX], tv4[NT];
+#pragma unroll
+  for (int u = 0; u < NX; ++u) {
+    const int e = t + u * kBlock, r = e / (L / 4), g = e % (L / 4);
+    const int64_t i = i0 + r < M ? i0 + r : M - 1;  // rows past M: unused
+    xv[u] = reinterpret_cast<const float4*>(X + i * L)[g];
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int e = t + u * kBlock, b = e >> 3, g = e & 7;
+    tv4[u] = c0 + 4 * g < C ? reinterpret_cast<const float4*>(T + (int64_t)b * C + c0)[g]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < NX; ++u) {
+    const int e = t + u * kBlock, r = e / (L / 4), g = e % (L / 4);
+    float* d = xs + r * XR + 4 * g;
+    d[0] = xv[u].x; d[1] = xv[u].y; d[2] = xv[u].z; d[3] = xv[u].w;
+  }
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int e = t + u * kBlock, b = e >> 3, g = e & 7;
+    float* d = ts + b * 33 + 4 * g;
+    d[0] = tv4[u].x; d[1] = tv4[u].y; d[2] = tv4[u].z; d[3] = tv4[u].w;
+  }
+  __syncthreads();
+  const int c = t & 31, rb = (t >> 5) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int b = 0; b < L; ++b) {
+    const float tv = ts[b * 33 + c];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = __builtin_fmaf(xs[(rb + r) * XR + b], tv, acc[r]);
+  }
+  if (c0 + c >= C) return;
+  const int64_t ib = i0 + rb;  // a multiple of 8; all 8 rows valid when ib < M
+  if (ib >= M) return;
+  if (out_rm) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) out_rm[(ib + r) * C + c0 + c] = acc[r];
+  }
+  if (out_t32) {
+    float* o = out_t32 + (int64_t)(c0 + c) * M + ib;
+    if ((reinterpret_cast<uintptr_t>(out_t32) & 15) == 0) {  // the caller's buffer may be 4-aligned
+      reinterpret_cast<float4*>(o)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      reinterpret_cast<float4*>(o)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) o[r] = acc[r];
+    }
+  }
+  if (out_t16) {
+    uint4 h;
+    h.x = f2h(acc[0]) | (f2h(acc[1]) << 16);
+    h.y = f2h(acc[2]) | (f2h(acc[3]) << 16);
+    h.z = f2h(acc[4]) | (f2h(acc[5]) << 16);
+    h.w = f2h(acc[6]) | (f2h(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out_t16 + (int64_t)(c0 + c) * M + ib) = h;
+  }
+}
+
 // ------------------------------------------------------------------ driver --
 
 struct Carve {
@@ -1256,6 +1332,21 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
                        L, G);
     return hipGetLastError();
   };
+  // X (M x L fp32) times T (L x C): apply_small_kernel where L <= 96 and C % 4 == 0 (its
+  // 16-byte loads of T stay aligned), else apply_kernel
+  auto apply = [&](const float* X, int64_t M, int C, float* o_rm, float* o_t32, uint16_t* o_t16) -> hipError_t {
+    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((C + 31) / 32));
+    if (C % 4 == 0 && L <= kLdsWidth) {
+      switch (L / kGrid) {
+        case 1: hipLaunchKernelGGL(apply_small_kernel<1>, grid, dim3(kBlock), 0, st, X, M, T, C, o_rm, o_t32, o_t16); break;
+        case 2: hipLaunchKernelGGL(apply_small_kernel<2>, grid, dim3(kBlock), 0, st, X, M, T, C, o_rm, o_t32, o_t16); break;
+        default: hipLaunchKernelGGL(apply_small_kernel<3>, grid, dim3(kBlock), 0, st, X, M, T, C, o_rm, o_t32, o_t16); break;
+      }
+    } else {
+      hipLaunchKernelGGL(apply_kernel, grid, dim3(kBlock), apply_lds, st, X, M, L, T, C, o_rm, o_t32, o_t16);
+    }
+    return hipGetLastError();
+  };
   // out32 (M x L fp32, may be null) and out16 (L x M binary16, transposed, may be null) =
   // X T with T from the Cholesky QR of X (M x L fp32): the Gram-Schmidt basis of X
   auto cholqr = [&](const float* X, int64_t M, float* out32, uint16_t* out16) -> hipError_t {
@@ -1266,9 +1357,7 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
     else
       hipLaunchKernelGGL(chol_inverse_kernel, dim3(1), dim3(kCholThreads), 0, st, G, V, L, T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((M + 63) / 64), (unsigned)(L / 32)), dim3(kBlock),
-                       apply_lds, st, X, M, L, T, L, out32, (float*)nullptr, out16);
-    return hipGetLastError();
+    return apply(X, M, L, out32, (float*)nullptr, out16);
   };
 
   if ((err = launch_residual(P.W, P.packed, P.scale16, P.zero16, m, n, P.nbits, P.group_size, dW,
@@ -1296,15 +1385,11 @@ hipError_t launch_lowrank(const LowrankParams& P, int cus, hipStream_t st) {
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 1, T, P.sigma);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((m + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock),
-                     apply_lds, st, Y, m, L, T, r, P.B, (float*)nullptr, (uint16_t*)nullptr);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = apply(Y, m, r, P.B, (float*)nullptr, (uint16_t*)nullptr)) != hipSuccess) return err;
   hipLaunchKernelGGL(transform_kernel, dim3((unsigned)((L * r + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                      V, ev, ord, L, r, 2, T, (float*)nullptr);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(apply_kernel, dim3((unsigned)((n + 63) / 64), (unsigned)((r + 31) / 32)), dim3(kBlock),
-                     apply_lds, st, Q32, n, L, T, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
-  return hipGetLastError();
+  return apply(Q32, n, r, (float*)nullptr, P.A, (uint16_t*)nullptr);
 }
 
 }  // namespace hqq
