@@ -128,7 +128,8 @@ constexpr int kLdsRow = kBK + 8;
 // P[z][i][j] = sum over k in split z's slice of A[i][k] * B[j][k]: A is M x K and B is
 // L x K binary16 (K contiguous), P fp32 (M x L per split).  128 x 128 tiles of four
 // wavefronts (2 x 2 v_mfma_f32_32x32x16_f16 each), 64-wide K steps through double-buffered
-// LDS.  M and K are multiples of 64; rows of B past L are zero.
+// LDS with two steps of loads in flight.  M and K are multiples of 64; rows of B past L
+// are zero.
 __global__ __launch_bounds__(kBlock) void gemm16_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
                                                         int64_t M, int64_t K, int L,
@@ -142,27 +143,49 @@ __global__ __launch_bounds__(kBlock) void gemm16_kernel(const uint16_t* __restri
   const int n0 = blockIdx.y * kBN;
   const int64_t kb = (int64_t)blockIdx.z * kslice;
   const int64_t ke = kb + kslice < K ? kb + kslice : K;
-  const int lr = tid >> 1, lh = tid & 1;
-  const bool a_ok = m0 + lr < M, b_ok = n0 + lr < L;
-  const uint16_t* arow = A + (a_ok ? m0 + lr : 0) * K;
-  const uint16_t* brow = B + (int64_t)(b_ok ? n0 + lr : 0) * K;
-  uint4 ar[4], br[4];
-  auto load_global = [&](int64_t k0) {
-    const uint4* ap = reinterpret_cast<const uint4*>(arow + k0 + 32 * lh);
-    const uint4* bp = reinterpret_cast<const uint4*>(brow + k0 + 32 * lh);
+  // loads: 8 adjacent lanes take one row's 64 K values (128 bytes, 16 each); load i of a
+  // thread covers rows lr + 32 i, so one wave's load reads 8 whole rows.  Rows past M or
+  // L read row 0 and are stored as zeros.
+  const int lr = tid >> 3, lg = tid & 7;
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  bool a_ok[4], b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lr + 32 * i;
+    a_ok[i] = m0 + r < M;
+    b_ok[i] = n0 + r < L;
+    arow[i] = A + (a_ok[i] ? m0 + r : 0) * K + 8 * lg;
+    brow[i] = B + (int64_t)(b_ok[i] ? n0 + r : 0) * K + 8 * lg;
+  }
+  // two register sets: while step s is multiplied out of LDS, step s + 1 is in flight in
+  // one set and step s + 2 is issued into the other (the loop is unrolled by two so the
+  // sets stay fixed registers); past the last step the loads repeat it and are unused
+  // Each row block starts its slice at its own step (blockIdx.x mod the step count) and
+  // wraps around, so that blocks running together read different 128-byte columns of
+  // the rows rather than addresses one row stride apart.
+  const int nst = kb < ke ? (int)((ke - kb) / kBK) : 0;
+  const int rot = nst > 0 ? (int)(blockIdx.x % (unsigned)nst) : 0;
+  auto kpos = [&](int st) {
+    int q = (st < nst ? st : nst - 1) + rot;
+    q = q >= nst ? q - nst : q;
+    return kb + (int64_t)q * kBK;
+  };
+  // native 4 x 32-bit vectors: a select between two of them stays in registers
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4), may_alias));
+  auto load_global = [&](u32x4 (&ra)[4], u32x4 (&rb)[4], int64_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ar[i] = a_ok ? ap[i] : make_uint4(0u, 0u, 0u, 0u);
-      br[i] = b_ok ? bp[i] : make_uint4(0u, 0u, 0u, 0u);
+      ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);
+      rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + k0);
     }
   };
-  auto store_lds = [&](int buf) {
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lr][32 * lh]);
-    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lr][32 * lh]);
+  auto store_lds = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ad[i] = ar[i];
-      bd[i] = br[i];
+      *reinterpret_cast<u32x4*>(&As[buf][lr + 32 * i][8 * lg]) = a_ok[i] ? ra[i] : z;
+      *reinterpret_cast<u32x4*>(&Bs[buf][lr + 32 * i][8 * lg]) = b_ok[i] ? rb[i] : z;
     }
   };
   float16_t acc[2][2];
@@ -172,15 +195,7 @@ __global__ __launch_bounds__(kBlock) void gemm16_kernel(const uint16_t* __restri
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (kb < ke) {
-    load_global(kb);
-    store_lds(0);
-  }
-  __syncthreads();
-  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
-    const int buf = (int)(((k0 - kb) / kBK) & 1);
-    const bool more = k0 + kBK < ke;
-    if (more) load_global(k0 + kBK);
+  auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kk = ks * 16 + (lane >> 5) * 8;
@@ -197,9 +212,31 @@ __global__ __launch_bounds__(kBlock) void gemm16_kernel(const uint16_t* __restri
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store_lds(buf ^ 1);
+  };
+  u32x4 a0[4], b0[4], a1[4], b1[4];
+  if (nst > 0) {
+    load_global(a0, b0, kpos(0));
+    load_global(a1, b1, kpos(1));
+    store_lds(0, a0, b0);
+  }
+  __syncthreads();
+  // pairs of steps in one straight-line body (even steps in LDS buffer 0, odd in 1), so
+  // each wait is for the older set only; an odd last step follows the loop
+  int st = 0;
+  // (the scheduling barriers keep each half's loads ahead of its products)
+  for (; st + 1 < nst; st += 2) {
+    load_global(a0, b0, kpos(st + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(0);
+    store_lds(1, a1, b1);
+    __syncthreads();
+    load_global(a1, b1, kpos(st + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(1);
+    store_lds(0, a0, b0);
     __syncthreads();
   }
+  if (st < nst) mfma_step(0);
   float* out = P + (int64_t)blockIdx.z * M * L;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -235,7 +272,8 @@ __global__ __launch_bounds__(kBlock) void split_sum_kernel(const float* __restri
 // Thread t: entry a0 + t % 32, b0 + 4 (t / 32) .. + 4.
 __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ X, int64_t M, int L,
                                                       int64_t rs, double* __restrict__ Gp) {
-  __shared__ float xa[64][33], xb[64][33];
+  __shared__ float xa[64][33];
+  __shared__ __align__(16) float xb[64][36];  // 16-byte rows: 4 values of a row in one read
   const int t = threadIdx.x;
   const int nt = L / 32;
   int A = 0, idx = blockIdx.x;
@@ -248,22 +286,45 @@ __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ 
   const int64_t r1 = r0 + rs < M ? r0 + rs : M;
   const int ta = t & 31, tb = (t >> 5) * 4;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  // a chunk: 64 rows x 32 columns of each slab, two 16-byte loads per slab and thread
+  // (rows past r1 read row r1 - 1 and count as zeros); the next chunk is loaded during
+  // this chunk's arithmetic
+  float4 pa[2], pb[2];
+  auto load = [&](int64_t i0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = t + u * kBlock, r = e >> 3, g = e & 7;
+      const int64_t i = i0 + r;
+      const float* row = X + (i < r1 ? i : r1 - 1) * L;
+      const float4 va = *reinterpret_cast<const float4*>(row + a0 + 4 * g);
+      const float4 vb = *reinterpret_cast<const float4*>(row + b0 + 4 * g);
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      pa[u] = i < r1 ? va : z;
+      pb[u] = i < r1 ? vb : z;
+    }
+  };
+  if (r0 < r1) load(r0);
   for (int64_t i0 = r0; i0 < r1; i0 += 64) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // 64 rows x 32 columns of each slab, 8 values per thread
-      const int e = t + u * kBlock;
-      const int r = e >> 5, c = e & 31;
-      const int64_t i = i0 + r;
-      xa[r][c] = i < r1 ? X[i * L + a0 + c] : 0.f;
-      xb[r][c] = i < r1 ? X[i * L + b0 + c] : 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int e = t + u * kBlock, r = e >> 3, g = e & 7;
+      xa[r][4 * g] = pa[u].x;
+      xa[r][4 * g + 1] = pa[u].y;
+      xa[r][4 * g + 2] = pa[u].z;
+      xa[r][4 * g + 3] = pa[u].w;
+      *reinterpret_cast<float4*>(&xb[r][4 * g]) = pb[u];
     }
     __syncthreads();
+    if (i0 + 64 < r1) load(i0 + 64);
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int r = 0; r < 64; ++r) {
       const float va = xa[r][ta];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[j] = __builtin_fmaf(va, xb[r][tb + j], part[j]);
+      const float4 vb = *reinterpret_cast<const float4*>(&xb[r][tb]);
+      part[0] = __builtin_fmaf(va, vb.x, part[0]);
+      part[1] = __builtin_fmaf(va, vb.y, part[1]);
+      part[2] = __builtin_fmaf(va, vb.z, part[2]);
+      part[3] = __builtin_fmaf(va, vb.w, part[3]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += (double)part[j];
@@ -276,7 +337,8 @@ __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ 
 
 // G[a][b] = sum over the splits of Gp[z][a][b], read from the tile on or above the
 // diagonal (so G is exactly symmetric).  Block: 64 entries x 4 groups of splits; group g
-// sums splits g, g + 4, ... in order, then the four group sums are added in order.
+// takes splits g, g + 4, ... into four chains in a fixed order, then the four group sums
+// are added in order, so the result does not depend on timing.
 constexpr int kGramSumGroups = kBlock / 64;
 __global__ __launch_bounds__(kBlock) void gram_sum_kernel(const double* __restrict__ Gp, int splits,
                                                           int L, double* __restrict__ G) {
@@ -289,14 +351,19 @@ __global__ __launch_bounds__(kBlock) void gram_sum_kernel(const double* __restri
   if (e < count) {
     const int a = (int)(e / L), b = (int)(e % L);
     src = (a >> 5) <= (b >> 5) ? e : (int64_t)b * L + a;
-    double s0 = 0.0, s1 = 0.0;  // two chains over alternate splits of the group
+    // four chains over the group's splits z = g + G (4 c + j), their loads issued
+    // together; then added in a fixed order
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
     int z = g;
-    for (; z + kGramSumGroups < splits; z += 2 * kGramSumGroups) {
-      s0 += Gp[(int64_t)z * count + src];
-      s1 += Gp[(int64_t)(z + kGramSumGroups) * count + src];
+    for (; z + 3 * kGramSumGroups < splits; z += 4 * kGramSumGroups) {
+      double v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = Gp[(int64_t)(z + j * kGramSumGroups) * count + src];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s[j] += v4[j];
     }
-    if (z < splits) s0 += Gp[(int64_t)z * count + src];
-    v = s0 + s1;
+    for (int j = 0; z < splits; z += kGramSumGroups, ++j) s[j] += Gp[(int64_t)z * count + src];
+    v = (s[0] + s[1]) + (s[2] + s[3]);
   }
   red[g][eo] = v;
   __syncthreads();
