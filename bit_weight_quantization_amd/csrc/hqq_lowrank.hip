@@ -288,43 +288,53 @@ __global__ __launch_bounds__(kBlock) void gram_kernel(const float* __restrict__ 
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   // a chunk: 64 rows x 32 columns of each slab, two 16-byte loads per slab and thread
   // (rows past r1 read row r1 - 1 and count as zeros); the next chunk is loaded during
-  // this chunk's arithmetic
+  // this chunk's arithmetic, past the end too
   float4 pa[2], pb[2];
+  bool pok[2];
   auto load = [&](int64_t i0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = t + u * kBlock, r = e >> 3, g = e & 7;
       const int64_t i = i0 + r;
       const float* row = X + (i < r1 ? i : r1 - 1) * L;
-      const float4 va = *reinterpret_cast<const float4*>(row + a0 + 4 * g);
-      const float4 vb = *reinterpret_cast<const float4*>(row + b0 + 4 * g);
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      pa[u] = i < r1 ? va : z;
-      pb[u] = i < r1 ? vb : z;
+      pa[u] = *reinterpret_cast<const float4*>(row + a0 + 4 * g);
+      pb[u] = *reinterpret_cast<const float4*>(row + b0 + 4 * g);
+      pok[u] = i < r1;
     }
   };
   if (r0 < r1) load(r0);
   for (int64_t i0 = r0; i0 < r1; i0 += 64) {
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = t + u * kBlock, r = e >> 3, g = e & 7;
-      xa[r][4 * g] = pa[u].x;
-      xa[r][4 * g + 1] = pa[u].y;
-      xa[r][4 * g + 2] = pa[u].z;
-      xa[r][4 * g + 3] = pa[u].w;
-      *reinterpret_cast<float4*>(&xb[r][4 * g]) = pb[u];
+      const float4 va = pok[u] ? pa[u] : z, vb = pok[u] ? pb[u] : z;
+      xa[r][4 * g] = va.x;
+      xa[r][4 * g + 1] = va.y;
+      xa[r][4 * g + 2] = va.z;
+      xa[r][4 * g + 3] = va.w;
+      *reinterpret_cast<float4*>(&xb[r][4 * g]) = vb;
     }
     __syncthreads();
-    if (i0 + 64 < r1) load(i0 + 64);
+    load(i0 + 64);  // unconditional (rows clamp), so nothing waits for it before the products
     float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int r = 0; r < 64; ++r) {
-      const float va = xa[r][ta];
-      const float4 vb = *reinterpret_cast<const float4*>(&xb[r][tb]);
-      part[0] = __builtin_fmaf(va, vb.x, part[0]);
-      part[1] = __builtin_fmaf(va, vb.y, part[1]);
-      part[2] = __builtin_fmaf(va, vb.z, part[2]);
-      part[3] = __builtin_fmaf(va, vb.w, part[3]);
+    // 8 rows of LDS reads at a time ahead of their 32 products (row order kept)
+#pragma unroll 2
+    for (int rb = 0; rb < 64; rb += 8) {
+      float va[8];
+      float4 vb[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        va[u] = xa[rb + u][ta];
+        vb[u] = *reinterpret_cast<const float4*>(&xb[rb + u][tb]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        part[0] = __builtin_fmaf(va[u], vb[u].x, part[0]);
+        part[1] = __builtin_fmaf(va[u], vb[u].y, part[1]);
+        part[2] = __builtin_fmaf(va[u], vb[u].z, part[2]);
+        part[3] = __builtin_fmaf(va[u], vb[u].w, part[3]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] += (double)part[j];
@@ -1306,7 +1316,7 @@ constexpr int64_t kGramBudget = 16ll << 20;     // bytes of partial Gram matrice
 // Row splits of a Gram computation over M rows: enough blocks to fill the chip.
 int gram_splits(int64_t M, int L) {
   const int64_t nt = L / 32, tiles = nt * (nt + 1) / 2;  // tiles on and above the diagonal
-  int64_t s = (768 + tiles - 1) / tiles;
+  int64_t s = (256 + tiles - 1) / tiles;
   if (s > (M + 63) / 64) s = (M + 63) / 64;
   const int64_t cap = kGramBudget / ((int64_t)L * L * 8);
   if (s > cap) s = cap;
