@@ -1325,7 +1325,7 @@ int gram_splits(int64_t M, int L) {
 
 int gemm_splits(int64_t M, int64_t K, int L) {
   const int64_t tiles = ((M + kBM - 1) / kBM) * ((L + kBN - 1) / kBN);
-  int64_t s = (1024 + tiles - 1) / tiles;
+  int64_t s = (512 + tiles - 1) / tiles;
   if (s > 8) s = 8;
   if (s > K / kBK) s = K / kBK;
   const int64_t cap = kPartialBudget / (M * L * 4);
