@@ -442,7 +442,10 @@ def measure_lowrank(hq, lib, torch, Ws, settings, solver, stream, sh, dev, rank=
     Algorithmic HBM bytes per call: the residual (read W, codes, s, z; write Delta W in two
     layouts: 2 + b/8 + 4/g + 4 bytes per weight) and 2 q + 2 passes of the matrix-core
     products over the binary16 Delta W (2 bytes per weight each).  Quality: the relative
-    Frobenius error of W_hat and of W_hat + B A against W."""
+    Frobenius error of W_hat and of W_hat + B A against W.  Then the same calls with each
+    matrix on a stream of its own (default priority) and its own workspace, two calls per
+    stream between events on the bench stream: the one-block factorizations of one matrix
+    run beside the products of the others ("concurrent_total_ms")."""
     out = {"entry_point": "hqq_lowrank", "rank": rank, "oversample": oversample,
            "power_iters": power_iters, "matrices": [list(W.shape) for W in Ws], "per_setting": []}
     wmax = max(hq.hqq_lowrank_workspace_bytes(W.shape[0], W.shape[1], rank, oversample)
@@ -452,6 +455,7 @@ def measure_lowrank(hq, lib, torch, Ws, settings, solver, stream, sh, dev, rank=
         rows = []
         tot_ms = tot_bytes = 0.0
         err0 = err1 = wn = 0.0
+        calls = []  # (args, tensors kept alive) per matrix, for the concurrent pass
         for W in Ws:
             q = hq.quantize(W, nb, g, p=solver.p, beta=solver.beta, kappa=solver.kappa,
                             iters=solver.iters)
@@ -485,10 +489,39 @@ def measure_lowrank(hq, lib, torch, Ws, settings, solver, stream, sh, dev, rank=
             err1 += float(((dW - B @ A).double() ** 2).sum())
             rows.append({"shape": [m, n], "ms": round(ms, 3),
                          "hbm_GBs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1)})
-            del dW, Wf, q
+            calls.append((args, (q, omega, B, A, S)))
+            del dW, Wf
+        streams = [torch.cuda.Stream(device=dev) for _ in Ws]
+        wss = [torch.empty(hq.hqq_lowrank_workspace_bytes(W.shape[0], W.shape[1], rank, oversample),
+                           dtype=torch.uint8, device=dev) for W in Ws]
+        cargs = [args[:15] + (w.data_ptr(), s.cuda_stream)
+                 for (args, _), w, s in zip(calls, wss, streams)]
+        done = [torch.cuda.Event() for _ in Ws]
+
+        def concurrent(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for s in streams:
+                s.wait_event(e0)
+            for _ in range(reps):
+                for a in cargs:
+                    assert lib.hqq_lowrank(*a) == 0
+            for s, d in zip(streams, done):
+                d.record(s)
+                stream.wait_event(d)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        concurrent(1)
+        conc_ms = concurrent(2)
+        del calls, cargs, wss
         rec = {"setting": f"b{nb}g{g}", "matrices": rows, "total_ms": round(tot_ms, 3),
                "hbm_GBs_algorithmic": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1),
                "hbm_frac": round(tot_bytes / (tot_ms * 1e-3) / PEAK_HBM, 4),
+               "concurrent_total_ms": round(conc_ms, 3),
+               "concurrent_hbm_frac": round(tot_bytes / (conc_ms * 1e-3) / PEAK_HBM, 4),
                "rel_fro_quantized": round((err0 / wn) ** 0.5, 6),
                "rel_fro_with_lowrank": round((err1 / wn) ** 0.5, 6),
                "captured_fraction_of_error": round(1 - err1 / err0, 5)}

@@ -178,3 +178,36 @@ def test_llama70b_matrix_structure(hq):
     cap = float((S.double() ** 2).sum())
     assert abs(res - (tot - cap)) <= 32 * U16 * cap + 1e-6 * tot
     _say(f"  captured {cap / tot:.4f} of |dW|^2 with rank 64")
+
+
+def test_concurrent_calls_on_two_streams_match_sequential(hq):
+    """Two matrices' calls on streams of their own, each with its own workspace, run at
+    the same time and give bit for bit what the same calls give one after the other (the
+    library keeps no state between calls, and every sum has a fixed order)."""
+    wl = workloads.WORKLOADS["attn_4096x4096"]
+    cases = [(512, 1024, 4, 64, 21), (384, 2048, 2, 32, 22)]
+    inputs = []
+    for rows, cols, nbits, g, seed in cases:
+        W = workloads.generate(rows, cols, wl.dist, seed, "cpu").numpy()
+        r = oracle.hqq_quantize(W, nbits, g)
+        q = _quantized_weight(hq, W, r.packed, r.scale_f16, r.zero_f16, nbits, g)
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(seed)
+        omega = torch.randn((64 + 32, cols), generator=gen, device="cuda").half()
+        inputs.append((_dev16(W).view(torch.float16), q, omega))
+    seq = [hq.lowrank(W, q, 64, oversample=32, power_iters=4, omega=om) for W, q, om in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in inputs]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    conc = []
+    for s, (W, q, om) in zip(streams, inputs):
+        ws = torch.empty(hq.hqq_lowrank_workspace_bytes(W.shape[0], W.shape[1], 64, 32),
+                         dtype=torch.uint8, device="cuda")
+        conc.append((hq.lowrank(W, q, 64, oversample=32, power_iters=4, omega=om, workspace=ws,
+                                stream=s), ws))
+    torch.cuda.synchronize()
+    for (rows, cols, nbits, g, _), a, (b, _) in zip(cases, seq, conc):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), (rows, cols, nbits, g)
+        _say(f"{rows}x{cols} b{nbits} g{g}: concurrent call bit-identical to the sequential one")
