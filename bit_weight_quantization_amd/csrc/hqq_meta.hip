@@ -62,11 +62,22 @@ __device__ __forceinline__ uint16_t f64_to_f16(double x) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-__device__ __forceinline__ uint8_t meta_code(uint16_t h, double mn, double d) {
+// The code is decided without a division per value: with rd = 1/d (one IEEE division
+// per group), num * rd is within 2^-44 of the quotient u = num / d (u <= 255, two
+// roundings of relative 2^-53).  Rounding u to binary32 moves it by at most 2^-17, so
+// unless u lies within 2^-15 of a half-integer, binary32(u) and num * rd are on the same
+// side of it and the code is the nearest integer of num * rd; the rare values near a
+// half-integer take the exact quotient as defined.
+__device__ __forceinline__ uint8_t meta_code(uint16_t h, double mn, double d, double rd) {
   if (!(d > 0.0)) return 0;
-  const double u = ((half_to_double(h) - mn) * 255.0) / d;
-  const float q = __builtin_amdgcn_fmed3f(__builtin_rintf((float)u), 0.f, 255.f);
-  return (uint8_t)q;
+  const double num = (half_to_double(h) - mn) * 255.0;  // exact
+  const double ua = num * rd;
+  const double fl = __builtin_floor(ua);
+  const double fr = ua - fl;  // exact
+  float q;
+  if (__builtin_fabs(fr - 0.5) > 0x1p-15) q = (float)(fr > 0.5 ? fl + 1.0 : fl);
+  else q = __builtin_rintf((float)(num / d));
+  return (uint8_t)__builtin_amdgcn_fmed3f(q, 0.f, 255.f);
 }
 
 // Wave-wide min and max of the keys (every lane ends with the result).
@@ -82,11 +93,12 @@ __device__ __forceinline__ void wave_minmax(uint32_t& kmin, uint32_t& kmax) {
 
 // Meta scale and offset of a group from its min and max keys.
 __device__ __forceinline__ void meta_params(uint32_t kmin, uint32_t kmax, double& mn, double& d,
-                                            uint16_t& scale16, uint16_t& offset16) {
+                                            double& rd, uint16_t& scale16, uint16_t& offset16) {
   uint16_t hmn = half_of_key(kmin);
   if ((hmn & 0x7fffu) == 0) hmn = 0;  // a zero minimum is stored as +0
   mn = half_to_double(hmn);
   d = half_to_double(half_of_key(kmax)) - mn;  // exact in fp64
+  rd = d > 0.0 ? 1.0 / d : 0.0;
   scale16 = f64_to_f16(d > 0.0 ? d / 255.0 : 1.0);
   offset16 = hmn;
 }
@@ -110,10 +122,10 @@ __global__ __launch_bounds__(kMetaBlock) void meta_grouped_kernel(const uint16_t
     kmax = k > kmax ? k : kmax;
   }
   wave_minmax(kmin, kmax);
-  double mn, d;
+  double mn, d, rd;
   uint16_t s16, o16;
-  meta_params(uniform32(kmin), uniform32(kmax), mn, d, s16, o16);
-  for (int64_t i = g0 + lane; i < g1; i += 64) codes[i] = meta_code(v[i], mn, d);
+  meta_params(uniform32(kmin), uniform32(kmax), mn, d, rd, s16, o16);
+  for (int64_t i = g0 + lane; i < g1; i += 64) codes[i] = meta_code(v[i], mn, d, rd);
   if (lane == 0) {
     mscale[grp] = s16;
     moffset[grp] = o16;
@@ -165,12 +177,12 @@ __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_kernel(
     kmax = b > kmax ? b : kmax;
   }
   block_minmax(kmin, kmax);
-  double mn, d;
+  double mn, d, rd;
   uint16_t s16, o16;
-  meta_params(kmin, kmax, mn, d, s16, o16);
+  meta_params(kmin, kmax, mn, d, rd, s16, o16);
   const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
   for (int64_t i = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; i < n; i += stride)
-    codes[i] = meta_code(v[i], mn, d);
+    codes[i] = meta_code(v[i], mn, d, rd);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mscale[0] = s16;
     moffset[0] = o16;
@@ -212,13 +224,13 @@ __device__ __forceinline__ void chunk_keys(const uint4& raw, uint32_t& kmin, uin
   }
 }
 
-__device__ __forceinline__ uint2 chunk_codes(const uint4& raw, double mn, double d) {
+__device__ __forceinline__ uint2 chunk_codes(const uint4& raw, double mn, double d, double rd) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t c[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    c[2 * j] = meta_code((uint16_t)(w[j] & 0xffffu), mn, d);
-    c[2 * j + 1] = meta_code((uint16_t)(w[j] >> 16), mn, d);
+    c[2 * j] = meta_code((uint16_t)(w[j] & 0xffffu), mn, d, rd);
+    c[2 * j + 1] = meta_code((uint16_t)(w[j] >> 16), mn, d, rd);
   }
   return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
@@ -240,11 +252,11 @@ __global__ __launch_bounds__(kMetaBlock) void meta_grouped_vec_kernel(
     uint32_t kmin = 0xffffffffu, kmax = 0u;
     if (in) chunk_keys(raw, kmin, kmax);
     seg_minmax<L>(kmin, kmax);  // lanes past the end contribute neutral keys
-    double mn, d;
+    double mn, d, rd;
     uint16_t s16, o16;
-    meta_params(kmin, kmax, mn, d, s16, o16);
+    meta_params(kmin, kmax, mn, d, rd, s16, o16);
     if (in) {
-      codes[c] = chunk_codes(raw, mn, d);
+      codes[c] = chunk_codes(raw, mn, d, rd);
       if ((lane & (L - 1)) == 0) {
         mscale[c / L] = s16;
         moffset[c / L] = o16;
@@ -277,12 +289,12 @@ __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_vec_kernel(
     kmax = b > kmax ? b : kmax;
   }
   block_minmax(kmin, kmax);
-  double mn, d;
+  double mn, d, rd;
   uint16_t s16, o16;
-  meta_params(kmin, kmax, mn, d, s16, o16);
+  meta_params(kmin, kmax, mn, d, rd, s16, o16);
   const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
   for (int64_t c = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; c < nchunks; c += stride)
-    codes[c] = chunk_codes(v[c], mn, d);
+    codes[c] = chunk_codes(v[c], mn, d, rd);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mscale[0] = s16;
     moffset[0] = o16;
@@ -347,17 +359,17 @@ __global__ __launch_bounds__(kMetaBlock) void meta_seg_kernel(
       }
       __syncthreads();  // block_minmax's LDS is reused for the next entry
     } else {
-      double mn, d;
+      double mn, d, rd;
       uint16_t s16, o16;
-      meta_params(ws[2 * e], ws[2 * e + 1], mn, d, s16, o16);
+      meta_params(ws[2 * e], ws[2 * e + 1], mn, d, rd, s16, o16);
       if constexpr (VEC) {
         const uint4* vv = reinterpret_cast<const uint4*>(v);
         uint2* cc = reinterpret_cast<uint2*>(codes);
         for (int64_t c = lo / 8 + threadIdx.x; c < hi / 8; c += kMetaBlock)
-          cc[c] = chunk_codes(vv[c], mn, d);
+          cc[c] = chunk_codes(vv[c], mn, d, rd);
       } else {
         for (int64_t i = lo + threadIdx.x; i < hi; i += kMetaBlock)
-          codes[i] = meta_code(v[i], mn, d);
+          codes[i] = meta_code(v[i], mn, d, rd);
       }
       if (threadIdx.x == 0 && lo == E[e].first_group) {  // the block holding the entry's start
         mscale[e] = s16;
