@@ -6,7 +6,9 @@ roundings of exact values, so every output is compared bit for bit: on the s and
 z arrays the solver produces for workload matrices (z as one group per array, s
 in groups of 128), on ragged group counts, and on edge cases (constant arrays,
 +0/-0 minima, one value, groups of 1, 3, 5 and 1000 values, binary16 triples
-whose quotient lands on a half-integer only after binary32 rounding).
+whose quotient lands on a half-integer only after binary32 rounding, and triples whose
+quotient is on a half-integer or within 2^-15 of one, where the kernels leave the
+group's reciprocal for the exact quotient).
 """
 import numpy as np
 import pytest
@@ -157,3 +159,33 @@ def test_meta_batch_equals_per_matrix(hq, nbits, g):
                            one_s.scale.view(torch.int16))
         assert torch.equal(mz.codes[g0:g0 + ng], one_z.codes)
         assert torch.equal(mz.offset[i:i + 1].view(torch.int16), one_z.offset.view(torch.int16))
+
+
+def _near_half_triples(seed, want):
+    """binary16 triples (min, max, v) whose quotient (v - min) 255 / (max - min) lies
+    within 2^-15 of a half-integer: exactly on it, or off it by less than the margin
+    inside which the codes take the exact quotient instead of the group's reciprocal."""
+    rng = np.random.default_rng(seed)
+    exact, near = [], []
+    while len(exact) < want or len(near) < want:
+        a = rng.standard_normal((1 << 20, 3)).astype(np.float16)
+        a = a[np.isfinite(a).all(axis=1)]
+        lo = np.minimum(a[:, 0], a[:, 1]).astype(np.float64)
+        hi = np.maximum(a[:, 0], a[:, 1]).astype(np.float64)
+        v = a[:, 2].astype(np.float64)
+        ok = (hi > lo) & (v >= lo) & (v <= hi)
+        u = (v - lo) * 255.0 / np.where(ok, hi - lo, 1.0)
+        off = np.abs(u - np.floor(u) - 0.5)
+        trip = np.stack([lo, hi, v], axis=1).astype(np.float16)
+        exact += list(trip[ok & (off == 0.0)][:want])
+        near += list(trip[ok & (off > 0.0) & (off < 2.0 ** -15)][:want])
+    return np.array(exact[:want]), np.array(near[:want])
+
+
+def test_meta_codes_at_and_near_half_integers(hq):
+    """Quotients on a half-integer or within 2^-15 of one, in groups of three: the codes
+    must match the definition's binary32-then-half-even rounding bit for bit."""
+    exact, near = _near_half_triples(7, 64)
+    vals = np.concatenate([exact, near]).reshape(-1).view(np.uint16)
+    _check(hq, vals, 3)
+    _say(f"{len(exact)} triples on a half-integer, {len(near)} within 2^-15 of one: bit-exact")
