@@ -12,8 +12,9 @@
 //          rounded once to binary32, then half-even: the weight codes' precision);
 //   meta scale = binary16(d / 255) (RNE from fp64), meta offset = mn (a zero minimum
 //   as +0); a constant group has codes 0 and meta scale 1.
-// The quotient is computed in fp64 exactly as defined (v - mn and the product are
-// exact, the division is IEEE), so codes are bit-identical to that definition.
+// Codes are bit-identical to that definition: an fp32 estimate decides them where it
+// is provably on the same side of every rounding boundary, and the fp64 quotient as
+// defined (v - mn and the product exact, the division IEEE) decides the rest.
 //
 // Layout: values, codes, scales and offsets are flat arrays; lanes read and write
 // consecutive elements (2-byte loads, 1-byte stores, coalesced per wavefront).
@@ -62,21 +63,22 @@ __device__ __forceinline__ uint16_t f64_to_f16(double x) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
-// The code is decided without a division per value: with rd = 1/d (one IEEE division
-// per group), num * rd is within 2^-44 of the quotient u = num / d (u <= 255, two
-// roundings of relative 2^-53).  Rounding u to binary32 moves it by at most 2^-17, so
-// unless u lies within 2^-15 of a half-integer, binary32(u) and num * rd are on the same
-// side of it and the code is the nearest integer of num * rd; the rare values near a
-// half-integer take the exact quotient as defined.
-__device__ __forceinline__ uint8_t meta_code(uint16_t h, double mn, double d, double rd) {
+// The code is decided in fp32 without a division per value: x - min is rounded once
+// (binary16 values are exact in fp32) and c = fl32(255 / d) once per group, so
+// (x - min) c is within 3 2^-24 relative, i.e. 2^-14.4 absolute (u <= 255), of the
+// quotient u = (x - min) 255 / d.  Rounding u to binary32 moves it by at most 2^-17, so
+// unless u lies within 2^-12 of a half-integer, binary32(u) and the fp32 estimate are on
+// the same side of it and the code is the estimate's nearest integer; the values near a
+// half-integer (about 0.1% of random ones, and the exact binary16 ties) take the exact
+// fp64 quotient as defined.
+__device__ __forceinline__ uint8_t meta_code(uint16_t h, double mn, double d, float mn32, float c32) {
   if (!(d > 0.0)) return 0;
-  const double num = (half_to_double(h) - mn) * 255.0;  // exact
-  const double ua = num * rd;
-  const double fl = __builtin_floor(ua);
-  const double fr = ua - fl;  // exact
+  const float ua = ((float)__builtin_bit_cast(_Float16, h) - mn32) * c32;
+  const float fl = __builtin_floorf(ua);
+  const float fr = ua - fl;  // exact
   float q;
-  if (__builtin_fabs(fr - 0.5) > 0x1p-15) q = (float)(fr > 0.5 ? fl + 1.0 : fl);
-  else q = __builtin_rintf((float)(num / d));
+  if (__builtin_fabsf(fr - 0.5f) > 0x1p-12f) q = fr > 0.5f ? fl + 1.f : fl;
+  else q = __builtin_rintf((float)(((half_to_double(h) - mn) * 255.0) / d));
   return (uint8_t)__builtin_amdgcn_fmed3f(q, 0.f, 255.f);
 }
 
@@ -93,12 +95,14 @@ __device__ __forceinline__ void wave_minmax(uint32_t& kmin, uint32_t& kmax) {
 
 // Meta scale and offset of a group from its min and max keys.
 __device__ __forceinline__ void meta_params(uint32_t kmin, uint32_t kmax, double& mn, double& d,
-                                            double& rd, uint16_t& scale16, uint16_t& offset16) {
+                                            float& mn32, float& c32, uint16_t& scale16,
+                                            uint16_t& offset16) {
   uint16_t hmn = half_of_key(kmin);
   if ((hmn & 0x7fffu) == 0) hmn = 0;  // a zero minimum is stored as +0
   mn = half_to_double(hmn);
   d = half_to_double(half_of_key(kmax)) - mn;  // exact in fp64
-  rd = d > 0.0 ? 1.0 / d : 0.0;
+  mn32 = (float)mn;                        // exact (a binary16 value)
+  c32 = d > 0.0 ? (float)(255.0 / d) : 0.f;  // relative 2^-24
   scale16 = f64_to_f16(d > 0.0 ? d / 255.0 : 1.0);
   offset16 = hmn;
 }
@@ -122,10 +126,11 @@ __global__ __launch_bounds__(kMetaBlock) void meta_grouped_kernel(const uint16_t
     kmax = k > kmax ? k : kmax;
   }
   wave_minmax(kmin, kmax);
-  double mn, d, rd;
+  double mn, d;
+  float mn32, c32;
   uint16_t s16, o16;
-  meta_params(uniform32(kmin), uniform32(kmax), mn, d, rd, s16, o16);
-  for (int64_t i = g0 + lane; i < g1; i += 64) codes[i] = meta_code(v[i], mn, d, rd);
+  meta_params(uniform32(kmin), uniform32(kmax), mn, d, mn32, c32, s16, o16);
+  for (int64_t i = g0 + lane; i < g1; i += 64) codes[i] = meta_code(v[i], mn, d, mn32, c32);
   if (lane == 0) {
     mscale[grp] = s16;
     moffset[grp] = o16;
@@ -177,12 +182,13 @@ __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_kernel(
     kmax = b > kmax ? b : kmax;
   }
   block_minmax(kmin, kmax);
-  double mn, d, rd;
+  double mn, d;
+  float mn32, c32;
   uint16_t s16, o16;
-  meta_params(kmin, kmax, mn, d, rd, s16, o16);
+  meta_params(kmin, kmax, mn, d, mn32, c32, s16, o16);
   const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
   for (int64_t i = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; i < n; i += stride)
-    codes[i] = meta_code(v[i], mn, d, rd);
+    codes[i] = meta_code(v[i], mn, d, mn32, c32);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mscale[0] = s16;
     moffset[0] = o16;
@@ -224,13 +230,14 @@ __device__ __forceinline__ void chunk_keys(const uint4& raw, uint32_t& kmin, uin
   }
 }
 
-__device__ __forceinline__ uint2 chunk_codes(const uint4& raw, double mn, double d, double rd) {
+__device__ __forceinline__ uint2 chunk_codes(const uint4& raw, double mn, double d, float mn32,
+                                             float c32) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t c[8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    c[2 * j] = meta_code((uint16_t)(w[j] & 0xffffu), mn, d, rd);
-    c[2 * j + 1] = meta_code((uint16_t)(w[j] >> 16), mn, d, rd);
+    c[2 * j] = meta_code((uint16_t)(w[j] & 0xffffu), mn, d, mn32, c32);
+    c[2 * j + 1] = meta_code((uint16_t)(w[j] >> 16), mn, d, mn32, c32);
   }
   return make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                     c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
@@ -244,19 +251,26 @@ __global__ __launch_bounds__(kMetaBlock) void meta_grouped_vec_kernel(
     uint16_t* __restrict__ mscale, uint16_t* __restrict__ moffset) {
   const int lane = threadIdx.x & 63;
   const int64_t nwaves = (int64_t)gridDim.x * (kMetaBlock / 64);
-  for (int64_t w = uniform64m(((int64_t)blockIdx.x * kMetaBlock + threadIdx.x) / 64);
-       w * 64 < nchunks; w += nwaves) {
+  const int64_t w0 = uniform64m(((int64_t)blockIdx.x * kMetaBlock + threadIdx.x) / 64);
+  // the next iteration's chunk is loaded before this one's arithmetic (from a clamped
+  // index, so the load is unconditional and nothing waits for it early)
+  auto fetch = [&](int64_t w) { const int64_t c = w * 64 + lane; return v[c < nchunks ? c : nchunks - 1]; };
+  uint4 nxt = w0 * 64 < nchunks ? fetch(w0) : make_uint4(0u, 0u, 0u, 0u);
+  for (int64_t w = w0; w * 64 < nchunks; w += nwaves) {
     const int64_t c = w * 64 + lane;
     const bool in = c < nchunks;
-    const uint4 raw = in ? v[c] : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 cur = nxt;
+    nxt = fetch(w + nwaves);
+    const uint4 raw = in ? cur : make_uint4(0u, 0u, 0u, 0u);
     uint32_t kmin = 0xffffffffu, kmax = 0u;
     if (in) chunk_keys(raw, kmin, kmax);
     seg_minmax<L>(kmin, kmax);  // lanes past the end contribute neutral keys
-    double mn, d, rd;
+    double mn, d;
+    float mn32, c32;
     uint16_t s16, o16;
-    meta_params(kmin, kmax, mn, d, rd, s16, o16);
+    meta_params(kmin, kmax, mn, d, mn32, c32, s16, o16);
     if (in) {
-      codes[c] = chunk_codes(raw, mn, d, rd);
+      codes[c] = chunk_codes(raw, mn, d, mn32, c32);
       if ((lane & (L - 1)) == 0) {
         mscale[c / L] = s16;
         moffset[c / L] = o16;
@@ -289,12 +303,13 @@ __global__ __launch_bounds__(kMetaBlock) void meta_quant_all_vec_kernel(
     kmax = b > kmax ? b : kmax;
   }
   block_minmax(kmin, kmax);
-  double mn, d, rd;
+  double mn, d;
+  float mn32, c32;
   uint16_t s16, o16;
-  meta_params(kmin, kmax, mn, d, rd, s16, o16);
+  meta_params(kmin, kmax, mn, d, mn32, c32, s16, o16);
   const int64_t stride = (int64_t)gridDim.x * kMetaBlock;
   for (int64_t c = (int64_t)blockIdx.x * kMetaBlock + threadIdx.x; c < nchunks; c += stride)
-    codes[c] = chunk_codes(v[c], mn, d, rd);
+    codes[c] = chunk_codes(v[c], mn, d, mn32, c32);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mscale[0] = s16;
     moffset[0] = o16;
@@ -359,17 +374,18 @@ __global__ __launch_bounds__(kMetaBlock) void meta_seg_kernel(
       }
       __syncthreads();  // block_minmax's LDS is reused for the next entry
     } else {
-      double mn, d, rd;
+      double mn, d;
+      float mn32, c32;
       uint16_t s16, o16;
-      meta_params(ws[2 * e], ws[2 * e + 1], mn, d, rd, s16, o16);
+      meta_params(ws[2 * e], ws[2 * e + 1], mn, d, mn32, c32, s16, o16);
       if constexpr (VEC) {
         const uint4* vv = reinterpret_cast<const uint4*>(v);
         uint2* cc = reinterpret_cast<uint2*>(codes);
         for (int64_t c = lo / 8 + threadIdx.x; c < hi / 8; c += kMetaBlock)
-          cc[c] = chunk_codes(vv[c], mn, d, rd);
+          cc[c] = chunk_codes(vv[c], mn, d, mn32, c32);
       } else {
         for (int64_t i = lo + threadIdx.x; i < hi; i += kMetaBlock)
-          codes[i] = meta_code(v[i], mn, d, rd);
+          codes[i] = meta_code(v[i], mn, d, mn32, c32);
       }
       if (threadIdx.x == 0 && lo == E[e].first_group) {  // the block holding the entry's start
         mscale[e] = s16;
