@@ -357,7 +357,10 @@ int hqq_residual(const void* W_f16, const void* packed_codes, const void* scale_
  *              memory, 256-byte aligned, owned by the caller, not shared by calls that may
  *              run at the same time (it holds Delta W in both layouts and the iterates).
  * All outputs are alignment 4.  Work is enqueued on `stream` (no allocation, no
- * synchronization); conventions and errors as for hqq_quantize.
+ * synchronization); conventions and errors as for hqq_quantize.  The library keeps no
+ * state between calls, so calls on different streams with workspaces of their own may
+ * run at the same time (one matrix's one-block factorizations then overlap another's
+ * products), with results bit-identical to the same calls made one after another.
  */
 int hqq_lowrank(const void* W_f16, const void* packed_codes, const void* scale_f16,
                 const void* zero_f16, int64_t rows, int64_t cols, int nbits, int group_size,
