@@ -8,13 +8,12 @@
 // values (no solver), groups of M consecutive values (M = 0: one group of all n
 // values; the last group may be shorter):
 //   mn, mx over the group; d = mx - mn;
-//   code = clamp(rint(binary32(((v - mn) * 255) / d)), 0, 255)  (fp64 quotient,
-//          rounded once to binary32, then half-even: the weight codes' precision);
+//   code = the integer nearest the exact ratio (v - mn) * 255 / d, half to even;
 //   meta scale = binary16(d / 255) (RNE from fp64), meta offset = mn (a zero minimum
 //   as +0); a constant group has codes 0 and meta scale 1.
 // Codes are bit-identical to that definition: an fp32 estimate decides them where it
-// is provably on the same side of every rounding boundary, and the fp64 quotient as
-// defined (v - mn and the product exact, the division IEEE) decides the rest.
+// is provably on the same side of every rounding boundary, and an exact fp64
+// comparison of the ratio with the half-integer decides the rest.
 //
 // Layout: values, codes, scales and offsets are flat arrays; lanes read and write
 // consecutive elements (2-byte loads, 1-byte stores, coalesced per wavefront).
@@ -66,19 +65,27 @@ __device__ __forceinline__ uint16_t f64_to_f16(double x) {
 // The code is decided in fp32 without a division per value: x - min is rounded once
 // (binary16 values are exact in fp32) and c = fl32(255 / d) once per group, so
 // (x - min) c is within 3 2^-24 relative, i.e. 2^-14.4 absolute (u <= 255), of the
-// quotient u = (x - min) 255 / d.  Rounding u to binary32 moves it by at most 2^-17, so
-// unless u lies within 2^-12 of a half-integer, binary32(u) and the fp32 estimate are on
-// the same side of it and the code is the estimate's nearest integer; the values near a
-// half-integer (about 0.1% of random ones, and the exact binary16 ties) take the exact
-// fp64 quotient as defined.
+// ratio u = (x - min) 255 / d.  Unless the estimate lies within 2^-12 of a
+// half-integer, u is on the same side of that half-integer and the code is the
+// estimate's nearest integer.  Near a half-integer (about 0.1% of random values, and
+// the exact binary16 ties) the candidates are fl and fl + 1 and the ratio is compared
+// with fl + 1/2 exactly: 2 (x - min) 255 against (2 fl + 1) d, where x - min, d and
+// both products are multiples of 2^-24 below 2^51 units, so every term is an exact
+// fp64 value and an exact midpoint goes to the even code.
 __device__ __forceinline__ uint8_t meta_code(uint16_t h, double mn, double d, float mn32, float c32) {
   if (!(d > 0.0)) return 0;
   const float ua = ((float)__builtin_bit_cast(_Float16, h) - mn32) * c32;
   const float fl = __builtin_floorf(ua);
   const float fr = ua - fl;  // exact
   float q;
-  if (__builtin_fabsf(fr - 0.5f) > 0x1p-12f) q = fr > 0.5f ? fl + 1.f : fl;
-  else q = __builtin_rintf((float)(((half_to_double(h) - mn) * 255.0) / d));
+  if (__builtin_fabsf(fr - 0.5f) > 0x1p-12f) {
+    q = fr > 0.5f ? fl + 1.f : fl;
+  } else {
+    const double num2 = 2.0 * ((half_to_double(h) - mn) * 255.0);
+    const double mid = (2.0 * (double)fl + 1.0) * d;
+    const bool odd = ((int)fl & 1) != 0;
+    q = (num2 > mid || (num2 == mid && odd)) ? fl + 1.f : fl;
+  }
   return (uint8_t)__builtin_amdgcn_fmed3f(q, 0.f, 255.f);
 }
 

@@ -58,6 +58,10 @@ def _load():
     lib.oracle_shrink_lp.argtypes = [D, D, D]
     lib.oracle_quantize_value.restype = D
     lib.oracle_quantize_value.argtypes = [D, D, D, I]
+    lib.oracle_round_ratio.restype = D
+    lib.oracle_round_ratio.argtypes = [D, D]
+    lib.oracle_quantize_init_value.restype = D
+    lib.oracle_quantize_init_value.argtypes = [D, D, D, I]
     lib.oracle_minmax_init.argtypes = [P, I, I, P, P, P]
     lib.oracle_group_error.restype = D
     lib.oracle_group_error.argtypes = [P, I, D]
@@ -127,6 +131,14 @@ def shrink_lp(x: float, beta: float, p: float) -> float:
 
 def quantize_value(w: float, inv_s: float, z: float, qmax: int) -> float:
     return _load().oracle_quantize_value(float(w), float(inv_s), float(z), int(qmax))
+
+
+def round_ratio(num: float, den: float) -> float:
+    return _load().oracle_round_ratio(float(num), float(den))
+
+
+def quantize_init_value(w: float, mn: float, mx: float, qmax: int) -> float:
+    return _load().oracle_quantize_init_value(float(w), float(mn), float(mx), int(qmax))
 
 
 def minmax_init(w: np.ndarray, nbits: int):

@@ -22,8 +22,11 @@
  * Readings where the page is silent (each listed in the design notes):
  *   init     min-max: s = (max-min)/qmax, inv_s = qmax/(max-min), z = -min*inv_s
  *            (real-valued z); a constant group takes s = inv_s = 1.
- *   round    round half to even (nearbyint under FE_TONEAREST), decided on the
- *            binary32 rounding of the fp64 value w/s + z (the device's precision).
+ *   round    round half to even.  At the initial zero-point z0 = -min/s the value
+ *            w/s + z0 = (w - min) qmax / (max - min) is a ratio of binary16
+ *            differences, and its code is decided exactly (integer-valued fp64
+ *            comparisons, no rounding); at later steps z is the oracle's fp64
+ *            iterate and the code is nearbyint of the fp64 value w (1/s) + z.
  *   clamp    codes clamped to [0, qmax] after rounding.
  *   shrink   exactly the section-2.1 operator; 0 at x = 0 (where |x|^(p-1)
  *            is undefined for p < 1).
@@ -44,9 +47,9 @@
  *            binary16 values, one group per array for the zero-points, runs of
  *            128 consecutive values (row-major group order, shorter last run) for
  *            the scales; the group min and max map to codes 0 and 255, the code
- *            is decided on the binary32 rounding of the fp64 quotient (as for the
- *            weight codes); a constant group takes scale 1, codes 0; the meta
- *            scale and offset are stored as binary16, a zero offset as +0.
+ *            is the exact half-even rounding of (v - min) 255 / (max - min); a
+ *            constant group takes scale 1, codes 0; the meta scale and offset are
+ *            stored as binary16, a zero offset as +0.
  *
  * Arithmetic: fp64, one thread, scalar loops, sums in index order.  The binary16
  * conversions are written out from the IEEE 754 definition (no compiler
@@ -123,16 +126,43 @@ double oracle_shrink_lp(double x, double beta, double p) {
   return x > 0.0 ? v : -v;
 }
 
-/* Q_{z,s}(W) of section 2 with the inverse scale: clamp(round(w*inv_s + z)).
- * The pre-round value is formed in fp64 and the integer decision is taken on its
- * binary32 rounding, the working precision of the device solver, so that both
- * implementations decide every code in the same precision.  fp64 noise
- * (~1e-16) is far below a binary32 half-ulp, so an exact mathematical tie such
- * as the midpoint of min and max is decided half-to-even as in exact
- * arithmetic. */
+/* Q_{z,s}(W) of section 2 with the inverse scale: clamp(round(w*inv_s + z)),
+ * the pre-round value formed in fp64 and rounded half to even (nearbyint under
+ * FE_TONEAREST).  Used at every step after the first, where z is the oracle's
+ * own fp64 iterate. */
 double oracle_quantize_value(double w, double inv_s, double z, int qmax) {
-  double x = (double)(float)(w * inv_s + z);
+  double x = w * inv_s + z;
   double q = nearbyint(x);
+  if (q < 0.0) q = 0.0;
+  if (q > (double)qmax) q = (double)qmax;
+  return q;
+}
+
+/* Half-even rounding of the exact ratio num/den (den > 0, num >= 0), for num and den
+ * that are multiples of 2^-24 below 2^25 and 2^17 and ratios below 256: every
+ * product k*den and difference below is then an exact fp64 value (at most 50
+ * significant bits), so the decision involves no rounding at all.  Returns the
+ * integer nearest num/den; at an exact midpoint the even one. */
+double oracle_round_ratio(double num, double den) {
+  double k = floor(num / den); /* a guess within one of the floor */
+  while (k * den > num) k -= 1.0;
+  while ((k + 1.0) * den <= num) k += 1.0;
+  /* now k*den <= num < (k+1)*den exactly; compare the remainder with den/2 */
+  const double rem2 = 2.0 * (num - k * den);
+  if (rem2 < den) return k;
+  if (rem2 > den) return k + 1.0;
+  return fmod(k, 2.0) == 0.0 ? k : k + 1.0; /* exact midpoint: half to even */
+}
+
+/* The code of w at the initial zero-point z0 = -mn/s with s = (mx - mn)/qmax: the
+ * value w/s + z0 is exactly (w - mn) qmax / (mx - mn).  For binary16 w, mn, mx the
+ * difference w - mn and the product with qmax are exact in fp64, so the code is the
+ * exact half-even rounding of that ratio (a constant group, mx = mn, has s = 1 and
+ * code 0).  fp64 evaluation of w*(1/s) + z0 would instead move exact midpoints,
+ * such as the mid-range element with odd qmax, by rounding noise. */
+double oracle_quantize_init_value(double w, double mn, double mx, int qmax) {
+  if (!(mx > mn)) return 0.0;
+  double q = oracle_round_ratio((w - mn) * (double)qmax, mx - mn);
   if (q < 0.0) q = 0.0;
   if (q > (double)qmax) q = (double)qmax;
   return q;
@@ -192,28 +222,41 @@ int oracle_hqq_group_replay(const double* w, int g, int nbits, double p, double 
   double q[ORACLE_MAX_GROUP], r[ORACLE_MAX_GROUP], we[ORACLE_MAX_GROUP], best_q[ORACLE_MAX_GROUP];
   double s, inv_s, z;
   oracle_minmax_init(w, g, qmax, &s, &inv_s, &z);
+  double mn = w[0], mx = w[0]; /* the range again, for the exact first decision */
+  for (int k = 1; k < g; ++k) {
+    if (w[k] < mn) mn = w[k];
+    if (w[k] > mx) mx = w[k];
+  }
 
   double beta = beta0;
   double best_e = INFINITY, best_z = z, e0 = NAN;
   int t_star = 0, n_eval = 0;
   for (int t = 0; t <= iters; ++t) {
-    /* W_q = Q(W) at the current z; residual r = W - Q^-1(W_q). */
-    for (int k = 0; k < g; ++k) q[k] = oracle_quantize_value(w[k], inv_s, z, qmax);
+    /* W_q = Q(W) at the current z; residual r = W - Q^-1(W_q).  At t = 0 the value
+     * w/s + z0 is an exact ratio and its code is decided exactly. */
+    for (int k = 0; k < g; ++k)
+      q[k] = t == 0 ? oracle_quantize_init_value(w[k], mn, mx, qmax)
+                    : oracle_quantize_value(w[k], inv_s, z, qmax);
     for (int f = 0; f < n_flip; ++f) {
       if (flip_eval[f] != n_eval || flip_elem[f] < 0 || flip_elem[f] >= g) continue;
       int k = flip_elem[f];
-      double x = (double)(float)(w[k] * inv_s + z);
+      double x = w[k] * inv_s + z;
       double other = x > q[k] ? q[k] + 1.0 : q[k] - 1.0;
       if (other >= 0.0 && other <= (double)qmax) q[k] = other;
     }
     for (int k = 0; k < g; ++k) r[k] = w[k] - s * (q[k] - z);
     if (err_pow == 0.0) {
-      /* The l0 error counts non-zero residuals: whether a residual is zero is an
-       * integer decision, taken like the code decision on the binary32 pre-round
-       * value (zero when it equals the code).  fp64 would count the rounding
-       * noise of, e.g., the max element, whose residual is exactly 0. */
-      for (int k = 0; k < g; ++k)
-        if ((double)(float)(w[k] * inv_s + z) == q[k]) r[k] = 0.0;
+      /* The l0 error counts non-zero residuals.  Whether w/s + z equals its code is
+       * decided like the code: exactly at t = 0 ((w - mn) qmax = q (mx - mn), both
+       * sides exact in fp64), on the fp64 value afterwards.  The fp64 residual
+       * itself would count the rounding noise of, e.g., the max element, whose
+       * residual at t = 0 is exactly 0. */
+      for (int k = 0; k < g; ++k) {
+        const int zero_res = t == 0 ? (mx > mn ? (w[k] - mn) * (double)qmax == q[k] * (mx - mn)
+                                               : 1)
+                                    : w[k] * inv_s + z == q[k];
+        if (zero_res) r[k] = 0.0;
+      }
     }
     double e = oracle_group_error(r, g, err_pow);
     if (trace) trace[n_eval] = e;
@@ -363,11 +406,12 @@ int oracle_hqq_dequantize(const uint8_t* packed, const uint16_t* scale_f16,
 
 /* Groups of `group` consecutive values (group = 0: one group of all n; the last
  * group may be shorter).  Per group: mn, mx over the binary16 values; d = mx - mn;
- * if d > 0 the code of v is clamp(nearbyint(binary32(((v - mn) * 255) / d)), 0, 255)
- * (v - mn and the product are exact in fp64, the quotient is rounded once) and the
- * meta scale is d / 255; a constant group has codes 0 and meta scale 1.  The meta
- * scale is stored as binary16 (RNE from fp64), the offset mn exactly.  Returns the
- * number of groups, or -1 for invalid arguments. */
+ * if d > 0 the code of v is the half-even rounding of the exact ratio
+ * ((v - mn) * 255) / d (v - mn and the product are exact in fp64, and
+ * oracle_round_ratio decides without rounding) and the meta scale is d / 255; a
+ * constant group has codes 0 and meta scale 1.  The meta scale is stored as binary16
+ * (RNE from fp64), the offset mn exactly.  Returns the number of groups, or -1 for
+ * invalid arguments. */
 int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, uint8_t* codes,
                              uint16_t* scale16, uint16_t* offset16) {
   if (n < 0 || group < 0) return -1;
@@ -387,8 +431,7 @@ int64_t oracle_meta_quantize(const uint16_t* values, int64_t n, int64_t group, u
     for (int64_t i = g0; i < g1; ++i) {
       double c = 0.0;
       if (d > 0.0) {
-        const double u = ((oracle_f16_to_f64(values[i]) - mn) * 255.0) / d;
-        c = nearbyint((double)(float)u);
+        c = oracle_round_ratio((oracle_f16_to_f64(values[i]) - mn) * 255.0, d);
         if (c < 0.0) c = 0.0;
         if (c > 255.0) c = 255.0;
       }

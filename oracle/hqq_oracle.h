@@ -26,6 +26,8 @@ void oracle_f64_to_f16_array(const double* v, int64_t n, uint16_t* out);
 
 double oracle_shrink_lp(double x, double beta, double p);
 double oracle_quantize_value(double w, double inv_s, double z, int qmax);
+double oracle_round_ratio(double num, double den);
+double oracle_quantize_init_value(double w, double mn, double mx, int qmax);
 void oracle_minmax_init(const double* w, int g, int qmax, double* s, double* inv_s, double* z);
 double oracle_group_error(const double* r, int g, double err_pow);
 double oracle_z_update(const double* q, const double* w, const double* we, double inv_s, int g);

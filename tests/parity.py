@@ -10,16 +10,25 @@ Tolerances (fp32 device solver against the fp64 oracle on the same fp16 bits):
     |delta| = 1 at a rounding tie (the oracle's w/s + z within 2e-3 code units of
     a half-integer);
   * every group that does not agree must be explained (``explain_divergence``):
-    replaying the oracle with at most four tie events reproduces the device's t*
-    and z.  A tie event is either a rounding tie (an element whose binary32
-    pre-round value lies within 8 ulps of a rounding boundary takes the other
+    replaying the oracle with at most four tie events reproduces the device's t*,
+    z (within 1e-3), codes (equal, or |delta| = 1 at a rounding tie of the
+    replay's z) and e_best (within 1e-4).  A tie event is either a rounding tie
+    (an element whose pre-round value lies within 8 binary32 ulps of a rounding
+    boundary -- within the device's working precision -- takes the other
     neighbour) or an error tie (the stop test of an evaluation whose error equals
     the best so far to within 1e-5 is inverted).  A single code flip moves the
     next z by 1/G, so fp32 and fp64 trajectories part at such ties; the replay
     shows that this, and nothing else, happened.  With p = 1 the error is
     piecewise linear in z and runs of exactly equal errors are common, so the
     p = 1 cases use a lower agreement floor; their divergent groups must still
-    all be explained.
+    all be explained;
+  * the reported errors e_0 and e_best (debug outputs, weight units) agree with the
+    oracle's to 1e-4 relative in >= 99.9% of the agreeing groups.
+
+The oracle decides the codes of the first evaluation exactly and later ones on fp64
+values; the device decides all of them on binary32 values.  Codes whose exact value
+lies within a binary32 rounding of a half-integer can therefore differ by one; the
+tie band above covers them, and ``compare`` reports how many there were.
 """
 from __future__ import annotations
 
@@ -35,6 +44,7 @@ TIE_BAND = 2e-3
 STOP_AGREE = 0.999
 CODE_AGREE = 0.9999
 FLIP_REL = 1e-5
+ERR_REL = 1e-4
 
 
 @dataclass
@@ -136,6 +146,7 @@ def compare(W16: np.ndarray, dev: DeviceResult, nbits: int, group_size: int, p=0
         if strict_ties_only:
             assert tie.all(), f"{(~tie).sum()} code mismatches away from a rounding tie"
     rep["code_mismatch_agreeing"] = int(mism.sum())
+    rep["code_mismatch_total"] = int((~eq).sum())
 
     # ---- groups that left the oracle's trajectory: each must be explained
     kinds = {"error_tie": 0, "rounding_tie": 0}
@@ -144,23 +155,27 @@ def compare(W16: np.ndarray, dev: DeviceResult, nbits: int, group_size: int, p=0
         assert dev.zero32 is not None and dev.stop is not None, "divergent group without debug outputs"
         kind = explain_divergence(Wd[i, j], nbits, int(dev.stop[i, j]), float(dev.zero32[i, j]),
                                   codes[i, j * group_size:(j + 1) * group_size], params,
-                                  float(ref.err_init[i, j]), float(ref.err_best[i, j]))
+                                  None if dev.err_best is None else float(dev.err_best[i, j]))
         assert kind is not None, (f"group {(i, j)}: device t*={dev.stop[i, j]} z={dev.zero32[i, j]} "
                                   f"vs oracle t*={ref.stop_step[i, j]} z={ref.zero[i, j]} unexplained")
         kinds[kind] += 1
     rep["divergent"] = kinds
 
-    # ---- reported errors (debug outputs), loose: fp32 sums of hardware log2/exp2 terms
-    if dev.err_init is not None:
-        e0 = ref.err_init
-        ok = np.abs(dev.err_init - e0) <= 1e-4 * np.maximum(e0, 1e-6)
-        assert ok.mean() >= STOP_AGREE
+    # ---- reported errors (debug outputs): fp32 sums of hardware log2/exp2 terms
+    for name, dv, rv in (("err_init", dev.err_init, ref.err_init),
+                         ("err_best", dev.err_best, ref.err_best)):
+        if dv is None:
+            continue
+        ok = np.abs(dv.astype(np.float64) - rv) <= ERR_REL * np.maximum(rv, 1e-6)
+        rep[f"{name}_off"] = int((~ok & agree).sum())
+        assert ok[agree].mean() >= STOP_AGREE, f"{name} agreement {ok[agree].mean():.5f}"
     return rep
 
 
 def _near_ties(w, inv_s, z, qmax, window_ulps=8.0):
-    """Elements whose binary32 pre-round value lies within a few ulps of a rounding boundary."""
-    x = (w * inv_s + z).astype(np.float32).astype(np.float64)
+    """Elements whose pre-round value lies within a few binary32 ulps (the device's working
+    precision) of a rounding boundary."""
+    x = w * inv_s + z
     dist = np.abs(np.abs(x - np.floor(x)) - 0.5)
     win = window_ulps * 2.0 ** -23 * np.maximum(np.abs(x), 1.0)
     inside = (x > -0.5 - win) & (x < qmax + 0.5 + win)
@@ -175,15 +190,30 @@ def _error_at(w, nbits, z, p):
     return oracle.group_error(w - s64 * (q - z), p)
 
 
-def explain_divergence(w, nbits, dev_t, dev_z, dev_codes, params, e0, best_e, max_events=4):
+def _codes_match(w, inv_s, z, qmax, dev_codes, ref_codes):
+    """Device codes equal the reference codes at z, except |delta| = 1 where the pre-round
+    value w/s + z lies within TIE_BAND of a half-integer."""
+    dc, rc = np.asarray(dev_codes, np.int64), np.asarray(ref_codes, np.int64)
+    diff = dc != rc
+    if not diff.any():
+        return True
+    pre = w[diff] * inv_s + z
+    tie = np.abs(pre - np.floor(pre) - 0.5) <= TIE_BAND
+    return bool((np.abs(dc[diff] - rc[diff]) == 1).all() and tie.all())
+
+
+def explain_divergence(w, nbits, dev_t, dev_z, dev_codes, params, dev_err_best=None,
+                       max_events=4):
     """Why a device group left the oracle's trajectory, or None if unexplained.
 
     Replays the oracle with at most `max_events` tie events and looks for the device's
-    stop step and z (within Z_ABS).  Events are (a) a rounding tie: an element whose
-    binary32 pre-round value lies within 8 ulps of a rounding boundary gets the other
-    neighbour; (b) an error tie: an evaluation whose error equals the best error so far
-    to within FLIP_REL has its stop decision inverted.  Returns "error_tie" if only
-    events of kind (b) were needed, else "rounding_tie"."""
+    stop step, z (within Z_ABS), codes (equal, or one apart at a rounding tie of the
+    replay's z) and e_best (within ERR_REL, when the device reported it).  Events are
+    (a) a rounding tie: an element whose pre-round value lies within 8 binary32 ulps of
+    a rounding boundary gets the other neighbour; (b) an error tie: an evaluation whose
+    error equals the best error so far to within FLIP_REL has its stop decision
+    inverted.  Returns "error_tie" if only events of kind (b) were needed, else
+    "rounding_tie"."""
     qmax = (1 << nbits) - 1
     _, inv_s, _ = oracle.minmax_init(w, nbits)
 
@@ -191,7 +221,14 @@ def explain_divergence(w, nbits, dev_t, dev_z, dev_codes, params, e0, best_e, ma
         return oracle.hqq_group_replay(w, nbits, flips, inverts, **params)
 
     def matches(res):
-        return res.stop_step == dev_t and abs(res.zero - dev_z) <= Z_ABS
+        if res.stop_step != dev_t or abs(res.zero - dev_z) > Z_ABS:
+            return False
+        if not _codes_match(w, inv_s, res.zero, qmax, dev_codes, res.codes):
+            return False
+        if dev_err_best is not None and \
+                abs(dev_err_best - res.err_best) > ERR_REL * max(res.err_best, 1e-6):
+            return False
+        return True
 
     def events(res, ztr, after):
         ev = []

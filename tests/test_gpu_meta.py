@@ -1,20 +1,23 @@
 """GPU parity of the 8-bit meta quantization (through the C ABI) against the oracle.
 
-The meta codes are integers decided on the binary32 rounding of an fp64 quotient
-on both sides, and the meta scale, offset and dequantized values are single
-roundings of exact values, so every output is compared bit for bit: on the s and
-z arrays the solver produces for workload matrices (z as one group per array, s
-in groups of 128), on ragged group counts, and on edge cases (constant arrays,
-+0/-0 minima, one value, groups of 1, 3, 5 and 1000 values, binary16 triples
-whose quotient lands on a half-integer only after binary32 rounding, and triples whose
-quotient is on a half-integer or within 2^-15 of one, where the kernels leave the
-group's reciprocal for the exact quotient).
+The meta codes are the exact half-even rounding of (v - min) 255 / (max - min) on
+both sides, and the meta scale, offset and dequantized values are single roundings
+of exact values, so every output is compared bit for bit: on the s and z arrays the
+solver produces for workload matrices (z as one group per array, s in groups of
+128), on ragged group counts, and on edge cases (constant arrays, +0/-0 minima, one
+value, groups of 1, 3, 5 and 1000 values, binary16 triples whose ratio lies off a
+half-integer by less than a binary32 rounding, and triples whose ratio is on a
+half-integer or within 2^-11 of one -- on both sides of the margin at which the
+kernels leave the group's reciprocal for the exact comparison -- including groups
+whose minimum is near -6e4 next to values near 2^-14, and groups a few binary16
+ulps wide).
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads
+from tests.test_oracle_meta_pins import NEAR_TIES
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -103,13 +106,13 @@ def test_meta_ragged_and_small_groups(hq):
 
 def test_meta_edge_cases(hq):
     f16 = lambda x: np.asarray(x, np.float16).view(np.uint16)
-    _say("constant, +0/-0, single value, binary32-decided ties")
+    _say("constant, +0/-0, single value, ties off by less than a binary32 rounding")
     _check(hq, f16([0.75] * 300), 0)
     _check(hq, f16([0.75] * 300), 128)
     _check(hq, f16([-0.0, 0.0, 1.0, -0.0]), 0)
     _check(hq, f16([0.0, -0.0, 2.0, 3.0, -0.0, 0.0]), 3)
     _check(hq, f16([3.5]), 0)
-    _check(hq, f16([-1.3779296875, 286.25, 214.625, -1.009765625, 170.625, 166.25]), 3)
+    _check(hq, f16(np.array(NEAR_TIES).reshape(-1)), 3)
     _check(hq, f16([0, 255, 2.5, 3.5, 4.5, 0.5, 1.5, 254.5]), 0)
     _check(hq, f16([-1, 0, 0.5, 2]), 0)
 
@@ -161,14 +164,20 @@ def test_meta_batch_equals_per_matrix(hq, nbits, g):
         assert torch.equal(mz.offset[i:i + 1].view(torch.int16), one_z.offset.view(torch.int16))
 
 
-def _near_half_triples(seed, want):
-    """binary16 triples (min, max, v) whose quotient (v - min) 255 / (max - min) lies
-    within 2^-15 of a half-integer: exactly on it, or off it by less than the margin
-    inside which the codes take the exact quotient instead of the group's reciprocal."""
+BANDS = ((0.0, 0.0), (0.0, 2.0 ** -15), (2.0 ** -15, 2.0 ** -12), (2.0 ** -12, 2.0 ** -11))
+
+
+def _near_half_triples(seed, want, draw, bands=BANDS):
+    """binary16 triples (min, max, v) from ``draw(rng, n)`` whose ratio
+    (v - min) 255 / (max - min) is on a half-integer or within 2^-11 of one, ``want`` of
+    each distance band in ``bands``: exactly on it, within 2^-15, from 2^-15 to 2^-12
+    (just inside the kernels' margin) and from 2^-12 to 2^-11 (just outside it)."""
     rng = np.random.default_rng(seed)
-    exact, near = [], []
-    while len(exact) < want or len(near) < want:
-        a = rng.standard_normal((1 << 20, 3)).astype(np.float16)
+    found = [[] for _ in bands]
+    for _ in range(200):
+        if min(len(f) for f in found) >= want:
+            break
+        a = draw(rng, 1 << 20)
         a = a[np.isfinite(a).all(axis=1)]
         lo = np.minimum(a[:, 0], a[:, 1]).astype(np.float64)
         hi = np.maximum(a[:, 0], a[:, 1]).astype(np.float64)
@@ -177,15 +186,52 @@ def _near_half_triples(seed, want):
         u = (v - lo) * 255.0 / np.where(ok, hi - lo, 1.0)
         off = np.abs(u - np.floor(u) - 0.5)
         trip = np.stack([lo, hi, v], axis=1).astype(np.float16)
-        exact += list(trip[ok & (off == 0.0)][:want])
-        near += list(trip[ok & (off > 0.0) & (off < 2.0 ** -15)][:want])
-    return np.array(exact[:want]), np.array(near[:want])
+        for f, (b0, b1) in zip(found, bands):
+            sel = ok & (off == 0.0) if b1 == 0.0 else ok & (off > b0) & (off < b1)
+            f += list(trip[sel][:max(want - len(f), 0)])
+    assert min(len(f) for f in found) >= want, [len(f) for f in found]
+    return [np.array(f[:want]) for f in found]
 
 
-def test_meta_codes_at_and_near_half_integers(hq):
-    """Quotients on a half-integer or within 2^-15 of one, in groups of three: the codes
-    must match the definition's binary32-then-half-even rounding bit for bit."""
-    exact, near = _near_half_triples(7, 64)
-    vals = np.concatenate([exact, near]).reshape(-1).view(np.uint16)
+def _draw_normal(rng, n):
+    return rng.standard_normal((n, 3)).astype(np.float16)
+
+
+def _draw_mixed_magnitudes(rng, n):
+    """A minimum near -6e4 beside values near 2^-14: v - min rounds in fp32."""
+    lo = -rng.uniform(2e4, 6.5e4, n)
+    hi = rng.uniform(-1.0, 50.0, n)
+    v = rng.standard_normal(n) * 2.0 ** -14
+    return np.stack([lo, hi, v], axis=1).astype(np.float16)
+
+
+@pytest.mark.parametrize("draw,bands", [(_draw_normal, BANDS),
+                                        (_draw_mixed_magnitudes, BANDS[1:])])
+def test_meta_codes_at_and_near_half_integers(hq, draw, bands):
+    """Ratios on a half-integer or up to 2^-11 from one, in groups of three: the codes must
+    match the exact definition bit for bit on both sides of the kernels' 2^-12 margin (the
+    mixed-magnitude draw has no exact ties)."""
+    found = _near_half_triples(7, 64, draw, bands)
+    vals = np.concatenate(found).reshape(-1).view(np.uint16)
     _check(hq, vals, 3)
-    _say(f"{len(exact)} triples on a half-integer, {len(near)} within 2^-15 of one: bit-exact")
+    _say(f"{draw.__name__}: {[len(b) for b in found]} triples per band {bands}: bit-exact")
+
+
+def test_meta_codes_of_narrow_groups(hq):
+    """Groups a few binary16 ulps wide (d tiny, so fl32(255/d) is large): ratios k 255 / m
+    with small m, exact ties among them."""
+    rng = np.random.default_rng(8)
+    groups = []
+    for _ in range(512):
+        base = np.float16(rng.standard_normal() * 10.0 ** rng.uniform(-4, 4))
+        if not np.isfinite(base):
+            continue
+        m = int(rng.integers(1, 12))
+        steps = np.concatenate([[0, m], rng.integers(0, m + 1, 6)])
+        vals = base.view(np.uint16).astype(np.int64) + np.where(base >= 0, steps, -steps)
+        grp = vals.astype(np.uint16)
+        if np.isfinite(grp.view(np.float16)).all():
+            groups.append(grp)
+    vals = np.concatenate(groups)
+    _check(hq, vals, 8)
+    _say(f"{len(groups)} groups of 8 values at most 11 ulps apart: bit-exact")

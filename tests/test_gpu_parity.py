@@ -231,6 +231,33 @@ def test_exact_ties_round_half_even(hq):
     assert np.array_equal(codes, ref.codes)
 
 
+def test_init_near_ties_below_binary32_resolution(hq):
+    """Groups holding a binary16 triple (min, max, w) whose exact initial ratio
+    (w - min) qmax / (max - min) lies off a half-integer by less than a binary32 rounding:
+    the oracle takes the exact code, the device's binary32 decision may take the other
+    neighbour.  Every such difference must be one code at a rounding tie, and every group
+    that then leaves the oracle's trajectory must be explained by the tie replay."""
+    from tests.test_oracle_pins import NEAR_TIE_TRIPLES
+    rng = np.random.default_rng(12)
+    total = {}
+    for qmax, nbits in ((15, 4), (7, 3), (3, 2), (255, 8)):
+        rows = []
+        for mn, mx, w in NEAR_TIE_TRIPLES[qmax]:
+            for _ in range(64):
+                grp = np.concatenate([[mn, mx, w], rng.uniform(mn, mx, 13)]).astype(np.float16)
+                grp[3:] = np.clip(grp[3:], np.float16(mn), np.float16(mx))
+                rows.append(grp)
+        W = np.stack(rows).reshape(-1, 64)
+        _say(f"init near ties b{nbits}: {W.shape[0] * 4} groups of 16")
+        Wt = torch.from_numpy(W).cuda()
+        q = _run(hq, Wt, nbits, 16)
+        rep = parity.compare(W.view(np.uint16), parity.from_quantized(q), nbits, 16,
+                             min_agree=0.5, min_code_agree=0.9)
+        total[nbits] = (rep["code_mismatch_total"], rep["divergent"])
+        _say(f"  {rep}")
+    _say(f"near-tie code mismatches and divergent groups per bit width: {total}")
+
+
 def test_hand_examples_are_exact_on_gpu(hq):
     """The worked examples of the oracle pins, duplicated to a group of 16, in dyadic arithmetic."""
     _say("hand examples")

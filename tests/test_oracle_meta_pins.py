@@ -11,6 +11,8 @@ groups, the group structure, monotonicity, the reconstruction bound, exact
 power-of-two scaling and reflection, and the single rounding of the
 dequantization (checked against numpy's own binary16 conversion).
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -151,14 +153,44 @@ def test_empty_and_invalid():
         oracle.meta_quantize(np.zeros(4, np.uint16), -1)
 
 
-def test_code_decided_in_binary32():
-    # Groups (min, max, v) whose exact quotient (v - min) * 255 / (max - min) lies within
-    # one binary32 rounding of a half-integer: 191.4999949... rounds to 191.5 in binary32
-    # and then half-even to 192 (191 in fp64); 248.5000057... rounds to 248.5, then to 248
-    # (249 in fp64).  Found by an exact-rational search over binary16 triples.
-    v = f16([-1.3779296875, 286.25, 214.625, -1.009765625, 170.625, 166.25])
+def _exact_half_even(x: Fraction) -> int:
+    k = x.numerator // x.denominator
+    rem = x - k
+    return k + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1) else k
+
+
+# Groups (min, max, v) whose exact quotient (v - min) * 255 / (max - min) lies off a
+# half-integer by less than a binary32 half-ulp, so that rounding the quotient to binary32
+# first would turn it into a tie (191.4999949... -> 191.5 -> 192, 248.5000057... -> 248.5
+# -> 248).  Found by a search over exact rationals; the expected codes are computed from the
+# rationals in the test.
+NEAR_TIES = [(-1.3779296875, 286.25, 214.625), (-1.009765625, 170.625, 166.25),
+             (-0.04083251953125, 0.0210418701171875, 5.310773849487305e-05),
+             (-3.36766242980957e-05, 0.04107666015625, 0.029388427734375),
+             (-0.0085906982421875, 0.0135040283203125, 3.057718276977539e-05),
+             (-0.025665283203125, 0.018890380859375, 0.00010710954666137695),
+             (0.00022685527801513672, 0.0225677490234375, 0.0106964111328125),
+             (-0.016876220703125, 0.01096343994140625, 0.00020968914031982422),
+             (-1.435546875, -0.0307769775390625, -0.64501953125),
+             (-1.287109375, 1.068359375, 0.0014705657958984375),
+             (-0.1456298828125, 0.7490234375, -2.944469451904297e-05),
+             (0.0102386474609375, 1.3017578125, 0.89404296875),
+             (-0.00853729248046875, 1.9033203125, 1.5546875),
+             (-0.8896484375, 0.047882080078125, -0.0017518997192382812)]
+
+
+def test_code_is_the_exact_rounding_next_to_half_integers():
+    """The code is round(v/s' + z') of the affine 8-bit quantizer taken on the exact quotient:
+    for each triple the exact code differs from the code of the binary32-rounded quotient."""
+    v = f16(np.array(NEAR_TIES).reshape(-1))
+    assert np.array_equal(v.astype(np.float64), np.array(NEAR_TIES).reshape(-1))
     codes, _, _ = oracle.meta_quantize(v.view(np.uint16), 3)
-    assert codes.tolist() == [0, 255, 192, 0, 255, 248]
+    for i, (mn, mx, x) in enumerate(NEAR_TIES):
+        q = (Fraction(x) - Fraction(mn)) * 255 / (Fraction(mx) - Fraction(mn))
+        exact = _exact_half_even(q)
+        assert int(np.rint(np.float64(np.float32(float(q))))) != exact
+        assert codes[3 * i:3 * i + 3].tolist() == [0, 255, exact]
+    assert codes[:6].tolist() == [0, 255, 191, 0, 255, 249]
 
 
 def test_zero_minimum_is_stored_as_plus_zero():

@@ -33,7 +33,14 @@ MUTANTS = {
     "stop step off by one": ("t_star = t;", "t_star = t > 0 ? t - 1 : 0;"),
     "beta never updated": ("beta = kappa * beta;", "beta = beta;"),
     "round half away from zero": ("double q = nearbyint(x);", "double q = round(x);"),
-    "decision in fp64": ("double x = (double)(float)(w * inv_s + z);", "double x = w * inv_s + z;"),
+    "later decisions in binary32": ("  double x = w * inv_s + z;\n  double q = nearbyint(x);",
+                                    "  double x = (double)(float)(w * inv_s + z);\n  double q = nearbyint(x);"),
+    "init decision in binary32": ("double q = oracle_round_ratio((w - mn) * (double)qmax, mx - mn);",
+                                  "double q = nearbyint((double)(float)(((w - mn) * (double)qmax) / (mx - mn)));"),
+    "init decision through fp64 1/s": ("q[k] = t == 0 ? oracle_quantize_init_value(w[k], mn, mx, qmax)",
+                                       "q[k] = t < 0 ? oracle_quantize_init_value(w[k], mn, mx, qmax)"),
+    "ratio midpoint rounds up": ("return fmod(k, 2.0) == 0.0 ? k : k + 1.0;", "return k + 1.0;"),
+    "ratio midpoint rounds down": ("if (rem2 < den) return k;", "if (rem2 <= den) return k;"),
     "no upper clamp": ("if (q > (double)qmax) q = (double)qmax;", ""),
     "error of squared residual": ("pow(fabs(r[k]), err_pow)", "pow(r[k] * r[k], err_pow)"),
     "pack MSB first": ("out[bit >> 3] |= (uint8_t)(1u << (bit & 7));",
@@ -52,10 +59,12 @@ MUTANTS = {
     "tensor total skips the last group": ("for (int t = 0; t <= iters; ++t) total[t] += trace[t];",
                                           "if (gi + 1 < ngroups) for (int t = 0; t <= iters; ++t) "
                                           "total[t] += trace[t];"),
-    "meta 256 levels": ("* 255.0) / d;", "* 256.0) / d;"),
-    "meta round half away from zero": ("c = nearbyint((double)(float)u);",
-                                       "c = round((double)(float)u);"),
-    "meta decision in fp64": ("c = nearbyint((double)(float)u);", "c = nearbyint(u);"),
+    "meta 256 levels": ("(oracle_f16_to_f64(values[i]) - mn) * 255.0, d);",
+                        "(oracle_f16_to_f64(values[i]) - mn) * 256.0, d);"),
+    "meta decision in binary32": ("c = oracle_round_ratio((oracle_f16_to_f64(values[i]) - mn) * 255.0, d);",
+                                  "c = nearbyint((double)(float)(((oracle_f16_to_f64(values[i]) - mn) * 255.0) / d));"),
+    "meta round half away from zero": ("c = oracle_round_ratio((oracle_f16_to_f64(values[i]) - mn) * 255.0, d);",
+                                       "c = round(((oracle_f16_to_f64(values[i]) - mn) * 255.0) / d);"),
     "meta offset is the max": ("offset16[ng] = oracle_f64_to_f16(mn);",
                                "offset16[ng] = oracle_f64_to_f16(mx);"),
     "meta scale over 256": ("d > 0.0 ? d / 255.0 : 1.0", "d > 0.0 ? d / 256.0 : 1.0"),

@@ -10,6 +10,7 @@ written next to each example).
 """
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -116,12 +117,98 @@ def test_quantize_rounds_half_to_even_and_clamps():
     assert [q(0.5), q(1.5), q(2.5), q(0.49), q(0.51)] == [0.0, 2.0, 2.0, 0.0, 1.0]
     assert [q(-0.5), q(-3.0), q(3.4), q(3.5), q(99.0)] == [0.0, 0.0, 3.0, 3.0, 3.0]
     assert q(254.5, 255) == 254.0 and q(253.5, 255) == 254.0
+    # the decision is taken on the fp64 value itself: values off a half-integer by far less
+    # than a binary32 half-ulp still go to the nearer integer
+    assert [q(0.5 + 2**-40), q(2.5 - 2**-40), q(1.5 + 2**-35), q(2.5 + 2**-45)] == [1.0, 2.0, 2.0, 3.0]
+    assert q(128.5 - 2**-30, 255) == 128.0 and q(127.5 + 2**-30, 255) == 128.0
+
+
+def _exact_half_even(num: Fraction) -> int:
+    """Round half to even of an exact rational (Python integers only)."""
+    k = num.numerator // num.denominator
+    rem = num - k
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    return k
+
+
+def test_round_ratio_is_exact_rational_rounding():
+    """The exact ratio rounding of the initial quantizer against Python's rationals, on
+    differences of random binary16 values (every magnitude, subnormals included) and on exact
+    midpoints."""
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 0x7BFF, (20000, 3)).astype(np.uint16)
+    v = bits.view(np.float16).astype(np.float64)
+    for qmax in (3, 7, 15, 255):
+        for a, b, c in v[:5000]:
+            lo, hi = min(a, b), max(a, b)
+            if not hi > lo:
+                continue
+            w = lo + (hi - lo) * (c / 65504.0)
+            w = float(np.float16(w))
+            if not lo <= w <= hi:
+                continue
+            num = (w - lo) * qmax  # exact in fp64
+            assert Fraction(num) == (Fraction(w) - Fraction(lo)) * qmax
+            exact = _exact_half_even((Fraction(w) - Fraction(lo)) * qmax / (Fraction(hi) - Fraction(lo)))
+            assert oracle.round_ratio(num, hi - lo) == exact
+    # exact midpoints: (2k+1)/2 of any binary16 difference goes to the even neighbour
+    for k in range(0, 255):
+        d = float(np.float16(rng.uniform(1e-3, 10)))
+        assert oracle.round_ratio((2 * k + 1) * d / 2, d) == (k if k % 2 == 0 else k + 1)
+
+
+# binary16 groups (min, max, w) whose exact ratio (w - min) qmax / (max - min) lies off a
+# half-integer by less than a binary32 half-ulp: the exact code is the nearer integer,
+# while rounding the ratio to binary32 first would make it a tie and pick the even one.
+# Found by a search over exact rationals (Python fractions); the expected code is computed
+# below from the rationals, not stored.
+NEAR_TIE_TRIPLES = {
+    15: [(-0.375, 0.286865234375, 5.698204040527344e-05),
+         (-0.375, 0.11407470703125, -4.273653030395508e-05),
+         (-0.375, 0.01293182373046875, 7.748603820800781e-07),
+         (-0.63232421875, 18.34375, 0.00021159648895263672),
+         (-0.63232421875, 5.69140625, 4.881620407104492e-05),
+         (-0.63232421875, 0.365966796875, -7.325410842895508e-05)],
+    7: [(-1.0859375, 14.1171875, 5.960464477539063e-08),
+        (-1.0859375, 3.982421875, 0.00013947486877441406),
+        (-1.0859375, 0.08355712890625, 2.181529998779297e-05),
+        (-0.49609375, 0.275634765625, 1.7464160919189453e-05)],
+    3: [(-0.36279296875, 1.8134765625, -8.13603401184082e-05),
+        (-1.6845703125, 1.6845703125, -5.960464477539063e-08),
+        (-1.6845703125, 0.3369140625, 5.960464477539063e-08),
+        (-0.75146484375, 0.1502685546875, -2.0325183868408203e-05)],
+    255: [(-0.04083251953125, 0.0210418701171875, 5.310773849487305e-05),
+          (-0.0085906982421875, 0.0135040283203125, 3.057718276977539e-05),
+          (-1.435546875, -0.0307769775390625, -0.64501953125),
+          (0.0102386474609375, 1.3017578125, 0.89404296875)],
+}
+
+
+def test_init_codes_are_exact_next_to_half_integers():
+    """Section 2's round(W/s + z) at the min-max initialisation, decided on the exact value:
+    for every triple the ratio is within a binary32 half-ulp of a half-integer, so the exact
+    code and the code of the binary32-rounded ratio differ; the oracle must give the exact
+    one, in the whole solver at T = 0 too."""
+    bits = {3: 2, 7: 3, 15: 4, 255: 8}
+    for qmax, triples in NEAR_TIE_TRIPLES.items():
+        for mn, mx, w in triples:
+            assert all(float(np.float16(x)) == x for x in (mn, mx, w))
+            ratio = (Fraction(w) - Fraction(mn)) * qmax / (Fraction(mx) - Fraction(mn))
+            exact = _exact_half_even(ratio)
+            half = Fraction(2 * (exact if ratio > exact else exact - 1) + 1, 2)
+            assert 0 < abs(ratio - half) <= Fraction(1, 2 ** 24) * half  # off the tie, below 2^-24
+            b32 = int(np.rint(np.float64(np.float32(float(ratio)))))
+            assert b32 != exact  # the case exists only below binary32 resolution
+            assert oracle.quantize_init_value(w, mn, mx, qmax) == exact
+            r = oracle.hqq_group(np.array([mn, mx, w]), bits[qmax], iters=0)
+            assert r.codes.tolist() == [0, qmax, exact]
 
 
 def test_exact_midpoint_tie_at_init_is_half_even():
     """An element at the exact midpoint of min and max has w/s + z = qmax/2 exactly (a tie for
-    odd qmax).  Exact arithmetic rounds 7.5 to 8 (half-even) whatever fp64 noise the product
-    w * (1/s) carries; the decision precision (binary32) absorbs that noise."""
+    odd qmax).  Exact arithmetic rounds 7.5 to 8 (half-even); evaluating w * (1/s) + z0 in
+    fp64 would leave it on either side of 7.5 by rounding noise."""
     rng = np.random.default_rng(17)
     hits = 0
     for _ in range(2000):
@@ -131,8 +218,8 @@ def test_exact_midpoint_tie_at_init_is_half_even():
             continue
         k = [i for i in range(16) if i not in (int(w.argmin()), int(w.argmax()))][0]
         w[k] = mid
-        s, inv_s, z = oracle.minmax_init(w, 4)
-        assert oracle.quantize_value(mid, inv_s, z, 15) == 8.0
+        assert oracle.quantize_init_value(mid, w.min(), w.max(), 15) == 8.0
+        assert oracle.hqq_group(w, 4, iters=0).codes[k] == 8
         hits += 1
     assert hits > 100
 
@@ -248,19 +335,34 @@ def test_hand_example_with_active_shrink_and_beta_schedule():
 def test_zero_iterations_is_round_to_nearest():
     """T = 0: the solver reduces to asymmetric min-max round-to-nearest (numpy fp64, half-even)."""
     rng = np.random.default_rng(21)
+    n_near = 0
     for nbits in (2, 3, 4, 8):
         qmax = (1 << nbits) - 1
         W = (rng.standard_normal((16, 128)) * 0.02).astype(np.float16)
+        # plant exact ties: the midpoint of a group's min and max, where it is a binary16
+        Wv = W.reshape(-1, 32)
+        for grp in Wv[::3]:
+            mid = (float(grp.min()) + float(grp.max())) / 2
+            j = [i for i in range(32) if i not in (int(grp.argmin()), int(grp.argmax()))][0]
+            if float(np.float16(mid)) == mid:
+                grp[j] = mid
         res = oracle.hqq_quantize(W, nbits, 32, iters=0)
         Wg = W.astype(np.float64).reshape(-1, 32)
         mn, mx = Wg.min(1, keepdims=True), Wg.max(1, keepdims=True)
         s = (mx - mn) / qmax
         pre = (Wg - mn) / s
         ref = np.clip(np.round(pre), 0, qmax)
-        tie = np.abs(np.abs(pre - np.floor(pre)) - 0.5) < 2e-5  # binary32 resolution below 256
-        assert np.array_equal(res.codes.reshape(-1, 32)[~tie], ref[~tie])
+        # within fp64 noise of a half-integer numpy's two roundings cannot decide: those
+        # elements take the exact rational answer instead, so every code is compared
+        near = np.abs(np.abs(pre - np.floor(pre)) - 0.5) < 1e-9
+        for i, j in zip(*np.nonzero(near)):
+            ratio = (Fraction(Wg[i, j]) - Fraction(mn[i, 0])) * qmax / (Fraction(mx[i, 0]) - Fraction(mn[i, 0]))
+            ref[i, j] = _exact_half_even(ratio)
+        n_near += int(near.sum())
+        assert np.array_equal(res.codes.reshape(-1, 32), ref)
         assert (res.stop_step == 0).all()
         assert np.allclose(res.zero.reshape(-1, 1), -mn / s, rtol=1e-14, atol=1e-12)
+    assert n_near > 0  # the exact ties of binary16 data are part of the comparison
 
 
 def test_early_stop_invariants_on_layer_like_groups():
