@@ -42,12 +42,22 @@ KERNEL_SRC = [os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", f)
 PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 PEAK_HBM = 8.0e12
 
-# Algorithmic VALU lane-ops per weight (general 0 < p < 1):
+# Algorithmic VALU lane-ops per weight (general 0 < p < 1), the builder's count:
 #   init   4: fp16->fp32, min, max, w/s + z
 #   eval  10: x = w/s + z, round, clamp, residual, log2 (2), *p, exp2 (2), error sum
 #   update 1: code sum for the z mean (no shrink: every |r| is below its threshold)
 #   final  4: x, round, clamp, pack
 OPS_INIT, OPS_EVAL, OPS_UPDATE, OPS_FINAL = 4, 10, 1, 4
+# The planning op model the roofline is also reported against: per weight
+#   3 + n_eval (8 + 2 tau) + n_upd 6
+# (init min/max and pack 3; per evaluation 7 full-rate ops, one amortized reduction and
+# two transcendentals of tau issue slots each; per update 6 full-rate ops, the shrink
+# included), with tau the measured cost of v_exp_f32 / v_log_f32 relative to v_add_f32.
+PLAN_BASE, PLAN_EVAL_FULL, PLAN_EVAL_TRANS, PLAN_UPDATE = 3, 8, 2, 6
+
+PROBE_LIB = os.path.join(ROOT, "bit_weight_quantization_amd", "libhqq_valu_probe.so")
+CLOCK_HZ = 2.4e9   # MI355X peak engine clock
+SIMDS = 256 * 4    # 256 CUs x 4 SIMDs
 
 
 def log(*a):
@@ -167,6 +177,228 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
     with open(os.path.join(out_dir, "hqq_solve_llama70b.md"), "w") as f:
         f.write("\n".join(lines))
     print(json.dumps(summary, indent=1))
+
+
+def measure_peaks(torch, dev, stream, trips=2048, reps=5):
+    """Issue rates of the VALU instruction classes the solver uses, from the probe library
+    (libhqq_valu_probe.so): 8 wavefronts per SIMD, each thread running 8 independent
+    chains of one instruction, HIP events around `reps` launches on the bench stream.
+    Reports SIMD cycles per wave64 instruction at the nominal 2.4 GHz clock and the ratio
+    to v_add_f32 (clock-independent); tau = the mean ratio of v_exp_f32 and v_log_f32."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hqq_probe_valu.restype = ctypes.c_int
+    lib.hqq_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.hqq_probe_kind_name.restype = ctypes.c_char_p
+    lib.hqq_probe_kind_name.argtypes = [ctypes.c_int]
+    blocks = 256 * 8  # 8 blocks of 4 wavefronts per CU: 8 wavefronts per SIMD
+    per_trip = lib.hqq_probe_instr_per_trip()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sh = int(stream.cuda_stream)
+    res = {}
+    for k in range(lib.hqq_probe_kinds()):
+        name = lib.hqq_probe_kind_name(k).decode()
+        assert lib.hqq_probe_valu(k, blocks, trips, out.data_ptr(), sh) == 0
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            assert lib.hqq_probe_valu(k, blocks, trips, out.data_ptr(), sh) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        wave_instr = blocks * 4 * trips * per_trip
+        res[name] = {"ms": round(ms, 4),
+                     "cycles_per_wave_instr": round(ms * 1e-3 * CLOCK_HZ * SIMDS / wave_instr, 3)}
+    base = res["v_add_f32"]["cycles_per_wave_instr"]
+    for v in res.values():
+        v["rel_to_add"] = round(v["cycles_per_wave_instr"] / base, 3)
+    tau = (res["v_exp_f32"]["rel_to_add"] + res["v_log_f32"]["rel_to_add"]) / 2
+    return {"probe": "libhqq_valu_probe.so", "waves_per_simd": 8, "trips": trips,
+            "instr": res, "tau": round(tau, 3)}
+
+
+def stop_hist_ops(hist, g, iters, tau):
+    """Algorithmic lane-ops of groups with the stop-step histogram `hist` (early stop): the
+    builder's count and the planning model's, and the mean evaluations per group."""
+    t = np.arange(len(hist))
+    n_eval = np.where(t == iters, iters + 1, t + 2)
+    n_upd = n_eval - 1
+    groups = max(float(hist.sum()), 1.0)
+    builder = g * float(np.sum(hist * (OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval + OPS_UPDATE * n_upd)))
+    plan = g * float(np.sum(hist * (PLAN_BASE + n_eval * (PLAN_EVAL_FULL + PLAN_EVAL_TRANS * tau) +
+                                    n_upd * PLAN_UPDATE)))
+    return builder, plan, float(np.sum(hist * n_eval) / groups)
+
+
+def sample_rows(rows, seed, n=14):
+    """First, last and n seeded rows of a matrix (sorted, distinct)."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, rows - 1), size=min(n, rows - 2), replace=False)
+    return np.unique(np.concatenate([[0, rows - 1], mid]))
+
+
+def collect_arena_rows(hq, torch, Ws, mats, nb, g, solver, packed, scale, zero):
+    """Sampled rows of the last layer's matrices from the output arena of the timed batched
+    launch (its largest byte and group offsets), with the same rows quantized on their own
+    (hqq_quantize_ex, debug outputs).  Rows are independent, so the two must be
+    bit-identical; the debug outputs let the oracle check explain any divergent group."""
+    firsts, acc = [], 0
+    for W in Ws:
+        firsts.append(acc)
+        acc += W.numel() // g
+    out = []
+    for mi in range(max(len(Ws) - 7, 0), len(Ws)):
+        W = Ws[mi]
+        r, c = W.shape
+        idx = sample_rows(r, mats[mi].seed)
+        it = torch.as_tensor(idx, device=W.device)
+        gpr, bpr = c // g, c * nb // 8
+        g0 = firsts[mi]
+        b0 = g0 * g * nb // 8
+        ap = packed[b0:b0 + r * bpr].view(r, bpr)[it]
+        as_ = scale[g0:g0 + r * gpr].view(r, gpr)[it]
+        az = zero[g0:g0 + r * gpr].view(r, gpr)[it]
+        Wsub = W[it].contiguous()
+        q = hq.quantize(Wsub, nb, g, p=solver.p, beta=solver.beta, kappa=solver.kappa,
+                        iters=solver.iters, debug=True)
+        torch.cuda.synchronize()
+        same = (torch.equal(ap.reshape(-1), q.packed) and
+                torch.equal(as_.view(torch.int16), q.scale.view(torch.int16)) and
+                torch.equal(az.view(torch.int16), q.zero.view(torch.int16)))
+        out.append({"matrix": mi, "shape": [r, c], "rows": idx.tolist(),
+                    "max_byte_offset": int(b0 + (int(idx[-1]) + 1) * bpr),
+                    "max_group_offset": int(g0 + (int(idx[-1]) + 1) * gpr),
+                    "arena_equals_rows_alone": bool(same),
+                    "W16": Wsub.cpu().numpy().view(np.uint16),
+                    "dev": {k: getattr(q, k).cpu().numpy() for k in
+                            ("packed", "scale", "zero", "scale_f32", "zero_f32", "stop_step",
+                             "err_init", "err_best")}})
+    return out
+
+
+CONFIGS = (("C1", "single_256x512"), ("C2", "attn_4096x4096"), ("C3", "mlp_11008x4096"),
+           ("C4", "llama7b_stack"))
+
+
+def measure_configs(hq, lib, torch, dev, stream, sh, tau, warmup=3, runs=10):
+    """The smaller workloads under the same timing rules as the headline: single matrices
+    (C1, C2, each C3 shape) 3 warm-ups then the median of 10 calls, each between its own
+    HIP events; the 7B-shaped stack (C4) resident in HBM, one batched launch per setting
+    between an event pair (3 warm-ups, median of 5).  Stop-step histograms come from an
+    untimed debug pass; both VALU fractions as for the headline.  The fp16 inputs of the
+    single matrices are kept on the host for the oracle's full-matrix timing."""
+    res = {}
+    host_inputs = {}
+    for cid, name in CONFIGS:
+        wl = workloads_mod().WORKLOADS[name]
+        solver = wl.solver
+        entry = {"workload": name, "settings": []}
+        if name != "llama7b_stack":
+            for mi, m in enumerate(wl.matrices):
+                W = workloads_mod().generate(m.rows, m.cols, wl.dist, m.seed, dev)
+                host_inputs[(cid, mi)] = W.cpu().numpy().view(np.uint16)
+                for nb, g in wl.settings:
+                    out = hq.quantize(W, nb, g, iters=0)
+                    args = (W.data_ptr(), m.rows, m.cols, nb, g, solver.p, solver.beta,
+                            solver.kappa, solver.iters, out.packed.data_ptr(),
+                            out.scale.data_ptr(), out.zero.data_ptr(), sh)
+                    for _ in range(warmup):
+                        assert lib.hqq_quantize(*args) == 0
+                    torch.cuda.synchronize()
+                    times = []
+                    for _ in range(runs):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        assert lib.hqq_quantize(*args) == 0
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        times.append(e0.elapsed_time(e1))
+                    ms = float(np.median(times))
+                    q = hq.quantize(W, nb, g, debug=True)
+                    torch.cuda.synchronize()
+                    hist = np.bincount(q.stop_step.cpu().numpy().ravel().astype(np.int64),
+                                       minlength=solver.iters + 1)
+                    b_ops, p_ops, mean_eval = stop_hist_ops(hist, g, solver.iters, tau)
+                    n = m.rows * m.cols
+                    entry["settings"].append({
+                        "matrix": [m.rows, m.cols], "setting": f"b{nb}g{g}",
+                        "median_ms": round(ms, 4), "min_ms": round(min(times), 4),
+                        "runs": runs, "G_weights_per_s": round(n / (ms * 1e-3) / 1e9, 2),
+                        "hbm_GBs_algorithmic": round(n * (2 + nb / 8 + 4 / g) / (ms * 1e-3) / 1e9, 1),
+                        "mean_evals_per_group": round(mean_eval, 4),
+                        "stop_step_hist": [int(x) for x in hist[:solver.iters + 1]],
+                        "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                        "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4)})
+                    log(f"config {cid} {entry['settings'][-1]}")
+                    del out, q
+                del W
+        else:
+            Ws = [workloads_mod().generate(m.rows, m.cols, wl.dist, m.seed, dev) for m in wl.matrices]
+            n_w = sum(W.numel() for W in Ws)
+            entry["matrices"] = len(Ws)
+            entry["weights_per_setting"] = n_w
+            for nb, g in wl.settings:
+                b = hq.quantize_batch(Ws, nb, g, p=solver.p, beta=solver.beta,
+                                      kappa=solver.kappa, iters=solver.iters)
+                entries, _ = hq.batch_table(Ws, g)
+                args = (entries, b.table.data_ptr(), len(Ws), nb, g, solver.p, solver.beta,
+                        solver.kappa, solver.iters, b.packed.data_ptr(), b.scale.data_ptr(),
+                        b.zero.data_ptr(), b.status.data_ptr(), sh)
+                for _ in range(warmup):
+                    assert lib.hqq_quantize_batch(*args) == 0
+                torch.cuda.synchronize()
+                b.check()
+                times = []
+                for _ in range(5):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    assert lib.hqq_quantize_batch(*args) == 0
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    times.append(e0.elapsed_time(e1))
+                ms = float(np.median(times))
+                hist = np.zeros(256, np.int64)
+                stop = torch.empty(max(W.numel() for W in Ws) // g, dtype=torch.uint8, device=dev)
+                opts = hq.hqq_options_t(1, 0, 0, stop.data_ptr(), 0, 0)
+                for W in Ws:
+                    r, c = W.shape
+                    assert hq.hqq_quantize_ex(W.data_ptr(), r, c, nb, g, solver.p, solver.beta,
+                                              solver.kappa, solver.iters,
+                                              b.packed.data_ptr(), b.scale.data_ptr(),
+                                              b.zero.data_ptr(), opts, sh) == 0
+                    hist += np.bincount(stop[:r * c // g].cpu().numpy().astype(np.int64),
+                                        minlength=256)
+                b_ops, p_ops, mean_eval = stop_hist_ops(hist, g, solver.iters, tau)
+                entry["settings"].append({
+                    "setting": f"b{nb}g{g}", "launch": "hqq_quantize_batch, one launch",
+                    "median_ms": round(ms, 3), "min_ms": round(min(times), 3), "runs": 5,
+                    "G_weights_per_s": round(n_w / (ms * 1e-3) / 1e9, 1),
+                    "hbm_GBs_algorithmic": round(n_w * (2 + nb / 8 + 4 / g) / (ms * 1e-3) / 1e9, 1),
+                    "mean_evals_per_group": round(mean_eval, 4),
+                    "stop_step_hist": [int(x) for x in hist[:solver.iters + 1]],
+                    "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                    "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4)})
+                log(f"config {cid} {entry['settings'][-1]}")
+                del b, stop
+            # a few rows of one matrix of each shape for the oracle's extrapolated time
+            for mi in (0, 4, 6):
+                m = wl.matrices[mi]
+                idx = sample_rows(m.rows, m.seed, n=6)
+                host_inputs[(cid, mi)] = Ws[mi][torch.as_tensor(idx, device=dev)].cpu().numpy().view(np.uint16)
+            del Ws
+        torch.cuda.empty_cache()
+        res[f"{cid}_{name}"] = entry
+    return res, host_inputs
+
+
+def workloads_mod():
+    import workloads
+    return workloads
 
 
 def measure_meta(hq, lib, torch, Ws, settings, calls, packed, scale, zero, stream, sh, dev):
@@ -653,6 +885,10 @@ def main():
     ap.add_argument("--no-meta", action="store_true",
                     help="skip the 8-bit meta-quantization measurement (next_rows)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the C1-C4 per-config measurements")
+    ap.add_argument("--peak-probe", metavar="OUT_MD", default=None,
+                    help="only measure the VALU issue rates and write their summary to OUT_MD")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 4 GiB device copy (HBM counter calibration)")
     ap.add_argument("--profile-run", action="store_true",
@@ -720,6 +956,26 @@ def main():
         log(f"copy probe: {n} bytes read, {n} bytes written")
         return
 
+    if args.peak_probe:
+        peaks = measure_peaks(torch, dev, torch.cuda.current_stream())
+        lines = ["# VALU issue rates on one MI355X (libhqq_valu_probe.so)", "",
+                 "256 CUs x 8 blocks of 4 wavefronts (8 wavefronts per SIMD); every thread runs "
+                 f"{peaks['trips']} trips of 64 instructions in 8 independent chains; HIP events "
+                 "around 5 launches per instruction. Cycles at the nominal 2.4 GHz clock; the "
+                 "ratio to v_add_f32 does not depend on the clock.", "",
+                 "| instruction | ms per launch | SIMD cycles per wave64 instruction | relative to v_add_f32 |",
+                 "|---|---|---|---|"]
+        for name, v in peaks["instr"].items():
+            lines.append(f"| {name} | {v['ms']:.4f} | {v['cycles_per_wave_instr']:.3f} | "
+                         f"{v['rel_to_add']:.3f} |")
+        lines += ["", f"tau (mean of v_exp_f32 and v_log_f32 relative to v_add_f32) = {peaks['tau']}",
+                  "", "Command:", "", "```", args.profile_command or "python bench.py --peak-probe OUT_MD",
+                  "```", ""]
+        with open(args.peak_probe, "w") as f:
+            f.write("\n".join(lines))
+        print(json.dumps(peaks), flush=True)
+        return
+
     lib = hq.load_library()
     wl = workloads.WORKLOADS[args.workload]
     if args.profile_matmul:
@@ -761,16 +1017,17 @@ def main():
     sh = int(stream.cuda_stream)
 
     calls = []  # (setting index, entry point, args)
-    tables = []  # host entry tables and their device copies (kept alive)
+    tables = []  # host entry tables, their device copies and status words (kept alive)
     for si, (nb, g) in enumerate(settings):
         if not args.per_matrix:
             entries, _ = hq.batch_table(Ws, g)
             dev_table = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8).to(dev)
-            tables.append((entries, dev_table))
+            status = torch.full((1,), -1, dtype=torch.int32, device=dev)
+            tables.append((entries, dev_table, status))
             calls.append((si, lib.hqq_quantize_batch,
                           (entries, dev_table.data_ptr(), len(Ws), nb, g, solver.p, solver.beta,
                            solver.kappa, solver.iters, packed.data_ptr(), scale.data_ptr(),
-                           zero.data_ptr(), sh)))
+                           zero.data_ptr(), status.data_ptr(), sh)))
             continue
         off_p = off_g = 0
         for W in Ws:
@@ -854,6 +1111,31 @@ def main():
     weights_per_step = n_weights * len(settings)
     value = weights_per_step * args.steps / (total_ms * 1e-3) / 1e9
 
+    # ---- the timed call's own output, sampled at its largest offsets (untimed) -----------
+    # The arena holds the last setting now; the other settings are launched once more with
+    # the timed call's arguments.  Each batched launch's status word must read HQQ_OK.
+    arena = {}
+    if not args.per_matrix:
+        for si in reversed(range(len(settings))):
+            if si != len(settings) - 1:
+                for sj, fn, a in calls:
+                    if sj == si:
+                        assert fn(*a) == 0
+                torch.cuda.synchronize()
+            status = int(tables[si][2].item())
+            assert status == 0, f"batched launch status {hq.hqq_status_string(status)}"
+            nb, g = settings[si]
+            arena[si] = collect_arena_rows(hq, torch, Ws, mats, nb, g, solver, packed, scale,
+                                           zero)
+            assert all(r["arena_equals_rows_alone"] for r in arena[si]), \
+                "batched arena rows differ from the same rows quantized alone"
+        log("arena check: sampled rows of the last layer equal the rows quantized alone")
+
+    # ---- issue rates of the VALU instruction classes (probe, untimed above) -------------
+    peaks = measure_peaks(torch, dev, stream)
+    tau = peaks["tau"]
+    log(f"VALU issue rates: {peaks}")
+
     # ---- stop-step histogram (separate, untimed pass) --------------------------------
     hist = []
     for si, (nb, g) in enumerate(settings):
@@ -871,19 +1153,12 @@ def main():
         hist.append(h.cpu().numpy())
     torch.cuda.synchronize()
 
-    def op_count(h, g):
-        t = np.arange(256)
-        n_eval = np.where(t == solver.iters, solver.iters + 1, t + 2)
-        n_upd = n_eval - 1
-        groups = h.sum()
-        ops = g * np.sum(h * (OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval + OPS_UPDATE * n_upd))
-        return float(ops), float(np.sum(h * n_eval) / groups)
-
-    ops_step = 0.0
+    ops_step = plan_step = 0.0
     detail = []
     for si, (nb, g) in enumerate(settings):
-        ops, mean_eval = op_count(hist[si], g)
+        ops, plan, mean_eval = stop_hist_ops(hist[si], g, solver.iters, tau)
         ops_step += ops
+        plan_step += plan
         bytes_alg = n_weights * (2 + nb / 8 + 4 / g)
         detail.append({
             "setting": f"b{nb}g{g}", "ms": round(per_setting_ms[si], 3),
@@ -892,10 +1167,17 @@ def main():
             "stop_step_hist": [int(x) for x in hist[si][: solver.iters + 1]],
             "valu_TOPs": round(ops / (per_setting_ms[si] * 1e-3) / 1e12, 2),
             "valu_frac": round(ops / (per_setting_ms[si] * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+            "valu_frac_plan_model": round(plan / (per_setting_ms[si] * 1e-3) / PEAK_VALU_LANE_OPS, 4),
             "hbm_GBs_algorithmic": round(bytes_alg / (per_setting_ms[si] * 1e-3) / 1e9, 1),
         })
     avg_launch_s = total_ms * 1e-3 / (args.steps * launches_per_step)
     achieved = ops_step / launches_per_step / avg_launch_s  # lane-ops/s
+    achieved_plan = plan_step / launches_per_step / avg_launch_s
+
+    # ---- the smaller workloads (C1-C4) under the same timing rules -----------------------
+    configs, config_inputs = None, {}
+    if not args.no_configs:
+        configs, config_inputs = measure_configs(hq, lib, torch, dev, stream, sh, tau)
     bytes_step = sum(n_weights * (2 + nb / 8 + 4 / g) for nb, g in settings)
     traffic = traffic_from_profile(n_weights * len(settings) / launches_per_step)
 
@@ -921,42 +1203,109 @@ def main():
     if not args.no_lowrank:
         lowrank = measure_lowrank(hq, lib, torch, Ws[:7], settings, solver, stream, sh, dev)
 
-    # ---- CPU baseline: the oracle on a bounded row sample, one core -------------------
+    # ---- CPU baseline: the oracle on a bounded sample, pinned to one host core ---------
+    # All GPU work is done; host blocks are copied out first.  The leg also compares the
+    # timed call's sampled rows (collected above) with the oracle under the parity
+    # tolerances, and times the oracle on the whole C1, C2 and C3 matrices.
     cpu = None
+    full_stack = None
     if not args.no_cpu_baseline:
         import oracle
+        from tests import parity
         oracle._load()
+        rows_each = 16
+        rng = np.random.default_rng(12345)
+        blocks = []  # (setting, matrix, first row, host bits) drawn from every layer
+        for k in range(600):
+            si = k % len(settings)
+            mi = int(rng.integers(0, len(Ws)))
+            r0 = int(rng.integers(0, Ws[mi].shape[0] - rows_each))
+            blocks.append((si, mi, r0, Ws[mi][r0:r0 + rows_each].cpu().numpy().view(np.uint16)))
+        torch.cuda.synchronize()
+        host_cores = len(os.sched_getaffinity(0))
+        core = min(os.sched_getaffinity(0))
+        os.sched_setaffinity(0, {core})  # this thread (the oracle's) on one core
+        kw = dict(p=solver.p, beta=solver.beta, kappa=solver.kappa, iters=solver.iters)
+
+        # the timed call's sampled rows against the oracle (parity tolerances)
+        t_check = 0.0
+        if arena:
+            full_stack = {"entry_point": "hqq_quantize_batch", "per_setting": []}
+            for si in sorted(arena):
+                nb, g = settings[si]
+                reps = []
+                for rec in arena[si]:
+                    t1 = time.thread_time()
+                    ref = oracle.hqq_quantize(rec["W16"], nb, g, **kw)
+                    t_check += time.thread_time() - t1
+                    d = rec["dev"]
+                    dev_res = parity.DeviceResult(
+                        packed=d["packed"], scale16=d["scale"].view(np.uint16),
+                        zero16=d["zero"].view(np.uint16), scale32=d["scale_f32"],
+                        zero32=d["zero_f32"], stop=d["stop_step"], err_init=d["err_init"],
+                        err_best=d["err_best"])
+                    rep = parity.compare(rec["W16"], dev_res, nb, g, ref=ref, **kw)
+                    reps.append(rep)
+                full_stack["per_setting"].append({
+                    "setting": f"b{nb}g{g}", "matrices": [r["matrix"] for r in arena[si]],
+                    "rows_per_matrix": [len(r["rows"]) for r in arena[si]],
+                    "max_byte_offset": max(r["max_byte_offset"] for r in arena[si]),
+                    "max_group_offset": max(r["max_group_offset"] for r in arena[si]),
+                    "arena_equals_rows_alone": all(r["arena_equals_rows_alone"] for r in arena[si]),
+                    "groups": sum(r["groups"] for r in reps),
+                    "stop_agree_min": min(r["stop_agree"] for r in reps),
+                    "code_mismatches": sum(r["code_mismatch_total"] for r in reps),
+                    "divergent_explained": {
+                        k: sum(r["divergent"][k] for r in reps) for k in ("error_tie", "rounding_tie")},
+                    "parity": "pass"})
+            log(f"full-stack check: {full_stack}")
+
         done_w = 0
         t_cpu = 0.0
-        sample = []
-        budget = args.cpu_seconds
-        layer0 = mats[:7] if len(mats) >= 7 else mats
-        rows_each = 16
-        while t_cpu < budget:
-            progressed = False
-            for si, (nb, g) in enumerate(settings):
-                for mi, W in enumerate(Ws[: len(layer0)]):
-                    r0 = (len(sample) * 7919) % (W.shape[0] - rows_each)
-                    host = W[r0: r0 + rows_each].cpu().numpy().view(np.uint16)
-                    t1 = time.process_time()
-                    oracle.hqq_quantize(host, nb, g, p=solver.p, beta=solver.beta,
-                                        kappa=solver.kappa, iters=solver.iters)
-                    t_cpu += time.process_time() - t1
-                    done_w += host.size
-                    sample.append((si, mi, r0))
-                    progressed = True
-                    if t_cpu >= budget:
-                        break
-                if t_cpu >= budget:
-                    break
-            if not progressed:
+        n_blocks = 0
+        for si, mi, r0, host in blocks:
+            nb, g = settings[si]
+            t1 = time.thread_time()
+            oracle.hqq_quantize(host, nb, g, **kw)
+            t_cpu += time.thread_time() - t1
+            done_w += host.size
+            n_blocks += 1
+            if t_cpu >= args.cpu_seconds:
                 break
         cpu = {"value": round(done_w / t_cpu / 1e9, 6), "unit": "G weights/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{len(sample)} blocks of {rows_each} consecutive rows from the 7 matrices "
-                         f"of layer 0, both settings alternating, {done_w / 1e6:.1f} M weights, "
-                         f"{t_cpu:.1f} s CPU (process time) on one thread of the host"}
+               "host_cores_available": host_cores, "kind": "oracle",
+               "sample": f"{n_blocks} blocks of {rows_each} consecutive rows at seeded positions "
+                         f"in all {len(Ws)} matrices, the settings alternating, "
+                         f"{done_w / 1e6:.1f} M weights, {t_cpu:.1f} s of CPU time of one "
+                         f"thread pinned to core {core} ({host_cores} available)"}
         log(f"cpu baseline: {cpu}")
+
+        # full-matrix oracle timings of C1-C3 (C4: rows of one matrix of each shape)
+        if configs:
+            for cid, name in CONFIGS:
+                wl_c = workloads.WORKLOADS[name]
+                entry = configs[f"{cid}_{name}"]
+                ow = ot = 0.0
+                full = name != "llama7b_stack"
+                for (c2, mi), bits in config_inputs.items():
+                    if c2 != cid:
+                        continue
+                    for nb, g in wl_c.settings:
+                        t1 = time.thread_time()
+                        oracle.hqq_quantize(bits, nb, g, p=wl_c.solver.p, beta=wl_c.solver.beta,
+                                            kappa=wl_c.solver.kappa, iters=wl_c.solver.iters)
+                        ot += time.thread_time() - t1
+                        ow += bits.size
+                entry["oracle"] = {
+                    "G_weights_per_s": round(ow / ot / 1e9, 6), "cores": 1,
+                    "sample": ("every matrix in full, every setting" if full else
+                               "first, last and 6 seeded rows of one matrix of each shape, "
+                               "every setting; the whole stack extrapolated"),
+                    "cpu_s": round(ot, 2)}
+                if not full:
+                    entry["oracle"]["stack_s_extrapolated"] = round(
+                        entry["weights_per_setting"] * len(wl_c.settings) / (ow / ot), 1)
+                log(f"oracle {cid}: {entry['oracle']}")
 
     out = {
         "metric": METRIC,
@@ -990,8 +1339,16 @@ def main():
             "ops_per_launch": round(ops_step / launches_per_step),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "hbm_frac_algorithmic": round(bytes_step / (ms_per_step * 1e-3) / PEAK_HBM, 4),
+            "plan_model": {
+                "ops_per_weight": "3 + n_eval (8 + 2 tau) + n_upd 6",
+                "tau": tau, "ops_per_launch": round(plan_step / launches_per_step),
+                "achieved": round(achieved_plan / 1e12, 3),
+                "frac": round(achieved_plan / PEAK_VALU_LANE_OPS, 4)},
+            "peaks_measured": peaks,
         },
         "per_setting": detail,
+        "full_stack_check": full_stack,
+        "per_config": configs,
         "cpu_baseline": cpu,
         "next_rows": {"meta_quantization": meta, "solver_variants": variants,
                       "quantized_matmul": matmul, "lowrank_compensation": lowrank},

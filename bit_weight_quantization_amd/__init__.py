@@ -24,6 +24,7 @@ HQQ_ERR_INVALID_ARG = 1
 HQQ_ERR_UNSUPPORTED = 2
 HQQ_ERR_ALIGNMENT = 3
 HQQ_ERR_LAUNCH = 4
+HQQ_ERR_TABLE_MISMATCH = 5
 
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
@@ -85,7 +86,7 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_tensor_stop_workspace_bytes.argtypes = [I]
     lib.hqq_quantize_batch.restype = I
     lib.hqq_quantize_batch.argtypes = [ctypes.POINTER(hqq_batch_entry_t), P, I, I, I, F, F, F, I,
-                                       P, P, P, P]
+                                       P, P, P, P, P]
     lib.hqq_meta_quantize.restype = I
     lib.hqq_meta_quantize.argtypes = [P, I64, I64, P, P, P, P, P]
     lib.hqq_meta_dequantize.restype = I
@@ -181,11 +182,11 @@ def hqq_tensor_stop_workspace_bytes(iters: int) -> int:
 
 def hqq_quantize_batch(entries, entries_device: int, count: int, nbits: int, group_size: int,
                        p: float, beta: float, kappa: float, iters: int, packed_codes: int,
-                       scale_f16: int, zero_f16: int, stream: int = 0) -> int:
+                       scale_f16: int, zero_f16: int, status_device: int, stream: int = 0) -> int:
     """``entries``: a ctypes array of ``hqq_batch_entry_t`` (host copy)."""
     return load_library().hqq_quantize_batch(entries, entries_device, count, nbits, group_size, p,
                                              beta, kappa, iters, packed_codes, scale_f16, zero_f16,
-                                             stream)
+                                             status_device, stream)
 
 
 def hqq_meta_groups(n: int, meta_group: int) -> int:
@@ -251,6 +252,26 @@ def _addr(t) -> int:
     return int(t.data_ptr()) if t is not None else 0
 
 
+def _alloc_on(stream):
+    """Context for allocating the outputs of a launch on ``stream``: the caching allocator
+    then ties them to that stream, so memory the caller drops early is not handed to
+    other streams while the launch may still write it."""
+    import contextlib
+
+    import torch
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _check_tensor(t, name: str, dtype, numel: int, shape=None):
+    import torch
+    if t is None or not isinstance(t, torch.Tensor):
+        raise ValueError(f"out.{name} is missing")
+    if t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"out.{name} must be a contiguous {dtype} CUDA tensor")
+    if t.numel() != numel or (shape is not None and tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"out.{name} has {tuple(t.shape)}, expected {shape or (numel,)}")
+
+
 def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
              kappa: float = 1.01, iters: int = 20, early_stop: bool = True, debug: bool = False,
              out: Optional[QuantizedWeight] = None, stream=None,
@@ -260,7 +281,7 @@ def quantize(W, nbits: int, group_size: int, p: float = 0.7, beta: float = 1.0,
     ``out`` may supply preallocated output tensors (reused as-is).  With ``debug`` the
     fp32 s and z, the stop step and the initial/best errors per group are returned too.
     """
-    out = _outputs(W, nbits, group_size, debug, out, "quantize")
+    out = _outputs(W, nbits, group_size, debug, out, "quantize", stream)
     rows, cols = W.shape
     opts = None
     if debug or not early_stop or refill_threshold or err_metric:
@@ -285,19 +306,18 @@ def quantize_tensor_stop(W, nbits: int, group_size: int, p: float = 0.7, beta: f
     CUDA tensor of at least hqq_tensor_stop_workspace_bytes(iters) bytes.
     """
     import torch
-    out = _outputs(W, nbits, group_size, debug, out, "quantize_tensor_stop")
+    out = _outputs(W, nbits, group_size, debug, out, "quantize_tensor_stop", stream)
     rows, cols = W.shape
     wb = hqq_tensor_stop_workspace_bytes(int(iters))
     if wb < 0:
         raise HQQError(HQQ_ERR_INVALID_ARG, "quantize_tensor_stop")
-    if workspace is None:
-        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
-        if stream is not None:  # freed on return: keep it until the stream's work is done
-            workspace.record_stream(stream)
-    elif workspace.numel() < wb or not workspace.is_cuda:
-        raise ValueError(f"workspace needs {wb} bytes of device memory")
-    totals = torch.empty(int(iters) + 1, dtype=torch.float64, device=W.device)
-    t_star = torch.empty(1, dtype=torch.int32, device=W.device)
+    with _alloc_on(stream):
+        if workspace is None:
+            workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+        elif workspace.numel() < wb or not workspace.is_cuda:
+            raise ValueError(f"workspace needs {wb} bytes of device memory")
+        totals = torch.empty(int(iters) + 1, dtype=torch.float64, device=W.device)
+        t_star = torch.empty(1, dtype=torch.int32, device=W.device)
     opts = _options(out, debug, True, 0, err_metric)
     st = hqq_quantize_tensor_stop(_addr(W), rows, cols, nbits, group_size, float(p), float(beta),
                                   float(kappa), int(iters), _addr(out.packed), _addr(out.scale),
@@ -309,8 +329,9 @@ def quantize_tensor_stop(W, nbits: int, group_size: int, p: float = 0.7, beta: f
 
 
 def _outputs(W, nbits: int, group_size: int, debug: bool, out: Optional[QuantizedWeight],
-             where: str) -> QuantizedWeight:
-    """Checks W and allocates the output tensors that ``out`` does not supply."""
+             where: str, stream=None) -> QuantizedWeight:
+    """Checks W, checks a supplied ``out`` against W's shape and the settings, and
+    allocates the output tensors that ``out`` does not supply."""
     import torch
     if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
         raise ValueError("W must be a contiguous 2-D float16 CUDA tensor")
@@ -320,19 +341,32 @@ def _outputs(W, nbits: int, group_size: int, debug: bool, out: Optional[Quantize
     if ng < 0 or nb < 0:
         raise HQQError(HQQ_ERR_INVALID_ARG if nb >= 0 else HQQ_ERR_UNSUPPORTED, where)
     dev = W.device
-    if out is None:
-        out = QuantizedWeight(
-            packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
-            scale=torch.empty((rows, cols // group_size), dtype=torch.float16, device=dev),
-            zero=torch.empty((rows, cols // group_size), dtype=torch.float16, device=dev),
-            rows=rows, cols=cols, nbits=nbits, group_size=group_size)
-    if debug and out.stop_step is None:
-        shp = (rows, cols // group_size)
-        out.scale_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
-        out.zero_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
-        out.stop_step = torch.empty(shp, dtype=torch.uint8, device=dev)
-        out.err_init = torch.empty(shp, dtype=torch.float32, device=dev)
-        out.err_best = torch.empty(shp, dtype=torch.float32, device=dev)
+    shp = (rows, cols // group_size)
+    if out is not None:
+        if (out.rows, out.cols, out.nbits, out.group_size) != (rows, cols, nbits, group_size):
+            raise ValueError(f"{where}: out was made for {out.rows}x{out.cols} b{out.nbits} "
+                             f"g{out.group_size}, not {rows}x{cols} b{nbits} g{group_size}")
+        _check_tensor(out.packed, "packed", torch.uint8, nb)
+        _check_tensor(out.scale, "scale", torch.float16, ng, shp)
+        _check_tensor(out.zero, "zero", torch.float16, ng, shp)
+        if debug and out.stop_step is not None:
+            for name, dt in (("scale_f32", torch.float32), ("zero_f32", torch.float32),
+                             ("stop_step", torch.uint8), ("err_init", torch.float32),
+                             ("err_best", torch.float32)):
+                _check_tensor(getattr(out, name), name, dt, ng, shp)
+    with _alloc_on(stream):
+        if out is None:
+            out = QuantizedWeight(
+                packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
+                scale=torch.empty(shp, dtype=torch.float16, device=dev),
+                zero=torch.empty(shp, dtype=torch.float16, device=dev),
+                rows=rows, cols=cols, nbits=nbits, group_size=group_size)
+        if debug and out.stop_step is None:
+            out.scale_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
+            out.zero_f32 = torch.empty(shp, dtype=torch.float32, device=dev)
+            out.stop_step = torch.empty(shp, dtype=torch.uint8, device=dev)
+            out.err_init = torch.empty(shp, dtype=torch.float32, device=dev)
+            out.err_best = torch.empty(shp, dtype=torch.float32, device=dev)
     return out
 
 
@@ -358,7 +392,8 @@ def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, stream=None
         raise ValueError(f"X has {K} columns, the weight {q.cols}")
     dt = torch.float32 if out_f32 else torch.float16
     if out is None:
-        out = torch.empty((M, q.rows), dtype=dt, device=X.device)
+        with _alloc_on(stream):
+            out = torch.empty((M, q.rows), dtype=dt, device=X.device)
     elif out.dtype != dt or tuple(out.shape) != (M, q.rows) or not out.is_contiguous():
         raise ValueError("out has the wrong dtype or shape")
     st = hqq_matmul(_addr(X), M, K, _addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows,
@@ -372,8 +407,9 @@ def residual(W, q: "QuantizedWeight", transposed: bool = False, stream=None):
     """Delta W = W - Q^-1(W_q) as float16 (hqq_residual); with ``transposed`` also its
     transpose.  Returns dW or (dW, dWT)."""
     import torch
-    dW = torch.empty_like(W)
-    dWT = torch.empty((W.shape[1], W.shape[0]), dtype=W.dtype, device=W.device) if transposed else None
+    with _alloc_on(stream):
+        dW = torch.empty_like(W)
+        dWT = torch.empty((W.shape[1], W.shape[0]), dtype=W.dtype, device=W.device) if transposed else None
     st = hqq_residual(_addr(W), _addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows, q.cols,
                       q.nbits, q.group_size, _addr(dW), _addr(dWT), _stream_handle(stream))
     if st != HQQ_OK:
@@ -396,13 +432,12 @@ def lowrank(W, q: "QuantizedWeight", rank: int, oversample: int = 32, power_iter
     wb = hqq_lowrank_workspace_bytes(rows, cols, rank, oversample)
     if wb < 0:
         raise HQQError(HQQ_ERR_INVALID_ARG, "lowrank")
-    if workspace is None:
-        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
-        if stream is not None:
-            workspace.record_stream(stream)
-    B = torch.empty((rows, rank), dtype=torch.float32, device=W.device)
-    A = torch.empty((rank, cols), dtype=torch.float32, device=W.device)
-    sigma = torch.empty(rank, dtype=torch.float32, device=W.device)
+    with _alloc_on(stream):
+        if workspace is None:
+            workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+        B = torch.empty((rows, rank), dtype=torch.float32, device=W.device)
+        A = torch.empty((rank, cols), dtype=torch.float32, device=W.device)
+        sigma = torch.empty(rank, dtype=torch.float32, device=W.device)
     st = hqq_lowrank(_addr(W), _addr(q.packed), _addr(q.scale), _addr(q.zero), rows, cols, q.nbits,
                      q.group_size, rank, oversample, power_iters, _addr(omega), _addr(B), _addr(A),
                      _addr(sigma), _addr(workspace), _stream_handle(stream))
@@ -422,6 +457,14 @@ class QuantizedBatch:
     nbits: int
     group_size: int
     table: "torch.Tensor"             # device copy of the entry table (kept for the launch)
+    status: "torch.Tensor"            # int32 status word the launch writes (table check)
+
+    def check(self) -> None:
+        """Synchronizes on the status word and raises if the launch found its device
+        entry table different from the validated host table (then it wrote nothing)."""
+        st = int(self.status.item())
+        if st != HQQ_OK:
+            raise HQQError(st, "hqq_quantize_batch")
 
     def matrix(self, i: int) -> QuantizedWeight:
         """Views of matrix i's outputs (no copy)."""
@@ -461,26 +504,37 @@ def quantize_batch(Ws, nbits: int, group_size: int, p: float = 0.7, beta: float 
         if W.dtype != torch.float16 or W.dim() != 2 or not W.is_cuda or not W.is_contiguous():
             raise ValueError("every W must be a contiguous 2-D float16 CUDA tensor")
     entries, total = batch_table(Ws, group_size)
+    nb = total * group_size * nbits // 8
+    table_bytes = max(len(Ws), 1) * ctypes.sizeof(hqq_batch_entry_t)
+    shapes = [tuple(W.shape) for W in Ws]
     if out is None:
         dev = Ws[0].device if Ws else torch.device("cuda")
-        nb = total * group_size * nbits // 8
         starts, g = [], 0
         for W in Ws:
             starts.append(g)
             g += W.numel() // group_size
-        out = QuantizedBatch(
-            packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
-            scale=torch.empty(total, dtype=torch.float16, device=dev),
-            zero=torch.empty(total, dtype=torch.float16, device=dev),
-            shapes=[tuple(W.shape) for W in Ws], first_group=starts, nbits=nbits,
-            group_size=group_size,
-            table=torch.empty(max(len(Ws), 1) * ctypes.sizeof(hqq_batch_entry_t), dtype=torch.uint8,
-                              device=dev))
+        with _alloc_on(stream):
+            out = QuantizedBatch(
+                packed=torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)[:nb],
+                scale=torch.empty(total, dtype=torch.float16, device=dev),
+                zero=torch.empty(total, dtype=torch.float16, device=dev),
+                shapes=shapes, first_group=starts, nbits=nbits, group_size=group_size,
+                table=torch.empty(table_bytes, dtype=torch.uint8, device=dev),
+                status=torch.empty(1, dtype=torch.int32, device=dev))
+    else:  # reuse only an arena made for exactly these shapes and settings
+        if (list(out.shapes) != shapes or out.nbits != nbits or out.group_size != group_size):
+            raise ValueError("quantize_batch: out was made for other shapes, nbits or group_size")
+        _check_tensor(out.packed, "packed", torch.uint8, nb)
+        _check_tensor(out.scale, "scale", torch.float16, total)
+        _check_tensor(out.zero, "zero", torch.float16, total)
+        _check_tensor(out.table, "table", torch.uint8, table_bytes)
+        _check_tensor(out.status, "status", torch.int32, 1)
     host = torch.frombuffer(bytearray(bytes(entries)), dtype=torch.uint8)
-    out.table.copy_(host[: out.table.numel()], non_blocking=False)
+    out.table.copy_(host, non_blocking=False)
     st = hqq_quantize_batch(entries, _addr(out.table), len(Ws), nbits, group_size, float(p),
                             float(beta), float(kappa), int(iters), _addr(out.packed),
-                            _addr(out.scale), _addr(out.zero), _stream_handle(stream))
+                            _addr(out.scale), _addr(out.zero), _addr(out.status),
+                            _stream_handle(stream))
     if st != HQQ_OK:
         raise HQQError(st, "hqq_quantize_batch")
     return out
@@ -508,12 +562,13 @@ def meta_quantize(values, meta_group: int, workspace=None, stream=None) -> MetaQ
     if ng < 0:
         raise HQQError(HQQ_ERR_INVALID_ARG, "meta_quantize")
     dev = values.device
-    out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
-                        scale=torch.empty(ng, dtype=torch.float16, device=dev),
-                        offset=torch.empty(ng, dtype=torch.float16, device=dev),
-                        n=n, meta_group=meta_group)
-    if meta_group == 0 and workspace is None:
-        workspace = torch.empty(hqq_meta_workspace_bytes(), dtype=torch.uint8, device=dev)
+    with _alloc_on(stream):
+        out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
+                            scale=torch.empty(ng, dtype=torch.float16, device=dev),
+                            offset=torch.empty(ng, dtype=torch.float16, device=dev),
+                            n=n, meta_group=meta_group)
+        if meta_group == 0 and workspace is None:
+            workspace = torch.empty(hqq_meta_workspace_bytes(), dtype=torch.uint8, device=dev)
     out.workspace = workspace
     st = hqq_meta_quantize(_addr(values), n, meta_group, _addr(out.codes), _addr(out.scale),
                            _addr(out.offset), _addr(workspace), _stream_handle(stream))
@@ -538,12 +593,13 @@ def meta_quantize_batch(b: "QuantizedBatch", which: str, meta_group: int, stream
                 0, rows, cols, g0
     ng = count if meta_group == 0 else (n // meta_group if meta_group else 0)
     dev = values.device
-    out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
-                        scale=torch.empty(ng, dtype=torch.float16, device=dev),
-                        offset=torch.empty(ng, dtype=torch.float16, device=dev),
-                        n=n, meta_group=meta_group)
-    if meta_group == 0:
-        out.workspace = torch.empty(max(8 * count, 4), dtype=torch.uint8, device=dev)
+    with _alloc_on(stream):
+        out = MetaQuantized(codes=torch.empty(n, dtype=torch.uint8, device=dev),
+                            scale=torch.empty(ng, dtype=torch.float16, device=dev),
+                            offset=torch.empty(ng, dtype=torch.float16, device=dev),
+                            n=n, meta_group=meta_group)
+        if meta_group == 0:
+            out.workspace = torch.empty(max(8 * count, 4), dtype=torch.uint8, device=dev)
     st = hqq_meta_quantize_batch(entries, _addr(b.table), count, b.group_size, _addr(values),
                                  meta_group, _addr(out.codes), _addr(out.scale), _addr(out.offset),
                                  _addr(out.workspace), _stream_handle(stream))
@@ -556,7 +612,10 @@ def meta_dequantize(m: MetaQuantized, out=None, stream=None):
     """offset + scale * code as a flat fp16 tensor of n values (single rounding)."""
     import torch
     if out is None:
-        out = torch.empty(m.n, dtype=torch.float16, device=m.codes.device)
+        with _alloc_on(stream):
+            out = torch.empty(m.n, dtype=torch.float16, device=m.codes.device)
+    else:
+        _check_tensor(out, "values", torch.float16, m.n)
     st = hqq_meta_dequantize(_addr(m.codes), _addr(m.scale), _addr(m.offset), m.n, m.meta_group,
                              _addr(out), _stream_handle(stream))
     if st != HQQ_OK:
@@ -568,7 +627,10 @@ def dequantize(q: QuantizedWeight, out=None, stream=None):
     """Return s*(W_q - z) as a rows x cols fp16 tensor (single rounding from the exact value)."""
     import torch
     if out is None:
-        out = torch.empty((q.rows, q.cols), dtype=torch.float16, device=q.scale.device)
+        with _alloc_on(stream):
+            out = torch.empty((q.rows, q.cols), dtype=torch.float16, device=q.scale.device)
+    else:
+        _check_tensor(out, "W", torch.float16, q.rows * q.cols, (q.rows, q.cols))
     st = hqq_dequantize(_addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows, q.cols, q.nbits,
                         q.group_size, _addr(out), _stream_handle(stream))
     if st != HQQ_OK:

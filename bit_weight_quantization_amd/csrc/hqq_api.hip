@@ -148,6 +148,7 @@ const char* hqq_status_string(int status) {
     case HQQ_ERR_UNSUPPORTED: return "unsupported nbits or group_size";
     case HQQ_ERR_ALIGNMENT: return "misaligned pointer";
     case HQQ_ERR_LAUNCH: return "kernel launch failed";
+    case HQQ_ERR_TABLE_MISMATCH: return "device entry table differs from the host table";
     default: return "unknown status";
   }
 }
@@ -223,7 +224,7 @@ int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int 
 int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t* entries_device,
                        int count, int nbits, int group_size, float p, float beta, float kappa,
                        int iters, void* packed_codes, void* scale_f16, void* zero_f16,
-                       void* stream) {
+                       int32_t* status_device, void* stream) {
   static_assert(sizeof(hqq_batch_entry_t) == sizeof(hqq::BatchEntry), "entry layout");
   static_assert(offsetof(hqq_batch_entry_t, first_group) == offsetof(hqq::BatchEntry, first_group),
                 "entry layout");
@@ -250,14 +251,21 @@ int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t
     total += groups;
   }
   if (total == 0) return HQQ_OK;
-  if (!packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
-  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2))
+  if (!packed_codes || !scale_f16 || !zero_f16 || !status_device) return HQQ_ERR_INVALID_ARG;
+  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
+      !aligned(status_device, 4))
     return HQQ_ERR_ALIGNMENT;
 
+  uint64_t hash = 0;  // of the table just validated; the kernel checks its copy against it
+  for (int i = 0; i < count; ++i)
+    hash += hqq::table_entry_hash((uint64_t)(uintptr_t)entries[i].W_f16, entries[i].rows,
+                                  entries[i].cols, entries[i].first_group, i);
   hqq::SolveParams prm = {};
   prm.W = nullptr;
   prm.batch = reinterpret_cast<const hqq::BatchEntry*>(entries_device);
   prm.batch_count = count;
+  prm.batch_hash = hash;
+  prm.batch_status = status_device;
   prm.packed = static_cast<uint8_t*>(packed_codes);
   prm.scale16 = static_cast<uint16_t*>(scale_f16);
   prm.zero16 = static_cast<uint16_t*>(zero_f16);

@@ -19,10 +19,32 @@ struct BatchEntry {
   int64_t first_group;     // global index of the matrix's first group
 };
 
+// Hash of a batch entry table, computed identically on the host (over the validated
+// table) and on the device (over the copy the kernel reads): the sum over entries i of
+// mix(mix(mix(mix(W + i) ^ rows) ^ cols) ^ first_group), with mix the SplitMix64
+// finalizer (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+// 2014).  The entry index enters every term, so a reordered table changes the sum too.
+__host__ __device__ inline uint64_t table_mix(uint64_t x) {
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ull;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebull;
+  return x ^ (x >> 31);
+}
+__host__ __device__ inline uint64_t table_entry_hash(uint64_t w, int64_t rows, int64_t cols,
+                                                     int64_t first_group, int i) {
+  uint64_t h = table_mix(w + (uint64_t)i);
+  h = table_mix(h ^ (uint64_t)rows);
+  h = table_mix(h ^ (uint64_t)cols);
+  return table_mix(h ^ (uint64_t)first_group);
+}
+
 struct SolveParams {
   const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8 (single matrix)
   const BatchEntry* batch; // device entry table (batched launch), else null
   int batch_count;
+  uint64_t batch_hash;     // hash of the validated host table (batched launch)
+  int32_t* batch_status;   // written by the batched launch: HQQ_OK or a table mismatch
   uint8_t* packed;         // packed code stream
   uint16_t* scale16;       // binary16 s per group
   uint16_t* zero16;        // binary16 z per group

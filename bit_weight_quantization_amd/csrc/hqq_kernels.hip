@@ -116,7 +116,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t C = P.chunk_groups;
   int64_t chunk = wave;
-  if (chunk * C >= P.ngroups) return;  // wave-uniform; the kernel has no block-wide barrier
+  // A batched launch reads weights through the device entry table only once that table
+  // is shown to be the validated one (else nothing is written).  Wave-uniform returns:
+  // the kernel has no block-wide barrier.
+  if constexpr (BATCH) {
+    if (!batch_table_matches(P)) return;
+  }
+  if (chunk * C >= P.ngroups) return;
   int64_t next = chunk * C;            // next group of the wave's queue
   int64_t q_end = next + C < P.ngroups ? next + C : P.ngroups;  // end of the current chunk
 

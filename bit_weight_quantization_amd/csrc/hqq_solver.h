@@ -152,6 +152,28 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Whether the device entry table of a batched launch is the one the host validated:
+// every lane hashes entries lane, lane + 64, ... (their fields only; no weight is
+// read), the wave adds the lane sums, and the total is compared with the host's hash.
+// Wave-uniform.  Thread 0 of block 0 records the verdict in the status word.
+__device__ __forceinline__ bool batch_table_matches(const SolveParams& P) {
+  const int lane = threadIdx.x & 63;
+  uint64_t h = 0;
+  for (int i = lane; i < P.batch_count; i += 64) {
+    const BatchEntry& e = P.batch[i];
+    h += table_entry_hash((uint64_t)(uintptr_t)e.W, e.rows, e.cols, e.first_group, i);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)h, off, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(h >> 32), off, 64);
+    h += ((uint64_t)hi << 32) | lo;
+  }
+  const bool ok = uniform64((int64_t)h) == (int64_t)P.batch_hash;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *P.batch_status = ok ? 0 : 5;  // HQQ_OK, HQQ_ERR_TABLE_MISMATCH
+  return ok;
+}
+
 // The entry of a batched launch that holds the wave's next group: its index, its
 // group range [first, end) and its weights.  Wave-uniform.
 struct BatchCursor {
@@ -205,6 +227,9 @@ __device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, const BatchCu
   }
 }
 
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
 // From the lane's 8 raw binary16 weights, compute its u values and the group scalars.
 // Called by all L lanes of a segment together (segment-wide DPP reductions).
 template <int L>
@@ -249,13 +274,36 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
   // constant group has a = 0, hence u = 0.
   const float c_lo = __builtin_fmaf(-g.inv_s, d, qmax) * rcp_d;
   const uint32_t pair[4] = {raw.x, raw.y, raw.z, raw.w};
-  float lsum;
+  bool half = false;  // some u of the lane is exactly a half-integer
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
     const float a = (k & 1) ? half_minus<true>(pair[k / 2], mn) : half_minus<false>(pair[k / 2], mn);
     u[k] = __builtin_fmaf(a, g.inv_s, a * c_lo);
-    lsum = k == 0 ? u[0] : lsum + u[k];
+    half |= __builtin_amdgcn_fractf(u[k]) == 0.5f;
   }
+  // The first code decision is round(U) of the exact ratio U = (w - mn) qmax / d.  u is
+  // U rounded once to fp32, and rounding is monotonic while half-integers are exact
+  // fp32 values, so rint(u) is round(U) unless u landed exactly on a half-integer that
+  // U is not on.  There the side is decided exactly in fp64 -- (w - mn) qmax against
+  // u (mx - mn), both products of binary16 differences and small integers, exact -- and
+  // u moves one ulp towards U, so that every later evaluation starts from a value on
+  // U's side of every half-integer.  A real tie stays exactly on the half-integer.
+  if (ballot(half) != 0) {
+    if (half) {
+      const double mn64 = (double)mn, d64 = (double)mx - mn64;
+#pragma unroll
+      for (int k = 0; k < kLaneElems; ++k) {
+        if (__builtin_amdgcn_fractf(u[k]) != 0.5f) continue;
+        const uint16_t hw = (uint16_t)(pair[k / 2] >> (16 * (k & 1)));
+        const double num = ((double)(float)__builtin_bit_cast(_Float16, hw) - mn64) * (double)qmax;
+        const double mid = (double)u[k] * d64;
+        if (num != mid) u[k] = bitsf(fbits(u[k]) + (num > mid ? 1u : 0xffffffffu));  // one ulp
+      }
+    }
+  }
+  float lsum = u[0];
+#pragma unroll
+  for (int k = 1; k < kLaneElems; ++k) lsum += u[k];
   g.usum = seg_sum<L>(lsum);
   g.z0 = -(mn * g.inv_s);
   // Without shrink every code lies in [0, qmax], so |z - z0| <= qmax and every
@@ -265,8 +313,6 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
   return g;
 }
 
-__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
-__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // Orders this wave's LDS accesses: lanes hand group state to other lanes of the same
 // wavefront through LDS (the standby pool and the done ring below).

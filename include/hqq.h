@@ -53,7 +53,9 @@ enum {
                               cols not a multiple of group_size, size overflow */
   HQQ_ERR_UNSUPPORTED = 2, /* nbits or group_size outside the supported sets */
   HQQ_ERR_ALIGNMENT = 3,   /* a pointer misses its documented alignment */
-  HQQ_ERR_LAUNCH = 4       /* the HIP runtime refused the launch (e.g. no device) */
+  HQQ_ERR_LAUNCH = 4,      /* the HIP runtime refused the launch (e.g. no device) */
+  HQQ_ERR_TABLE_MISMATCH = 5 /* written by hqq_quantize_batch's kernel to its status word:
+                                the device entry table differs from the validated host one */
 };
 
 /* Optional outputs and switches of hqq_quantize_ex.  Every pointer may be NULL.
@@ -191,19 +193,27 @@ typedef struct {
  * entries_device  device copy of the same `count` entries (8-byte aligned), made by
  *                 the caller; the kernel reads W_f16 and first_group from it, so it
  *                 must hold exactly what `entries` holds and stay unchanged until the
- *                 launch has completed.
+ *                 launch has completed.  The library hashes the validated host table
+ *                 and passes the hash to the kernel by value; every wavefront hashes
+ *                 the device copy before it reads any weight and, if the two differ,
+ *                 writes nothing at all (see status_device).
  * count           >= 0; 0 (or no group at all) is a valid no-op.
  * packed_codes    total_groups * group_size * nbits / 8 bytes, 8-byte aligned; the
  *                 codes of group k start at byte k * group_size * nbits / 8 (the
  *                 LSB-first bitstream of hqq_quantize, matrix after matrix).
  * scale_f16, zero_f16  total_groups binary16 values each, 2-byte aligned.
+ * status_device   one int32 of device memory (4-byte aligned, required when there is
+ *                 a group to quantize).  The launch writes HQQ_OK there when the
+ *                 device table matched, HQQ_ERR_TABLE_MISMATCH when it did not (then
+ *                 no output byte is written).  A call with no group launches nothing
+ *                 and leaves it untouched.  Read it after the stream has completed.
  * Other arguments, conventions and errors as for hqq_quantize; every entry is
  * validated before anything is enqueued.
  */
 int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t* entries_device,
                        int count, int nbits, int group_size, float p, float beta, float kappa,
                        int iters, void* packed_codes, void* scale_f16, void* zero_f16,
-                       void* stream);
+                       int32_t* status_device, void* stream);
 
 /*
  * hqq_dequantize -- the inverse quantizer Q^-1(W_q) = s (W_q - z) of section 2,
@@ -223,8 +233,8 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
  * 128.  Reading: affine min-max round-to-nearest (no solver) over the binary16
  * values, in groups of meta_group consecutive values; per group, with mn and mx its
  * minimum and maximum and d = mx - mn:
- *   code  = clamp(round_half_even(binary32(((v - mn) * 255) / d)), 0, 255)
- *           (the fp64 quotient rounded once to binary32, as for the weight codes),
+ *   code  = the integer nearest the exact ratio (v - mn) * 255 / d, half to even
+ *           (decided exactly, without rounding the ratio first),
  *   scale = binary16(d / 255) (nearest even), offset = mn (+0 for a zero minimum);
  * a constant group has codes 0 and scale 1.  The value is recovered as
  * offset + scale * code (hqq_meta_dequantize).

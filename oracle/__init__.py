@@ -405,6 +405,13 @@ def hqq_residual(W_f16: np.ndarray, packed: np.ndarray, scale_f16: np.ndarray,
     return out
 
 
+def singular_values(dW: np.ndarray) -> np.ndarray:
+    """All singular values of Delta W in decreasing order (fp64, LAPACK as the library
+    step): the exact rank-r truncation of the EoRA page's plain SVD compensation captures
+    the sum of the r largest squares of them."""
+    return np.linalg.svd(np.asarray(dW, np.float64), compute_uv=False)
+
+
 def lowrank_svd(dW: np.ndarray, rank: int):
     """The LoRA factors of the plain SVD compensation (EoRA page, section 1): with
     Delta W = U Sigma V^T (singular values in decreasing order), B = U_r Sigma_r (rows x r)

@@ -59,8 +59,8 @@ def test_size_helpers(lib):
 
 
 def test_status_strings(lib):
-    for st in range(5):
-        assert hq.hqq_status_string(st)
+    for st in range(6):
+        assert hq.hqq_status_string(st) != "unknown status"
     assert hq.hqq_status_string(0) == "ok"
     assert hq.hqq_status_string(99) == "unknown status"
 
@@ -277,7 +277,7 @@ def _entries(shapes, g=64, W=FAKE, first=None):
 
 def _qb(entries, count, **kw):
     a = dict(entries_device=FAKE, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01, iters=20,
-             packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, stream=0)
+             packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, status_device=FAKE, stream=0)
     a.update(kw)
     return hq.hqq_quantize_batch(entries, a.pop("entries_device"), count, **a)
 
@@ -297,6 +297,8 @@ def _qb(entries, count, **kw):
     ([(16, 128)], None, dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
     ([(16, 128)], None, dict(packed_codes=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
     ([(16, 128)], None, dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(status_device=0), hq.HQQ_ERR_INVALID_ARG),
+    ([(16, 128)], None, dict(status_device=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
 ])
 def test_quantize_batch_rejects_before_launch(lib, shapes, first, kw, status):
     assert _qb(_entries(shapes, first=first), len(shapes), **kw) == status
@@ -310,16 +312,16 @@ def test_quantize_batch_entry_checks(lib):
     assert _qb(e, 2) == hq.HQQ_ERR_ALIGNMENT
     assert _qb(e, -1) == hq.HQQ_ERR_INVALID_ARG
     assert hq.hqq_quantize_batch(None, FAKE, 1, 4, 64, 0.7, 1.0, 1.01, 20, FAKE, FAKE, FAKE,
-                                 0) == hq.HQQ_ERR_INVALID_ARG
+                                 FAKE, 0) == hq.HQQ_ERR_INVALID_ARG
     assert ctypes.sizeof(hq.hqq_batch_entry_t) == 32
 
 
 def test_quantize_batch_empty_is_a_no_op(lib):
     assert _qb(_entries([]), 0, entries_device=0, packed_codes=0, scale_f16=0,
-               zero_f16=0) == hq.HQQ_OK
-    # entries without a single group: no launch, outputs may be null
+               zero_f16=0, status_device=0) == hq.HQQ_OK
+    # entries without a single group: no launch, outputs and status word may be null
     assert _qb(_entries([(0, 64), (5, 0)], W=0), 2, packed_codes=0, scale_f16=0,
-               zero_f16=0) == hq.HQQ_OK
+               zero_f16=0, status_device=0) == hq.HQQ_OK
 
 
 def test_meta_groups(lib):

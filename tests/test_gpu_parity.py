@@ -129,10 +129,19 @@ def _c1(device="cuda"):
     return workloads.generate_matrix(workloads.WORKLOADS["single_256x512"], 0, device)
 
 
+# With 8-bit codes the code grid is 16-64 times finer relative to a binary32 ulp than at
+# 2-4 bits, so after the first update (where the device's binary32 iterate u + delta and
+# the oracle's fp64 value are two approximations of the same step) pre-round values fall
+# within that noise of a half-integer correspondingly more often, and a few groups in a
+# thousand take another path.  The floor is 99.5% there; every such group must still be
+# explained by the tie replay.
+BITS8_FLOOR = dict(min_agree=0.995)
+
+
 @pytest.mark.parametrize("nbits,g", [(8, 64), (3, 64), (4, 128), (4, 16), (8, 128), (3, 16)])
 def test_bits_and_group_sizes(hq, nbits, g):
     _say(f"single_256x512 b{nbits} g{g}")
-    _check_full(hq, _c1(), nbits, g)
+    _check_full(hq, _c1(), nbits, g, **(BITS8_FLOOR if nbits == 8 else {}))
 
 
 def test_active_shrink_large_beta(hq):
@@ -234,9 +243,9 @@ def test_exact_ties_round_half_even(hq):
 def test_init_near_ties_below_binary32_resolution(hq):
     """Groups holding a binary16 triple (min, max, w) whose exact initial ratio
     (w - min) qmax / (max - min) lies off a half-integer by less than a binary32 rounding:
-    the oracle takes the exact code, the device's binary32 decision may take the other
-    neighbour.  Every such difference must be one code at a rounding tie, and every group
-    that then leaves the oracle's trajectory must be explained by the tie replay."""
+    its fp32 rounding lands on the half-integer, and the device must still take the exact
+    code (the oracle's).  At T = 0 (the initial quantizer alone) every code must equal the
+    oracle's bit for bit; with the full solver, the usual tolerances apply."""
     from tests.test_oracle_pins import NEAR_TIE_TRIPLES
     rng = np.random.default_rng(12)
     total = {}
@@ -250,9 +259,12 @@ def test_init_near_ties_below_binary32_resolution(hq):
         W = np.stack(rows).reshape(-1, 64)
         _say(f"init near ties b{nbits}: {W.shape[0] * 4} groups of 16")
         Wt = torch.from_numpy(W).cuda()
+        q0 = _run(hq, Wt, nbits, 16, iters=0)
+        ref0 = oracle.hqq_quantize(W, nbits, 16, iters=0)
+        codes0 = oracle.unpack_codes(q0.packed.cpu().numpy(), W.size, nbits).reshape(W.shape)
+        assert np.array_equal(codes0, ref0.codes), "initial codes differ from the exact ones"
         q = _run(hq, Wt, nbits, 16)
-        rep = parity.compare(W.view(np.uint16), parity.from_quantized(q), nbits, 16,
-                             min_agree=0.5, min_code_agree=0.9)
+        rep = parity.compare(W.view(np.uint16), parity.from_quantized(q), nbits, 16, min_agree=0.99)
         total[nbits] = (rep["code_mismatch_total"], rep["divergent"])
         _say(f"  {rep}")
     _say(f"near-tie code mismatches and divergent groups per bit width: {total}")
@@ -345,6 +357,59 @@ def test_batch_equals_per_matrix_calls(hq, nbits, g):
     torch.cuda.synchronize()
     assert b2 is b
     _assert_same_outputs(b.matrix(4), hq.quantize(Ws[4], nbits, g))
+
+
+def test_batch_rejects_a_device_table_that_differs(hq):
+    """The kernel checks its device copy of the entry table against the validated host
+    table before it reads any weight.  With two entries swapped in the copy (every pointer
+    still a valid tensor of the same shape, so an undetected mismatch could not fault) or
+    one pointer replaced by another tensor's, the launch writes nothing and reports
+    HQQ_ERR_TABLE_MISMATCH in its status word; with the right copy it reports HQQ_OK."""
+    import ctypes
+    dist = workloads.WORKLOADS["attn_4096x4096"].dist
+    Ws = [workloads.generate(64, 256, dist, 950 + i, "cuda") for i in range(4)]
+    b = hq.quantize_batch(Ws[:3], 4, 64)
+    b.check()
+    _say("batched launch with a device table that differs from the host table")
+    entries, _ = hq.batch_table(Ws[:3], 64)
+    for wrong in ([Ws[1], Ws[0], Ws[2]], [Ws[0], Ws[1], Ws[3]]):
+        dev_entries, _ = hq.batch_table(wrong, 64)
+        b.table.copy_(torch.frombuffer(bytearray(bytes(dev_entries)), dtype=torch.uint8))
+        b.packed.fill_(0xA5)
+        b.scale.fill_(7.0)
+        b.zero.fill_(-3.0)
+        b.status.fill_(-1)
+        st = hq.hqq_quantize_batch(entries, b.table.data_ptr(), 3, 4, 64, 0.7, 1.0, 1.01, 20,
+                                   b.packed.data_ptr(), b.scale.data_ptr(), b.zero.data_ptr(),
+                                   b.status.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == hq.HQQ_OK  # the host side validated its own table and launched
+        torch.cuda.synchronize()
+        assert int(b.status.item()) == hq.HQQ_ERR_TABLE_MISMATCH
+        assert bool((b.packed == 0xA5).all()) and bool((b.scale == 7.0).all())
+        assert bool((b.zero == -3.0).all())
+        with pytest.raises(hq.HQQError):
+            b.check()
+    b2 = hq.quantize_batch(Ws[:3], 4, 64, out=b)
+    b2.check()
+    assert ctypes.sizeof(hq.hqq_batch_entry_t) == 32
+    for i, W in enumerate(Ws[:3]):
+        _assert_same_outputs(b2.matrix(i), hq.quantize(W, 4, 64))
+
+
+def test_batch_out_must_match(hq):
+    """An arena passed as out is reused only for the shapes and settings it was made for."""
+    dist = workloads.WORKLOADS["attn_4096x4096"].dist
+    Ws = [workloads.generate(64, 256, dist, 960 + i, "cuda") for i in range(3)]
+    b = hq.quantize_batch(Ws[:2], 4, 64)
+    other = [Ws[0], workloads.generate(64, 128, dist, 963, "cuda")]
+    for args in ((Ws, 4, 64), (Ws[:2], 2, 64), (Ws[:2], 4, 32), (other, 4, 64)):
+        with pytest.raises(ValueError):
+            hq.quantize_batch(*args, out=b)
+    q = hq.quantize(Ws[0], 4, 64)
+    with pytest.raises(ValueError):
+        hq.quantize(Ws[0][:32].contiguous(), 4, 64, out=q)
+    with pytest.raises(ValueError):
+        hq.dequantize(q, out=torch.empty((64, 128), dtype=torch.float16, device="cuda"))
 
 
 @pytest.mark.parametrize("nbits,g", [(2, 32), (4, 64)])

@@ -50,8 +50,8 @@ def test_residual_is_zero_on_grid_and_matches_the_dequantizer():
                                                       nbits, g))
         half_ulp = np.spacing(np.abs(deq).astype(np.float16)).astype(np.float64) / 2
         assert np.all(np.abs(dW - (W.astype(np.float64) - deq)) <= half_ulp + 1e-300)
-        # |Delta W| <= s/2 on the solver's fp64 grid (plus the binary32 decision band) where
-        # the code is not clamped, plus what the binary16 storage of s and z moves
+        # |Delta W| <= s/2 on the solver's fp64 grid (plus fp64 rounding) where the code is
+        # not clamped, plus what the binary16 storage of s and z moves
         q = r.codes.astype(np.float64)
         s64 = np.repeat(r.scale, g, axis=1)
         z64 = np.repeat(r.zero, g, axis=1)
@@ -60,6 +60,14 @@ def test_residual_is_zero_on_grid_and_matches_the_dequantizer():
         storage = np.abs(s16 * (q - z16) - s64 * (q - z64))
         inner = (r.codes > 0) & (r.codes < (1 << nbits) - 1)
         assert np.all(np.abs(dW[inner]) <= (s64 * (0.5 + 1e-6) + storage * (1 + 1e-9))[inner])
+
+
+def test_singular_values_are_the_planted_ones():
+    sig = [7.0, 3.0, 2.0, 0.5]
+    U, S, V = _planted(50, 30, sig, seed=3)
+    s = oracle.singular_values((U * S) @ V.T)
+    assert s.shape == (30,)
+    assert np.allclose(s[:4], sig, rtol=1e-12) and np.all(np.abs(s[4:]) <= 1e-12)
 
 
 @pytest.mark.parametrize("m,n", [(60, 40), (40, 70)])
