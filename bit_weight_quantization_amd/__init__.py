@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hq
                     "hqq_residual", "hqq_lowrank", "hqq_lowrank_workspace_bytes",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
-                    "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string")
+                    "hqq_packed_bytes", "hqq_num_groups", "hqq_status_string",
+                    "hqq_quantize_tensor_stop_noalloc", "hqq_tensor_stop_noalloc_max_bytes")
 
 
 class HQQError(RuntimeError):
@@ -74,6 +75,11 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_quantize_tensor_stop.restype = I
     lib.hqq_quantize_tensor_stop.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
                                              ctypes.POINTER(hqq_options_t), P, P, P, P]
+    lib.hqq_quantize_tensor_stop_noalloc.restype = I
+    lib.hqq_quantize_tensor_stop_noalloc.argtypes = [P, I64, I64, I, I, F, F, F, I, P, P, P,
+                                                     ctypes.POINTER(hqq_options_t), P, P, P]
+    lib.hqq_tensor_stop_noalloc_max_bytes.restype = I64
+    lib.hqq_tensor_stop_noalloc_max_bytes.argtypes = []
     lib.hqq_residual.restype = I
     lib.hqq_residual.argtypes = [P, P, P, P, I64, I64, I, I, P, P, P]
     lib.hqq_lowrank.restype = I
@@ -148,6 +154,21 @@ def hqq_quantize_tensor_stop(W_f16: int, rows: int, cols: int, nbits: int, group
     return load_library().hqq_quantize_tensor_stop(W_f16, rows, cols, nbits, group_size, p, beta,
                                                    kappa, iters, packed_codes, scale_f16, zero_f16,
                                                    opt, totals_f64, t_star_i32, workspace, stream)
+
+
+def hqq_quantize_tensor_stop_noalloc(W_f16: int, rows: int, cols: int, nbits: int,
+                                     group_size: int, p: float, beta: float, kappa: float,
+                                     iters: int, packed_codes: int, scale_f16: int,
+                                     zero_f16: int, options: Optional[hqq_options_t],
+                                     totals_f64: int, t_star_i32: int, stream: int = 0) -> int:
+    opt = ctypes.byref(options) if options is not None else None
+    return load_library().hqq_quantize_tensor_stop_noalloc(
+        W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters, packed_codes, scale_f16,
+        zero_f16, opt, totals_f64, t_star_i32, stream)
+
+
+def hqq_tensor_stop_noalloc_max_bytes() -> int:
+    return load_library().hqq_tensor_stop_noalloc_max_bytes()
 
 
 def hqq_matmul(X_f16: int, M: int, K: int, packed_codes: int, scale_f16: int, zero_f16: int,

@@ -1,10 +1,13 @@
 // hqq_api.hip -- extern "C" entry points of the HQQ quantizer (see include/hqq.h):
 // argument validation, grid sizing and the launch on the caller's stream.
-// No allocation, no synchronization, no global mutable state.
+// No allocation, no synchronization.  The only global state is the device-resident
+// scratch of hqq_quantize_tensor_stop_noalloc and its per-device address, looked up once.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/hqq.h"
 #include "hqq_internal.h"
@@ -219,6 +222,71 @@ int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int 
   hipError_t err = hqq::launch_tensor_stop(prm, X, group_size, power_mode_of(p), cus,
                                            static_cast<hipStream_t>(stream));
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---- hqq_quantize_tensor_stop_noalloc: the tensor stop's scratch as a static device array --
+//
+// The whole-tensor stop needs per-block partial totals and the totals themselves between
+// its kernels (hqq_tensor_stop_workspace_bytes(iters) bytes, 4 MiB at iters = 255).  For
+// callers that cannot allocate, that scratch is a file-scope device array, one copy per
+// GPU, sized for the largest iters.  In host code the array's name is only a stand-in,
+// so its device address is looked up once per device with hipGetSymbolAddress (on the
+// first call on that device, with that device current) and every launch uses that
+// address.  Calls on one GPU share the array: calls that may overlap on one GPU race.
+// Every byte the kernels read is written earlier in the same call, so nothing has to be
+// cleared between calls.
+namespace {
+
+constexpr int64_t kNoallocScratchBytes = (int64_t)hqq::kTensorStopHeader +
+                                         (int64_t)sizeof(double) * (kMaxIters + 1) *
+                                             hqq::kTensorStopMaxBlocks;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+// The calling thread's current device's copy of `scratch` (null if the lookup failed).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(scratch_once[dev], [dev]() {
+    void* ptr = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hqq_tensor_stop_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int hqq_quantize_tensor_stop_noalloc(const void* W_f16, int64_t rows, int64_t cols, int nbits,
+                                     int group_size, float p, float beta, float kappa, int iters,
+                                     void* packed_codes, void* scale_f16, void* zero_f16,
+                                     const hqq_options_t* opt, void* totals_f64, void* t_star_i32,
+                                     void* stream) {
+  int64_t n = 0;
+  int st = validate_single(W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters,
+                           packed_codes, scale_f16, zero_f16, n);
+  if (st != HQQ_OK || n == 0) return st;
+  hqq_options_t o;  // everything hqq_quantize_tensor_stop checks, before the scratch is touched
+  st = read_options(opt, o);
+  if (st != HQQ_OK) return st;
+  if ((totals_f64 && !aligned(totals_f64, 8)) || (t_star_i32 && !aligned(t_star_i32, 4)))
+    return HQQ_ERR_ALIGNMENT;
+  if (hqq::tensor_stop_workspace_bytes(iters) > kNoallocScratchBytes) return HQQ_ERR_INVALID_ARG;
+  void* ws = scratch_of_current_device();
+  if (!ws) return HQQ_ERR_LAUNCH;
+  return hqq_quantize_tensor_stop(W_f16, rows, cols, nbits, group_size, p, beta, kappa, iters,
+                                  packed_codes, scale_f16, zero_f16, opt, totals_f64, t_star_i32,
+                                  ws, stream);
 }
 
 int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t* entries_device,

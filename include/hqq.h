@@ -168,6 +168,30 @@ int hqq_quantize_tensor_stop(const void* W_f16, int64_t rows, int64_t cols, int 
  * (iters + 1)); -1 for iters outside 0 .. 255. */
 int64_t hqq_tensor_stop_workspace_bytes(int iters);
 
+/*
+ * hqq_quantize_tensor_stop_noalloc -- hqq_quantize_tensor_stop without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The scratch the
+ * whole-tensor stop needs between its kernels lives in a device array inside the library
+ * (hqq_tensor_stop_noalloc_max_bytes() bytes, enough for every iters up to 255; one copy
+ * per GPU, held until the process ends); the first call on a device looks up that
+ * device's copy.  The call allocates, frees and synchronizes nothing.  Calls on one GPU
+ * share the array, so calls that may run at the same time on one GPU (other streams,
+ * other threads) race and must be serialized by the caller; each call writes every
+ * scratch byte it reads, so no clearing is needed between calls.  Arguments, results and
+ * errors as for hqq_quantize_tensor_stop (bit-identical outputs); HQQ_ERR_INVALID_ARG if
+ * the scratch would exceed the array, HQQ_ERR_LAUNCH if the array's address cannot be
+ * obtained.
+ */
+int hqq_quantize_tensor_stop_noalloc(const void* W_f16, int64_t rows, int64_t cols, int nbits,
+                                     int group_size, float p, float beta, float kappa, int iters,
+                                     void* packed_codes, void* scale_f16, void* zero_f16,
+                                     const hqq_options_t* opt, void* totals_f64, void* t_star_i32,
+                                     void* stream);
+
+/* Size of the device array behind hqq_quantize_tensor_stop_noalloc, in bytes. */
+int64_t hqq_tensor_stop_noalloc_max_bytes(void);
+
 /* One input matrix of hqq_quantize_batch (32 bytes; the same layout is read on
  * the host and on the device). */
 typedef struct {

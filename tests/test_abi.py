@@ -253,6 +253,31 @@ def test_tensor_stop_options_and_empty(lib):
                t_star_i32=0, workspace=0) == hq.HQQ_OK
 
 
+def _ts_noalloc(**kw):
+    a = dict(W_f16=FAKE, rows=16, cols=128, nbits=4, group_size=64, p=0.7, beta=1.0, kappa=1.01,
+             iters=20, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, options=None,
+             totals_f64=0, t_star_i32=0, stream=0)
+    a.update(kw)
+    return hq.hqq_quantize_tensor_stop_noalloc(**a)
+
+
+def test_tensor_stop_noalloc_size_and_rejections(lib):
+    """The static scratch holds the workspace of every iters up to 255 (2 KiB of totals and
+    fp64 partial totals of up to 2048 blocks per step); arguments are validated as for
+    hqq_quantize_tensor_stop before the scratch is touched.  Only rejected calls here: a
+    call that passed validation would launch."""
+    assert hq.hqq_tensor_stop_noalloc_max_bytes() == 256 * 8 + 8 * 256 * 2048
+    assert hq.hqq_tensor_stop_noalloc_max_bytes() >= hq.hqq_tensor_stop_workspace_bytes(255)
+    assert _ts_noalloc(iters=256) == hq.HQQ_ERR_INVALID_ARG
+    assert _ts_noalloc(nbits=5) == hq.HQQ_ERR_UNSUPPORTED
+    assert _ts_noalloc(cols=100) == hq.HQQ_ERR_INVALID_ARG
+    assert _ts_noalloc(W_f16=FAKE + 2) == hq.HQQ_ERR_ALIGNMENT
+    assert _ts_noalloc(packed_codes=0) == hq.HQQ_ERR_INVALID_ARG
+    assert _ts_noalloc(options=hq.hqq_options_t(1, 0, 0, 0, 0, 0, 0, 3)) == hq.HQQ_ERR_INVALID_ARG
+    assert _ts_noalloc(totals_f64=FAKE + 4) == hq.HQQ_ERR_ALIGNMENT
+    assert _ts_noalloc(rows=0, W_f16=0, packed_codes=0, scale_f16=0, zero_f16=0) == hq.HQQ_OK
+
+
 @pytest.mark.parametrize("args,status", [
     ((FAKE, FAKE, FAKE, 16, 128, 6, 64, FAKE), hq.HQQ_ERR_UNSUPPORTED),
     ((FAKE, FAKE, FAKE, 16, 100, 4, 64, FAKE), hq.HQQ_ERR_INVALID_ARG),
