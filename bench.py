@@ -36,24 +36,29 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "hqq_solve_llama70b_pmc.json")
 KERNEL_SRC = [os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", f)
               for f in ("hqq_solver.h", "hqq_kernels.hip", "hqq_internal.h")]
 
-# MI355X: 256 CUs x 4 SIMDs x 16 fp32 lanes per clock x 2.4 GHz.  Packed-fp32 issue is
-# not used, so this is the VALU ceiling for the solver; v_log_f32 / v_exp_f32 issue at
-# half rate and are counted as 2 lane-ops each (measured on the device).
-PEAK_VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# MI355X fp32 vector peak: 157.3 TFLOP/s counts an FMA as two flops, i.e. 78.6 T full-rate
+# lane-operations per second = 256 CUs x 4 SIMDs x 32 lanes per clock x 2.4 GHz (one wave64
+# instruction per SIMD every 2 clocks).  Packed fp32 is not used: the probe
+# (libhqq_valu_probe.so) shows plain v_add/v_mul/v_fma_f32 issuing at about that rate
+# already.  Half-rate instructions (v_rndne_f32, v_med3_f32) take 2 of those issue slots,
+# quarter-rate ones (v_exp_f32, v_log_f32) 4; the probe measures all classes.
+PEAK_VALU_SLOTS = 256 * 4 * 32 * 2.4e9
 PEAK_HBM = 8.0e12
 
-# Algorithmic VALU lane-ops per weight (general 0 < p < 1), the builder's count:
-#   init   4: fp16->fp32, min, max, w/s + z
-#   eval  10: x = w/s + z, round, clamp, residual, log2 (2), *p, exp2 (2), error sum
+# Algorithmic VALU issue slots per weight (general 0 < p < 1), by the rate classes above:
+#   init   4: fp16->fp32, min, max, w/s + z                                   (full rate)
+#   eval  16: x = w/s + z 1, round 2, clamp 2, residual 1, log2 4, *p 1, exp2 4, error sum 1
 #   update 1: code sum for the z mean (no shrink: every |r| is below its threshold)
-#   final  4: x, round, clamp, pack
-OPS_INIT, OPS_EVAL, OPS_UPDATE, OPS_FINAL = 4, 10, 1, 4
+#   final  6: x 1, round 2, clamp 2, pack 1
+OPS_INIT, OPS_EVAL, OPS_UPDATE, OPS_FINAL = 4, 16, 1, 6
 # The planning op model the roofline is also reported against: per weight
 #   3 + n_eval (8 + 2 tau) + n_upd 6
 # (init min/max and pack 3; per evaluation 7 full-rate ops, one amortized reduction and
 # two transcendentals of tau issue slots each; per update 6 full-rate ops, the shrink
-# included), with tau the measured cost of v_exp_f32 / v_log_f32 relative to v_add_f32.
+# included), with tau the measured cost of v_exp_f32 / v_log_f32 in full-rate slots
+# (cycles per wave64 instruction over the 2 of a full-rate one).
 PLAN_BASE, PLAN_EVAL_FULL, PLAN_EVAL_TRANS, PLAN_UPDATE = 3, 8, 2, 6
+FULL_RATE_CYCLES = 2.0
 
 PROBE_LIB = os.path.join(ROOT, "bit_weight_quantization_amd", "libhqq_valu_probe.so")
 CLOCK_HZ = 2.4e9   # MI355X peak engine clock
@@ -137,6 +142,16 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
                 "active_lane_fraction": c.get("SQ_THREAD_CYCLES_VALU", 0) / max(
                     64 * c.get("SQ_ACTIVE_INST_VALU", 1), 1),
                 "waves": c.get("SQ_WAVES")}
+    # engine clock during each solver launch: GRBM_GUI_ACTIVE (busy cycles, counted on
+    # each of the 8 XCDs) over the dispatch's own duration
+    clk_csv = os.path.join(pmc_dir, "clk", "run_counter_collection.csv")
+    if os.path.exists(clk_csv):
+        for r in csv.DictReader(open(clk_csv)):
+            k = _kernel_key(r["Kernel_Name"])
+            if k and k.startswith("hqq_solve") and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                extra.setdefault(k, {})["clock_GHz"] = round(
+                    float(r["Counter_Value"]) / 8 / dur / 1e9, 3)
     stats = {}
     kt_csv = os.path.join(kt_dir, "kt_kernel_stats.csv")
     for r in csv.DictReader(open(kt_csv)):
@@ -173,6 +188,9 @@ def summarize_profiles(pmc_dir: str, kt_dir: str, out_dir: str, command: str, la
         lines.append(f"| {k}: VALU wave-instr / trans / active lanes | "
                      f"{v['valu_wave_instr_per_launch']:.4g} / {v['trans_wave_instr_per_launch']:.4g}"
                      f" / {v['active_lane_fraction']:.3f} |")
+        if "clock_GHz" in v:
+            lines.append(f"| {k}: engine clock during the launch (GRBM_GUI_ACTIVE / 8 XCDs / "
+                         f"duration) | {v['clock_GHz']:.3f} GHz |")
     lines += ["", "Command:", "", "```", command, "```", ""]
     with open(os.path.join(out_dir, "hqq_solve_llama70b.md"), "w") as f:
         f.write("\n".join(lines))
@@ -183,8 +201,9 @@ def measure_peaks(torch, dev, stream, trips=2048, reps=5):
     """Issue rates of the VALU instruction classes the solver uses, from the probe library
     (libhqq_valu_probe.so): 8 wavefronts per SIMD, each thread running 8 independent
     chains of one instruction, HIP events around `reps` launches on the bench stream.
-    Reports SIMD cycles per wave64 instruction at the nominal 2.4 GHz clock and the ratio
-    to v_add_f32 (clock-independent); tau = the mean ratio of v_exp_f32 and v_log_f32."""
+    Reports SIMD cycles per wave64 instruction at the nominal 2.4 GHz clock, the ratio to
+    v_add_f32 (clock-independent) and the cost in full-rate issue slots (2 cycles); tau =
+    the mean slot cost of v_exp_f32 and v_log_f32."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     lib.hqq_probe_valu.restype = ctypes.c_int
@@ -215,9 +234,10 @@ def measure_peaks(torch, dev, stream, trips=2048, reps=5):
     base = res["v_add_f32"]["cycles_per_wave_instr"]
     for v in res.values():
         v["rel_to_add"] = round(v["cycles_per_wave_instr"] / base, 3)
-    tau = (res["v_exp_f32"]["rel_to_add"] + res["v_log_f32"]["rel_to_add"]) / 2
+        v["slots"] = round(v["cycles_per_wave_instr"] / FULL_RATE_CYCLES, 3)
+    tau = (res["v_exp_f32"]["slots"] + res["v_log_f32"]["slots"]) / 2
     return {"probe": "libhqq_valu_probe.so", "waves_per_simd": 8, "trips": trips,
-            "instr": res, "tau": round(tau, 3)}
+            "full_rate_cycles": FULL_RATE_CYCLES, "instr": res, "tau": round(tau, 3)}
 
 
 def stop_hist_ops(hist, g, iters, tau):
@@ -331,8 +351,8 @@ def measure_configs(hq, lib, torch, dev, stream, sh, tau, warmup=3, runs=10):
                         "hbm_GBs_algorithmic": round(n * (2 + nb / 8 + 4 / g) / (ms * 1e-3) / 1e9, 1),
                         "mean_evals_per_group": round(mean_eval, 4),
                         "stop_step_hist": [int(x) for x in hist[:solver.iters + 1]],
-                        "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
-                        "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4)})
+                        "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_SLOTS, 4),
+                        "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_SLOTS, 4)})
                     log(f"config {cid} {entry['settings'][-1]}")
                     del out, q
                 del W
@@ -381,8 +401,8 @@ def measure_configs(hq, lib, torch, dev, stream, sh, tau, warmup=3, runs=10):
                     "hbm_GBs_algorithmic": round(n_w * (2 + nb / 8 + 4 / g) / (ms * 1e-3) / 1e9, 1),
                     "mean_evals_per_group": round(mean_eval, 4),
                     "stop_step_hist": [int(x) for x in hist[:solver.iters + 1]],
-                    "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
-                    "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4)})
+                    "valu_frac": round(b_ops / (ms * 1e-3) / PEAK_VALU_SLOTS, 4),
+                    "valu_frac_plan_model": round(p_ops / (ms * 1e-3) / PEAK_VALU_SLOTS, 4)})
                 log(f"config {cid} {entry['settings'][-1]}")
                 del b, stop
             # a few rows of one matrix of each shape for the oracle's extrapolated time
@@ -585,7 +605,7 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
             frac_key = "nominal_valu_frac" if v.get("tensor") else "valu_frac"
             row = {"variant": name, "ms": round(ms, 3),
                    "G_weights_per_s": round(n_w / (ms * 1e-3) / 1e9, 1),
-                   frac_key: round(ops / (ms * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+                   frac_key: round(ops / (ms * 1e-3) / PEAK_VALU_SLOTS, 4),
                    **extra, "quality": quality(outs)}
             if name == "per_group_lp":
                 row["quality_meta8"] = quality(outs, meta=True)
@@ -962,13 +982,15 @@ def main():
                  "256 CUs x 8 blocks of 4 wavefronts (8 wavefronts per SIMD); every thread runs "
                  f"{peaks['trips']} trips of 64 instructions in 8 independent chains; HIP events "
                  "around 5 launches per instruction. Cycles at the nominal 2.4 GHz clock; the "
-                 "ratio to v_add_f32 does not depend on the clock.", "",
-                 "| instruction | ms per launch | SIMD cycles per wave64 instruction | relative to v_add_f32 |",
-                 "|---|---|---|---|"]
+                 "ratio to v_add_f32 does not depend on the clock. Slots: cycles over the 2 "
+                 "cycles of a full-rate wave64 instruction (the 157.3 TFLOP/s fp32 vector peak "
+                 "= 78.6 T full-rate lane-operations per second).", "",
+                 "| instruction | ms per launch | SIMD cycles per wave64 instruction | relative to v_add_f32 | full-rate slots |",
+                 "|---|---|---|---|---|"]
         for name, v in peaks["instr"].items():
             lines.append(f"| {name} | {v['ms']:.4f} | {v['cycles_per_wave_instr']:.3f} | "
-                         f"{v['rel_to_add']:.3f} |")
-        lines += ["", f"tau (mean of v_exp_f32 and v_log_f32 relative to v_add_f32) = {peaks['tau']}",
+                         f"{v['rel_to_add']:.3f} | {v['slots']:.3f} |")
+        lines += ["", f"tau (mean slot cost of v_exp_f32 and v_log_f32) = {peaks['tau']}",
                   "", "Command:", "", "```", args.profile_command or "python bench.py --peak-probe OUT_MD",
                   "```", ""]
         with open(args.peak_probe, "w") as f:
@@ -1166,8 +1188,8 @@ def main():
             "mean_evals_per_group": round(mean_eval, 4),
             "stop_step_hist": [int(x) for x in hist[si][: solver.iters + 1]],
             "valu_TOPs": round(ops / (per_setting_ms[si] * 1e-3) / 1e12, 2),
-            "valu_frac": round(ops / (per_setting_ms[si] * 1e-3) / PEAK_VALU_LANE_OPS, 4),
-            "valu_frac_plan_model": round(plan / (per_setting_ms[si] * 1e-3) / PEAK_VALU_LANE_OPS, 4),
+            "valu_frac": round(ops / (per_setting_ms[si] * 1e-3) / PEAK_VALU_SLOTS, 4),
+            "valu_frac_plan_model": round(plan / (per_setting_ms[si] * 1e-3) / PEAK_VALU_SLOTS, 4),
             "hbm_GBs_algorithmic": round(bytes_alg / (per_setting_ms[si] * 1e-3) / 1e9, 1),
         })
     avg_launch_s = total_ms * 1e-3 / (args.steps * launches_per_step)
@@ -1330,20 +1352,25 @@ def main():
         },
         "roofline": {
             "bound": "alu",
-            "achieved": round(achieved / 1e12, 3),
-            "peak": round(PEAK_VALU_LANE_OPS / 1e12, 3),
+            "achieved": round(achieved_plan / 1e12, 3),
+            "peak": round(PEAK_VALU_SLOTS / 1e12, 3),
             "unit": "TOP/s",
-            "frac": round(achieved / PEAK_VALU_LANE_OPS, 4),
+            "frac": round(achieved_plan / PEAK_VALU_SLOTS, 4),
+            "ops_model": "planning model 3 + n_eval (8 + 2 tau) + n_upd 6 slots per weight, "
+                         "tau measured, against 157.3 TFLOP/s fp32 vector = 78.6 T full-rate "
+                         "lane-op slots/s",
             "traffic": traffic,
             "kernel": "hqq_solve_kernel<32|64, general p>",
-            "ops_per_launch": round(ops_step / launches_per_step),
+            "tau": tau,
+            "ops_per_launch": round(plan_step / launches_per_step),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "hbm_frac_algorithmic": round(bytes_step / (ms_per_step * 1e-3) / PEAK_HBM, 4),
-            "plan_model": {
-                "ops_per_weight": "3 + n_eval (8 + 2 tau) + n_upd 6",
-                "tau": tau, "ops_per_launch": round(plan_step / launches_per_step),
-                "achieved": round(achieved_plan / 1e12, 3),
-                "frac": round(achieved_plan / PEAK_VALU_LANE_OPS, 4)},
+            "class_weighted_count": {
+                "ops_per_weight": "4 + 16 n_eval + n_upd + 6 slots (rate classes: full 1, "
+                                  "round/clamp 2, log2/exp2 4)",
+                "ops_per_launch": round(ops_step / launches_per_step),
+                "achieved": round(achieved / 1e12, 3),
+                "frac": round(achieved / PEAK_VALU_SLOTS, 4)},
             "peaks_measured": peaks,
         },
         "per_setting": detail,

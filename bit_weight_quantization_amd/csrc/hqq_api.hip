@@ -369,8 +369,8 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
   prm.scale16 = static_cast<const uint16_t*>(scale_f16);
   prm.zero16 = static_cast<const uint16_t*>(zero_f16);
   prm.out = static_cast<uint4*>(W_out_f16);
-  prm.nchunks = n / hqq::kLaneElems;
-  prm.chunks_per_group = group_size / hqq::kLaneElems;
+  prm.nchunks = n / hqq::kDequantElems;
+  prm.chunks_per_group = group_size / hqq::kDequantElems;
   prm.nbits = nbits;
   int cus = compute_units();
   if (cus <= 0) return HQQ_ERR_LAUNCH;

@@ -14,7 +14,7 @@ enum ErrMetric : int { kErrP = 0, kErrL1 = 1, kErrL2 = 2 };
 
 // Device view of one hqq_batch_entry_t (same 32-byte layout).
 struct BatchEntry {
-  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8
+  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8 halves
   int64_t rows, cols;
   int64_t first_group;     // global index of the matrix's first group
 };
@@ -40,7 +40,7 @@ __host__ __device__ inline uint64_t table_entry_hash(uint64_t w, int64_t rows, i
 }
 
 struct SolveParams {
-  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8 (single matrix)
+  const uint4* W;          // fp16 weights viewed as 16-byte chunks of 8 halves (single matrix)
   const BatchEntry* batch; // device entry table (batched launch), else null
   int batch_count;
   uint64_t batch_hash;     // hash of the validated host table (batched launch)
@@ -77,8 +77,8 @@ struct DequantParams {
   const uint16_t* scale16;
   const uint16_t* zero16;
   uint4* out;              // fp16 output as 16-byte chunks of 8
-  int64_t nchunks;         // elements / 8
-  int chunks_per_group;    // group_size / 8
+  int64_t nchunks;         // elements / kDequantElems
+  int chunks_per_group;    // group_size / kDequantElems
   int nbits;
 };
 
@@ -101,8 +101,10 @@ hipError_t launch_meta_dequantize(const uint8_t* codes, const uint16_t* mscale,
                                   const uint16_t* moffset, int64_t n, int64_t M, uint16_t* out,
                                   int cus, hipStream_t stream);
 
-// Segment geometry shared with the host grid sizing: each lane holds 8 weights.
-constexpr int kLaneElems = 8;
+// Segment geometry shared with the host grid sizing: each solver lane holds 16 weights
+// (two consecutive 16-byte chunks); the dequantization kernel handles 8 per lane.
+constexpr int kLaneElems = 16;
+constexpr int kDequantElems = 8;
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 

@@ -8,12 +8,15 @@
 // computed with 1/s; section 4.1 the early exit once the error stops improving.
 //
 // Solver kernel layout (one fused pass: load, init, iterate, pack, store):
-//   * every lane holds 8 consecutive fp16 weights (one 16-byte load, fully
-//     coalesced inside a wavefront); group min/max run on the binary16 pairs;
-//   * a group of G weights lives in a segment of L = G/8 adjacent lanes; a
-//     wavefront holds S = 64/L groups; group sums/min/max are DPP butterflies
-//     inside the segment (quad_perm, row_half_mirror, row_mirror), so every
-//     lane of a segment ends with the bit-identical total;
+//   * every lane holds 16 consecutive fp16 weights (two 16-byte loads; a
+//     wavefront reads 2 KB contiguous); group min/max run on the binary16 pairs.
+//     The per-lane control of the solver (ballots, scalar state, group sums) is
+//     spread over 16 weights;
+//   * a group of G weights lives in a segment of L = G/16 adjacent lanes; a
+//     wavefront holds S = 64/L groups; a lane sums its 16 terms as a binary
+//     tree, and group sums/min/max are DPP butterflies inside the segment
+//     (quad_perm, row_half_mirror), so every lane of a segment ends with the
+//     bit-identical total;
 //   * the iteration runs in "code units".  At load each weight becomes
 //     u = (w - min) * qmax / (max - min) = w/s + z_0, rounded once to fp32 (an
 //     FMA of the exact product with a double-float qmax/(max - min)), so an exact
@@ -60,13 +63,14 @@ namespace {
 template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
-  // Wavefronts per SIMD the kernel is compiled for (VGPR budget): seven at G = 32,
-  // where the extra wavefront outweighs the smaller pool, six otherwise (measured).
-  static constexpr int kWavesPerSimd = G == 32 ? 7 : 6;
+  // Wavefronts per SIMD the kernel is compiled for (the VGPR budget).  A wavefront
+  // holds 1024 weights, so its LDS share is S(2G + 20) words, 35 KB (G = 128) to 53 KB
+  // (G = 16) per block of four wavefronts: three blocks per CU fit in its 160 KB at
+  // G = 16 and 32, four at G = 64 and 128 (measured: the fourth wavefront per SIMD is
+  // worth more than a deeper pool).
+  static constexpr int kWavesPerSimd = G <= 32 ? 3 : 4;
   // A prime batch adds up to S groups to the pool, a hand-over up to S to the ring.
-  // The pool holds 1.5 S groups, so it is restocked before it runs dry, where the LDS
-  // of kWavesPerSimd wavefronts allows (G = 64, 128); S otherwise.
-  static constexpr int kStandby = (G == 16 || G == 32) ? S : S + S / 2;
+  static constexpr int kStandby = S;
   static constexpr int kDone = S;
   float u[kWavesPerBlock][kStandby + kDone][G];
   uint4 standby_hdr[kWavesPerBlock][kStandby][3];
@@ -76,16 +80,19 @@ struct SolveLds {
 template <int G>
 __device__ __forceinline__ void store_u(float* slot_u, int sl, const float (&u)[kLaneElems]) {
   float4* dst = reinterpret_cast<float4*>(slot_u + sl * kLaneElems);
-  dst[0] = make_float4(u[0], u[1], u[2], u[3]);
-  dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+#pragma unroll
+  for (int i = 0; i < kLaneElems / 4; ++i)
+    dst[i] = make_float4(u[4 * i], u[4 * i + 1], u[4 * i + 2], u[4 * i + 3]);
 }
 
 template <int G>
 __device__ __forceinline__ void load_u(const float* slot_u, int sl, float (&u)[kLaneElems]) {
   const float4* src = reinterpret_cast<const float4*>(slot_u + sl * kLaneElems);
-  const float4 a = src[0], b = src[1];
-  u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
-  u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
+#pragma unroll
+  for (int i = 0; i < kLaneElems / 4; ++i) {
+    const float4 a = src[i];
+    u[4 * i] = a.x; u[4 * i + 1] = a.y; u[4 * i + 2] = a.z; u[4 * i + 3] = a.w;
+  }
 }
 
 // Every group takes at least two evaluations (t = 0 is always accepted), so a wave
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
   // latency overlaps the work in between.
   BatchCursor cursor = {0, 0, P.ngroups, P.W};
   if constexpr (BATCH) cursor = batch_cursor(P, next);
-  uint4 prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
+  LaneW prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
 
   // Dense batch: segment j initializes group next + j and runs its first two steps.
   auto prime = [&]() {
@@ -317,18 +324,18 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
     const float s = (float)__builtin_bit_cast(_Float16, P.scale16[g]);
     const float z = (float)__builtin_bit_cast(_Float16, P.zero16[g]);
     const float sz = s * z;
-    uint32_t c[kLaneElems];
+    uint32_t c[kDequantElems];
     switch (P.nbits) {
       case 4: {
         const uint32_t v = reinterpret_cast<const uint32_t*>(P.packed)[chunk];
 #pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) c[k] = (v >> (4 * k)) & 15u;
+        for (int k = 0; k < kDequantElems; ++k) c[k] = (v >> (4 * k)) & 15u;
         break;
       }
       case 2: {
         const uint32_t v = reinterpret_cast<const uint16_t*>(P.packed)[chunk];
 #pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) c[k] = (v >> (2 * k)) & 3u;
+        for (int k = 0; k < kDequantElems; ++k) c[k] = (v >> (2 * k)) & 3u;
         break;
       }
       case 8: {
@@ -344,13 +351,13 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
         const uint8_t* src = P.packed + chunk * 3;
         const uint32_t v = (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16);
 #pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) c[k] = (v >> (3 * k)) & 7u;
+        for (int k = 0; k < kDequantElems; ++k) c[k] = (v >> (3 * k)) & 7u;
         break;
       }
     }
-    uint16_t h[kLaneElems];
+    uint16_t h[kDequantElems];
 #pragma unroll
-    for (int k = 0; k < kLaneElems; ++k) h[k] = dequant_one(s, sz, c[k]);
+    for (int k = 0; k < kDequantElems; ++k) h[k] = dequant_one(s, sz, c[k]);
     uint4 o;
     o.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
     o.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);

@@ -45,6 +45,14 @@ __device__ __forceinline__ float seg_sum(float v) {
   return v;
 }
 
+// Sum of v[K0 .. K0 + N) as a balanced binary tree (N a power of two): fp32 rounding
+// error grows with the tree's depth, log2 N, not with N.
+template <int K0, int N>
+__device__ __forceinline__ float tree_sum(const float (&v)[kLaneElems]) {
+  if constexpr (N == 1) return v[K0];
+  else return tree_sum<K0, N / 2>(v) + tree_sum<K0 + N / 2, N / 2>(v);
+}
+
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }   // v_log_f32
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32
 
@@ -209,38 +217,47 @@ __device__ __forceinline__ void batch_advance(const SolveParams& P, BatchCursor&
   }
 }
 
-// The lane's 16-byte chunk of group `gi`.  Past the end of the wave's queue the
-// lane reads the queue's last group instead (a valid address; the value is unused),
-// so the load is unconditional and its registers need no other initialisation.  In a
-// batched launch a prime batch never extends past the cursor's entry, so the chunk
-// comes from that entry (past its end or the queue's, the lane reads the entry's
-// first group, a valid address whose value is unused).
+// The lane's 16 binary16 weights: two consecutive 16-byte chunks.
+struct LaneW {
+  uint4 lo, hi;
+};
+
+// The lane's 32 bytes of group `gi`.  Past the end of the wave's queue the lane reads
+// the queue's last group instead (a valid address; the value is unused), so the loads
+// are unconditional and their registers need no other initialisation.  In a batched
+// launch a prime batch never extends past the cursor's entry, so the weights come from
+// that entry (past its end or the queue's, the lane reads the entry's first group, a
+// valid address whose value is unused).
 template <int L, bool BATCH>
-__device__ __forceinline__ uint4 fetch_chunk(const SolveParams& P, const BatchCursor& c,
+__device__ __forceinline__ LaneW fetch_chunk(const SolveParams& P, const BatchCursor& c,
                                              int64_t gi, int64_t g_end, int sl) {
+  const uint4* p;
   if constexpr (!BATCH) {
-    return P.W[(gi < g_end ? gi : g_end - 1) * L + sl];
+    p = P.W + 2 * ((gi < g_end ? gi : g_end - 1) * L + sl);
   } else {
     const int64_t limit = g_end < c.end ? g_end : c.end;
     const int64_t g = gi < limit ? gi : c.first;
-    return c.W[(g - c.first) * L + sl];
+    p = c.W + 2 * ((g - c.first) * L + sl);
   }
+  return LaneW{p[0], p[1]};
 }
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// From the lane's 8 raw binary16 weights, compute its u values and the group scalars.
+// From the lane's 16 raw binary16 weights, compute its u values and the group scalars.
 // Called by all L lanes of a segment together (segment-wide DPP reductions).
 template <int L>
-__device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint4& raw,
+__device__ __forceinline__ GroupInit init_group(const SolveParams& P, const LaneW& raw,
                                                 float (&u)[kLaneElems]) {
   const float qmax = P.qmax;
   // Group min and max on the binary16 values themselves (exact): pairwise packed
-  // min/max over the 4 words, then one word (-min, max) reduced over the segment
+  // min/max over the 8 words, then one word (-min, max) reduced over the segment
   // with packed max.
-  const uint32_t m = pk_min_f16(pk_min_f16(raw.x, raw.y), pk_min_f16(raw.z, raw.w));
-  const uint32_t M = pk_max_f16(pk_max_f16(raw.x, raw.y), pk_max_f16(raw.z, raw.w));
+  const uint32_t m = pk_min_f16(pk_min_f16(pk_min_f16(raw.lo.x, raw.lo.y), pk_min_f16(raw.lo.z, raw.lo.w)),
+                                pk_min_f16(pk_min_f16(raw.hi.x, raw.hi.y), pk_min_f16(raw.hi.z, raw.hi.w)));
+  const uint32_t M = pk_max_f16(pk_max_f16(pk_max_f16(raw.lo.x, raw.lo.y), pk_max_f16(raw.lo.z, raw.lo.w)),
+                                pk_max_f16(pk_max_f16(raw.hi.x, raw.hi.y), pk_max_f16(raw.hi.z, raw.hi.w)));
   uint32_t v = pk_max_neglo_f16(__builtin_amdgcn_perm(M, m, 0x05040100u),   // (m.lo, M.lo)
                                 __builtin_amdgcn_perm(M, m, 0x07060302u));  // (m.hi, M.hi)
   if constexpr (L >= 2) v = pk_max_f16(v, dpp_u32<kDppQuadSwap1>(v));
@@ -273,7 +290,8 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
   // correctly rounded otherwise except within 2^-46 of a rounding midpoint.  A
   // constant group has a = 0, hence u = 0.
   const float c_lo = __builtin_fmaf(-g.inv_s, d, qmax) * rcp_d;
-  const uint32_t pair[4] = {raw.x, raw.y, raw.z, raw.w};
+  const uint32_t pair[8] = {raw.lo.x, raw.lo.y, raw.lo.z, raw.lo.w,
+                            raw.hi.x, raw.hi.y, raw.hi.z, raw.hi.w};
   bool half = false;  // some u of the lane is exactly a half-integer
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
@@ -301,10 +319,7 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const uint
       }
     }
   }
-  float lsum = u[0];
-#pragma unroll
-  for (int k = 1; k < kLaneElems; ++k) lsum += u[k];
-  g.usum = seg_sum<L>(lsum);
+  g.usum = seg_sum<L>(tree_sum<0, kLaneElems>(u));
   g.z0 = -(mn * g.inv_s);
   // Without shrink every code lies in [0, qmax], so |z - z0| <= qmax and every
   // |r| = s|x - W_q| <= s * max(0.5, qmax) = d: the shrink stays zero if d is below
@@ -323,23 +338,21 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// One evaluation of the lane's 8 weights at x = u + delta: the segment's lp error
+// One evaluation of the lane's 16 weights at x = u + delta: the segment's lp error
 // (code units) and code sum.  CLAMP = false is the exact shortcut for |delta| < 1/2.
 template <int L, int PM, bool CLAMP, bool ZERO = false>
 __device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float delta, float qmax,
                                            float p, float& e, float& sq) {
+  float a[kLaneElems], q[kLaneElems];
 #pragma unroll
   for (int k = 0; k < kLaneElems; ++k) {
     const float x = ZERO ? u[k] : u[k] + delta;  // ZERO: delta == 0 (x = u + 0 = u exactly)
-    float q = __builtin_rintf(x);
-    if constexpr (CLAMP) q = __builtin_amdgcn_fmed3f(q, 0.f, qmax);
-    const float rc = x - q;
-    const float a = pow_p<PM>(rc, p);
-    e = k == 0 ? a : e + a;
-    sq = k == 0 ? q : sq + q;
+    q[k] = __builtin_rintf(x);
+    if constexpr (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
+    a[k] = pow_p<PM>(x - q[k], p);
   }
-  e = seg_sum<L>(e);
-  sq = seg_sum<L>(sq);  // exact: a sum of small integers
+  e = seg_sum<L>(tree_sum<0, kLaneElems>(a));
+  sq = seg_sum<L>(tree_sum<0, kLaneElems>(q));  // exact: a sum of small integers
 }
 
 // State of one group held by a segment (identical in all L lanes of the segment).
@@ -403,7 +416,7 @@ __device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool
         else cs = q.inv_s * q.inv_s;
         const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
         const float ib = cs * inv_beta;  // s^(p-2) / beta_t
-        float acc = 0.f;
+        float we[kLaneElems];  // W_e / s
 #pragma unroll
         for (int k = 0; k < kLaneElems; ++k) {
           const float x = q.u[k] + q.delta;
@@ -412,9 +425,9 @@ __device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool
           const float a = __builtin_fabsf(rc);
           float m = 0.f;
           if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
-          acc += __builtin_copysignf(m, rc);  // W_e / s
+          we[k] = __builtin_copysignf(m, rc);
         }
-        num += seg_sum<L>(acc);
+        num += seg_sum<L>(tree_sum<0, kLaneElems>(we));
       }
     }
   }
@@ -425,7 +438,7 @@ __device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool
 
 // Codes at the accepted z, packed into the LSB-first bitstream, and the group's
 // binary16 s and z (plus the optional fp32 and error outputs).  Called by the L lanes
-// of a segment; lane sl writes the codes of its 8 elements.  CLAMP = false is exact
+// of a segment; lane sl writes the codes of its 16 elements.  CLAMP = false is exact
 // when |bd| < 1/2 (the argument of needs_clamp); ZERO: bd == 0 (codes rint(u)).
 template <int L, int PM, bool CLAMP, bool ZERO = false>
 __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
@@ -447,33 +460,37 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
     for (int k = n - 2; k >= 0; --k) acc = __builtin_fmaf(acc, radix, q[k0 + k]);
     return (uint32_t)acc;
   };
-  const int64_t chunk = gi * L + sl;  // index of this lane's 8 elements
+  const int64_t chunk = gi * L + sl;  // index of this lane's 16 elements
   switch (P.nbits) {
-    case 4: {
-      const uint32_t v = horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16);
-      reinterpret_cast<uint32_t*>(P.packed)[chunk] = v;
-      break;
-    }
-    case 2: {
-      reinterpret_cast<uint16_t*>(P.packed)[chunk] = (uint16_t)horner(0, 8, 4.f);
-      break;
-    }
-    case 8: {
-      uint2 v = make_uint2(0u, 0u);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k], (uint32_t)k, v.x);
-        v.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 4], (uint32_t)k, v.y);
-      }
+    case 4: {  // 16 codes = 8 bytes
+      const uint2 v = make_uint2(horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16),
+                                 horner(8, 4, 16.f) | (horner(12, 4, 16.f) << 16));
       reinterpret_cast<uint2*>(P.packed)[chunk] = v;
       break;
     }
-    default: {  // 3 bits: 8 codes = 24 bits = 3 bytes
-      const uint32_t v = horner(0, 8, 8.f);
-      uint8_t* dst = P.packed + chunk * 3;
-      dst[0] = (uint8_t)v;
-      dst[1] = (uint8_t)(v >> 8);
-      dst[2] = (uint8_t)(v >> 16);
+    case 2: {  // 4 bytes
+      reinterpret_cast<uint32_t*>(P.packed)[chunk] = horner(0, 8, 4.f) | (horner(8, 8, 4.f) << 16);
+      break;
+    }
+    case 8: {  // 16 bytes, written as two 8-byte halves (the stream is 8-byte aligned)
+      uint2 v0 = make_uint2(0u, 0u), v1 = make_uint2(0u, 0u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v0.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k], (uint32_t)k, v0.x);
+        v0.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 4], (uint32_t)k, v0.y);
+        v1.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 8], (uint32_t)k, v1.x);
+        v1.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 12], (uint32_t)k, v1.y);
+      }
+      reinterpret_cast<uint2*>(P.packed)[2 * chunk] = v0;
+      reinterpret_cast<uint2*>(P.packed)[2 * chunk + 1] = v1;
+      break;
+    }
+    default: {  // 3 bits: 16 codes = 48 bits = 6 bytes, 2-byte aligned
+      const uint32_t a = horner(0, 8, 8.f), b = horner(8, 8, 8.f);  // 24 bits each
+      uint16_t* dst = reinterpret_cast<uint16_t*>(P.packed + chunk * 6);
+      dst[0] = (uint16_t)a;
+      dst[1] = (uint16_t)((a >> 16) | (b << 8));
+      dst[2] = (uint16_t)(b >> 8);
       break;
     }
   }

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(kBlock) void hqq_lockstep_kernel(const SolveParams 
     const int64_t left = P.ngroups - g0;
     const int n = left < S ? (int)left : S;
     // Every lane loads (a segment past the end reads the batch's first group).
-    const uint4 raw = P.W[(seg < n ? g0 + seg : g0) * L + sl];
+    const uint4* wp = P.W + 2 * ((seg < n ? g0 + seg : g0) * L + sl);
+    const LaneW raw = {wp[0], wp[1]};
     Slot a;
     a.active = a.pending = false;
     a.gidx = g0 + seg;
