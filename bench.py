@@ -639,9 +639,11 @@ def measure_matmul(hq, lib, torch, Ws, settings, solver, stream, sh, dev,
         for M in rows:
             Xs = [(torch.randn((M, W.shape[1]), device=dev) * 0.5).half() for W in Ws]
             Ys = [torch.empty((M, W.shape[0]), dtype=torch.float16, device=dev) for W in Ws]
+            wss = [torch.empty(max(hq.hqq_matmul_workspace_bytes(M, W.shape[0], W.shape[1], nb, g), 1),
+                               dtype=torch.uint8, device=dev) for W in Ws]
             calls = [(X.data_ptr(), M, W.shape[1], q.packed.data_ptr(), q.scale.data_ptr(),
-                      q.zero.data_ptr(), W.shape[0], nb, g, Y.data_ptr(), 0, sh)
-                     for W, q, X, Y in zip(Ws, qs, Xs, Ys)]
+                      q.zero.data_ptr(), W.shape[0], nb, g, Y.data_ptr(), 0, ws.data_ptr(), sh)
+                     for W, q, X, Y, ws in zip(Ws, qs, Xs, Ys, wss)]
 
             def run(handle):
                 for a in calls:
@@ -790,14 +792,17 @@ KERNEL_SUMMARIES = {
              "of the whole stack after the solver, hqq_meta_quantize_batch, both settings, 1 "
              "warm-up + 5 timed passes, then 1 + 20 passes of hqq_meta_quantize over the "
              "largest matrix alone (bench.py measure_meta)."),
-    "matmul": (("_gem", "_skinny"), "hqq_matmul_llama70b_layer0.md",
+    "matmul": (("_gem", "_skinny", "_splitk"), "hqq_matmul_llama70b_layer0.md",
                "Product with the quantized weight on the 7 matrices of Llama-2-70B layer 0",
                "hqq_matmul, one call per matrix, M = 1, 4, 16, 64, 512, 4096 rows of X, b2 g32 and "
-               "b4 g64 weights from hqq_quantize, 1 warm-up + 20 / 5 / 2 timed passes "
-               "(bench.py measure_matmul); hqq_gemv_packed_kernel<b, M rows, weight rows per "
-               "wave, g = 16> for M <= 2, hqq_skinny_kernel<b, 16-row blocks of X, 16-row "
-               "weight groups per wavefront, log2 g> for M <= 64, hqq_gemm_kernel<b, "
-               "wavefront rows WM, 2, 2> ((64 WM) x 128 tiles) above."),
+               "b4 g64 weights from hqq_quantize, 1 warm-up + 50 / 5 / 2 timed replays of a HIP "
+               "graph of the 7 calls (bench.py measure_matmul); hqq_gemv_packed_kernel<b, M "
+               "rows, weight rows per wave, g = 16> for M <= 2, hqq_skinny_kernel<b, 16-row "
+               "blocks of X, 16-row weight groups per wavefront, log2 g> for M <= 16, "
+               "hqq_splitk_kernel<b, 16-row blocks of X, 16-row weight groups per wavefront, "
+               "log2 g> plus hqq_splitk_reduce_kernel (the partial sums of the K splits, in "
+               "order) for M <= 64, hqq_gemm_kernel<b, wavefront rows WM, 2, 2> ((64 WM) x 128 "
+               "tiles) above."),
     "lowrank": ("hqq", "hqq_lowrank_llama70b_layer0.md",
                 "Low-rank compensation (rank 64) on the 7 matrices of Llama-2-70B layer 0",
                 "hqq_lowrank (residual_kernel; gemm16_kernel split-K products over the binary16 "
@@ -853,7 +858,7 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
         for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
             acc = {}
             for r in csv.DictReader(open(f)):
-                m = re.search(r"(hqq_\w+_kernel<[^>]*>)", r["Kernel_Name"])
+                m = re.search(r"(hqq_\w+_kernel(<[^>]*>)?)", r["Kernel_Name"])
                 if not m or "solve" in m.group(1):
                     continue
                 acc.setdefault(m.group(1), {}).setdefault(r["Counter_Name"], []).append(
@@ -864,7 +869,8 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     names = sorted({n for c in tab.values() for n in c})
     kernels = sorted(tab)
     lines = ["# Counters of the product kernels on one 28672 x 8192 b2 g32 weight", "",
-             "hqq_matmul at M = 1 (hqq_gemv_packed_kernel), M = 4, 16, 64 (hqq_skinny_kernel) "
+             "hqq_matmul at M = 1 (hqq_gemv_packed_kernel), M = 4, 16 (hqq_skinny_kernel), "
+             "M = 64 (hqq_splitk_kernel + hqq_splitk_reduce_kernel) "
              "and M = 512, 4096 (hqq_gemm_kernel), "
              "5 calls each (bench.py --profile-matmul); values per dispatch, averaged. "
              "GRBM_GUI_ACTIVE counts on every XCD (8 per device).", "",

@@ -29,6 +29,7 @@ HQQ_ERR_TABLE_MISMATCH = 5
 # Symbols declared in include/hqq.h.
 EXPORTED_SYMBOLS = ("hqq_quantize", "hqq_quantize_ex", "hqq_quantize_batch", "hqq_dequantize",
                     "hqq_quantize_tensor_stop", "hqq_tensor_stop_workspace_bytes", "hqq_matmul",
+                    "hqq_matmul_workspace_bytes",
                     "hqq_residual", "hqq_lowrank", "hqq_lowrank_workspace_bytes",
                     "hqq_meta_quantize", "hqq_meta_dequantize", "hqq_meta_groups",
                     "hqq_meta_workspace_bytes", "hqq_meta_quantize_batch",
@@ -87,7 +88,9 @@ def load_library(path: str = LIB_PATH):
     lib.hqq_lowrank_workspace_bytes.restype = I64
     lib.hqq_lowrank_workspace_bytes.argtypes = [I64, I64, I, I]
     lib.hqq_matmul.restype = I
-    lib.hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P, I, P]
+    lib.hqq_matmul.argtypes = [P, I64, I64, P, P, P, I64, I, I, P, I, P, P]
+    lib.hqq_matmul_workspace_bytes.restype = I64
+    lib.hqq_matmul_workspace_bytes.argtypes = [I64, I64, I64, I, I]
     lib.hqq_tensor_stop_workspace_bytes.restype = I64
     lib.hqq_tensor_stop_workspace_bytes.argtypes = [I]
     lib.hqq_quantize_batch.restype = I
@@ -172,9 +175,14 @@ def hqq_tensor_stop_noalloc_max_bytes() -> int:
 
 
 def hqq_matmul(X_f16: int, M: int, K: int, packed_codes: int, scale_f16: int, zero_f16: int,
-               N: int, nbits: int, group_size: int, Y: int, out_f32: int, stream: int = 0) -> int:
+               N: int, nbits: int, group_size: int, Y: int, out_f32: int, workspace: int = 0,
+               stream: int = 0) -> int:
     return load_library().hqq_matmul(X_f16, M, K, packed_codes, scale_f16, zero_f16, N, nbits,
-                                     group_size, Y, out_f32, stream)
+                                     group_size, Y, out_f32, workspace, stream)
+
+
+def hqq_matmul_workspace_bytes(M: int, N: int, K: int, nbits: int, group_size: int) -> int:
+    return load_library().hqq_matmul_workspace_bytes(M, N, K, nbits, group_size)
 
 
 def hqq_residual(W_f16: int, packed_codes: int, scale_f16: int, zero_f16: int, rows: int,
@@ -401,10 +409,12 @@ def _options(out: QuantizedWeight, debug: bool, early_stop: bool, refill_thresho
                          int(err_metric))
 
 
-def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, stream=None):
+def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, workspace=None,
+           stream=None):
     """Y = X Q^-1(W_q)^T (hqq_matmul) for a contiguous M x K float16 CUDA tensor X and a
     weight quantized as q (rows = N outputs, cols = K inputs).  Returns an M x N float16
-    (or float32) tensor, or fills ``out``."""
+    (or float32) tensor, or fills ``out``.  ``workspace`` may supply a uint8 CUDA tensor of
+    at least hqq_matmul_workspace_bytes(M, N, K, nbits, group_size) bytes."""
     import torch
     if X.dtype != torch.float16 or X.dim() != 2 or not X.is_cuda or not X.is_contiguous():
         raise ValueError("X must be a contiguous 2-D float16 CUDA tensor")
@@ -412,13 +422,21 @@ def matmul(X, q: "QuantizedWeight", out_f32: bool = False, out=None, stream=None
     if K != q.cols:
         raise ValueError(f"X has {K} columns, the weight {q.cols}")
     dt = torch.float32 if out_f32 else torch.float16
-    if out is None:
-        with _alloc_on(stream):
+    wb = hqq_matmul_workspace_bytes(M, q.rows, K, q.nbits, q.group_size)
+    if wb < 0:
+        raise HQQError(HQQ_ERR_INVALID_ARG, "hqq_matmul")
+    with _alloc_on(stream):
+        if out is None:
             out = torch.empty((M, q.rows), dtype=dt, device=X.device)
-    elif out.dtype != dt or tuple(out.shape) != (M, q.rows) or not out.is_contiguous():
+        if wb > 0 and workspace is None:
+            workspace = torch.empty(wb, dtype=torch.uint8, device=X.device)
+    if out.dtype != dt or tuple(out.shape) != (M, q.rows) or not out.is_contiguous():
         raise ValueError("out has the wrong dtype or shape")
+    if wb > 0 and (workspace.numel() < wb or not workspace.is_cuda):
+        raise ValueError(f"workspace needs {wb} bytes of device memory")
     st = hqq_matmul(_addr(X), M, K, _addr(q.packed), _addr(q.scale), _addr(q.zero), q.rows,
-                    q.nbits, q.group_size, _addr(out), int(bool(out_f32)), _stream_handle(stream))
+                    q.nbits, q.group_size, _addr(out), int(bool(out_f32)),
+                    _addr(workspace) if wb > 0 else 0, _stream_handle(stream))
     if st != HQQ_OK:
         raise HQQError(st, "hqq_matmul")
     return out

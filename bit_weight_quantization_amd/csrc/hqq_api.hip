@@ -381,9 +381,16 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
   return err == hipSuccess ? HQQ_OK : HQQ_ERR_LAUNCH;
 }
 
+int64_t hqq_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int nbits,
+                                   int group_size) {
+  if (checked_elems(M, K) < 0 || checked_elems(N, K) < 0 || checked_elems(M, N) < 0) return -1;
+  if (!supported_nbits(nbits) || !supported_group(group_size)) return -1;
+  return hqq::matmul_workspace_bytes(M, N, K, nbits, group_size);
+}
+
 int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes,
                const void* scale_f16, const void* zero_f16, int64_t N, int nbits,
-               int group_size, void* Y, int out_f32, void* stream) {
+               int group_size, void* Y, int out_f32, void* workspace, void* stream) {
   if (checked_elems(M, K) < 0 || checked_elems(N, K) < 0 || checked_elems(M, N) < 0)
     return HQQ_ERR_INVALID_ARG;
   if (!supported_nbits(nbits) || !supported_group(group_size)) return HQQ_ERR_UNSUPPORTED;
@@ -398,7 +405,12 @@ int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes
   if (K > 0 && (!aligned(X_f16, 16) || !aligned(packed_codes, 16) || !aligned(scale_f16, 2) ||
                 !aligned(zero_f16, 2)))
     return HQQ_ERR_ALIGNMENT;
+  if (hqq::matmul_workspace_bytes(M, N, K, nbits, group_size) > 0) {
+    if (!workspace) return HQQ_ERR_INVALID_ARG;
+    if (!aligned(workspace, 16)) return HQQ_ERR_ALIGNMENT;
+  }
   hqq::MatmulParams prm;
+  prm.part = static_cast<float*>(workspace);
   prm.X = static_cast<const uint16_t*>(X_f16);
   prm.packed = static_cast<const uint8_t*>(packed_codes);
   prm.scale16 = static_cast<const uint16_t*>(scale_f16);

@@ -16,6 +16,9 @@ struct MatmulParams {
   int nbits, group_size;
   int group_shift;          // log2(group_size)
   int out_f32;
+  float* part;              // split-K partial slabs (caller's workspace), or null
+  int64_t slab;             // floats per partial slab: M*N rounded up to a multiple of 4
+  int ksplit;               // splits of K (1: no partials)
 };
 
 // Rows of X up to which the wavefront-per-row kernel is used (kGemvAlignedMaxRows where
@@ -25,7 +28,13 @@ struct MatmulParams {
 constexpr int kGemvMaxRows = 8;
 constexpr int kGemvAlignedMaxRows = 2;
 constexpr int kSkinnyMaxRows = 64;
+constexpr int kSplitMinRows = 16;  // above this (and up to kSkinnyMaxRows) K is split
 
-hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream);
+// Bytes of workspace the product needs for these shapes (the split-K partial slabs of
+// the skinny path; 0 when the path writes Y directly).  Depends on the shapes only.
+int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int nbits, int group_size);
+
+// `prm.part` must hold matmul_workspace_bytes(...) bytes where that is not 0.
+hipError_t launch_matmul(MatmulParams prm, int cus, hipStream_t stream);
 
 }  // namespace hqq

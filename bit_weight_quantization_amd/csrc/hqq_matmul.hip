@@ -373,6 +373,15 @@ hipError_t launch_gemv_packed(const MatmulParams& P, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Block barrier that orders LDS accesses only: __syncthreads() also makes every wavefront
+// wait for its outstanding global loads (vmcnt(0)), which would end each prefetch at
+// the barrier.  The workgroup fences here are restricted to the LDS address space.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------- GEMM --
 
 constexpr int kBK = 64;
@@ -594,8 +603,8 @@ void hqq_gemm_kernel(const MatmulParams P) {
     dequant_b(other, k0 + kBK, bv);
     mfma_step(S);
     write_lds(other, S ^ 1, k0 + kBK, bv);  // (after the last step: unused; unconditional, so
-    __syncthreads();                         // the dequantization is not sunk past the MFMAs)
-  };
+    lds_barrier();                           // the dequantization is not sunk past the MFMAs;
+  };                                         // the loads of step k0 + 128 stay in flight)
 
   if (P.K > 0) {
     constexpr std::integral_constant<int, 0> s0{};
@@ -606,7 +615,7 @@ void hqq_gemm_kernel(const MatmulParams P) {
     dequant_b(s0, 0, bv);
     write_lds(s0, 0, 0, bv);
   }
-  __syncthreads();
+  lds_barrier();
   for (int64_t k0 = 0; k0 < P.K; k0 += 2 * kBK) {
     step(std::integral_constant<int, 0>{}, k0);
     if (k0 + kBK >= P.K) break;
@@ -1108,11 +1117,276 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
     }
 }
 
+// ------------------------------------------------------------- split-K GEMM --
+
+// 17 to 64 rows of X (M <= 16 MT) for 2-, 4- and 8-bit codes, groups of GS = 5, 6, 7, K a
+// multiple of 256 and 16-byte aligned s and z, with the rows of X shared by the block:
+// a block of kSplitWaves wavefronts covers 16 NW weight rows per wavefront and one
+// contiguous share (split blockIdx.y of `ksplit`) of the 256-wide blocks of K.  Per block
+// of K the block loads the block's tile of X (16 MT rows x 256, 16-byte loads, two whole
+// 128-byte lines per wavefront and instruction) into LDS once for all its wavefronts, so
+// X costs 16 MT / (64 NW) reads per weight row instead of one per wavefront's 16 NW rows
+// (measured at M = 64: 2x faster than a kernel whose wavefronts each read their own X
+// straight from global memory, whose address unit then stalled).  Double-buffered with
+// one LDS-only barrier per block of K (the weight loads stay in flight across it); the
+// next block's X is held in registers during this block's arithmetic.  Lane j + 16 kq
+// takes the 64 consecutive
+// codes k0 + 64 kq .. + 64 of each of its weight rows in one load, and MFMA step i
+// (v_mfma_f32_16x16x32_f16) gives the instruction's k index 8 kq + e the real
+// k0 + 64 kq + 8 i + e on both operands (X read from LDS at that column), so the
+// product is the same sum in another order.  The weight enters as in the other kernels
+// (s*q - s*z in fp32, one rounding, binary16).  With ksplit = 1 the block writes Y; else
+// its fp32 partial tile goes to part[split][m][n] (slabs of `slab` floats) and
+// hqq_splitk_reduce_kernel adds the splits in order.  C: lane j + 16 kq, element v holds
+// X row 16 t + 4 kq + v, weight row n0 + 16 w + j.
+constexpr int kSplitWaves = 4;            // wavefronts per block, each its own weight rows
+constexpr int kXRowBytes = 512 + 16;       // a row of X per block of K in LDS (+16: rows 4 banks apart)
+
+template <int NB, int MT, int NW, int GS>
+__global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const MatmulParams P) {
+  static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
+  static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
+  constexpr int XR = 16 * MT;                    // rows of X
+  constexpr int kRounds = XR / 8;                // 16-byte loads per thread per block of K
+  constexpr int kCW = 2 * NB;                    // code words per lane and weight row (64 codes)
+  constexpr int kSZ = GS == 5 ? 2 : 1;           // groups per lane and weight row
+  __shared__ __align__(16) unsigned char xs[2][XR * kXRowBytes];
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid & (kWave - 1);
+  const int j = lane & 15, kq = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * (kSplitWaves * 16 * NW) + wid * (16 * NW);
+  const int ksplit = P.ksplit;
+  const int64_t nkb = P.K >> 8;
+  const int64_t kb0 = blockIdx.y * nkb / ksplit, kb1 = (blockIdx.y + 1) * nkb / ksplit;
+  const int64_t row_bytes = (P.K >> 3) * NB;
+  const int64_t gpr = P.K >> GS;
+  // weight rows past N read the last one; their results are not stored
+  const uint8_t* cbase[NW];
+  const uint16_t* sbase[NW];
+  const uint16_t* zbase[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int64_t n = n0 + 16 * w + j;
+    const int64_t nn = n < P.N ? n : P.N - 1;
+    cbase[w] = P.packed + nn * row_bytes + kq * (8 * NB);
+    sbase[w] = P.scale16 + nn * gpr + ((64 * kq) >> GS);
+    zbase[w] = P.zero16 + nn * gpr + ((64 * kq) >> GS);
+  }
+  // the thread's share of a block's X tile: rows 8 r + tid / 32, 16-byte granule tid % 32
+  const int xrow0 = tid >> 5, xg = tid & 31;
+  const uint16_t* xsrc[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t m = 8 * r + xrow0;
+    xsrc[r] = P.X + (m < P.M ? m : P.M - 1) * P.K + 8 * xg;
+  }
+  float4_t acc[MT][NW];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc[t][w] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  struct Wt {
+    uint32_t cw[NW][kCW];                  // the lane's 64 codes of each weight row
+    uint32_t sz[NW];                       // binary16 s (GS = 5: two, one per group)
+    uint32_t zz[NW];                       // binary16 z
+  };
+  auto load_wt = [&](int64_t c, Wt& o) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint4* cp = reinterpret_cast<const uint4*>(cbase[w] + c * (32 * NB));
+#pragma unroll
+      for (int h = 0; h < kCW / 4; ++h) {
+        const uint4 v = cp[h];
+        o.cw[w][4 * h] = v.x; o.cw[w][4 * h + 1] = v.y; o.cw[w][4 * h + 2] = v.z; o.cw[w][4 * h + 3] = v.w;
+      }
+      const int64_t g = (c << 8) >> GS;  // first group of the block of K in the row
+      if constexpr (kSZ == 2) {
+        o.sz[w] = *reinterpret_cast<const uint32_t*>(sbase[w] + g);
+        o.zz[w] = *reinterpret_cast<const uint32_t*>(zbase[w] + g);
+      } else {
+        o.sz[w] = sbase[w][g];
+        o.zz[w] = zbase[w][g];
+      }
+    }
+  };
+  lds_u32x4 xr[kRounds];
+  auto load_x = [&](int64_t c) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) xr[r] = *reinterpret_cast<const lds_u32x4*>(xsrc[r] + (c << 8));
+  };
+  auto write_x = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r)
+      *reinterpret_cast<lds_u32x4*>(&xs[buf][(8 * r + xrow0) * kXRowBytes + 16 * xg]) = xr[r];
+  };
+
+  // one block of K from LDS buffer `buf` and weights `cur`; the next block's X and
+  // weights (the last block re-reads itself: no branch, so the waits count exactly)
+  // are loaded first and land in the other buffer after this block's reads
+  auto block = [&](int64_t c, int buf, const Wt& cur, Wt& nxt) {
+    const int64_t cn = c + 1 < kb1 ? c + 1 : c;
+    load_x(cn);
+    load_wt(cn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* xb = xs[buf] + j * kXRowBytes + 128 * kq;
+#pragma unroll
+    for (int ip = 0; ip < 4; ++ip) {  // steps 2 ip, 2 ip + 1: 16 codes per row
+      half8_t bf[2][NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        CodePairs<NB> cp;
+        uint32_t ws[CodePairs<NB>::kWords];
+#pragma unroll
+        for (int u = 0; u < CodePairs<NB>::kWords; ++u) ws[u] = cur.cw[w][ip * CodePairs<NB>::kWords + u];
+        cp.from(ws);
+        // codes 16 ip .. + 16 of the lane's 64: one group (GS = 5: group ip / 2)
+        const int hs = kSZ == 2 ? 16 * (ip >> 1) : 0;
+        const float sv = h2f((cur.sz[w] >> hs) & 0xffffu);
+        const float sz = sv * h2f((cur.zz[w] >> hs) & 0xffffu);  // exact
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const half2_t qq = cp.q[4 * b + e];
+            const float w0 = __builtin_fmaf(sv, (float)qq[0], -sz);
+            const float w1 = __builtin_fmaf(sv, (float)qq[1], -sz);
+            const half2_t hv = __builtin_convertvector((float2_t){w0, w1}, half2_t);
+            bf[b][w][2 * e] = hv[0];
+            bf[b][w][2 * e + 1] = hv[1];
+          }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int i = 2 * ip + b;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const half8_t af = __builtin_bit_cast(
+              half8_t, *reinterpret_cast<const lds_u32x4*>(xb + (16 * t) * kXRowBytes + 16 * i));
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            acc[t][w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b][w], acc[t][w], 0, 0, 0);
+        }
+      }
+    }
+    write_x(buf ^ 1);  // every wavefront finished reading that buffer before the last barrier
+    lds_barrier();
+  };
+  if (kb0 < kb1) {
+    Wt wa, wb;
+    load_x(kb0);
+    load_wt(kb0, wa);
+    write_x(0);
+    lds_barrier();
+    for (int64_t c = kb0; c < kb1; c += 2) {
+      block(c, (int)((c - kb0) & 1), wa, wb);
+      if (c + 1 >= kb1) break;
+      block(c + 1, (int)((c + 1 - kb0) & 1), wb, wa);
+    }
+  }
+  // the wavefront's tile: Y directly (one split) or the split's partial slab
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int64_t n = n0 + 16 * w + j;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = 16 * t + 4 * kq + v;
+        if (m < P.M && n < P.N) {
+          const float y = acc[t][w][v];
+          if (ksplit > 1) P.part[blockIdx.y * P.slab + m * P.N + n] = y;
+          else if (P.out_f32) static_cast<float*>(P.Y)[m * P.N + n] = y;
+          else static_cast<_Float16*>(P.Y)[m * P.N + n] = (_Float16)y;
+        }
+      }
+    }
+}
+
+// Y = the sum of the ksplit partial slabs in split order (fp32), 4 elements per thread;
+// binary16 output is the nearest-even rounding of that sum.
+__global__ __launch_bounds__(kBlock) void hqq_splitk_reduce_kernel(const MatmulParams P) {
+  const int64_t mn = P.M * P.N;
+  const int64_t stride = (int64_t)gridDim.x * kBlock * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4; i < mn; i += stride) {
+    const float* src = P.part + i;
+    float4_t y = *reinterpret_cast<const float4_t*>(src);
+    int k = 1;
+    for (; k + 8 <= P.ksplit; k += 8) {  // eight loads in flight, added in split order
+      float4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4_t*>(src + (k + u) * P.slab);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y += v[u];
+    }
+    for (; k < P.ksplit; ++k) y += *reinterpret_cast<const float4_t*>(src + k * P.slab);
+    const int n = mn - i < 4 ? (int)(mn - i) : 4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v < n) {
+        if (P.out_f32) static_cast<float*>(P.Y)[i + v] = y[v];
+        else static_cast<_Float16*>(P.Y)[i + v] = (_Float16)y[v];
+      }
+    }
+  }
+}
+
 // The aligned skinny kernel applies: byte-aligned codes, groups of 32-128, K a multiple
 // of 256, 16-byte aligned s and z.
 bool skinny_aligned(const MatmulParams& P) {
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(P.scale16) | reinterpret_cast<uintptr_t>(P.zero16)) & 15) == 0;
   return P.nbits != 3 && P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7;
+}
+
+// Split-K geometry of the aligned skinny path, from the shapes alone (results do not
+// depend on the device): 16 NW weight rows per wavefront, and K split so that there are
+// about kSplitTargetBlocks blocks (two per CU) where K allows.
+constexpr int kSplitTargetBlocks = 512;
+struct SplitGeom {
+  int nw, ksplit;
+  int64_t row_blocks;
+};
+SplitGeom split_geometry(int64_t N, int64_t K) {
+  SplitGeom g;
+  g.nw = N >= 4096 ? 2 : 1;
+  g.row_blocks = (N + kSplitWaves * 16 * g.nw - 1) / (kSplitWaves * 16 * g.nw);
+  int64_t ks = (kSplitTargetBlocks + g.row_blocks / 2) / g.row_blocks;
+  const int64_t nkb = K >> 8;
+  if (ks > nkb) ks = nkb;
+  g.ksplit = ks < 1 ? 1 : (int)ks;
+  return g;
+}
+
+// The split-K path applies (s and z alignment aside, checked at the call): 17 to 64 rows
+// of X (up to 16 the aligned skinny kernel, which needs no workspace, is as fast).
+bool splitk_shapes(int64_t M, int64_t K, int nbits, int group_size) {
+  return nbits != 3 && K % 256 == 0 && group_size >= 32 && group_size <= 128 &&
+         M > kSplitMinRows && M <= kSkinnyMaxRows;
+}
+
+template <int NB, int MT, int NW>
+void launch_splitk_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
+  const dim3 block(kSplitWaves * kWave);
+  switch (P.group_shift) {
+    case 5: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 5>), grid, block, 0, st, P); return;
+    case 6: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 6>), grid, block, 0, st, P); return;
+    default: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 7>), grid, block, 0, st, P); return;
+  }
+}
+
+template <int NB, int MT>
+void launch_splitk(MatmulParams P, hipStream_t st) {
+  const SplitGeom g = split_geometry(P.N, P.K);
+  P.ksplit = g.ksplit;
+  P.slab = (P.M * P.N + 3) & ~(int64_t)3;
+  const dim3 grid((unsigned)g.row_blocks, (unsigned)g.ksplit);
+  if (g.nw == 2) launch_splitk_nw<NB, MT, 2>(P, grid, st);
+  else launch_splitk_nw<NB, MT, 1>(P, grid, st);
+  if (g.ksplit > 1) {
+    int64_t blocks = (P.M * P.N + 4 * kBlock - 1) / (4 * kBlock);
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(hqq_splitk_reduce_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, P);
+  }
 }
 
 template <int NB, int MT, int NW>
@@ -1151,6 +1425,13 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
       return launch_gemv_packed<NB, 1>(P, st);
     }
   }
+  if constexpr (NB != 3) {
+    if (skinny_aligned(P) && splitk_shapes(P.M, P.K, NB, P.group_size)) {
+      if (P.M <= 32) launch_splitk<NB, 2>(P, st);
+      else launch_splitk<NB, 4>(P, st);
+      return hipGetLastError();
+    }
+  }
   if (P.M > gemv_max && P.M <= kSkinnyMaxRows) {
     if (P.M <= 16) launch_skinny<NB, 1>(P, st);
     else if (P.M <= 32) launch_skinny<NB, 2>(P, st);
@@ -1184,7 +1465,16 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_matmul(const MatmulParams& prm, int cus, hipStream_t stream) {
+int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int nbits, int group_size) {
+  if (!splitk_shapes(M, K, nbits, group_size) || N <= 0) return 0;
+  const SplitGeom g = split_geometry(N, K);
+  if (g.ksplit <= 1) return 0;
+  return (int64_t)g.ksplit * ((M * N + 3) & ~(int64_t)3) * (int64_t)sizeof(float);
+}
+
+hipError_t launch_matmul(MatmulParams prm, int cus, hipStream_t stream) {
+  prm.ksplit = 1;
+  prm.slab = 0;
   switch (prm.nbits) {
     case 2: return launch_nb<2>(prm, cus, stream);
     case 3: return launch_nb<3>(prm, cus, stream);

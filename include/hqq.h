@@ -338,11 +338,23 @@ int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
  * nbits, group_size  as quantized (2, 3, 4, 8 and 16, 32, 64, 128).
  * Y            M x N row-major: binary16 (out_f32 = 0, RNE of the fp32 sum; 2-byte
  *              aligned) or fp32 (out_f32 = 1; 4-byte aligned).
+ * workspace    hqq_matmul_workspace_bytes(M, N, K, nbits, group_size) bytes of device
+ *              memory, 16-byte aligned, or NULL where that is 0.  For 17 to 64 rows of X
+ *              with 2-, 4- or 8-bit codes, groups of 32-128 and K a multiple of 256, K is
+ *              split over several blocks whose fp32 partial products go to the workspace
+ *              and are added in a fixed order (results do not depend on the device or the
+ *              run); the split depends on the shapes only.  Written and read on `stream`,
+ *              no state between calls: calls that share a workspace must be ordered.
+ *              NULL where it is needed: HQQ_ERR_INVALID_ARG.
  * Conventions and errors as for hqq_quantize.
  */
 int hqq_matmul(const void* X_f16, int64_t M, int64_t K, const void* packed_codes,
                const void* scale_f16, const void* zero_f16, int64_t N, int nbits,
-               int group_size, void* Y, int out_f32, void* stream);
+               int group_size, void* Y, int out_f32, void* workspace, void* stream);
+
+/* Bytes of the workspace of hqq_matmul for these shapes (0: none needed); -1 for invalid
+ * shapes, widths or group sizes. */
+int64_t hqq_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int nbits, int group_size);
 
 /*
  * hqq_residual -- the quantization error Delta W = W - Q^-1(W_q) of a weight quantized

@@ -127,7 +127,7 @@ def test_quantize_ex_option_validation(lib):
 
 def _mm(**kw):
     a = dict(X_f16=FAKE, M=4, K=256, packed_codes=FAKE, scale_f16=FAKE, zero_f16=FAKE, N=16,
-             nbits=4, group_size=64, Y=FAKE, out_f32=0, stream=0)
+             nbits=4, group_size=64, Y=FAKE, out_f32=0, workspace=0, stream=0)
     a.update(kw)
     return hq.hqq_matmul(**a)
 
@@ -149,9 +149,29 @@ def _mm(**kw):
     (dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
     (dict(Y=FAKE + 2, out_f32=1), hq.HQQ_ERR_ALIGNMENT),
     (dict(Y=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
+    # split-K path (17..64 rows, K = 8192 in 32 blocks of 256): the workspace is required
+    (dict(M=32, N=1024, K=8192), hq.HQQ_ERR_INVALID_ARG),
+    (dict(M=32, N=1024, K=8192, workspace=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
 ])
 def test_matmul_rejects_before_launch(lib, kw, status):
     assert _mm(**kw) == status
+
+
+def test_matmul_workspace_bytes(lib):
+    wb = hq.hqq_matmul_workspace_bytes
+    # split-K path: 17..64 rows of X, 2/4/8-bit codes, groups of 32..128, K % 256 == 0
+    # (N = 1024: 16 blocks of 64 weight rows, K = 8192: 32 blocks of 256 -> 32 splits)
+    assert wb(32, 1024, 8192, 4, 64) == 32 * 32 * 1024 * 4
+    assert wb(64, 8192, 8192, 2, 32) == 8 * 64 * 8192 * 4   # 64 blocks of 128 rows: 8 splits
+    assert wb(17, 5, 256, 8, 128) == 0      # one block of K: no partials
+    assert wb(17, 7, 1024, 4, 64) == 4 * 120 * 4  # M N = 119 rounded up to 120 floats per slab
+    for args in [(16, 1024, 8192, 4, 64), (2, 1024, 8192, 4, 64), (65, 1024, 8192, 4, 64),
+                 (32, 1024, 8192, 3, 64), (32, 1024, 8192, 4, 16), (32, 1024, 8160, 4, 32),
+                 (0, 1024, 8192, 4, 64)]:
+        assert wb(*args) == 0, args
+    assert wb(-1, 1024, 8192, 4, 64) == -1
+    assert wb(16, 1024, 8192, 5, 64) == -1
+    assert wb(16, 1024, 8192, 4, 48) == -1
 
 
 def test_matmul_empty_is_a_no_op(lib):

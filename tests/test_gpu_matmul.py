@@ -63,8 +63,12 @@ def _run(hq, X, packed, s, z, N, nbits, g, out_f32, sz_offset=0):
     sd = torch.from_numpy(np.concatenate([pad, s.view(np.int16).ravel()])).cuda()
     zd = torch.from_numpy(np.concatenate([pad, z.view(np.int16).ravel()])).cuda()
     Y = torch.empty((M, N), dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
+    wb = hq.hqq_matmul_workspace_bytes(M, N, K, nbits, g)
+    assert wb >= 0
+    ws = torch.empty(max(wb, 1), dtype=torch.uint8, device="cuda")
     st = hq.hqq_matmul(Xd.data_ptr(), M, K, pd.data_ptr(), sd.data_ptr() + 2 * sz_offset,
-                       zd.data_ptr() + 2 * sz_offset, N, nbits, g, Y.data_ptr(), int(out_f32), 0)
+                       zd.data_ptr() + 2 * sz_offset, N, nbits, g, Y.data_ptr(), int(out_f32),
+                       ws.data_ptr() if wb > 0 else 0)
     assert st == hq.HQQ_OK, hq.hqq_status_string(st)
     torch.cuda.synchronize()
     return Y.cpu().numpy().astype(np.float64)
@@ -124,10 +128,11 @@ def test_exact_products_all_paths(hq, nbits, g):
 @pytest.mark.parametrize("nbits", [2, 4, 8])
 def test_exact_products_skinny_paths(hq, nbits):
     """Small batches (2 < M <= 64) on the matrix-core skinny kernels: K a multiple of 256
-    with 1, 9 (split unevenly over the 8 wavefronts of a block) and 16 blocks of 256, one
-    and two 16-row weight groups per block (N below and above 4096, ragged), every
-    16-row tile count of X (M = 9 .. 64), groups of 32, 64 and 128, and s, z off 16-byte
-    alignment (the general kernel): bit-exact on exact inputs."""
+    with 1, 2, 9 and 16 blocks of 256 (split over 1, 2 and 16 partial sums; the general
+    kernel splits 9 unevenly over the 8 wavefronts of a block), one and two 16-row weight
+    groups per wavefront (N below and above 4096, ragged), every 16-row tile count of X
+    (M = 3 .. 64), groups of 32, 64 and 128, and s, z off 16-byte alignment (the general
+    kernel): bit-exact on exact inputs."""
     rng = np.random.default_rng(400 + nbits)
     cases = [(3, 100, 512, 32, 0), (4, 130, 2304, 128, 0), (8, 4100, 256, 64, 0),
              (9, 100, 256, 32, 0), (16, 300, 2304, 64, 0), (17, 129, 4096, 128, 0),
@@ -143,6 +148,35 @@ def test_exact_products_skinny_paths(hq, nbits):
             bad = np.argwhere(Y != want)
             assert bad.size == 0, (M, N, K, g, off, out_f32, bad[:5], Y[tuple(bad[0])], want[tuple(bad[0])])
         _say(f"b{nbits} M={M} N={N} K={K} g{g} s/z offset {off}: exact")
+
+
+def test_split_k_is_deterministic_and_exact(hq):
+    """The split-K path (17 to 64 rows of X): many partial slabs (N = 1024, K = 8192: 32
+    splits; N = 8192, K = 4096: 8) are added in a fixed order, so repeated calls give
+    identical bits on general inputs, and exact inputs give the exact product."""
+    rng = np.random.default_rng(77)
+    for M, N, K, nbits, g in [(64, 1024, 8192, 4, 64), (24, 8192, 4096, 2, 32),
+                              (37, 1000, 8192, 8, 128)]:
+        wb = hq.hqq_matmul_workspace_bytes(M, N, K, nbits, g)
+        assert wb > 0
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=M + N)
+        X = np.asarray(rng.standard_normal((M, K)), np.float16)
+        Y1 = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
+        Y2 = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
+        assert np.array_equal(Y1, Y2)
+        rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 30, replace=False)]))
+        bpr = K * nbits // 8
+        ref = oracle.hqq_matmul(X, packed.reshape(N, bpr)[rows].ravel(), s[rows], z[rows],
+                                len(rows), nbits, g)
+        b = _bound(X, codes[rows], s[rows], z[rows], g, False, 1, ref)
+        assert np.all(np.abs(Y1[:, rows] - ref) <= b)
+        codes, packed, s, z = _weight(N, K, nbits, g, seed=M + N + 1, exact=True)
+        Xe = rng.integers(-2, 3, (M, K)).astype(np.float16)
+        Ye = _run(hq, Xe, packed, s, z, N, nbits, g, out_f32=1)
+        ref = oracle.hqq_matmul(Xe, packed.reshape(N, bpr)[rows].ravel(), s[rows], z[rows],
+                                len(rows), nbits, g)
+        assert np.array_equal(Ye[:, rows], ref)
+        _say(f"split-K M={M} N={N} K={K} b{nbits} g{g}: {wb} workspace bytes, repeatable, exact")
 
 
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 32), (8, 128)])
