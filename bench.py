@@ -884,6 +884,54 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     print("\n".join(lines))
 
 
+def summarize_issue(pmc_dir: str, out_dir: str, command: str):
+    """Issued VALU work of the solver kernels per dispatch, from one rocprofv3 --pmc pass
+    over bench.py --variants-only (profiles/hqq_solver_variants_issue_llama70b_layer0.md):
+    VALU wave-instructions, the transcendental ones, active lanes, and the issue fraction
+    = issued full-rate slots (a transcendental counted as TAU slots, every other
+    instruction as one) over the dispatch's duration, against 78.6 T slots/s.  This counts
+    work the kernel actually did, where the algorithmic op model of the whole-tensor stop
+    counts evaluations its kernels skip."""
+    import csv
+    import glob
+    import re
+    tau = 4.0  # quarter-rate transcendentals (measured 8.2 cycles against 2.0-2.5)
+    acc = {}
+    for f in glob.glob(os.path.join(pmc_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(f)):
+            m = re.search(r"(hqq_\w+_kernel(<[^>]*>)?)", r["Kernel_Name"])
+            if not m:
+                continue
+            d = acc.setdefault(m.group(1), {}).setdefault(r["Dispatch_Id"], {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["_dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    lines = ["# Issued VALU work of the solver kernels on Llama-2-70B layer 0 (solver variants)", "",
+             "rocprofv3 --pmc over bench.py --layers 1 --variants-only (per-group stop on the lp, "
+             "l1 and l2 error, no stop, the whole-tensor stop, RTN; b2 g32 and b4 g64); values "
+             "per dispatch, summed over the kernel's dispatches. Issue fraction = (VALU "
+             f"wave-instructions + {tau - 1:g} x transcendental ones) x 64 lanes over the summed "
+             "dispatch durations x 78.6 T full-rate lane-slots/s.", "",
+             "| kernel | dispatches | total ms | VALU wave-instr | transcendental | active lanes | issue fraction |",
+             "|---|---|---|---|---|---|---|"]
+    for k in sorted(acc):
+        ds = acc[k].values()
+        dur = sum(d["_dur"] for d in ds)
+        vi = sum(d.get("SQ_INSTS_VALU", 0.0) for d in ds)
+        tr = sum(d.get("SQ_INSTS_VALU_TRANS_F32", 0.0) for d in ds)
+        av = sum(d.get("SQ_ACTIVE_INST_VALU", 0.0) for d in ds)
+        tc = sum(d.get("SQ_THREAD_CYCLES_VALU", 0.0) for d in ds)
+        if dur <= 0 or vi <= 0:
+            continue
+        frac = (vi + (tau - 1) * tr) * 64 / dur / PEAK_VALU_SLOTS
+        lanes = tc / max(64 * av, 1)
+        lines.append(f"| {k} | {len(ds)} | {dur * 1e3:.3f} | {vi:.4g} | {tr:.4g} | {lanes:.3f} | {frac:.3f} |")
+    lines += ["", "Command:", "", "```", command, "```", ""]
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_solver_variants_issue_llama70b_layer0.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -930,6 +978,8 @@ def main():
                          "from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write profiles/ summaries from rocprofv3 counter and trace output")
+    ap.add_argument("--summarize-issue", metavar="PMC_DIR", default=None,
+                    help="write the issued-VALU summary of the solver kernels (profiles/)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
                     help="write the profiles/ summary of rocprofv3 --pmc passes over "
                          "--profile-matmul")
@@ -939,6 +989,10 @@ def main():
     if args.summarize_kernels:
         summarize_kernels(args.summarize_kernels[0], args.summarize_kernels[1],
                           os.path.join(ROOT, "profiles"), args.profile_command)
+        return
+
+    if args.summarize_issue:
+        summarize_issue(args.summarize_issue, os.path.join(ROOT, "profiles"), args.profile_command)
         return
 
     if args.summarize_counters:
@@ -997,7 +1051,7 @@ def main():
             lines.append(f"| {name} | {v['ms']:.4f} | {v['cycles_per_wave_instr']:.3f} | "
                          f"{v['rel_to_add']:.3f} | {v['slots']:.3f} |")
         lines += ["", f"tau (mean slot cost of v_exp_f32 and v_log_f32) = {peaks['tau']}",
-                  "", "Command:", "", "```", args.profile_command or "python bench.py --peak-probe OUT_MD",
+                  "", "Command:", "", "```", args.profile_command or f"python bench.py --peak-probe {args.peak_probe}",
                   "```", ""]
         with open(args.peak_probe, "w") as f:
             f.write("\n".join(lines))
