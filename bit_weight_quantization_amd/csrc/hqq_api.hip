@@ -134,7 +134,7 @@ int validate_single(const void* W_f16, int64_t rows, int64_t cols, int nbits, in
   n = rows * cols;
   if (n == 0) return HQQ_OK;
   if (!W_f16 || !packed_codes || !scale_f16 || !zero_f16) return HQQ_ERR_INVALID_ARG;
-  if (!aligned(W_f16, 16) || !aligned(packed_codes, 8) || !aligned(scale_f16, 2) ||
+  if (!aligned(W_f16, 16) || !aligned(packed_codes, 4) || !aligned(scale_f16, 2) ||
       !aligned(zero_f16, 2))
     return HQQ_ERR_ALIGNMENT;
   return HQQ_OK;
@@ -320,7 +320,7 @@ int hqq_quantize_batch(const hqq_batch_entry_t* entries, const hqq_batch_entry_t
   }
   if (total == 0) return HQQ_OK;
   if (!packed_codes || !scale_f16 || !zero_f16 || !status_device) return HQQ_ERR_INVALID_ARG;
-  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
+  if (!aligned(packed_codes, 4) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
       !aligned(status_device, 4))
     return HQQ_ERR_ALIGNMENT;
 
@@ -361,7 +361,7 @@ int hqq_dequantize(const void* packed_codes, const void* scale_f16, const void* 
   const int64_t n = rows * cols;
   if (n == 0) return HQQ_OK;
   if (!packed_codes || !scale_f16 || !zero_f16 || !W_out_f16) return HQQ_ERR_INVALID_ARG;
-  if (!aligned(packed_codes, 8) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
+  if (!aligned(packed_codes, 4) || !aligned(scale_f16, 2) || !aligned(zero_f16, 2) ||
       !aligned(W_out_f16, 16))
     return HQQ_ERR_ALIGNMENT;
   hqq::DequantParams prm;

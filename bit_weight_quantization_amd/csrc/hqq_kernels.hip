@@ -338,12 +338,13 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
         for (int k = 0; k < kDequantElems; ++k) c[k] = (v >> (2 * k)) & 3u;
         break;
       }
-      case 8: {
-        const uint2 v = reinterpret_cast<const uint2*>(P.packed)[chunk];
+      case 8: {  // two 4-byte words (the stream is 4-byte aligned)
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(P.packed) + 2 * chunk;
+        const uint32_t v0 = src[0], v1 = src[1];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          c[k] = (v.x >> (8 * k)) & 255u;
-          c[k + 4] = (v.y >> (8 * k)) & 255u;
+          c[k] = (v0 >> (8 * k)) & 255u;
+          c[k + 4] = (v1 >> (8 * k)) & 255u;
         }
         break;
       }

@@ -462,27 +462,25 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
   };
   const int64_t chunk = gi * L + sl;  // index of this lane's 16 elements
   switch (P.nbits) {
-    case 4: {  // 16 codes = 8 bytes
-      const uint2 v = make_uint2(horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16),
-                                 horner(8, 4, 16.f) | (horner(12, 4, 16.f) << 16));
-      reinterpret_cast<uint2*>(P.packed)[chunk] = v;
+    case 4: {  // 16 codes = 8 bytes, as two 4-byte words (the stream is 4-byte aligned)
+      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 2 * chunk;
+      dst[0] = horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16);
+      dst[1] = horner(8, 4, 16.f) | (horner(12, 4, 16.f) << 16);
       break;
     }
     case 2: {  // 4 bytes
       reinterpret_cast<uint32_t*>(P.packed)[chunk] = horner(0, 8, 4.f) | (horner(8, 8, 4.f) << 16);
       break;
     }
-    case 8: {  // 16 bytes, written as two 8-byte halves (the stream is 8-byte aligned)
-      uint2 v0 = make_uint2(0u, 0u), v1 = make_uint2(0u, 0u);
+    case 8: {  // 16 bytes, as four 4-byte words
+      uint32_t v[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v0.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k], (uint32_t)k, v0.x);
-        v0.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 4], (uint32_t)k, v0.y);
-        v1.x = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 8], (uint32_t)k, v1.x);
-        v1.y = __builtin_amdgcn_cvt_pk_u8_f32(q[k + 12], (uint32_t)k, v1.y);
-      }
-      reinterpret_cast<uint2*>(P.packed)[2 * chunk] = v0;
-      reinterpret_cast<uint2*>(P.packed)[2 * chunk + 1] = v1;
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v[w] = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * w + k], (uint32_t)k, v[w]);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 4 * chunk;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dst[w] = v[w];
       break;
     }
     default: {  // 3 bits: 16 codes = 48 bits = 6 bytes, 2-byte aligned

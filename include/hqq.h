@@ -112,7 +112,7 @@ typedef struct {
  * packed_codes hqq_packed_bytes(rows, cols, nbits) bytes: an LSB-first
  *              little-endian bitstream over the row-major elements (element n
  *              occupies bits [n*nbits, (n+1)*nbits); bit i of a byte is 2^i).
- *              nbits = 4: byte k = code[2k] | code[2k+1] << 4.  8-byte aligned.
+ *              nbits = 4: byte k = code[2k] | code[2k+1] << 4.  4-byte aligned.
  * scale_f16    hqq_num_groups(...) binary16 values of s.  2-byte aligned.
  * zero_f16     hqq_num_groups(...) binary16 values of z, in code units
  *              (real-valued, not rounded to an integer).  2-byte aligned.
@@ -222,7 +222,7 @@ typedef struct {
  *                 the device copy before it reads any weight and, if the two differ,
  *                 writes nothing at all (see status_device).
  * count           >= 0; 0 (or no group at all) is a valid no-op.
- * packed_codes    total_groups * group_size * nbits / 8 bytes, 8-byte aligned; the
+ * packed_codes    total_groups * group_size * nbits / 8 bytes, 4-byte aligned; the
  *                 codes of group k start at byte k * group_size * nbits / 8 (the
  *                 LSB-first bitstream of hqq_quantize, matrix after matrix).
  * scale_f16, zero_f16  total_groups binary16 values each, 2-byte aligned.

@@ -95,7 +95,7 @@ def _q(**kw):
     (dict(scale_f16=0), hq.HQQ_ERR_INVALID_ARG),
     (dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
     (dict(W_f16=FAKE + 8), hq.HQQ_ERR_ALIGNMENT),
-    (dict(packed_codes=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    (dict(packed_codes=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
     (dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
     (dict(zero_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
 ])
@@ -340,7 +340,7 @@ def _qb(entries, count, **kw):
     ([(16, 128)], None, dict(entries_device=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
     ([(16, 128)], None, dict(packed_codes=0), hq.HQQ_ERR_INVALID_ARG),
     ([(16, 128)], None, dict(zero_f16=0), hq.HQQ_ERR_INVALID_ARG),
-    ([(16, 128)], None, dict(packed_codes=FAKE + 4), hq.HQQ_ERR_ALIGNMENT),
+    ([(16, 128)], None, dict(packed_codes=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),
     ([(16, 128)], None, dict(scale_f16=FAKE + 1), hq.HQQ_ERR_ALIGNMENT),
     ([(16, 128)], None, dict(status_device=0), hq.HQQ_ERR_INVALID_ARG),
     ([(16, 128)], None, dict(status_device=FAKE + 2), hq.HQQ_ERR_ALIGNMENT),

@@ -298,6 +298,31 @@ def test_dequantize_is_single_rounding(hq, nbits, g):
     assert np.array_equal(Wd.cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("nbits,g", [(4, 64), (8, 128), (2, 32), (3, 16)])
+def test_packed_stream_four_byte_aligned(hq, nbits, g):
+    """The packed stream needs only 4-byte alignment: quantizing into a buffer 4 bytes past
+    an aligned allocation gives the same bytes, and hqq_dequantize reads them back from
+    there bit for bit."""
+    _say(f"packed stream at a 4-byte offset, b{nbits} g{g}")
+    W = workloads.generate(256, 512, workloads.WORKLOADS["mlp_11008x4096"].dist, 23, "cuda")
+    ref = hq.quantize(W, nbits, g)
+    nb = hq.hqq_packed_bytes(256, 512, nbits)
+    buf = torch.full((nb + 16,), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.empty_like(ref.scale)
+    z = torch.empty_like(ref.zero)
+    st = hq.hqq_quantize(W.data_ptr(), 256, 512, nbits, g, 0.7, 1.0, 1.01, 20,
+                         buf.data_ptr() + 4, s.data_ptr(), z.data_ptr())
+    assert st == hq.HQQ_OK, hq.hqq_status_string(st)
+    out = torch.empty_like(W)
+    st = hq.hqq_dequantize(buf.data_ptr() + 4, s.data_ptr(), z.data_ptr(), 256, 512, nbits, g,
+                           out.data_ptr())
+    assert st == hq.HQQ_OK, hq.hqq_status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[4:4 + nb], ref.packed)
+    assert int(buf[:4].ne(0xA5).sum()) == 0 and int(buf[4 + nb:].ne(0xA5).sum()) == 0
+    assert torch.equal(out.view(torch.int16), hq.dequantize(ref).view(torch.int16))
+
+
 def test_plain_entry_point_equals_debug_entry_point_and_is_deterministic(hq):
     _say("hqq_quantize vs hqq_quantize_ex, repeatability, side stream")
     W = workloads.generate_matrix(workloads.WORKLOADS["attn_4096x4096"], 0, "cuda")
