@@ -1221,13 +1221,16 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const M
       *reinterpret_cast<lds_u32x4*>(&xs[buf][(8 * r + xrow0) * kXRowBytes + 16 * xg]) = xr[r];
   };
 
-  // one block of K from LDS buffer `buf` and weights `cur`; the next block's X and
-  // weights (the last block re-reads itself: no branch, so the waits count exactly)
-  // are loaded first and land in the other buffer after this block's reads
-  auto block = [&](int64_t c, int buf, const Wt& cur, Wt& nxt) {
-    const int64_t cn = c + 1 < kb1 ? c + 1 : c;
-    load_x(cn);
-    load_wt(cn, nxt);
+  // one block of K from LDS buffer `buf` and weights `cur`; unless it is the split's
+  // last (LAST, a separate copy of the body, so the loop has no branch and its waits
+  // count exactly), the next block's X and weights are loaded first and land in the
+  // other buffer after this block's reads
+  auto block = [&](auto last_const, int64_t c, int buf, const Wt& cur, Wt& nxt) {
+    constexpr bool LAST = decltype(last_const)::value;
+    if constexpr (!LAST) {
+      load_x(c + 1);
+      load_wt(c + 1, nxt);
+    }
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* xb = xs[buf] + j * kXRowBytes + 128 * kq;
 #pragma unroll
@@ -1269,19 +1272,29 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const M
         }
       }
     }
-    write_x(buf ^ 1);  // every wavefront finished reading that buffer before the last barrier
-    lds_barrier();
+    if constexpr (!LAST) {
+      write_x(buf ^ 1);  // every wavefront finished reading that buffer before the last barrier
+      lds_barrier();
+    }
   };
   if (kb0 < kb1) {
+    constexpr std::integral_constant<bool, false> more{};
+    constexpr std::integral_constant<bool, true> last{};
     Wt wa, wb;
     load_x(kb0);
     load_wt(kb0, wa);
     write_x(0);
     lds_barrier();
-    for (int64_t c = kb0; c < kb1; c += 2) {
-      block(c, (int)((c - kb0) & 1), wa, wb);
-      if (c + 1 >= kb1) break;
-      block(c + 1, (int)((c + 1 - kb0) & 1), wb, wa);
+    int64_t c = kb0;
+    for (; c + 2 < kb1; c += 2) {
+      block(more, c, 0, wa, wb);
+      block(more, c + 1, 1, wb, wa);
+    }
+    if (c + 1 < kb1) {  // two blocks left
+      block(more, c, 0, wa, wb);
+      block(last, c + 1, 1, wb, wa);
+    } else {
+      block(last, c, 0, wa, wb);
     }
   }
   // the wavefront's tile: Y directly (one split) or the split's partial slab
