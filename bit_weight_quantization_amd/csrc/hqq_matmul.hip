@@ -1147,7 +1147,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const M
   static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
   static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
   constexpr int XR = 16 * MT;                    // rows of X
-  constexpr int kRounds = XR / 8;                // 16-byte loads per thread per block of K
+  constexpr int kXRows = kSplitWaves * kWave / 32;  // rows of X per round of 16-byte loads
+  constexpr int kRounds = XR / kXRows;           // 16-byte loads per thread per block of K
   constexpr int kCW = 2 * NB;                    // code words per lane and weight row (64 codes)
   constexpr int kSZ = GS == 5 ? 2 : 1;           // groups per lane and weight row
   __shared__ __align__(16) unsigned char xs[2][XR * kXRowBytes];
@@ -1177,7 +1178,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const M
   const uint16_t* xsrc[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    const int64_t m = 8 * r + xrow0;
+    const int64_t m = kXRows * r + xrow0;
     xsrc[r] = P.X + (m < P.M ? m : P.M - 1) * P.K + 8 * xg;
   }
   float4_t acc[MT][NW];
@@ -1218,7 +1219,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const M
   auto write_x = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r)
-      *reinterpret_cast<lds_u32x4*>(&xs[buf][(8 * r + xrow0) * kXRowBytes + 16 * xg]) = xr[r];
+      *reinterpret_cast<lds_u32x4*>(&xs[buf][(kXRows * r + xrow0) * kXRowBytes + 16 * xg]) = xr[r];
   };
 
   // one block of K from LDS buffer `buf` and weights `cur`; unless it is the split's
@@ -1354,7 +1355,7 @@ bool skinny_aligned(const MatmulParams& P) {
 // Split-K geometry of the aligned skinny path, from the shapes alone (results do not
 // depend on the device): 16 NW weight rows per wavefront, and K split so that there are
 // about kSplitTargetBlocks blocks (two per CU) where K allows.
-constexpr int kSplitTargetBlocks = 512;
+constexpr int kSplitTargetBlocks = 2048 / kSplitWaves;  // 2048 wavefronts
 struct SplitGeom {
   int nw, ksplit;
   int64_t row_blocks;
