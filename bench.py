@@ -884,6 +884,50 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     print("\n".join(lines))
 
 
+def summarize_vmix(dirs: list, weights_per_launch: float, out_dir: str, command: str):
+    """Dynamic instruction mix of the solver kernels from rocprofv3 --pmc passes over an
+    8-layer batch (profiles/hqq_solve_instruction_mix_llama70b.md): wave-instructions per
+    1024 weights (one wavefront's load of 16 weights per lane) by class."""
+    import csv
+    import glob
+    acc = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            per = {}
+            for r in csv.DictReader(open(f)):
+                k = _kernel_key(r["Kernel_Name"])
+                if not k or not k.startswith("hqq_solve"):
+                    continue
+                per.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+                per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            for k, c in per.items():
+                acc.setdefault(k, {}).update(c)
+    names = sorted({n for c in acc.values() for n in c if n != "SQ_WAVES"})
+    kernels = sorted(acc)
+    scale = 1024.0 / weights_per_launch
+    lines = ["# Instruction mix of hqq_solve_kernel on the Llama-2-70B-shaped stack", "",
+             f"rocprofv3 --pmc passes over one batched launch per setting on the first 8 layers "
+             f"({weights_per_launch / 1e9:.3f} G weights); wave-instructions per 1024 weights "
+             "(one wavefront's share: 16 weights per lane). VALU classes not listed (round, "
+             "median, compare, select, fract, DPP, packed f16, bit operations) are the "
+             "difference between SQ_INSTS_VALU and the listed classes.", "",
+             "| counter | " + " | ".join(kernels) + " |", "|---" * (len(kernels) + 1) + "|"]
+    for n in names:
+        lines.append(f"| {n} | " + " | ".join(f"{acc[k].get(n, float('nan')) * scale:.1f}" for k in kernels) + " |")
+    listed = ["SQ_INSTS_VALU_ADD_F32", "SQ_INSTS_VALU_MUL_F32", "SQ_INSTS_VALU_FMA_F32",
+              "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_INT32",
+              "SQ_INSTS_VALU_INT64", "SQ_INSTS_VALU_ADD_F64", "SQ_INSTS_VALU_MUL_F64",
+              "SQ_INSTS_VALU_FMA_F64"]
+    lines.append("| VALU not in the listed classes | " + " | ".join(
+        f"{(acc[k].get('SQ_INSTS_VALU', 0.0) - sum(acc[k].get(n, 0.0) for n in listed)) * scale:.1f}"
+        for k in kernels) + " |")
+    lines += ["", "Command:", "", "```", command, "```", ""]
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_solve_instruction_mix_llama70b.md"), "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def summarize_issue(pmc_dir: str, out_dir: str, command: str):
     """Issued VALU work of the solver kernels per dispatch, from one rocprofv3 --pmc pass
     over bench.py --variants-only (profiles/hqq_solver_variants_issue_llama70b_layer0.md):
@@ -978,6 +1022,8 @@ def main():
                          "from a rocprofv3 kernel trace")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PMC_DIR", "KT_DIR"),
                     help="write profiles/ summaries from rocprofv3 counter and trace output")
+    ap.add_argument("--summarize-vmix", nargs="+", metavar="PMC_DIR",
+                    help="write the solver's instruction-mix summary (profiles/)")
     ap.add_argument("--summarize-issue", metavar="PMC_DIR", default=None,
                     help="write the issued-VALU summary of the solver kernels (profiles/)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
@@ -989,6 +1035,14 @@ def main():
     if args.summarize_kernels:
         summarize_kernels(args.summarize_kernels[0], args.summarize_kernels[1],
                           os.path.join(ROOT, "profiles"), args.profile_command)
+        return
+
+    if args.summarize_vmix:
+        import workloads
+        wl = workloads.WORKLOADS[args.workload]
+        mats = list(wl.matrices)[: 7 * args.layers] if args.layers else list(wl.matrices)
+        summarize_vmix(args.summarize_vmix, float(sum(m.rows * m.cols for m in mats)),
+                       os.path.join(ROOT, "profiles"), args.profile_command)
         return
 
     if args.summarize_issue:
