@@ -59,10 +59,15 @@ namespace {
 // first two evaluations, waiting for a free segment), u slots [kStandby, kStandby + S)
 // the done ring (stopped groups waiting to be written).  A slot holds the G
 // code-unit values u of a group; standby slots have a 12-word header (the full solver
-// state), done slots an 8-word one.
+// state), done slots an 8-word one.  The u values are stored as four planes of 16-byte
+// chunks: chunk i of lane sl of a slot sits at plane i, position slot * L + sl.  A
+// wavefront's accesses go to consecutive slots in lane order (pool, ring and take
+// ranks, finalize segments), so consecutive lanes touch consecutive 16-byte chunks and
+// each 16-byte access instruction is free of bank conflicts.
 template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
+  static constexpr int L = G / kLaneElems;
   // Wavefronts per SIMD the kernel is compiled for (the VGPR budget).  A wavefront
   // holds 1024 weights, so its LDS share is S(2G + 20) words, 35 KB (G = 128) to 53 KB
   // (G = 16) per block of four wavefronts: three blocks per CU fit in its 160 KB at
@@ -72,25 +77,30 @@ struct SolveLds {
   // A prime batch adds up to S groups to the pool, a hand-over up to S to the ring.
   static constexpr int kStandby = S;
   static constexpr int kDone = S;
-  float u[kWavesPerBlock][kStandby + kDone][G];
+  static constexpr int kSlots = kStandby + kDone;
+  float4 u[kWavesPerBlock][kLaneElems / 4][kSlots * L];
   uint4 standby_hdr[kWavesPerBlock][kStandby][3];
   uint4 done_hdr[kWavesPerBlock][kDone][2];
 };
 
+// The wavefront's u planes: plane i, position slot * L + sl.
 template <int G>
-__device__ __forceinline__ void store_u(float* slot_u, int sl, const float (&u)[kLaneElems]) {
-  float4* dst = reinterpret_cast<float4*>(slot_u + sl * kLaneElems);
+using UPlanes = float4 (*)[SolveLds<G>::kSlots * SolveLds<G>::L];
+
+template <int G>
+__device__ __forceinline__ void store_u(UPlanes<G> U, int slot, int sl, const float (&u)[kLaneElems]) {
+  constexpr int L = G / kLaneElems;
 #pragma unroll
   for (int i = 0; i < kLaneElems / 4; ++i)
-    dst[i] = make_float4(u[4 * i], u[4 * i + 1], u[4 * i + 2], u[4 * i + 3]);
+    U[i][slot * L + sl] = make_float4(u[4 * i], u[4 * i + 1], u[4 * i + 2], u[4 * i + 3]);
 }
 
 template <int G>
-__device__ __forceinline__ void load_u(const float* slot_u, int sl, float (&u)[kLaneElems]) {
-  const float4* src = reinterpret_cast<const float4*>(slot_u + sl * kLaneElems);
+__device__ __forceinline__ void load_u(UPlanes<G> U, int slot, int sl, float (&u)[kLaneElems]) {
+  constexpr int L = G / kLaneElems;
 #pragma unroll
   for (int i = 0; i < kLaneElems / 4; ++i) {
-    const float4 a = src[i];
+    const float4 a = U[i][slot * L + sl];
     u[4 * i] = a.x; u[4 * i + 1] = a.y; u[4 * i + 2] = a.z; u[4 * i + 3] = a.w;
   }
 }
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
   int64_t next = chunk * C;            // next group of the wave's queue
   int64_t q_end = next + C < P.ngroups ? next + C : P.ngroups;  // end of the current chunk
 
-  float (*U)[G] = lds.u[wid];
+  UPlanes<G> U = lds.u[wid];
   uint4 (*H)[3] = lds.standby_hdr[wid];
   uint4 (*D)[2] = lds.done_hdr[wid];  // done slot j has u slot kStandby + j
 
@@ -163,9 +173,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     const int n = avail < S ? (int)avail : S;
     Slot a;
     a.active = a.pending = false;
+    uint32_t nm_mx = 0u;
     if (seg < n) {
       a.gidx = next + seg;
-      const GroupInit gq = init_group<L>(P, prefetch, a.u);
+      const GroupInit gq = init_group<L, false>(P, prefetch, a.u);
       a.s = gq.s;
       a.inv_s = gq.inv_s;
       a.z0 = gq.z0;
@@ -175,6 +186,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
       a.best_e = __builtin_inff();
       a.t = a.t_star = 0;
       a.active = true;
+      nm_mx = gq.nm_mx;
     }
     next = uniform64(next + n);
     if (next >= q_end) {  // next chunk of the queue
@@ -185,20 +197,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     if constexpr (BATCH) {
       if (next < q_end) batch_advance(P, cursor, next);
     }
+    // t = 0: delta = 0, no clamp needed.  The evaluation also packs the codes rint(u)
+    // (the output of every group that stops at t = 1) and finds u lying exactly on a
+    // half-integer; those are settled from the raw weights (still in `prefetch`), and if
+    // one moved the wave recomputes the sums and the evaluation.
+    float e = 0.f, sq = 0.f;
+    uint2 pk0 = make_uint2(0u, 0u);
+    bool tie = false;
+    if (a.active) tie = eval_first<L, PM>(a.u, P.nbits, P.p, e, sq, pk0);
+    if (ballot(tie) != 0) {
+      bool moved = false;
+      if (tie) moved = settle_ties(prefetch, nm_mx, P.qmax, a.u);
+      if (ballot(moved) != 0) {
+        if (a.active) {
+          a.usum = seg_sum<L>(tree_sum<0, kLaneElems>(a.u));
+          eval_first<L, PM>(a.u, P.nbits, P.p, e, sq, pk0);
+        }
+      }
+    }
     prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
-    // t = 0: delta = 0, no clamp needed.
-    if (a.active) solver_step<L, PM, true>(P, a, false);
+    if (a.active) step_tail<L, PM>(P, a, e, sq);
     if (ballot(a.active) != 0) {
       const bool clamp = ballot(needs_clamp(a)) != 0;
       if (a.active) solver_step<L, PM>(P, a, clamp);
     }
-    // Groups stopping here have t* = 0 (they stopped at t = 1) unless iters == 1.
-    write_group_any<L, PM, true>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0,
-                                 a.best_e, a.t_star);
+    // Groups stopping here have t* = 0 (they stopped at t = 1) unless iters == 1: their
+    // codes are the packed rint(u) of the first evaluation (8-bit codes are rounded again).
+    if (P.nbits != 8 && ballot(a.pending && a.best_delta != 0.f) == 0) {
+      if (a.pending) {
+        store_codes(P, a.gidx * L + sl, PackedCodes{{pk0.x, pk0.y, 0u, 0u}});
+        if (sl == 0) write_meta<PM>(P, a.gidx, a.s, a.z0 + 0.f, a.e0, a.best_e, a.t_star);
+      }
+    } else {
+      write_group_any<L, PM>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0,
+                             a.best_e, a.t_star);
+    }
     const uint64_t m = ballot(a.active);
     if (a.active) {
       const int slot = n_standby + lanes_below(m) / L;  // n_standby <= kStandby - S
-      store_u<G>(U[slot], sl, a.u);
+      store_u<G>(U, slot, sl, a.u);
       if (sl == 0) {
         H[slot][0] = make_uint4((uint32_t)a.gidx, (uint32_t)(a.gidx >> 32), fbits(a.s), fbits(a.inv_s));
         H[slot][1] = make_uint4(fbits(a.z0), fbits(a.usum), fbits(a.delta), fbits(a.best_delta));
@@ -218,7 +255,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     const int rank = lanes_below(m) / L;
     if (want && rank < n_standby) {
       const int slot = n_standby - 1 - rank;
-      load_u<G>(U[slot], sl, sg.u);
+      load_u<G>(U, slot, sl, sg.u);
       const uint4 h0 = H[slot][0], h1 = H[slot][1], h2 = H[slot][2];
       sg.gidx = (int64_t)(((uint64_t)h0.y << 32) | h0.x);
       sg.s = bitsf(h0.z);
@@ -244,7 +281,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     const bool write = seg < n;
     const int slot = kStandby + (int)((unsigned)(done_head + (write ? seg : 0)) % (unsigned)kDone);
     float uu[kLaneElems];
-    load_u<G>(U[slot], sl, uu);
+    load_u<G>(U, slot, sl, uu);
     const uint4 h0 = D[slot - kStandby][0], h1 = D[slot - kStandby][1];
     write_group_any<L, PM>(P, write, sl, uu, (int64_t)(((uint64_t)h0.y << 32) | h0.x),
                            bitsf(h0.z), bitsf(h0.w), bitsf(h1.x), bitsf(h1.y), bitsf(h1.z),
@@ -273,7 +310,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
       if (sg.pending) {
         const int rank = lanes_below(pm) / L;
         const int slot = kStandby + (int)((unsigned)(done_head + done_count + rank) % (unsigned)kDone);
-        store_u<G>(U[slot], sl, sg.u);
+        store_u<G>(U, slot, sl, sg.u);
         if (sl == 0) {
           D[slot - kStandby][0] = make_uint4((uint32_t)sg.gidx, (uint32_t)(sg.gidx >> 32), fbits(sg.s),
                                       fbits(sg.z0));

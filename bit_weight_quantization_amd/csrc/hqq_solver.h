@@ -149,6 +149,7 @@ __device__ __forceinline__ float scalar_pow(float x, float p) {
 // Group scalars fixed at load.
 struct GroupInit {
   float s, inv_s, z0, usum;
+  uint32_t nm_mx;   // the group's -min (low half) and max (high half) as binary16
   bool may_shrink;  // the shrink can be non-zero at some step (|r| <= max - min always)
 };
 
@@ -217,6 +218,9 @@ __device__ __forceinline__ void batch_advance(const SolveParams& P, BatchCursor&
   }
 }
 
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
 // The lane's 16 binary16 weights: two consecutive 16-byte chunks.
 struct LaneW {
   uint4 lo, hi;
@@ -242,12 +246,42 @@ __device__ __forceinline__ LaneW fetch_chunk(const SolveParams& P, const BatchCu
   return LaneW{p[0], p[1]};
 }
 
-__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
-__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+// The first code decision is round(U) of the exact ratio U = (w - mn) qmax / d.  u is
+// U rounded once to fp32, and rounding is monotonic while half-integers are exact fp32
+// values, so rint(u) is round(U) unless u landed exactly on a half-integer that U is not
+// on.  For every u of the lane that lies exactly on a half-integer, the side is decided
+// exactly in fp64 -- (w - mn) qmax against u (mx - mn), both products of binary16
+// differences and small integers, exact -- and u moves one ulp towards U, so that every
+// later evaluation starts from a value on U's side of every half-integer.  A real tie
+// stays exactly on the half-integer.  Returns whether some u of the lane moved.
+// nm_mx: the group's -min (low half) and max (high half) as binary16.
+__device__ __forceinline__ bool settle_ties(const LaneW& raw, uint32_t nm_mx, float qmax,
+                                            float (&u)[kLaneElems]) {
+  const uint32_t pair[8] = {raw.lo.x, raw.lo.y, raw.lo.z, raw.lo.w,
+                            raw.hi.x, raw.hi.y, raw.hi.z, raw.hi.w};
+  const double mn64 = -(double)(float)__builtin_bit_cast(_Float16, (uint16_t)(nm_mx & 0xffffu));
+  const double d64 = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(nm_mx >> 16)) - mn64;
+  bool moved = false;
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    if (__builtin_amdgcn_fractf(u[k]) != 0.5f) continue;
+    const uint16_t hw = (uint16_t)(pair[k / 2] >> (16 * (k & 1)));
+    const double num = ((double)(float)__builtin_bit_cast(_Float16, hw) - mn64) * (double)qmax;
+    const double mid = (double)u[k] * d64;
+    if (num != mid) {
+      u[k] = bitsf(fbits(u[k]) + (num > mid ? 1u : 0xffffffffu));  // one ulp
+      moved = true;
+    }
+  }
+  return moved;
+}
 
 // From the lane's 16 raw binary16 weights, compute its u values and the group scalars.
-// Called by all L lanes of a segment together (segment-wide DPP reductions).
-template <int L>
+// Called by all L lanes of a segment together (segment-wide DPP reductions).  With
+// SETTLE the exact side of half-integer u is decided here (settle_ties); without, the
+// caller does it (the per-group kernel finds such u in its first evaluation) and must
+// recompute usum if a u moves.
+template <int L, bool SETTLE = true>
 __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const LaneW& raw,
                                                 float (&u)[kLaneElems]) {
   const float qmax = P.qmax;
@@ -268,6 +302,7 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const Lane
   const float mx = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
   const float d = mx - mn;
   GroupInit g;
+  g.nm_mx = v;
   // s = d / qmax and 1/s = qmax / d, each correctly rounded: a reciprocal estimate,
   // then one exact FMA residual step (d, qmax and the residuals are exact in fp32).
   const float rcp_d = d > 0.f ? __builtin_amdgcn_rcpf(d) : 0.f;
@@ -297,26 +332,11 @@ __device__ __forceinline__ GroupInit init_group(const SolveParams& P, const Lane
   for (int k = 0; k < kLaneElems; ++k) {
     const float a = (k & 1) ? half_minus<true>(pair[k / 2], mn) : half_minus<false>(pair[k / 2], mn);
     u[k] = __builtin_fmaf(a, g.inv_s, a * c_lo);
-    half |= __builtin_amdgcn_fractf(u[k]) == 0.5f;
+    if constexpr (SETTLE) half |= __builtin_amdgcn_fractf(u[k]) == 0.5f;
   }
-  // The first code decision is round(U) of the exact ratio U = (w - mn) qmax / d.  u is
-  // U rounded once to fp32, and rounding is monotonic while half-integers are exact
-  // fp32 values, so rint(u) is round(U) unless u landed exactly on a half-integer that
-  // U is not on.  There the side is decided exactly in fp64 -- (w - mn) qmax against
-  // u (mx - mn), both products of binary16 differences and small integers, exact -- and
-  // u moves one ulp towards U, so that every later evaluation starts from a value on
-  // U's side of every half-integer.  A real tie stays exactly on the half-integer.
-  if (ballot(half) != 0) {
-    if (half) {
-      const double mn64 = (double)mn, d64 = (double)mx - mn64;
-#pragma unroll
-      for (int k = 0; k < kLaneElems; ++k) {
-        if (__builtin_amdgcn_fractf(u[k]) != 0.5f) continue;
-        const uint16_t hw = (uint16_t)(pair[k / 2] >> (16 * (k & 1)));
-        const double num = ((double)(float)__builtin_bit_cast(_Float16, hw) - mn64) * (double)qmax;
-        const double mid = (double)u[k] * d64;
-        if (num != mid) u[k] = bitsf(fbits(u[k]) + (num > mid ? 1u : 0xffffffffu));  // one ulp
-      }
+  if constexpr (SETTLE) {
+    if (ballot(half) != 0) {
+      if (half) settle_ties(raw, v, qmax, u);
     }
   }
   g.usum = seg_sum<L>(tree_sum<0, kLaneElems>(u));
@@ -372,23 +392,13 @@ struct Slot {
 __device__ __forceinline__ bool far_delta(float delta) { return !(__builtin_fabsf(delta) < 0.4999f); }
 __device__ __forceinline__ bool needs_clamp(const Slot& q) { return q.active && far_delta(q.delta); }
 
-// One step of the solver for an active group: evaluation at the current z (codes,
-// residual, lp error), the early-stop test of section 4.1, and unless the group
-// stops, the sp1 shrink (only where it can be non-zero) and the sp2 mean.
-// FIRST: the step at t = 0 (delta = 0, no clamp needed).  Returns the evaluated
-// error (code units).
-template <int L, int PM, bool FIRST = false>
-__device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool clamp) {
+// What a solver step does after its evaluation (error e, code sum sq): the early-stop
+// test of section 4.1, and unless the group stops, the sp1 shrink (only where it can be
+// non-zero) and the sp2 mean.
+template <int L, int PM>
+__device__ __forceinline__ void step_tail(const SolveParams& P, Slot& q, float e, float sq) {
   constexpr float kInvG = 1.0f / (float)(L * kLaneElems);
   const float qmax = P.qmax;
-  float e, sq;
-  if constexpr (FIRST) {
-    eval_group<L, PM, false, true>(q.u, 0.f, qmax, P.p, e, sq);
-  } else if (clamp) {
-    eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
-  } else {
-    eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
-  }
   if (P.err_init && q.t == 0) q.e0 = e;
   const bool accept = !P.early_stop || (e < q.best_e);
   if (accept) {
@@ -399,7 +409,7 @@ __device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool
   if (!accept || q.t == P.iters) {
     q.active = false;
     q.pending = true;
-    return e;
+    return;
   }
   float num = sq - q.usum;
   if (ballot(q.may_shrink) != 0) {
@@ -433,7 +443,136 @@ __device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool
   }
   q.delta = num * kInvG;
   ++q.t;
+}
+
+// One step of the solver for an active group: evaluation at the current z (codes,
+// residual, lp error), then step_tail.  FIRST: the step at t = 0 (delta = 0, no clamp
+// needed).  Returns the evaluated error (code units).
+template <int L, int PM, bool FIRST = false>
+__device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool clamp) {
+  const float qmax = P.qmax;
+  float e, sq;
+  if constexpr (FIRST) {
+    eval_group<L, PM, false, true>(q.u, 0.f, qmax, P.p, e, sq);
+  } else if (clamp) {
+    eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
+  } else {
+    eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
+  }
+  step_tail<L, PM>(P, q, e, sq);
   return e;
+}
+
+// The lane's 16 codes packed as the bitstream stores them (LSB first): 2 bits in w[0],
+// 4 bits in w[0..1], 8 bits in w[0..3], 3 bits as two 24-bit fields in w[0..1].
+// Sum_k q_k 2^(nbits k) over up to 24 bits is an exact fp32 integer, so the fields are
+// assembled with FMAs and converted once.
+struct PackedCodes {
+  uint32_t w[4];
+};
+
+// The two words of 2-, 3- or 4-bit codes.
+__device__ __forceinline__ uint2 pack_codes_narrow(int nbits, const float (&q)[kLaneElems]) {
+  auto horner = [&](int k0, int n, float radix) {
+    float acc = q[k0 + n - 1];
+#pragma unroll
+    for (int k = n - 2; k >= 0; --k) acc = __builtin_fmaf(acc, radix, q[k0 + k]);
+    return (uint32_t)acc;
+  };
+  switch (nbits) {
+    case 4:
+      return make_uint2(horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16),
+                        horner(8, 4, 16.f) | (horner(12, 4, 16.f) << 16));
+    case 2:
+      return make_uint2(horner(0, 8, 4.f) | (horner(8, 8, 4.f) << 16), 0u);
+    default:  // 3 bits
+      return make_uint2(horner(0, 8, 8.f), horner(8, 8, 8.f));
+  }
+}
+
+__device__ __forceinline__ PackedCodes pack_codes(int nbits, const float (&q)[kLaneElems]) {
+  PackedCodes c = {{0u, 0u, 0u, 0u}};
+  if (nbits == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) c.w[w] = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * w + k], (uint32_t)k, c.w[w]);
+  } else {
+    const uint2 n = pack_codes_narrow(nbits, q);
+    c.w[0] = n.x;
+    c.w[1] = n.y;
+  }
+  return c;
+}
+
+// Stores the lane's packed codes; chunk = index of the lane's 16 elements.
+__device__ __forceinline__ void store_codes(const SolveParams& P, int64_t chunk, const PackedCodes& c) {
+  switch (P.nbits) {
+    case 4: {  // 16 codes = 8 bytes, as two 4-byte words (the stream is 4-byte aligned)
+      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 2 * chunk;
+      dst[0] = c.w[0];
+      dst[1] = c.w[1];
+      break;
+    }
+    case 2:  // 4 bytes
+      reinterpret_cast<uint32_t*>(P.packed)[chunk] = c.w[0];
+      break;
+    case 8: {  // 16 bytes, as four 4-byte words
+      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 4 * chunk;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) dst[w] = c.w[w];
+      break;
+    }
+    default: {  // 3 bits: 16 codes = 48 bits = 6 bytes, 2-byte aligned
+      uint16_t* dst = reinterpret_cast<uint16_t*>(P.packed + chunk * 6);
+      dst[0] = (uint16_t)c.w[0];
+      dst[1] = (uint16_t)((c.w[0] >> 16) | (c.w[1] << 8));
+      dst[2] = (uint16_t)(c.w[1] >> 8);
+      break;
+    }
+  }
+}
+
+// The evaluation at t = 0 in the per-group kernel (delta = 0, x = u, no clamp): error and
+// code sum as eval_group, the codes packed for storing (2, 3 and 4 bits; nothing for 8),
+// and whether some u of the lane is exactly a half-integer (|u - rint(u)| = 1/2;
+// u - rint(u) is exact), i.e. needs settle_ties.
+template <int L, int PM>
+__device__ __forceinline__ bool eval_first(const float (&u)[kLaneElems], int nbits, float p,
+                                           float& e, float& sq, uint2& pk) {
+  float a[kLaneElems], q[kLaneElems], r[kLaneElems];
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    q[k] = __builtin_rintf(u[k]);
+    r[k] = __builtin_fabsf(u[k] - q[k]);
+    a[k] = pow_p<PM>(u[k] - q[k], p);
+  }
+  e = seg_sum<L>(tree_sum<0, kLaneElems>(a));
+  sq = seg_sum<L>(tree_sum<0, kLaneElems>(q));
+  if (nbits != 8) pk = pack_codes_narrow(nbits, q);
+  // max |rc| over the 16 elements (three-operand max instructions)
+  float m = __builtin_fmaxf(__builtin_fmaxf(r[0], r[1]), r[2]);
+#pragma unroll
+  for (int k = 3; k + 1 < kLaneElems; k += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, r[k]), r[k + 1]);
+  m = __builtin_fmaxf(m, r[kLaneElems - 1]);
+  return m == 0.5f;
+}
+
+// The group's binary16 s and z (plus the optional fp32, stop-step and error outputs),
+// written by lane 0 of the segment (sl == 0).
+template <int PM>
+__device__ __forceinline__ void write_meta(const SolveParams& P, int64_t gi, float gs, float best_z,
+                                           float e0, float best_e, int t_star) {
+  P.scale16[gi] = float_to_half_bits(gs);
+  P.zero16[gi] = float_to_half_bits(best_z);
+  if (P.scale32) P.scale32[gi] = gs;
+  if (P.zero32) P.zero32[gi] = best_z;
+  if (P.stop_step) P.stop_step[gi] = (uint8_t)t_star;
+  if (P.err_init || P.err_best) {
+    const float sp = scalar_pow<PM>(gs, P.p);
+    if (P.err_init) P.err_init[gi] = e0 * sp;
+    if (P.err_best) P.err_best[gi] = best_e * sp;
+  }
 }
 
 // Codes at the accepted z, packed into the LSB-first bitstream, and the group's
@@ -452,71 +591,17 @@ __device__ __forceinline__ void write_group(const SolveParams& P, int sl,
     q[k] = __builtin_rintf(ZERO ? u[k] : u[k] + bd);
     if (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
   }
-  // Packing: sum_k q_k 2^(nbits k) over up to 24 bits is an exact fp32 integer, so the
-  // fields are assembled with FMAs and converted once.
-  auto horner = [&](int k0, int n, float radix) {
-    float acc = q[k0 + n - 1];
-#pragma unroll
-    for (int k = n - 2; k >= 0; --k) acc = __builtin_fmaf(acc, radix, q[k0 + k]);
-    return (uint32_t)acc;
-  };
-  const int64_t chunk = gi * L + sl;  // index of this lane's 16 elements
-  switch (P.nbits) {
-    case 4: {  // 16 codes = 8 bytes, as two 4-byte words (the stream is 4-byte aligned)
-      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 2 * chunk;
-      dst[0] = horner(0, 4, 16.f) | (horner(4, 4, 16.f) << 16);
-      dst[1] = horner(8, 4, 16.f) | (horner(12, 4, 16.f) << 16);
-      break;
-    }
-    case 2: {  // 4 bytes
-      reinterpret_cast<uint32_t*>(P.packed)[chunk] = horner(0, 8, 4.f) | (horner(8, 8, 4.f) << 16);
-      break;
-    }
-    case 8: {  // 16 bytes, as four 4-byte words
-      uint32_t v[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) v[w] = __builtin_amdgcn_cvt_pk_u8_f32(q[4 * w + k], (uint32_t)k, v[w]);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(P.packed) + 4 * chunk;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) dst[w] = v[w];
-      break;
-    }
-    default: {  // 3 bits: 16 codes = 48 bits = 6 bytes, 2-byte aligned
-      const uint32_t a = horner(0, 8, 8.f), b = horner(8, 8, 8.f);  // 24 bits each
-      uint16_t* dst = reinterpret_cast<uint16_t*>(P.packed + chunk * 6);
-      dst[0] = (uint16_t)a;
-      dst[1] = (uint16_t)((a >> 16) | (b << 8));
-      dst[2] = (uint16_t)(b >> 8);
-      break;
-    }
-  }
-  if (sl == 0) {
-    const float best_z = z0 + bd;
-    P.scale16[gi] = float_to_half_bits(gs);
-    P.zero16[gi] = float_to_half_bits(best_z);
-    if (P.scale32) P.scale32[gi] = gs;
-    if (P.zero32) P.zero32[gi] = best_z;
-    if (P.stop_step) P.stop_step[gi] = (uint8_t)t_star;
-    if (P.err_init || P.err_best) {
-      const float sp = scalar_pow<PM>(gs, P.p);
-      if (P.err_init) P.err_init[gi] = e0 * sp;
-      if (P.err_best) P.err_best[gi] = best_e * sp;
-    }
-  }
+  store_codes(P, gi * L + sl, pack_codes(P.nbits, q));
+  if (sl == 0) write_meta<PM>(P, gi, gs, z0 + bd, e0, best_e, t_star);
 }
 
-// write_group with the clamp only where some written group of the wave needs it;
-// TRY_ZERO adds the shortcut for bd == 0 in every written group.
-template <int L, int PM, bool TRY_ZERO = false>
+// write_group with the clamp only where some written group of the wave needs it.
+template <int L, int PM>
 __device__ __forceinline__ void write_group_any(const SolveParams& P, bool write, int sl,
                                                 const float (&u)[kLaneElems], int64_t gi, float gs,
                                                 float z0, float bd, float e0, float best_e,
                                                 int t_star) {
-  if (TRY_ZERO && ballot(write && bd != 0.f) == 0) {
-    if (write) write_group<L, PM, false, true>(P, sl, u, gi, gs, z0, 0.f, e0, best_e, t_star);
-  } else if (ballot(write && far_delta(bd)) != 0) {
+  if (ballot(write && far_delta(bd)) != 0) {
     if (write) write_group<L, PM, true>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
   } else {
     if (write) write_group<L, PM, false>(P, sl, u, gi, gs, z0, bd, e0, best_e, t_star);
