@@ -217,16 +217,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     }
     prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
     if (a.active) step_tail<L, PM>(P, a, e, sq);
+    // t = 1, with the codes packed as well
+    uint2 pk1 = make_uint2(0u, 0u);
     if (ballot(a.active) != 0) {
-      const bool clamp = ballot(needs_clamp(a)) != 0;
-      if (a.active) solver_step<L, PM>(P, a, clamp);
+      if (ballot(needs_clamp(a)) != 0) {
+        if (a.active) eval_group<L, PM, true, false, true>(a.u, a.delta, P.qmax, P.p, e, sq, P.nbits, &pk1);
+      } else {
+        if (a.active) eval_group<L, PM, false, false, true>(a.u, a.delta, P.qmax, P.p, e, sq, P.nbits, &pk1);
+      }
+      if (a.active) step_tail<L, PM>(P, a, e, sq);
     }
-    // Groups stopping here have t* = 0 (they stopped at t = 1) unless iters == 1: their
-    // codes are the packed rint(u) of the first evaluation (8-bit codes are rounded again).
-    if (P.nbits != 8 && ballot(a.pending && a.best_delta != 0.f) == 0) {
+    // Groups stopping here have t* = 0 or 1: their codes are those of the first or the
+    // second evaluation, already packed (8-bit codes are rounded again).  The clamp the
+    // second evaluation applied or skipped gives the codes write_group gives at that z
+    // (skipping it is exact for |delta| < 1/2).
+    if (P.nbits != 8) {
       if (a.pending) {
-        store_codes(P, a.gidx * L + sl, PackedCodes{{pk0.x, pk0.y, 0u, 0u}});
-        if (sl == 0) write_meta<PM>(P, a.gidx, a.s, a.z0 + 0.f, a.e0, a.best_e, a.t_star);
+        const uint2 pk = a.t_star == 0 ? pk0 : pk1;
+        store_codes(P, a.gidx * L + sl, PackedCodes{{pk.x, pk.y, 0u, 0u}});
+        if (sl == 0) write_meta<PM>(P, a.gidx, a.s, a.z0 + a.best_delta, a.e0, a.best_e, a.t_star);
       }
     } else {
       write_group_any<L, PM>(P, a.pending, sl, a.u, a.gidx, a.s, a.z0, a.best_delta, a.e0,
@@ -291,13 +300,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     wave_lds_sync();
   };
 
-  // One pass per solver step of the iterating set.  A pass hands stopped groups to
-  // the done ring, writes full done batches, primes a batch when segments are idle
-  // and the pool is empty, and gives idle segments standby groups.
+  // Each round of the loop runs one pass of the iterating set (a solver step of every
+  // segment's group) once every segment holds a group, or when nothing is left to feed
+  // the idle ones; otherwise it primes a batch (the pool is empty) and gives idle
+  // segments standby groups first, so that passes run on full wavefronts.  A pass hands
+  // stopped groups to the done ring and writes full done batches.  Every round makes
+  // progress: it runs a pass, or primes (the queue advances), or hands out standby groups.
   while (true) {
     const bool any_active = ballot(sg.active) != 0;
-    if (!any_active && n_standby == 0 && next >= q_end) break;
-    if (any_active) {
+    const bool feed = n_standby > 0 || next < q_end;  // groups left for idle segments
+    if (!any_active && !feed) break;
+    const bool full = __builtin_popcountll(ballot(sg.active || sg.pending)) == kWave;
+    if (any_active && (full || !feed)) {
       const bool clamp = ballot(needs_clamp(sg)) != 0;
       if (sg.active) solver_step<L, PM>(P, sg, clamp);
     }

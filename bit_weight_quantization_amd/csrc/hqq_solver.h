@@ -358,111 +358,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// One evaluation of the lane's 16 weights at x = u + delta: the segment's lp error
-// (code units) and code sum.  CLAMP = false is the exact shortcut for |delta| < 1/2.
-template <int L, int PM, bool CLAMP, bool ZERO = false>
-__device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float delta, float qmax,
-                                           float p, float& e, float& sq) {
-  float a[kLaneElems], q[kLaneElems];
-#pragma unroll
-  for (int k = 0; k < kLaneElems; ++k) {
-    const float x = ZERO ? u[k] : u[k] + delta;  // ZERO: delta == 0 (x = u + 0 = u exactly)
-    q[k] = __builtin_rintf(x);
-    if constexpr (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
-    a[k] = pow_p<PM>(x - q[k], p);
-  }
-  e = seg_sum<L>(tree_sum<0, kLaneElems>(a));
-  sq = seg_sum<L>(tree_sum<0, kLaneElems>(q));  // exact: a sum of small integers
-}
-
-// State of one group held by a segment (identical in all L lanes of the segment).
-struct Slot {
-  float u[kLaneElems];  // this lane's code-unit values
-  float s, inv_s, z0, usum;
-  float delta, best_delta, best_e, e0;
-  int t, t_star;
-  int64_t gidx;
-  bool may_shrink;
-  bool active;   // iterating
-  bool pending;  // stopped, outputs not yet written or handed to the done ring
-};
-
-// Clamping is a no-op while |delta| < 1/2: u lies in [0, qmax], so x = u + delta
-// stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
-__device__ __forceinline__ bool far_delta(float delta) { return !(__builtin_fabsf(delta) < 0.4999f); }
-__device__ __forceinline__ bool needs_clamp(const Slot& q) { return q.active && far_delta(q.delta); }
-
-// What a solver step does after its evaluation (error e, code sum sq): the early-stop
-// test of section 4.1, and unless the group stops, the sp1 shrink (only where it can be
-// non-zero) and the sp2 mean.
-template <int L, int PM>
-__device__ __forceinline__ void step_tail(const SolveParams& P, Slot& q, float e, float sq) {
-  constexpr float kInvG = 1.0f / (float)(L * kLaneElems);
-  const float qmax = P.qmax;
-  if (P.err_init && q.t == 0) q.e0 = e;
-  const bool accept = !P.early_stop || (e < q.best_e);
-  if (accept) {
-    q.best_e = e;
-    q.best_delta = q.delta;
-    q.t_star = q.t;
-  }
-  if (!accept || q.t == P.iters) {
-    q.active = false;
-    q.pending = true;
-    return;
-  }
-  float num = sq - q.usum;
-  if (ballot(q.may_shrink) != 0) {
-    // beta_t^(-1/(2-p)) and 1/beta_t, from t
-    const float tf = (float)q.t;
-    const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
-    const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(q.delta)) + 1e-5f * (qmax + 1.f);
-    const bool need = q.may_shrink && bound >= tau * q.inv_s * (1.0f - 1e-4f);
-    if (ballot(need) != 0) {
-      if (need) {
-        float cs;  // s^(p-2)
-        if constexpr (shrink_mode(PM) == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
-        else if constexpr (shrink_mode(PM) == kPowOne) cs = q.inv_s;
-        else cs = q.inv_s * q.inv_s;
-        const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
-        const float ib = cs * inv_beta;  // s^(p-2) / beta_t
-        float we[kLaneElems];  // W_e / s
-#pragma unroll
-        for (int k = 0; k < kLaneElems; ++k) {
-          const float x = q.u[k] + q.delta;
-          const float qc = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
-          const float rc = x - qc;
-          const float a = __builtin_fabsf(rc);
-          float m = 0.f;
-          if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
-          we[k] = __builtin_copysignf(m, rc);
-        }
-        num += seg_sum<L>(tree_sum<0, kLaneElems>(we));
-      }
-    }
-  }
-  q.delta = num * kInvG;
-  ++q.t;
-}
-
-// One step of the solver for an active group: evaluation at the current z (codes,
-// residual, lp error), then step_tail.  FIRST: the step at t = 0 (delta = 0, no clamp
-// needed).  Returns the evaluated error (code units).
-template <int L, int PM, bool FIRST = false>
-__device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool clamp) {
-  const float qmax = P.qmax;
-  float e, sq;
-  if constexpr (FIRST) {
-    eval_group<L, PM, false, true>(q.u, 0.f, qmax, P.p, e, sq);
-  } else if (clamp) {
-    eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
-  } else {
-    eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
-  }
-  step_tail<L, PM>(P, q, e, sq);
-  return e;
-}
-
 // The lane's 16 codes packed as the bitstream stores them (LSB first): 2 bits in w[0],
 // 4 bits in w[0..1], 8 bits in w[0..3], 3 bits as two 24-bit fields in w[0..1].
 // Sum_k q_k 2^(nbits k) over up to 24 bits is an exact fp32 integer, so the fields are
@@ -531,6 +426,126 @@ __device__ __forceinline__ void store_codes(const SolveParams& P, int64_t chunk,
       break;
     }
   }
+}
+
+// One evaluation of the lane's 16 weights at x = u + delta: the segment's lp error
+// (code units) and code sum.  CLAMP = false is the exact shortcut for |delta| < 1/2.
+// PACK: also the codes packed as stored (2, 3 and 4 bits; nothing for 8).
+template <int L, int PM, bool CLAMP, bool ZERO = false, bool PACK = false>
+__device__ __forceinline__ void eval_group(const float (&u)[kLaneElems], float delta, float qmax,
+                                           float p, float& e, float& sq, int nbits = 0,
+                                           uint2* pk = nullptr) {
+  float a[kLaneElems], q[kLaneElems];
+#pragma unroll
+  for (int k = 0; k < kLaneElems; ++k) {
+    const float x = ZERO ? u[k] : u[k] + delta;  // ZERO: delta == 0 (x = u + 0 = u exactly)
+    q[k] = __builtin_rintf(x);
+    if constexpr (CLAMP) q[k] = __builtin_amdgcn_fmed3f(q[k], 0.f, qmax);
+    a[k] = pow_p<PM>(x - q[k], p);
+  }
+  e = seg_sum<L>(tree_sum<0, kLaneElems>(a));
+  sq = seg_sum<L>(tree_sum<0, kLaneElems>(q));  // exact: a sum of small integers
+  if constexpr (PACK) {
+    if (nbits != 8) *pk = pack_codes_narrow(nbits, q);
+  }
+}
+
+// State of one group held by a segment (identical in all L lanes of the segment).
+struct Slot {
+  float u[kLaneElems];  // this lane's code-unit values
+  float s, inv_s, z0, usum;
+  float delta, best_delta, best_e, e0;
+  int t, t_star;
+  int64_t gidx;
+  bool may_shrink;
+  bool active;   // iterating
+  bool pending;  // stopped, outputs not yet written or handed to the done ring
+};
+
+// Clamping is a no-op while |delta| < 1/2: u lies in [0, qmax], so x = u + delta
+// stays inside (-1/2, qmax + 1/2) and rounds into [0, qmax].
+__device__ __forceinline__ bool far_delta(float delta) { return !(__builtin_fabsf(delta) < 0.4999f); }
+__device__ __forceinline__ bool needs_clamp(const Slot& q) { return q.active && far_delta(q.delta); }
+
+// What a solver step does after its evaluation (error e, code sum sq): the early-stop
+// test of section 4.1, and unless the group stops, the sp1 shrink (only where it can be
+// non-zero) and the sp2 mean.
+template <int L, int PM>
+__device__ __forceinline__ void step_tail(const SolveParams& P, Slot& q, float e, float sq) {
+  constexpr float kInvG = 1.0f / (float)(L * kLaneElems);
+  const float qmax = P.qmax;
+  if (P.err_init && q.t == 0) q.e0 = e;
+  const bool accept = !P.early_stop || (e < q.best_e);
+  if (accept) {
+    q.best_e = e;
+    q.best_delta = q.delta;
+    q.t_star = q.t;
+  }
+  if (!accept || q.t == P.iters) {
+    q.active = false;
+    q.pending = true;
+    return;
+  }
+  float num = sq - q.usum;
+  if (ballot(q.may_shrink) != 0) {
+    // beta_t^(-1/(2-p)) and 1/beta_t, from t
+    const float tf = (float)q.t;
+    const float tau = P.tau0 * exp2_hw(tf * P.log2_rho);
+    const float bound = __builtin_fmaxf(0.5f, __builtin_fabsf(q.delta)) + 1e-5f * (qmax + 1.f);
+    const bool need = q.may_shrink && bound >= tau * q.inv_s * (1.0f - 1e-4f);
+    if (ballot(need) != 0) {
+      if (need) {
+        float cs;  // s^(p-2)
+        if constexpr (shrink_mode(PM) == kPowGeneral) cs = exp2_hw(P.pm2 * log2_hw(q.s));
+        else if constexpr (shrink_mode(PM) == kPowOne) cs = q.inv_s;
+        else cs = q.inv_s * q.inv_s;
+        const float inv_beta = P.inv_beta0 * exp2_hw(-tf * P.log2_kappa);
+        const float ib = cs * inv_beta;  // s^(p-2) / beta_t
+        float we[kLaneElems];  // W_e / s
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k) {
+          const float x = q.u[k] + q.delta;
+          const float qc = __builtin_amdgcn_fmed3f(__builtin_rintf(x), 0.f, qmax);
+          const float rc = x - qc;
+          const float a = __builtin_fabsf(rc);
+          float m = 0.f;
+          if (a > 0.f) m = __builtin_fmaxf(__builtin_fmaf(-pow_pm1<PM>(a, P.pm1), ib, a), 0.f);
+          we[k] = __builtin_copysignf(m, rc);
+        }
+        num += seg_sum<L>(tree_sum<0, kLaneElems>(we));
+      }
+    }
+  }
+  const float next = num * kInvG;
+  // With the per-group stop, a z update that leaves delta bit for bit unchanged makes the
+  // next evaluation repeat this one (same x, codes, error and order of sums), so that
+  // step cannot improve and the group stops there with this step as its best: stop now,
+  // with the state that evaluation would have left.
+  if (P.early_stop && fbits(next) == fbits(q.delta)) {
+    q.active = false;
+    q.pending = true;
+    return;
+  }
+  q.delta = next;
+  ++q.t;
+}
+
+// One step of the solver for an active group: evaluation at the current z (codes,
+// residual, lp error), then step_tail.  FIRST: the step at t = 0 (delta = 0, no clamp
+// needed).  Returns the evaluated error (code units).
+template <int L, int PM, bool FIRST = false>
+__device__ __forceinline__ float solver_step(const SolveParams& P, Slot& q, bool clamp) {
+  const float qmax = P.qmax;
+  float e, sq;
+  if constexpr (FIRST) {
+    eval_group<L, PM, false, true>(q.u, 0.f, qmax, P.p, e, sq);
+  } else if (clamp) {
+    eval_group<L, PM, true>(q.u, q.delta, qmax, P.p, e, sq);
+  } else {
+    eval_group<L, PM, false>(q.u, q.delta, qmax, P.p, e, sq);
+  }
+  step_tail<L, PM>(P, q, e, sq);
+  return e;
 }
 
 // The evaluation at t = 0 in the per-group kernel (delta = 0, x = u, no clamp): error and
