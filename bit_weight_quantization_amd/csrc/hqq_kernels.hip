@@ -68,15 +68,18 @@ template <int G>
 struct SolveLds {
   static constexpr int S = kWave * kLaneElems / G;
   static constexpr int L = G / kLaneElems;
-  // Wavefronts per SIMD the kernel is compiled for (the VGPR budget).  A wavefront
-  // holds 1024 weights, so its LDS share is S(2G + 20) words, 35 KB (G = 128) to 53 KB
-  // (G = 16) per block of four wavefronts: three blocks per CU fit in its 160 KB at
-  // G = 16 and 32, four at G = 64 and 128 (measured: the fourth wavefront per SIMD is
-  // worth more than a deeper pool).
-  static constexpr int kWavesPerSimd = G <= 32 ? 3 : 4;
+  // Wavefronts per SIMD the kernel is compiled for (the VGPR budget: 128 registers).
+  // A wavefront holds 1024 weights; its LDS share is the pool (S slots, 12-word header)
+  // and the done ring (kDone slots, 8-word header) of G code-unit values each.  With a
+  // ring of S slots at G = 16 and 32 only three blocks of four wavefronts would fit in a
+  // CU's 160 KB, so there the ring has S/2 slots (40 KB per block at G = 16, 32 KB at
+  // G = 32; 37 KB at G = 64, 35 KB at G = 128 with S slots): four blocks per CU at every
+  // group size (measured: the fourth wavefront per SIMD is worth more than a deeper pool
+  // or ring).  A hand-over larger than the ring is written straight from registers.
+  static constexpr int kWavesPerSimd = 4;
   // A prime batch adds up to S groups to the pool, a hand-over up to S to the ring.
   static constexpr int kStandby = S;
-  static constexpr int kDone = S;
+  static constexpr int kDone = G <= 32 ? S / 2 : S;
   static constexpr int kSlots = kStandby + kDone;
   float4 u[kWavesPerBlock][kLaneElems / 4][kSlots * L];
   uint4 standby_hdr[kWavesPerBlock][kStandby][3];
@@ -174,6 +177,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     Slot a;
     a.active = a.pending = false;
     uint32_t nm_mx = 0u;
+    const BatchCursor entry = cursor;  // the entry holding this batch (wave-uniform)
     if (seg < n) {
       a.gidx = next + seg;
       const GroupInit gq = init_group<L, false>(P, prefetch, a.u);
@@ -197,17 +201,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     if constexpr (BATCH) {
       if (next < q_end) batch_advance(P, cursor, next);
     }
+    prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
     // t = 0: delta = 0, no clamp needed.  The evaluation also packs the codes rint(u)
     // (the output of every group that stops at t = 1) and finds u lying exactly on a
-    // half-integer; those are settled from the raw weights (still in `prefetch`), and if
-    // one moved the wave recomputes the sums and the evaluation.
+    // half-integer; those are settled from the raw weights (read again: the lane's two
+    // chunks, from the batch's entry), and if one moved the wave recomputes the sums and
+    // the evaluation.
     float e = 0.f, sq = 0.f;
     uint2 pk0 = make_uint2(0u, 0u);
     bool tie = false;
     if (a.active) tie = eval_first<L, PM>(a.u, P.nbits, P.p, e, sq, pk0);
     if (ballot(tie) != 0) {
       bool moved = false;
-      if (tie) moved = settle_ties(prefetch, nm_mx, P.qmax, a.u);
+      if (tie) {
+        const uint4* wp = BATCH ? entry.W + 2 * ((a.gidx - entry.first) * L + sl)
+                                : P.W + 2 * (a.gidx * L + sl);
+        moved = settle_ties(LaneW{wp[0], wp[1]}, nm_mx, P.qmax, a.u);
+      }
       if (ballot(moved) != 0) {
         if (a.active) {
           a.usum = seg_sum<L>(tree_sum<0, kLaneElems>(a.u));
@@ -215,7 +225,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
         }
       }
     }
-    prefetch = fetch_chunk<L, BATCH>(P, cursor, next + seg, q_end, sl);
     if (a.active) step_tail<L, PM>(P, a, e, sq);
     // t = 1, with the codes packed as well
     uint2 pk1 = make_uint2(0u, 0u);
@@ -321,7 +330,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     const int npend = __builtin_popcountll(pm) / L;
     if (npend > 0 && (npend >= P.refill_at || ballot(sg.active) == 0)) {
       if (done_count + npend > kDone) finalize(done_count);  // rare: make room first
-      if (sg.pending) {
+      if (npend > kDone) {  // more than the ring holds: written straight from registers
+        write_group_any<L, PM>(P, sg.pending, sl, sg.u, sg.gidx, sg.s, sg.z0, sg.best_delta, sg.e0,
+                               sg.best_e, sg.t_star);
+      } else if (sg.pending) {
         const int rank = lanes_below(pm) / L;
         const int slot = kStandby + (int)((unsigned)(done_head + done_count + rank) % (unsigned)kDone);
         store_u<G>(U, slot, sl, sg.u);
@@ -332,10 +344,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
                                       (uint32_t)sg.t_star);
         }
       }
-      done_count = uniform(done_count + npend);
+      if (npend <= kDone) done_count = uniform(done_count + npend);
       sg.pending = false;
       wave_lds_sync();
-      if (done_count >= S) finalize(S);
+      if (done_count >= kDone) finalize(kDone);
     }
 
     // ---- keep the pool stocked (a batch adds at most S), feed idle segments ------
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds
     const bool idle = !sg.active && !sg.pending;
     if (n_standby > 0 && ballot(idle) != 0) take_standby(idle);
   }
-  while (done_count > 0) finalize(done_count < S ? done_count : S);
+  while (done_count > 0) finalize(done_count < kDone ? done_count : kDone);
 }
 
 // ---------------------------------------------------------------- dequant --
