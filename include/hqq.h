@@ -72,7 +72,7 @@ typedef struct {
   float* err_init;     /* e_0 = sum |W - Q^-1(Q(W))|^p at the initial z */
   float* err_best;     /* e_{t*}, the error at the returned z */
   int refill_threshold; /* performance knob, no effect on any output: a wavefront
-                           iterates 64*8/group_size groups at a time and hands stopped
+                           iterates 64*16/group_size groups at a time and hands stopped
                            groups over (replacing them from its standby pool) once this
                            many have stopped.  0 = default (1); values above the slot
                            count are clamped; < 0 invalid. */

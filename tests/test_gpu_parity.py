@@ -344,6 +344,24 @@ def test_plain_entry_point_equals_debug_entry_point_and_is_deterministic(hq):
     assert torch.equal(top.zero.view(torch.int16), a.zero[:100].view(torch.int16))
 
 
+@pytest.mark.parametrize("nbits,g", [(2, 16), (2, 32), (4, 64)])
+def test_refill_threshold_changes_no_output(hq, nbits, g):
+    """The hand-over threshold only changes the schedule.  A high threshold lets up to
+    every segment of a wavefront stop before the hand-over, more than the done ring holds
+    at g <= 32 (those groups are written straight from registers), and the result must be
+    bit-identical to the default schedule."""
+    _say(f"refill thresholds, b{nbits} g{g}")
+    W = workloads.generate_matrix(workloads.WORKLOADS["attn_4096x4096"], 0, "cuda")
+    ref = hq.quantize(W, nbits, g)
+    slots = 64 * 16 // g
+    for thr in (2, 5, slots // 2 + 1, slots):
+        q = hq.quantize(W, nbits, g, refill_threshold=thr)
+        torch.cuda.synchronize()
+        assert torch.equal(q.packed, ref.packed), thr
+        assert torch.equal(q.scale.view(torch.int16), ref.scale.view(torch.int16)), thr
+        assert torch.equal(q.zero.view(torch.int16), ref.zero.view(torch.int16)), thr
+
+
 def test_empty_input(hq):
     W = torch.empty((0, 64), dtype=torch.float16, device="cuda")
     q = hq.quantize(W, 4, 64)
