@@ -432,8 +432,9 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 }
 
 // Persistent grid: as many blocks as can be resident at once (LDS and VGPRs set the
-// limit), or fewer for small inputs; the wavefronts deal the chunks round robin.
-constexpr int kChunkBatches = 4;  // chunk = 4 prime batches
+// limit), or fewer for small inputs; the wavefronts deal the chunks round robin.  A chunk
+// is 4 prime batches, or one when that leaves wavefronts without a chunk.
+constexpr int kChunkBatches = 4;
 
 template <int G, int PM>
 struct SolveLaunch {
@@ -447,7 +448,11 @@ struct SolveLaunch {
     if (err != hipSuccess) return err;
     constexpr int S = kWave * kLaneElems / G;
     prm.chunk_groups = kChunkBatches * S;
-    const int64_t nchunks = (prm.ngroups + prm.chunk_groups - 1) / prm.chunk_groups;
+    int64_t nchunks = (prm.ngroups + prm.chunk_groups - 1) / prm.chunk_groups;
+    if (nchunks < resident) {  // small input: one prime batch per chunk spreads it wider
+      prm.chunk_groups = S;
+      nchunks = (prm.ngroups + S - 1) / S;
+    }
     const int64_t nwaves = nchunks < resident ? nchunks : resident;
     const int64_t blocks = (nwaves + kWavesPerBlock - 1) / kWavesPerBlock;
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, prm);
