@@ -433,7 +433,9 @@ __global__ __launch_bounds__(kBlock) void hqq_dequant_kernel(const DequantParams
 
 // Persistent grid: as many blocks as can be resident at once (LDS and VGPRs set the
 // limit), or fewer for small inputs; the wavefronts deal the chunks round robin.  A chunk
-// is 4 prime batches, or one when that leaves wavefronts without a chunk.
+// is 4 consecutive prime batches (measured faster than single batches once there are
+// about 3 chunks per wavefront), or one when 4 would give fewer than 2 chunks per
+// wavefront, so that a small input spreads over more wavefronts.
 constexpr int kChunkBatches = 4;
 
 template <int G, int PM>
@@ -449,7 +451,7 @@ struct SolveLaunch {
     constexpr int S = kWave * kLaneElems / G;
     prm.chunk_groups = kChunkBatches * S;
     int64_t nchunks = (prm.ngroups + prm.chunk_groups - 1) / prm.chunk_groups;
-    if (nchunks < resident) {  // small input: one prime batch per chunk spreads it wider
+    if (nchunks < 2 * resident) {  // one prime batch per chunk: wider spread, finer balance
       prm.chunk_groups = S;
       nchunks = (prm.ngroups + S - 1) / S;
     }
