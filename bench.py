@@ -93,6 +93,36 @@ def traffic_from_profile(weights_per_launch: float):
     return round(prof["hbm_bytes_per_weight"] * weights_per_launch)
 
 
+def issued_valu_from_profile(n_weights: float, settings, step_s: float):
+    """The VALU work the solver kernels actually issue, from the committed rocprofv3 PMC
+    summary (VALU wave-instructions per launch of the 8-layer batch, each transcendental
+    priced at 4 full-rate slots, x 64 lanes, per weight), scaled to the timed launches and
+    set against their measured time: the raw VALU issue fraction beside the op-model
+    fractions.  None if the summary is absent or was taken on another kernel source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    with open(PROFILE_PMC) as f:
+        prof = json.load(f)
+    if prof.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if prof.get("workload") != "llama70b_stack":
+        return None
+    slots = 0.0
+    for _, g in settings:
+        sq = prof.get("sq", {}).get(f"hqq_solve_kernel<{g}>")
+        if not sq:
+            return None
+        per_weight = (sq["valu_wave_instr_per_launch"] + 3.0 * sq["trans_wave_instr_per_launch"]) \
+            * 64 / prof["weights_per_launch"]
+        slots += per_weight * n_weights
+    achieved = slots / step_s
+    return {"slots_per_weight": round(slots / (n_weights * len(settings)), 2),
+            "achieved": round(achieved / 1e12, 3), "frac": round(achieved / PEAK_VALU_SLOTS, 4),
+            "count": "issued VALU wave-instructions x 64 lanes, a transcendental as 4 full-rate "
+                     "slots (counters of the committed profile, same kernel source), over the "
+                     "timed launches"}
+
+
 def _kernel_key(name: str):
     for g in (16, 32, 64, 128):
         if f"hqq_solve_kernel<{g}," in name:
@@ -1316,6 +1346,7 @@ def main():
         configs, config_inputs = measure_configs(hq, lib, torch, dev, stream, sh, tau)
     bytes_step = sum(n_weights * (2 + nb / 8 + 4 / g) for nb, g in settings)
     traffic = traffic_from_profile(n_weights * len(settings) / launches_per_step)
+    issued = issued_valu_from_profile(n_weights, settings, total_ms * 1e-3 / args.steps)
 
     # ---- next row: 8-bit meta quantization of the solver's s and z (untimed above) -------
     meta = None
@@ -1485,6 +1516,7 @@ def main():
                 "ops_per_launch": round(ops_step / launches_per_step),
                 "achieved": round(achieved / 1e12, 3),
                 "frac": round(achieved / PEAK_VALU_SLOTS, 4)},
+            "issued_valu": issued,
             "peaks_measured": peaks,
         },
         "per_setting": detail,
