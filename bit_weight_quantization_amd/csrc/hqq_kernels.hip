@@ -43,9 +43,14 @@
 //     batches) and writes the groups that stopped at once (about 60% of them on
 //     heavy-tailed weights).  The others wait in an LDS standby pool; each segment
 //     of the wave iterates one of them, and a segment whose group stopped copies
-//     its u values and header into an LDS done ring and takes a standby group in
-//     the same pass.  Done groups are packed and written in dense batches of S.
-//     Every group runs exactly the same instruction sequence whatever its batch or
+//     its u values and header into an LDS done ring and takes a standby group.
+//     Done groups are packed and written in dense batches.  A pass of the
+//     iterating set runs once every segment holds a group (or nothing is left to
+//     feed), so passes run on full wavefronts;
+//   * a z update that leaves delta bit for bit unchanged would make the next
+//     evaluation repeat the last one, which cannot improve: the group stops there
+//     without evaluating it (same outputs);
+//   * every group runs exactly the same instruction sequence whatever its batch or
 //     slot, so results do not depend on the schedule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -112,10 +117,10 @@ __device__ __forceinline__ void load_u(UPlanes<G> U, int slot, int sl, float (&u
 // runs them densely for S fresh groups at a time ("prime" batches): init and two
 // solver steps in every segment.  Groups that stopped are written at once; the
 // others wait in the standby pool for a segment of the iterating set.  Iterating
-// segments whose group stops hand it to the done ring and take a standby group in
-// the same pass; done groups are written in dense batches of S.  Every group runs
-// exactly the same instruction sequence whatever its batch or slot, so results do
-// not depend on the schedule.
+// segments whose group stops hand it to the done ring and take a standby group;
+// done groups are written in dense batches.  Every group runs exactly the same
+// instruction sequence whatever its batch or slot, so results do not depend on the
+// schedule.
 template <int G, int PM, bool BATCH>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SolveLds<G>::kWavesPerSimd))) void hqq_solve_kernel(const SolveParams P) {
   constexpr int L = G / kLaneElems;  // lanes per group
