@@ -385,6 +385,34 @@ def test_early_stop_invariants_on_layer_like_groups():
                         assert r.n_eval == 21
 
 
+def test_unchanged_zero_point_repeats_the_error():
+    """The error of an evaluation depends on z alone, so a z update that leaves z unchanged
+    repeats the last error: under the strict-improvement stop that step is rejected and
+    the group ends with the last accepted z (which the device uses to stop such a group
+    without evaluating the repeat).  Checked on the no-stop trajectory: wherever z after
+    t + 1 updates equals z after t updates, error t + 1 equals error t exactly; and the
+    early-stop run then stops at the first such repeat (if not earlier)."""
+    wl = workloads.WORKLOADS["llama70b_stack"]
+    W = workloads.generate(16, 512, wl.dist, 321, "cpu").numpy().astype(np.float64)
+    repeats = groups = 0
+    for nbits, g in ((2, 32), (4, 64)):
+        for grp in W.reshape(-1, g)[:48]:
+            full = oracle.hqq_group(grp, nbits, iters=20, early_stop=False)
+            z = [oracle.hqq_group(grp, nbits, iters=t, early_stop=False).zero for t in range(21)]
+            first = None
+            for t in range(20):
+                if z[t + 1] == z[t]:
+                    assert full.trace[t + 1] == full.trace[t]
+                    first = t if first is None else first
+            r = oracle.hqq_group(grp, nbits, iters=20)
+            if first is not None:
+                assert r.stop_step <= first
+                repeats += r.stop_step == first
+            groups += 1
+    # the early stop ends at such a repeat for about a third of these groups
+    assert repeats >= groups // 5
+
+
 def test_constant_and_on_grid_groups_are_exact():
     # constant group: s = 1, z = -w, all codes 0, e0 = 0, t* = 0
     r = oracle.hqq_group(np.full(32, -0.0625), 4)
