@@ -1121,13 +1121,17 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
 
 // 17 to 64 rows of X (M <= 16 MT) for 2-, 4- and 8-bit codes, groups of GS = 5, 6, 7, K a
 // multiple of 256 and 16-byte aligned s and z, with the rows of X shared by the block:
-// a block of kSplitWaves wavefronts covers 16 NW weight rows per wavefront and one
+// a block of split_waves<NB>() wavefronts covers 16 NW weight rows per wavefront and one
 // contiguous share (split blockIdx.y of `ksplit`) of the 256-wide blocks of K.  Per block
 // of K the block loads the block's tile of X (16 MT rows x 256, 16-byte loads, two whole
 // 128-byte lines per wavefront and instruction) into LDS once for all its wavefronts, so
-// X costs 16 MT / (64 NW) reads per weight row instead of one per wavefront's 16 NW rows
-// (measured at M = 64: 2x faster than a kernel whose wavefronts each read their own X
-// straight from global memory, whose address unit then stalled).  Double-buffered with
+// the block's weight rows share one read of X instead of one per wavefront's 16 NW rows
+// (measured at M = 64: 2x faster than a kernel whose wavefronts each read their own
+// X straight from global memory, whose address unit then stalled).  For 2- and 4-bit
+// codes a block is 8 wavefronts of 16 rows, which fit 128 registers, so two blocks run on
+// a CU at four wavefronts per SIMD (4-8% faster at M = 32-64 than 4 wavefronts of 32 rows
+// at two per SIMD, same sums); 8-bit codes need more registers for the weights and keep 4
+// wavefronts of 16 NW rows (NW = 2 from 4096 weight rows).  Double-buffered with
 // one LDS-only barrier per block of K (the weight loads stay in flight across it); the
 // next block's X is held in registers during this block's arithmetic.  Lane j + 16 kq
 // takes the 64 consecutive
@@ -1139,13 +1143,15 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
 // its fp32 partial tile goes to part[split][m][n] (slabs of `slab` floats) and
 // hqq_splitk_reduce_kernel adds the splits in order.  C: lane j + 16 kq, element v holds
 // X row 16 t + 4 kq + v, weight row n0 + 16 w + j.
-constexpr int kSplitWaves = 4;            // wavefronts per block, each its own weight rows
+template <int NB>
+constexpr int split_waves() { return NB == 8 ? 4 : 8; }  // wavefronts per block, each its own weight rows
 constexpr int kXRowBytes = 512 + 16;       // a row of X per block of K in LDS (+16: rows 4 banks apart)
 
 template <int NB, int MT, int NW, int GS>
-__global__ __launch_bounds__(kSplitWaves * kWave) void hqq_splitk_kernel(const MatmulParams P) {
+__global__ __launch_bounds__(split_waves<NB>() * kWave, NB == 8 ? 1 : 4) void hqq_splitk_kernel(const MatmulParams P) {
   static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
   static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
+  constexpr int kSplitWaves = split_waves<NB>();
   constexpr int XR = 16 * MT;                    // rows of X
   constexpr int kXRows = kSplitWaves * kWave / 32;  // rows of X per round of 16-byte loads
   constexpr int kRounds = XR / kXRows;           // 16-byte loads per thread per block of K
@@ -1352,18 +1358,21 @@ bool skinny_aligned(const MatmulParams& P) {
   return P.nbits != 3 && P.K % 256 == 0 && aligned16 && P.group_shift >= 5 && P.group_shift <= 7;
 }
 
-// Split-K geometry of the aligned skinny path, from the shapes alone (results do not
-// depend on the device): 16 NW weight rows per wavefront, and K split so that there are
-// about kSplitTargetBlocks blocks (two per CU) where K allows.
-constexpr int kSplitTargetBlocks = 2048 / kSplitWaves;  // 2048 wavefronts
+// Split-K geometry of the aligned skinny path, from the shapes and the code width alone
+// (results do not depend on the device): 16 NW weight rows per wavefront (NW = 2 only for
+// 8-bit codes from 4096 rows), and K split so that there are about kSplitTargetBlocks
+// blocks (two per CU) where K allows.
+constexpr int kSplitTargetBlocks = 512;
 struct SplitGeom {
-  int nw, ksplit;
+  int waves, nw, ksplit;
   int64_t row_blocks;
 };
-SplitGeom split_geometry(int64_t N, int64_t K) {
+SplitGeom split_geometry(int64_t N, int64_t K, int nbits) {
   SplitGeom g;
-  g.nw = N >= 4096 ? 2 : 1;
-  g.row_blocks = (N + kSplitWaves * 16 * g.nw - 1) / (kSplitWaves * 16 * g.nw);
+  g.waves = nbits == 8 ? split_waves<8>() : split_waves<2>();
+  g.nw = nbits == 8 && N >= 4096 ? 2 : 1;
+  const int64_t rows = (int64_t)g.waves * 16 * g.nw;
+  g.row_blocks = (N + rows - 1) / rows;
   int64_t ks = (kSplitTargetBlocks + g.row_blocks / 2) / g.row_blocks;
   const int64_t nkb = K >> 8;
   if (ks > nkb) ks = nkb;
@@ -1380,7 +1389,7 @@ bool splitk_shapes(int64_t M, int64_t K, int nbits, int group_size) {
 
 template <int NB, int MT, int NW>
 void launch_splitk_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
-  const dim3 block(kSplitWaves * kWave);
+  const dim3 block(split_waves<NB>() * kWave);
   switch (P.group_shift) {
     case 5: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 5>), grid, block, 0, st, P); return;
     case 6: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 6>), grid, block, 0, st, P); return;
@@ -1390,12 +1399,19 @@ void launch_splitk_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
 
 template <int NB, int MT>
 void launch_splitk(MatmulParams P, hipStream_t st) {
-  const SplitGeom g = split_geometry(P.N, P.K);
+  const SplitGeom g = split_geometry(P.N, P.K, NB);
   P.ksplit = g.ksplit;
   P.slab = (P.M * P.N + 3) & ~(int64_t)3;
   const dim3 grid((unsigned)g.row_blocks, (unsigned)g.ksplit);
-  if (g.nw == 2) launch_splitk_nw<NB, MT, 2>(P, grid, st);
-  else launch_splitk_nw<NB, MT, 1>(P, grid, st);
+  if constexpr (NB == 8) {
+    if (g.nw == 2) {
+      launch_splitk_nw<NB, MT, 2>(P, grid, st);
+    } else {
+      launch_splitk_nw<NB, MT, 1>(P, grid, st);
+    }
+  } else {
+    launch_splitk_nw<NB, MT, 1>(P, grid, st);
+  }
   if (g.ksplit > 1) {
     int64_t blocks = (P.M * P.N + 4 * kBlock - 1) / (4 * kBlock);
     if (blocks > 4096) blocks = 4096;
@@ -1481,7 +1497,7 @@ hipError_t launch_nb(const MatmulParams& P, int cus, hipStream_t st) {
 
 int64_t matmul_workspace_bytes(int64_t M, int64_t N, int64_t K, int nbits, int group_size) {
   if (!splitk_shapes(M, K, nbits, group_size) || N <= 0) return 0;
-  const SplitGeom g = split_geometry(N, K);
+  const SplitGeom g = split_geometry(N, K, nbits);
   if (g.ksplit <= 1) return 0;
   return (int64_t)g.ksplit * ((M * N + 3) & ~(int64_t)3) * (int64_t)sizeof(float);
 }

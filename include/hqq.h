@@ -343,8 +343,9 @@ int hqq_meta_quantize_batch(const hqq_batch_entry_t* entries,
  *              with 2-, 4- or 8-bit codes, groups of 32-128 and K a multiple of 256, K is
  *              split over several blocks whose fp32 partial products go to the workspace
  *              and are added in a fixed order (results do not depend on the device or the
- *              run); the split depends on the shapes only.  Written and read on `stream`,
- *              no state between calls: calls that share a workspace must be ordered.
+ *              run); the split depends on the shapes and nbits only.  Written and read on
+ *              `stream`, no state between calls: calls that share a workspace must be
+ *              ordered.
  *              NULL where it is needed: HQQ_ERR_INVALID_ARG.
  * Conventions and errors as for hqq_quantize.
  */

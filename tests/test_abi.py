@@ -160,7 +160,7 @@ def test_matmul_rejects_before_launch(lib, kw, status):
 def test_matmul_workspace_bytes(lib):
     wb = hq.hqq_matmul_workspace_bytes
     # split-K path: 17..64 rows of X, 2/4/8-bit codes, groups of 32..128, K % 256 == 0
-    # (N = 1024: 16 blocks of 64 weight rows, K = 8192: 32 blocks of 256 -> 32 splits)
+    # (N = 1024: 8 blocks of 128 weight rows, K = 8192: 32 blocks of 256 -> 32 splits)
     assert wb(32, 1024, 8192, 4, 64) == 32 * 32 * 1024 * 4
     assert wb(64, 8192, 8192, 2, 32) == 8 * 64 * 8192 * 4   # 64 blocks of 128 rows: 8 splits
     assert wb(17, 5, 256, 8, 128) == 0      # one block of K: no partials
