@@ -900,7 +900,7 @@ def summarize_counters(dirs: list, out_dir: str, command: str):
     kernels = sorted(tab)
     lines = ["# Counters of the product kernels on one 28672 x 8192 b2 g32 weight", "",
              "hqq_matmul at M = 1 (hqq_gemv_packed_kernel), M = 4, 16 (hqq_skinny_kernel), "
-             "M = 64 (hqq_splitk_kernel + hqq_splitk_reduce_kernel) "
+             "M = 64 (hqq_splitk_kernel; K is not split at this shape) "
              "and M = 512, 4096 (hqq_gemm_kernel), "
              "5 calls each (bench.py --profile-matmul); values per dispatch, averaged. "
              "GRBM_GUI_ACTIVE counts on every XCD (8 per device).", "",

@@ -1368,9 +1368,10 @@ bool skinny_aligned(const MatmulParams& P) {
 
 // Split-K geometry of the aligned skinny path, from the shapes and the code width alone
 // (results do not depend on the device): 16 NW weight rows per wavefront (NW = 2 only for
-// 8-bit codes from 4096 rows), and K split so that there are about kSplitTargetBlocks
-// blocks (two per CU) where K allows.
-constexpr int kSplitTargetBlocks = 512;
+// 8-bit codes from 4096 rows), and K split so that a launch has about kSplitTargetWaves
+// wavefronts where K allows (two per SIMD; with 8-wavefront blocks, 4096 split the
+// 28672-row matrices in two and were 1-4% slower at M = 32-64 than no split there).
+constexpr int kSplitTargetWaves = 2048;
 struct SplitGeom {
   int waves, nw, ksplit;
   int64_t row_blocks;
@@ -1381,7 +1382,8 @@ SplitGeom split_geometry(int64_t N, int64_t K, int nbits) {
   g.nw = nbits == 8 && N >= 4096 ? 2 : 1;
   const int64_t rows = (int64_t)g.waves * 16 * g.nw;
   g.row_blocks = (N + rows - 1) / rows;
-  int64_t ks = (kSplitTargetBlocks + g.row_blocks / 2) / g.row_blocks;
+  const int64_t target = kSplitTargetWaves / g.waves;  // blocks
+  int64_t ks = (target + g.row_blocks / 2) / g.row_blocks;
   const int64_t nkb = K >> 8;
   if (ks > nkb) ks = nkb;
   g.ksplit = ks < 1 ? 1 : (int)ks;

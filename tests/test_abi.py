@@ -162,7 +162,9 @@ def test_matmul_workspace_bytes(lib):
     # split-K path: 17..64 rows of X, 2/4/8-bit codes, groups of 32..128, K % 256 == 0
     # (N = 1024: 8 blocks of 128 weight rows, K = 8192: 32 blocks of 256 -> 32 splits)
     assert wb(32, 1024, 8192, 4, 64) == 32 * 32 * 1024 * 4
-    assert wb(64, 8192, 8192, 2, 32) == 8 * 64 * 8192 * 4   # 64 blocks of 128 rows: 8 splits
+    assert wb(64, 8192, 8192, 2, 32) == 4 * 64 * 8192 * 4   # 64 blocks of 128 rows: 4 splits
+    assert wb(64, 8192, 8192, 8, 32) == 8 * 64 * 8192 * 4   # 8-bit: 4-wavefront blocks, 8 splits
+    assert wb(64, 28672, 8192, 4, 64) == 0                  # 224 blocks fill the chip: no split
     assert wb(17, 5, 256, 8, 128) == 0      # one block of K: no partials
     assert wb(17, 7, 1024, 4, 64) == 4 * 120 * 4  # M N = 119 rounded up to 120 floats per slab
     for args in [(16, 1024, 8192, 4, 64), (2, 1024, 8192, 4, 64), (65, 1024, 8192, 4, 64),

@@ -152,7 +152,7 @@ def test_exact_products_skinny_paths(hq, nbits):
 
 def test_split_k_is_deterministic_and_exact(hq):
     """The split-K path (17 to 64 rows of X): many partial slabs (N = 1024, K = 8192: 32
-    splits; N = 8192, K = 4096: 8) are added in a fixed order, so repeated calls give
+    splits; N = 8192, K = 4096: 4) are added in a fixed order, so repeated calls give
     identical bits on general inputs, and exact inputs give the exact product."""
     rng = np.random.default_rng(77)
     for M, N, K, nbits, g in [(64, 1024, 8192, 4, 64), (24, 8192, 4096, 2, 32),
