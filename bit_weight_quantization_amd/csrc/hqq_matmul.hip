@@ -1128,12 +1128,16 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
 // the block's weight rows share one read of X instead of one per wavefront's 16 NW rows
 // (measured at M = 64: 2x faster than a kernel whose wavefronts each read their own
 // X straight from global memory, whose address unit then stalled).  For 2- and 4-bit
-// codes a block is 8 wavefronts of 16 rows, which fit 128 registers, so two blocks run on
-// a CU at four wavefronts per SIMD (4-8% faster at M = 32-64 than 4 wavefronts of 32 rows
-// at two per SIMD, same sums); 8-bit codes need more registers for the weights and keep 4
-// wavefronts of 16 NW rows (NW = 2 from 4096 weight rows).  Double-buffered with
-// one LDS-only barrier per block of K (the weight loads stay in flight across it); the
-// next block's X is held in registers during this block's arithmetic.  Lane j + 16 kq
+// codes a block is 8 wavefronts of 16 rows (4-8% faster at M = 32-64 than 4 wavefronts of
+// 32 rows, same sums); a launch has about 256 blocks, one per CU, so each wavefront may
+// use up to 256 registers (two per SIMD); 8-bit codes need more registers for the
+// weights and keep 4 wavefronts of 16 NW rows (NW = 2 from 4096 weight rows).
+// Double-buffered with one LDS-only barrier per block of K (the weight loads stay in
+// flight across it); the next block's X is held in registers during this block's
+// arithmetic, and the X fragments of each pair of MFMA steps are read from LDS one pair
+// ahead (M = 64 layer 0.264 -> 0.239 ms b2, same sums).  Blocks of 7 wavefronts for the
+// 28672-row matrices (256 blocks instead of 224 of 8) were measured no faster: the time
+// follows each wavefront's own chain of decode, loads and MFMAs, not the CU count.  Lane j + 16 kq
 // takes the 64 consecutive
 // codes k0 + 64 kq .. + 64 of each of its weight rows in one load, and MFMA step i
 // (v_mfma_f32_16x16x32_f16) gives the instruction's k index 8 kq + e the real
@@ -1145,10 +1149,24 @@ __global__ __launch_bounds__(kSkinnyWaves2 * kWave) void hqq_skinny_kernel(const
 // X row 16 t + 4 kq + v, weight row n0 + 16 w + j.
 template <int NB>
 constexpr int split_waves() { return NB == 8 ? 4 : 8; }  // wavefronts per block, each its own weight rows
+// Register sets of X and weights per wavefront: the block of K it works on and the next
+// one in flight.  (Deeper rings, 3-5 sets with the loads issued 2-4 blocks ahead, were
+// measured no faster at M = 32 and 64: the loop is not waiting on HBM.)
+template <int NB>
+constexpr int split_prefetch() { return 2; }
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 constexpr int kXRowBytes = 512 + 16;       // a row of X per block of K in LDS (+16: rows 4 banks apart)
 
-template <int NB, int MT, int NW, int GS>
-__global__ __launch_bounds__(split_waves<NB>() * kWave, NB == 8 ? 1 : 4) void hqq_splitk_kernel(const MatmulParams P) {
+template <int NB, int MT, int NW, int GS, int PD>
+__global__ __launch_bounds__(split_waves<NB>() * kWave, NB == 8 ? 1 : 2) void hqq_splitk_kernel(const MatmulParams P) {
   static_assert(NB == 2 || NB == 4 || NB == 8, "byte-aligned widths");
   static_assert(GS >= 5 && GS <= 7, "groups of 32, 64 or 128");
   constexpr int kSplitWaves = split_waves<NB>();
@@ -1225,31 +1243,60 @@ __global__ __launch_bounds__(split_waves<NB>() * kWave, NB == 8 ? 1 : 4) void hq
       }
     }
   };
-  lds_u32x4 xr[kRounds];
-  auto load_x = [&](int64_t c) {
+  // X and weights of PD - 1 blocks of K in flight, in register rings of PD sets (slot =
+  // block index within the split mod PD); X goes to LDS one block ahead
+  lds_u32x4 xr[PD][kRounds];
+  Wt wr[PD];
+  auto load_x = [&](int64_t c, lds_u32x4 (&o)[kRounds]) {
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) xr[r] = *reinterpret_cast<const lds_u32x4*>(xsrc[r] + (c << 8));
+    for (int r = 0; r < kRounds; ++r) o[r] = *reinterpret_cast<const lds_u32x4*>(xsrc[r] + (c << 8));
   };
-  auto write_x = [&](int buf) {
+  auto write_x = [&](int buf, const lds_u32x4 (&o)[kRounds]) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r)
-      *reinterpret_cast<lds_u32x4*>(&xs[buf][(kXRows * r + xrow0) * kXRowBytes + 16 * xpos]) = xr[r];
+      *reinterpret_cast<lds_u32x4*>(&xs[buf][(kXRows * r + xrow0) * kXRowBytes + 16 * xpos]) = o[r];
   };
 
-  // one block of K from LDS buffer `buf` and weights `cur`; unless it is the split's
-  // last (LAST, a separate copy of the body, so the loop has no branch and its waits
-  // count exactly), the next block's X and weights are loaded first and land in the
-  // other buffer after this block's reads
-  auto block = [&](auto last_const, int64_t c, int buf, const Wt& cur, Wt& nxt) {
-    constexpr bool LAST = decltype(last_const)::value;
-    if constexpr (!LAST) {
-      load_x(c + 1);
-      load_wt(c + 1, nxt);
+  // block c of the split (slot I = its index mod PD, LDS buffer B = its index mod 2):
+  // first the loads of block c + PD - 1 into slot (I + PD - 1) mod PD (its previous
+  // block was read by block c - 1; LOAD = 0: none, 1: always, 2: if inside the split),
+  // then the arithmetic of block c from LDS and slot I, then X of block c + 1 into the
+  // other LDS buffer (every wavefront finished reading it before the last barrier)
+  auto block = [&](auto i_const, auto load_const, int64_t c) {
+    constexpr int I = decltype(i_const)::value % PD;
+    constexpr int buf = decltype(i_const)::value & 1;
+    constexpr int LOAD = decltype(load_const)::value;
+    constexpr int IN = (I + PD - 1) % PD;
+    if constexpr (LOAD == 1) {
+      load_x(c + PD - 1, xr[IN]);
+      load_wt(c + PD - 1, wr[IN]);
+    } else if constexpr (LOAD == 2) {
+      if (c + PD - 1 < kb1) {
+        load_x(c + PD - 1, xr[IN]);
+        load_wt(c + PD - 1, wr[IN]);
+      }
     }
+    const Wt& cur = wr[I];
     __builtin_amdgcn_sched_barrier(0);
     const unsigned char* xb = xs[buf] + j * kXRowBytes + 128 * kqp;
+    auto read_af = [&](int i, int t) -> half8_t {
+      return __builtin_bit_cast(half8_t, *reinterpret_cast<const lds_u32x4*>(xb + (16 * t) * kXRowBytes + 16 * i));
+    };
+    // the X fragments of the step pair ip + 1 are read while ip's codes are decoded and
+    // multiplied (each MFMA otherwise waited on the LDS read issued just before it)
+    half8_t afs[2][2][MT];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) afs[0][b][t] = read_af(b, t);
 #pragma unroll
     for (int ip = 0; ip < 4; ++ip) {  // steps 2 ip, 2 ip + 1: 16 codes per row
+      if (ip + 1 < 4) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) afs[(ip + 1) & 1][b][t] = read_af(2 * (ip + 1) + b, t);
+      }
       half8_t bf[2][NW];
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
@@ -1276,41 +1323,40 @@ __global__ __launch_bounds__(split_waves<NB>() * kWave, NB == 8 ? 1 : 4) void hq
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int i = 2 * ip + b;
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const half8_t af = __builtin_bit_cast(
-              half8_t, *reinterpret_cast<const lds_u32x4*>(xb + (16 * t) * kXRowBytes + 16 * i));
+          const half8_t af = afs[ip & 1][b][t];
 #pragma unroll
           for (int w = 0; w < NW; ++w)
             acc[t][w] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[b][w], acc[t][w], 0, 0, 0);
         }
       }
     }
-    if constexpr (!LAST) {
-      write_x(buf ^ 1);  // every wavefront finished reading that buffer before the last barrier
+    if (LOAD == 1 || c + 1 < kb1) {
+      write_x(buf ^ 1, xr[(I + 1) % PD]);
       lds_barrier();
     }
   };
+  // U = lcm(PD, 2) blocks per round of the loop, whose loads all lie inside the split
+  // (unconditional: their waits count exactly); the last up to U + PD - 2 blocks after it
+  constexpr int U = PD % 2 == 0 ? PD : 2 * PD;
   if (kb0 < kb1) {
-    constexpr std::integral_constant<bool, false> more{};
-    constexpr std::integral_constant<bool, true> last{};
-    Wt wa, wb;
-    load_x(kb0);
-    load_wt(kb0, wa);
-    write_x(0);
+#pragma unroll
+    for (int p = 0; p + 1 < PD; ++p) {
+      if (kb0 + p < kb1) {
+        load_x(kb0 + p, xr[p]);
+        load_wt(kb0 + p, wr[p]);
+      }
+    }
+    write_x(0, xr[0]);
     lds_barrier();
     int64_t c = kb0;
-    for (; c + 2 < kb1; c += 2) {
-      block(more, c, 0, wa, wb);
-      block(more, c + 1, 1, wb, wa);
+    for (; c + U + PD - 2 < kb1; c += U) {
+      static_for<U>([&](auto i) { block(i, std::integral_constant<int, 1>{}, c + i); });
     }
-    if (c + 1 < kb1) {  // two blocks left
-      block(more, c, 0, wa, wb);
-      block(last, c + 1, 1, wb, wa);
-    } else {
-      block(last, c, 0, wa, wb);
-    }
+    static_for<U + PD - 2>([&](auto i) {
+      if (c + i < kb1) block(i, std::integral_constant<int, 2>{}, c + i);
+    });
   }
   // the wavefront's tile: Y directly (one split) or the split's partial slab
 #pragma unroll
@@ -1400,10 +1446,11 @@ bool splitk_shapes(int64_t M, int64_t K, int nbits, int group_size) {
 template <int NB, int MT, int NW>
 void launch_splitk_nw(const MatmulParams& P, dim3 grid, hipStream_t st) {
   const dim3 block(split_waves<NB>() * kWave);
+  constexpr int PD = split_prefetch<NB>();
   switch (P.group_shift) {
-    case 5: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 5>), grid, block, 0, st, P); return;
-    case 6: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 6>), grid, block, 0, st, P); return;
-    default: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 7>), grid, block, 0, st, P); return;
+    case 5: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 5, PD>), grid, block, 0, st, P); return;
+    case 6: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 6, PD>), grid, block, 0, st, P); return;
+    default: hipLaunchKernelGGL((hqq_splitk_kernel<NB, MT, NW, 7, PD>), grid, block, 0, st, P); return;
   }
 }
 
