@@ -35,6 +35,11 @@ PROFILE_PMC = os.path.join(ROOT, "profiles", "hqq_solve_llama70b_pmc.json")
 # Sources of the solver kernel (the profile's counters are void once they change).
 KERNEL_SRC = [os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", f)
               for f in ("hqq_solver.h", "hqq_kernels.hip", "hqq_internal.h")]
+# Counters of the solver variants (one rocprofv3 pass over --variants-only), and the
+# sources of the whole-tensor stop's kernels they are void without.
+PROFILE_VARIANTS = os.path.join(ROOT, "profiles", "hqq_solver_variants_issue_llama70b_layer0.json")
+TENSOR_STOP_SRC = [os.path.join(ROOT, "bit_weight_quantization_amd", "csrc", f)
+                   for f in ("hqq_solver.h", "hqq_tensor_stop.hip", "hqq_internal.h")]
 
 # MI355X fp32 vector peak: 157.3 TFLOP/s counts an FMA as two flops, i.e. 78.6 T full-rate
 # lane-operations per second = 256 CUs x 4 SIMDs x 32 lanes per clock x 2.4 GHz (one wave64
@@ -69,9 +74,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(paths=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRC:
+    for path in (KERNEL_SRC if paths is None else paths):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -121,6 +126,35 @@ def issued_valu_from_profile(n_weights: float, settings, step_s: float):
             "count": "issued VALU wave-instructions x 64 lanes, a transcendental as 4 full-rate "
                      "slots (counters of the committed profile, same kernel source), over the "
                      "timed launches"}
+
+
+def tensor_stop_issued_from_profile(g: int, n_matrices: int, n_weights: float, ms: float):
+    """Issued VALU work of the whole-tensor stop's two lockstep kernels at group size g,
+    from the committed counter summary of the solver variants (VALU wave-instructions, a
+    transcendental priced at 4 full-rate slots, x 64 lanes, per weight: the profiled pass
+    made dispatches / n_matrices calls per matrix over the same matrices), set against the
+    live time `ms` of one call per matrix.  Unlike the op model, this counts only work the
+    kernels did, so the fraction is at most 1.  None if the summary is absent or was taken
+    on another source of those kernels."""
+    if not os.path.exists(PROFILE_VARIANTS):
+        return None
+    with open(PROFILE_VARIANTS) as f:
+        prof = json.load(f)
+    if prof.get("tensor_stop_source_sha256_16") != kernel_source_hash(TENSOR_STOP_SRC):
+        return None
+    ks = [k for k in prof.get("kernels", {}) if k.startswith(f"hqq_lockstep_kernel<{g},")]
+    first = prof["kernels"].get(f"hqq_lockstep_kernel<{g}, 0, false>")
+    if not ks or not first or n_matrices <= 0:
+        return None
+    runs = first["dispatches"] / n_matrices
+    slots = sum((prof["kernels"][k]["valu_wave_instr"] + 3.0 * prof["kernels"][k]["trans_wave_instr"])
+                * 64 for k in ks)
+    per_weight = slots / (runs * n_weights)
+    return {"slots_per_weight": round(per_weight, 2),
+            "frac": round(per_weight * n_weights / (ms * 1e-3) / PEAK_VALU_SLOTS, 4),
+            "count": "issued VALU wave-instructions x 64 lanes of hqq_lockstep_kernel, a "
+                     "transcendental as 4 full-rate slots (committed counter summary, same "
+                     "kernel source), over the live time"}
 
 
 def _kernel_key(name: str):
@@ -623,6 +657,9 @@ def measure_variants(hq, lib, torch, Ws, settings, solver, stream, sh, dev, reps
                 ops = float(np.sum(g_per * g * (2 * OPS_INIT + OPS_FINAL + OPS_EVAL * n_eval +
                                                 OPS_UPDATE * n_upd)))
                 extra = {"t_star_per_matrix": [int(x) for x in ts]}
+                issued = tensor_stop_issued_from_profile(g, len(Ws), n_w, ms)
+                if issued is not None:
+                    extra["issued_valu"] = issued
             else:
                 it = v["iters"]
                 if v["early_stop"]:
@@ -987,6 +1024,8 @@ def summarize_issue(pmc_dir: str, out_dir: str, command: str):
              "dispatch durations x 78.6 T full-rate lane-slots/s.", "",
              "| kernel | dispatches | total ms | VALU wave-instr | transcendental | active lanes | issue fraction |",
              "|---|---|---|---|---|---|---|"]
+    side = {"tensor_stop_source_sha256_16": kernel_source_hash(TENSOR_STOP_SRC),
+            "solver_source_sha256_16": kernel_source_hash(), "kernels": {}}
     for k in sorted(acc):
         ds = acc[k].values()
         dur = sum(d["_dur"] for d in ds)
@@ -999,8 +1038,15 @@ def summarize_issue(pmc_dir: str, out_dir: str, command: str):
         frac = (vi + (tau - 1) * tr) * 64 / dur / PEAK_VALU_SLOTS
         lanes = tc / max(64 * av, 1)
         lines.append(f"| {k} | {len(ds)} | {dur * 1e3:.3f} | {vi:.4g} | {tr:.4g} | {lanes:.3f} | {frac:.3f} |")
-    lines += ["", "Command:", "", "```", command, "```", ""]
+        side["kernels"][k] = {"dispatches": len(ds), "total_ms": round(dur * 1e3, 4),
+                              "valu_wave_instr": vi, "trans_wave_instr": tr}
+    lines += ["", f"Kernel sources (sha256, first 16 hex digits): whole-tensor stop "
+              f"{side['tensor_stop_source_sha256_16']}, per-group solver "
+              f"{side['solver_source_sha256_16']}.",
+              "", "Command:", "", "```", command, "```", ""]
     os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, "hqq_solver_variants_issue_llama70b_layer0.json"), "w") as f:
+        json.dump(side, f, indent=1)
     with open(os.path.join(out_dir, "hqq_solver_variants_issue_llama70b_layer0.md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))

@@ -65,3 +65,41 @@ def test_committed_profile_matches_the_solver_source():
         prof = json.load(f)
     assert prof["kernel_source_sha256_16"] == bench.kernel_source_hash()
     assert set(prof["sq"]) == {"hqq_solve_kernel<32>", "hqq_solve_kernel<64>"}
+
+
+def _variants_profile(tmp_path, sha):
+    prof = {"tensor_stop_source_sha256_16": sha, "kernels": {
+        "hqq_lockstep_kernel<32, 0, false>": {"dispatches": 14, "total_ms": 1.0,
+                                              "valu_wave_instr": 1000.0, "trans_wave_instr": 100.0},
+        "hqq_lockstep_kernel<32, 0, true>": {"dispatches": 14, "total_ms": 1.0,
+                                             "valu_wave_instr": 500.0, "trans_wave_instr": 50.0},
+        "hqq_lockstep_kernel<64, 0, false>": {"dispatches": 14, "total_ms": 1.0,
+                                              "valu_wave_instr": 9e9, "trans_wave_instr": 9e9},
+        "hqq_tensor_total_kernel": {"dispatches": 28, "total_ms": 0.1,
+                                    "valu_wave_instr": 9e9, "trans_wave_instr": 0.0}}}
+    path = tmp_path / "variants.json"
+    path.write_text(json.dumps(prof))
+    return str(path)
+
+
+def test_tensor_stop_issued_from_a_matching_profile(tmp_path, monkeypatch):
+    sha = bench.kernel_source_hash(bench.TENSOR_STOP_SRC)
+    monkeypatch.setattr(bench, "PROFILE_VARIANTS", _variants_profile(tmp_path, sha))
+    got = bench.tensor_stop_issued_from_profile(32, 7, 1000.0, 1e-6)
+    # 14 dispatches over 7 matrices = 2 calls each; only the g = 32 lockstep kernels count:
+    # (1000 + 3*100 + 500 + 3*50) * 64 lane-slots over 2 * 1000 weights = 62.4 per weight
+    assert got["slots_per_weight"] == pytest.approx(62.4)
+    assert got["frac"] == pytest.approx(62.4 * 1000 / 1e-9 / bench.PEAK_VALU_SLOTS, rel=1e-3)
+
+
+def test_tensor_stop_issued_is_null_on_another_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_VARIANTS", _variants_profile(tmp_path, "0" * 16))
+    assert bench.tensor_stop_issued_from_profile(32, 7, 1000.0, 1e-6) is None
+    monkeypatch.setattr(bench, "PROFILE_VARIANTS", str(tmp_path / "absent.json"))
+    assert bench.tensor_stop_issued_from_profile(32, 7, 1000.0, 1e-6) is None
+
+
+def test_committed_variants_profile_matches_the_tensor_stop_source():
+    with open(bench.PROFILE_VARIANTS) as f:
+        prof = json.load(f)
+    assert prof["tensor_stop_source_sha256_16"] == bench.kernel_source_hash(bench.TENSOR_STOP_SRC)
