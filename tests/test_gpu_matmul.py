@@ -179,6 +179,29 @@ def test_split_k_is_deterministic_and_exact(hq):
         _say(f"split-K M={M} N={N} K={K} b{nbits} g{g}: {wb} workspace bytes, repeatable, exact")
 
 
+@pytest.mark.parametrize("nbits,g", [(2, 32), (4, 64)])
+def test_split_k_unsplit_odd_block_count(hq, nbits, g):
+    """The split-K kernel with one split over many blocks of K: a ragged 28722-row weight
+    (225 blocks of 128 rows, so K is not split) with an odd count of 7 blocks of 256.
+    This runs full rounds of its loop, whose loads run a block ahead, and then a last
+    block that loads nothing.  Exact inputs give the exact product on sampled rows
+    (including the ragged last ones); repeated calls are bit-identical."""
+    N, K = 28722, 7 * 256
+    assert hq.hqq_matmul_workspace_bytes(64, N, K, nbits, g) == 0  # one split: no slabs
+    codes, packed, s, z = _weight(N, K, nbits, g, seed=N + nbits, exact=True)
+    rng = np.random.default_rng(5 + nbits)
+    rows = np.unique(np.concatenate([[0, N - 2, N - 1], rng.choice(N, 40, replace=False)]))
+    bpr = K * nbits // 8
+    for M in (64, 20):
+        X = rng.integers(-2, 3, (M, K)).astype(np.float16)
+        Y = _run(hq, X, packed, s, z, N, nbits, g, out_f32=1)
+        assert np.array_equal(Y, _run(hq, X, packed, s, z, N, nbits, g, out_f32=1))
+        ref = oracle.hqq_matmul(X, packed.reshape(N, bpr)[rows].ravel(), s[rows], z[rows],
+                                len(rows), nbits, g)
+        assert np.array_equal(Y[:, rows], ref)
+        _say(f"split-K unsplit M={M} N={N} K={K} b{nbits} g{g}: exact, repeatable")
+
+
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 32), (8, 128)])
 def test_exact_products_large_tiles(hq, nbits, g):
     """A large ragged product on the matrix-core kernel (M = 1040 and N = 16500, 645+
